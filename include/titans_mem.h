@@ -1,0 +1,161 @@
+/*
+ * titans_mem.h -- C ABI of the MI355X (gfx950) Titans neural long-term memory.
+ *
+ * One call runs the memory's whole hot path over a batch of independent
+ * (batch, head) streams: the chunked test-time update and per-token retrieval
+ * of "Titans: Learning to Memorize at Test Time" (mer.dev notes):
+ *
+ *   loss      l(M; x_t) = ||M(k_t) - v_t||^2          section 3.1, "Objective"
+ *   surprise  S_t = eta_t S_{t-1} - theta_t grad l    section 3.1, "Learning
+ *                                                      Process and Surprise Metric"
+ *   write     M_t = (1 - alpha_t) M_{t-1} + S_t        section 3.1, "Forgetting
+ *                                                      Mechanism"
+ *   read      y_t = M*(q_t), no weight change          section 3.1, "Retrieving
+ *                                                      a Memory"
+ *   chunking  gradients of a chunk of b tokens taken at the chunk-start
+ *             weights M_{t'}                           section 3.2, "How to
+ *                                                      Parallelize ..."
+ *
+ * The memory M is a matrix W (n_layers == 1, M(k) = W k) or a bias-free MLP
+ * (n_layers >= 2) d -> hidden -> ... -> hidden -> d with SiLU after every
+ * layer but the last (section 3.1 "Memory Architecture"; block details in
+ * section 4.4 use SiLU).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensors are contiguous and row-major.  Streams are indexed
+ *   s = b * H + h.  Token rows are [N, d] per stream.
+ * - Parameter layout per stream: layers 1..L concatenated, layer l stored
+ *   row-major as [n_l x n_{l-1}] (column-vector convention M(k) = W k); S
+ *   has the same layout.  P = sum_l n_l n_{l-1} (titans_mem_param_count).
+ * - The gradient used is (M(k) - v) dM/dW, i.e. the gradient of
+ *   0.5 ||M(k) - v||^2, the scale section 3.2 prints for the linear case.
+ *   Pass 2*theta for the gradient of ||.||^2 itself (theta enters linearly).
+ * - Tokens are 0-indexed; chunk c covers [c*chunk, min((c+1)*chunk, N)) and
+ *   differentiates at the state left by the previous chunk.  N need not be
+ *   a multiple of chunk: the last chunk is shorter.
+ * - Gates are not range-checked; non-finite values propagate.
+ * - Device pointers must be 16-byte aligned.
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *   stream): they return after enqueueing and never synchronise.  Argument
+ *   errors (codes -1..-4) are detected on the host before anything is
+ *   enqueued, so they can be tested without a GPU.
+ * - The library allocates no device memory and keeps no global mutable
+ *   state; calls are re-entrant.  The caller owns every buffer.
+ */
+#ifndef TITANS_MEM_H
+#define TITANS_MEM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TITANS_MEM_ABI_VERSION 1
+
+/* status codes */
+#define TM_OK               0
+#define TM_ERR_INVALID     -1  /* null pointer, dimension <= 0, chunk <= 0, misaligned pointer, bad enum, wrong abi_version */
+#define TM_ERR_UNSUPPORTED -2  /* shape / dtype / flag combination this build has no kernel for */
+#define TM_ERR_WORKSPACE   -3  /* workspace smaller than titans_mem_workspace_bytes() */
+#define TM_ERR_ALIAS       -4  /* illegal overlap between buffers */
+#define TM_ERR_HIP         -5  /* the HIP runtime reported an error when launching */
+
+/* dtype of k, v, q and y (the io tensors); state and gates are always fp32 */
+#define TM_IO_F32  0
+#define TM_IO_BF16 1
+
+#define TM_ACT_SILU 0
+
+/* which state retrieval reads (section 3.1 "Retrieving a Memory" has no
+ * time index; the write-then-read memory view of section 2.1 reads M_t) */
+#define TM_READ_AFTER_WRITE 0  /* y_t = M_{W_t}(q_t): the state after token t's write */
+#define TM_READ_CHUNK_START 1  /* y_t = M_{W_t'}(q_t): the state at the start of t's chunk */
+
+/* flags */
+#define TM_FLAG_FORCE_GENERIC 1u  /* run the shape-generic fp32 kernel even where a specialised one exists */
+
+/* kernel paths reported by titans_mem_select_path */
+#define TM_PATH_GENERIC_F32   0   /* any shape: fp32 VALU, state in global memory */
+#define TM_PATH_MLP2_D64_H256 1   /* 2-layer, d=64, hidden=256, chunk<=64, bf16 io: MFMA, register-resident state */
+
+typedef struct {
+    int32_t abi_version;  /* must equal TITANS_MEM_ABI_VERSION */
+    int32_t B, H, N;      /* batch, heads, tokens per stream (N >= 0) */
+    int32_t d;            /* key = value = query width */
+    int32_t hidden;       /* MLP width; ignored when n_layers == 1 */
+    int32_t n_layers;     /* 1 = linear memory W (d x d); >= 2 = MLP */
+    int32_t activation;   /* TM_ACT_SILU */
+    int32_t io_dtype;     /* TM_IO_F32 or TM_IO_BF16 */
+    int32_t read_mode;    /* TM_READ_AFTER_WRITE or TM_READ_CHUNK_START */
+    uint32_t flags;       /* TM_FLAG_* */
+} titans_mem_desc;
+
+/* ABI version this library was built with. */
+int32_t titans_mem_abi_version(void);
+
+/* Parameters per stream (P), or a negative status for an invalid shape. */
+int64_t titans_mem_param_count(const titans_mem_desc* desc);
+
+/* Kernel path titans_mem_forward would run for (desc, chunk), or a negative
+ * status (TM_ERR_INVALID / TM_ERR_UNSUPPORTED). */
+int32_t titans_mem_select_path(const titans_mem_desc* desc, int32_t chunk);
+
+/* Device workspace titans_mem_forward needs for (desc, chunk), in bytes
+ * (0 when the selected kernel needs none), or a negative status. */
+int64_t titans_mem_workspace_bytes(const titans_mem_desc* desc, int32_t chunk);
+
+/*
+ * titans_mem_forward -- chunked update plus retrieval over all B*H streams.
+ *
+ *   k, v, q    [B,H,N,d]  io dtype, device, read-only
+ *   alpha, eta, theta  [B,H,N] fp32, device, read-only: forgetting gate,
+ *              surprise decay, momentary-surprise weight
+ *   W_in, S_in [B,H,P]  fp32, device, read-only: memory weights and
+ *              surprise momentum before token 0
+ *   chunk      b >= 1: tokens per chunk (gradients at the chunk-start state)
+ *   y_out      [B,H,N,d]  io dtype, device, written: y_t per token
+ *              (computed in fp32, rounded once to nearest-even)
+ *   W_out, S_out [B,H,P] fp32, device, written: state after token N-1.
+ *              W_out == W_in and/or S_out == S_in (exact in-place) is
+ *              allowed; any other overlap among all buffers is TM_ERR_ALIAS.
+ *   workspace  device scratch of at least titans_mem_workspace_bytes(desc,
+ *              chunk) bytes (may be NULL when that is 0); its contents on
+ *              entry do not matter and are undefined on return.
+ *   stream     hipStream_t to enqueue on (NULL = default stream).
+ *
+ * Returns TM_OK or a negative status.  Resuming: passing (W_out, S_out) of
+ * a call as (W_in, S_in) of the next, with a split on a chunk boundary,
+ * continues the same sequence.
+ */
+int titans_mem_forward(const titans_mem_desc* desc,
+                       const void* k, const void* v, const void* q,
+                       const float* alpha, const float* eta, const float* theta,
+                       const float* W_in, const float* S_in,
+                       int32_t chunk,
+                       void* y_out, float* W_out, float* S_out,
+                       void* workspace, int64_t workspace_bytes,
+                       void* stream);
+
+/*
+ * titans_mem_retrieve -- pure retrieval y = M*_W(q) at a fixed state
+ * (section 3.1 "Retrieving a Memory": a forward pass without weight
+ * adjustment), e.g. a lookup after a context has been consumed.
+ *
+ *   q      [B,H,N,d] io dtype, device
+ *   W      [B,H,P]   fp32, device (the state to read)
+ *   y_out  [B,H,N,d] io dtype, device, must not overlap q or W
+ * Uses desc's shape fields (read_mode and flags are ignored).
+ */
+int titans_mem_retrieve(const titans_mem_desc* desc, const void* q, const float* W,
+                        void* y_out, void* stream);
+
+/* Static text for a status code. */
+const char* titans_mem_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TITANS_MEM_H */

@@ -1,0 +1,61 @@
+"""Build libtitans_mem.so in-tree with hipcc for gfx950.
+
+Every call recompiles (the "does it build" check).  Objects go to _build/;
+the shared library lands next to this file, where the binding loads it.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+OUT = os.path.join(PKG, "libtitans_mem.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+ARCH = "gfx950"
+
+SOURCES = ["tm_host.cpp", "tm_generic.hip", "tm_mlp2.hip"]
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-I" + CSRC]
+# no packed fp32 instructions in device code (v_pk_* fp32 forms)
+DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-munsafe-fp-atomics"]
+
+
+def hipcc() -> str:
+    for cand in ("/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def _compile(src: str, extra=()) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    path = os.path.join(CSRC, src)
+    cmd = [hipcc()] + COMMON + list(extra)
+    if src.endswith(".hip"):
+        cmd += ["-x", "hip"] + DEVICE
+    cmd += ["-c", path, "-o", obj]
+    subprocess.check_call(cmd)
+    return obj
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
+    tmp = OUT + ".tmp%d" % os.getpid()
+    subprocess.check_call([hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs)
+    os.replace(tmp, OUT)
+    if verbose:
+        print("built", OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    build(verbose=True, extra=sys.argv[1:])

@@ -1,0 +1,193 @@
+// Host side of the C ABI declared in include/titans_mem.h: argument
+// validation (before anything is enqueued), kernel selection and launch.
+#include <string.h>
+
+#include "tm_internal.h"
+
+namespace {
+
+using titans::Shape;
+
+int build_shape(const titans_mem_desc* desc, Shape* s) {
+  if (!desc) return TM_ERR_INVALID;
+  if (desc->abi_version != TITANS_MEM_ABI_VERSION) return TM_ERR_INVALID;
+  if (desc->B <= 0 || desc->H <= 0 || desc->N < 0 || desc->d <= 0 || desc->n_layers <= 0)
+    return TM_ERR_INVALID;
+  if (desc->n_layers >= 2 && desc->hidden <= 0) return TM_ERR_INVALID;
+  if (desc->activation != TM_ACT_SILU) return TM_ERR_INVALID;
+  if (desc->io_dtype != TM_IO_F32 && desc->io_dtype != TM_IO_BF16) return TM_ERR_INVALID;
+  if (desc->read_mode != TM_READ_AFTER_WRITE && desc->read_mode != TM_READ_CHUNK_START)
+    return TM_ERR_INVALID;
+  if (desc->flags & ~TM_FLAG_FORCE_GENERIC) return TM_ERR_INVALID;
+  if (desc->n_layers > titans::kMaxLayers) return TM_ERR_UNSUPPORTED;
+  const int64_t streams = (int64_t)desc->B * desc->H;
+  if (streams > (int64_t)1 << 30) return TM_ERR_UNSUPPORTED;
+  s->streams = (int)streams;
+  s->N = desc->N;
+  s->d = desc->d;
+  s->hidden = desc->n_layers >= 2 ? desc->hidden : 0;
+  s->L = desc->n_layers;
+  s->io = desc->io_dtype;
+  s->read_mode = desc->read_mode;
+  s->widths[0] = desc->d;
+  for (int l = 1; l < s->L; ++l) s->widths[l] = desc->hidden;
+  s->widths[s->L] = desc->d;
+  s->P = 0;
+  s->maxw = 0;
+  for (int l = 0; l <= s->L; ++l)
+    if (s->widths[l] > s->maxw) s->maxw = s->widths[l];
+  for (int l = 1; l <= s->L; ++l) {
+    s->off[l] = s->P;
+    s->P += (int64_t)s->widths[l] * s->widths[l - 1];
+  }
+  return TM_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Range {
+  const char* lo;
+  int64_t bytes;
+  bool writes;
+};
+
+bool overlap(const Range& a, const Range& b) {
+  if (!a.lo || !b.lo || a.bytes <= 0 || b.bytes <= 0) return false;
+  return a.lo < b.lo + b.bytes && b.lo < a.lo + a.bytes;
+}
+
+int select_path(const titans_mem_desc* desc, const Shape& s, int chunk) {
+  if (chunk <= 0) return TM_ERR_INVALID;
+  if (!(desc->flags & TM_FLAG_FORCE_GENERIC) && titans::mlp2_supported(s, chunk))
+    return TM_PATH_MLP2_D64_H256;
+  if (chunk > titans::kMaxChunkGeneric || s.maxw > titans::kMaxWidthGeneric) return TM_ERR_UNSUPPORTED;
+  return TM_PATH_GENERIC_F32;
+}
+
+int64_t workspace_for(const Shape& s, int path, int chunk) {
+  if (path == TM_PATH_MLP2_D64_H256) return titans::mlp2_ws_bytes(s, chunk);
+  const int b = chunk < s.N ? chunk : (s.N > 0 ? s.N : 1);
+  return titans::generic_ws_floats_per_stream(s, b) * (int64_t)sizeof(float) * s.streams;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t titans_mem_abi_version(void) { return TITANS_MEM_ABI_VERSION; }
+
+int64_t titans_mem_param_count(const titans_mem_desc* desc) {
+  Shape s;
+  int rc = build_shape(desc, &s);
+  return rc ? rc : s.P;
+}
+
+int32_t titans_mem_select_path(const titans_mem_desc* desc, int32_t chunk) {
+  Shape s;
+  int rc = build_shape(desc, &s);
+  if (rc) return rc;
+  return select_path(desc, s, chunk);
+}
+
+int64_t titans_mem_workspace_bytes(const titans_mem_desc* desc, int32_t chunk) {
+  Shape s;
+  int rc = build_shape(desc, &s);
+  if (rc) return rc;
+  int path = select_path(desc, s, chunk);
+  if (path < 0) return path;
+  return workspace_for(s, path, chunk);
+}
+
+int titans_mem_forward(const titans_mem_desc* desc, const void* k, const void* v, const void* q,
+                       const float* alpha, const float* eta, const float* theta,
+                       const float* W_in, const float* S_in, int32_t chunk, void* y_out,
+                       float* W_out, float* S_out, void* workspace, int64_t workspace_bytes,
+                       void* stream) {
+  Shape s;
+  int rc = build_shape(desc, &s);
+  if (rc) return rc;
+  if (chunk <= 0) return TM_ERR_INVALID;
+  const bool has_tokens = s.N > 0;
+  const void* token_ptrs[] = {k, v, q, alpha, eta, theta, y_out};
+  for (const void* p : token_ptrs) {
+    if (has_tokens && !p) return TM_ERR_INVALID;
+    if (p && !aligned16(p)) return TM_ERR_INVALID;
+  }
+  const void* state_ptrs[] = {W_in, S_in, W_out, S_out};
+  for (const void* p : state_ptrs)
+    if (!p || !aligned16(p)) return TM_ERR_INVALID;
+  if (workspace && !aligned16(workspace)) return TM_ERR_INVALID;
+  int path = select_path(desc, s, chunk);
+  if (path < 0) return path;
+  const int64_t need = workspace_for(s, path, chunk);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return TM_ERR_WORKSPACE;
+
+  const int64_t esz = s.io == TM_IO_BF16 ? 2 : 4;
+  const int64_t tok_bytes = (int64_t)s.streams * s.N * s.d * esz;
+  const int64_t gate_bytes = (int64_t)s.streams * s.N * 4;
+  const int64_t state_bytes = (int64_t)s.streams * s.P * 4;
+  const Range ranges[] = {
+      {(const char*)k, tok_bytes, false},          {(const char*)v, tok_bytes, false},
+      {(const char*)q, tok_bytes, false},          {(const char*)alpha, gate_bytes, false},
+      {(const char*)eta, gate_bytes, false},       {(const char*)theta, gate_bytes, false},
+      {(const char*)W_in, state_bytes, false},     {(const char*)S_in, state_bytes, false},
+      {(const char*)y_out, tok_bytes, true},       {(const char*)W_out, state_bytes, true},
+      {(const char*)S_out, state_bytes, true},     {(const char*)workspace, need, true},
+  };
+  const int nr = sizeof(ranges) / sizeof(ranges[0]);
+  for (int i = 0; i < nr; ++i) {
+    for (int j = i + 1; j < nr; ++j) {
+      if (!ranges[i].writes && !ranges[j].writes) continue;
+      if (!overlap(ranges[i], ranges[j])) continue;
+      // exact in-place state update is the one allowed overlap
+      const bool w_inplace = i == 6 && j == 9 && (const void*)W_in == (const void*)W_out;
+      const bool s_inplace = i == 7 && j == 10 && (const void*)S_in == (const void*)S_out;
+      if (w_inplace || s_inplace) continue;
+      return TM_ERR_ALIAS;
+    }
+  }
+
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t err;
+  if (path == TM_PATH_MLP2_D64_H256)
+    err = titans::launch_mlp2(s, chunk, k, v, q, alpha, eta, theta, W_in, S_in, y_out, W_out, S_out,
+                          workspace, st);
+  else
+    err = titans::launch_generic(s, chunk, k, v, q, alpha, eta, theta, W_in, S_in, y_out, W_out,
+                             S_out, (float*)workspace, st);
+  return err == hipSuccess ? TM_OK : TM_ERR_HIP;
+}
+
+int titans_mem_retrieve(const titans_mem_desc* desc, const void* q, const float* W, void* y_out,
+                        void* stream) {
+  Shape s;
+  int rc = build_shape(desc, &s);
+  if (rc) return rc;
+  if (s.N > 0 && (!q || !y_out)) return TM_ERR_INVALID;
+  if (!W || !aligned16(W) || (q && !aligned16(q)) || (y_out && !aligned16(y_out)))
+    return TM_ERR_INVALID;
+  if (s.maxw > titans::kMaxWidthRetrieve) return TM_ERR_UNSUPPORTED;
+  const int64_t esz = s.io == TM_IO_BF16 ? 2 : 4;
+  const int64_t tok_bytes = (int64_t)s.streams * s.N * s.d * esz;
+  const Range yr = {(const char*)y_out, tok_bytes, true};
+  if (overlap(yr, Range{(const char*)q, tok_bytes, false}) ||
+      overlap(yr, Range{(const char*)W, (int64_t)s.streams * s.P * 4, false}))
+    return TM_ERR_ALIAS;
+  if (s.N == 0) return TM_OK;
+  hipError_t err = titans::launch_retrieve_generic(s, q, W, y_out, (hipStream_t)stream);
+  return err == hipSuccess ? TM_OK : TM_ERR_HIP;
+}
+
+const char* titans_mem_status_string(int status) {
+  switch (status) {
+    case TM_OK: return "ok";
+    case TM_ERR_INVALID: return "invalid argument";
+    case TM_ERR_UNSUPPORTED: return "unsupported shape, dtype or flag combination";
+    case TM_ERR_WORKSPACE: return "workspace too small";
+    case TM_ERR_ALIAS: return "illegal buffer overlap";
+    case TM_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// Internal declarations shared by the host layer and the kernel files of
+// libtitans_mem.so.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "titans_mem.h"
+
+namespace titans {
+
+constexpr int kMaxLayers = 8;        // generic path
+constexpr int kMaxChunkGeneric = 4096;
+constexpr int kMaxWidthGeneric = 8192;
+constexpr int kRetrieveTile = 8;     // tokens per block in titans_mem_retrieve
+constexpr int kMaxWidthRetrieve = 1024;
+
+struct Shape {
+  int streams, N, d, hidden, L, io, read_mode;
+  int widths[kMaxLayers + 1];
+  int64_t off[kMaxLayers + 1];
+  int64_t P;
+  int maxw;
+};
+
+// Workspace floats per stream of the generic kernel for chunk b.
+int64_t generic_ws_floats_per_stream(const Shape& s, int b);
+
+hipError_t launch_generic(const Shape& s, int chunk, const void* k, const void* v, const void* q,
+                          const float* alpha, const float* eta, const float* theta,
+                          const float* W_in, const float* S_in, void* y, float* W_out,
+                          float* S_out, float* ws, hipStream_t stream);
+
+hipError_t launch_retrieve_generic(const Shape& s, const void* q, const float* W, void* y,
+                                   hipStream_t stream);
+
+// Specialised 2-layer d=64 hidden=256 MFMA kernel (chunk <= 64, bf16 io).
+bool mlp2_supported(const Shape& s, int chunk);
+int64_t mlp2_ws_bytes(const Shape& s, int chunk);
+hipError_t launch_mlp2(const Shape& s, int chunk, const void* k, const void* v, const void* q,
+                       const float* alpha, const float* eta, const float* theta,
+                       const float* W_in, const float* S_in, void* y, float* W_out,
+                       float* S_out, void* ws, hipStream_t stream);
+
+}  // namespace titans

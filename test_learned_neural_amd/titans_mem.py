@@ -1,0 +1,196 @@
+"""ctypes binding of libtitans_mem.so (include/titans_mem.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, outputs/workspace are allocated with torch when the caller does
+not pass them, and the C entry points run on torch's current HIP stream.
+Every step of the memory's computation happens in the library's kernels;
+there is no Python or CPU fallback -- a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+ABI_VERSION = 1
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_ALIAS, ERR_HIP = 0, -1, -2, -3, -4, -5
+IO_F32, IO_BF16 = 0, 1
+ACT_SILU = 0
+READ_AFTER_WRITE, READ_CHUNK_START = 0, 1
+FLAG_FORCE_GENERIC = 1
+PATH_GENERIC_F32, PATH_MLP2_D64_H256 = 0, 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtitans_mem.so")
+
+EXPORTS = ("titans_mem_abi_version", "titans_mem_param_count", "titans_mem_select_path",
+           "titans_mem_workspace_bytes", "titans_mem_forward", "titans_mem_retrieve",
+           "titans_mem_status_string")
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("B", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("d", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("n_layers", ctypes.c_int32), ("activation", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("read_mode", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
+
+
+def make_desc(B: int, H: int, N: int, d: int, hidden: int, n_layers: int, io: str = "bf16",
+              read_mode: int = READ_AFTER_WRITE, flags: int = 0) -> Desc:
+    return Desc(ABI_VERSION, B, H, N, d, hidden if n_layers >= 2 else 0, n_layers, ACT_SILU,
+                IO_BF16 if io == "bf16" else IO_F32, read_mode, flags)
+
+
+_lib = None
+
+
+class TitansMemError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+def load():
+    """Load the library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m test_learned_neural_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, fp, i32, i64 = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    dp = ctypes.POINTER(Desc)
+    lib.titans_mem_abi_version.restype = i32
+    lib.titans_mem_abi_version.argtypes = []
+    lib.titans_mem_param_count.restype = i64
+    lib.titans_mem_param_count.argtypes = [dp]
+    lib.titans_mem_select_path.restype = i32
+    lib.titans_mem_select_path.argtypes = [dp, i32]
+    lib.titans_mem_workspace_bytes.restype = i64
+    lib.titans_mem_workspace_bytes.argtypes = [dp, i32]
+    lib.titans_mem_forward.restype = ctypes.c_int
+    lib.titans_mem_forward.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, i32, vp, fp, fp, vp, i64, vp]
+    lib.titans_mem_retrieve.restype = ctypes.c_int
+    lib.titans_mem_retrieve.argtypes = [dp, vp, fp, vp, vp]
+    lib.titans_mem_status_string.restype = ctypes.c_char_p
+    lib.titans_mem_status_string.argtypes = [ctypes.c_int]
+    if lib.titans_mem_abi_version() != ABI_VERSION:
+        raise ImportError("libtitans_mem.so ABI version mismatch")
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().titans_mem_status_string(int(status)).decode()
+
+
+def param_count(desc: Desc) -> int:
+    return int(load().titans_mem_param_count(ctypes.byref(desc)))
+
+
+def select_path(desc: Desc, chunk: int) -> int:
+    return int(load().titans_mem_select_path(ctypes.byref(desc), int(chunk)))
+
+
+def workspace_bytes(desc: Desc, chunk: int) -> int:
+    return int(load().titans_mem_workspace_bytes(ctypes.byref(desc), int(chunk)))
+
+
+def raw_forward(desc: Desc, k, v, q, alpha, eta, theta, W_in, S_in, chunk, y_out, W_out, S_out,
+                workspace, workspace_bytes_, stream) -> int:
+    """Direct call with integer device addresses (0 for NULL); returns the status."""
+    return int(load().titans_mem_forward(ctypes.byref(desc), k, v, q, alpha, eta, theta, W_in, S_in,
+                                         int(chunk), y_out, W_out, S_out, workspace,
+                                         int(workspace_bytes_), stream))
+
+
+# ----------------------------------------------------------------------------
+# torch-facing wrappers
+# ----------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _check(t, name, shape, dtype, device):
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def forward(k, v, q, alpha, eta, theta, W_in, S_in, chunk: int, *, hidden: int, n_layers: int,
+            read_mode: int = READ_AFTER_WRITE, force_generic: bool = False,
+            y_out=None, W_out=None, S_out=None, workspace=None) -> Tuple:
+    """Run titans_mem_forward on torch tensors.
+
+    k, v, q: [B, H, N, d] (float32 or bfloat16); alpha, eta, theta: [B, H, N]
+    float32; W_in, S_in: [B, H, P] float32.  Returns (y, W_out, S_out).
+    """
+    torch = _torch()
+    B, H, N, d = k.shape
+    io = "bf16" if k.dtype == torch.bfloat16 else "f32"
+    desc = make_desc(B, H, N, d, hidden, n_layers, io, read_mode,
+                     FLAG_FORCE_GENERIC if force_generic else 0)
+    P = param_count(desc)
+    if P < 0:
+        raise TitansMemError(P, "titans_mem_param_count")
+    dev = k.device
+    for name, t in (("k", k), ("v", v), ("q", q)):
+        _check(t, name, (B, H, N, d), k.dtype, dev)
+    for name, t in (("alpha", alpha), ("eta", eta), ("theta", theta)):
+        _check(t, name, (B, H, N), torch.float32, dev)
+    for name, t in (("W_in", W_in), ("S_in", S_in)):
+        _check(t, name, (B, H, P), torch.float32, dev)
+    if y_out is None:
+        y_out = torch.empty((B, H, N, d), dtype=k.dtype, device=dev)
+    if W_out is None:
+        W_out = torch.empty((B, H, P), dtype=torch.float32, device=dev)
+    if S_out is None:
+        S_out = torch.empty((B, H, P), dtype=torch.float32, device=dev)
+    _check(y_out, "y_out", (B, H, N, d), k.dtype, dev)
+    _check(W_out, "W_out", (B, H, P), torch.float32, dev)
+    _check(S_out, "S_out", (B, H, P), torch.float32, dev)
+    need = workspace_bytes(desc, chunk)
+    if need < 0:
+        raise TitansMemError(need, "titans_mem_workspace_bytes")
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = raw_forward(desc, _ptr(k), _ptr(v), _ptr(q), _ptr(alpha), _ptr(eta), _ptr(theta),
+                     _ptr(W_in), _ptr(S_in), chunk, _ptr(y_out), _ptr(W_out), _ptr(S_out),
+                     _ptr(workspace), ws_bytes, stream)
+    if rc != OK:
+        raise TitansMemError(rc, "titans_mem_forward")
+    return y_out, W_out, S_out
+
+
+def retrieve(q, W, *, hidden: int, n_layers: int, y_out=None):
+    """y = M*_W(q) at a fixed state.  q: [B,H,N,d]; W: [B,H,P] float32."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    io = "bf16" if q.dtype == torch.bfloat16 else "f32"
+    desc = make_desc(B, H, N, d, hidden, n_layers, io)
+    P = param_count(desc)
+    if P < 0:
+        raise TitansMemError(P, "titans_mem_param_count")
+    _check(q, "q", (B, H, N, d), q.dtype, q.device)
+    _check(W, "W", (B, H, P), torch.float32, q.device)
+    if y_out is None:
+        y_out = torch.empty_like(q)
+    _check(y_out, "y_out", (B, H, N, d), q.dtype, q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = int(load().titans_mem_retrieve(ctypes.byref(desc), _ptr(q), _ptr(W), _ptr(y_out), stream))
+    if rc != OK:
+        raise TitansMemError(rc, "titans_mem_retrieve")
+    return y_out

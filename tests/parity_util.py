@@ -1,0 +1,111 @@
+"""Shared helpers for the GPU parity tests: input staging and the error norm.
+
+Error criterion (per stream, max over streams):
+    e(X) = ||X_gpu - X_ref||_F / max(||X_ref||_F, floor_X)
+with floor_W = floor_S = 1e-30 * max(1, ||W_in||_F) and
+floor_y = 1e-30 * max(1, ||v||_F).  The floor only matters once the
+memory has decayed towards the W = 0 fixed point (the bias-free MLP's
+state underflows fp32 late in the long workloads); a non-finite GPU value
+where the reference is finite always fails.  Limits: 1e-3 for fp32 io,
+2e-2 for bf16 io.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from test_learned_neural_amd import workloads as wl
+
+TOL = {"f32": 1e-3, "bf16": 2e-2}
+
+
+def to_device(cfg, inp, n_streams_shape=None, device="cuda"):
+    """numpy inputs -> torch device tensors shaped [B, H, N, ...]."""
+    import torch
+    S, N = inp["alpha"].shape
+    B, H = n_streams_shape if n_streams_shape else (cfg.B, cfg.H)
+    assert B * H == S
+
+    def tok(a):
+        if cfg.io == "bf16":
+            t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(a)
+        return t.reshape(B, H, N, cfg.d).to(device)
+
+    def per(a, last):
+        return torch.from_numpy(np.ascontiguousarray(a)).reshape(B, H, last).to(device)
+
+    return dict(k=tok(inp["k"]), v=tok(inp["v"]), q=tok(inp["q"]),
+                alpha=per(inp["alpha"], N), eta=per(inp["eta"], N), theta=per(inp["theta"], N),
+                W0=per(inp["W0"], cfg.param_count), S0=per(inp["S0"], cfg.param_count))
+
+
+def y_to_f64(cfg, y):
+    """torch y [B,H,N,d] (io dtype) -> float64 numpy [S, N, d]."""
+    import torch
+    if y.dtype == torch.bfloat16:
+        y = y.float()
+    a = y.detach().cpu().numpy().astype(np.float64)
+    return a.reshape(-1, a.shape[-2], a.shape[-1])
+
+
+def run_gpu(cfg, dev, chunk=None, **kw):
+    from test_learned_neural_amd import titans_mem as tmm
+    return tmm.forward(dev["k"], dev["v"], dev["q"], dev["alpha"], dev["eta"], dev["theta"],
+                       dev["W0"], dev["S0"], cfg.chunk if chunk is None else chunk,
+                       hidden=cfg.hidden, n_layers=cfg.n_layers, **kw)
+
+
+def run_oracle(cfg, inp, chunk=None, read_mode=0, threads=0):
+    import oracle
+    f = wl.inputs_f64(cfg, inp)
+    return oracle.forward(f["k"], f["v"], f["q"], f["alpha"], f["eta"], f["theta"], f["W0"], f["S0"],
+                          d=cfg.d, hidden=cfg.hidden, n_layers=cfg.n_layers,
+                          chunk=cfg.chunk if chunk is None else chunk, read_mode=read_mode,
+                          threads=threads)
+
+
+def rel_err(x, ref, floor):
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if not np.all(np.isfinite(x[np.isfinite(ref)])):
+        return np.inf
+    return float(np.linalg.norm(x - ref) / max(np.linalg.norm(ref), floor))
+
+
+def stream_errors(cfg, inp, y_gpu, W_gpu, S_gpu, y_ref, W_ref, S_ref, idx=None):
+    """Per-stream (e_y, e_W, e_S); idx maps rows of the refs to GPU streams."""
+    idx = list(range(len(y_ref))) if idx is None else list(idx)
+    vin = wl.io_to_f64(inp["v"], cfg.io)
+    out = []
+    for r, s in enumerate(idx):
+        fw = 1e-30 * max(1.0, float(np.linalg.norm(inp["W0"][r].astype(np.float64))))
+        fy = 1e-30 * max(1.0, float(np.linalg.norm(vin[r])))
+        out.append((rel_err(y_gpu[s], y_ref[r], fy), rel_err(W_gpu[s], W_ref[r], fw),
+                    rel_err(S_gpu[s], S_ref[r], fw)))
+    return np.array(out)
+
+
+def window_errors(cfg, inp, y_gpu, y_ref, idx=None, windows=8):
+    """Relative y error per window of the sequence, for windows whose
+    reference norm is above the floor; returns the max (0 if none)."""
+    idx = list(range(len(y_ref))) if idx is None else list(idx)
+    vin = wl.io_to_f64(inp["v"], cfg.io)
+    worst = 0.0
+    N = y_ref.shape[1]
+    bounds = np.linspace(0, N, windows + 1).astype(int)
+    for r, s in enumerate(idx):
+        for a, b in zip(bounds[:-1], bounds[1:]):
+            if b <= a:
+                continue
+            fy = 1e-30 * max(1.0, float(np.linalg.norm(vin[r, a:b])))
+            if np.linalg.norm(y_ref[r, a:b]) < fy:
+                continue
+            worst = max(worst, rel_err(y_gpu[s, a:b], y_ref[r, a:b], fy))
+    return worst
+
+
+def live_length(w_norm_traj, chunk, floor):
+    """Last token at which the reference ||W_t||_F stays above the floor."""
+    alive = np.nonzero(w_norm_traj > floor)[0]
+    return 0 if len(alive) == 0 else int((alive[-1] + 1) * chunk)

@@ -1,0 +1,164 @@
+"""Host-only checks of the C ABI (no GPU needed).
+
+Every error path of titans_mem_forward / titans_mem_retrieve is detected on
+the host before anything is enqueued, so each case below passes fake
+(aligned, never dereferenced) device addresses with exactly one defect.
+"""
+import re
+
+import pytest
+
+from test_learned_neural_amd import titans_mem as tmm
+
+HEADER = __import__("os").path.join(__import__("os").path.dirname(__file__), "..", "include", "titans_mem.h")
+
+BASE = 0x7f0000000000  # fake device addresses: never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tmm.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(titans_mem_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert names == sorted(tmm.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.titans_mem_abi_version() == tmm.ABI_VERSION
+
+
+def test_param_count_and_paths(lib):
+    d3 = tmm.make_desc(8, 16, 16384, 64, 256, 2, "bf16")
+    assert tmm.param_count(d3) == 2 * 64 * 256
+    d5 = tmm.make_desc(4, 8, 32768, 128, 512, 4, "bf16")
+    assert tmm.param_count(d5) == 128 * 512 + 2 * 512 * 512 + 512 * 128
+    d1 = tmm.make_desc(1, 1, 1024, 64, 0, 1, "f32")
+    assert tmm.param_count(d1) == 64 * 64
+    assert tmm.select_path(d1, 16) == tmm.PATH_GENERIC_F32
+    assert tmm.select_path(d5, 128) == tmm.PATH_GENERIC_F32
+    assert tmm.select_path(d3, 0) == tmm.ERR_INVALID
+    forced = tmm.make_desc(8, 16, 16384, 64, 256, 2, "bf16", flags=tmm.FLAG_FORCE_GENERIC)
+    assert tmm.select_path(forced, 64) == tmm.PATH_GENERIC_F32
+    assert tmm.workspace_bytes(d1, 16) > 0
+
+
+@pytest.mark.parametrize("field,value", [("abi_version", 2), ("B", 0), ("H", -1), ("N", -1), ("d", 0),
+                                         ("n_layers", 0), ("activation", 3), ("io_dtype", 7),
+                                         ("read_mode", 5), ("flags", 0x80)])
+def test_invalid_descriptor(lib, field, value):
+    d = tmm.make_desc(2, 2, 64, 16, 32, 2, "f32")
+    setattr(d, field, value)
+    assert tmm.param_count(d) == tmm.ERR_INVALID
+    assert tmm.select_path(d, 16) == tmm.ERR_INVALID
+    assert tmm.workspace_bytes(d, 16) == tmm.ERR_INVALID
+
+
+def test_hidden_required_for_mlp(lib):
+    d = tmm.make_desc(1, 1, 8, 16, 32, 2, "f32")
+    d.hidden = 0
+    assert tmm.param_count(d) == tmm.ERR_INVALID
+    d = tmm.make_desc(1, 1, 8, 16, 0, 1, "f32")
+    assert tmm.param_count(d) == 256  # hidden ignored for the matrix memory
+
+
+def test_too_many_layers_is_unsupported(lib):
+    d = tmm.make_desc(1, 1, 8, 16, 32, 9, "f32")
+    assert tmm.param_count(d) == tmm.ERR_UNSUPPORTED
+
+
+class Buffers:
+    """Disjoint fake device ranges laid out for one descriptor."""
+
+    def __init__(self, desc, chunk):
+        esz = 2 if desc.io_dtype == tmm.IO_BF16 else 4
+        S = desc.B * desc.H
+        P = tmm.param_count(desc)
+        sizes = dict(k=S * desc.N * desc.d * esz, v=S * desc.N * desc.d * esz, q=S * desc.N * desc.d * esz,
+                     alpha=S * desc.N * 4, eta=S * desc.N * 4, theta=S * desc.N * 4,
+                     W_in=S * P * 4, S_in=S * P * 4, y=S * desc.N * desc.d * esz, W_out=S * P * 4,
+                     S_out=S * P * 4, ws=max(tmm.workspace_bytes(desc, chunk), 16))
+        self.ptr = {}
+        cur = BASE
+        for name, n in sizes.items():
+            self.ptr[name] = cur
+            cur += (n + 4095) // 4096 * 4096 + 4096
+        self.ws_bytes = tmm.workspace_bytes(desc, chunk)
+
+    def call(self, desc, chunk, **over):
+        p = dict(self.ptr)
+        ws_bytes = over.pop("ws_bytes", self.ws_bytes)
+        p.update(over)
+        return tmm.raw_forward(desc, p["k"], p["v"], p["q"], p["alpha"], p["eta"], p["theta"],
+                               p["W_in"], p["S_in"], chunk, p["y"], p["W_out"], p["S_out"], p["ws"],
+                               ws_bytes, 0)
+
+
+@pytest.fixture
+def setup(lib):
+    desc = tmm.make_desc(2, 3, 100, 16, 32, 2, "f32")
+    return desc, Buffers(desc, 8)
+
+
+@pytest.mark.parametrize("name", ["k", "v", "q", "alpha", "eta", "theta", "W_in", "S_in", "y", "W_out", "S_out"])
+def test_null_pointer(setup, name):
+    desc, b = setup
+    assert b.call(desc, 8, **{name: 0}) == tmm.ERR_INVALID
+
+
+@pytest.mark.parametrize("name", ["k", "alpha", "W_in", "y", "W_out", "ws"])
+def test_misaligned_pointer(setup, name):
+    desc, b = setup
+    assert b.call(desc, 8, **{name: b.ptr[name] + 4}) == tmm.ERR_INVALID
+
+
+def test_chunk_must_be_positive(setup):
+    desc, b = setup
+    assert b.call(desc, 0) == tmm.ERR_INVALID
+    assert b.call(desc, -3) == tmm.ERR_INVALID
+
+
+def test_workspace_too_small(setup):
+    desc, b = setup
+    assert b.call(desc, 8, ws_bytes=b.ws_bytes - 16) == tmm.ERR_WORKSPACE
+    assert b.call(desc, 8, ws=0, ws_bytes=0) == tmm.ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("a,b_,shift", [("y", "k", 0), ("W_out", "S_in", 0), ("W_out", "W_in", 16),
+                                        ("S_out", "W_out", 0), ("ws", "y", 64), ("y", "alpha", 32),
+                                        ("S_out", "S_in", 16)])
+def test_illegal_aliasing(setup, a, b_, shift):
+    desc, b = setup
+    assert b.call(desc, 8, **{a: b.ptr[b_] + shift}) == tmm.ERR_ALIAS
+
+
+def test_empty_sequence_allows_null_token_buffers(lib):
+    desc = tmm.make_desc(1, 2, 0, 16, 32, 2, "bf16")
+    P = tmm.param_count(desc)
+    # a misaligned state pointer still fails: the only defect, detected before launch
+    rc = tmm.raw_forward(desc, 0, 0, 0, 0, 0, 0, BASE + 4, BASE + 8192, 4, 0, BASE + 2 * 8192,
+                         BASE + 3 * 8192, 0, 0, 0)
+    assert rc == tmm.ERR_INVALID
+    assert P == 2 * 16 * 32
+
+
+def test_retrieve_validation(lib):
+    import ctypes
+    desc = tmm.make_desc(1, 2, 10, 16, 32, 2, "f32")
+    f = lib.titans_mem_retrieve
+    assert f(ctypes.byref(desc), BASE, 0, BASE + 8192, 0) == tmm.ERR_INVALID
+    assert f(ctypes.byref(desc), 0, BASE + 8192, BASE + 16384, 0) == tmm.ERR_INVALID
+    assert f(ctypes.byref(desc), BASE, BASE + 65536, BASE + 64, 0) == tmm.ERR_ALIAS
+    wide = tmm.make_desc(1, 1, 10, 16, 2048, 2, "f32")
+    assert f(ctypes.byref(wide), BASE, BASE + (1 << 24), BASE + (2 << 24), 0) == tmm.ERR_UNSUPPORTED
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5, 17):
+        assert isinstance(tmm.status_string(code), str) and tmm.status_string(code)

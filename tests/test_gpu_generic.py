@@ -1,0 +1,145 @@
+"""GPU parity of the shape-generic fp32 kernel against the fp64 oracle.
+
+Forced onto the generic path (TM_FLAG_FORCE_GENERIC) so that it is checked
+even for shapes that also have a specialised kernel.  fp32 arithmetic, so
+the bar is the fp32-io tolerance (1e-3) on every case.
+"""
+import numpy as np
+import pytest
+
+from test_learned_neural_amd import workloads as wl
+from parity_util import (TOL, rel_err, run_gpu, run_oracle, stream_errors, to_device, window_errors,
+                         y_to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    return torch
+
+
+def _check(cfg, inp, out, ref, tol, idx=None, windows=True):
+    """y is held to its io dtype's bar (bf16 output rounding alone is ~2e-3);
+    W and S, fp32 end to end on this path, to ``tol``."""
+    y, W, S = out
+    tol_y = max(tol, TOL[cfg.io])
+    yg = y_to_f64(cfg, y)
+    Wg = W.reshape(-1, cfg.param_count).cpu().double().numpy()
+    Sg = S.reshape(-1, cfg.param_count).cpu().double().numpy()
+    e = stream_errors(cfg, inp, yg, Wg, Sg, *ref, idx=idx)
+    print(f"{cfg.name}: max e_y {e[:, 0].max():.2e} e_W {e[:, 1].max():.2e} e_S {e[:, 2].max():.2e}", flush=True)
+    assert np.all(e[:, 0] < tol_y) and np.all(e[:, 1:] < tol), e.max(axis=0)
+    if windows:
+        we = window_errors(cfg, inp, yg, ref[0], idx=idx)
+        assert we < tol_y, we
+
+
+def test_generic_linear_config1_full():
+    cfg = wl.CONFIGS[1]
+    inp = wl.make_inputs(cfg)
+    out = run_gpu(cfg, to_device(cfg, inp), force_generic=True)
+    _check(cfg, inp, out, run_oracle(cfg, inp), TOL["f32"])
+
+
+@pytest.mark.parametrize("cfg_i,n_tokens,BH", [(2, 640, (2, 3)), (3, 300, (1, 5)), (5, 300, (1, 3))])
+def test_generic_mlp_prefix(cfg_i, n_tokens, BH):
+    cfg = wl.CONFIGS[cfg_i].with_(B=BH[0], H=BH[1], N=n_tokens)
+    inp = wl.make_inputs(cfg)
+    out = run_gpu(cfg, to_device(cfg, inp), force_generic=True)
+    _check(cfg, inp, out, run_oracle(cfg, inp), TOL["f32"])
+
+
+@pytest.mark.parametrize("L,d,h,N,chunk,io", [(1, 16, 0, 77, 5, "f32"), (2, 16, 48, 130, 64, "f32"),
+                                              (3, 24, 40, 97, 16, "bf16"), (2, 32, 96, 65, 1, "bf16"),
+                                              (2, 64, 256, 50, 64, "bf16"), (4, 8, 20, 33, 200, "f32")])
+def test_generic_shapes_and_ragged_chunks(L, d, h, N, chunk, io):
+    cfg = wl.CONFIGS[2].with_(B=1, H=2, N=N, d=d, hidden=h, n_layers=L, chunk=chunk, io=io)
+    inp = wl.make_inputs(cfg)
+    out = run_gpu(cfg, to_device(cfg, inp), force_generic=True)
+    _check(cfg, inp, out, run_oracle(cfg, inp), TOL["f32"], windows=False)
+
+
+def test_generic_read_chunk_start():
+    cfg = wl.CONFIGS[2].with_(B=1, H=3, N=200)
+    inp = wl.make_inputs(cfg)
+    out = run_gpu(cfg, to_device(cfg, inp), force_generic=True, read_mode=1)
+    _check(cfg, inp, out, run_oracle(cfg, inp, read_mode=1), TOL["f32"])
+
+
+def test_retrieve_matches_memory_forward():
+    import oracle
+    from test_learned_neural_amd import titans_mem as tmm
+    import torch
+    for L, d, h in ((1, 64, 0), (2, 64, 256), (4, 128, 512), (3, 20, 36)):
+        cfg = wl.CONFIGS[2].with_(B=2, H=2, N=37, d=d, hidden=h, n_layers=L, io="bf16")
+        inp = wl.make_inputs(cfg)
+        dev = to_device(cfg, inp)
+        W = dev["W0"] * 3.0
+        y = tmm.retrieve(dev["q"], W, hidden=h, n_layers=L)
+        yg = y_to_f64(cfg, y)
+        q64 = wl.io_to_f64(inp["q"], "bf16")
+        W64 = W.reshape(-1, cfg.param_count).cpu().double().numpy()
+        for s in range(4):
+            ref = np.stack([oracle.memory_apply(W64[s], q64[s, t], d, h, L) for t in range(cfg.N)])
+            assert rel_err(yg[s], ref, 1e-30) < 2e-2
+        torch.cuda.synchronize()
+
+
+def test_generic_empty_inplace_and_deterministic():
+    import torch
+    cfg = wl.CONFIGS[2].with_(B=1, H=2, N=0)
+    inp = wl.make_inputs(cfg)
+    dev = to_device(cfg, inp)
+    y, W, S = run_gpu(cfg, dev, force_generic=True)
+    assert torch.equal(W, dev["W0"]) and torch.equal(S, dev["S0"])
+    cfg = wl.CONFIGS[2].with_(B=1, H=2, N=150)
+    inp = wl.make_inputs(cfg)
+    dev = to_device(cfg, inp)
+    y1, W1, S1 = run_gpu(cfg, dev, force_generic=True)
+    y2, W2, S2 = run_gpu(cfg, dev, force_generic=True)
+    assert torch.equal(y1, y2) and torch.equal(W1, W2) and torch.equal(S1, S2)
+    Wi, Si = dev["W0"].clone(), dev["S0"].clone()
+    y3, W3, S3 = run_gpu(cfg, dev | {"W0": Wi, "S0": Si}, force_generic=True, W_out=Wi, S_out=Si)
+    assert W3.data_ptr() == Wi.data_ptr()
+    assert torch.equal(y3, y1) and torch.equal(W3, W1) and torch.equal(S3, S1)
+
+
+def test_generic_split_resume():
+    import torch
+    cfg = wl.CONFIGS[2].with_(B=1, H=2, N=256)
+    inp = wl.make_inputs(cfg)
+    dev = to_device(cfg, inp)
+    y, W, S = run_gpu(cfg, dev, force_generic=True)
+    cut = 128
+    first = {k: (v[:, :, :cut].contiguous() if k in ("k", "v", "q", "alpha", "eta", "theta") else v)
+             for k, v in dev.items()}
+    ya, Wa, Sa = run_gpu(cfg, first, force_generic=True)
+    second = {k: (v[:, :, cut:].contiguous() if k in ("k", "v", "q", "alpha", "eta", "theta") else v)
+              for k, v in dev.items()}
+    second["W0"], second["S0"] = Wa, Sa
+    yb, Wb, Sb = run_gpu(cfg, second, force_generic=True)
+    assert torch.equal(torch.cat([ya, yb], dim=2), y)
+    assert torch.equal(Wb, W) and torch.equal(Sb, S)
+
+
+def test_generic_gate_edge_cases():
+    import torch
+    cfg = wl.CONFIGS[2].with_(B=1, H=2, N=130)
+    inp = wl.make_inputs(cfg)
+    dev = to_device(cfg, inp)
+    # theta = 0: surprise stays zero, W decays by the product of (1 - alpha)
+    dz = dev | {"theta": torch.zeros_like(dev["theta"])}
+    y, W, S = run_gpu(cfg, dz, force_generic=True)
+    assert not S.any()
+    decay = torch.prod(1 - dev["alpha"].double(), dim=-1, keepdim=True)
+    assert torch.allclose(W.double(), decay * dev["W0"].double(), rtol=1e-5, atol=0)
+    # alpha = 1: the old memory is erased at every token, so W == S (up to the
+    # rounding of A_n W_0 + F_n S_0 - G versus E_n S_0 - G with A_n = 0, F_n = E_n)
+    d1 = dev | {"alpha": torch.ones_like(dev["alpha"])}
+    y, W, S = run_gpu(cfg, d1, force_generic=True)
+    # (norm-wise: single entries can cancel, E_n S_0 ~ G)
+    rel = (torch.linalg.norm(W.double() - S.double()) / torch.linalg.norm(S.double())).item()
+    assert rel < 1e-6, rel
