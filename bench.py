@@ -1,0 +1,184 @@
+#!/usr/bin/env python3
+"""Throughput of the Titans memory hot path (chunked update + retrieval) on one GPU.
+
+One step = one titans_mem_forward call over the whole workload (every
+stream, every chunk: coefficient scan, key forward, backprop, masked
+retrieval, state fold).  Inputs are synthetic (seeded generator), resident
+in HBM before the timed region; outputs are preallocated.
+
+Prints ONE JSON line: memory tokens/s (B*H*N per step time), the roofline
+of the dominant kernel measured with HIP events on the launch stream, and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks (dense)
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+
+
+def algorithmic_work(cfg):
+    """(FLOPs, HBM bytes) per memory token (one token of one stream) of the
+    chunked method: key forward P, backprop P - d*n_1, two weighted
+    reductions 2P, and retrieval 2P + b * sum(n_{l-1} + n_l) MACs; bytes
+    are k, v, q, y, the three gates, and the state read/written once."""
+    w = cfg.widths
+    P = cfg.param_count
+    b = cfg.chunk
+    upd = 4 * P - w[0] * w[1]
+    ret = 2 * P + b * sum(w[i] + w[i + 1] for i in range(cfg.n_layers))
+    flops = 2 * (upd + ret)
+    esz = 2 if cfg.io == "bf16" else 4
+    byts = 4 * cfg.d * esz + 3 * 4 + 4 * P * 4 / cfg.N
+    return flops, byts
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=3, help="workload index (1-5)")
+    ap.add_argument("--force-generic", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the memory's (batch, head) streams are independent "
+              "and this build runs them on a single device; --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from test_learned_neural_amd import titans_mem as tmm
+    from test_learned_neural_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tmm.load()
+    cfg = wl.CONFIGS[args.config]
+    t0 = time.time()
+    inp = wl.make_inputs(cfg, workers=min(16, len(os.sched_getaffinity(0))))
+    print(f"[bench] generated {cfg.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    B, H, N, d, P = cfg.B, cfg.H, cfg.N, cfg.d, cfg.param_count
+
+    def tok(a):
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if cfg.io == "bf16" else torch.from_numpy(a)
+        return t.reshape(B, H, N, d).to(dev)
+
+    def per(a, n):
+        return torch.from_numpy(a).reshape(B, H, n).to(dev)
+
+    k, v, q = tok(inp["k"]), tok(inp["v"]), tok(inp["q"])
+    alpha, eta, theta = per(inp["alpha"], N), per(inp["eta"], N), per(inp["theta"], N)
+    W0, S0 = per(inp["W0"], P), per(inp["S0"], P)
+    y = torch.empty_like(k)
+    W_out = torch.empty_like(W0)
+    S_out = torch.empty_like(S0)
+    flags = tmm.FLAG_FORCE_GENERIC if args.force_generic else 0
+    desc = tmm.make_desc(B, H, N, d, cfg.hidden, cfg.n_layers, cfg.io, flags=flags)
+    path = tmm.select_path(desc, cfg.chunk)
+    ws_bytes = tmm.workspace_bytes(desc, cfg.chunk)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        rc = tmm.raw_forward(desc, k.data_ptr(), v.data_ptr(), q.data_ptr(), alpha.data_ptr(),
+                             eta.data_ptr(), theta.data_ptr(), W0.data_ptr(), S0.data_ptr(), cfg.chunk,
+                             y.data_ptr(), W_out.data_ptr(), S_out.data_ptr(), ws.data_ptr(), ws_bytes,
+                             stream.cuda_stream)
+        if rc != tmm.OK:
+            raise tmm.TitansMemError(rc, "titans_mem_forward")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = wall * 1e3 / args.steps
+    mem_tokens = B * H * N
+    value = mem_tokens / (ms_per_step / 1e3)
+    flops_tok, bytes_tok = algorithmic_work(cfg)
+    avg_launch_s = float(np.mean(launch_ms)) / 1e3
+    dtype = "f32" if path == tmm.PATH_GENERIC_F32 else "f16"
+    achieved = flops_tok * mem_tokens / avg_launch_s / 1e12
+    peak = PEAK_TFLOPS[dtype]
+    bound = "alu" if path == tmm.PATH_GENERIC_F32 else "mfma"
+    print(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step, event avg {np.mean(launch_ms):.3f} ms, "
+          f"min {np.min(launch_ms):.3f} ms; {achieved:.1f} TFLOP/s; HBM {bytes_tok * mem_tokens / avg_launch_s / 1e9:.0f} GB/s",
+          file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        f = wl.inputs_f64(cfg, {kk: vv for kk, vv in inp.items()})
+        done = 0
+        elapsed = 0.0
+        streams_total = B * H
+        batch = min(cores, streams_total)
+        while done < streams_total and elapsed < args.cpu_seconds:
+            sl = slice(done, min(done + batch, streams_total))
+            t1 = time.perf_counter()
+            oracle.forward(f["k"][sl], f["v"][sl], f["q"][sl], f["alpha"][sl], f["eta"][sl], f["theta"][sl],
+                           f["W0"][sl], f["S0"][sl], d=d, hidden=cfg.hidden, n_layers=cfg.n_layers,
+                           chunk=cfg.chunk, threads=batch)
+            elapsed += time.perf_counter() - t1
+            done = sl.stop
+        cpu = {"value": done * N / elapsed, "unit": "memory-tokens/s", "cores": batch, "kind": "oracle",
+               "sample": f"{done} of {streams_total} streams x {N} tokens, fp64 token-by-token, "
+                         f"{batch} OpenMP threads, {elapsed:.1f} s"}
+        print(f"[bench] cpu oracle: {cpu['value']:.3g} memory-tokens/s ({cpu['sample']})", file=sys.stderr,
+              flush=True)
+
+    out = {
+        "metric": "memory tokens/sec (retrieve + chunked update), 1 GPU",
+        "value": value,
+        "unit": "memory-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": B, "H": H, "N": N, "d": d, "hidden": cfg.hidden,
+                   "n_layers": cfg.n_layers, "chunk": cfg.chunk, "io": cfg.io,
+                   "kernel_path": {tmm.PATH_GENERIC_F32: "generic_f32",
+                                   tmm.PATH_MLP2_D64_H256: "mlp2_d64_h256_mfma"}.get(path, str(path)),
+                   "sequence_tokens_per_s": B * N / (ms_per_step / 1e3)},
+        "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None,
+                     "algorithmic_flops_per_launch": flops_tok * mem_tokens,
+                     "avg_launch_ms": avg_launch_s * 1e3,
+                     "hbm_achieved_gbs": bytes_tok * mem_tokens / avg_launch_s / 1e9,
+                     "hbm_peak_gbs": PEAK_HBM_GBS},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,15 +1,847 @@
-// Specialised MFMA kernel for the 2-layer d=64 hidden=256 memory (placeholder
-// until the kernel lands: reports the shape as unsupported).
+// Specialised MFMA kernel: 2-layer memory, d = 64, hidden = 256, chunk <= 64,
+// bf16 keys/values/queries/outputs, fp32 state and gates.
+//
+// Method ("Titans: Learning to Memorize at Test Time", mer.dev notes): the
+// chunked test-time update of section 3.2 (gradients of every token of a
+// chunk taken at the chunk-start weights), with the surprise momentum and
+// forgetting of section 3.1, and retrieval after each token's write.  Per
+// chunk of n tokens with chunk-start state (W_0, S_0):
+//
+//   a1  A_j = prod_{m<=j}(1-alpha_m), E_j = prod eta_m,
+//       F_j = (1-alpha_j) F_{j-1} + E_j, U_i = theta_i prod_{m>i} eta_m,
+//       D[j,i] = (1-alpha_j) D[j-1,i] + theta_i prod_{i<m<=j} eta_m (D[i,i] = theta_i)
+//   a2  Z1 = K W1_0^T, A1 = SiLU(Z1), O = A1 W2_0^T
+//   a3  Delta2 = O - V, Delta1 = (Delta2 W2_0) * SiLU'(Z1)
+//   a5  Zq1 = diag(A) Q W1_0^T + diag(F) Q S1_0^T - (D o Q K^T) Delta1, H1 = SiLU(Zq1)
+//       y   = diag(A) H1 W2_0^T + diag(F) H1 S2_0^T - (D o H1 A1^T) Delta2
+//   a4  W_l <- A_n W_l + F_n S_l - G_l(D[n-1,:]),  S_l <- E_n S_l - G_l(U)
+//       G_1(w) = sum_j w_j Delta1_j k_j^T,  G_2(w) = sum_j w_j Delta2_j a1_j^T
+//
+// MI355X mapping
+// --------------
+// * Each (batch, head) stream runs on a PAIR of workgroups (two CUs), one per
+//   half of the hidden layer; each workgroup is 4 waves (one per SIMD) and
+//   wave w owns 32 hidden units.  Everything per hidden unit (the state rows
+//   and columns, A1, Delta1, H1, the state update) is local to its wave.
+//   Only the two contractions over all 256 hidden units cross the pair: O
+//   (needed before the backprop: one exchange per chunk on the critical
+//   path) and y (exchanged one chunk late, riding on the next O exchange).
+//   With 128 streams this fills all 256 CUs, and it halves the state each
+//   CU must hold.
+// * The fp32 state of a wave (W1, S1, W2, S2 restricted to its 32 hidden
+//   units: 4 x 64 x 32 floats) lives in accumulation registers (AGPRs) for
+//   the whole sequence, in the accumulator layout of
+//   v_mfma_f32_32x32x16_f16: the update GEMMs land in that layout, and an
+//   accumulator tile (lane = column, registers = rows) feeds the next MFMA
+//   as an operand contracting over its rows, so the state is used as an
+//   MFMA operand without an LDS round trip (only W2 needs one transposed
+//   copy per chunk, for the backprop).
+// * Every MFMA operand is fp16 with a power-of-two scale per operand block
+//   and chunk (fp32 accumulation, exact rescaling).  bf16 operands lose
+//   about 1e-2 relative on the state; scaled fp16 keeps about 1e-3.
+// * The pair exchanges partial sums through global memory with agent-
+//   coherent (sc1) relaxed accesses: data stores, s_waitcnt vmcnt(0), then a
+//   sequence flag; the reader polls the flag with a bounded spin.  A pair
+//   whose partner never arrives gives up, writes NaN to its stream's state
+//   and records the failure in the workspace status word.  Sums are formed
+//   in a fixed order (half 0 + half 1), so results are bitwise reproducible
+//   and identical in both halves.
 #include "tm_internal.h"
 
-namespace titans {
+#include <hip/hip_bf16.h>
 
-bool mlp2_supported(const Shape&, int) { return false; }
-int64_t mlp2_ws_bytes(const Shape&, int) { return 0; }
-hipError_t launch_mlp2(const Shape&, int, const void*, const void*, const void*, const float*,
-                       const float*, const float*, const float*, const float*, void*, float*,
-                       float*, void*, hipStream_t) {
-  return hipErrorInvalidConfiguration;
+namespace titans {
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 64;
+constexpr int kH = 256;
+constexpr int kB = 64;           // token rows per chunk tile
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kHW = 32;          // hidden units per wave
+constexpr int kHC = kWaves * kHW;  // hidden units per workgroup (half of kH)
+constexpr int kP = 2 * kD * kH;
+constexpr int RS = 68;           // fp16 row stride (halves) of 64-wide tiles
+constexpr int RSA = 36;          // fp16 row stride of the 32-wide A1 copy
+constexpr int RSF = 68;          // fp32 row stride (floats)
+constexpr int kMaxPairs = 128;
+constexpr unsigned kSpinMax = 1u << 21;
+
+// ---- LDS layout (bytes) ----
+constexpr int kTileH = kB * RS * 2;                  // 64 x 68 fp16 = 8704
+constexpr int OFF_K = 0;
+constexpr int OFF_KT = OFF_K + kTileH;
+constexpr int OFF_Q = OFF_KT + kTileH;
+constexpr int OFF_D2 = OFF_Q + kTileH;
+constexpr int OFF_D2T = OFF_D2 + kTileH;
+constexpr int OFF_SC1 = OFF_D2T + kTileH;
+constexpr int OFF_DM = OFF_SC1 + kTileH;             // fp32 [64][68]
+constexpr int OFF_COEF = OFF_DM + kB * RSF * 4;
+constexpr int COEF_ALPHA = 0, COEF_ETA = 64, COEF_THETA = 128, COEF_A = 192, COEF_E = 256,
+              COEF_F = 320, COEF_U = 384, COEF_DN = 448;            // float index
+constexpr int COEF_H16 = 512 * 4;                                   // byte offset of fp16 arrays
+constexpr int H16_WU = 128, H16_WD = 192;                           // half index
+constexpr int COEF_INT = COEF_H16 + 256 * 2;                        // byte offset of int slots
+constexpr int kCoefBytes = COEF_INT + 16 * 4;
+constexpr int OFF_WAVE = (OFF_COEF + kCoefBytes + 255) / 256 * 256;
+// per-wave region: [A1 copy 64 x RSA fp16][W2 copy 32 x RS fp16 | O half-partial 32 x RSF fp32];
+// later the whole region holds the wave's y^T partial (64 x RSF fp32)
+constexpr int kA1Bytes = kB * RSA * 2;               // 4608
+constexpr int kWaveRegion = kD * RSF * 4;            // 17408
+constexpr int kLdsBytes = OFF_WAVE + kWaves * kWaveRegion;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+static_assert(kA1Bytes + 32 * RSF * 4 <= kWaveRegion, "A1 copy + O half-partial");
+static_assert(kA1Bytes + kHW * RS * 2 <= kWaveRegion, "A1 copy + W2 copy");
+
+constexpr int INT_AMAX_SC1 = 0, INT_AMAX_D2 = 1, INT_EWU = 2, INT_EWD = 3, INT_FAIL = 4;
+
+// ---- global workspace layout, per pair (bytes) ----
+constexpr int64_t kXO = 2 * 2 * kB * kD * 4;         // [half][parity][64][64] fp32
+constexpr int64_t kXY = 2 * 2 * 32 * kD * 4;         // [half][parity][32][64] fp32
+constexpr int64_t kPairBytes = kXO + kXY;
+constexpr int64_t kFlagStride = 128;                  // bytes between flags (own cache line)
+
+struct Params {
+  int N, chunk, streams, n_pairs;
+  const __hip_bfloat16* k;
+  const __hip_bfloat16* v;
+  const __hip_bfloat16* q;
+  const float* alpha;
+  const float* eta;
+  const float* theta;
+  const float* W_in;
+  const float* S_in;
+  __hip_bfloat16* y;
+  float* W_out;
+  float* S_out;
+  unsigned char* xbuf;   // n_pairs * kPairBytes
+  unsigned* flags;       // n_pairs * 2 flags, kFlagStride apart
+  unsigned* status;      // set to 1 when a pair gave up waiting
+  unsigned spin_max;
+};
+
+// accumulator row of register r for lane group lg (32x32 tile)
+__device__ __forceinline__ int crow(int r, int lg) { return 8 * (r >> 2) + 4 * lg + (r & 3); }
+
+__device__ __forceinline__ f16v mfma(h8 a, h8 b, f16v c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// 8 fp16 operand values of one lane for K-step s of a 32-wide block at
+// column kbase of an LDS row: contraction slots follow the accumulator row
+// order (two runs of 4: kbase+4lg.. and kbase+8+4lg..).
+__device__ __forceinline__ h8 lds_frag(const _Float16* row, int kbase, int lg) {
+  h4 lo = *(const h4*)(row + kbase + 4 * lg);
+  h4 hi = *(const h4*)(row + kbase + 8 + 4 * lg);
+  return h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ h8 hmul(h8 a, h8 b) { return a * b; }
+
+// The fp32 state lives in accumulation registers (AGPRs); VALU reaches it
+// only through these moves, which keeps the architectural VGPRs for the
+// chunk's working set.
+__device__ __forceinline__ float ag_get(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+__device__ __forceinline__ float ag_put(float v) {
+  float a;
+  asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(a) : "v"(v));
+  return a;
+}
+struct Tile {   // one 32x32 fp32 accumulator tile of the state
+  float r[16];
+};
+
+__device__ __forceinline__ h8 state_frag(const Tile& t, int s, int e) {
+  h8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (_Float16)ldexpf(ag_get(t.r[8 * s + i]), e);
+  return r;
+}
+
+__device__ __forceinline__ float state_amax(const Tile& t) {
+  float m = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(ag_get(t.r[r])));
+  return m;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+// power-of-two scale exponent bringing amax into [2^13, 2^14)
+__device__ __forceinline__ int scale_exp(float amax) {
+  if (!(amax > 0.f) || !(amax < INFINITY)) return 0;
+  int e;
+  (void)frexpf(amax, &e);
+  return 14 - e;
+}
+
+__device__ __forceinline__ float sigmoidf_(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
+// agent-coherent relaxed accesses for the pair exchange
+__device__ __forceinline__ void xstore2(float* p, float a, float b) {
+  const unsigned long long v = (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
+  __hip_atomic_store((unsigned long long*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void xload2(const float* p, float& a, float& b) {
+  const unsigned long long v = __hip_atomic_load((const unsigned long long*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  a = __uint_as_float((unsigned)v);
+  b = __uint_as_float((unsigned)(v >> 32));
+}
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+__global__ void zero_flags_kernel(unsigned* flags, int n, unsigned* status) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    flags[(int64_t)i * (kFlagStride / 4)] = 0u;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0u;
+}
+
+__global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  _Float16* sK = (_Float16*)(smem + OFF_K);
+  _Float16* sKT = (_Float16*)(smem + OFF_KT);
+  _Float16* sQ = (_Float16*)(smem + OFF_Q);
+  _Float16* sD2 = (_Float16*)(smem + OFF_D2);
+  _Float16* sD2T = (_Float16*)(smem + OFF_D2T);
+  _Float16* sSC1 = (_Float16*)(smem + OFF_SC1);
+  float* sDM = (float*)(smem + OFF_DM);
+  float* cf = (float*)(smem + OFF_COEF);
+  _Float16* ch = (_Float16*)(smem + OFF_COEF + COEF_H16);
+  int* ci = (int*)(smem + OFF_COEF + COEF_INT);
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int lr = lane & 31;
+  const int lg = lane >> 5;
+
+  // pair / half: blocks g and g + 8 usually share an XCD (round-robin dispatch),
+  // so pairs are formed that way when the grid allows it; correctness does
+  // not depend on the placement
+  int pair, half;
+  {
+    const int g = blockIdx.x;
+    if ((gridDim.x & 15) == 0) {
+      const int slot = g >> 3;
+      pair = (g & 7) + 8 * (slot >> 1);
+      half = slot & 1;
+    } else {
+      pair = g >> 1;
+      half = g & 1;
+    }
+  }
+  const int hs = kHC * half + kHW * w;   // first hidden unit of this wave
+  _Float16* sRA = (_Float16*)(smem + OFF_WAVE + w * kWaveRegion);       // A1 copy [j][h_l]
+  _Float16* sRW = (_Float16*)(smem + OFF_WAVE + w * kWaveRegion + kA1Bytes);  // W2 copy [h_l][c]
+  float* sRP = (float*)(smem + OFF_WAVE + w * kWaveRegion + kA1Bytes);   // O half-partial [j][c]
+  float* sRF = (float*)(smem + OFF_WAVE + w * kWaveRegion);              // y^T partial [c][j]
+
+  unsigned char* xb = p.xbuf + (int64_t)pair * kPairBytes;
+  float* xO_me = (float*)(xb) + half * 2 * kB * kD;
+  const float* xO_pt = (const float*)(xb) + (1 - half) * 2 * kB * kD;
+  float* xY_me = (float*)(xb + kXO) + half * 2 * 32 * kD;
+  const float* xY_pt = (const float*)(xb + kXO) + (1 - half) * 2 * 32 * kD;
+  unsigned* flag_me = p.flags + (int64_t)(2 * pair + half) * (kFlagStride / 4);
+  const unsigned* flag_pt = p.flags + (int64_t)(2 * pair + 1 - half) * (kFlagStride / 4);
+
+  // pair handshake: publish `seq` and wait for the partner's; false = gave up
+  auto handshake = [&](unsigned seq) -> bool {
+    wait_stores();
+    __syncthreads();
+    if (tid == 0) {
+      __hip_atomic_store(flag_me, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      unsigned it = 0;
+      while (__hip_atomic_load(flag_pt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < seq) {
+        if (++it >= p.spin_max) break;
+        __builtin_amdgcn_s_sleep(4);
+      }
+      const int ok = it < p.spin_max;
+      if (!ok) __hip_atomic_store(p.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ci[INT_FAIL] = ok ? 0 : 1;
+    }
+    __syncthreads();
+    return ci[INT_FAIL] == 0;
+  };
+
+  // my y rows of the previous chunk, kept across the chunk boundary:
+  // thread t covers row j = 32*half + t/8, columns (t%8)*8 .. +8
+  float ymine[8];
+  int64_t prev_row0 = -1;   // global token row of the previous chunk's first token
+  int prev_n = 0;
+  unsigned seq = 0;
+  bool failed = false;
+
+  auto finish_prev_y = [&](unsigned parity) {
+    // partner's partial for my rows of the previous chunk, then the fixed-order sum
+    const int jr = tid >> 3, cc = (tid & 7) * 8;
+    const float* src = xY_pt + parity * 32 * kD + jr * kD + cc;
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) xload2(src + i, pv[i], pv[i + 1]);
+    const int j = 32 * half + jr;
+    if (j < prev_n) {
+      __hip_bfloat16* yr = p.y + (prev_row0 + j) * kD + cc;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) yr[i] = __float2bfloat16(half == 0 ? ymine[i] + pv[i] : pv[i] + ymine[i]);
+    }
+  };
+
+  for (int s = pair; s < p.streams && !failed; s += p.n_pairs) {
+    const int64_t tok0 = (int64_t)s * p.N;
+    // ---- this wave's state, AGPR-resident ----
+    // W1m[ct]: rows c = 32ct + crow, cols h = hs + lr   (W1[h][c])
+    // W2m[ct]: rows h = hs + crow, cols c = 32ct + lr   (W2[c][h])
+    Tile W1m[2], S1m[2], W2m[2], S2m[2];
+    {
+      const float* Wi = p.W_in + (int64_t)s * kP;
+      const float* Si = p.S_in + (int64_t)s * kP;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c1 = 32 * ct + crow(r, lg), h1 = hs + lr;
+          W1m[ct].r[r] = ag_put(Wi[h1 * kD + c1]);
+          S1m[ct].r[r] = ag_put(Si[h1 * kD + c1]);
+          const int h2 = hs + crow(r, lg), c2 = 32 * ct + lr;
+          W2m[ct].r[r] = ag_put(Wi[kH * kD + c2 * kH + h2]);
+          S2m[ct].r[r] = ag_put(Si[kH * kD + c2 * kH + h2]);
+        }
+    }
+
+    for (int c0 = 0; c0 < p.N; c0 += p.chunk) {
+      const int n = min(p.chunk, p.N - c0);
+
+      // ================= load the chunk (K, K^T, Q as fp16; gates) =================
+      {
+        const int j = tid >> 2, cb = (tid & 3) * 16;
+        float kv[16], qv[16];
+        if (j < n) {
+          const __hip_bfloat16* kr = p.k + (tok0 + c0 + j) * kD + cb;
+          const __hip_bfloat16* qr = p.q + (tok0 + c0 + j) * kD + cb;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            kv[i] = __bfloat162float(kr[i]);
+            qv[i] = __bfloat162float(qr[i]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) kv[i] = qv[i] = 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; i += 4) {
+          *(h4*)(sK + j * RS + cb + i) = h4{(_Float16)kv[i], (_Float16)kv[i + 1], (_Float16)kv[i + 2], (_Float16)kv[i + 3]};
+          *(h4*)(sQ + j * RS + cb + i) = h4{(_Float16)qv[i], (_Float16)qv[i + 1], (_Float16)qv[i + 2], (_Float16)qv[i + 3]};
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sKT[(cb + i) * RS + j] = (_Float16)kv[i];
+        if (tid < kB) {
+          const bool ok = tid < n;
+          cf[COEF_ALPHA + tid] = ok ? p.alpha[tok0 + c0 + tid] : 0.f;   // padding: no forgetting,
+          cf[COEF_ETA + tid] = ok ? p.eta[tok0 + c0 + tid] : 1.f;       // no decay,
+          cf[COEF_THETA + tid] = ok ? p.theta[tok0 + c0 + tid] : 0.f;   // no write
+        }
+        if (tid < 2) ci[tid] = 0;
+      }
+      __syncthreads();
+
+      // ================= a1: coefficients (both halves compute them identically) =================
+      if (w == 0) {
+        const int i = lane;   // column i of D, and U_i
+        const float thi = cf[COEF_THETA + i];
+        float di = 0.f, pr = 1.f, dlast = 0.f;
+        for (int j = 0; j < kB; ++j) {
+          if (j == i) {
+            di = thi;
+          } else if (j > i) {
+            pr *= cf[COEF_ETA + j];
+            di = (1.f - cf[COEF_ALPHA + j]) * di + thi * pr;
+          }
+          sDM[j * RSF + i] = (j >= i) ? di : 0.f;
+          if (j == n - 1) dlast = (j >= i) ? di : 0.f;
+        }
+        const float ui = thi * pr;   // theta_i prod_{m>i} eta_m (padding has eta = 1)
+        cf[COEF_U + i] = ui;
+        cf[COEF_DN + i] = dlast;
+        const float mu = wave_max(fabsf(ui)), md = wave_max(fabsf(dlast));
+        int eu = 0, ed = 0;
+        if (mu > 0.f && mu < INFINITY) { (void)frexpf(mu, &eu); eu = -eu; }
+        if (md > 0.f && md < INFINITY) { (void)frexpf(md, &ed); ed = -ed; }
+        // weights scaled into (0.5, 1]: products with unit-size operands stay in fp16 range
+        ch[H16_WU + i] = (_Float16)ldexpf(ui, eu);
+        ch[H16_WD + i] = (_Float16)ldexpf(dlast, ed);
+        if (lane == 0) { ci[INT_EWU] = eu; ci[INT_EWD] = ed; }
+      } else if (w == 1) {
+        const int j = lane;
+        float a = 1.f, e = 1.f, f = 0.f;
+        for (int m = 0; m <= j; ++m) {
+          const float om = 1.f - cf[COEF_ALPHA + m];
+          a *= om;
+          e *= cf[COEF_ETA + m];
+          f = om * f + e;
+        }
+        cf[COEF_A + j] = a;
+        cf[COEF_E + j] = e;
+        cf[COEF_F + j] = f;
+      }
+
+      // state scales (joint for W and S of a layer, per wave)
+      const int e1 = scale_exp(wave_max(fmaxf(fmaxf(state_amax(W1m[0]), state_amax(W1m[1])),
+                                              fmaxf(state_amax(S1m[0]), state_amax(S1m[1])))));
+      const int e2 = scale_exp(wave_max(fmaxf(fmaxf(state_amax(W2m[0]), state_amax(W2m[1])),
+                                              fmaxf(state_amax(S2m[0]), state_amax(S2m[1])))));
+
+      // ================= a2: key-side forward Z1 = K W1^T (rows j, cols h) =================
+      // A1 = SiLU(Z1) (scaled fp16: kept for the update, copied to LDS for the
+      // contractions over h), SiLU'(Z1) (fp16, for backprop)
+      h8 A1h[2][2], SPh[2][2];
+      int eA1;
+      {
+        f16v Z[2];
+        float am = 0.f;
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          f16v acc = {};
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+              acc = mfma(lds_frag(sK + (32 * jt + lr) * RS, 32 * ct + 16 * st, lg), state_frag(W1m[ct], st, e1), acc);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float z = ldexpf(acc[r], -e1);
+            const float sg = sigmoidf_(z);
+            const float a = z * sg;
+            Z[jt][r] = a;
+            am = fmaxf(am, fabsf(a));
+            SPh[jt][r >> 3][r & 7] = (_Float16)(sg + a * (1.f - sg));   // s (1 + z (1 - s))
+          }
+        }
+        eA1 = scale_exp(wave_max(am));
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const _Float16 hv = (_Float16)ldexpf(Z[jt][r], eA1);
+            A1h[jt][r >> 3][r & 7] = hv;
+            sRA[(32 * jt + crow(r, lg)) * RSA + lr] = hv;   // A1 copy [j][h_l]
+          }
+      }
+      __syncthreads();   // coefficients (D, A, E, F, U, weights) visible from here on
+
+      // ================= O = A1 W2^T: wave partials -> this half's sum (two passes of 32 rows) =================
+      float om[2][8];
+      const int rj = lane >> 3, rc = (lane & 7) * 8;   // this lane's 8 outputs of a reduced row block
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          f16v acc = {};
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+            acc = mfma(lds_frag(sRA + (32 * pass + lr) * RSA, 16 * st, lg), state_frag(W2m[ct], st, e2), acc);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sRP[crow(r, lg) * RSF + 32 * ct + lr] = ldexpf(acc[r], -(eA1 + e2));
+        }
+        __syncthreads();
+        const int jl = 8 * w + rj;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) om[pass][i] = 0.f;
+#pragma unroll
+        for (int src = 0; src < kWaves; ++src) {
+          const float* sp = (const float*)(smem + OFF_WAVE + src * kWaveRegion + kA1Bytes) + jl * RSF + rc;
+          const f4v x0 = *(const f4v*)sp, x1 = *(const f4v*)(sp + 4);
+          om[pass][0] += x0[0]; om[pass][1] += x0[1]; om[pass][2] += x0[2]; om[pass][3] += x0[3];
+          om[pass][4] += x1[0]; om[pass][5] += x1[1]; om[pass][6] += x1[2]; om[pass][7] += x1[3];
+        }
+        __syncthreads();
+      }
+      // publish this half's O (and, implied by the flag, last chunk's y partial)
+      const unsigned par = seq & 1u;
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        float* dst = xO_me + par * kB * kD + (32 * pass + 8 * w + rj) * kD + rc;
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) xstore2(dst + i, om[pass][i], om[pass][i + 1]);
+      }
+
+      // ---- work that does not need the partner: first-layer scores, W2 copy ----
+      f16v sc;
+      {
+        const int jt = w >> 1, it = w & 1;
+        f16v acc = {};
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+            acc = mfma(lds_frag(sQ + (32 * jt + lr) * RS, 32 * ct + 16 * st, lg),
+                       lds_frag(sK + (32 * it + lr) * RS, 32 * ct + 16 * st, lg), acc);
+        float am = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sc[r] = acc[r] * sDM[(32 * jt + crow(r, lg)) * RSF + 32 * it + lr];
+          am = fmaxf(am, fabsf(sc[r]));
+        }
+        am = wave_max(am);
+        if (lane == 0) atomicMax((unsigned int*)&ci[INT_AMAX_SC1], __float_as_uint(am));
+      }
+      // W2 copy for the backprop: [h_l][c] fp16 (the O partial buffer is free again)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sRW[crow(r, lg) * RS + 32 * ct + lr] = (_Float16)ldexpf(ag_get(W2m[ct].r[r]), e2);
+
+      if (!handshake(seq + 1)) { failed = true; break; }
+
+      // last chunk's y rows (the partner published them before this flag)
+      if (prev_row0 >= 0) finish_prev_y(par ^ 1u);
+
+      // ================= O = half 0 + half 1, Delta2 = O - V =================
+      float d2v[2][8];
+      {
+        float am = 0.f;
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+          const int j = 32 * pass + 8 * w + rj;
+          const float* src = xO_pt + par * kB * kD + j * kD + rc;
+          float pv[8];
+#pragma unroll
+          for (int i = 0; i < 8; i += 2) xload2(src + i, pv[i], pv[i + 1]);
+          if (j < n) {
+            const __hip_bfloat16* vr = p.v + (tok0 + c0 + j) * kD + rc;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const float o = half == 0 ? om[pass][i] + pv[i] : pv[i] + om[pass][i];
+              d2v[pass][i] = o - __bfloat162float(vr[i]);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) d2v[pass][i] = 0.f;
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(d2v[pass][i]));
+        }
+        am = wave_max(am);
+        if (lane == 0) atomicMax((unsigned int*)&ci[INT_AMAX_D2], __float_as_uint(am));
+      }
+      const int eSC = scale_exp(__uint_as_float((unsigned)ci[INT_AMAX_SC1]));
+      {
+        const int jt = w >> 1, it = w & 1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sSC1[(32 * jt + crow(r, lg)) * RS + 32 * it + lr] = (_Float16)ldexpf(sc[r], eSC);
+      }
+      __syncthreads();
+      const int eD2 = scale_exp(__uint_as_float((unsigned)ci[INT_AMAX_D2]));
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        const int j = 32 * pass + 8 * w + rj;
+        h8 hv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[i] = (_Float16)ldexpf(d2v[pass][i], eD2);
+        *(h4*)(sD2 + j * RS + rc) = h4{hv[0], hv[1], hv[2], hv[3]};
+        *(h4*)(sD2 + j * RS + rc + 4) = h4{hv[4], hv[5], hv[6], hv[7]};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sD2T[(rc + i) * RS + j] = hv[i];
+      }
+      __syncthreads();
+
+      // ================= a3: Delta1 = (Delta2 W2) * SiLU'(Z1)  (rows j, cols h) =================
+      h8 D1h[2][2];
+      int eD1;
+      {
+        f16v Df[2];
+        float am = 0.f;
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          f16v acc = {};
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+              acc = mfma(lds_frag(sD2 + (32 * jt + lr) * RS, 32 * ct + 16 * st, lg),
+                         lds_frag(sRW + lr * RS, 32 * ct + 16 * st, lg), acc);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float x = ldexpf(acc[r], -(eD2 + e2)) * (float)SPh[jt][r >> 3][r & 7];
+            Df[jt][r] = x;
+            am = fmaxf(am, fabsf(x));
+          }
+        }
+        eD1 = scale_exp(wave_max(am));
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) D1h[jt][r >> 3][r & 7] = (_Float16)ldexpf(Df[jt][r], eD1);
+      }
+
+      // ================= a5 layer 1: Zq1^T = W1 (A q)^T + S1 (F q)^T - Delta1^T SC1^T (rows h, cols j) =================
+      h8 H1h[2][2];
+      int eH1[2];
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        // per-token A_j, F_j (lane = token) applied to fp32 accumulators
+        const float aj = cf[COEF_A + 32 * jt + lr], fj = cf[COEF_F + 32 * jt + lr];
+        f16v accW = {}, accS = {}, acc3 = {};
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const h8 qf = lds_frag(sQ + (32 * jt + lr) * RS, 32 * ct + 16 * st, lg);
+            accW = mfma(state_frag(W1m[ct], st, e1), qf, accW);
+            accS = mfma(state_frag(S1m[ct], st, e1), qf, accS);
+          }
+#pragma unroll
+        for (int it = 0; it < 2; ++it)
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+            acc3 = mfma(D1h[it][st], lds_frag(sSC1 + (32 * jt + lr) * RS, 32 * it + 16 * st, lg), acc3);
+        f16v Hf;
+        float am = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float z = ldexpf(aj * accW[r] + fj * accS[r], -e1) - ldexpf(acc3[r], -(eD1 + eSC));
+          Hf[r] = z * sigmoidf_(z);
+          am = fmaxf(am, fabsf(Hf[r]));
+        }
+        eH1[jt] = scale_exp(wave_max(am));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) H1h[jt][r >> 3][r & 7] = (_Float16)ldexpf(Hf[r], eH1[jt]);
+      }
+
+      const float An = cf[COEF_A + n - 1], En = cf[COEF_E + n - 1], Fn = cf[COEF_F + n - 1];
+      const int ewU = ci[INT_EWU], ewD = ci[INT_EWD];
+      // ================= a4, layer 1 (W1, S1 are not read again this chunk) =================
+      // G1^T[c][h] = sum_j K[j][c] w_j Delta1[j][h]
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        f16v gU = {}, gD = {};
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const h8 kf = lds_frag(sKT + (32 * ct + lr) * RS, 32 * jt + 16 * st, lg);
+            gU = mfma(hmul(kf, lds_frag(ch + H16_WU, 32 * jt + 16 * st, lg)), D1h[jt][st], gU);
+            gD = mfma(hmul(kf, lds_frag(ch + H16_WD, 32 * jt + 16 * st, lg)), D1h[jt][st], gD);
+          }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float w0 = ag_get(W1m[ct].r[r]), s0 = ag_get(S1m[ct].r[r]);
+          W1m[ct].r[r] = ag_put(An * w0 + Fn * s0 - ldexpf(gD[r], -(ewD + eD1)));
+          S1m[ct].r[r] = ag_put(En * s0 - ldexpf(gU[r], -(ewU + eD1)));
+        }
+      }
+
+      // ================= masked second-layer scores (D o (H1 A1^T))^T (rows i, cols j) =================
+      h8 DPh[2][2][2];
+      int eDP[2];
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        f16v Pf[2];
+        float am = 0.f;
+        const int j = 32 * jt + lr;
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          f16v acc = {};
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+            acc = mfma(lds_frag(sRA + (32 * it + lr) * RSA, 16 * st, lg), H1h[jt][st], acc);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f4v dv = *(const f4v*)(sDM + j * RSF + 32 * it + 8 * g + 4 * lg);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float x = ldexpf(acc[4 * g + q], -(eA1 + eH1[jt])) * dv[q];
+              Pf[it][4 * g + q] = x;
+              am = fmaxf(am, fabsf(x));
+            }
+          }
+        }
+        eDP[jt] = scale_exp(wave_max(am));
+#pragma unroll
+        for (int it = 0; it < 2; ++it)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) DPh[it][jt][r >> 3][r & 7] = (_Float16)ldexpf(Pf[it][r], eDP[jt]);
+      }
+
+      // ================= a5 layer 2: y^T partial = W2 (A H1)^T + S2 (F H1)^T - Delta2^T (D o P)^T =================
+      // tiles go straight to this wave's region (fp32 [c][j]): the wave is past
+      // its last read of its A1 and W2 copies, and other waves read the region
+      // only after the next barrier
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        const float aj = cf[COEF_A + 32 * jt + lr], fj = cf[COEF_F + 32 * jt + lr];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          f16v accW = {}, accS = {}, acc3 = {};
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            accW = mfma(state_frag(W2m[ct], st, e2), H1h[jt][st], accW);
+            accS = mfma(state_frag(S2m[ct], st, e2), H1h[jt][st], accS);
+          }
+#pragma unroll
+          for (int it = 0; it < 2; ++it)
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+              acc3 = mfma(lds_frag(sD2T + (32 * ct + lr) * RS, 32 * it + 16 * st, lg), DPh[it][jt][st], acc3);
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sRF[(32 * ct + crow(r, lg)) * RSF + 32 * jt + lr] =
+                ldexpf(aj * accW[r] + fj * accS[r], -(e2 + eH1[jt])) - ldexpf(acc3[r], -(eD2 + eDP[jt]));
+        }
+      }
+
+      // ================= a4, layer 2: G2^T[h][c] = sum_j A1[j][h] w_j Delta2[j][c] =================
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        f16v gU = {}, gD = {};
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const h8 df = lds_frag(sD2T + (32 * ct + lr) * RS, 32 * jt + 16 * st, lg);
+            gU = mfma(A1h[jt][st], hmul(df, lds_frag(ch + H16_WU, 32 * jt + 16 * st, lg)), gU);
+            gD = mfma(A1h[jt][st], hmul(df, lds_frag(ch + H16_WD, 32 * jt + 16 * st, lg)), gD);
+          }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float w0 = ag_get(W2m[ct].r[r]), s0 = ag_get(S2m[ct].r[r]);
+          W2m[ct].r[r] = ag_put(An * w0 + Fn * s0 - ldexpf(gD[r], -(ewD + eA1 + eD2)));
+          S2m[ct].r[r] = ag_put(En * s0 - ldexpf(gU[r], -(ewU + eA1 + eD2)));
+        }
+      }
+      __syncthreads();
+
+      // ---- this half's y: sum the 4 wave partials; send the partner its rows, keep mine ----
+      {
+        const int jr = tid >> 3, cc = (tid & 7) * 8;
+        float send[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { send[i] = 0.f; ymine[i] = 0.f; }
+#pragma unroll
+        for (int src = 0; src < kWaves; ++src) {
+          const float* rp = (const float*)(smem + OFF_WAVE + src * kWaveRegion);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            send[i] += rp[(cc + i) * RSF + 32 * (1 - half) + jr];
+            ymine[i] += rp[(cc + i) * RSF + 32 * half + jr];
+          }
+        }
+        float* dst = xY_me + par * 32 * kD + jr * kD + cc;
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) xstore2(dst + i, send[i], send[i + 1]);
+      }
+      prev_row0 = tok0 + c0;
+      prev_n = n;
+      ++seq;
+      __syncthreads();   // LDS tiles and wave regions are rewritten by the next chunk
+    }
+
+    if (failed) {
+      // partner never arrived: poison this stream's state so the failure is visible
+      float* Wo = p.W_out + (int64_t)s * kP;
+      float* So = p.S_out + (int64_t)s * kP;
+      for (int i = tid; i < kP; i += kThreads) { Wo[i] = __builtin_nanf(""); So[i] = __builtin_nanf(""); }
+      break;
+    }
+    // ---- write this wave's part of the final state ----
+    {
+      float* Wo = p.W_out + (int64_t)s * kP;
+      float* So = p.S_out + (int64_t)s * kP;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c1 = 32 * ct + crow(r, lg), h1 = hs + lr;
+          Wo[h1 * kD + c1] = ag_get(W1m[ct].r[r]);
+          So[h1 * kD + c1] = ag_get(S1m[ct].r[r]);
+          const int h2 = hs + crow(r, lg), c2 = 32 * ct + lr;
+          Wo[kH * kD + c2 * kH + h2] = ag_get(W2m[ct].r[r]);
+          So[kH * kD + c2 * kH + h2] = ag_get(S2m[ct].r[r]);
+        }
+    }
+  }
+
+  // the last chunk's y rows: one more handshake (a flag value no chunk uses)
+  if (!failed && prev_row0 >= 0) {
+    if (handshake(seq + 1)) finish_prev_y((seq - 1) & 1u);
+  }
+}
+
+}  // namespace
+
+bool mlp2_supported(const Shape& s, int chunk) {
+  return s.L == 2 && s.d == kD && s.hidden == kH && s.io == TM_IO_BF16 &&
+         s.read_mode == TM_READ_AFTER_WRITE && chunk >= 1 && chunk <= kB;
+}
+
+static int64_t pairs_for(const Shape& s) { return s.streams < kMaxPairs ? s.streams : kMaxPairs; }
+
+int64_t mlp2_ws_bytes(const Shape& s, int) {
+  const int64_t np = pairs_for(s);
+  return np * kPairBytes + 2 * np * kFlagStride + 256;
+}
+
+hipError_t launch_mlp2(const Shape& s, int chunk, const void* k, const void* v, const void* q,
+                       const float* alpha, const float* eta, const float* theta,
+                       const float* W_in, const float* S_in, void* y, float* W_out,
+                       float* S_out, void* ws, hipStream_t stream) {
+  static bool configured = false;   // attribute set once per process (idempotent)
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute((const void*)mlp2_pair_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  // every pair must be resident at once (one workgroup per CU)
+  int64_t np = pairs_for(s);
+  if (np > cus / 2) np = cus / 2;
+  if (np < 1) return hipErrorInvalidConfiguration;
+  Params p;
+  p.N = s.N;
+  p.chunk = chunk;
+  p.streams = s.streams;
+  p.n_pairs = (int)np;
+  p.k = (const __hip_bfloat16*)k;
+  p.v = (const __hip_bfloat16*)v;
+  p.q = (const __hip_bfloat16*)q;
+  p.alpha = alpha;
+  p.eta = eta;
+  p.theta = theta;
+  p.W_in = W_in;
+  p.S_in = S_in;
+  p.y = (__hip_bfloat16*)y;
+  p.W_out = W_out;
+  p.S_out = S_out;
+  unsigned char* base = (unsigned char*)ws;
+  p.xbuf = base;
+  p.flags = (unsigned*)(base + pairs_for(s) * kPairBytes);
+  p.status = (unsigned*)(base + pairs_for(s) * kPairBytes + 2 * pairs_for(s) * kFlagStride);
+  p.spin_max = kSpinMax;
+  hipLaunchKernelGGL(zero_flags_kernel, dim3(1), dim3(256), 0, stream, p.flags, (int)(2 * np), p.status);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mlp2_pair_kernel, dim3((unsigned)(2 * np)), dim3(kThreads), kLdsBytes, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace titans

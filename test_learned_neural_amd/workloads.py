@@ -184,7 +184,7 @@ def stream_ids(cfg: MemoryConfig) -> List[Tuple[int, int]]:
 
 
 def make_inputs(cfg: MemoryConfig, streams: Optional[Sequence[Tuple[int, int]]] = None,
-                n_tokens: Optional[int] = None) -> Dict[str, np.ndarray]:
+                n_tokens: Optional[int] = None, workers: int = 1) -> Dict[str, np.ndarray]:
     """Draw the inputs of ``cfg`` for the selected (b, h) streams.
 
     Returns numpy arrays with a leading stream axis (in the order given, by
@@ -206,7 +206,8 @@ def make_inputs(cfg: MemoryConfig, streams: Optional[Sequence[Tuple[int, int]]] 
         "theta": np.empty((S, n), np.float32),
         "W0": np.empty((S, P), np.float32), "S0": np.zeros((S, P), np.float32),
     }
-    for i, (b, h) in enumerate(ids):
+    def fill(i):
+        b, h = ids[i]
         k, v, q, a, e, t, w0 = _draw_stream(cfg, b, h, n)
         out["k"][i] = round_io(k, cfg.io)
         out["v"][i] = round_io(v, cfg.io)
@@ -215,6 +216,15 @@ def make_inputs(cfg: MemoryConfig, streams: Optional[Sequence[Tuple[int, int]]] 
         out["eta"][i] = e
         out["theta"][i] = t
         out["W0"][i] = w0
+
+    if workers > 1 and S > 1:
+        # each stream has its own generators, so the fill order is irrelevant
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(fill, range(S)))
+    else:
+        for i in range(S):
+            fill(i)
     return out
 
 
