@@ -27,6 +27,11 @@ DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-p
           "-munsafe-fp-atomics"]
 
 
+# MFMA results in VGPRs: the MFMA kernel post-processes every accumulator on
+# the VALU, and its AGPRs hold the memory state
+PER_FILE = {"tm_mlp2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def hipcc() -> str:
     for cand in ("/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -39,7 +44,7 @@ def _compile(src: str, extra=()) -> str:
     path = os.path.join(CSRC, src)
     cmd = [hipcc()] + COMMON + list(extra)
     if src.endswith(".hip"):
-        cmd += ["-x", "hip"] + DEVICE
+        cmd += ["-x", "hip"] + DEVICE + PER_FILE.get(src, [])
     cmd += ["-c", path, "-o", obj]
     subprocess.check_call(cmd)
     return obj

@@ -87,13 +87,18 @@ constexpr int COEF_ALPHA = 0, COEF_ETA = 64, COEF_THETA = 128, COEF_A = 192, COE
 constexpr int COEF_H16 = 512 * 4;                                   // byte offset of fp16 arrays
 constexpr int H16_WU = 128, H16_WD = 192;                           // half index
 constexpr int COEF_INT = COEF_H16 + 256 * 2;                        // byte offset of int slots
-constexpr int kCoefBytes = COEF_INT + 16 * 4;
+constexpr int COEF_PAIR = COEF_INT + 16 * 4;                        // byte offset of (1-alpha, eta) pairs
+constexpr int kCoefBytes = COEF_PAIR + kB * 8;
 constexpr int OFF_WAVE = (OFF_COEF + kCoefBytes + 255) / 256 * 256;
 // per-wave region: [A1 copy 64 x RSA fp16][W2 copy 32 x RS fp16 | O half-partial 32 x RSF fp32];
-// later the whole region holds the wave's y^T partial (64 x RSF fp32)
+// later the whole region holds the wave's y partial (64 x RSF fp32, token-major)
 constexpr int kA1Bytes = kB * RSA * 2;               // 4608
 constexpr int kWaveRegion = kD * RSF * 4;            // 17408
-constexpr int kLdsBytes = OFF_WAVE + kWaves * kWaveRegion;
+// staging for the next chunk's raw bf16 K, Q rows and gates (filled during the
+// pair handshake, converted at the next chunk's start)
+constexpr int OFF_STAGE = OFF_WAVE + kWaves * kWaveRegion;
+constexpr int kStageBytes = 2 * kB * kD * 2 + 3 * kB * 4;
+constexpr int kLdsBytes = OFF_STAGE + kStageBytes;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 static_assert(kA1Bytes + 32 * RSF * 4 <= kWaveRegion, "A1 copy + O half-partial");
 static_assert(kA1Bytes + kHW * RS * 2 <= kWaveRegion, "A1 copy + W2 copy");
@@ -167,13 +172,6 @@ __device__ __forceinline__ h8 state_frag(const Tile& t, int s, int e) {
   return r;
 }
 
-__device__ __forceinline__ float state_amax(const Tile& t) {
-  float m = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(ag_get(t.r[r])));
-  return m;
-}
-
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -192,17 +190,89 @@ __device__ __forceinline__ float sigmoidf_(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
-// agent-coherent relaxed accesses for the pair exchange
+// Pair exchange accessors: agent-coherent (sc1) relaxed accesses, ordered by
+// s_waitcnt vmcnt(0) before each flag store.  (An L2-local variant using sc0
+// loads was tried: on gfx950 a poller then kept reading a stale flag, so the
+// exchange stays agent-coherent.)
 __device__ __forceinline__ void xstore2(float* p, float a, float b) {
   const unsigned long long v = (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
   __hip_atomic_store((unsigned long long*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void xload2(const float* p, float& a, float& b) {
-  const unsigned long long v = __hip_atomic_load((const unsigned long long*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  a = __uint_as_float((unsigned)v);
-  b = __uint_as_float((unsigned)(v >> 32));
+// 8 consecutive floats at each of p0 and p1
+__device__ __forceinline__ void xload8x2(const float* p0, const float* p1, float* a, float* b) {
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    unsigned long long v = __hip_atomic_load((const unsigned long long*)(p0 + i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    a[i] = __uint_as_float((unsigned)v);
+    a[i + 1] = __uint_as_float((unsigned)(v >> 32));
+    v = __hip_atomic_load((const unsigned long long*)(p1 + i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    b[i] = __uint_as_float((unsigned)v);
+    b[i + 1] = __uint_as_float((unsigned)(v >> 32));
+  }
 }
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+// one thread's share of a chunk's raw inputs: 16 bf16 of a K row and of a Q
+// row (row j = tid/4, columns (tid%4)*16..), and for tid < 64 the gates of
+// token tid; rows and tokens past the chunk end read as zeros (gates as
+// "no forgetting, no decay, no write")
+struct ChunkRegs {
+  uint4 k0, k1, q0, q1;
+  float ga, ge, gt;
+};
+
+__device__ __forceinline__ ChunkRegs load_chunk_regs(const Params& p, int64_t row0, int n, int tid) {
+  ChunkRegs r;
+  const int j = tid >> 2, cb = (tid & 3) * 16;
+  if (j < n) {
+    const uint4* kr = (const uint4*)(p.k + (row0 + j) * kD + cb);
+    const uint4* qr = (const uint4*)(p.q + (row0 + j) * kD + cb);
+    r.k0 = kr[0]; r.k1 = kr[1]; r.q0 = qr[0]; r.q1 = qr[1];
+  } else {
+    r.k0 = r.k1 = r.q0 = r.q1 = make_uint4(0, 0, 0, 0);
+  }
+  r.ga = 0.f; r.ge = 1.f; r.gt = 0.f;
+  if (tid < kB && tid < n) {
+    r.ga = p.alpha[row0 + tid];
+    r.ge = p.eta[row0 + tid];
+    r.gt = p.theta[row0 + tid];
+  }
+  return r;
+}
+
+__device__ __forceinline__ void stage_chunk_regs(unsigned char* stage, const ChunkRegs& r, int tid) {
+  uint4* sk = (uint4*)stage;
+  uint4* sq = (uint4*)(stage + kB * kD * 2);
+  sk[2 * tid] = r.k0; sk[2 * tid + 1] = r.k1;
+  sq[2 * tid] = r.q0; sq[2 * tid + 1] = r.q1;
+  if (tid < kB) {
+    float* g = (float*)(stage + 2 * kB * kD * 2);
+    g[tid] = r.ga; g[kB + tid] = r.ge; g[2 * kB + tid] = r.gt;
+  }
+}
+
+__device__ __forceinline__ ChunkRegs unstage_chunk_regs(const unsigned char* stage, int tid) {
+  ChunkRegs r;
+  const uint4* sk = (const uint4*)stage;
+  const uint4* sq = (const uint4*)(stage + kB * kD * 2);
+  r.k0 = sk[2 * tid]; r.k1 = sk[2 * tid + 1];
+  r.q0 = sq[2 * tid]; r.q1 = sq[2 * tid + 1];
+  r.ga = 0.f; r.ge = 1.f; r.gt = 0.f;
+  if (tid < kB) {
+    const float* g = (const float*)(stage + 2 * kB * kD * 2);
+    r.ga = g[tid]; r.ge = g[kB + tid]; r.gt = g[2 * kB + tid];
+  }
+  return r;
+}
+
+__device__ __forceinline__ void bf16x8_to_h(const uint4 u, _Float16* out) {
+  const unsigned w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = (_Float16)__uint_as_float(w[i] << 16);
+    out[2 * i + 1] = (_Float16)__uint_as_float(w[i] & 0xffff0000u);
+  }
+}
 
 __global__ void zero_flags_kernel(unsigned* flags, int n, unsigned* status) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
@@ -248,18 +318,20 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
   _Float16* sRA = (_Float16*)(smem + OFF_WAVE + w * kWaveRegion);       // A1 copy [j][h_l]
   _Float16* sRW = (_Float16*)(smem + OFF_WAVE + w * kWaveRegion + kA1Bytes);  // W2 copy [h_l][c]
   float* sRP = (float*)(smem + OFF_WAVE + w * kWaveRegion + kA1Bytes);   // O half-partial [j][c]
-  float* sRF = (float*)(smem + OFF_WAVE + w * kWaveRegion);              // y^T partial [c][j]
+  float* sRF = (float*)(smem + OFF_WAVE + w * kWaveRegion);              // y partial [j][c]
 
   unsigned char* xb = p.xbuf + (int64_t)pair * kPairBytes;
   float* xO_me = (float*)(xb) + half * 2 * kB * kD;
   const float* xO_pt = (const float*)(xb) + (1 - half) * 2 * kB * kD;
   float* xY_me = (float*)(xb + kXO) + half * 2 * 32 * kD;
   const float* xY_pt = (const float*)(xb + kXO) + (1 - half) * 2 * 32 * kD;
+  bool failed0 = false;
   unsigned* flag_me = p.flags + (int64_t)(2 * pair + half) * (kFlagStride / 4);
   const unsigned* flag_pt = p.flags + (int64_t)(2 * pair + 1 - half) * (kFlagStride / 4);
 
-  // pair handshake: publish `seq` and wait for the partner's; false = gave up
-  auto handshake = [&](unsigned seq) -> bool {
+  // pair handshake: publish `seq`, run `during` (waves 1..3 while thread 0
+  // polls), and wait for the partner's `seq`; false = gave up
+  auto handshake = [&](unsigned seq, auto&& during) -> bool {
     wait_stores();
     __syncthreads();
     if (tid == 0) {
@@ -267,15 +339,21 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       unsigned it = 0;
       while (__hip_atomic_load(flag_pt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < seq) {
         if (++it >= p.spin_max) break;
-        __builtin_amdgcn_s_sleep(4);
+        __builtin_amdgcn_s_sleep(1);
       }
       const int ok = it < p.spin_max;
       if (!ok) __hip_atomic_store(p.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       ci[INT_FAIL] = ok ? 0 : 1;
+    } else {
+      during();
     }
     __syncthreads();
     return ci[INT_FAIL] == 0;
   };
+  auto nothing = [] {};
+
+  // the pair starts together (also flushes any stale flag value of this launch)
+  if (!handshake(1u, nothing)) failed0 = true;
 
   // my y rows of the previous chunk, kept across the chunk boundary:
   // thread t covers row j = 32*half + t/8, columns (t%8)*8 .. +8
@@ -283,15 +361,15 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
   int64_t prev_row0 = -1;   // global token row of the previous chunk's first token
   int prev_n = 0;
   unsigned seq = 0;
-  bool failed = false;
+  bool failed = failed0;
+  bool staged = false;   // the staging area holds the rows of the chunk about to start
 
   auto finish_prev_y = [&](unsigned parity) {
     // partner's partial for my rows of the previous chunk, then the fixed-order sum
     const int jr = tid >> 3, cc = (tid & 7) * 8;
     const float* src = xY_pt + parity * 32 * kD + jr * kD + cc;
-    float pv[8];
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) xload2(src + i, pv[i], pv[i + 1]);
+    float pv[8], unused[8];
+    xload8x2(src, src, pv, unused);
     const int j = 32 * half + jr;
     if (j < prev_n) {
       __hip_bfloat16* yr = p.y + (prev_row0 + j) * kD + cc;
@@ -306,6 +384,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
     // W1m[ct]: rows c = 32ct + crow, cols h = hs + lr   (W1[h][c])
     // W2m[ct]: rows h = hs + crow, cols c = 32ct + lr   (W2[c][h])
     Tile W1m[2], S1m[2], W2m[2], S2m[2];
+    float m1 = 0.f, m2 = 0.f;   // this lane's max |W|,|S| per layer (for the operand scales)
     {
       const float* Wi = p.W_in + (int64_t)s * kP;
       const float* Si = p.S_in + (int64_t)s * kP;
@@ -314,95 +393,50 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int c1 = 32 * ct + crow(r, lg), h1 = hs + lr;
-          W1m[ct].r[r] = ag_put(Wi[h1 * kD + c1]);
-          S1m[ct].r[r] = ag_put(Si[h1 * kD + c1]);
+          const float w1 = Wi[h1 * kD + c1], s1 = Si[h1 * kD + c1];
+          W1m[ct].r[r] = ag_put(w1);
+          S1m[ct].r[r] = ag_put(s1);
+          m1 = fmaxf(m1, fmaxf(fabsf(w1), fabsf(s1)));
           const int h2 = hs + crow(r, lg), c2 = 32 * ct + lr;
-          W2m[ct].r[r] = ag_put(Wi[kH * kD + c2 * kH + h2]);
-          S2m[ct].r[r] = ag_put(Si[kH * kD + c2 * kH + h2]);
+          const float w2 = Wi[kH * kD + c2 * kH + h2], s2 = Si[kH * kD + c2 * kH + h2];
+          W2m[ct].r[r] = ag_put(w2);
+          S2m[ct].r[r] = ag_put(s2);
+          m2 = fmaxf(m2, fmaxf(fabsf(w2), fabsf(s2)));
         }
     }
 
     for (int c0 = 0; c0 < p.N; c0 += p.chunk) {
       const int n = min(p.chunk, p.N - c0);
 
-      // ================= load the chunk (K, K^T, Q as fp16; gates) =================
+      // ================= the chunk's K, K^T, Q (fp16) and gates into LDS =================
       {
+        // rows come from the staging area when the previous chunk prefetched them
+        const ChunkRegs cr = staged ? unstage_chunk_regs(smem + OFF_STAGE, tid) : load_chunk_regs(p, tok0 + c0, n, tid);
         const int j = tid >> 2, cb = (tid & 3) * 16;
-        float kv[16], qv[16];
-        if (j < n) {
-          const __hip_bfloat16* kr = p.k + (tok0 + c0 + j) * kD + cb;
-          const __hip_bfloat16* qr = p.q + (tok0 + c0 + j) * kD + cb;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            kv[i] = __bfloat162float(kr[i]);
-            qv[i] = __bfloat162float(qr[i]);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) kv[i] = qv[i] = 0.f;
-        }
+        _Float16 kv[16], qv[16];
+        bf16x8_to_h(cr.k0, kv);
+        bf16x8_to_h(cr.k1, kv + 8);
+        bf16x8_to_h(cr.q0, qv);
+        bf16x8_to_h(cr.q1, qv + 8);
 #pragma unroll
         for (int i = 0; i < 16; i += 4) {
-          *(h4*)(sK + j * RS + cb + i) = h4{(_Float16)kv[i], (_Float16)kv[i + 1], (_Float16)kv[i + 2], (_Float16)kv[i + 3]};
-          *(h4*)(sQ + j * RS + cb + i) = h4{(_Float16)qv[i], (_Float16)qv[i + 1], (_Float16)qv[i + 2], (_Float16)qv[i + 3]};
+          *(h4*)(sK + j * RS + cb + i) = h4{kv[i], kv[i + 1], kv[i + 2], kv[i + 3]};
+          *(h4*)(sQ + j * RS + cb + i) = h4{qv[i], qv[i + 1], qv[i + 2], qv[i + 3]};
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sKT[(cb + i) * RS + j] = (_Float16)kv[i];
+        for (int i = 0; i < 16; ++i) sKT[(cb + i) * RS + j] = kv[i];
         if (tid < kB) {
-          const bool ok = tid < n;
-          cf[COEF_ALPHA + tid] = ok ? p.alpha[tok0 + c0 + tid] : 0.f;   // padding: no forgetting,
-          cf[COEF_ETA + tid] = ok ? p.eta[tok0 + c0 + tid] : 1.f;       // no decay,
-          cf[COEF_THETA + tid] = ok ? p.theta[tok0 + c0 + tid] : 0.f;   // no write
+          cf[COEF_THETA + tid] = cr.gt;
+          float2* pairs = (float2*)(smem + OFF_COEF + COEF_PAIR);
+          pairs[tid] = make_float2(1.f - cr.ga, cr.ge);
         }
         if (tid < 2) ci[tid] = 0;
       }
       __syncthreads();
 
-      // ================= a1: coefficients (both halves compute them identically) =================
-      if (w == 0) {
-        const int i = lane;   // column i of D, and U_i
-        const float thi = cf[COEF_THETA + i];
-        float di = 0.f, pr = 1.f, dlast = 0.f;
-        for (int j = 0; j < kB; ++j) {
-          if (j == i) {
-            di = thi;
-          } else if (j > i) {
-            pr *= cf[COEF_ETA + j];
-            di = (1.f - cf[COEF_ALPHA + j]) * di + thi * pr;
-          }
-          sDM[j * RSF + i] = (j >= i) ? di : 0.f;
-          if (j == n - 1) dlast = (j >= i) ? di : 0.f;
-        }
-        const float ui = thi * pr;   // theta_i prod_{m>i} eta_m (padding has eta = 1)
-        cf[COEF_U + i] = ui;
-        cf[COEF_DN + i] = dlast;
-        const float mu = wave_max(fabsf(ui)), md = wave_max(fabsf(dlast));
-        int eu = 0, ed = 0;
-        if (mu > 0.f && mu < INFINITY) { (void)frexpf(mu, &eu); eu = -eu; }
-        if (md > 0.f && md < INFINITY) { (void)frexpf(md, &ed); ed = -ed; }
-        // weights scaled into (0.5, 1]: products with unit-size operands stay in fp16 range
-        ch[H16_WU + i] = (_Float16)ldexpf(ui, eu);
-        ch[H16_WD + i] = (_Float16)ldexpf(dlast, ed);
-        if (lane == 0) { ci[INT_EWU] = eu; ci[INT_EWD] = ed; }
-      } else if (w == 1) {
-        const int j = lane;
-        float a = 1.f, e = 1.f, f = 0.f;
-        for (int m = 0; m <= j; ++m) {
-          const float om = 1.f - cf[COEF_ALPHA + m];
-          a *= om;
-          e *= cf[COEF_ETA + m];
-          f = om * f + e;
-        }
-        cf[COEF_A + j] = a;
-        cf[COEF_E + j] = e;
-        cf[COEF_F + j] = f;
-      }
-
       // state scales (joint for W and S of a layer, per wave)
-      const int e1 = scale_exp(wave_max(fmaxf(fmaxf(state_amax(W1m[0]), state_amax(W1m[1])),
-                                              fmaxf(state_amax(S1m[0]), state_amax(S1m[1])))));
-      const int e2 = scale_exp(wave_max(fmaxf(fmaxf(state_amax(W2m[0]), state_amax(W2m[1])),
-                                              fmaxf(state_amax(S2m[0]), state_amax(S2m[1])))));
+      const int e1 = scale_exp(wave_max(m1));
+      const int e2 = scale_exp(wave_max(m2));
 
       // ================= a2: key-side forward Z1 = K W1^T (rows j, cols h) =================
       // A1 = SiLU(Z1) (scaled fp16: kept for the update, copied to LDS for the
@@ -412,14 +446,19 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       {
         f16v Z[2];
         float am = 0.f;
+        f16v zacc[2] = {{}, {}};
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const h8 wf = state_frag(W1m[ct], st, e1);
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt)
+              zacc[jt] = mfma(lds_frag(sK + (32 * jt + lr) * RS, 32 * ct + 16 * st, lg), wf, zacc[jt]);
+          }
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
-          f16v acc = {};
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-              acc = mfma(lds_frag(sK + (32 * jt + lr) * RS, 32 * ct + 16 * st, lg), state_frag(W1m[ct], st, e1), acc);
+          const f16v acc = zacc[jt];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float z = ldexpf(acc[r], -e1);
@@ -440,11 +479,15 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
             sRA[(32 * jt + crow(r, lg)) * RSA + lr] = hv;   // A1 copy [j][h_l]
           }
       }
-      __syncthreads();   // coefficients (D, A, E, F, U, weights) visible from here on
 
       // ================= O = A1 W2^T: wave partials -> this half's sum (two passes of 32 rows) =================
       float om[2][8];
       const int rj = lane >> 3, rc = (lane & 7) * 8;   // this lane's 8 outputs of a reduced row block
+      h8 w2f[2][2];   // W2 operand fragments [ct][st] (scaled fp16), reused for the W2 copy
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) w2f[ct][st] = state_frag(W2m[ct], st, e2);
 #pragma unroll
       for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -452,7 +495,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
           f16v acc = {};
 #pragma unroll
           for (int st = 0; st < 2; ++st)
-            acc = mfma(lds_frag(sRA + (32 * pass + lr) * RSA, 16 * st, lg), state_frag(W2m[ct], st, e2), acc);
+            acc = mfma(lds_frag(sRA + (32 * pass + lr) * RSA, 16 * st, lg), w2f[ct][st], acc);
 #pragma unroll
           for (int r = 0; r < 16; ++r) sRP[crow(r, lg) * RSF + 32 * ct + lr] = ldexpf(acc[r], -(eA1 + e2));
         }
@@ -478,7 +521,94 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
         for (int i = 0; i < 8; i += 2) xstore2(dst + i, om[pass][i], om[pass][i + 1]);
       }
 
-      // ---- work that does not need the partner: first-layer scores, W2 copy ----
+      // ---- work that does not need the partner: W2 copy, prefetch ----
+      // W2 copy for the backprop: [h_l][c] fp16 (the O partial buffer is free again)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sRW[crow(r, lg) * RS + 32 * ct + lr] = w2f[ct][r >> 3][r & 7];
+
+      // prefetch: this chunk's V (used right after the handshake) and the next
+      // chunk's raw K, Q and gates (staged in LDS once they arrive)
+      uint4 vr0 = make_uint4(0, 0, 0, 0), vr1 = make_uint4(0, 0, 0, 0);
+      {
+        const int j0 = 8 * w + rj, j1 = 32 + 8 * w + rj;
+        if (j0 < n) vr0 = *(const uint4*)(p.v + (tok0 + c0 + j0) * kD + rc);
+        if (j1 < n) vr1 = *(const uint4*)(p.v + (tok0 + c0 + j1) * kD + rc);
+      }
+      int next_s = s, next_c0 = c0 + p.chunk;
+      if (next_c0 >= p.N) { next_s = s + p.n_pairs; next_c0 = 0; }
+      const bool has_next = next_s < p.streams && p.N > 0;
+      ChunkRegs nxt;
+      if (has_next) nxt = load_chunk_regs(p, (int64_t)next_s * p.N + next_c0, min(p.chunk, p.N - next_c0), tid);
+
+      // ================= a1: coefficients (both halves compute them identically) =================
+      // run by waves 3 and 2 while thread 0 awaits the partner (first used after that barrier)
+      // wave 0: one lane per column i of D (and U_i); wave 1: one lane per
+      // token j (A_j, E_j, F_j).  Gates are read as LDS broadcasts of
+      // (1 - alpha_m, eta_m) pairs; the recurrences stay in registers and
+      // run over all 64 steps with selects instead of branches.
+      auto coef_work = [&] {
+      if (w >= 2) {
+        const float2* pairs = (const float2*)(smem + OFF_COEF + COEF_PAIR);
+        if (w == 3) {
+          // column i = lane.  p = prod_{i<m<=j} eta_m from j = i on (0 before),
+          // d = D[j][i]; both recurrences run uniformly over all j, with p
+          // injected as 1 at j == i, so the loop has no branches.
+          const int i = lane;
+          const float thi = cf[COEF_THETA + i];
+          float di = 0.f, pr = 0.f, dlast = 0.f;
+#pragma unroll
+          for (int j = 0; j < kB; ++j) {
+            const float2 g = pairs[j];
+            pr = (j == i) ? 1.f : pr * g.y;
+            di = fmaf(g.x, di, thi * pr);
+            sDM[j * RSF + i] = di;
+            dlast = (j == n - 1) ? di : dlast;
+          }
+          const float ui = thi * pr;   // theta_i prod_{m>i} eta_m (padding has eta = 1)
+          cf[COEF_U + i] = ui;
+          cf[COEF_DN + i] = dlast;
+          const float mu = wave_max(fabsf(ui)), md = wave_max(fabsf(dlast));
+          int eu = 0, ed = 0;
+          if (mu > 0.f && mu < INFINITY) { (void)frexpf(mu, &eu); eu = -eu; }
+          if (md > 0.f && md < INFINITY) { (void)frexpf(md, &ed); ed = -ed; }
+          // weights scaled into (0.5, 1]: products with unit-size operands stay in fp16 range
+          ch[H16_WU + i] = (_Float16)ldexpf(ui, eu);
+          ch[H16_WD + i] = (_Float16)ldexpf(dlast, ed);
+          if (lane == 0) { ci[INT_EWU] = eu; ci[INT_EWD] = ed; }
+        } else {
+          // the running products are the same for every lane; lane j keeps
+          // their values after token j
+          const int j = lane;
+          float ar = 1.f, er = 1.f, fr = 0.f, a = 1.f, e = 1.f, f = 0.f;
+#pragma unroll
+          for (int m = 0; m < kB; ++m) {
+            const float2 g = pairs[m];
+            ar *= g.x;
+            er *= g.y;
+            fr = fmaf(g.x, fr, er);
+            const bool at = m == j;
+            a = at ? ar : a;
+            e = at ? er : e;
+            f = at ? fr : f;
+          }
+          cf[COEF_A + j] = a;
+          cf[COEF_E + j] = e;
+          cf[COEF_F + j] = f;
+        }
+      }
+      };
+
+      if (!handshake(seq + 2, coef_work)) { failed = true; break; }
+      if (has_next) stage_chunk_regs(smem + OFF_STAGE, nxt, tid);
+      staged = has_next;
+
+      // last chunk's y rows (the partner published them before this flag)
+      if (prev_row0 >= 0) finish_prev_y(par ^ 1u);
+
+      // ================= first-layer scores SC1 = D o (Q K^T): one 32x32 tile per wave =================
       f16v sc;
       {
         const int jt = w >> 1, it = w & 1;
@@ -498,35 +628,26 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
         am = wave_max(am);
         if (lane == 0) atomicMax((unsigned int*)&ci[INT_AMAX_SC1], __float_as_uint(am));
       }
-      // W2 copy for the backprop: [h_l][c] fp16 (the O partial buffer is free again)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          sRW[crow(r, lg) * RS + 32 * ct + lr] = (_Float16)ldexpf(ag_get(W2m[ct].r[r]), e2);
-
-      if (!handshake(seq + 1)) { failed = true; break; }
-
-      // last chunk's y rows (the partner published them before this flag)
-      if (prev_row0 >= 0) finish_prev_y(par ^ 1u);
 
       // ================= O = half 0 + half 1, Delta2 = O - V =================
       float d2v[2][8];
       {
         float am = 0.f;
+        float pvv[2][8];
+        xload8x2(xO_pt + par * kB * kD + (8 * w + rj) * kD + rc, xO_pt + par * kB * kD + (32 + 8 * w + rj) * kD + rc,
+                 pvv[0], pvv[1]);
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
           const int j = 32 * pass + 8 * w + rj;
-          const float* src = xO_pt + par * kB * kD + j * kD + rc;
-          float pv[8];
-#pragma unroll
-          for (int i = 0; i < 8; i += 2) xload2(src + i, pv[i], pv[i + 1]);
+          const float* pv = pvv[pass];
           if (j < n) {
-            const __hip_bfloat16* vr = p.v + (tok0 + c0 + j) * kD + rc;
+            const uint4 vu = pass ? vr1 : vr0;
+            const unsigned vw[4] = {vu.x, vu.y, vu.z, vu.w};
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
               const float o = half == 0 ? om[pass][i] + pv[i] : pv[i] + om[pass][i];
-              d2v[pass][i] = o - __bfloat162float(vr[i]);
+              const float vv = __uint_as_float((i & 1) ? (vw[i >> 1] & 0xffff0000u) : (vw[i >> 1] << 16));
+              d2v[pass][i] = o - vv;
             }
           } else {
 #pragma unroll
@@ -538,6 +659,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
         am = wave_max(am);
         if (lane == 0) atomicMax((unsigned int*)&ci[INT_AMAX_D2], __float_as_uint(am));
       }
+      __syncthreads();   // every wave's SC1 and Delta2 amax is in
       const int eSC = scale_exp(__uint_as_float((unsigned)ci[INT_AMAX_SC1]));
       {
         const int jt = w >> 1, it = w & 1;
@@ -545,7 +667,6 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
         for (int r = 0; r < 16; ++r)
           sSC1[(32 * jt + crow(r, lg)) * RS + 32 * it + lr] = (_Float16)ldexpf(sc[r], eSC);
       }
-      __syncthreads();
       const int eD2 = scale_exp(__uint_as_float((unsigned)ci[INT_AMAX_D2]));
 #pragma unroll
       for (int pass = 0; pass < 2; ++pass) {
@@ -625,6 +746,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
 
       const float An = cf[COEF_A + n - 1], En = cf[COEF_E + n - 1], Fn = cf[COEF_F + n - 1];
       const int ewU = ci[INT_EWU], ewD = ci[INT_EWD];
+      float m1n = 0.f, m2n = 0.f;
       // ================= a4, layer 1 (W1, S1 are not read again this chunk) =================
       // G1^T[c][h] = sum_j K[j][c] w_j Delta1[j][h]
 #pragma unroll
@@ -641,8 +763,11 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float w0 = ag_get(W1m[ct].r[r]), s0 = ag_get(S1m[ct].r[r]);
-          W1m[ct].r[r] = ag_put(An * w0 + Fn * s0 - ldexpf(gD[r], -(ewD + eD1)));
-          S1m[ct].r[r] = ag_put(En * s0 - ldexpf(gU[r], -(ewU + eD1)));
+          const float wn = An * w0 + Fn * s0 - ldexpf(gD[r], -(ewD + eD1));
+          const float sn = En * s0 - ldexpf(gU[r], -(ewU + eD1));
+          W1m[ct].r[r] = ag_put(wn);
+          S1m[ct].r[r] = ag_put(sn);
+          m1n = fmaxf(m1n, fmaxf(fabsf(wn), fabsf(sn)));
         }
       }
 
@@ -699,9 +824,15 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
             for (int st = 0; st < 2; ++st)
               acc3 = mfma(lds_frag(sD2T + (32 * ct + lr) * RS, 32 * it + 16 * st, lg), DPh[it][jt][st], acc3);
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            sRF[(32 * ct + crow(r, lg)) * RSF + 32 * jt + lr] =
-                ldexpf(aj * accW[r] + fj * accS[r], -(e2 + eH1[jt])) - ldexpf(acc3[r], -(eD2 + eDP[jt]));
+          for (int g4 = 0; g4 < 4; ++g4) {   // rows c = 32ct + 8g4 + 4lg + 0..3 are consecutive
+            f4v o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int r = 4 * g4 + q;
+              o[q] = ldexpf(aj * accW[r] + fj * accS[r], -(e2 + eH1[jt])) - ldexpf(acc3[r], -(eD2 + eDP[jt]));
+            }
+            *(f4v*)(sRF + (32 * jt + lr) * RSF + 32 * ct + 8 * g4 + 4 * lg) = o;
+          }
         }
       }
 
@@ -720,8 +851,11 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float w0 = ag_get(W2m[ct].r[r]), s0 = ag_get(S2m[ct].r[r]);
-          W2m[ct].r[r] = ag_put(An * w0 + Fn * s0 - ldexpf(gD[r], -(ewD + eA1 + eD2)));
-          S2m[ct].r[r] = ag_put(En * s0 - ldexpf(gU[r], -(ewU + eA1 + eD2)));
+          const float wn = An * w0 + Fn * s0 - ldexpf(gD[r], -(ewD + eA1 + eD2));
+          const float sn = En * s0 - ldexpf(gU[r], -(ewU + eA1 + eD2));
+          W2m[ct].r[r] = ag_put(wn);
+          S2m[ct].r[r] = ag_put(sn);
+          m2n = fmaxf(m2n, fmaxf(fabsf(wn), fabsf(sn)));
         }
       }
       __syncthreads();
@@ -735,16 +869,22 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
 #pragma unroll
         for (int src = 0; src < kWaves; ++src) {
           const float* rp = (const float*)(smem + OFF_WAVE + src * kWaveRegion);
+          const float* ps = rp + (32 * (1 - half) + jr) * RSF + cc;
+          const float* pm = rp + (32 * half + jr) * RSF + cc;
+          const f4v s0 = *(const f4v*)ps, s1 = *(const f4v*)(ps + 4);
+          const f4v m0 = *(const f4v*)pm, m1v = *(const f4v*)(pm + 4);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            send[i] += rp[(cc + i) * RSF + 32 * (1 - half) + jr];
-            ymine[i] += rp[(cc + i) * RSF + 32 * half + jr];
+          for (int i = 0; i < 4; ++i) {
+            send[i] += s0[i]; send[4 + i] += s1[i];
+            ymine[i] += m0[i]; ymine[4 + i] += m1v[i];
           }
         }
         float* dst = xY_me + par * 32 * kD + jr * kD + cc;
 #pragma unroll
         for (int i = 0; i < 8; i += 2) xstore2(dst + i, send[i], send[i + 1]);
       }
+      m1 = m1n;
+      m2 = m2n;
       prev_row0 = tok0 + c0;
       prev_n = n;
       ++seq;
@@ -778,7 +918,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
 
   // the last chunk's y rows: one more handshake (a flag value no chunk uses)
   if (!failed && prev_row0 >= 0) {
-    if (handshake(seq + 1)) finish_prev_y((seq - 1) & 1u);
+    if (handshake(seq + 2, nothing)) finish_prev_y((seq - 1) & 1u);
   }
 }
 
