@@ -25,6 +25,38 @@ PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 
 
+# dominant kernel of each path: (kernel function, its source under csrc/)
+DOMINANT_KERNEL = {"mlp2_d64_h256_mfma": ("mlp2_pair_kernel", "tm_mlp2.hip"),
+                   "generic_f32": ("generic_kernel", "tm_generic.hip")}
+
+
+def measured_traffic(kernel_path, workload):
+    """HBM bytes per launch of the path's dominant kernel on ``workload``, from
+    the committed byte-counter summary, or None when there is none or it was
+    taken on another version of the kernel source."""
+    import hashlib
+    if kernel_path not in DOMINANT_KERNEL:
+        return None
+    kernel, src = DOMINANT_KERNEL[kernel_path]
+    summary = os.path.join(ROOT, "profiles", f"{kernel}__{workload}__hbm_traffic.txt")
+    if not os.path.exists(summary):
+        return None
+    with open(os.path.join(ROOT, "test_learned_neural_amd", "csrc", src), "rb") as fh:
+        digest = hashlib.sha256(fh.read()).hexdigest()
+    fields = {}
+    with open(summary) as fh:
+        for line in fh:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.split()[0] if v.split() else ""
+    if fields.get("kernel_source_sha256") != digest:
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def algorithmic_work(cfg):
     """(FLOPs, HBM bytes) per memory token (one token of one stream) of the
     chunked method: key forward P, backprop P - d*n_1, two weighted
@@ -50,6 +82,9 @@ def main():
     ap.add_argument("--force-generic", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES (three times), to scale "
+                         "HBM byte counters, and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the memory's (batch, head) streams are independent "
@@ -58,6 +93,15 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        src = torch.empty(args.calibrate_copy, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": args.calibrate_copy, "copies": 3}))
+        return
 
     from test_learned_neural_amd import titans_mem as tmm
     from test_learned_neural_amd import workloads as wl
@@ -151,6 +195,8 @@ def main():
         print(f"[bench] cpu oracle: {cpu['value']:.3g} memory-tokens/s ({cpu['sample']})", file=sys.stderr,
               flush=True)
 
+    kernel_path_name = {tmm.PATH_GENERIC_F32: "generic_f32",
+                        tmm.PATH_MLP2_D64_H256: "mlp2_d64_h256_mfma"}.get(path, str(path))
     out = {
         "metric": "memory tokens/sec (retrieve + chunked update), 1 GPU",
         "value": value,
@@ -166,11 +212,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": B, "H": H, "N": N, "d": d, "hidden": cfg.hidden,
                    "n_layers": cfg.n_layers, "chunk": cfg.chunk, "io": cfg.io,
-                   "kernel_path": {tmm.PATH_GENERIC_F32: "generic_f32",
-                                   tmm.PATH_MLP2_D64_H256: "mlp2_d64_h256_mfma"}.get(path, str(path)),
+                   "kernel_path": kernel_path_name,
                    "sequence_tokens_per_s": B * N / (ms_per_step / 1e3)},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None,
+                     "frac": achieved / peak, "traffic": measured_traffic(kernel_path_name, cfg.name),
                      "algorithmic_flops_per_launch": flops_tok * mem_tokens,
                      "avg_launch_ms": avg_launch_s * 1e3,
                      "hbm_achieved_gbs": bytes_tok * mem_tokens / avg_launch_s / 1e9,

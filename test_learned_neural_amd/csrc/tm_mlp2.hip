@@ -106,8 +106,8 @@ static_assert(kA1Bytes + kHW * RS * 2 <= kWaveRegion, "A1 copy + W2 copy");
 constexpr int INT_AMAX_SC1 = 0, INT_AMAX_D2 = 1, INT_EWU = 2, INT_EWD = 3, INT_FAIL = 4;
 
 // ---- global workspace layout, per pair (bytes) ----
-constexpr int64_t kXO = 2 * 2 * kB * kD * 4;         // [half][parity][64][64] fp32
-constexpr int64_t kXY = 2 * 2 * 32 * kD * 4;         // [half][parity][32][64] fp32
+constexpr int64_t kXO = 2 * 2 * kB * kD * 4;         // [half][parity] x 64 x 64 fp32, thread-major
+constexpr int64_t kXY = 2 * 2 * 32 * kD * 4;         // [half][parity] x 32 x 64 fp32, thread-major
 constexpr int64_t kPairBytes = kXO + kXY;
 constexpr int64_t kFlagStride = 128;                  // bytes between flags (own cache line)
 
@@ -194,20 +194,24 @@ __device__ __forceinline__ float sigmoidf_(float z) {
 // s_waitcnt vmcnt(0) before each flag store.  (An L2-local variant using sc0
 // loads was tried: on gfx950 a poller then kept reading a stale flag, so the
 // exchange stays agent-coherent.)
-__device__ __forceinline__ void xstore2(float* p, float a, float b) {
+// The exchange buffers are thread-major: 8-byte element e of thread t sits
+// at (e * kThreads + t) * 8 bytes, so each store or load instruction of a
+// wave covers 512 contiguous bytes (whole lines: an agent-coherent store
+// writes through L2, and scattered 8-byte pieces would each cost a sector).
+// Every thread reads back exactly the elements the same thread of the
+// partner wrote.
+__device__ __forceinline__ void xstore2(float* base, int e, int t, float a, float b) {
   const unsigned long long v = (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
-  __hip_atomic_store((unsigned long long*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((unsigned long long*)base + (e * kThreads + t), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// 8 consecutive floats at each of p0 and p1
-__device__ __forceinline__ void xload8x2(const float* p0, const float* p1, float* a, float* b) {
+// 8 floats = elements e0 .. e0+3 of thread t
+__device__ __forceinline__ void xload8(const float* base, int e0, int t, float* a) {
 #pragma unroll
-  for (int i = 0; i < 8; i += 2) {
-    unsigned long long v = __hip_atomic_load((const unsigned long long*)(p0 + i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    a[i] = __uint_as_float((unsigned)v);
-    a[i + 1] = __uint_as_float((unsigned)(v >> 32));
-    v = __hip_atomic_load((const unsigned long long*)(p1 + i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    b[i] = __uint_as_float((unsigned)v);
-    b[i + 1] = __uint_as_float((unsigned)(v >> 32));
+  for (int i = 0; i < 4; ++i) {
+    const unsigned long long v = __hip_atomic_load((const unsigned long long*)base + ((e0 + i) * kThreads + t),
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    a[2 * i] = __uint_as_float((unsigned)v);
+    a[2 * i + 1] = __uint_as_float((unsigned)(v >> 32));
   }
 }
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
@@ -367,9 +371,8 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
   auto finish_prev_y = [&](unsigned parity) {
     // partner's partial for my rows of the previous chunk, then the fixed-order sum
     const int jr = tid >> 3, cc = (tid & 7) * 8;
-    const float* src = xY_pt + parity * 32 * kD + jr * kD + cc;
-    float pv[8], unused[8];
-    xload8x2(src, src, pv, unused);
+    float pv[8];
+    xload8(xY_pt + parity * 32 * kD, 0, tid, pv);
     const int j = 32 * half + jr;
     if (j < prev_n) {
       __hip_bfloat16* yr = p.y + (prev_row0 + j) * kD + cc;
@@ -516,9 +519,8 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       const unsigned par = seq & 1u;
 #pragma unroll
       for (int pass = 0; pass < 2; ++pass) {
-        float* dst = xO_me + par * kB * kD + (32 * pass + 8 * w + rj) * kD + rc;
 #pragma unroll
-        for (int i = 0; i < 8; i += 2) xstore2(dst + i, om[pass][i], om[pass][i + 1]);
+        for (int i = 0; i < 8; i += 2) xstore2(xO_me + par * kB * kD, 4 * pass + i / 2, tid, om[pass][i], om[pass][i + 1]);
       }
 
       // ---- work that does not need the partner: W2 copy, prefetch ----
@@ -634,8 +636,8 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       {
         float am = 0.f;
         float pvv[2][8];
-        xload8x2(xO_pt + par * kB * kD + (8 * w + rj) * kD + rc, xO_pt + par * kB * kD + (32 + 8 * w + rj) * kD + rc,
-                 pvv[0], pvv[1]);
+        xload8(xO_pt + par * kB * kD, 0, tid, pvv[0]);   // rows 8w + rj, columns rc .. rc+7
+        xload8(xO_pt + par * kB * kD, 4, tid, pvv[1]);   // rows 32 + 8w + rj
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
           const int j = 32 * pass + 8 * w + rj;
@@ -879,9 +881,8 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
             ymine[i] += m0[i]; ymine[4 + i] += m1v[i];
           }
         }
-        float* dst = xY_me + par * 32 * kD + jr * kD + cc;
 #pragma unroll
-        for (int i = 0; i < 8; i += 2) xstore2(dst + i, send[i], send[i + 1]);
+        for (int i = 0; i < 8; i += 2) xstore2(xY_me + par * 32 * kD, i / 2, tid, send[i], send[i + 1]);
       }
       m1 = m1n;
       m2 = m2n;
