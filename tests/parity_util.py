@@ -109,3 +109,30 @@ def live_length(w_norm_traj, chunk, floor):
     """Last token at which the reference ||W_t||_F stays above the floor."""
     alive = np.nonzero(w_norm_traj > floor)[0]
     return 0 if len(alive) == 0 else int((alive[-1] + 1) * chunk)
+
+
+TOKEN_KEYS = ("k", "v", "q", "alpha", "eta", "theta")
+
+
+def prefix_inputs(inp, n):
+    """The first n tokens of every stream (the generator draws a prefix
+    bit-identically, so this equals make_inputs(..., n_tokens=n))."""
+    return {k: (np.ascontiguousarray(a[:, :n]) if k in TOKEN_KEYS else a) for k, a in inp.items()}
+
+
+def y_errors(cfg, inp, y_gpu, y_ref):
+    """Per-stream relative y error with the y floor."""
+    vin = wl.io_to_f64(inp["v"], cfg.io)
+    return np.array([rel_err(y_gpu[s], y_ref[s], 1e-30 * max(1.0, float(np.linalg.norm(vin[s]))))
+                     for s in range(len(y_ref))])
+
+
+def state_below_floor(cfg, inp, W_gpu, S_gpu, tol):
+    """For a reference state that is exactly zero: the relative error against
+    it, ||X_gpu|| / floor, per stream (W and S), must stay under tol."""
+    worst = 0.0
+    for s in range(len(W_gpu)):
+        fw = 1e-30 * max(1.0, float(np.linalg.norm(inp["W0"][s].astype(np.float64))))
+        worst = max(worst, rel_err(W_gpu[s], np.zeros_like(W_gpu[s]), fw),
+                    rel_err(S_gpu[s], np.zeros_like(S_gpu[s]), fw))
+    return worst < tol, worst

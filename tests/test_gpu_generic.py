@@ -8,8 +8,8 @@ import numpy as np
 import pytest
 
 from test_learned_neural_amd import workloads as wl
-from parity_util import (TOL, rel_err, run_gpu, run_oracle, stream_errors, to_device, window_errors,
-                         y_to_f64)
+from parity_util import (TOL, prefix_inputs, rel_err, run_gpu, run_oracle, state_below_floor, stream_errors,
+                         to_device, window_errors, y_errors, y_to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -60,6 +60,45 @@ def test_generic_shapes_and_ragged_chunks(L, d, h, N, chunk, io):
     inp = wl.make_inputs(cfg)
     out = run_gpu(cfg, to_device(cfg, inp), force_generic=True)
     _check(cfg, inp, out, run_oracle(cfg, inp), TOL["f32"], windows=False)
+
+
+def test_deep_memory_full_length():
+    """The deep-memory workload (4-layer MLP, d = 128, hidden 512, 4 x 8
+    streams, 32768 tokens, chunk 128) at full size on the path that serves it.
+    The first 2048 tokens of every stream are checked against the oracle's
+    run on that prefix (prefix inputs are drawn bit-identically; outputs are
+    causal); by the end the fp64 state has decayed into the exactly-zero
+    fixed point, so the final W and S must be below the error floor."""
+    import torch
+    from test_learned_neural_amd import titans_mem as tmm
+    cfg = wl.CONFIGS[5]
+    desc = tmm.make_desc(cfg.B, cfg.H, cfg.N, cfg.d, cfg.hidden, cfg.n_layers, cfg.io)
+    assert tmm.select_path(desc, cfg.chunk) == tmm.PATH_GENERIC_F32
+    inp = wl.make_inputs(cfg, workers=16)
+    y, W, S = run_gpu(cfg, to_device(cfg, inp))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all()) and bool(torch.isfinite(W).all()) and bool(torch.isfinite(S).all())
+    n_pre = 2048
+    pre = cfg.with_(N=n_pre)
+    sub = prefix_inputs(inp, n_pre)
+    y_ref = run_oracle(pre, sub, threads=16)[0]
+    yg = y_to_f64(pre, y[:, :, :n_pre].contiguous())
+    ey = y_errors(pre, sub, yg, y_ref)
+    we = window_errors(pre, sub, yg, y_ref)
+    ok, es = state_below_floor(cfg, inp, W.reshape(-1, cfg.param_count).cpu().double().numpy(),
+                               S.reshape(-1, cfg.param_count).cpu().double().numpy(), TOL["f32"])
+    print(f"{cfg.name}: prefix {n_pre} max e_y {ey.max():.2e} window_y {we:.2e}; final state vs zero {es:.2e}",
+          flush=True)
+    assert np.all(ey < TOL["bf16"]) and we < TOL["bf16"]
+    assert ok, es
+
+
+def test_generic_deep_memory_prefix_all_streams():
+    """Deep memory, 2048-token prefix, all 32 streams, y, W and S."""
+    cfg = wl.CONFIGS[5].with_(N=2048)
+    inp = wl.make_inputs(cfg, workers=16)
+    out = run_gpu(cfg, to_device(cfg, inp))
+    _check(cfg, inp, out, run_oracle(cfg, inp, threads=16), TOL["f32"])
 
 
 def test_generic_read_chunk_start():

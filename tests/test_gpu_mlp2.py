@@ -13,7 +13,8 @@ import numpy as np
 import pytest
 
 from test_learned_neural_amd import workloads as wl
-from parity_util import (TOL, run_gpu, run_oracle, stream_errors, to_device, window_errors, y_to_f64)
+from parity_util import (TOL, prefix_inputs, run_gpu, run_oracle, state_below_floor, stream_errors, to_device,
+                         window_errors, y_errors, y_to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,23 +85,53 @@ def test_mlp2_matches_generic_kernel():
     torch.cuda.synchronize()
 
 
-def test_mlp2_full_length_config3_sampled_streams():
-    """The full headline workload (8 x 16 streams, 16384 tokens, chunk 64) in the
-    launch configuration the benchmark times; the oracle checks 4 streams."""
+def test_mlp2_full_length_headline_all_streams():
+    """The headline workload (8 x 16 streams, 16384 tokens, chunk 64) at full
+    size, in the launch configuration the benchmark times, every stream
+    against the oracle (y, W, S; the state has decayed below the floor by the
+    end, so y windows and the prefix test carry the non-vacuous part)."""
     cfg = wl.CONFIGS[3]
     inp = wl.make_inputs(cfg, workers=16)
     out = run_gpu(cfg, to_device(cfg, inp))
-    idx = [0, 37, 90, 127]
-    ids = [wl.stream_ids(cfg)[i] for i in idx]
-    sub = wl.make_inputs(cfg, streams=ids)
-    ref = run_oracle(cfg, sub, threads=4)
-    yg, Wg, Sg = _np(cfg, out)
-    assert np.all(np.isfinite(yg)) and np.all(np.isfinite(Wg)) and np.all(np.isfinite(Sg))
-    e = stream_errors(cfg, sub, yg, Wg, Sg, *ref, idx=idx)
-    we = window_errors(cfg, sub, yg, ref[0], idx=idx)
-    print(f"config 3 full, sampled streams {idx}: max e_y {e[:, 0].max():.2e} e_W {e[:, 1].max():.2e} "
-          f"e_S {e[:, 2].max():.2e} window_y {we:.2e}", flush=True)
-    assert np.all(e < TOL["bf16"]) and we < TOL["bf16"]
+    _check(cfg, inp, out, run_oracle(cfg, inp, threads=16))
+
+
+def test_mlp2_full_length_32_streams():
+    """The 4 x 8-stream, 4096-token workload at full size against the oracle."""
+    cfg = wl.CONFIGS[2]
+    inp = wl.make_inputs(cfg, workers=16)
+    out = run_gpu(cfg, to_device(cfg, inp))
+    _check(cfg, inp, out, run_oracle(cfg, inp, threads=16))
+
+
+def test_mlp2_million_token_streams_full_length():
+    """The streaming workload (16 streams x 1,048,576 tokens, chunk 64) in one
+    launch.  The first 16,384 tokens of every stream are checked against the
+    oracle's run on that prefix: the inputs of a prefix are drawn
+    bit-identically and each output depends only on earlier tokens.  Beyond
+    that the fp64 memory decays into the exactly-zero state, a fixed point of
+    the bias-free MLP (pinned on the oracle), so the final W and S must be
+    below the error floor; every output must be finite."""
+    import torch
+    cfg = wl.CONFIGS[4]
+    inp = wl.make_inputs(cfg, workers=16)
+    dev = to_device(cfg, inp)
+    y, W, S = run_gpu(cfg, dev)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all()) and bool(torch.isfinite(W).all()) and bool(torch.isfinite(S).all())
+    n_pre = 16384
+    pre = cfg.with_(N=n_pre)
+    sub = prefix_inputs(inp, n_pre)
+    y_ref = run_oracle(pre, sub, threads=16)[0]
+    yg = y_to_f64(pre, y[:, :, :n_pre].contiguous())
+    ey = y_errors(pre, sub, yg, y_ref)
+    we = window_errors(pre, sub, yg, y_ref)
+    ok, es = state_below_floor(cfg, inp, W.reshape(-1, cfg.param_count).cpu().double().numpy(),
+                               S.reshape(-1, cfg.param_count).cpu().double().numpy(), TOL["bf16"])
+    print(f"{cfg.name}: prefix {n_pre} max e_y {ey.max():.2e} window_y {we:.2e}; final state vs zero {es:.2e}",
+          flush=True)
+    assert np.all(ey < TOL["bf16"]) and we < TOL["bf16"]
+    assert ok, es
 
 
 def test_mlp2_empty_inplace_deterministic():

@@ -330,6 +330,24 @@ def test_alpha_one_clears_memory(oracle_mod, L, d, h):
     assert not Wo.any() and not So.any() and not y.any()
 
 
+@pytest.mark.parametrize("L,d,h", [(2, 4, 8), (4, 3, 6)])
+def test_zero_state_is_a_fixed_point_of_the_mlp(oracle_mod, L, d, h):
+    """A bias-free MLP memory (mer.dev 3.1 "Memory Architecture", no biases)
+    at W = S = 0 has zero gradient for any (k, v): every layer's gradient
+    carries either an activation SiLU(0) = 0 or a delta back-propagated
+    through a zero matrix (checked here with torch autograd).  So zero
+    state stays exactly zero under any gates, and every read is zero --
+    the state the long workloads decay into."""
+    rng = np.random.default_rng(23)
+    N, chunk = 40, 6
+    P = oracle_mod.param_count(d, h, L)
+    k, v, q = rand_stream(rng, N, d, P)
+    assert not autograd_grad(np.zeros(P), widths_of(d, h, L), k[0], v[0]).any()
+    a, e, t = rng.uniform(0, 1, N), rng.uniform(0, 1, N), rng.uniform(0, 1, N)
+    y, Wo, So = run_oracle(oracle_mod, k, v, q, a, e, t, np.zeros(P), np.zeros(P), d, h, L, chunk)
+    assert not Wo.any() and not So.any() and not y.any()
+
+
 # ----------------------------------------------------------------------------
 # P7/P8/P9: attention special cases (mer.dev section 2.1)
 # ----------------------------------------------------------------------------
