@@ -172,10 +172,59 @@ __device__ __forceinline__ h8 state_frag(const Tile& t, int s, int e) {
   return r;
 }
 
+// ---- cross-lane helpers on DPP (no LDS traffic); call with all 64 lanes active ----
+// DPP controls: quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E, row_shr:n = 0x110 + n,
+// row_mirror = 0x140, row_half_mirror = 0x141, row_bcast:15 = 0x142, row_bcast:31 = 0x143
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xf, 0xf, false));
+}
+// lanes whose DPP source is out of range (or whose row is masked off) get `ident`
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ float dpp_or(float ident, float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(ident), __float_as_int(x), kCtrl, kRowMask, 0xf, false));
+}
+__device__ __forceinline__ float lane_value(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// maximum over the wave, returned uniformly
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  v = fmaxf(v, dpp_mov<0x141>(v));
+  v = fmaxf(v, dpp_mov<0x140>(v));   // every lane of a row of 16 holds the row's maximum
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
+
+// inclusive prefix product over the lanes (lane l: x_0 * ... * x_l)
+__device__ __forceinline__ float wave_prefix_prod(float x) {
+  x *= dpp_or<0x111>(1.f, x);
+  x *= dpp_or<0x112>(1.f, x);
+  x *= dpp_or<0x114>(1.f, x);
+  x *= dpp_or<0x118>(1.f, x);
+  x *= dpp_or<0x142, 0xa>(1.f, x);
+  x *= dpp_or<0x143, 0xc>(1.f, x);
+  return x;
+}
+
+// inclusive scan of the affine maps f_l(u) = a_l u + b_l over the lanes:
+// on return lane l holds f_l o ... o f_0 as (a, b), i.e. a = a_0 ... a_l and
+// b = the value of u_l = a_l u_{l-1} + b_l started from u_{-1} = 0
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ void affine_step(float& a, float& b) {
+  const float a2 = dpp_or<kCtrl, kRowMask>(1.f, a);
+  const float b2 = dpp_or<kCtrl, kRowMask>(0.f, b);
+  b = fmaf(a, b2, b);
+  a *= a2;
+}
+__device__ __forceinline__ void wave_affine_scan(float& a, float& b) {
+  affine_step<0x111>(a, b);
+  affine_step<0x112>(a, b);
+  affine_step<0x114>(a, b);
+  affine_step<0x118>(a, b);
+  affine_step<0x142, 0xa>(a, b);
+  affine_step<0x143, 0xc>(a, b);
 }
 
 // power-of-two scale exponent bringing amax into [2^13, 2^14)
@@ -547,29 +596,35 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
 
       // ================= a1: coefficients (both halves compute them identically) =================
       // run by waves 3 and 2 while thread 0 awaits the partner (first used after that barrier)
-      // wave 0: one lane per column i of D (and U_i); wave 1: one lane per
-      // token j (A_j, E_j, F_j).  Gates are read as LDS broadcasts of
-      // (1 - alpha_m, eta_m) pairs; the recurrences stay in registers and
-      // run over all 64 steps with selects instead of branches.
+      // Lane m of both waves holds token m's (1 - alpha_m, eta_m).
       auto coef_work = [&] {
       if (w >= 2) {
-        const float2* pairs = (const float2*)(smem + OFF_COEF + COEF_PAIR);
+        const float2 gl = ((const float2*)(smem + OFF_COEF + COEF_PAIR))[lane];
         if (w == 3) {
-          // column i = lane.  p = prod_{i<m<=j} eta_m from j = i on (0 before),
-          // d = D[j][i]; both recurrences run uniformly over all j, with p
-          // injected as 1 at j == i, so the loop has no branches.
+          // wave 3: column i = lane of D, one row j per step (the step's gates
+          // broadcast with readlane).  t = theta_i prod_{i<m<=j} eta_m, started
+          // at j == i by adding theta_i to a zero product, and
+          // D[j][i] = (1 - alpha_j) D[j-1][i] + t: one fma per step on each of
+          // the two loop-carried values.
+          const int glx = __float_as_int(gl.x), gly = __float_as_int(gl.y);
           const int i = lane;
           const float thi = cf[COEF_THETA + i];
-          float di = 0.f, pr = 0.f, dlast = 0.f;
+          float di = 0.f, t = 0.f;
+          int iv = i;
 #pragma unroll
           for (int j = 0; j < kB; ++j) {
-            const float2 g = pairs[j];
-            pr = (j == i) ? 1.f : pr * g.y;
-            di = fmaf(g.x, di, thi * pr);
+            // opaque copy of the lane index: keeps the 64 compares in the loop
+            // (hoisted, their masks would be spilled and reloaded every step)
+            asm volatile("" : "+v"(iv));
+            const float ga = __int_as_float(__builtin_amdgcn_readlane(glx, j));
+            const float ge = __int_as_float(__builtin_amdgcn_readlane(gly, j));
+            const float inj = (j == iv) ? thi : 0.f;
+            t = fmaf(ge, t, inj);
+            di = fmaf(ga, di, t);
             sDM[j * RSF + i] = di;
-            dlast = (j == n - 1) ? di : dlast;
           }
-          const float ui = thi * pr;   // theta_i prod_{m>i} eta_m (padding has eta = 1)
+          const float ui = t;   // theta_i prod_{m>i} eta_m (padding has eta = 1)
+          const float dlast = sDM[(n - 1) * RSF + i];   // this wave's own store above
           cf[COEF_U + i] = ui;
           cf[COEF_DN + i] = dlast;
           const float mu = wave_max(fabsf(ui)), md = wave_max(fabsf(dlast));
@@ -581,24 +636,15 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
           ch[H16_WD + i] = (_Float16)ldexpf(dlast, ed);
           if (lane == 0) { ci[INT_EWU] = eu; ci[INT_EWD] = ed; }
         } else {
-          // the running products are the same for every lane; lane j keeps
-          // their values after token j
-          const int j = lane;
-          float ar = 1.f, er = 1.f, fr = 0.f, a = 1.f, e = 1.f, f = 0.f;
-#pragma unroll
-          for (int m = 0; m < kB; ++m) {
-            const float2 g = pairs[m];
-            ar *= g.x;
-            er *= g.y;
-            fr = fmaf(g.x, fr, er);
-            const bool at = m == j;
-            a = at ? ar : a;
-            e = at ? er : e;
-            f = at ? fr : f;
-          }
-          cf[COEF_A + j] = a;
-          cf[COEF_E + j] = e;
-          cf[COEF_F + j] = f;
+          // wave 2: lane j = token j.  E_j by a prefix product of eta, then
+          // (A_j, F_j) by a prefix scan of the maps u -> (1 - alpha_j) u + E_j
+          // (A_j is the scan's product part, F_j its value from F_{-1} = 0)
+          const float e = wave_prefix_prod(gl.y);
+          float a = gl.x, f = e;
+          wave_affine_scan(a, f);
+          cf[COEF_A + lane] = a;
+          cf[COEF_E + lane] = e;
+          cf[COEF_F + lane] = f;
         }
       }
       };
