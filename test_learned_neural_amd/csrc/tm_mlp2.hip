@@ -150,15 +150,16 @@ __device__ __forceinline__ h8 hmul(h8 a, h8 b) { return a * b; }
 
 // The fp32 state lives in accumulation registers (AGPRs); VALU reaches it
 // only through these moves, which keeps the architectural VGPRs for the
-// chunk's working set.
+// chunk's working set.  They are plain register moves (not volatile), so
+// the scheduler may place them freely.
 __device__ __forceinline__ float ag_get(float a) {
   float v;
-  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  asm("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
   return v;
 }
 __device__ __forceinline__ float ag_put(float v) {
   float a;
-  asm volatile("v_accvgpr_write_b32 %0, %1" : "=a"(a) : "v"(v));
+  asm("v_accvgpr_write_b32 %0, %1" : "=a"(a) : "v"(v));
   return a;
 }
 struct Tile {   // one 32x32 fp32 accumulator tile of the state
@@ -610,15 +611,15 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
           const int i = lane;
           const float thi = cf[COEF_THETA + i];
           float di = 0.f, t = 0.f;
-          int iv = i;
 #pragma unroll
           for (int j = 0; j < kB; ++j) {
-            // opaque copy of the lane index: keeps the 64 compares in the loop
-            // (hoisted, their masks would be spilled and reloaded every step)
-            asm volatile("" : "+v"(iv));
             const float ga = __int_as_float(__builtin_amdgcn_readlane(glx, j));
             const float ge = __int_as_float(__builtin_amdgcn_readlane(gly, j));
-            const float inj = (j == iv) ? thi : 0.f;
+            // theta_i in lane j only: a select on the constant lane mask 1 << j
+            // (a lane-index compare would be hoisted out of the chunk loop as
+            // 64 live masks)
+            float inj;
+            asm("v_cndmask_b32_e64 %0, 0, %1, %2" : "=v"(inj) : "v"(thi), "s"(1ull << j));
             t = fmaf(ge, t, inj);
             di = fmaf(ga, di, t);
             sDM[j * RSF + i] = di;
