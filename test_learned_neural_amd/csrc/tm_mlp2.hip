@@ -236,6 +236,25 @@ __device__ __forceinline__ int scale_exp(float amax) {
   return 14 - e;
 }
 
+// 2^-k as a float multiplier: exact rescaling (same result as ldexpf(x, -k))
+// while 2^-k is a normal float, i.e. k <= 126; beyond that the factor
+// flushes towards zero (scaled values far below any tolerance floor).  k is
+// clamped below so that the factor stays finite.
+__device__ __forceinline__ float pow2neg(int k) { return ldexpf(1.f, -max(k, -126)); }
+
+// per-token factors of the retrieval operands: (A_j, F_j) scaled by a
+// common power of two 2^s so that the larger lies in (0.5, 1] (fp16 keeps
+// both with 11 significant bits); s is returned for the unscaling
+__device__ __forceinline__ void token_factors(float a, float f, _Float16& ah, _Float16& fh, int& s) {
+  const float m = fmaxf(fabsf(a), fabsf(f));
+  int e = 0;
+  if (m > 0.f && m < INFINITY) (void)frexpf(m, &e);
+  s = -e;
+  ah = (_Float16)ldexpf(a, s);
+  fh = (_Float16)ldexpf(f, s);
+}
+__device__ __forceinline__ h8 hscale(h8 x, _Float16 c) { return x * c; }
+
 __device__ __forceinline__ float sigmoidf_(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
@@ -760,37 +779,52 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       }
 
       // ================= a5 layer 1: Zq1^T = W1 (A q)^T + S1 (F q)^T - Delta1^T SC1^T (rows h, cols j) =================
+      // One accumulator per token tile: the query fragment of token j (lane
+      // column) is scaled by A_j 2^s_j for the W1 product and by F_j 2^s_j for
+      // the S1 product; W1 and S1 fragments are converted once for both tiles.
       h8 H1h[2][2];
       int eH1[2];
+      {
+        _Float16 ajh[2], fjh[2];
+        int sj[2];
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        // per-token A_j, F_j (lane = token) applied to fp32 accumulators
-        const float aj = cf[COEF_A + 32 * jt + lr], fj = cf[COEF_F + 32 * jt + lr];
-        f16v accW = {}, accS = {}, acc3 = {};
+        for (int jt = 0; jt < 2; ++jt)
+          token_factors(cf[COEF_A + 32 * jt + lr], cf[COEF_F + 32 * jt + lr], ajh[jt], fjh[jt], sj[jt]);
+        f16v accZ[2] = {};
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
-            const h8 qf = lds_frag(sQ + (32 * jt + lr) * RS, 32 * ct + 16 * st, lg);
-            accW = mfma(state_frag(W1m[ct], st, e1), qf, accW);
-            accS = mfma(state_frag(S1m[ct], st, e1), qf, accS);
+            const h8 wf = state_frag(W1m[ct], st, e1), sf = state_frag(S1m[ct], st, e1);
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) {
+              const h8 qf = lds_frag(sQ + (32 * jt + lr) * RS, 32 * ct + 16 * st, lg);
+              accZ[jt] = mfma(wf, hscale(qf, ajh[jt]), accZ[jt]);
+              accZ[jt] = mfma(sf, hscale(qf, fjh[jt]), accZ[jt]);
+            }
           }
+        const float c3 = pow2neg(eD1 + eSC);
 #pragma unroll
-        for (int it = 0; it < 2; ++it)
+        for (int jt = 0; jt < 2; ++jt) {
+          f16v acc3 = {};
 #pragma unroll
-          for (int st = 0; st < 2; ++st)
-            acc3 = mfma(D1h[it][st], lds_frag(sSC1 + (32 * jt + lr) * RS, 32 * it + 16 * st, lg), acc3);
-        f16v Hf;
-        float am = 0.f;
+          for (int it = 0; it < 2; ++it)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float z = ldexpf(aj * accW[r] + fj * accS[r], -e1) - ldexpf(acc3[r], -(eD1 + eSC));
-          Hf[r] = z * sigmoidf_(z);
-          am = fmaxf(am, fabsf(Hf[r]));
+            for (int st = 0; st < 2; ++st)
+              acc3 = mfma(D1h[it][st], lds_frag(sSC1 + (32 * jt + lr) * RS, 32 * it + 16 * st, lg), acc3);
+          const float cz = pow2neg(e1 + sj[jt]);
+          f16v Hf;
+          float am = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float z = fmaf(acc3[r], -c3, accZ[jt][r] * cz);
+            Hf[r] = z * sigmoidf_(z);
+            am = fmaxf(am, fabsf(Hf[r]));
+          }
+          eH1[jt] = scale_exp(wave_max(am));
+#pragma unroll
+          for (int r = 0; r < 16; ++r) H1h[jt][r >> 3][r & 7] = (_Float16)ldexpf(Hf[r], eH1[jt]);
         }
-        eH1[jt] = scale_exp(wave_max(am));
-#pragma unroll
-        for (int r = 0; r < 16; ++r) H1h[jt][r >> 3][r & 7] = (_Float16)ldexpf(Hf[r], eH1[jt]);
       }
 
       const float An = cf[COEF_A + n - 1], En = cf[COEF_E + n - 1], Fn = cf[COEF_F + n - 1];
@@ -855,32 +889,45 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       // ================= a5 layer 2: y^T partial = W2 (A H1)^T + S2 (F H1)^T - Delta2^T (D o P)^T =================
       // tiles go straight to this wave's region (fp32 [c][j]): the wave is past
       // its last read of its A1 and W2 copies, and other waves read the region
-      // only after the next barrier
+      // only after the next barrier.  As in layer 1, one accumulator per tile
+      // with the per-token factors on the H1 fragments.
+      {
+        _Float16 ajh[2], fjh[2];
+        int sj[2];
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        const float aj = cf[COEF_A + 32 * jt + lr], fj = cf[COEF_F + 32 * jt + lr];
+        for (int jt = 0; jt < 2; ++jt)
+          token_factors(cf[COEF_A + 32 * jt + lr], cf[COEF_F + 32 * jt + lr], ajh[jt], fjh[jt], sj[jt]);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          f16v accW = {}, accS = {}, acc3 = {};
+          f16v accY[2] = {};
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
-            accW = mfma(state_frag(W2m[ct], st, e2), H1h[jt][st], accW);
-            accS = mfma(state_frag(S2m[ct], st, e2), H1h[jt][st], accS);
+            const h8 wf = state_frag(W2m[ct], st, e2), sf = state_frag(S2m[ct], st, e2);
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) {
+              accY[jt] = mfma(wf, hscale(H1h[jt][st], ajh[jt]), accY[jt]);
+              accY[jt] = mfma(sf, hscale(H1h[jt][st], fjh[jt]), accY[jt]);
+            }
           }
 #pragma unroll
-          for (int it = 0; it < 2; ++it)
+          for (int jt = 0; jt < 2; ++jt) {
+            f16v acc3 = {};
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
-              acc3 = mfma(lds_frag(sD2T + (32 * ct + lr) * RS, 32 * it + 16 * st, lg), DPh[it][jt][st], acc3);
+            for (int it = 0; it < 2; ++it)
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {   // rows c = 32ct + 8g4 + 4lg + 0..3 are consecutive
-            f4v o;
+              for (int st = 0; st < 2; ++st)
+                acc3 = mfma(lds_frag(sD2T + (32 * ct + lr) * RS, 32 * it + 16 * st, lg), DPh[it][jt][st], acc3);
+            const float cy = pow2neg(e2 + eH1[jt] + sj[jt]), c3 = pow2neg(eD2 + eDP[jt]);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int r = 4 * g4 + q;
-              o[q] = ldexpf(aj * accW[r] + fj * accS[r], -(e2 + eH1[jt])) - ldexpf(acc3[r], -(eD2 + eDP[jt]));
+            for (int g4 = 0; g4 < 4; ++g4) {   // rows c = 32ct + 8g4 + 4lg + 0..3 are consecutive
+              f4v o;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int r = 4 * g4 + q;
+                o[q] = fmaf(acc3[r], -c3, accY[jt][r] * cy);
+              }
+              *(f4v*)(sRF + (32 * jt + lr) * RSF + 32 * ct + 8 * g4 + 4 * lg) = o;
             }
-            *(f4v*)(sRF + (32 * jt + lr) * RSF + 32 * ct + 8 * g4 + 4 * lg) = o;
           }
         }
       }
