@@ -82,8 +82,10 @@ constexpr int OFF_D2T = OFF_D2 + kTileH;
 constexpr int OFF_SC1 = OFF_D2T + kTileH;
 constexpr int OFF_DM = OFF_SC1 + kTileH;             // fp32 [64][68]
 constexpr int OFF_COEF = OFF_DM + kB * RSF * 4;
-constexpr int COEF_ALPHA = 0, COEF_ETA = 64, COEF_THETA = 128, COEF_A = 192, COEF_E = 256,
-              COEF_F = 320, COEF_U = 384, COEF_DN = 448;            // float index
+// float index: XT = the D recurrences' carried products (see the a1 stage),
+// T11/T12 = transfer of rows 32..63 (32 entries each)
+constexpr int COEF_XT = 0, COEF_T11 = 64, COEF_T12 = 96, COEF_THETA = 128, COEF_A = 192, COEF_E = 256,
+              COEF_F = 320;
 constexpr int COEF_H16 = 512 * 4;                                   // byte offset of fp16 arrays
 constexpr int H16_WU = 128, H16_WD = 192;                           // half index
 constexpr int COEF_INT = COEF_H16 + 256 * 2;                        // byte offset of int slots
@@ -103,7 +105,7 @@ static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 static_assert(kA1Bytes + 32 * RSF * 4 <= kWaveRegion, "A1 copy + O half-partial");
 static_assert(kA1Bytes + kHW * RS * 2 <= kWaveRegion, "A1 copy + W2 copy");
 
-constexpr int INT_AMAX_SC1 = 0, INT_AMAX_D2 = 1, INT_EWU = 2, INT_EWD = 3, INT_FAIL = 4;
+constexpr int INT_AMAX_SC1 = 0, INT_AMAX_D2 = 1, INT_EWU = 2, INT_EWD = 3, INT_FAIL = 4, INT_T22 = 5;
 
 // ---- global workspace layout, per pair (bytes) ----
 constexpr int64_t kXO = 2 * 2 * kB * kD * 4;         // [half][parity] x 64 x 64 fp32, thread-major
@@ -402,13 +404,16 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
   unsigned* flag_me = p.flags + (int64_t)(2 * pair + half) * (kFlagStride / 4);
   const unsigned* flag_pt = p.flags + (int64_t)(2 * pair + 1 - half) * (kFlagStride / 4);
 
-  // pair handshake: publish `seq`, run `during` (waves 1..3 while thread 0
-  // polls), and wait for the partner's `seq`; false = gave up
-  auto handshake = [&](unsigned seq, auto&& during) -> bool {
+  // pair handshake: publish `seq`, then every thread runs `first` (loads
+  // that must not delay the flag: the flag waits for this wave's earlier
+  // memory operations, loads included), then waves 1..3 run `during` while
+  // thread 0 waits for the partner's `seq`; false = gave up
+  auto handshake = [&](unsigned seq, auto&& first, auto&& during) -> bool {
     wait_stores();
     __syncthreads();
+    if (tid == 0) __hip_atomic_store(flag_me, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    first();
     if (tid == 0) {
-      __hip_atomic_store(flag_me, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       unsigned it = 0;
       while (__hip_atomic_load(flag_pt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < seq) {
         if (++it >= p.spin_max) break;
@@ -426,7 +431,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
   auto nothing = [] {};
 
   // the pair starts together (also flushes any stale flag value of this launch)
-  if (!handshake(1u, nothing)) failed0 = true;
+  if (!handshake(1u, nothing, nothing)) failed0 = true;
 
   // my y rows of the previous chunk, kept across the chunk boundary:
   // thread t covers row j = 32*half + t/8, columns (t%8)*8 .. +8
@@ -600,76 +605,111 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
         for (int r = 0; r < 16; ++r)
           sRW[crow(r, lg) * RS + 32 * ct + lr] = w2f[ct][r >> 3][r & 7];
 
-      // prefetch: this chunk's V (used right after the handshake) and the next
-      // chunk's raw K, Q and gates (staged in LDS once they arrive)
+      // loads issued right after this half's flag: this chunk's V (used
+      // right after the handshake) and the next chunk's raw K, Q and gates
+      // (staged in LDS once they arrive)
       uint4 vr0 = make_uint4(0, 0, 0, 0), vr1 = make_uint4(0, 0, 0, 0);
-      {
-        const int j0 = 8 * w + rj, j1 = 32 + 8 * w + rj;
-        if (j0 < n) vr0 = *(const uint4*)(p.v + (tok0 + c0 + j0) * kD + rc);
-        if (j1 < n) vr1 = *(const uint4*)(p.v + (tok0 + c0 + j1) * kD + rc);
-      }
       int next_s = s, next_c0 = c0 + p.chunk;
       if (next_c0 >= p.N) { next_s = s + p.n_pairs; next_c0 = 0; }
       const bool has_next = next_s < p.streams && p.N > 0;
       ChunkRegs nxt;
-      if (has_next) nxt = load_chunk_regs(p, (int64_t)next_s * p.N + next_c0, min(p.chunk, p.N - next_c0), tid);
+      auto issue_loads = [&] {
+        const int j0 = 8 * w + rj, j1 = 32 + 8 * w + rj;
+        if (j0 < n) vr0 = *(const uint4*)(p.v + (tok0 + c0 + j0) * kD + rc);
+        if (j1 < n) vr1 = *(const uint4*)(p.v + (tok0 + c0 + j1) * kD + rc);
+        if (has_next) nxt = load_chunk_regs(p, (int64_t)next_s * p.N + next_c0, min(p.chunk, p.N - next_c0), tid);
+      };
 
       // ================= a1: coefficients (both halves compute them identically) =================
-      // run by waves 3 and 2 while thread 0 awaits the partner (first used after that barrier)
-      // Lane m of both waves holds token m's (1 - alpha_m, eta_m).
+      // Run by waves 1..3 while thread 0 of wave 0 awaits the partner (first
+      // used after that barrier).  Lane m of each wave holds token m's
+      // (1 - alpha_m, eta_m).
+      //
+      // D, one lane per column i: t = theta_i prod_{i<m<=j} eta_m, started at
+      // j == i by adding theta_i to a zero product, and
+      // D[j][i] = (1 - alpha_j) D[j-1][i] + t -- one fma per row on each of the
+      // two carried values, the row's gates broadcast with readlane.  Wave 3
+      // runs rows 0..31 and wave 1 rows 32..63.  For columns i >= 32 wave 1's
+      // rows are exact (their recurrences start at row i); for i < 32 wave 1
+      // starts from zero, and the rows are completed after the wait from wave
+      // 3's carried pair at row 31 through the (column-independent) transfer
+      //   (D, t)_j = (T11_j D_31 + T12_j t_31, T22_j t_31),
+      // T11_j = prod_{32<=m<=j} (1 - alpha_m), T22_j = prod_{32<=m<=j} eta_m,
+      // T12_j = sum_{32<=l<=j} prod_{l<m<=j} (1 - alpha_m) T22_l,
+      // which wave 2 gets from prefix scans restarted at row 32.
       auto coef_work = [&] {
-      if (w >= 2) {
+      if (w >= 1) {
         const float2 gl = ((const float2*)(smem + OFF_COEF + COEF_PAIR))[lane];
-        if (w == 3) {
-          // wave 3: column i = lane of D, one row j per step (the step's gates
-          // broadcast with readlane).  t = theta_i prod_{i<m<=j} eta_m, started
-          // at j == i by adding theta_i to a zero product, and
-          // D[j][i] = (1 - alpha_j) D[j-1][i] + t: one fma per step on each of
-          // the two loop-carried values.
+        if (w != 2) {
           const int glx = __float_as_int(gl.x), gly = __float_as_int(gl.y);
           const int i = lane;
+          const int j0 = __builtin_amdgcn_readfirstlane(w == 3 ? 0 : 32);
           const float thi = cf[COEF_THETA + i];
           float di = 0.f, t = 0.f;
+          float* drow = sDM + j0 * RSF + i;
 #pragma unroll
-          for (int j = 0; j < kB; ++j) {
+          for (int jj = 0; jj < 32; ++jj) {
+            const int j = j0 + jj;
             const float ga = __int_as_float(__builtin_amdgcn_readlane(glx, j));
             const float ge = __int_as_float(__builtin_amdgcn_readlane(gly, j));
-            // theta_i in lane j only: a select on the constant lane mask 1 << j
-            // (a lane-index compare would be hoisted out of the chunk loop as
-            // 64 live masks)
+            // theta_i in lane j only: a select on the lane mask 1 << j
             float inj;
             asm("v_cndmask_b32_e64 %0, 0, %1, %2" : "=v"(inj) : "v"(thi), "s"(1ull << j));
             t = fmaf(ge, t, inj);
             di = fmaf(ga, di, t);
-            sDM[j * RSF + i] = di;
+            drow[jj * RSF] = di;
           }
-          const float ui = t;   // theta_i prod_{m>i} eta_m (padding has eta = 1)
-          const float dlast = sDM[(n - 1) * RSF + i];   // this wave's own store above
-          cf[COEF_U + i] = ui;
-          cf[COEF_DN + i] = dlast;
-          const float mu = wave_max(fabsf(ui)), md = wave_max(fabsf(dlast));
-          int eu = 0, ed = 0;
-          if (mu > 0.f && mu < INFINITY) { (void)frexpf(mu, &eu); eu = -eu; }
-          if (md > 0.f && md < INFINITY) { (void)frexpf(md, &ed); ed = -ed; }
-          // weights scaled into (0.5, 1]: products with unit-size operands stay in fp16 range
-          ch[H16_WU + i] = (_Float16)ldexpf(ui, eu);
-          ch[H16_WD + i] = (_Float16)ldexpf(dlast, ed);
-          if (lane == 0) { ci[INT_EWU] = eu; ci[INT_EWD] = ed; }
+          // wave 3: t at row 31 for i < 32; wave 1: t at row 63 (= U_i) for i >= 32
+          if ((w == 3) == (i < 32)) cf[COEF_XT + i] = t;
         } else {
-          // wave 2: lane j = token j.  E_j by a prefix product of eta, then
-          // (A_j, F_j) by a prefix scan of the maps u -> (1 - alpha_j) u + E_j
-          // (A_j is the scan's product part, F_j its value from F_{-1} = 0)
+          // lane j = token j: E_j by a prefix product of eta, then (A_j, F_j) by
+          // a prefix scan of the maps u -> (1 - alpha_j) u + E_j (A_j is the
+          // scan's product part, F_j its value from F_{-1} = 0)
           const float e = wave_prefix_prod(gl.y);
           float a = gl.x, f = e;
           wave_affine_scan(a, f);
           cf[COEF_A + lane] = a;
           cf[COEF_E + lane] = e;
           cf[COEF_F + lane] = f;
+          // the same scans restarted at row 32 (identity maps below it)
+          const bool lo = lane < 32;
+          const float e2 = wave_prefix_prod(lo ? 1.f : gl.y);
+          float a2 = lo ? 1.f : gl.x, f2 = lo ? 0.f : e2;
+          wave_affine_scan(a2, f2);
+          if (!lo) {
+            cf[COEF_T11 + lane - 32] = a2;
+            cf[COEF_T12 + lane - 32] = f2;
+          }
+          if (lane == 63) ci[INT_T22] = __float_as_int(e2);
         }
       }
       };
 
-      if (!handshake(seq + 2, coef_work)) { failed = true; break; }
+      if (!handshake(seq + 2, issue_loads, coef_work)) { failed = true; break; }
+      {
+        // D rows 32..63 of columns 0..31: 8 row groups x 32 columns, 4 rows each
+        const int i = tid & 31, jr = 32 + 4 * (tid >> 5);
+        const float d31 = sDM[31 * RSF + i], t31 = cf[COEF_XT + i];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          sDM[(jr + q) * RSF + i] = fmaf(cf[COEF_T11 + jr + q - 32], d31, cf[COEF_T12 + jr + q - 32] * t31);
+      }
+      __syncthreads();
+      if (w == 3) {
+        // weights of the state update: U_i = theta_i prod_{m>i} eta_m and
+        // D[n-1][i], each scaled into (0.5, 1] for fp16 (padding has eta = 1)
+        const int i = lane;
+        const float ti = cf[COEF_XT + i];
+        const float ui = i < 32 ? ti * __int_as_float(ci[INT_T22]) : ti;
+        const float dlast = sDM[(n - 1) * RSF + i];
+        const float mu = wave_max(fabsf(ui)), md = wave_max(fabsf(dlast));
+        int eu = 0, ed = 0;
+        if (mu > 0.f && mu < INFINITY) { (void)frexpf(mu, &eu); eu = -eu; }
+        if (md > 0.f && md < INFINITY) { (void)frexpf(md, &ed); ed = -ed; }
+        ch[H16_WU + i] = (_Float16)ldexpf(ui, eu);
+        ch[H16_WD + i] = (_Float16)ldexpf(dlast, ed);
+        if (lane == 0) { ci[INT_EWU] = eu; ci[INT_EWD] = ed; }
+      }
       if (has_next) stage_chunk_regs(smem + OFF_STAGE, nxt, tid);
       staged = has_next;
 
@@ -1013,7 +1053,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
 
   // the last chunk's y rows: one more handshake (a flag value no chunk uses)
   if (!failed && prev_row0 >= 0) {
-    if (handshake(seq + 2, nothing)) finish_prev_y((seq - 1) & 1u);
+    if (handshake(seq + 2, nothing, nothing)) finish_prev_y((seq - 1) & 1u);
   }
 }
 
