@@ -442,11 +442,11 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
   bool failed = failed0;
   bool staged = false;   // the staging area holds the rows of the chunk about to start
 
-  auto finish_prev_y = [&](unsigned parity) {
-    // partner's partial for my rows of the previous chunk, then the fixed-order sum
+  // the partner's partial for my rows of the previous chunk (thread-major)
+  auto load_prev_y = [&](unsigned parity, float* pv) { xload8(xY_pt + parity * 32 * kD, 0, tid, pv); };
+  // the fixed-order sum of the two partials, stored as bf16
+  auto finish_prev_y = [&](const float* pv) {
     const int jr = tid >> 3, cc = (tid & 7) * 8;
-    float pv[8];
-    xload8(xY_pt + parity * 32 * kD, 0, tid, pv);
     const int j = 32 * half + jr;
     if (j < prev_n) {
       __hip_bfloat16* yr = p.y + (prev_row0 + j) * kD + cc;
@@ -686,6 +686,12 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       };
 
       if (!handshake(seq + 2, issue_loads, coef_work)) { failed = true; break; }
+      // the partner's data (published before its flag) is loaded now and
+      // used after the D completion, the update weights and SC1
+      float pvv[2][8], pyv[8];
+      xload8(xO_pt + par * kB * kD, 0, tid, pvv[0]);   // rows 8w + rj, columns rc .. rc+7
+      xload8(xO_pt + par * kB * kD, 4, tid, pvv[1]);   // rows 32 + 8w + rj
+      if (prev_row0 >= 0) load_prev_y(par ^ 1u, pyv);
       {
         // D rows 32..63 of columns 0..31: 8 row groups x 32 columns, 4 rows each
         const int i = tid & 31, jr = 32 + 4 * (tid >> 5);
@@ -714,7 +720,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       staged = has_next;
 
       // last chunk's y rows (the partner published them before this flag)
-      if (prev_row0 >= 0) finish_prev_y(par ^ 1u);
+      if (prev_row0 >= 0) finish_prev_y(pyv);
 
       // ================= first-layer scores SC1 = D o (Q K^T): one 32x32 tile per wave =================
       f16v sc;
@@ -741,9 +747,6 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       float d2v[2][8];
       {
         float am = 0.f;
-        float pvv[2][8];
-        xload8(xO_pt + par * kB * kD, 0, tid, pvv[0]);   // rows 8w + rj, columns rc .. rc+7
-        xload8(xO_pt + par * kB * kD, 4, tid, pvv[1]);   // rows 32 + 8w + rj
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
           const int j = 32 * pass + 8 * w + rj;
@@ -1053,7 +1056,11 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
 
   // the last chunk's y rows: one more handshake (a flag value no chunk uses)
   if (!failed && prev_row0 >= 0) {
-    if (handshake(seq + 2, nothing, nothing)) finish_prev_y((seq - 1) & 1u);
+    if (handshake(seq + 2, nothing, nothing)) {
+      float pyv[8];
+      load_prev_y((seq - 1) & 1u, pyv);
+      finish_prev_y(pyv);
+    }
   }
 }
 
