@@ -262,9 +262,10 @@ __device__ __forceinline__ float sigmoidf_(float z) {
 }
 
 // Pair exchange accessors: agent-coherent (sc1) relaxed accesses, ordered by
-// s_waitcnt vmcnt(0) before each flag store.  (An L2-local variant using sc0
-// loads was tried: on gfx950 a poller then kept reading a stale flag, so the
-// exchange stays agent-coherent.)
+// s_waitcnt vmcnt(0) before each flag store.  (L2-local variants for halves
+// on one XCD -- workgroup-scope stores and loads, with or without dropping
+// the reader's L1 lines before each poll -- left a poller reading a stale
+// flag on gfx950, so the exchange stays agent-coherent.)
 // The exchange buffers are thread-major: 8-byte element e of thread t sits
 // at (e * kThreads + t) * 8 bytes, so each store or load instruction of a
 // wave covers 512 contiguous bytes (whole lines: an agent-coherent store
@@ -315,25 +316,49 @@ __device__ __forceinline__ ChunkRegs load_chunk_regs(const Params& p, int64_t ro
   return r;
 }
 
-__device__ __forceinline__ void stage_chunk_regs(unsigned char* stage, const ChunkRegs& r, int tid) {
+// Prefetch of a chunk's raw rows straight into the LDS staging area
+// (global_load_lds: lane l of an instruction writes 16 bytes at base + 16 l,
+// or 4 bytes at base + 4 l; lanes that do not load write nothing).  Thread
+// t = 64 w + l loads the same 32 bytes of a K and a Q row that
+// load_chunk_regs gives it: slot (2w + i) * 64 + l of each area holds its
+// i-th 16 bytes.  Wave 0 loads the gates.  Rows and tokens past the chunk end
+// are left out and replaced on unstaging.
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+__device__ __forceinline__ void prefetch_chunk_lds(const Params& p, int64_t row0, int n, int tid, unsigned char* stage) {
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int j = tid >> 2, cb = (tid & 3) * 16;
   uint4* sk = (uint4*)stage;
   uint4* sq = (uint4*)(stage + kB * kD * 2);
-  sk[2 * tid] = r.k0; sk[2 * tid + 1] = r.k1;
-  sq[2 * tid] = r.q0; sq[2 * tid + 1] = r.q1;
-  if (tid < kB) {
+  if (j < n) {
+    const uint4* kr = (const uint4*)(p.k + (row0 + j) * kD + cb);
+    const uint4* qr = (const uint4*)(p.q + (row0 + j) * kD + cb);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_global_load_lds((const void*)(kr + i), (lds_void_ptr)(sk + (2 * w + i) * 64), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(qr + i), (lds_void_ptr)(sq + (2 * w + i) * 64), 16, 0, 0);
+    }
+  }
+  if (w == 0 && lane < n) {
     float* g = (float*)(stage + 2 * kB * kD * 2);
-    g[tid] = r.ga; g[kB + tid] = r.ge; g[2 * kB + tid] = r.gt;
+    __builtin_amdgcn_global_load_lds((const void*)(p.alpha + row0 + lane), (lds_void_ptr)g, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(p.eta + row0 + lane), (lds_void_ptr)(g + kB), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(p.theta + row0 + lane), (lds_void_ptr)(g + 2 * kB), 4, 0, 0);
   }
 }
 
-__device__ __forceinline__ ChunkRegs unstage_chunk_regs(const unsigned char* stage, int tid) {
+__device__ __forceinline__ ChunkRegs unstage_chunk_regs(const unsigned char* stage, int n, int tid) {
   ChunkRegs r;
+  const int w = tid >> 6, lane = tid & 63, j = tid >> 2;
   const uint4* sk = (const uint4*)stage;
   const uint4* sq = (const uint4*)(stage + kB * kD * 2);
-  r.k0 = sk[2 * tid]; r.k1 = sk[2 * tid + 1];
-  r.q0 = sq[2 * tid]; r.q1 = sq[2 * tid + 1];
+  if (j < n) {
+    r.k0 = sk[(2 * w) * 64 + lane]; r.k1 = sk[(2 * w + 1) * 64 + lane];
+    r.q0 = sq[(2 * w) * 64 + lane]; r.q1 = sq[(2 * w + 1) * 64 + lane];
+  } else {
+    r.k0 = r.k1 = r.q0 = r.q1 = make_uint4(0, 0, 0, 0);
+  }
   r.ga = 0.f; r.ge = 1.f; r.gt = 0.f;
-  if (tid < kB) {
+  if (tid < kB && tid < n) {
     const float* g = (const float*)(stage + 2 * kB * kD * 2);
     r.ga = g[tid]; r.ge = g[kB + tid]; r.gt = g[2 * kB + tid];
   }
@@ -488,7 +513,8 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       // ================= the chunk's K, K^T, Q (fp16) and gates into LDS =================
       {
         // rows come from the staging area when the previous chunk prefetched them
-        const ChunkRegs cr = staged ? unstage_chunk_regs(smem + OFF_STAGE, tid) : load_chunk_regs(p, tok0 + c0, n, tid);
+        if (staged) __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's staging loads (long done)
+        const ChunkRegs cr = staged ? unstage_chunk_regs(smem + OFF_STAGE, n, tid) : load_chunk_regs(p, tok0 + c0, n, tid);
         const int j = tid >> 2, cb = (tid & 3) * 16;
         _Float16 kv[16], qv[16];
         bf16x8_to_h(cr.k0, kv);
@@ -510,6 +536,12 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
         if (tid < 2) ci[tid] = 0;
       }
       __syncthreads();
+      // the next chunk's rows go straight to the staging area (read at its start)
+      int next_s = s, next_c0 = c0 + p.chunk;
+      if (next_c0 >= p.N) { next_s = s + p.n_pairs; next_c0 = 0; }
+      const bool has_next = next_s < p.streams && p.N > 0;
+      if (has_next) prefetch_chunk_lds(p, (int64_t)next_s * p.N + next_c0, min(p.chunk, p.N - next_c0), tid, smem + OFF_STAGE);
+      staged = has_next;
 
       // state scales (joint for W and S of a layer, per wave)
       const int e1 = scale_exp(wave_max(m1));
@@ -606,18 +638,12 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
           sRW[crow(r, lg) * RS + 32 * ct + lr] = w2f[ct][r >> 3][r & 7];
 
       // loads issued right after this half's flag: this chunk's V (used
-      // right after the handshake) and the next chunk's raw K, Q and gates
-      // (staged in LDS once they arrive)
+      // after the handshake)
       uint4 vr0 = make_uint4(0, 0, 0, 0), vr1 = make_uint4(0, 0, 0, 0);
-      int next_s = s, next_c0 = c0 + p.chunk;
-      if (next_c0 >= p.N) { next_s = s + p.n_pairs; next_c0 = 0; }
-      const bool has_next = next_s < p.streams && p.N > 0;
-      ChunkRegs nxt;
       auto issue_loads = [&] {
         const int j0 = 8 * w + rj, j1 = 32 + 8 * w + rj;
         if (j0 < n) vr0 = *(const uint4*)(p.v + (tok0 + c0 + j0) * kD + rc);
         if (j1 < n) vr1 = *(const uint4*)(p.v + (tok0 + c0 + j1) * kD + rc);
-        if (has_next) nxt = load_chunk_regs(p, (int64_t)next_s * p.N + next_c0, min(p.chunk, p.N - next_c0), tid);
       };
 
       // ================= a1: coefficients (both halves compute them identically) =================
@@ -716,8 +742,6 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
         ch[H16_WD + i] = (_Float16)ldexpf(dlast, ed);
         if (lane == 0) { ci[INT_EWU] = eu; ci[INT_EWD] = ed; }
       }
-      if (has_next) stage_chunk_regs(smem + OFF_STAGE, nxt, tid);
-      staged = has_next;
 
       // last chunk's y rows (the partner published them before this flag)
       if (prev_row0 >= 0) finish_prev_y(pyv);
@@ -1062,6 +1086,9 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       finish_prev_y(pyv);
     }
   }
+  // no load into this workgroup's LDS may outlive it (a pair that gave up
+  // can leave a staging prefetch in flight)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 }  // namespace
