@@ -380,6 +380,9 @@ __global__ void zero_flags_kernel(unsigned* flags, int n, unsigned* status) {
   if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0u;
 }
 
+// kRW: retrieval after each token's write (true) or at the chunk-start
+// state (false: y_j = M_{W_0}(q_j), without the masked correction terms)
+template <bool kRW>
 __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   _Float16* sK = (_Float16*)(smem + OFF_K);
@@ -748,7 +751,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
 
       // ================= first-layer scores SC1 = D o (Q K^T): one 32x32 tile per wave =================
       f16v sc;
-      {
+      if constexpr (kRW) {
         const int jt = w >> 1, it = w & 1;
         f16v acc = {};
 #pragma unroll
@@ -796,7 +799,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       }
       __syncthreads();   // every wave's SC1 and Delta2 amax is in
       const int eSC = scale_exp(__uint_as_float((unsigned)ci[INT_AMAX_SC1]));
-      {
+      if constexpr (kRW) {
         const int jt = w >> 1, it = w & 1;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -851,7 +854,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       // the S1 product; W1 and S1 fragments are converted once for both tiles.
       h8 H1h[2][2];
       int eH1[2];
-      {
+      if constexpr (kRW) {
         _Float16 ajh[2], fjh[2];
         int sj[2];
 #pragma unroll
@@ -893,6 +896,34 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
           for (int r = 0; r < 16; ++r) H1h[jt][r >> 3][r & 7] = (_Float16)ldexpf(Hf[r], eH1[jt]);
         }
       }
+      else {
+        // chunk-start read: Zq1^T = W1_0 q^T
+        f16v accZ[2] = {};
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const h8 wf = state_frag(W1m[ct], st, e1);
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt)
+              accZ[jt] = mfma(wf, lds_frag(sQ + (32 * jt + lr) * RS, 32 * ct + 16 * st, lg), accZ[jt]);
+          }
+        const float cz = pow2neg(e1);
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          f16v Hf;
+          float am = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float z = accZ[jt][r] * cz;
+            Hf[r] = z * sigmoidf_(z);
+            am = fmaxf(am, fabsf(Hf[r]));
+          }
+          eH1[jt] = scale_exp(wave_max(am));
+#pragma unroll
+          for (int r = 0; r < 16; ++r) H1h[jt][r >> 3][r & 7] = (_Float16)ldexpf(Hf[r], eH1[jt]);
+        }
+      }
 
       const float An = cf[COEF_A + n - 1], En = cf[COEF_E + n - 1], Fn = cf[COEF_F + n - 1];
       const int ewU = ci[INT_EWU], ewD = ci[INT_EWD];
@@ -924,6 +955,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       // ================= masked second-layer scores (D o (H1 A1^T))^T (rows i, cols j) =================
       h8 DPh[2][2][2];
       int eDP[2];
+      if constexpr (kRW)
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
         f16v Pf[2];
@@ -958,7 +990,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       // its last read of its A1 and W2 copies, and other waves read the region
       // only after the next barrier.  As in layer 1, one accumulator per tile
       // with the per-token factors on the H1 fragments.
-      {
+      if constexpr (kRW) {
         _Float16 ajh[2], fjh[2];
         int sj[2];
 #pragma unroll
@@ -993,6 +1025,30 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
                 const int r = 4 * g4 + q;
                 o[q] = fmaf(acc3[r], -c3, accY[jt][r] * cy);
               }
+              *(f4v*)(sRF + (32 * jt + lr) * RSF + 32 * ct + 8 * g4 + 4 * lg) = o;
+            }
+          }
+        }
+      }
+      else {
+        // chunk-start read: y^T partial = W2_0 H1^T
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          f16v accY[2] = {};
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const h8 wf = state_frag(W2m[ct], st, e2);
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) accY[jt] = mfma(wf, H1h[jt][st], accY[jt]);
+          }
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt) {
+            const float cy = pow2neg(e2 + eH1[jt]);
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              f4v o;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) o[q] = accY[jt][4 * g4 + q] * cy;
               *(f4v*)(sRF + (32 * jt + lr) * RSF + 32 * ct + 8 * g4 + 4 * lg) = o;
             }
           }
@@ -1095,7 +1151,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
 
 bool mlp2_supported(const Shape& s, int chunk) {
   return s.L == 2 && s.d == kD && s.hidden == kH && s.io == TM_IO_BF16 &&
-         s.read_mode == TM_READ_AFTER_WRITE && chunk >= 1 && chunk <= kB;
+         (s.read_mode == TM_READ_AFTER_WRITE || s.read_mode == TM_READ_CHUNK_START) && chunk >= 1 && chunk <= kB;
 }
 
 static int64_t pairs_for(const Shape& s) { return s.streams < kMaxPairs ? s.streams : kMaxPairs; }
@@ -1109,10 +1165,13 @@ hipError_t launch_mlp2(const Shape& s, int chunk, const void* k, const void* v, 
                        const float* alpha, const float* eta, const float* theta,
                        const float* W_in, const float* S_in, void* y, float* W_out,
                        float* S_out, void* ws, hipStream_t stream) {
-  static bool configured = false;   // attribute set once per process (idempotent)
+  static bool configured = false;   // attributes set once per process (idempotent)
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute((const void*)mlp2_pair_kernel,
+    hipError_t e = hipFuncSetAttribute((const void*)mlp2_pair_kernel<true>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)mlp2_pair_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kLdsBytes);
     if (e != hipSuccess) return e;
     configured = true;
   }
@@ -1149,7 +1208,10 @@ hipError_t launch_mlp2(const Shape& s, int chunk, const void* k, const void* v, 
   hipLaunchKernelGGL(zero_flags_kernel, dim3(1), dim3(256), 0, stream, p.flags, (int)(2 * np), p.status);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mlp2_pair_kernel, dim3((unsigned)(2 * np)), dim3(kThreads), kLdsBytes, stream, p);
+  if (s.read_mode == TM_READ_AFTER_WRITE)
+    hipLaunchKernelGGL(mlp2_pair_kernel<true>, dim3((unsigned)(2 * np)), dim3(kThreads), kLdsBytes, stream, p);
+  else
+    hipLaunchKernelGGL(mlp2_pair_kernel<false>, dim3((unsigned)(2 * np)), dim3(kThreads), kLdsBytes, stream, p);
   return hipGetLastError();
 }
 

@@ -46,6 +46,13 @@ def test_param_count_and_paths(lib):
     assert tmm.select_path(d3, 0) == tmm.ERR_INVALID
     forced = tmm.make_desc(8, 16, 16384, 64, 256, 2, "bf16", flags=tmm.FLAG_FORCE_GENERIC)
     assert tmm.select_path(forced, 64) == tmm.PATH_GENERIC_F32
+    # the MFMA kernel serves both read modes of the 2-layer d=64 h=256 bf16 memory, chunks 1..64
+    for rm in (0, 1):
+        d = tmm.make_desc(8, 16, 16384, 64, 256, 2, "bf16", read_mode=rm)
+        assert tmm.select_path(d, 64) == tmm.PATH_MLP2_D64_H256
+        assert tmm.select_path(d, 1) == tmm.PATH_MLP2_D64_H256
+        assert tmm.select_path(d, 65) == tmm.PATH_GENERIC_F32
+    assert tmm.select_path(tmm.make_desc(8, 16, 16384, 64, 256, 2, "f32"), 64) == tmm.PATH_GENERIC_F32
     assert tmm.workspace_bytes(d1, 16) > 0
 
 

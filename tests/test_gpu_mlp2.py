@@ -36,6 +36,7 @@ def _np(cfg, out):
 
 
 def _check(cfg, inp, out, ref, idx=None, tol=None, label=""):
+    """y, W, S per stream (norm-wise, with floors) and y per window, to the bf16-io bar."""
     tol = TOL[cfg.io] if tol is None else tol
     yg, Wg, Sg = _np(cfg, out)
     e = stream_errors(cfg, inp, yg, Wg, Sg, *ref, idx=idx)
@@ -184,3 +185,32 @@ def test_mlp2_gate_edge_cases():
     y, W, S = run_gpu(cfg, d1)
     rel = (torch.linalg.norm(W.double() - S.double()) / torch.linalg.norm(S.double())).item()
     assert rel < 1e-5, rel
+
+
+@pytest.mark.parametrize("cfg_i,n_tokens,BH,chunk", [(3, 2048, None, 64), (2, 130, (1, 3), 40), (2, 77, (2, 5), 16)])
+def test_mlp2_chunk_start_read(cfg_i, n_tokens, BH, chunk):
+    """Retrieval at the chunk-start state (y_j = M_{W_0}(q_j), the read that
+    precedes a segment's write) on the MFMA kernel, against the oracle in the
+    same read mode; the state update is the same as in the default mode."""
+    from test_learned_neural_amd import titans_mem as tmm
+    cfg = wl.CONFIGS[cfg_i].with_(N=n_tokens, chunk=chunk)
+    if BH:
+        cfg = cfg.with_(B=BH[0], H=BH[1])
+    d = tmm.make_desc(cfg.B, cfg.H, cfg.N, cfg.d, cfg.hidden, cfg.n_layers, cfg.io, read_mode=1)
+    assert tmm.select_path(d, chunk) == tmm.PATH_MLP2_D64_H256
+    inp = wl.make_inputs(cfg, workers=8)
+    out = run_gpu(cfg, to_device(cfg, inp), read_mode=1)
+    _check(cfg, inp, out, run_oracle(cfg, inp, read_mode=1, threads=16), label=f"{cfg.name} chunk-start read")
+
+
+def test_mlp2_chunk_start_read_matches_generic():
+    import torch
+    cfg = wl.CONFIGS[3].with_(B=2, H=4, N=320)
+    inp = wl.make_inputs(cfg)
+    dev = to_device(cfg, inp)
+    fast = _np(cfg, run_gpu(cfg, dev, read_mode=1))
+    gen = _np(cfg, run_gpu(cfg, dev, read_mode=1, force_generic=True))
+    for a, b in zip(fast, gen):
+        for s in range(cfg.streams):
+            assert np.linalg.norm(a[s] - b[s]) <= 2e-2 * max(np.linalg.norm(b[s]), 1e-30)
+    torch.cuda.synchronize()
