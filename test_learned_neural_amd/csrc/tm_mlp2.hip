@@ -670,23 +670,32 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       if (w >= 1) {
         const float2 gl = ((const float2*)(smem + OFF_COEF + COEF_PAIR))[lane];
         if (w != 2) {
-          const int glx = __float_as_int(gl.x), gly = __float_as_int(gl.y);
           const int i = lane;
           const int j0 = __builtin_amdgcn_readfirstlane(w == 3 ? 0 : 32);
           const float thi = cf[COEF_THETA + i];
           float di = 0.f, t = 0.f;
           float* drow = sDM + j0 * RSF + i;
-#pragma unroll
-          for (int jj = 0; jj < 32; ++jj) {
-            const int j = j0 + jj;
-            const float ga = __int_as_float(__builtin_amdgcn_readlane(glx, j));
-            const float ge = __int_as_float(__builtin_amdgcn_readlane(gly, j));
+          auto step = [&](int jj, float ga, float ge) {
             // theta_i in lane j only: a select on the lane mask 1 << j
             float inj;
-            asm("v_cndmask_b32_e64 %0, 0, %1, %2" : "=v"(inj) : "v"(thi), "s"(1ull << j));
+            asm("v_cndmask_b32_e64 %0, 0, %1, %2" : "=v"(inj) : "v"(thi), "s"(1ull << (j0 + jj)));
             t = fmaf(ge, t, inj);
             di = fmaf(ga, di, t);
             drow[jj * RSF] = di;
+          };
+          // the steps' (1 - alpha_j, eta_j) pairs (padding included) as LDS
+          // broadcasts, two steps per 16-byte read, a batch of 8 steps ahead
+          const float4* pairs4 = (const float4*)(smem + OFF_COEF + COEF_PAIR) + j0 / 2;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            float4 g[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) g[q] = pairs4[4 * b + q];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              step(8 * b + 2 * q, g[q].x, g[q].y);
+              step(8 * b + 2 * q + 1, g[q].z, g[q].w);
+            }
           }
           // wave 3: t at row 31 for i < 32; wave 1: t at row 63 (= U_i) for i >= 32
           if ((w == 3) == (i < 32)) cf[COEF_XT + i] = t;
