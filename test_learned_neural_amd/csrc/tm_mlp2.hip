@@ -92,9 +92,10 @@ constexpr int COEF_INT = COEF_H16 + 256 * 2;                        // byte offs
 constexpr int COEF_PAIR = COEF_INT + 16 * 4;                        // byte offset of (1-alpha, eta) pairs
 constexpr int kCoefBytes = COEF_PAIR + kB * 8;
 constexpr int OFF_WAVE = (OFF_COEF + kCoefBytes + 255) / 256 * 256;
-// per-wave region: [A1 copy 64 x RSA fp16][W2 copy 32 x RS fp16 | O half-partial 32 x RSF fp32];
+// per-wave region: [A1 copy 64 x RSA fp16][W2 copy [h_l][c] 32 x RS fp16][W2 copy [c][h_l] 64 x RSA fp16];
 // later the whole region holds the wave's y partial (64 x RSF fp32, token-major)
 constexpr int kA1Bytes = kB * RSA * 2;               // 4608
+constexpr int kW2Bytes = kHW * RS * 2;               // 4352: W2 copy [h_l][c]
 constexpr int kWaveRegion = kD * RSF * 4;            // 17408
 // staging for the next chunk's raw bf16 K, Q rows and gates (filled during the
 // pair handshake, converted at the next chunk's start)
@@ -102,10 +103,10 @@ constexpr int OFF_STAGE = OFF_WAVE + kWaves * kWaveRegion;
 constexpr int kStageBytes = 2 * kB * kD * 2 + 3 * kB * 4;
 constexpr int kLdsBytes = OFF_STAGE + kStageBytes;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-static_assert(kA1Bytes + 32 * RSF * 4 <= kWaveRegion, "A1 copy + O half-partial");
-static_assert(kA1Bytes + kHW * RS * 2 <= kWaveRegion, "A1 copy + W2 copy");
+static_assert(kA1Bytes + kW2Bytes + kD * RSA * 2 <= kWaveRegion, "A1 copy + both W2 copies");
 
 constexpr int INT_AMAX_SC1 = 0, INT_AMAX_D2 = 1, INT_EWU = 2, INT_EWD = 3, INT_FAIL = 4, INT_T22 = 5;
+constexpr int INT_M2 = 6, INT_MA1 = 10;   // per-wave maxima (4 slots each) for the workgroup-wide scales
 
 // ---- global workspace layout, per pair (bytes) ----
 constexpr int64_t kXO = 2 * 2 * kB * kD * 4;         // [half][parity] x 64 x 64 fp32, thread-major
@@ -420,7 +421,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
   const int hs = kHC * half + kHW * w;   // first hidden unit of this wave
   _Float16* sRA = (_Float16*)(smem + OFF_WAVE + w * kWaveRegion);       // A1 copy [j][h_l]
   _Float16* sRW = (_Float16*)(smem + OFF_WAVE + w * kWaveRegion + kA1Bytes);  // W2 copy [h_l][c]
-  float* sRP = (float*)(smem + OFF_WAVE + w * kWaveRegion + kA1Bytes);   // O half-partial [j][c]
+  _Float16* sRW2 = (_Float16*)(smem + OFF_WAVE + w * kWaveRegion + kA1Bytes + kW2Bytes);   // W2 copy [c][h_l]
   float* sRF = (float*)(smem + OFF_WAVE + w * kWaveRegion);              // y partial [j][c]
 
   unsigned char* xb = p.xbuf + (int64_t)pair * kPairBytes;
@@ -538,6 +539,10 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
         }
         if (tid < 2) ci[tid] = 0;
       }
+      {
+        const float wm2 = wave_max(m2);
+        if (lane == 0) ci[INT_M2 + w] = __float_as_int(wm2);
+      }
       __syncthreads();
       // the next chunk's rows go straight to the staging area (read at its start)
       int next_s = s, next_c0 = c0 + p.chunk;
@@ -546,9 +551,11 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       if (has_next) prefetch_chunk_lds(p, (int64_t)next_s * p.N + next_c0, min(p.chunk, p.N - next_c0), tid, smem + OFF_STAGE);
       staged = has_next;
 
-      // state scales (joint for W and S of a layer, per wave)
+      // state scales: W1/S1 per wave; W2/S2 joint over the workgroup (the
+      // half's O is one contraction over all its waves' W2 copies)
       const int e1 = scale_exp(wave_max(m1));
-      const int e2 = scale_exp(wave_max(m2));
+      const int e2 = scale_exp(fmaxf(fmaxf(__int_as_float(ci[INT_M2]), __int_as_float(ci[INT_M2 + 1])),
+                                     fmaxf(__int_as_float(ci[INT_M2 + 2]), __int_as_float(ci[INT_M2 + 3]))));
 
       // ================= a2: key-side forward Z1 = K W1^T (rows j, cols h) =================
       // A1 = SiLU(Z1) (scaled fp16: kept for the update, copied to LDS for the
@@ -581,7 +588,32 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
             SPh[jt][r >> 3][r & 7] = (_Float16)(sg + a * (1.f - sg));   // s (1 + z (1 - s))
           }
         }
-        eA1 = scale_exp(wave_max(am));
+        {
+          const float wam = wave_max(am);
+          if (lane == 0) ci[INT_MA1 + w] = __float_as_int(wam);
+        }
+        // W2 fragments (workgroup-wide scale) and this wave's two W2 copies:
+        // [h_l][c] for the backprop, [c][h_l] for the half's O (the fragment
+        // slots follow the operand order 16s + 8(i/4) + 4lg + i%4 over h_l)
+        h8 w2f[2][2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            w2f[ct][st] = state_frag(W2m[ct], st, e2);
+            _Float16* row = sRW2 + (32 * ct + lr) * RSA + 16 * st + 4 * lg;
+            *(h4*)row = h4{w2f[ct][st][0], w2f[ct][st][1], w2f[ct][st][2], w2f[ct][st][3]};
+            *(h4*)(row + 8) = h4{w2f[ct][st][4], w2f[ct][st][5], w2f[ct][st][6], w2f[ct][st][7]};
+          }
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sRW[crow(r, lg) * RS + 32 * ct + lr] = w2f[ct][r >> 3][r & 7];
+        __syncthreads();   // every wave's A1 maximum and W2 copies
+        // A1 with the workgroup-wide scale, kept for the update and copied to LDS
+        eA1 = scale_exp(fmaxf(fmaxf(__int_as_float(ci[INT_MA1]), __int_as_float(ci[INT_MA1 + 1])),
+                              fmaxf(__int_as_float(ci[INT_MA1 + 2]), __int_as_float(ci[INT_MA1 + 3]))));
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
@@ -591,62 +623,44 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
             sRA[(32 * jt + crow(r, lg)) * RSA + lr] = hv;   // A1 copy [j][h_l]
           }
       }
+      __syncthreads();   // every wave's A1 copy
 
-      // ================= O = A1 W2^T: wave partials -> this half's sum (two passes of 32 rows) =================
-      float om[2][8];
-      const int rj = lane >> 3, rc = (lane & 7) * 8;   // this lane's 8 outputs of a reduced row block
-      h8 w2f[2][2];   // W2 operand fragments [ct][st] (scaled fp16), reused for the W2 copy
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int st = 0; st < 2; ++st) w2f[ct][st] = state_frag(W2m[ct], st, e2);
-#pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          f16v acc = {};
-#pragma unroll
-          for (int st = 0; st < 2; ++st)
-            acc = mfma(lds_frag(sRA + (32 * pass + lr) * RSA, 16 * st, lg), w2f[ct][st], acc);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sRP[crow(r, lg) * RSF + 32 * ct + lr] = ldexpf(acc[r], -(eA1 + e2));
-        }
-        __syncthreads();
-        const int jl = 8 * w + rj;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) om[pass][i] = 0.f;
+      // ================= this half's O^T = W2 A1^T over its 128 hidden units =================
+      // wave w: the 32 x 32 tile (tokens 32 jt.., columns 32 ct..), jt = w >> 1,
+      // ct = w & 1, straight from the four waves' A1 and W2 [c][h_l] copies;
+      // lane = token j = 32 jt + lr, its 16 columns c = 32 ct + 8g + 4lg + q
+      // (register 4g + q)
+      float om[16];
+      const int tj = 32 * (w >> 1) + lr, tc = 32 * (w & 1) + 4 * lg;
+      {
+        f16v acc = {};
 #pragma unroll
         for (int src = 0; src < kWaves; ++src) {
-          const float* sp = (const float*)(smem + OFF_WAVE + src * kWaveRegion + kA1Bytes) + jl * RSF + rc;
-          const f4v x0 = *(const f4v*)sp, x1 = *(const f4v*)(sp + 4);
-          om[pass][0] += x0[0]; om[pass][1] += x0[1]; om[pass][2] += x0[2]; om[pass][3] += x0[3];
-          om[pass][4] += x1[0]; om[pass][5] += x1[1]; om[pass][6] += x1[2]; om[pass][7] += x1[3];
+          const _Float16* a1 = (const _Float16*)(smem + OFF_WAVE + src * kWaveRegion);
+          const _Float16* w2 = (const _Float16*)(smem + OFF_WAVE + src * kWaveRegion + kA1Bytes + kW2Bytes);
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+            acc = mfma(lds_frag(w2 + (32 * (w & 1) + lr) * RSA, 16 * st, lg),
+                       lds_frag(a1 + (32 * (w >> 1) + lr) * RSA, 16 * st, lg), acc);
         }
-        __syncthreads();
+        const float co = pow2neg(eA1 + e2);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) om[r] = acc[r] * co;
       }
       // publish this half's O (and, implied by the flag, last chunk's y partial)
       const unsigned par = seq & 1u;
 #pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) xstore2(xO_me + par * kB * kD, 4 * pass + i / 2, tid, om[pass][i], om[pass][i + 1]);
-      }
-
-      // ---- work that does not need the partner: W2 copy, prefetch ----
-      // W2 copy for the backprop: [h_l][c] fp16 (the O partial buffer is free again)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          sRW[crow(r, lg) * RS + 32 * ct + lr] = w2f[ct][r >> 3][r & 7];
+      for (int e = 0; e < 8; ++e) xstore2(xO_me + par * kB * kD, e, tid, om[2 * e], om[2 * e + 1]);
 
       // loads issued right after this half's flag: this chunk's V (used
       // after the handshake)
-      uint4 vr0 = make_uint4(0, 0, 0, 0), vr1 = make_uint4(0, 0, 0, 0);
+      uint2 vq[4] = {make_uint2(0, 0), make_uint2(0, 0), make_uint2(0, 0), make_uint2(0, 0)};
       auto issue_loads = [&] {
-        const int j0 = 8 * w + rj, j1 = 32 + 8 * w + rj;
-        if (j0 < n) vr0 = *(const uint4*)(p.v + (tok0 + c0 + j0) * kD + rc);
-        if (j1 < n) vr1 = *(const uint4*)(p.v + (tok0 + c0 + j1) * kD + rc);
+        // V[tj][tc + 8g .. +3] for this thread's O elements
+        if (tj < n) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) vq[g] = *(const uint2*)(p.v + (tok0 + c0 + tj) * kD + tc + 8 * g);
+        }
       };
 
       // ================= a1: coefficients (both halves compute them identically) =================
@@ -726,9 +740,9 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       if (!handshake(seq + 2, issue_loads, coef_work)) { failed = true; break; }
       // the partner's data (published before its flag) is loaded now and
       // used after the D completion, the update weights and SC1
-      float pvv[2][8], pyv[8];
-      xload8(xO_pt + par * kB * kD, 0, tid, pvv[0]);   // rows 8w + rj, columns rc .. rc+7
-      xload8(xO_pt + par * kB * kD, 4, tid, pvv[1]);   // rows 32 + 8w + rj
+      float pvv[16], pyv[8];
+      xload8(xO_pt + par * kB * kD, 0, tid, pvv);       // the partner's values of this thread's O elements
+      xload8(xO_pt + par * kB * kD, 4, tid, pvv + 8);
       if (prev_row0 >= 0) load_prev_y(par ^ 1u, pyv);
       {
         // D rows 32..63 of columns 0..31: 8 row groups x 32 columns, 4 rows each
@@ -780,28 +794,20 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       }
 
       // ================= O = half 0 + half 1, Delta2 = O - V =================
-      float d2v[2][8];
+      float d2v[16];
       {
         float am = 0.f;
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-          const int j = 32 * pass + 8 * w + rj;
-          const float* pv = pvv[pass];
-          if (j < n) {
-            const uint4 vu = pass ? vr1 : vr0;
-            const unsigned vw[4] = {vu.x, vu.y, vu.z, vu.w};
+        for (int g = 0; g < 4; ++g) {
+          const unsigned vw[2] = {vq[g].x, vq[g].y};
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const float o = half == 0 ? om[pass][i] + pv[i] : pv[i] + om[pass][i];
-              const float vv = __uint_as_float((i & 1) ? (vw[i >> 1] & 0xffff0000u) : (vw[i >> 1] << 16));
-              d2v[pass][i] = o - vv;
-            }
-          } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) d2v[pass][i] = 0.f;
+          for (int q = 0; q < 4; ++q) {
+            const int r = 4 * g + q;
+            const float o = half == 0 ? om[r] + pvv[r] : pvv[r] + om[r];
+            const float vv = __uint_as_float((q & 1) ? (vw[q >> 1] & 0xffff0000u) : (vw[q >> 1] << 16));
+            d2v[r] = tj < n ? o - vv : 0.f;
+            am = fmaxf(am, fabsf(d2v[r]));
           }
-#pragma unroll
-          for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(d2v[pass][i]));
         }
         am = wave_max(am);
         if (lane == 0) atomicMax((unsigned int*)&ci[INT_AMAX_D2], __float_as_uint(am));
@@ -816,15 +822,14 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       }
       const int eD2 = scale_exp(__uint_as_float((unsigned)ci[INT_AMAX_D2]));
 #pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
-        const int j = 32 * pass + 8 * w + rj;
-        h8 hv;
+      for (int g = 0; g < 4; ++g) {
+        h4 hv;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) hv[i] = (_Float16)ldexpf(d2v[pass][i], eD2);
-        *(h4*)(sD2 + j * RS + rc) = h4{hv[0], hv[1], hv[2], hv[3]};
-        *(h4*)(sD2 + j * RS + rc + 4) = h4{hv[4], hv[5], hv[6], hv[7]};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) sD2T[(rc + i) * RS + j] = hv[i];
+        for (int q = 0; q < 4; ++q) {
+          hv[q] = (_Float16)ldexpf(d2v[4 * g + q], eD2);
+          sD2T[(tc + 8 * g + q) * RS + tj] = hv[q];
+        }
+        *(h4*)(sD2 + tj * RS + tc + 8 * g) = hv;
       }
       __syncthreads();
 
