@@ -561,6 +561,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       // A1 = SiLU(Z1) (scaled fp16: kept for the update, copied to LDS for the
       // contractions over h), SiLU'(Z1) (fp16, for backprop)
       h8 A1h[2][2], SPh[2][2];
+      h8 w1f[2][2];   // W1 operand fragments (scaled fp16), reused by the layer-1 retrieval
       int eA1;
       {
         f16v Z[2];
@@ -570,10 +571,10 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
-            const h8 wf = state_frag(W1m[ct], st, e1);
+            w1f[ct][st] = state_frag(W1m[ct], st, e1);
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt)
-              zacc[jt] = mfma(lds_frag(sK + (32 * jt + lr) * RS, 32 * ct + 16 * st, lg), wf, zacc[jt]);
+              zacc[jt] = mfma(lds_frag(sK + (32 * jt + lr) * RS, 32 * ct + 16 * st, lg), w1f[ct][st], zacc[jt]);
           }
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
@@ -879,7 +880,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
-            const h8 wf = state_frag(W1m[ct], st, e1), sf = state_frag(S1m[ct], st, e1);
+            const h8 wf = w1f[ct][st], sf = state_frag(S1m[ct], st, e1);
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt) {
               const h8 qf = lds_frag(sQ + (32 * jt + lr) * RS, 32 * ct + 16 * st, lg);
@@ -917,7 +918,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
-            const h8 wf = state_frag(W1m[ct], st, e1);
+            const h8 wf = w1f[ct][st];
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt)
               accZ[jt] = mfma(wf, lds_frag(sQ + (32 * jt + lr) * RS, 32 * ct + 16 * st, lg), accZ[jt]);
@@ -986,17 +987,19 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
             const f4v dv = *(const f4v*)(sDM + j * RSF + 32 * it + 8 * g + 4 * lg);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const float x = ldexpf(acc[4 * g + q], -(eA1 + eH1[jt])) * dv[q];
+              // unscaled by 2^-(eA1 + eH1) through the exponent below, not per element
+              const float x = acc[4 * g + q] * dv[q];
               Pf[it][4 * g + q] = x;
               am = fmaxf(am, fabsf(x));
             }
           }
         }
-        eDP[jt] = scale_exp(wave_max(am));
+        const int er = scale_exp(wave_max(am));
+        eDP[jt] = er + eA1 + eH1[jt];   // the scale of the true scores
 #pragma unroll
         for (int it = 0; it < 2; ++it)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) DPh[it][jt][r >> 3][r & 7] = (_Float16)ldexpf(Pf[it][r], eDP[jt]);
+          for (int r = 0; r < 16; ++r) DPh[it][jt][r >> 3][r & 7] = (_Float16)ldexpf(Pf[it][r], er);
       }
 
       // ================= a5 layer 2: y^T partial = W2 (A H1)^T + S2 (F H1)^T - Delta2^T (D o P)^T =================
