@@ -288,6 +288,15 @@ __device__ __forceinline__ void xload8(const float* base, int e0, int t, float* 
   }
 }
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+// A flag read through the XCD's L2: a scalar load that bypasses the scalar
+// cache (glc).  Valid when the writer runs on the same XCD, whose stores pass
+// through that L2; a writer on another XCD could leave a stale L2 line, so the
+// caller uses it only after checking that both halves share an XCD.
+__device__ __forceinline__ unsigned load_flag_l2(const unsigned* f) {
+  unsigned v;
+  asm volatile("s_load_dword %0, %1, 0x0 glc\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(f) : "memory");
+  return v;
+}
 
 // one thread's share of a chunk's raw inputs: 16 bf16 of a K row and of a Q
 // row (row j = tid/4, columns (tid%4)*16..), and for tid < 64 the gates of
@@ -437,6 +446,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
   // that must not delay the flag: the flag waits for this wave's earlier
   // memory operations, loads included), then waves 1..3 run `during` while
   // thread 0 waits for the partner's `seq`; false = gave up
+  bool same_xcd = false;   // set after the first handshake (which polls through memory)
   auto handshake = [&](unsigned seq, auto&& first, auto&& during) -> bool {
     wait_stores();
     __syncthreads();
@@ -444,9 +454,16 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
     first();
     if (tid == 0) {
       unsigned it = 0;
-      while (__hip_atomic_load(flag_pt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < seq) {
-        if (++it >= p.spin_max) break;
-        __builtin_amdgcn_s_sleep(1);
+      if (same_xcd) {
+        while (load_flag_l2(flag_pt) < seq) {
+          if (++it >= p.spin_max) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+      } else {
+        while (__hip_atomic_load(flag_pt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < seq) {
+          if (++it >= p.spin_max) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
       }
       const int ok = it < p.spin_max;
       if (!ok) __hip_atomic_store(p.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -459,8 +476,14 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
   };
   auto nothing = [] {};
 
-  // the pair starts together (also flushes any stale flag value of this launch)
+  // the pair starts together, polling through memory; each half also
+  // publishes the XCD it runs on (before its flag), and when the two agree
+  // the later polls read the flag through the shared L2
+  const unsigned xcc_me = __builtin_amdgcn_s_getreg((15 << 11) | 20) & 0xfu;   // HW_REG_XCC_ID
+  if (tid == 0) __hip_atomic_store(flag_me + 1, xcc_me, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (!handshake(1u, nothing, nothing)) failed0 = true;
+  same_xcd = __builtin_amdgcn_readfirstlane(
+                 __hip_atomic_load(flag_pt + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == xcc_me ? 1 : 0) != 0;
 
   // my y rows of the previous chunk, kept across the chunk boundary:
   // thread t covers row j = 32*half + t/8, columns (t%8)*8 .. +8
