@@ -713,28 +713,33 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
           const float thi = cf[COEF_THETA + i];
           float di = 0.f, t = 0.f;
           float* drow = sDM + j0 * RSF + i;
+          // the 32 rows stay in registers and are stored after the loop, so the
+          // gate reads below never wait behind row stores
+          float drows[32];
           auto step = [&](int jj, float ga, float ge) {
             // theta_i in lane j only: a select on the lane mask 1 << j
             float inj;
             asm("v_cndmask_b32_e64 %0, 0, %1, %2" : "=v"(inj) : "v"(thi), "s"(1ull << (j0 + jj)));
             t = fmaf(ge, t, inj);
             di = fmaf(ga, di, t);
-            drow[jj * RSF] = di;
+            drows[jj] = di;
           };
           // the steps' (1 - alpha_j, eta_j) pairs (padding included) as LDS
-          // broadcasts, two steps per 16-byte read, a batch of 8 steps ahead
+          // broadcasts, two steps per 16-byte read, 16 steps per batch
           const float4* pairs4 = (const float4*)(smem + OFF_COEF + COEF_PAIR) + j0 / 2;
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            float4 g[4];
+          for (int b = 0; b < 2; ++b) {
+            float4 g[8];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) g[q] = pairs4[4 * b + q];
+            for (int q = 0; q < 8; ++q) g[q] = pairs4[8 * b + q];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              step(8 * b + 2 * q, g[q].x, g[q].y);
-              step(8 * b + 2 * q + 1, g[q].z, g[q].w);
+            for (int q = 0; q < 8; ++q) {
+              step(16 * b + 2 * q, g[q].x, g[q].y);
+              step(16 * b + 2 * q + 1, g[q].z, g[q].w);
             }
           }
+#pragma unroll
+          for (int jj = 0; jj < 32; ++jj) drow[jj * RSF] = drows[jj];
           // wave 3: t at row 31 for i < 32; wave 1: t at row 63 (= U_i) for i >= 32
           if ((w == 3) == (i < 32)) cf[COEF_XT + i] = t;
         } else {
