@@ -1210,18 +1210,14 @@ hipError_t launch_mlp2(const Shape& s, int chunk, const void* k, const void* v, 
                        const float* alpha, const float* eta, const float* theta,
                        const float* W_in, const float* S_in, void* y, float* W_out,
                        float* S_out, void* ws, hipStream_t stream) {
-  static bool configured = false;   // attributes set once per process (idempotent)
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute((const void*)mlp2_pair_kernel<true>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)mlp2_pair_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            kLdsBytes);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  // the kernel's dynamic LDS size, set on every call (no state kept between
+  // calls; idempotent and cheap next to the kernel)
+  const void* kfn = s.read_mode == TM_READ_AFTER_WRITE ? (const void*)mlp2_pair_kernel<true>
+                                                       : (const void*)mlp2_pair_kernel<false>;
+  hipError_t e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  if (e != hipSuccess) return e;
   int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
+  e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
