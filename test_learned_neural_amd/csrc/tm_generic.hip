@@ -32,7 +32,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTile = 64;
-constexpr int kTk = 16;
 
 struct GParams {
   int N, d, L, io, read_mode, chunk;
@@ -75,53 +74,60 @@ __device__ __forceinline__ void store_io(void* p, int64_t i, float x, int io) {
     ((float*)p)[i] = x;
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
 // C[M x N] = sum_k A(m, k) B(k, n), handed to epi(m, n, value).  The whole
 // workgroup cooperates; operands come through accessors (global/L2 reads)
-// and are staged through LDS in 64 x 16 / 16 x 64 tiles.
+// and are staged through LDS in kGk x 64 k-major tiles, the next tile's
+// operands loaded into registers while the current one is multiplied.  Each
+// of the four waves computes one 32 x 32 quarter of a 64 x 64 output tile
+// with the fp32 matrix instruction v_mfma_f32_32x32x2_f32 (lane l supplies
+// A[l%32][l/32] and B[l/32][l%32]; accumulator register r holds row
+// 8(r/4) + 4(l/32) + r%4, column l%32), so the arithmetic stays fp32.
+constexpr int kGk = 32;                                  // k per staged tile
+constexpr int kGPer = kTile * kGk / kThreads;             // operand elements per thread per tile
 template <class FA, class FB, class FE>
 __device__ void block_gemm(int M, int N, int K, FA fa, FB fb, FE epi) {
-  __shared__ float As[kTk][kTile + 1];
-  __shared__ float Bs[kTk][kTile + 1];
+  __shared__ float As[kGk][kTile + 1];
+  __shared__ float Bs[kGk][kTile + 1];
   const int tid = threadIdx.x;
-  const int tx = tid % 16, ty = tid / 16;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int wm = (wv >> 1) * 32, wn = (wv & 1) * 32;   // this wave's quarter
+  const int li = lane & 31, lk = lane >> 5;
   for (int m0 = 0; m0 < M; m0 += kTile) {
     for (int n0 = 0; n0 < N; n0 += kTile) {
-      float acc[4][4];
+      float ra[kGPer], rb[kGPer];
+      auto fetch = [&](int k0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-      for (int k0 = 0; k0 < K; k0 += kTk) {
-        for (int e = tid; e < kTile * kTk; e += kThreads) {
-          const int mm = e / kTk, kk = e % kTk;
-          As[kk][mm] = (m0 + mm < M && k0 + kk < K) ? fa(m0 + mm, k0 + kk) : 0.f;
+        for (int q = 0; q < kGPer; ++q) {
+          const int e = tid + q * kThreads;
+          const int mm = e / kGk, ka = e % kGk;        // A element (m0 + mm, k0 + ka)
+          ra[q] = (m0 + mm < M && k0 + ka < K) ? fa(m0 + mm, k0 + ka) : 0.f;
+          const int kb = e / kTile, nn = e % kTile;    // B element (k0 + kb, n0 + nn)
+          rb[q] = (n0 + nn < N && k0 + kb < K) ? fb(k0 + kb, n0 + nn) : 0.f;
         }
-        for (int e = tid; e < kTk * kTile; e += kThreads) {
-          const int kk = e / kTile, nn = e % kTile;
-          Bs[kk][nn] = (n0 + nn < N && k0 + kk < K) ? fb(k0 + kk, n0 + nn) : 0.f;
+      };
+      fetch(0);
+      f32x16 acc = {};
+      for (int k0 = 0; k0 < K; k0 += kGk) {
+#pragma unroll
+        for (int q = 0; q < kGPer; ++q) {
+          const int e = tid + q * kThreads;
+          As[e % kGk][e / kGk] = ra[q];
+          Bs[e / kTile][e % kTile] = rb[q];
         }
         __syncthreads();
+        if (k0 + kGk < K) fetch(k0 + kGk);   // in flight during the products below
 #pragma unroll
-        for (int kk = 0; kk < kTk; ++kk) {
-          float a[4], bb[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) bb[j] = Bs[kk][tx + 16 * j];
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], bb[j], acc[i][j]);
-        }
+        for (int kk = 0; kk < kGk; kk += 2)
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[kk + lk][wm + li], Bs[kk + lk][wn + li], acc, 0, 0, 0);
         __syncthreads();
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int m = m0 + ty + 16 * i, n = n0 + tx + 16 * j;
-          if (m < M && n < N) epi(m, n, acc[i][j]);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm + 8 * (r >> 2) + 4 * lk + (r & 3), n = n0 + wn + li;
+        if (m < M && n < N) epi(m, n, acc[r]);
+      }
     }
   }
   __syncthreads();
