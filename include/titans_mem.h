@@ -75,6 +75,11 @@ extern "C" {
 
 /* flags */
 #define TM_FLAG_FORCE_GENERIC 1u  /* run the shape-generic fp32 kernel even where a specialised one exists */
+#define TM_FLAG_CHUNK_GATES   2u  /* alpha, eta, theta hold one value per chunk, [B,H,ceil(N/chunk)],
+                                     shared by the chunk's tokens ("Titans: Learning to Memorize at
+                                     Test Time", mer.dev notes, section 3.2 "Parameters as the
+                                     Function of Chunks": inside a chunk the update is then
+                                     time-invariant) */
 
 /* kernel paths reported by titans_mem_select_path */
 #define TM_PATH_GENERIC_F32   0   /* any shape: fp32 VALU, state in global memory */
@@ -113,6 +118,7 @@ int64_t titans_mem_workspace_bytes(const titans_mem_desc* desc, int32_t chunk);
  *   k, v, q    [B,H,N,d]  io dtype, device, read-only
  *   alpha, eta, theta  [B,H,N] fp32, device, read-only: forgetting gate,
  *              surprise decay, momentary-surprise weight
+ *              ([B,H,ceil(N/chunk)] with TM_FLAG_CHUNK_GATES)
  *   W_in, S_in [B,H,P]  fp32, device, read-only: memory weights and
  *              surprise momentum before token 0
  *   chunk      b >= 1: tokens per chunk (gradients at the chunk-start state)

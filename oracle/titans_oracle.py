@@ -99,14 +99,24 @@ def memory_grad(W: np.ndarray, k: np.ndarray, v: np.ndarray, d: int, hidden: int
 
 
 def forward(k, v, q, alpha, eta, theta, W_in, S_in, *, d: int, hidden: int, n_layers: int,
-            chunk: int, read_mode: int = 0, threads: int = 0, want_w_norm: bool = False):
+            chunk: int, read_mode: int = 0, threads: int = 0, want_w_norm: bool = False,
+            chunk_gates: bool = False):
     """Chunked memory over independent streams (leading axis of every array).
 
     k, v, q: [S, N, d]; alpha, eta, theta: [S, N]; W_in, S_in: [S, P].
     Returns (y [S,N,d], W_out [S,P], S_out [S,P]) and, if asked, the
     per-chunk ||W||_F trajectory [S, ceil(N/chunk)].
+
+    chunk_gates: alpha, eta, theta are [S, ceil(N/chunk)], one value per
+    chunk shared by all its tokens ("Parameters as the Function of Chunks",
+    mer.dev notes section 3.2); the token loop then runs with each token
+    taking its chunk's values.
     """
     k, v, q = _c(k), _c(v), _c(q)
+    if chunk_gates:
+        N = k.shape[1]
+        alpha, eta, theta = (np.repeat(np.asarray(g, np.float64), chunk, axis=1)[:, :N]
+                             for g in (alpha, eta, theta))
     alpha, eta, theta = _c(alpha), _c(eta), _c(theta)
     W_in, S_in = _c(W_in), _c(S_in)
     S, N = alpha.shape

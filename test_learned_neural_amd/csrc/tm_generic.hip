@@ -35,6 +35,7 @@ constexpr int kTile = 64;
 
 struct GParams {
   int N, d, L, io, read_mode, chunk;
+  int chunk_gates;   // gates hold one value per chunk
   int widths[kMaxLayers + 1];
   int64_t off[kMaxLayers + 1];
   int64_t P;
@@ -185,9 +186,13 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
 
   for (int c0 = 0; c0 < p.N; c0 += p.chunk) {
     const int n = min(p.chunk, p.N - c0);
-    const float* al = p.alpha + tok0 + c0;
-    const float* et = p.eta + tok0 + c0;
-    const float* th = p.theta + tok0 + c0;
+    // the chunk's gates: token j at index j * gs (one shared value when the
+    // gates are given per chunk)
+    const int64_t g0 = p.chunk_gates ? (int64_t)s * ((p.N + p.chunk - 1) / p.chunk) + c0 / p.chunk : tok0 + c0;
+    const int gs = p.chunk_gates ? 0 : 1;
+    const float* al = p.alpha + g0;
+    const float* et = p.eta + g0;
+    const float* th = p.theta + g0;
 
     // ---- load the chunk's keys, values and queries (fp32 copies) ----
     for (int e = tid; e < n * d; e += kThreads) {
@@ -198,22 +203,22 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
     }
     // ---- a1: coefficient recurrences (one thread per column i of D) ----
     for (int i = tid; i < n; i += kThreads) {
-      float di = th[i], pr = 1.f;
+      float di = th[i * gs], pr = 1.f;
       for (int j = 0; j < i; ++j) w.D[j * n + i] = 0.f;
       w.D[i * n + i] = di;
       for (int j = i + 1; j < n; ++j) {
-        pr *= et[j];
-        di = (1.f - al[j]) * di + th[i] * pr;
+        pr *= et[j * gs];
+        di = (1.f - al[j * gs]) * di + th[i * gs] * pr;
         w.D[j * n + i] = di;
       }
-      w.U[i] = th[i] * pr;
+      w.U[i] = th[i * gs] * pr;
     }
     if (tid == 0) {
       float a = 1.f, e = 1.f, f = 0.f;
       for (int j = 0; j < n; ++j) {
-        a *= 1.f - al[j];
-        e *= et[j];
-        f = (1.f - al[j]) * f + e;
+        a *= 1.f - al[j * gs];
+        e *= et[j * gs];
+        f = (1.f - al[j * gs]) * f + e;
         w.A[j] = a;
         w.E[j] = e;
         w.F[j] = f;
@@ -382,6 +387,7 @@ GParams make_params(const Shape& s, int chunk) {
   p.L = s.L;
   p.io = s.io;
   p.read_mode = s.read_mode;
+  p.chunk_gates = s.chunk_gates;
   p.chunk = chunk;
   for (int l = 0; l <= s.L; ++l) p.widths[l] = s.widths[l];
   for (int l = 1; l <= s.L; ++l) p.off[l] = s.off[l];

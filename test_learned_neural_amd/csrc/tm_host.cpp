@@ -18,7 +18,7 @@ int build_shape(const titans_mem_desc* desc, Shape* s) {
   if (desc->io_dtype != TM_IO_F32 && desc->io_dtype != TM_IO_BF16) return TM_ERR_INVALID;
   if (desc->read_mode != TM_READ_AFTER_WRITE && desc->read_mode != TM_READ_CHUNK_START)
     return TM_ERR_INVALID;
-  if (desc->flags & ~TM_FLAG_FORCE_GENERIC) return TM_ERR_INVALID;
+  if (desc->flags & ~(TM_FLAG_FORCE_GENERIC | TM_FLAG_CHUNK_GATES)) return TM_ERR_INVALID;
   if (desc->n_layers > titans::kMaxLayers) return TM_ERR_UNSUPPORTED;
   const int64_t streams = (int64_t)desc->B * desc->H;
   if (streams > (int64_t)1 << 30) return TM_ERR_UNSUPPORTED;
@@ -29,6 +29,7 @@ int build_shape(const titans_mem_desc* desc, Shape* s) {
   s->L = desc->n_layers;
   s->io = desc->io_dtype;
   s->read_mode = desc->read_mode;
+  s->chunk_gates = (desc->flags & TM_FLAG_CHUNK_GATES) ? 1 : 0;
   s->widths[0] = desc->d;
   for (int l = 1; l < s->L; ++l) s->widths[l] = desc->hidden;
   s->widths[s->L] = desc->d;
@@ -124,7 +125,8 @@ int titans_mem_forward(const titans_mem_desc* desc, const void* k, const void* v
 
   const int64_t esz = s.io == TM_IO_BF16 ? 2 : 4;
   const int64_t tok_bytes = (int64_t)s.streams * s.N * s.d * esz;
-  const int64_t gate_bytes = (int64_t)s.streams * s.N * 4;
+  const int64_t gate_rows = s.chunk_gates ? ((int64_t)s.N + chunk - 1) / chunk : s.N;
+  const int64_t gate_bytes = (int64_t)s.streams * gate_rows * 4;
   const int64_t state_bytes = (int64_t)s.streams * s.P * 4;
   const Range ranges[] = {
       {(const char*)k, tok_bytes, false},          {(const char*)v, tok_bytes, false},

@@ -17,6 +17,7 @@ constexpr int kMaxWidthRetrieve = 1024;
 
 struct Shape {
   int streams, N, d, hidden, L, io, read_mode;
+  int chunk_gates;   // gates given per chunk (TM_FLAG_CHUNK_GATES)
   int widths[kMaxLayers + 1];
   int64_t off[kMaxLayers + 1];
   int64_t P;

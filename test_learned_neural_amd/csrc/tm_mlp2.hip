@@ -131,7 +131,13 @@ struct Params {
   unsigned* flags;       // n_pairs * 2 flags, kFlagStride apart
   unsigned* status;      // set to 1 when a pair gave up waiting
   unsigned spin_max;
+  int chunk_gates;       // gates hold one value per chunk
 };
+
+// index of token t0's gate, and the step per following token of the chunk
+__device__ __forceinline__ int64_t gate_base(const Params& p, int s, int c0) {
+  return p.chunk_gates ? (int64_t)s * ((p.N + p.chunk - 1) / p.chunk) + c0 / p.chunk : (int64_t)s * p.N + c0;
+}
 
 // accumulator row of register r for lane group lg (32x32 tile)
 __device__ __forceinline__ int crow(int r, int lg) { return 8 * (r >> 2) + 4 * lg + (r & 3); }
@@ -307,7 +313,7 @@ struct ChunkRegs {
   float ga, ge, gt;
 };
 
-__device__ __forceinline__ ChunkRegs load_chunk_regs(const Params& p, int64_t row0, int n, int tid) {
+__device__ __forceinline__ ChunkRegs load_chunk_regs(const Params& p, int64_t row0, int64_t g0, int n, int tid) {
   ChunkRegs r;
   const int j = tid >> 2, cb = (tid & 3) * 16;
   if (j < n) {
@@ -319,9 +325,10 @@ __device__ __forceinline__ ChunkRegs load_chunk_regs(const Params& p, int64_t ro
   }
   r.ga = 0.f; r.ge = 1.f; r.gt = 0.f;
   if (tid < kB && tid < n) {
-    r.ga = p.alpha[row0 + tid];
-    r.ge = p.eta[row0 + tid];
-    r.gt = p.theta[row0 + tid];
+    const int64_t gi = g0 + (p.chunk_gates ? 0 : tid);
+    r.ga = p.alpha[gi];
+    r.ge = p.eta[gi];
+    r.gt = p.theta[gi];
   }
   return r;
 }
@@ -334,7 +341,8 @@ __device__ __forceinline__ ChunkRegs load_chunk_regs(const Params& p, int64_t ro
 // i-th 16 bytes.  Wave 0 loads the gates.  Rows and tokens past the chunk end
 // are left out and replaced on unstaging.
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
-__device__ __forceinline__ void prefetch_chunk_lds(const Params& p, int64_t row0, int n, int tid, unsigned char* stage) {
+__device__ __forceinline__ void prefetch_chunk_lds(const Params& p, int64_t row0, int64_t g0, int n, int tid,
+                                                   unsigned char* stage) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int j = tid >> 2, cb = (tid & 3) * 16;
   uint4* sk = (uint4*)stage;
@@ -350,9 +358,10 @@ __device__ __forceinline__ void prefetch_chunk_lds(const Params& p, int64_t row0
   }
   if (w == 0 && lane < n) {
     float* g = (float*)(stage + 2 * kB * kD * 2);
-    __builtin_amdgcn_global_load_lds((const void*)(p.alpha + row0 + lane), (lds_void_ptr)g, 4, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(p.eta + row0 + lane), (lds_void_ptr)(g + kB), 4, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(p.theta + row0 + lane), (lds_void_ptr)(g + 2 * kB), 4, 0, 0);
+    const int64_t gi = g0 + (p.chunk_gates ? 0 : lane);   // per-chunk gates: every lane loads the one value
+    __builtin_amdgcn_global_load_lds((const void*)(p.alpha + gi), (lds_void_ptr)g, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(p.eta + gi), (lds_void_ptr)(g + kB), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(p.theta + gi), (lds_void_ptr)(g + 2 * kB), 4, 0, 0);
   }
 }
 
@@ -541,7 +550,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       {
         // rows come from the staging area when the previous chunk prefetched them
         if (staged) __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's staging loads (long done)
-        const ChunkRegs cr = staged ? unstage_chunk_regs(smem + OFF_STAGE, n, tid) : load_chunk_regs(p, tok0 + c0, n, tid);
+        const ChunkRegs cr = staged ? unstage_chunk_regs(smem + OFF_STAGE, n, tid) : load_chunk_regs(p, tok0 + c0, gate_base(p, s, c0), n, tid);
         const int j = tid >> 2, cb = (tid & 3) * 16;
         _Float16 kv[16], qv[16];
         bf16x8_to_h(cr.k0, kv);
@@ -571,7 +580,9 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       int next_s = s, next_c0 = c0 + p.chunk;
       if (next_c0 >= p.N) { next_s = s + p.n_pairs; next_c0 = 0; }
       const bool has_next = next_s < p.streams && p.N > 0;
-      if (has_next) prefetch_chunk_lds(p, (int64_t)next_s * p.N + next_c0, min(p.chunk, p.N - next_c0), tid, smem + OFF_STAGE);
+      if (has_next)
+        prefetch_chunk_lds(p, (int64_t)next_s * p.N + next_c0, gate_base(p, next_s, next_c0), min(p.chunk, p.N - next_c0),
+                           tid, smem + OFF_STAGE);
       staged = has_next;
 
       // state scales: W1/S1 per wave; W2/S2 joint over the workgroup (the
@@ -1246,6 +1257,7 @@ hipError_t launch_mlp2(const Shape& s, int chunk, const void* k, const void* v, 
   p.flags = (unsigned*)(base + pairs_for(s) * kPairBytes);
   p.status = (unsigned*)(base + pairs_for(s) * kPairBytes + 2 * pairs_for(s) * kFlagStride);
   p.spin_max = kSpinMax;
+  p.chunk_gates = s.chunk_gates;
   hipLaunchKernelGGL(zero_flags_kernel, dim3(1), dim3(256), 0, stream, p.flags, (int)(2 * np), p.status);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

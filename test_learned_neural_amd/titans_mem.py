@@ -18,6 +18,7 @@ IO_F32, IO_BF16 = 0, 1
 ACT_SILU = 0
 READ_AFTER_WRITE, READ_CHUNK_START = 0, 1
 FLAG_FORCE_GENERIC = 1
+FLAG_CHUNK_GATES = 2
 PATH_GENERIC_F32, PATH_MLP2_D64_H256 = 0, 1
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtitans_mem.so")
@@ -129,26 +130,28 @@ def _check(t, name, shape, dtype, device):
 
 
 def forward(k, v, q, alpha, eta, theta, W_in, S_in, chunk: int, *, hidden: int, n_layers: int,
-            read_mode: int = READ_AFTER_WRITE, force_generic: bool = False,
+            read_mode: int = READ_AFTER_WRITE, force_generic: bool = False, chunk_gates: bool = False,
             y_out=None, W_out=None, S_out=None, workspace=None) -> Tuple:
     """Run titans_mem_forward on torch tensors.
 
     k, v, q: [B, H, N, d] (float32 or bfloat16); alpha, eta, theta: [B, H, N]
-    float32; W_in, S_in: [B, H, P] float32.  Returns (y, W_out, S_out).
+    float32 ([B, H, ceil(N / chunk)] with chunk_gates: one value per chunk);
+    W_in, S_in: [B, H, P] float32.  Returns (y, W_out, S_out).
     """
     torch = _torch()
     B, H, N, d = k.shape
     io = "bf16" if k.dtype == torch.bfloat16 else "f32"
     desc = make_desc(B, H, N, d, hidden, n_layers, io, read_mode,
-                     FLAG_FORCE_GENERIC if force_generic else 0)
+                     (FLAG_FORCE_GENERIC if force_generic else 0) | (FLAG_CHUNK_GATES if chunk_gates else 0))
     P = param_count(desc)
     if P < 0:
         raise TitansMemError(P, "titans_mem_param_count")
     dev = k.device
     for name, t in (("k", k), ("v", v), ("q", q)):
         _check(t, name, (B, H, N, d), k.dtype, dev)
+    n_gates = (N + chunk - 1) // chunk if chunk_gates and chunk > 0 else N
     for name, t in (("alpha", alpha), ("eta", eta), ("theta", theta)):
-        _check(t, name, (B, H, N), torch.float32, dev)
+        _check(t, name, (B, H, n_gates), torch.float32, dev)
     for name, t in (("W_in", W_in), ("S_in", S_in)):
         _check(t, name, (B, H, P), torch.float32, dev)
     if y_out is None:

@@ -21,7 +21,8 @@ TOL = {"f32": 1e-3, "bf16": 2e-2}
 def to_device(cfg, inp, n_streams_shape=None, device="cuda"):
     """numpy inputs -> torch device tensors shaped [B, H, N, ...]."""
     import torch
-    S, N = inp["alpha"].shape
+    S, N = inp["k"].shape[:2]
+    G = inp["alpha"].shape[1]       # N per-token gates, or one per chunk
     B, H = n_streams_shape if n_streams_shape else (cfg.B, cfg.H)
     assert B * H == S
 
@@ -36,7 +37,7 @@ def to_device(cfg, inp, n_streams_shape=None, device="cuda"):
         return torch.from_numpy(np.ascontiguousarray(a)).reshape(B, H, last).to(device)
 
     return dict(k=tok(inp["k"]), v=tok(inp["v"]), q=tok(inp["q"]),
-                alpha=per(inp["alpha"], N), eta=per(inp["eta"], N), theta=per(inp["theta"], N),
+                alpha=per(inp["alpha"], G), eta=per(inp["eta"], G), theta=per(inp["theta"], G),
                 W0=per(inp["W0"], cfg.param_count), S0=per(inp["S0"], cfg.param_count))
 
 
@@ -56,13 +57,22 @@ def run_gpu(cfg, dev, chunk=None, **kw):
                        hidden=cfg.hidden, n_layers=cfg.n_layers, **kw)
 
 
-def run_oracle(cfg, inp, chunk=None, read_mode=0, threads=0):
+def run_oracle(cfg, inp, chunk=None, read_mode=0, threads=0, chunk_gates=False):
     import oracle
     f = wl.inputs_f64(cfg, inp)
     return oracle.forward(f["k"], f["v"], f["q"], f["alpha"], f["eta"], f["theta"], f["W0"], f["S0"],
                           d=cfg.d, hidden=cfg.hidden, n_layers=cfg.n_layers,
                           chunk=cfg.chunk if chunk is None else chunk, read_mode=read_mode,
-                          threads=threads)
+                          threads=threads, chunk_gates=chunk_gates)
+
+
+def chunk_gate_inputs(inp, chunk):
+    """The same inputs with one gate value per chunk (each chunk keeps the
+    gates its first token drew): alpha, eta, theta become [S, ceil(N/chunk)]."""
+    out = dict(inp)
+    for g in ("alpha", "eta", "theta"):
+        out[g] = np.ascontiguousarray(inp[g][:, ::chunk])
+    return out
 
 
 def rel_err(x, ref, floor):

@@ -145,6 +145,25 @@ def test_illegal_aliasing(setup, a, b_, shift):
     assert b.call(desc, 8, **{a: b.ptr[b_] + shift}) == tmm.ERR_ALIAS
 
 
+def test_chunk_gates_flag(lib):
+    """One gate value per chunk is a valid descriptor flag, served by the same paths."""
+    d = tmm.make_desc(8, 16, 16384, 64, 256, 2, "bf16", flags=tmm.FLAG_CHUNK_GATES)
+    assert tmm.param_count(d) == 2 * 64 * 256
+    assert tmm.select_path(d, 64) == tmm.PATH_MLP2_D64_H256
+    g = tmm.make_desc(2, 3, 100, 16, 32, 2, "f32", flags=tmm.FLAG_CHUNK_GATES | tmm.FLAG_FORCE_GENERIC)
+    assert tmm.select_path(g, 8) == tmm.PATH_GENERIC_F32
+
+
+def test_chunk_gates_alias_range(lib):
+    """With per-chunk gates a gate array spans B*H*ceil(N/chunk) floats: an
+    output inside that span is still rejected."""
+    desc = tmm.make_desc(2, 3, 100, 16, 32, 2, "f32", flags=tmm.FLAG_CHUNK_GATES)
+    b = Buffers(desc, 8)
+    span = 2 * 3 * 13 * 4              # 13 chunks of 8 cover 100 tokens (312 bytes)
+    assert b.call(desc, 8, y=b.ptr["theta"] + span - 24) == tmm.ERR_ALIAS
+    assert b.call(desc, 8, W_out=b.ptr["eta"] + span - 40) == tmm.ERR_ALIAS
+
+
 def test_empty_sequence_allows_null_token_buffers(lib):
     desc = tmm.make_desc(1, 2, 0, 16, 32, 2, "bf16")
     P = tmm.param_count(desc)

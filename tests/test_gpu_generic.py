@@ -8,8 +8,8 @@ import numpy as np
 import pytest
 
 from test_learned_neural_amd import workloads as wl
-from parity_util import (TOL, prefix_inputs, rel_err, run_gpu, run_oracle, state_below_floor, stream_errors,
-                         to_device, window_errors, y_errors, y_to_f64)
+from parity_util import (TOL, chunk_gate_inputs, prefix_inputs, rel_err, run_gpu, run_oracle, state_below_floor,
+                         stream_errors, to_device, window_errors, y_errors, y_to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -182,3 +182,14 @@ def test_generic_gate_edge_cases():
     # (norm-wise: single entries can cancel, E_n S_0 ~ G)
     rel = (torch.linalg.norm(W.double() - S.double()) / torch.linalg.norm(S.double())).item()
     assert rel < 1e-6, rel
+
+
+@pytest.mark.parametrize("cfg_i,n_tokens,BH,chunk,read_mode", [(1, 1000, (1, 4), 16, 0), (3, 300, (1, 5), 64, 0),
+                                                              (5, 250, (1, 2), 128, 1), (2, 97, (2, 3), 13, 0)])
+def test_generic_chunk_gates(cfg_i, n_tokens, BH, chunk, read_mode):
+    """One alpha, eta, theta per chunk on the generic path, ragged tails
+    included, against the oracle fed the same per-chunk gates."""
+    cfg = wl.CONFIGS[cfg_i].with_(B=BH[0], H=BH[1], N=n_tokens, chunk=chunk)
+    inp = chunk_gate_inputs(wl.make_inputs(cfg), chunk)
+    out = run_gpu(cfg, to_device(cfg, inp), force_generic=True, read_mode=read_mode, chunk_gates=True)
+    _check(cfg, inp, out, run_oracle(cfg, inp, read_mode=read_mode, chunk_gates=True), TOL["f32"])

@@ -13,8 +13,8 @@ import numpy as np
 import pytest
 
 from test_learned_neural_amd import workloads as wl
-from parity_util import (TOL, prefix_inputs, run_gpu, run_oracle, state_below_floor, stream_errors, to_device,
-                         window_errors, y_errors, y_to_f64)
+from parity_util import (TOL, chunk_gate_inputs, prefix_inputs, run_gpu, run_oracle, state_below_floor,
+                         stream_errors, to_device, window_errors, y_errors, y_to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -214,3 +214,39 @@ def test_mlp2_chunk_start_read_matches_generic():
         for s in range(cfg.streams):
             assert np.linalg.norm(a[s] - b[s]) <= 2e-2 * max(np.linalg.norm(b[s]), 1e-30)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("cfg_i,n_tokens,BH,chunk,read_mode", [(3, 2048, None, 64, 0), (2, 150, (1, 4), 40, 0),
+                                                              (2, 77, (2, 5), 16, 1), (2, 1024, (2, 4), 16, 0)])
+def test_mlp2_chunk_gates(cfg_i, n_tokens, BH, chunk, read_mode):
+    """One alpha, eta, theta per chunk (the chunk-constant parameterisation
+    that makes each chunk a time-invariant system) on the MFMA kernel, ragged
+    tails included, against the oracle fed the same per-chunk gates.  Long
+    uniform-law runs use chunks of 16: held over a whole 64-token chunk, an
+    eta near 1 with theta near 0.05 applies the chunk-start gradient ~100
+    times over and some streams diverge (the oracle overflows too), which is
+    the method's behaviour under such gates, not a kernel's."""
+    from test_learned_neural_amd import titans_mem as tmm
+    cfg = wl.CONFIGS[cfg_i].with_(N=n_tokens, chunk=chunk)
+    if BH:
+        cfg = cfg.with_(B=BH[0], H=BH[1])
+    d = tmm.make_desc(cfg.B, cfg.H, cfg.N, cfg.d, cfg.hidden, cfg.n_layers, cfg.io, read_mode=read_mode,
+                      flags=tmm.FLAG_CHUNK_GATES)
+    assert tmm.select_path(d, chunk) == tmm.PATH_MLP2_D64_H256
+    inp = chunk_gate_inputs(wl.make_inputs(cfg, workers=8), chunk)
+    out = run_gpu(cfg, to_device(cfg, inp), read_mode=read_mode, chunk_gates=True)
+    ref = run_oracle(cfg, inp, read_mode=read_mode, threads=16, chunk_gates=True)
+    _check(cfg, inp, out, ref, label=f"{cfg.name} chunk gates")
+
+
+def test_mlp2_chunk_gates_match_repeated_token_gates():
+    """Per-chunk gates give what per-token gates repeated over each chunk give."""
+    cfg = wl.CONFIGS[3].with_(B=2, H=4, N=300)
+    inp = chunk_gate_inputs(wl.make_inputs(cfg), cfg.chunk)
+    rep = dict(inp)
+    for g in ("alpha", "eta", "theta"):
+        rep[g] = np.ascontiguousarray(np.repeat(inp[g], cfg.chunk, axis=1)[:, :cfg.N])
+    a = _np(cfg, run_gpu(cfg, to_device(cfg, inp), chunk_gates=True))
+    b = _np(cfg, run_gpu(cfg, to_device(cfg, rep)))
+    for x, z in zip(a, b):
+        assert np.array_equal(x, z)

@@ -349,6 +349,60 @@ def test_zero_state_is_a_fixed_point_of_the_mlp(oracle_mod, L, d, h):
 
 
 # ----------------------------------------------------------------------------
+# gates shared within a chunk (mer.dev section 3.2, "Parameters as the
+# Function of Chunks": the chunk is then a time-invariant system)
+# ----------------------------------------------------------------------------
+def test_chunk_gates_are_the_chunks_tokens_gates(oracle_mod):
+    """One value per chunk means every token of the chunk uses it."""
+    rng = np.random.default_rng(41)
+    d, h, L, N, chunk = 4, 6, 2, 23, 5
+    P = oracle_mod.param_count(d, h, L)
+    k, v, q = rand_stream(rng, N, d, P)
+    nc = -(-N // chunk)
+    a, e, t = rng.uniform(0, .3, nc), rng.uniform(.5, 1, nc), rng.uniform(0, .3, nc)
+    W0 = rng.standard_normal(P) * 0.3
+    got = oracle_mod.forward(k[None], v[None], q[None], a[None], e[None], t[None], W0[None], np.zeros((1, P)),
+                             d=d, hidden=h, n_layers=L, chunk=chunk, chunk_gates=True)
+    rep = lambda g: np.repeat(g, chunk)[:N]
+    ref = run_oracle(oracle_mod, k, v, q, rep(a), rep(e), rep(t), W0, np.zeros(P), d, h, L, chunk)
+    for x, y in zip(got, ref):
+        assert np.array_equal(x, y)
+
+
+def test_chunk_gates_make_the_chunk_time_invariant():
+    """With alpha, eta, theta constant over a chunk the unrolled coefficients
+    depend on j - i only: A_j = a^(j+1), E_j = e^(j+1), U_i = theta e^(n-1-i)
+    and D Toeplitz with D[j, i] = theta sum_{u=0}^{j-i} a^(j-i-u) e^u."""
+    n, a_, e_, t_ = 9, 0.8, 0.6, 0.3
+    A, E, Fc, C, D = coeff_brute(np.full(n, 1 - a_), np.full(n, e_), np.full(n, t_))
+    jj = np.arange(n)
+    np.testing.assert_allclose(A, a_ ** (jj + 1), rtol=1e-13)
+    np.testing.assert_allclose(E, e_ ** (jj + 1), rtol=1e-13)
+    np.testing.assert_allclose(C[n - 1], t_ * e_ ** (n - 1 - jj), rtol=1e-13)
+    lag = lambda m: t_ * sum(a_ ** (m - u) * e_ ** u for u in range(m + 1))
+    for j in range(n):
+        for i in range(n):
+            np.testing.assert_allclose(D[j, i], lag(j - i) if i <= j else 0.0, rtol=1e-13, atol=1e-15)
+
+
+def test_chunk_gates_linear_memory_is_a_causal_convolution(oracle_mod):
+    """Linear memory, zero start, one chunk with constant gates: retrieval is
+    y_t = sum_{i<=t} D[t-i] (k_i . q_t) v_i with the Toeplitz lags above --
+    the convolution the time-invariant form allows (section 3.2)."""
+    rng = np.random.default_rng(42)
+    d, N = 5, 12
+    k, v, q = rand_stream(rng, N, d, d * d)
+    a_, e_, t_ = 0.15, 0.7, 0.4
+    y, _, _ = oracle_mod.forward(k[None], v[None], q[None], np.array([[a_]]), np.array([[e_]]),
+                                 np.array([[t_]]), np.zeros((1, d * d)), np.zeros((1, d * d)),
+                                 d=d, hidden=0, n_layers=1, chunk=N, chunk_gates=True)
+    lag = lambda m: t_ * sum((1 - a_) ** (m - u) * e_ ** u for u in range(m + 1))
+    for t in range(N):
+        ref = sum(lag(t - i) * float(k[i] @ q[t]) * v[i] for i in range(t + 1))
+        np.testing.assert_allclose(y[0, t], ref, rtol=1e-12, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
 # P7/P8/P9: attention special cases (mer.dev section 2.1)
 # ----------------------------------------------------------------------------
 def test_causal_linear_attention(oracle_mod):
