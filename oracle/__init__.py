@@ -6,3 +6,4 @@ CPU-baseline leg may import this package; the GPU library never does.
 from .titans_oracle import (  # noqa: F401
     build, lib_path, param_count, memory_apply, memory_grad, forward, max_threads,
 )
+from .input_oracle import input_side  # noqa: F401

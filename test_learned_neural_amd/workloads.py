@@ -237,3 +237,84 @@ def inputs_f64(cfg: MemoryConfig, inp: Dict[str, np.ndarray]) -> Dict[str, np.nd
         "theta": inp["theta"].astype(np.float64),
         "W0": inp["W0"].astype(np.float64), "S0": inp["S0"].astype(np.float64),
     }
+
+
+# ----------------------------------------------------------------------------
+# input side: model activations and projection / convolution / gate weights
+# ----------------------------------------------------------------------------
+_TAG_X, _TAG_WPROJ, _TAG_CONV, _TAG_WGATE, _TAG_BGATE = range(16, 21)
+
+
+@dataclasses.dataclass(frozen=True)
+class InputConfig:
+    """Shape and input law of the input side (x -> k, v, q and the gates).
+
+    x [B, N, D] ~ N(0, 1) rounded to bf16; projection and gate weights
+    ~ N(0, 1/D) rounded to bf16 (so each projected channel is ~N(0, 1));
+    depthwise taps ~ N(0, 1/w) fp32; gate biases ~ N(0, 0.25) fp32.  The
+    gate scales put alpha and theta in (0, 0.1) and eta in (0, 1), the law
+    of the sigmoid memory workload.
+    """
+    name: str
+    seed: int
+    B: int
+    N: int
+    D: int
+    H: int
+    d: int
+    conv_width: int = 4
+    gate_scale: Tuple[float, float, float] = (0.1, 1.0, 0.1)
+
+    @property
+    def channels(self) -> int:
+        return self.H * self.d
+
+    def with_(self, **kw) -> "InputConfig":
+        return dataclasses.replace(self, **kw)
+
+
+# the input side of the headline memory workload: 16 heads of width 64 over a
+# model width of 1024, 8 sequences of 16,384 tokens
+INPUT_CONFIGS: Dict[str, InputConfig] = {
+    "headline": InputConfig("input_D1024_h16_d64_b8_n16384_w4_bf16", 2003, B=8, N=16384, D=1024, H=16, d=64),
+    "small": InputConfig("input_D256_h4_d64_b2_n700_w4_bf16", 2001, B=2, N=700, D=256, H=4, d=64),
+}
+
+
+def make_input_side(cfg: InputConfig, n_tokens: Optional[int] = None, workers: int = 1) -> Dict[str, np.ndarray]:
+    """Draw x and the weights of ``cfg`` (x for the first n_tokens of each
+    sequence; a prefix is drawn bit-identically to the full sequence).
+
+    Returns bf16 bit patterns (uint16) for x [B, n, D], w_proj [3, H*d, D]
+    and w_gate [3, H, D]; float32 conv_w [3, H*d, w] and b_gate [3, H]; and
+    the gate scales as a float64 array of 3.
+    """
+    n = cfg.N if n_tokens is None else n_tokens
+    C, D = cfg.channels, cfg.D
+    out = {"x": np.empty((cfg.B, n, D), np.uint16)}
+
+    def fill(b):
+        out["x"][b] = f64_to_bf16_bits(_rng(cfg.seed, b, 0, _TAG_X).standard_normal((n, D)))
+
+    if workers > 1 and cfg.B > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(fill, range(cfg.B)))
+    else:
+        for b in range(cfg.B):
+            fill(b)
+    sd = 1.0 / math.sqrt(D)
+    out["w_proj"] = f64_to_bf16_bits(_rng(cfg.seed, 0, 0, _TAG_WPROJ).standard_normal((3, C, D)) * sd)
+    out["conv_w"] = (_rng(cfg.seed, 0, 0, _TAG_CONV).standard_normal((3, C, cfg.conv_width))
+                     / math.sqrt(cfg.conv_width)).astype(np.float32)
+    out["w_gate"] = f64_to_bf16_bits(_rng(cfg.seed, 0, 0, _TAG_WGATE).standard_normal((3, cfg.H, D)) * sd)
+    out["b_gate"] = (0.5 * _rng(cfg.seed, 0, 0, _TAG_BGATE).standard_normal((3, cfg.H))).astype(np.float32)
+    out["gate_scale"] = np.array(cfg.gate_scale, np.float64)
+    return out
+
+
+def input_side_f64(inp: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
+    """Exact float64 views of stored input-side tensors (what the oracle consumes)."""
+    return {"x": bf16_bits_to_f64(inp["x"]), "w_proj": bf16_bits_to_f64(inp["w_proj"]),
+            "conv_w": inp["conv_w"].astype(np.float64), "w_gate": bf16_bits_to_f64(inp["w_gate"]),
+            "b_gate": inp["b_gate"].astype(np.float64), "gate_scale": inp["gate_scale"]}
