@@ -158,6 +158,57 @@ int titans_mem_forward(const titans_mem_desc* desc,
 int titans_mem_retrieve(const titans_mem_desc* desc, const void* q, const float* W,
                         void* y_out, void* stream);
 
+/*
+ * titans_mem_input -- the step before the memory: model activations x to
+ * the memory's keys, values, queries and gates, for whole sequences.
+ *
+ * Per sequence b, token t, head h (mer.dev notes):
+ *   projections  k = x W_K, v = x W_V      section 3.1, "Objective"
+ *                q = x W_Q                 section 3.1, "Retrieving a Memory"
+ *   convolution  causal depthwise over time after each projection, width w:
+ *                u_t[c] = sum_{j<w} conv_w[c][j] * proj_{t-j}[c], tokens before
+ *                the sequence start count as zero   section 4.4, "Convolution"
+ *   activation   SiLU on k, v and q; k and q divided by their l2 norm over
+ *                the head's d channels (floored at 1e-6)
+ *                                          section 4.4, "Architectural Details"
+ *   gates        alpha, eta, theta = scale_g * sigmoid(x . w_gate[g][h] +
+ *                b_gate[g][h]): per token and head, input dependent
+ *                                          section 3.1, "Learning Process and
+ *                                          Surprise Metric"
+ * There are no projection biases.  Arithmetic: bf16 x bf16 products, fp32
+ * sums and epilogue, k, v, q rounded once to bf16 (nearest-even).
+ *
+ *   x          [B,N,D]     bf16, device, read-only
+ *   w_proj     [3,H*d,D]   bf16, device: rows of W_K, then W_V, then W_Q;
+ *              channel c of head h is row h*d + c (out = x . row)
+ *   conv_w     [3,H*d,w]   fp32, device: tap j weighs the token j steps back
+ *   w_gate     [3,H,D]     bf16, device: logit weights of alpha, eta, theta
+ *   b_gate     [3,H]       fp32, device: logit biases
+ *   *_scale    host scalars multiplying the three sigmoids
+ *   k_out, v_out, q_out  [B,H,N,d] bf16, device, written (the layout
+ *              titans_mem_forward reads)
+ *   alpha_out, eta_out, theta_out  [B,H,N] fp32, device, written
+ * Supported: D a positive multiple of 32, d in {16, 32, 64, 128}, H*d a
+ * multiple of 128, 1 <= w <= 4 (else TM_ERR_UNSUPPORTED).  Outputs must not
+ * overlap each other or any input (TM_ERR_ALIAS).  N == 0 enqueues nothing.
+ */
+typedef struct {
+    int32_t abi_version;  /* must equal TITANS_MEM_ABI_VERSION */
+    int32_t B, N;         /* sequences, tokens per sequence (N >= 0) */
+    int32_t D;            /* model width */
+    int32_t H, d;         /* heads, head width */
+    int32_t conv_width;   /* w: causal depthwise taps */
+    uint32_t flags;       /* must be 0 */
+} titans_input_desc;
+
+int titans_mem_input(const titans_input_desc* desc,
+                     const void* x, const void* w_proj, const float* conv_w,
+                     const void* w_gate, const float* b_gate,
+                     float alpha_scale, float eta_scale, float theta_scale,
+                     void* k_out, void* v_out, void* q_out,
+                     float* alpha_out, float* eta_out, float* theta_out,
+                     void* stream);
+
 /* Static text for a status code. */
 const char* titans_mem_status_string(int status);
 

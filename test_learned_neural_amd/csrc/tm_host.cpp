@@ -180,6 +180,46 @@ int titans_mem_retrieve(const titans_mem_desc* desc, const void* q, const float*
   return err == hipSuccess ? TM_OK : TM_ERR_HIP;
 }
 
+int titans_mem_input(const titans_input_desc* desc, const void* x, const void* w_proj, const float* conv_w,
+                     const void* w_gate, const float* b_gate, float alpha_scale, float eta_scale,
+                     float theta_scale, void* k_out, void* v_out, void* q_out, float* alpha_out,
+                     float* eta_out, float* theta_out, void* stream) {
+  if (!desc || desc->abi_version != TITANS_MEM_ABI_VERSION) return TM_ERR_INVALID;
+  if (desc->B <= 0 || desc->N < 0 || desc->D <= 0 || desc->H <= 0 || desc->d <= 0 || desc->conv_width <= 0 ||
+      desc->flags != 0)
+    return TM_ERR_INVALID;
+  if (!titans::input_supported(desc->D, desc->H, desc->d, desc->conv_width)) return TM_ERR_UNSUPPORTED;
+  const void* ptrs[] = {x, w_proj, conv_w, w_gate, b_gate, k_out, v_out, q_out, alpha_out, eta_out, theta_out};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return TM_ERR_INVALID;
+  const int64_t R = (int64_t)desc->B * desc->N;
+  const int64_t C = (int64_t)desc->H * desc->d;
+  if (titans::input_grid(R, desc->D, desc->H, desc->d, desc->conv_width) >= ((int64_t)1 << 31))
+    return TM_ERR_UNSUPPORTED;
+  const int64_t tok = R * C * 2, gate = R * desc->H * 4;
+  const Range ranges[] = {
+      {(const char*)x, R * desc->D * 2, false},
+      {(const char*)w_proj, 3 * C * desc->D * 2, false},
+      {(const char*)conv_w, 3 * C * desc->conv_width * 4, false},
+      {(const char*)w_gate, (int64_t)3 * desc->H * desc->D * 2, false},
+      {(const char*)b_gate, (int64_t)3 * desc->H * 4, false},
+      {(const char*)k_out, tok, true},     {(const char*)v_out, tok, true},
+      {(const char*)q_out, tok, true},     {(const char*)alpha_out, gate, true},
+      {(const char*)eta_out, gate, true},  {(const char*)theta_out, gate, true},
+  };
+  const int nr = sizeof(ranges) / sizeof(ranges[0]);
+  for (int i = 0; i < nr; ++i)
+    for (int j = i + 1; j < nr; ++j)
+      if ((ranges[i].writes || ranges[j].writes) && overlap(ranges[i], ranges[j])) return TM_ERR_ALIAS;
+  if (R == 0) return TM_OK;
+  const float scale[3] = {alpha_scale, eta_scale, theta_scale};
+  void* const kvq[3] = {k_out, v_out, q_out};
+  float* const gates[3] = {alpha_out, eta_out, theta_out};
+  hipError_t err = titans::launch_input(desc->B, desc->N, desc->D, desc->H, desc->d, desc->conv_width, x, w_proj,
+                                        conv_w, w_gate, b_gate, scale, kvq, gates, (hipStream_t)stream);
+  return err == hipSuccess ? TM_OK : TM_ERR_HIP;
+}
+
 const char* titans_mem_status_string(int status) {
   switch (status) {
     case TM_OK: return "ok";

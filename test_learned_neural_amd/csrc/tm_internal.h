@@ -43,4 +43,12 @@ hipError_t launch_mlp2(const Shape& s, int chunk, const void* k, const void* v, 
                        const float* W_in, const float* S_in, void* y, float* W_out,
                        float* S_out, void* ws, hipStream_t stream);
 
+// Input side (x -> k, v, q and the gates): bf16 MFMA GEMM with a fused
+// convolution / SiLU / l2-norm / sigmoid epilogue.
+bool input_supported(int D, int H, int d, int w);
+int64_t input_grid(int64_t R, int D, int H, int d, int w);
+hipError_t launch_input(int B, int N, int D, int H, int d, int w, const void* x, const void* w_proj,
+                        const float* conv_w, const void* w_gate, const float* b_gate, const float scale[3],
+                        void* const kvq[3], float* const gates[3], hipStream_t stream);
+
 }  // namespace titans

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtitans_m
 
 EXPORTS = ("titans_mem_abi_version", "titans_mem_param_count", "titans_mem_select_path",
            "titans_mem_workspace_bytes", "titans_mem_forward", "titans_mem_retrieve",
-           "titans_mem_status_string")
+           "titans_mem_input", "titans_mem_status_string")
 
 
 class Desc(ctypes.Structure):
@@ -34,6 +34,16 @@ class Desc(ctypes.Structure):
                 ("n_layers", ctypes.c_int32), ("activation", ctypes.c_int32),
                 ("io_dtype", ctypes.c_int32), ("read_mode", ctypes.c_int32),
                 ("flags", ctypes.c_uint32)]
+
+
+class InputDesc(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("B", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("H", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("conv_width", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+def make_input_desc(B: int, N: int, D: int, H: int, d: int, conv_width: int = 4, flags: int = 0) -> InputDesc:
+    return InputDesc(ABI_VERSION, B, N, D, H, d, conv_width, flags)
 
 
 def make_desc(B: int, H: int, N: int, d: int, hidden: int, n_layers: int, io: str = "bf16",
@@ -74,6 +84,9 @@ def load():
     lib.titans_mem_forward.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, i32, vp, fp, fp, vp, i64, vp]
     lib.titans_mem_retrieve.restype = ctypes.c_int
     lib.titans_mem_retrieve.argtypes = [dp, vp, fp, vp, vp]
+    lib.titans_mem_input.restype = ctypes.c_int
+    lib.titans_mem_input.argtypes = [ctypes.POINTER(InputDesc), vp, vp, fp, vp, fp, ctypes.c_float, ctypes.c_float,
+                                     ctypes.c_float, vp, vp, vp, fp, fp, fp, vp]
     lib.titans_mem_status_string.restype = ctypes.c_char_p
     lib.titans_mem_status_string.argtypes = [ctypes.c_int]
     if lib.titans_mem_abi_version() != ABI_VERSION:
@@ -104,6 +117,14 @@ def raw_forward(desc: Desc, k, v, q, alpha, eta, theta, W_in, S_in, chunk, y_out
     return int(load().titans_mem_forward(ctypes.byref(desc), k, v, q, alpha, eta, theta, W_in, S_in,
                                          int(chunk), y_out, W_out, S_out, workspace,
                                          int(workspace_bytes_), stream))
+
+
+def raw_input(desc: InputDesc, x, w_proj, conv_w, w_gate, b_gate, scales, k_out, v_out, q_out, alpha_out,
+              eta_out, theta_out, stream) -> int:
+    """Direct call of titans_mem_input with integer device addresses; returns the status."""
+    return int(load().titans_mem_input(ctypes.byref(desc), x, w_proj, conv_w, w_gate, b_gate, float(scales[0]),
+                                       float(scales[1]), float(scales[2]), k_out, v_out, q_out, alpha_out,
+                                       eta_out, theta_out, stream))
 
 
 # ----------------------------------------------------------------------------
@@ -197,3 +218,36 @@ def retrieve(q, W, *, hidden: int, n_layers: int, y_out=None):
     if rc != OK:
         raise TitansMemError(rc, "titans_mem_retrieve")
     return y_out
+
+
+def input_side(x, w_proj, conv_w, w_gate, b_gate, gate_scale, *, H: int, d: int, out=None):
+    """x -> (k, v, q, alpha, eta, theta) through titans_mem_input.
+
+    x: [B, N, D] bfloat16; w_proj: [3, H*d, D] bfloat16; conv_w: [3, H*d, w]
+    float32; w_gate: [3, H, D] bfloat16; b_gate: [3, H] float32; gate_scale:
+    three floats.  Returns k, v, q as [B, H, N, d] bfloat16 and the gates as
+    [B, H, N] float32 (``out`` may supply the six output tensors).
+    """
+    torch = _torch()
+    B, N, D = x.shape
+    C = H * d
+    w = conv_w.shape[-1]
+    dev = x.device
+    _check(x, "x", (B, N, D), torch.bfloat16, dev)
+    _check(w_proj, "w_proj", (3, C, D), torch.bfloat16, dev)
+    _check(conv_w, "conv_w", (3, C, w), torch.float32, dev)
+    _check(w_gate, "w_gate", (3, H, D), torch.bfloat16, dev)
+    _check(b_gate, "b_gate", (3, H), torch.float32, dev)
+    if out is None:
+        out = tuple(torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev) for _ in range(3)) + \
+              tuple(torch.empty((B, H, N), dtype=torch.float32, device=dev) for _ in range(3))
+    for i, t in enumerate(out):
+        _check(t, ("k", "v", "q", "alpha", "eta", "theta")[i], (B, H, N, d) if i < 3 else (B, H, N),
+               torch.bfloat16 if i < 3 else torch.float32, dev)
+    desc = make_input_desc(B, N, D, H, d, w)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = raw_input(desc, _ptr(x), _ptr(w_proj), _ptr(conv_w), _ptr(w_gate), _ptr(b_gate), gate_scale,
+                   *[_ptr(t) for t in out], stream)
+    if rc != OK:
+        raise TitansMemError(rc, "titans_mem_input")
+    return out

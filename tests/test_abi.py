@@ -188,3 +188,60 @@ def test_retrieve_validation(lib):
 def test_status_strings(lib):
     for code in (0, -1, -2, -3, -4, -5, 17):
         assert isinstance(tmm.status_string(code), str) and tmm.status_string(code)
+
+
+# ----------------------------------------------------------------------------
+# titans_mem_input (x -> k, v, q and the gates)
+# ----------------------------------------------------------------------------
+class InputBuffers:
+    """Disjoint fake device ranges for one input-side descriptor."""
+
+    def __init__(self, desc):
+        R, C = desc.B * desc.N, desc.H * desc.d
+        sizes = dict(x=R * desc.D * 2, w_proj=3 * C * desc.D * 2, conv_w=3 * C * desc.conv_width * 4,
+                     w_gate=3 * desc.H * desc.D * 2, b_gate=3 * desc.H * 4, k=R * C * 2, v=R * C * 2, q=R * C * 2,
+                     alpha=R * desc.H * 4, eta=R * desc.H * 4, theta=R * desc.H * 4)
+        self.ptr = {}
+        cur = BASE
+        for name, n in sizes.items():
+            self.ptr[name] = cur
+            cur += (n + 4095) // 4096 * 4096 + 4096
+
+    def call(self, desc, **over):
+        p = dict(self.ptr)
+        p.update(over)
+        return tmm.raw_input(desc, p["x"], p["w_proj"], p["conv_w"], p["w_gate"], p["b_gate"], (0.1, 1.0, 0.1),
+                             p["k"], p["v"], p["q"], p["alpha"], p["eta"], p["theta"], 0)
+
+
+@pytest.mark.parametrize("field,value,code", [("abi_version", 3, -1), ("B", 0, -1), ("N", -1, -1), ("D", 0, -1),
+                                              ("H", 0, -1), ("d", 0, -1), ("conv_width", 0, -1), ("flags", 1, -1),
+                                              ("D", 48, -2), ("d", 48, -2), ("d", 8, -2), ("conv_width", 5, -2),
+                                              ("H", 3, -2)])
+def test_input_invalid_descriptor(lib, field, value, code):
+    desc = tmm.make_input_desc(2, 100, 256, 4, 64, 4)
+    b = InputBuffers(desc)
+    setattr(desc, field, value)
+    assert b.call(desc) == code
+
+
+@pytest.mark.parametrize("name", ["x", "w_proj", "conv_w", "w_gate", "b_gate", "k", "v", "q", "alpha", "eta",
+                                  "theta"])
+def test_input_null_and_misaligned(lib, name):
+    desc = tmm.make_input_desc(2, 100, 256, 4, 64, 4)
+    b = InputBuffers(desc)
+    assert b.call(desc, **{name: 0}) == tmm.ERR_INVALID
+    assert b.call(desc, **{name: b.ptr[name] + 4}) == tmm.ERR_INVALID
+
+
+@pytest.mark.parametrize("a,b_,shift", [("k", "x", 0), ("v", "k", 256), ("alpha", "w_gate", 16), ("theta", "eta", 0),
+                                        ("q", "conv_w", 32), ("eta", "b_gate", 0)])
+def test_input_aliasing(lib, a, b_, shift):
+    desc = tmm.make_input_desc(2, 100, 256, 4, 64, 4)
+    b = InputBuffers(desc)
+    assert b.call(desc, **{a: b.ptr[b_] + shift}) == tmm.ERR_ALIAS
+
+
+def test_input_empty_sequences(lib):
+    desc = tmm.make_input_desc(3, 0, 256, 4, 64, 4)
+    assert InputBuffers(desc).call(desc) == tmm.OK
