@@ -27,7 +27,8 @@ PEAK_HBM_GBS = 8000.0
 
 # dominant kernel of each path: (kernel function, its source under csrc/)
 DOMINANT_KERNEL = {"mlp2_d64_h256_mfma": ("mlp2_pair_kernel", "tm_mlp2.hip"),
-                   "generic_f32": ("generic_kernel", "tm_generic.hip")}
+                   "generic_f32": ("generic_kernel", "tm_generic.hip"),
+                   "input_side": ("input_kernel", "tm_input.hip")}
 
 
 def measured_traffic(kernel_path, workload):
@@ -73,6 +74,75 @@ def algorithmic_work(cfg):
     return flops, byts
 
 
+def input_side_work(icfg):
+    """(FLOPs, HBM bytes) per launch of the input side: the projection GEMM
+    [B*N x D] . [D x 3*(H*d + H)], and x, the weights, k, v, q (bf16) and
+    the gates (fp32) moved once."""
+    R, C = icfg.B * icfg.N, icfg.channels
+    flops = 2.0 * R * icfg.D * (3 * C + 3 * icfg.H)
+    byts = R * icfg.D * 2 + 3 * (C + icfg.H) * icfg.D * 2 + R * 3 * C * 2 + R * 3 * icfg.H * 4
+    return flops, byts
+
+
+def bench_input_side(args, np, torch, tmm, wl):
+    """The step before the memory (x -> k, v, q and the gates) on the
+    headline workload's input side; returns the JSON object describing it."""
+    icfg = wl.INPUT_CONFIGS["headline"]
+    inp = wl.make_input_side(icfg, workers=min(16, len(os.sched_getaffinity(0))))
+
+    def bf(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+    x, wp, wg = bf(inp["x"]), bf(inp["w_proj"]), bf(inp["w_gate"])
+    cw, bg = torch.from_numpy(inp["conv_w"]).cuda(), torch.from_numpy(inp["b_gate"]).cuda()
+    scales = tuple(float(v) for v in inp["gate_scale"])
+    out = tmm.input_side(x, wp, cw, wg, bg, scales, H=icfg.H, d=icfg.d)
+    stream = torch.cuda.current_stream()
+    desc = tmm.make_input_desc(icfg.B, icfg.N, icfg.D, icfg.H, icfg.d, icfg.conv_width)
+    ptrs = [x.data_ptr(), wp.data_ptr(), cw.data_ptr(), wg.data_ptr(), bg.data_ptr()]
+    optrs = [t.data_ptr() for t in out]
+
+    def step():
+        rc = tmm.raw_input(desc, *ptrs, scales, *optrs, stream.cuda_stream)
+        if rc != tmm.OK:
+            raise tmm.TitansMemError(rc, "titans_mem_input")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    wall0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    launch_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    flops, byts = input_side_work(icfg)
+    achieved = flops / launch_s / 1e12
+    tokens = icfg.B * icfg.N
+    res = {"workload": icfg.name, "value": tokens / (wall / args.steps), "unit": "tokens/s",
+           "ms_per_step": wall * 1e3 / args.steps, "dtype": "bf16",
+           "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                        "frac": achieved / PEAK_TFLOPS["bf16"],
+                        "traffic": measured_traffic("input_side", icfg.name),
+                        "algorithmic_flops_per_launch": flops, "avg_launch_ms": launch_s * 1e3,
+                        "hbm_achieved_gbs": byts / launch_s / 1e9, "hbm_peak_gbs": PEAK_HBM_GBS}}
+    print(f"[bench] input side {icfg.name}: {launch_s * 1e3:.3f} ms/launch, {achieved:.1f} TFLOP/s "
+          f"({achieved / PEAK_TFLOPS['bf16'] * 100:.1f}% of bf16 peak)", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        import oracle
+        f = wl.input_side_f64(wl.make_input_side(icfg.with_(B=1), n_tokens=2048))
+        t1 = time.perf_counter()
+        oracle.input_side(f["x"], f["w_proj"], f["conv_w"], f["w_gate"], f["b_gate"], f["gate_scale"],
+                          H=icfg.H, d=icfg.d)
+        el = time.perf_counter() - t1
+        res["cpu_baseline"] = {"value": 2048 / el, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
+                               "kind": "oracle", "sample": f"1 sequence x 2048 tokens, fp64 numpy, {el:.2f} s"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -82,6 +152,9 @@ def main():
     ap.add_argument("--force-generic", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-input-side", action="store_true", help="skip the input-side leg")
+    ap.add_argument("--input-side-only", action="store_true",
+                    help="time only the input side (x -> k, v, q, gates) and print its JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (three times), to scale "
                          "HBM byte counters, and exit")
@@ -110,6 +183,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tmm.load()
+    if args.input_side_only:
+        print(json.dumps({"metric": "input-side tokens/sec (x -> k, v, q, gates), 1 GPU", "n_gpus": 1,
+                          "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+                          "data": "synthetic", **bench_input_side(args, np, torch, tmm, wl)}), flush=True)
+        return
     cfg = wl.CONFIGS[args.config]
     t0 = time.time()
     inp = wl.make_inputs(cfg, workers=min(16, len(os.sched_getaffinity(0))))
@@ -222,6 +300,8 @@ def main():
                      "hbm_peak_gbs": PEAK_HBM_GBS},
         "cpu_baseline": cpu,
     }
+    if not args.no_input_side:
+        out["input_side"] = bench_input_side(args, np, torch, tmm, wl)
     print(json.dumps(out), flush=True)
 
 

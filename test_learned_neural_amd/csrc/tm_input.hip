@@ -31,9 +31,12 @@
 //   (lane shuffles), the normalisation and the bf16 store (8 bytes per lane,
 //   a head row per group).  Gate tiles read logits from a padded LDS copy
 //   with one thread per token, so stores of a gate row are contiguous.
-// - Grid: block i runs on XCD i % 8 (round-robin dispatch); blocks of one
-//   XCD take its token tiles in turn and sweep all channel tiles of each,
-//   so the 512 KiB x tile is reused from that XCD's L2.
+// - Grid: block i runs on XCD i % 8 (round-robin dispatch).  An XCD takes
+//   its token tiles in groups of 8 and walks the channel tiles once per
+//   group, the 8 token tiles of a group side by side: a channel tile's
+//   256 KiB of weights is then fetched into the XCD's L2 once per group
+//   instead of once per token tile (6.4 MiB of weights do not fit a 4 MiB
+//   L2), and each 512 KiB x tile stays there while the group runs.
 #include "tm_internal.h"
 
 namespace titans {
@@ -46,6 +49,7 @@ constexpr int kThreads = 256;
 constexpr int kStageA = kMT * kKT * 2;
 constexpr int kStageB = kNT * kKT * 2;
 constexpr int kStage = kStageA + kStageB;
+constexpr int kRowGroup = 8;      // token tiles of one XCD sharing each channel tile's weights
 constexpr int kGatePass = 64;     // gate logits per epilogue pass
 constexpr int kGateStride = kGatePass + 1;
 constexpr float kNormFloor2 = 1e-12f;   // (1e-6)^2: k, q = s / max(||s||, 1e-6)
@@ -84,9 +88,13 @@ __device__ __forceinline__ float sigmoidf(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+// two floats -> two bf16 (nearest-even) in one register: v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  const __bf16 ha = (__bf16)a, hb = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Stage `stage` <- x rows [r0, r0 + 256) and weight rows [0, 128) of
@@ -122,6 +130,25 @@ __device__ __forceinline__ void issue_stage(const InParams& p, unsigned char* sm
 
 __device__ __forceinline__ bf16x8 frag(const unsigned char* base, int row, int c) {
   return *(const bf16x8*)(base + row * 64 + 16 * (c ^ ((row >> 1) & 3)));
+}
+
+// Sum over aligned groups of G lanes (G = 4, 8, 16, 32), result in every
+// lane of the group: DPP quad permutations, then half-row and row mirrors
+// (lane i meets lane 7 - i, then 15 - i, whose partial sums cover the other
+// half), and a cross-row swap for 32.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, true));
+}
+
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp<0xB1>(x);                  // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);                  // quad_perm [2,3,0,1]
+  if (G >= 8) x += dpp<0x141>(x);     // row_half_mirror
+  if (G >= 16) x += dpp<0x140>(x);    // row_mirror
+  if (G >= 32) x += __shfl_xor(x, 16);
+  return x;
 }
 
 // accumulator register r of a 32x32 tile holds row 8 (r / 4) + 4 (lane / 32) + r % 4
@@ -162,43 +189,81 @@ __device__ __forceinline__ void kvq_epilogue(const InParams& p, float* ep, const
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int tau = 0; tau < 4; ++tau) tap[j][tau] = tau < p.w ? p.conv[(int64_t)(cg + j) * p.w + tau] : 0.0f;
-    if (i0 >= i1) continue;
-    int64_t gr = r0 + i0;
-    if (gr >= p.R) continue;
-    int64_t bb = gr / p.N;
-    int t = (int)(gr - bb * p.N);
-    uint16_t* out = p.kvq[which];
-    for (int i = i0; i < i1; ++i, ++gr) {
-      if (gr >= p.R) break;
-      float u[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int tau = 0; tau < 4; ++tau) {
-        if (tau < p.w && tau <= t) {
-          const float4 pv = *(const float4*)(ep + (i - tau) * PW + cl);
-          u[0] += tap[0][tau] * pv.x;
-          u[1] += tap[1][tau] * pv.y;
-          u[2] += tap[2][tau] * pv.z;
-          u[3] += tap[3][tau] * pv.w;
-        }
-      }
-      float s[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) s[j] = u[j] * sigmoidf(u[j]);
+    // rows [i0, iend) of this range; rows past the last token are not stored
+    const int iend = (int)(r0 + i1 <= p.R ? i1 : p.R - r0);
+    if (i0 >= iend) continue;
+    const int64_t gr0 = r0 + i0;
+    int64_t bb = gr0 / p.N;
+    int t = (int)(gr0 - bb * p.N);
+    uint16_t* base = p.kvq[which];
+    uint16_t* dst = base + ((bb * p.H + h) * p.N + t) * kD + cq;
+    // the three previous rows' projections (rows before the tile's halo
+    // are never needed: i0 - tau < 0 only for taps tau >= w, which are 0)
+    float4 w1 = p.w > 1 ? *(const float4*)(ep + (i0 - 1) * PW + cl) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 w2 = p.w > 2 ? *(const float4*)(ep + (i0 - 2) * PW + cl) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 w3 = p.w > 3 ? *(const float4*)(ep + (i0 - 3) * PW + cl) : make_float4(0.f, 0.f, 0.f, 0.f);
+    auto emit = [&](const float4& c, const float4& a1, const float4& a2, const float4& a3, uint16_t* o) {
+      const float u0 = tap[0][0] * c.x + tap[0][1] * a1.x + tap[0][2] * a2.x + tap[0][3] * a3.x;
+      const float u1 = tap[1][0] * c.y + tap[1][1] * a1.y + tap[1][2] * a2.y + tap[1][3] * a3.y;
+      const float u2 = tap[2][0] * c.z + tap[2][1] * a1.z + tap[2][2] * a2.z + tap[2][3] * a3.z;
+      const float u3 = tap[3][0] * c.w + tap[3][1] * a1.w + tap[3][2] * a2.w + tap[3][3] * a3.w;
+      float s0 = u0 * sigmoidf(u0), s1 = u1 * sigmoidf(u1), s2 = u2 * sigmoidf(u2), s3 = u3 * sigmoidf(u3);
       if (which != 1) {
-        float ss = s[0] * s[0] + s[1] * s[1] + s[2] * s[2] + s[3] * s[3];
-#pragma unroll
-        for (int m = 1; m < G; m <<= 1) ss += __shfl_xor(ss, m);
+        const float ss = group_sum<G>(s0 * s0 + s1 * s1 + s2 * s2 + s3 * s3);
         const float inv = __builtin_amdgcn_rsqf(ss > kNormFloor2 ? ss : kNormFloor2);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) s[j] *= inv;
+        s0 *= inv;
+        s1 *= inv;
+        s2 *= inv;
+        s3 *= inv;
       }
       uint2 pk;
-      pk.x = pack_bf16(s[0], s[1]);
-      pk.y = pack_bf16(s[2], s[3]);
-      *(uint2*)(out + ((bb * p.H + h) * p.N + t) * kD + cq) = pk;
-      if (++t == p.N) {
-        t = 0;
-        ++bb;
+      pk.x = pack_bf16(s0, s1);
+      pk.y = pack_bf16(s2, s3);
+      *(uint2*)o = pk;
+    };
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t >= 3 && t + (iend - i0) <= p.N) {
+      // no sequence start in the range: every tap is live, the output row
+      // advances by one head row per token
+      int i = i0;
+      for (; i + 4 <= iend; i += 4) {
+        const float4 c0 = *(const float4*)(ep + (i + 0) * PW + cl);
+        const float4 c1 = *(const float4*)(ep + (i + 1) * PW + cl);
+        const float4 c2 = *(const float4*)(ep + (i + 2) * PW + cl);
+        const float4 c3 = *(const float4*)(ep + (i + 3) * PW + cl);
+        emit(c0, w1, w2, w3, dst);
+        emit(c1, c0, w1, w2, dst + kD);
+        emit(c2, c1, c0, w1, dst + 2 * kD);
+        emit(c3, c2, c1, c0, dst + 3 * kD);
+        dst += 4 * kD;
+        w3 = c1;
+        w2 = c2;
+        w1 = c3;
+      }
+      for (; i < iend; ++i) {
+        const float4 c0 = *(const float4*)(ep + i * PW + cl);
+        emit(c0, w1, w2, w3, dst);
+        dst += kD;
+        w3 = w2;
+        w2 = w1;
+        w1 = c0;
+      }
+    } else {
+      // a sequence starts inside the range (or just before it): taps that
+      // would reach before the start are dropped
+      for (int i = i0; i < iend; ++i) {
+        const float4 c0 = *(const float4*)(ep + i * PW + cl);
+        emit(c0, t >= 1 ? w1 : z4, t >= 2 ? w2 : z4, t >= 3 ? w3 : z4, dst);
+        w3 = w2;
+        w2 = w1;
+        w1 = c0;
+        if (++t == p.N) {
+          t = 0;
+          ++bb;
+          dst = base + (bb * p.H + h) * (int64_t)p.N * kD + cq;
+        } else {
+          dst += kD;
+        }
       }
     }
   }
@@ -243,9 +308,11 @@ __global__ __launch_bounds__(kThreads, 2) void input_kernel(InParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t bi = blockIdx.x;
-  const int64_t m = bi >> 3;
-  const int col = (int)(m % p.n_col_tiles);
-  const int64_t rt = (bi & 7) + 8 * (m / p.n_col_tiles);
+  const int64_t m = bi >> 3;                    // position in this XCD's sequence
+  const int64_t grp = m / (kRowGroup * p.n_col_tiles);
+  const int idx = (int)(m - grp * (kRowGroup * p.n_col_tiles));
+  const int col = idx / kRowGroup;
+  const int64_t rt = (bi & 7) + 8 * (grp * kRowGroup + idx % kRowGroup);
   if (rt >= p.n_row_tiles) return;
   const int64_t r0 = rt * p.mo - p.halo;
   const bool gate_tile = col >= p.n_kvq_tiles;
@@ -320,11 +387,12 @@ bool input_supported(int D, int H, int d, int w) {
 
 int64_t input_grid(int64_t R, int D, int H, int d, int w) {
   (void)D;
+  // token tiles padded to whole groups on every XCD; the padding exits at once
   const int mo = kMT - (w - 1);
   const int64_t rows = (R + mo - 1) / mo;
-  const int64_t rows8 = (rows + 7) / 8 * 8;
+  const int64_t per_xcd = ((rows + 7) / 8 + kRowGroup - 1) / kRowGroup * kRowGroup;
   const int64_t cols = (int64_t)3 * H * d / kNT + (3 * H + kNT - 1) / kNT;
-  return rows8 * cols;
+  return 8 * per_xcd * cols;
 }
 
 hipError_t launch_input(int B, int N, int D, int H, int d, int w, const void* x, const void* w_proj,
