@@ -133,13 +133,14 @@ def bench_input_side(args, np, torch, tmm, wl):
           f"({achieved / PEAK_TFLOPS['bf16'] * 100:.1f}% of bf16 peak)", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         import oracle
-        f = wl.input_side_f64(wl.make_input_side(icfg.with_(B=1), n_tokens=2048))
+        f = wl.input_side_f64(wl.make_input_side(icfg.with_(B=1)))
         t1 = time.perf_counter()
         oracle.input_side(f["x"], f["w_proj"], f["conv_w"], f["w_gate"], f["b_gate"], f["gate_scale"],
                           H=icfg.H, d=icfg.d)
         el = time.perf_counter() - t1
-        res["cpu_baseline"] = {"value": 2048 / el, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
-                               "kind": "oracle", "sample": f"1 sequence x 2048 tokens, fp64 numpy, {el:.2f} s"}
+        res["cpu_baseline"] = {"value": icfg.N / el, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
+                               "kind": "oracle",
+                               "sample": f"1 of {icfg.B} sequences x {icfg.N} tokens, fp64 numpy matmuls, {el:.2f} s"}
     return res
 
 
