@@ -7,3 +7,4 @@ from .titans_oracle import (  # noqa: F401
     build, lib_path, param_count, memory_apply, memory_grad, forward, max_threads,
 )
 from .input_oracle import input_side  # noqa: F401
+from .backward_oracle import backward, forward_torch  # noqa: F401
