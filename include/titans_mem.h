@@ -159,6 +159,41 @@ int titans_mem_retrieve(const titans_mem_desc* desc, const void* q, const float*
                         void* y_out, void* stream);
 
 /*
+ * titans_mem_backward -- gradients through titans_mem_forward, for training
+ * what produces the memory's inputs (section 3.1, "Objective": the memory's
+ * weights are fitted in an inner loop at test time; the rest of the model
+ * learns in an outer loop, through the memory).
+ *
+ * Returns the vector-Jacobian products of the forward map (same desc,
+ * inputs and chunk as the forward call) with the output adjoints:
+ *   dy               [B,H,N,d] fp32, device, or NULL (zero): dL/dy
+ *   dW_out, dS_out   [B,H,P] fp32, device, or NULL (zero): dL/dW_out, dL/dS_out
+ * into
+ *   dk, dv, dq       [B,H,N,d] fp32, device, written
+ *   dalpha, deta, dtheta  [B,H,N] fp32 ([B,H,ceil(N/chunk)] with
+ *                    TM_FLAG_CHUNK_GATES), device, written
+ *   dW_in, dS_in     [B,H,P] fp32, device, written
+ * The derivative includes the second-order term of the chunk-start
+ * gradients (each token's inner gradient depends on W at its chunk start).
+ * Both read modes.  Arithmetic is fp32 whatever the io dtype (bf16 inputs
+ * are read exactly).  Outputs must not overlap each other or any input.
+ * Supported: every layer width a multiple of 4, at most 1024, N >= 1.
+ * The workspace holds (W, S) at every chunk start and one chunk's per-token
+ * states: titans_mem_backward_workspace_bytes(desc, chunk) bytes.
+ */
+int64_t titans_mem_backward_workspace_bytes(const titans_mem_desc* desc, int32_t chunk);
+
+int titans_mem_backward(const titans_mem_desc* desc,
+                        const void* k, const void* v, const void* q,
+                        const float* alpha, const float* eta, const float* theta,
+                        const float* W_in, const float* S_in, int32_t chunk,
+                        const float* dy, const float* dW_out, const float* dS_out,
+                        float* dk, float* dv, float* dq,
+                        float* dalpha, float* deta, float* dtheta,
+                        float* dW_in, float* dS_in,
+                        void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * titans_mem_input -- the step before the memory: model activations x to
  * the memory's keys, values, queries and gates, for whole sequences.
  *

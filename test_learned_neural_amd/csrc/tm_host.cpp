@@ -180,6 +180,61 @@ int titans_mem_retrieve(const titans_mem_desc* desc, const void* q, const float*
   return err == hipSuccess ? TM_OK : TM_ERR_HIP;
 }
 
+int64_t titans_mem_backward_workspace_bytes(const titans_mem_desc* desc, int32_t chunk) {
+  Shape s;
+  int rc = build_shape(desc, &s);
+  if (rc) return rc;
+  if (chunk <= 0) return TM_ERR_INVALID;
+  if (!titans::backward_supported(s, chunk)) return TM_ERR_UNSUPPORTED;
+  return titans::backward_ws_floats_per_stream(s, chunk) * (int64_t)sizeof(float) * s.streams;
+}
+
+int titans_mem_backward(const titans_mem_desc* desc, const void* k, const void* v, const void* q,
+                        const float* alpha, const float* eta, const float* theta, const float* W_in,
+                        const float* S_in, int32_t chunk, const float* dy, const float* dW_out,
+                        const float* dS_out, float* dk, float* dv, float* dq, float* dalpha, float* deta,
+                        float* dtheta, float* dW_in, float* dS_in, void* workspace, int64_t workspace_bytes,
+                        void* stream) {
+  Shape s;
+  int rc = build_shape(desc, &s);
+  if (rc) return rc;
+  if (chunk <= 0) return TM_ERR_INVALID;
+  const void* required[] = {k, v, q, alpha, eta, theta, W_in, S_in, dk, dv, dq, dalpha, deta, dtheta, dW_in, dS_in};
+  for (const void* p : required)
+    if (!p || !aligned16(p)) return TM_ERR_INVALID;
+  const void* optional[] = {dy, dW_out, dS_out, workspace};
+  for (const void* p : optional)
+    if (p && !aligned16(p)) return TM_ERR_INVALID;
+  if (!titans::backward_supported(s, chunk)) return TM_ERR_UNSUPPORTED;
+  const int64_t need = titans::backward_ws_floats_per_stream(s, chunk) * (int64_t)sizeof(float) * s.streams;
+  if (!workspace || workspace_bytes < need) return TM_ERR_WORKSPACE;
+  const int64_t esz = s.io == TM_IO_BF16 ? 2 : 4;
+  const int64_t tok = (int64_t)s.streams * s.N * s.d;
+  const int64_t gate_rows = s.chunk_gates ? ((int64_t)s.N + chunk - 1) / chunk : s.N;
+  const int64_t gates = (int64_t)s.streams * gate_rows * 4;
+  const int64_t state = (int64_t)s.streams * s.P * 4;
+  const Range ranges[] = {
+      {(const char*)k, tok * esz, false},   {(const char*)v, tok * esz, false},
+      {(const char*)q, tok * esz, false},   {(const char*)alpha, gates, false},
+      {(const char*)eta, gates, false},     {(const char*)theta, gates, false},
+      {(const char*)W_in, state, false},    {(const char*)S_in, state, false},
+      {(const char*)dy, tok * 4, false},    {(const char*)dW_out, state, false},
+      {(const char*)dS_out, state, false},  {(const char*)dk, tok * 4, true},
+      {(const char*)dv, tok * 4, true},     {(const char*)dq, tok * 4, true},
+      {(const char*)dalpha, gates, true},   {(const char*)deta, gates, true},
+      {(const char*)dtheta, gates, true},   {(const char*)dW_in, state, true},
+      {(const char*)dS_in, state, true},    {(const char*)workspace, need, true},
+  };
+  const int nr = sizeof(ranges) / sizeof(ranges[0]);
+  for (int i = 0; i < nr; ++i)
+    for (int j = i + 1; j < nr; ++j)
+      if ((ranges[i].writes || ranges[j].writes) && overlap(ranges[i], ranges[j])) return TM_ERR_ALIAS;
+  hipError_t err = titans::launch_backward(s, chunk, k, v, q, alpha, eta, theta, W_in, S_in, dy, dW_out, dS_out,
+                                           dk, dv, dq, dalpha, deta, dtheta, dW_in, dS_in, (float*)workspace,
+                                           (hipStream_t)stream);
+  return err == hipSuccess ? TM_OK : TM_ERR_HIP;
+}
+
 int titans_mem_input(const titans_input_desc* desc, const void* x, const void* w_proj, const float* conv_w,
                      const void* w_gate, const float* b_gate, float alpha_scale, float eta_scale,
                      float theta_scale, void* k_out, void* v_out, void* q_out, float* alpha_out,

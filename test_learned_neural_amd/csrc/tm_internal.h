@@ -43,6 +43,17 @@ hipError_t launch_mlp2(const Shape& s, int chunk, const void* k, const void* v, 
                        const float* W_in, const float* S_in, void* y, float* W_out,
                        float* S_out, void* ws, hipStream_t stream);
 
+// Backward pass through the memory (generic fp32, one workgroup per stream).
+constexpr int kMaxWidthBackward = 1024;
+bool backward_supported(const Shape& s, int chunk);
+int backward_lds_bytes(const Shape& s);
+int64_t backward_ws_floats_per_stream(const Shape& s, int chunk);
+hipError_t launch_backward(const Shape& s, int chunk, const void* k, const void* v, const void* q,
+                           const float* alpha, const float* eta, const float* theta, const float* W_in,
+                           const float* S_in, const float* dy, const float* dW_out, const float* dS_out, float* dk,
+                           float* dv, float* dq, float* dalpha, float* deta, float* dtheta, float* dW_in,
+                           float* dS_in, float* ws, hipStream_t stream);
+
 // Input side (x -> k, v, q and the gates): bf16 MFMA GEMM with a fused
 // convolution / SiLU / l2-norm / sigmoid epilogue.
 bool input_supported(int D, int H, int d, int w);

@@ -25,7 +25,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtitans_m
 
 EXPORTS = ("titans_mem_abi_version", "titans_mem_param_count", "titans_mem_select_path",
            "titans_mem_workspace_bytes", "titans_mem_forward", "titans_mem_retrieve",
-           "titans_mem_input", "titans_mem_status_string")
+           "titans_mem_input", "titans_mem_backward", "titans_mem_backward_workspace_bytes",
+           "titans_mem_status_string")
 
 
 class Desc(ctypes.Structure):
@@ -84,6 +85,11 @@ def load():
     lib.titans_mem_forward.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, i32, vp, fp, fp, vp, i64, vp]
     lib.titans_mem_retrieve.restype = ctypes.c_int
     lib.titans_mem_retrieve.argtypes = [dp, vp, fp, vp, vp]
+    lib.titans_mem_backward_workspace_bytes.restype = i64
+    lib.titans_mem_backward_workspace_bytes.argtypes = [dp, i32]
+    lib.titans_mem_backward.restype = ctypes.c_int
+    lib.titans_mem_backward.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, i32, fp, fp, fp,
+                                        fp, fp, fp, fp, fp, fp, fp, fp, vp, i64, vp]
     lib.titans_mem_input.restype = ctypes.c_int
     lib.titans_mem_input.argtypes = [ctypes.POINTER(InputDesc), vp, vp, fp, vp, fp, ctypes.c_float, ctypes.c_float,
                                      ctypes.c_float, vp, vp, vp, fp, fp, fp, vp]
@@ -117,6 +123,18 @@ def raw_forward(desc: Desc, k, v, q, alpha, eta, theta, W_in, S_in, chunk, y_out
     return int(load().titans_mem_forward(ctypes.byref(desc), k, v, q, alpha, eta, theta, W_in, S_in,
                                          int(chunk), y_out, W_out, S_out, workspace,
                                          int(workspace_bytes_), stream))
+
+
+def backward_workspace_bytes(desc: Desc, chunk: int) -> int:
+    return int(load().titans_mem_backward_workspace_bytes(ctypes.byref(desc), int(chunk)))
+
+
+def raw_backward(desc: Desc, k, v, q, alpha, eta, theta, W_in, S_in, chunk, dy, dW_out, dS_out, dk, dv, dq,
+                 dalpha, deta, dtheta, dW_in, dS_in, workspace, workspace_bytes_, stream) -> int:
+    """Direct call of titans_mem_backward with integer device addresses; returns the status."""
+    return int(load().titans_mem_backward(ctypes.byref(desc), k, v, q, alpha, eta, theta, W_in, S_in, int(chunk),
+                                          dy, dW_out, dS_out, dk, dv, dq, dalpha, deta, dtheta, dW_in, dS_in,
+                                          workspace, int(workspace_bytes_), stream))
 
 
 def raw_input(desc: InputDesc, x, w_proj, conv_w, w_gate, b_gate, scales, k_out, v_out, q_out, alpha_out,
@@ -251,3 +269,49 @@ def input_side(x, w_proj, conv_w, w_gate, b_gate, gate_scale, *, H: int, d: int,
     if rc != OK:
         raise TitansMemError(rc, "titans_mem_input")
     return out
+
+
+def backward(k, v, q, alpha, eta, theta, W_in, S_in, chunk: int, *, hidden: int, n_layers: int,
+             dy=None, dW_out=None, dS_out=None, read_mode: int = READ_AFTER_WRITE, chunk_gates: bool = False):
+    """Gradients through titans_mem_forward (titans_mem_backward).
+
+    Same inputs as forward(); dy [B,H,N,d], dW_out / dS_out [B,H,P] are
+    float32 adjoints of the outputs (None = zero).  Returns a dict of
+    float32 tensors: k, v, q [B,H,N,d]; alpha, eta, theta (the gates'
+    shape); W_in, S_in [B,H,P].
+    """
+    torch = _torch()
+    B, H, N, d = k.shape
+    io = "bf16" if k.dtype == torch.bfloat16 else "f32"
+    desc = make_desc(B, H, N, d, hidden, n_layers, io, read_mode, FLAG_CHUNK_GATES if chunk_gates else 0)
+    P = param_count(desc)
+    if P < 0:
+        raise TitansMemError(P, "titans_mem_param_count")
+    dev = k.device
+    for name, t in (("k", k), ("v", v), ("q", q)):
+        _check(t, name, (B, H, N, d), k.dtype, dev)
+    n_gates = (N + chunk - 1) // chunk if chunk_gates and chunk > 0 else N
+    for name, t in (("alpha", alpha), ("eta", eta), ("theta", theta)):
+        _check(t, name, (B, H, n_gates), torch.float32, dev)
+    for name, t in (("W_in", W_in), ("S_in", S_in)):
+        _check(t, name, (B, H, P), torch.float32, dev)
+    if dy is not None:
+        _check(dy, "dy", (B, H, N, d), torch.float32, dev)
+    for name, t in (("dW_out", dW_out), ("dS_out", dS_out)):
+        if t is not None:
+            _check(t, name, (B, H, P), torch.float32, dev)
+    g = {n: torch.empty((B, H, N, d), dtype=torch.float32, device=dev) for n in ("k", "v", "q")}
+    g.update({n: torch.empty((B, H, n_gates), dtype=torch.float32, device=dev) for n in ("alpha", "eta", "theta")})
+    g.update({n: torch.empty((B, H, P), dtype=torch.float32, device=dev) for n in ("W_in", "S_in")})
+    need = backward_workspace_bytes(desc, chunk)
+    if need < 0:
+        raise TitansMemError(need, "titans_mem_backward_workspace_bytes")
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = raw_backward(desc, _ptr(k), _ptr(v), _ptr(q), _ptr(alpha), _ptr(eta), _ptr(theta), _ptr(W_in), _ptr(S_in),
+                      chunk, _ptr(dy), _ptr(dW_out), _ptr(dS_out), _ptr(g["k"]), _ptr(g["v"]), _ptr(g["q"]),
+                      _ptr(g["alpha"]), _ptr(g["eta"]), _ptr(g["theta"]), _ptr(g["W_in"]), _ptr(g["S_in"]),
+                      _ptr(ws), need, stream)
+    if rc != OK:
+        raise TitansMemError(rc, "titans_mem_backward")
+    return g

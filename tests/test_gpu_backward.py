@@ -1,0 +1,127 @@
+"""GPU parity of titans_mem_backward against the fp64 gradient oracle.
+
+The kernel is fp32 throughout, so the bar is the fp32 tolerance, 1e-3,
+norm-wise per stream for every gradient (dk, dv, dq, the three gates, dW_in,
+dS_in).  Cases: linear, 2- and 3-layer memories, both read modes, chunks
+from 1 to longer than the sequence, ragged tails, per-chunk gates, bf16
+inputs, each output adjoint alone, and the headline memory shape (d = 64,
+hidden = 256) on a short prefix.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from test_learned_neural_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    return torch
+
+
+def _problem(seed, B, H, N, d, h, L, io="f32", chunk_gates=False, chunk=8):
+    """Seeded inputs in the stable regime of the gradient pins (unit keys
+    and queries, theta <= 0.15, eta <= 0.9)."""
+    rng = np.random.default_rng(seed)
+    S = B * H
+    P = oracle.param_count(d, h, L)
+    unit = lambda a: a / np.linalg.norm(a, axis=-1, keepdims=True)
+    x = dict(k=unit(rng.standard_normal((S, N, d))), v=0.5 * rng.standard_normal((S, N, d)),
+             q=unit(rng.standard_normal((S, N, d))))
+    G = -(-N // chunk) if chunk_gates else N
+    x.update(alpha=rng.uniform(0, .2, (S, G)), eta=rng.uniform(.5, .9, (S, G)), theta=rng.uniform(0, .15, (S, G)),
+             W_in=rng.standard_normal((S, P)) * 0.3 / np.sqrt(max(d, 1) / 4), S_in=rng.standard_normal((S, P)) * 0.02)
+    # storage rounding: the io dtype for k, v, q, fp32 for the rest; the oracle sees the rounded values
+    for n in ("k", "v", "q"):
+        x[n] = wl.io_to_f64(wl.round_io(x[n], io), io)
+    for n in ("alpha", "eta", "theta", "W_in", "S_in"):
+        x[n] = x[n].astype(np.float32).astype(np.float64)
+    adj = dict(dy=rng.standard_normal((S, N, d)).astype(np.float32).astype(np.float64),
+               dW_out=rng.standard_normal((S, P)).astype(np.float32).astype(np.float64),
+               dS_out=rng.standard_normal((S, P)).astype(np.float32).astype(np.float64))
+    return x, adj, P
+
+
+def _to_dev(a, shape, dtype=None):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, np.float32)).reshape(shape).cuda()
+    return t if dtype is None else t.to(dtype)
+
+
+def _run(x, adj, B, H, N, d, h, L, chunk, io="f32", read_mode=0, chunk_gates=False, use=("dy", "dW_out", "dS_out")):
+    import torch
+    from test_learned_neural_amd import titans_mem as tmm
+    P = x["W_in"].shape[1]
+    tdt = torch.bfloat16 if io == "bf16" else None
+    G = x["alpha"].shape[1]
+    dev = {n: _to_dev(x[n], (B, H, N, d), tdt) for n in ("k", "v", "q")}
+    dev.update({n: _to_dev(x[n], (B, H, G)) for n in ("alpha", "eta", "theta")})
+    dev.update({n: _to_dev(x[n], (B, H, P)) for n in ("W_in", "S_in")})
+    kw = {}
+    if "dy" in use:
+        kw["dy"] = _to_dev(adj["dy"], (B, H, N, d))
+    if "dW_out" in use:
+        kw["dW_out"] = _to_dev(adj["dW_out"], (B, H, P))
+    if "dS_out" in use:
+        kw["dS_out"] = _to_dev(adj["dS_out"], (B, H, P))
+    g = tmm.backward(dev["k"], dev["v"], dev["q"], dev["alpha"], dev["eta"], dev["theta"], dev["W_in"], dev["S_in"],
+                     chunk, hidden=h, n_layers=L, read_mode=read_mode, chunk_gates=chunk_gates, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.backward(**x, dy=adj["dy"] if "dy" in use else None,
+                          dW_out=adj["dW_out"] if "dW_out" in use else None,
+                          dS_out=adj["dS_out"] if "dS_out" in use else None,
+                          d=d, hidden=h, n_layers=L, chunk=chunk, read_mode=read_mode, chunk_gates=chunk_gates)
+    S = B * H
+    worst = {}
+    for name, r in ref.items():
+        gg = g[name].cpu().double().numpy().reshape(r.shape)
+        assert np.all(np.isfinite(gg)), name
+        for s in range(S):
+            nr = np.linalg.norm(r[s])
+            e = np.linalg.norm(gg[s] - r[s]) / max(nr, 1e-30) if nr > 0 else np.linalg.norm(gg[s])
+            worst[name] = max(worst.get(name, 0.0), e)
+    print(f"L{L} d{d} h{h} N{N} chunk{chunk} io {io} read {read_mode} gates/chunk {chunk_gates} {use}: " +
+          " ".join(f"{n} {e:.1e}" for n, e in worst.items()), flush=True)
+    for name, e in worst.items():
+        assert e < TOL, (name, e)
+
+
+@pytest.mark.parametrize("B,H,N,d,h,L,chunk", [(1, 1, 40, 16, 0, 1, 8), (1, 2, 37, 8, 16, 2, 5), (2, 1, 30, 8, 12, 3, 4),
+                                               (1, 1, 24, 16, 32, 2, 1), (1, 2, 20, 8, 16, 2, 64),
+                                               (1, 1, 33, 4, 8, 4, 6)])
+def test_backward_shapes(B, H, N, d, h, L, chunk):
+    x, adj, P = _problem(100 + N + L, B, H, N, d, h, L)
+    _run(x, adj, B, H, N, d, h, L, chunk)
+
+
+def test_backward_chunk_start_read():
+    x, adj, P = _problem(201, 1, 2, 29, 8, 16, 2)
+    _run(x, adj, 1, 2, 29, 8, 16, 2, 6, read_mode=1)
+
+
+def test_backward_chunk_gates():
+    x, adj, P = _problem(202, 1, 2, 27, 8, 16, 2, chunk_gates=True, chunk=5)
+    _run(x, adj, 1, 2, 27, 8, 16, 2, 5, chunk_gates=True)
+
+
+def test_backward_bf16_inputs():
+    x, adj, P = _problem(203, 1, 2, 31, 16, 32, 2, io="bf16")
+    _run(x, adj, 1, 2, 31, 16, 32, 2, 8, io="bf16")
+
+
+@pytest.mark.parametrize("use", [("dy",), ("dW_out",), ("dS_out",)])
+def test_backward_each_adjoint(use):
+    x, adj, P = _problem(204, 1, 1, 19, 8, 16, 2)
+    _run(x, adj, 1, 1, 19, 8, 16, 2, 4, use=use)
+
+
+def test_backward_headline_shape_prefix():
+    """d = 64, hidden = 256, chunk 64 (the headline memory) on 96 tokens."""
+    x, adj, P = _problem(205, 1, 2, 96, 64, 256, 2, io="bf16")
+    _run(x, adj, 1, 2, 96, 64, 256, 2, 64, io="bf16")
