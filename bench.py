@@ -144,6 +144,74 @@ def bench_input_side(args, np, torch, tmm, wl):
     return res
 
 
+def backward_flops_per_token(cfg):
+    """Algorithmic FLOPs of titans_mem_backward per memory token: the chunk
+    recomputation twice (forward sweep and reverse sweep: key forward,
+    backprop, state update), the retrieval forward and backward, the gate
+    inner products, and the Hessian-vector term (the inner backward's own
+    backward pass)."""
+    w = cfg.widths
+    P = cfg.param_count
+    first = w[0] * w[1]
+    run_chunk = 10 * P - 2 * first
+    reverse = 25 * P - 4 * first
+    return 2 * run_chunk + reverse
+
+
+def bench_backward(args, np, torch, tmm, wl, prefix=1024, steps=3):
+    """Gradients through the memory (titans_mem_backward) on the headline
+    memory shape, every stream, the first `prefix` tokens."""
+    cfg = wl.CONFIGS[args.config].with_(N=prefix)
+    inp = wl.make_inputs(cfg, workers=min(16, len(os.sched_getaffinity(0))))
+    B, H, N, d, P = cfg.B, cfg.H, cfg.N, cfg.d, cfg.param_count
+    if cfg.io == "bf16":
+        tok = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).reshape(B, H, N, d).cuda()
+    else:
+        tok = lambda a: torch.from_numpy(a).reshape(B, H, N, d).cuda()
+    per = lambda a, n: torch.from_numpy(a).reshape(B, H, n).cuda()
+    k, v, q = tok(inp["k"]), tok(inp["v"]), tok(inp["q"])
+    al, et, th = per(inp["alpha"], N), per(inp["eta"], N), per(inp["theta"], N)
+    W0, S0 = per(inp["W0"], P), per(inp["S0"], P)
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    dy = torch.randn(B, H, N, d, device="cuda", generator=gen)
+    run = lambda: tmm.backward(k, v, q, al, et, th, W0, S0, cfg.chunk, hidden=cfg.hidden, n_layers=cfg.n_layers,
+                               dy=dy)
+    run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    wall0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    launch_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    tokens = B * H * N
+    flops = backward_flops_per_token(cfg) * tokens
+    achieved = flops / launch_s / 1e12
+    res = {"workload": f"{cfg.name} (first {prefix} tokens of every stream)", "value": tokens / (wall / steps),
+           "unit": "memory-tokens/s", "ms_per_step": wall * 1e3 / steps, "dtype": "f32", "steps": steps,
+           "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
+                        "frac": achieved / PEAK_TFLOPS["f32"], "traffic": None,
+                        "algorithmic_flops_per_launch": flops, "avg_launch_ms": launch_s * 1e3}}
+    print(f"[bench] backward {cfg.name}, {prefix} tokens: {launch_s * 1e3:.1f} ms/launch, "
+          f"{tokens / launch_s:.3g} memory-tokens/s, {achieved:.2f} TFLOP/s fp32", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        import oracle
+        f = wl.inputs_f64(cfg, wl.make_inputs(cfg, streams=[(0, 0)], n_tokens=64))
+        dyn = dy[0, 0, :64].double().cpu().numpy()[None]
+        t1 = time.perf_counter()
+        oracle.backward(f["k"], f["v"], f["q"], f["alpha"], f["eta"], f["theta"], f["W0"], f["S0"], dyn, None, None,
+                        d=d, hidden=cfg.hidden, n_layers=cfg.n_layers, chunk=cfg.chunk)
+        el = time.perf_counter() - t1
+        res["cpu_baseline"] = {"value": 64 / el, "unit": "memory-tokens/s", "cores": torch.get_num_threads(),
+                               "kind": "oracle",
+                               "sample": f"1 stream x 64 tokens, fp64 torch reverse mode, {el:.2f} s"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,6 +222,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-input-side", action="store_true", help="skip the input-side leg")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the backward (gradients through the memory) and print its JSON line")
     ap.add_argument("--input-side-only", action="store_true",
                     help="time only the input side (x -> k, v, q, gates) and print its JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -184,6 +255,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tmm.load()
+    if args.backward_only:
+        print(json.dumps({"metric": "backward memory tokens/sec (gradients through the memory), 1 GPU", "n_gpus": 1,
+                          "higher_is_better": True, "data": "synthetic",
+                          **bench_backward(args, np, torch, tmm, wl)}), flush=True)
+        return
     if args.input_side_only:
         print(json.dumps({"metric": "input-side tokens/sec (x -> k, v, q, gates), 1 GPU", "n_gpus": 1,
                           "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
@@ -303,6 +379,8 @@ def main():
     }
     if not args.no_input_side:
         out["input_side"] = bench_input_side(args, np, torch, tmm, wl)
+    if not args.no_backward:
+        out["backward"] = bench_backward(args, np, torch, tmm, wl)
     print(json.dumps(out), flush=True)
 
 

@@ -118,18 +118,27 @@ __device__ __forceinline__ float d2act(float z) {
 // 16 lanes per row, float4 loads.  Ends with a barrier.
 __device__ void mv_rows(float* out, const float* M, const float* x, int n_out, int n_in) {
   const int sl = threadIdx.x & 15, gr = threadIdx.x >> 4;
-  for (int i0 = 0; i0 < n_out; i0 += kBT / 16) {
-    const int i = i0 + gr;
-    float s = 0.f;
-    if (i < n_out) {
-      const float* row = M + (int64_t)i * n_in;
-      for (int j = 4 * sl; j < n_in; j += 64) {
-        const float4 m = *(const float4*)(row + j);
-        s += m.x * x[j] + m.y * x[j + 1] + m.z * x[j + 2] + m.w * x[j + 3];
+  constexpr int kRowsPerPass = kBT / 16;
+  // four row passes at a time, so that four independent loads are in flight
+  for (int i0 = 0; i0 < n_out; i0 += 4 * kRowsPerPass) {
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 4 * sl; j < n_in; j += 64) {
+      float4 m[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kRowsPerPass + gr;
+        m[u] = i < n_out ? *(const float4*)(M + (int64_t)i * n_in + j) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
+      const float x0 = x[j], x1 = x[j + 1], x2 = x[j + 2], x3 = x[j + 3];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) s[u] += m[u].x * x0 + m[u].y * x1 + m[u].z * x2 + m[u].w * x3;
     }
-    s = sum16(s);
-    if (i < n_out && sl == 0) out[i] = s;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float t = sum16(s[u]);
+      const int i = i0 + u * kRowsPerPass + gr;
+      if (i < n_out && sl == 0) out[i] = t;
+    }
   }
   __syncthreads();
 }
@@ -159,6 +168,7 @@ __device__ void mv_cols(float* out, const float* M, const float* z, int n_out, i
   const int c = threadIdx.x % cg, g = threadIdx.x / cg;
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   if (g < rg) {
+#pragma unroll 4
     for (int i = g; i < n_out; i += rg) {
       const float4 m = *(const float4*)(M + (int64_t)i * n_in + 4 * c);
       const float zi = z[i];
@@ -178,6 +188,7 @@ __device__ void mv_cols(float* out, const float* M, const float* z, int n_out, i
 // M[i][j] += sc * a[i] b[j]   (float4 over j; no barrier)
 __device__ void rank1(float* M, const float* a, const float* b, int n_out, int n_in, float sc) {
   const int64_t n4 = (int64_t)n_out * n_in / 4;
+#pragma unroll 4
   for (int64_t e = threadIdx.x; e < n4; e += kBT) {
     const int64_t f = 4 * e;
     const int i = (int)(f / n_in), j = (int)(f - (int64_t)i * n_in);
@@ -256,6 +267,7 @@ __device__ void run_chunk(const BwdParams& p, int s, int c, float* base, float* 
       const float* dd = dl + p.zo[l];
       const int n_in = p.w[l - 1];
       const int64_t n4 = (int64_t)p.w[l] * n_in / 4;
+#pragma unroll 4
       for (int64_t e = threadIdx.x; e < n4; e += kBT) {
         const int64_t f = p.off[l] + 4 * e;
         const int i = (int)(4 * e / n_in), m = (int)(4 * e - (int64_t)i * n_in);
@@ -372,6 +384,7 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
 
       // (2) W_t = (1 - alpha) W_{t-1} + S_t, and eta's inner product
       float pa = 0.f, pe = 0.f;
+#pragma unroll 4
       for (int64_t e = threadIdx.x; e < P / 4; e += kBT) {
         float4 wb = ((float4*)Wb)[e], sb = ((float4*)Sb)[e];
         const float4 wp = ((const float4*)Wp)[e], sp = ((const float4*)Sp)[e];
@@ -442,6 +455,7 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
         __syncthreads();
       }
       // S_{t-1} adjoint
+#pragma unroll 4
       for (int64_t e = threadIdx.x; e < P / 4; e += kBT) {
         float4 sb = ((float4*)Sb)[e];
         sb.x *= et; sb.y *= et; sb.z *= et; sb.w *= et;
