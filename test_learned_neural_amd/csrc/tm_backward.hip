@@ -29,13 +29,15 @@
 //   zbar_{l-1} gets abar_{l-1} * s'(z_{l-1});  kbar = abar_0.
 //
 // Execution: one workgroup per stream, fp32 throughout.  A forward sweep
-// stores (W, S) at every chunk start in the workspace; the reverse sweep
+// (the generic kernel's chunked closed form, without retrieval) stores
+// (W, S) at every chunk start in the workspace; the reverse sweep
 // recomputes each chunk's per-token states W_t, S_t and the key-side
 // vectors (z, delta, b at W_c) into the workspace, then walks its tokens
 // backwards.  Matrices stay in global memory (L2-resident for the small
 // memories); vectors live in LDS.  Matrix-vector products use 16-lane
 // groups per row (float4 loads, DPP sums) or column groups with an LDS
-// reduction; rank-1 updates and inner products are float4 element loops.
+// reduction; the state adjoints are updated in one float4 pass per layer
+// that folds in every rank-1 term of the step.
 #include "tm_internal.h"
 
 #include <hip/hip_bf16.h>
@@ -43,7 +45,7 @@
 namespace titans {
 namespace {
 
-constexpr int kBT = 256;      // threads per workgroup
+constexpr int kBT = 512;      // threads per workgroup
 constexpr int kBW = kBT / 64;
 
 struct BwdParams {
@@ -185,20 +187,6 @@ __device__ void mv_cols(float* out, const float* M, const float* z, int n_out, i
   __syncthreads();
 }
 
-// M[i][j] += sc * a[i] b[j]   (float4 over j; no barrier)
-__device__ void rank1(float* M, const float* a, const float* b, int n_out, int n_in, float sc) {
-  const int64_t n4 = (int64_t)n_out * n_in / 4;
-#pragma unroll 4
-  for (int64_t e = threadIdx.x; e < n4; e += kBT) {
-    const int64_t f = 4 * e;
-    const int i = (int)(f / n_in), j = (int)(f - (int64_t)i * n_in);
-    const float ai = sc * a[i];
-    float4 m = *(float4*)(M + f);
-    m.x += ai * b[j]; m.y += ai * b[j + 1]; m.z += ai * b[j + 2]; m.w += ai * b[j + 3];
-    *(float4*)(M + f) = m;
-  }
-}
-
 __device__ __forceinline__ float io_load(const void* base, int io, int64_t i) {
   if (io == TM_IO_BF16) {
     const unsigned short u = ((const unsigned short*)base)[i];
@@ -207,9 +195,6 @@ __device__ __forceinline__ float io_load(const void* base, int io, int64_t i) {
   return ((const float*)base)[i];
 }
 
-__device__ void copy_p(float* dst, const float* src, int64_t P) {
-  for (int64_t e = threadIdx.x; e < P / 4; e += kBT) ((float4*)dst)[e] = ((const float4*)src)[e];
-}
 
 // Recompute chunk c from its checkpoint: per token j the key-side vectors at
 // W_c (z, delta, b into tv), and S_t, W_t into cs[j], cw[j].  Leaves xk
@@ -296,18 +281,8 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
   float* Sb = base + p.o_sb;
   float* Wcb = base + p.o_wcb;
 
-  // ---- forward sweep: (W, S) at every chunk start ----
-  copy_p(base, p.W_in + (int64_t)s * P, P);
-  copy_p(base + P, p.S_in + (int64_t)s * P, P);
-  __syncthreads();
-  for (int c = 0; c + 1 < p.nchunks; ++c) {
-    run_chunk(p, s, c, base, lds);
-    const int n = min(p.chunk, p.N - c * p.chunk);
-    copy_p(base + (int64_t)(c + 1) * 2 * P, base + p.o_cw + (int64_t)(n - 1) * P, P);
-    copy_p(base + (int64_t)(c + 1) * 2 * P + P, base + p.o_cs + (int64_t)(n - 1) * P, P);
-    __syncthreads();
-  }
-
+  // (W, S) at every chunk start are in the workspace: the chunked forward
+  // sweep that precedes this kernel on the stream wrote them.
   // ---- reverse sweep ----
   for (int64_t e = threadIdx.x; e < P; e += kBT) {
     Wb[e] = p.dW_out ? p.dW_out[(int64_t)s * P + e] : 0.f;
@@ -331,7 +306,10 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
   float* zb = db + p.sumn;             // zbar
   float* zs = zb + p.sumn;             // the s'' part of zbar
   float* rp = zs + p.sumn;             // r'_l = Sbar_l^T delta_l, [L][maxw]
+  float* dzq = rp + p.L * p.maxw;      // the retrieval backprop's dz_l (sum of widths)
+  float* ee = dzq + p.sumn;            // e_l = deltabar_l * s'(z_l) of the Hessian-vector term
 
+  float eta_prev = 1.f;   // Sbar still owes this factor (the last processed token's eta)
   for (int c = p.nchunks - 1; c >= 0; --c) {
     run_chunk(p, s, c, base, lds);
     const int c0 = c * p.chunk;
@@ -351,7 +329,6 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
 
       // (1) retrieval: y_t = M_{Wr}(q_t)
       const float* Wr = p.read_mode == TM_READ_CHUNK_START ? Wc : Wt;
-      float* Rb = p.read_mode == TM_READ_CHUNK_START ? Wcb : Wb;
       if (p.dy) {
         for (int i = threadIdx.x; i < p.d; i += kBT) {
           xq[i] = io_load(p.q, p.io, tt * p.d + i);
@@ -366,10 +343,9 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
           __syncthreads();
         }
         for (int l = p.L; l >= 1; --l) {
-          const float* ain = l == 1 ? xq : qa + p.zo[l - 1];
-          // da = Wr_l^T dz_l (read before Rb changes: Rb and Wr are different arrays)
+          // da = Wr_l^T dz_l; dz_l is kept for the fused state-adjoint passes
           mv_cols(v2, Wr + p.off[l], v1, p.w[l], p.w[l - 1], red);
-          rank1(Rb + p.off[l], v1, ain, p.w[l], p.w[l - 1], 1.f);
+          for (int i = threadIdx.x; i < p.w[l]; i += kBT) dzq[p.zo[l] + i] = v1[i];
           __syncthreads();
           if (l > 1) {
             for (int i = threadIdx.x; i < p.w[l - 1]; i += kBT) v1[i] = v2[i] * dact(qz[p.zo[l - 1] + i]);
@@ -381,19 +357,41 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
       } else {
         for (int i = threadIdx.x; i < p.d; i += kBT) p.dq[tt * p.d + i] = 0.f;
       }
+      // the retrieval's rank-1 terms go to Wbar (read-after-write) or to W_c's
+      // adjoint (chunk-start read); none without dL/dy (xq and qa are then unset)
+      const bool rw = p.dy && p.read_mode != TM_READ_CHUNK_START;
+      const bool rc = p.dy && p.read_mode == TM_READ_CHUNK_START;
 
-      // (2) W_t = (1 - alpha) W_{t-1} + S_t, and eta's inner product
+      // (2) W_t = (1 - alpha) W_{t-1} + S_t, and eta's inner product.  Folded
+      // into the same pass: the retrieval's rank-1 terms dz_l aq_{l-1}^T
+      // (read-after-write) and the previous token's Sbar <- eta Sbar.
       float pa = 0.f, pe = 0.f;
+      for (int l = 1; l <= p.L; ++l) {
+        const float* aq = l == 1 ? xq : qa + p.zo[l - 1];
+        const float* dz = dzq + p.zo[l];
+        const int n_in = p.w[l - 1];
+        const int64_t n4 = (int64_t)p.w[l] * n_in / 4;
+        float4* wb4 = (float4*)(Wb + p.off[l]);
+        float4* sb4 = (float4*)(Sb + p.off[l]);
+        const float4* wp4 = (const float4*)(Wp + p.off[l]);
+        const float4* sp4 = (const float4*)(Sp + p.off[l]);
 #pragma unroll 4
-      for (int64_t e = threadIdx.x; e < P / 4; e += kBT) {
-        float4 wb = ((float4*)Wb)[e], sb = ((float4*)Sb)[e];
-        const float4 wp = ((const float4*)Wp)[e], sp = ((const float4*)Sp)[e];
-        pa += wb.x * wp.x + wb.y * wp.y + wb.z * wp.z + wb.w * wp.w;
-        sb.x += wb.x; sb.y += wb.y; sb.z += wb.z; sb.w += wb.w;
-        pe += sb.x * sp.x + sb.y * sp.y + sb.z * sp.z + sb.w * sp.w;
-        wb.x *= 1.f - al; wb.y *= 1.f - al; wb.z *= 1.f - al; wb.w *= 1.f - al;
-        ((float4*)Wb)[e] = wb;
-        ((float4*)Sb)[e] = sb;
+        for (int64_t e = threadIdx.x; e < n4; e += kBT) {
+          const int i = (int)(4 * e / n_in), j = (int)(4 * e - (int64_t)i * n_in);
+          float4 wb = wb4[e], sb = sb4[e];
+          const float4 wp = wp4[e], sp = sp4[e];
+          if (rw) {
+            const float di = dz[i];
+            wb.x += di * aq[j]; wb.y += di * aq[j + 1]; wb.z += di * aq[j + 2]; wb.w += di * aq[j + 3];
+          }
+          pa += wb.x * wp.x + wb.y * wp.y + wb.z * wp.z + wb.w * wp.w;
+          sb.x = eta_prev * sb.x + wb.x; sb.y = eta_prev * sb.y + wb.y;
+          sb.z = eta_prev * sb.z + wb.z; sb.w = eta_prev * sb.w + wb.w;
+          pe += sb.x * sp.x + sb.y * sp.y + sb.z * sp.z + sb.w * sp.w;
+          wb.x *= 1.f - al; wb.y *= 1.f - al; wb.z *= 1.f - al; wb.w *= 1.f - al;
+          wb4[e] = wb;
+          sb4[e] = sb;
+        }
       }
       const float abar = -block_sum(pa, red);
       const float ebar = block_sum(pe, red);
@@ -425,12 +423,11 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
         const int nl = p.w[l - 1];
         for (int i = threadIdx.x; i < nl; i += kBT) {
           const float z = za[p.zo[l - 1] + i], dbv = db[p.zo[l - 1] + i];
-          v1[i] = dbv * dact(z);                                   // e_{l-1}
+          ee[p.zo[l - 1] + i] = dbv * dact(z);                     // e_{l-1}
           zs[p.zo[l - 1] + i] = dbv * bb[p.zo[l - 1] + i] * d2act(z);
         }
         __syncthreads();
-        mv_rows(v2, Wc + p.off[l], v1, p.w[l], nl);                // W_l e_{l-1}
-        rank1(Wcb + p.off[l], dl + p.zo[l], v1, p.w[l], nl, 1.f);  // delta_l e_{l-1}^T
+        mv_rows(v2, Wc + p.off[l], ee + p.zo[l - 1], p.w[l], nl);  // W_l e_{l-1}
         for (int i = threadIdx.x; i < p.w[l]; i += kBT) db[p.zo[l] + i] = -th * up[p.zo[l] + i] + v2[i];
         __syncthreads();
       }
@@ -444,7 +441,35 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
         const float* ain = l == 1 ? xk : aa + p.zo[l - 1];
         // abar_{l-1} = W_l^T zbar_l + r_l, r_l = -theta r'_l
         mv_cols(v2, Wc + p.off[l], zb + p.zo[l], p.w[l], p.w[l - 1], red, rp + (l - 1) * p.maxw, -th);
-        rank1(Wcb + p.off[l], zb + p.zo[l], ain, p.w[l], p.w[l - 1], 1.f);
+        // W_c's adjoint, layer l: zbar_l a_{l-1}^T + delta_l e_{l-1}^T (l >= 2), and with the
+        // chunk-start read the retrieval's dz_l aq_{l-1}^T
+        {
+          const float* zbl = zb + p.zo[l];
+          const float* dll = dl + p.zo[l];
+          const float* eel = ee + p.zo[l - 1];
+          const float* dzl = dzq + p.zo[l];
+          const float* aq = l == 1 ? xq : qa + p.zo[l - 1];
+          const bool two = l >= 2, three = rc;
+          const int n_in = p.w[l - 1];
+          const int64_t n4 = (int64_t)p.w[l] * n_in / 4;
+          float4* m4 = (float4*)(Wcb + p.off[l]);
+#pragma unroll 4
+          for (int64_t e = threadIdx.x; e < n4; e += kBT) {
+            const int i = (int)(4 * e / n_in), j = (int)(4 * e - (int64_t)i * n_in);
+            float4 m = m4[e];
+            const float zi = zbl[i];
+            m.x += zi * ain[j]; m.y += zi * ain[j + 1]; m.z += zi * ain[j + 2]; m.w += zi * ain[j + 3];
+            if (two) {
+              const float di = dll[i];
+              m.x += di * eel[j]; m.y += di * eel[j + 1]; m.z += di * eel[j + 2]; m.w += di * eel[j + 3];
+            }
+            if (three) {
+              const float qi = dzl[i];
+              m.x += qi * aq[j]; m.y += qi * aq[j + 1]; m.z += qi * aq[j + 2]; m.w += qi * aq[j + 3];
+            }
+            m4[e] = m;
+          }
+        }
         __syncthreads();
         if (l > 1) {
           for (int i = threadIdx.x; i < p.w[l - 1]; i += kBT)
@@ -454,13 +479,8 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
         }
         __syncthreads();
       }
-      // S_{t-1} adjoint
-#pragma unroll 4
-      for (int64_t e = threadIdx.x; e < P / 4; e += kBT) {
-        float4 sb = ((float4*)Sb)[e];
-        sb.x *= et; sb.y *= et; sb.z *= et; sb.w *= et;
-        ((float4*)Sb)[e] = sb;
-      }
+      // S_{t-1}'s adjoint is eta_t Sbar: applied in the next token's pass (or at the end)
+      eta_prev = et;
       if (threadIdx.x == 0) {
         if (p.chunk_gates) {
           gsum_a += abar; gsum_e += ebar; gsum_t += tbar;
@@ -480,7 +500,7 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
   }
   for (int64_t e = threadIdx.x; e < P; e += kBT) {
     p.dW_in[(int64_t)s * P + e] = Wb[e];
-    p.dS_in[(int64_t)s * P + e] = Sb[e];
+    p.dS_in[(int64_t)s * P + e] = eta_prev * Sb[e];
   }
 }
 
@@ -497,8 +517,8 @@ bool backward_supported(const Shape& s, int chunk) {
 int backward_lds_bytes(const Shape& s) {
   int sumn = 0;
   for (int l = 1; l <= s.L; ++l) sumn += s.widths[l];
-  // run_chunk: xk, z, a, delta, b, red; reverse sweep: xq, qz, qa, v1, v2, up, db, zb, zs, rp
-  const int floats = s.maxw + 4 * sumn + kBT * 4 + 3 * s.maxw + 6 * sumn + s.L * s.maxw;
+  // run_chunk: xk, z, a, delta, b, red; reverse sweep: xq, qz, qa, v1, v2, up, db, zb, zs, rp, dzq, ee
+  const int floats = s.maxw + 4 * sumn + kBT * 4 + 3 * s.maxw + 8 * sumn + s.L * s.maxw;
   return floats * 4;
 }
 
@@ -507,7 +527,8 @@ int64_t backward_ws_floats_per_stream(const Shape& s, int chunk) {
   const int b = chunk < s.N ? chunk : s.N;
   int sumn = 0;
   for (int l = 1; l <= s.L; ++l) sumn += s.widths[l];
-  return (int64_t)nchunks * 2 * s.P + 2 * (int64_t)b * s.P + (int64_t)b * 3 * sumn + 3 * s.P + 64;
+  return (int64_t)nchunks * 2 * s.P + 2 * (int64_t)b * s.P + (int64_t)b * 3 * sumn + 3 * s.P +
+         (generic_ws_floats_per_stream(s, b) + 3) / 4 * 4 + 64;
 }
 
 hipError_t launch_backward(const Shape& s, int chunk, const void* k, const void* v, const void* q,
@@ -552,9 +573,17 @@ hipError_t launch_backward(const Shape& s, int chunk, const void* k, const void*
   p.o_wb = p.o_tv + ((int64_t)b * 3 * p.sumn + 3) / 4 * 4;
   p.o_sb = p.o_wb + s.P;
   p.o_wcb = p.o_sb + s.P;
+  const int64_t o_gen = p.o_wcb + s.P;
+  // forward sweep: the chunk-start states, through the generic kernel's
+  // chunked form (its running state lives in this stream's Wbar, Sbar slots,
+  // which the reverse sweep then initialises)
+  hipError_t err = launch_generic_checkpoints(s, chunk, k, v, q, alpha, eta, theta, W_in, S_in, ws + p.o_wb,
+                                              ws + p.o_sb, p.ws_stream, ws, p.ws_stream, ws + o_gen, p.ws_stream,
+                                              stream);
+  if (err != hipSuccess) return err;
   const int lds = backward_lds_bytes(s);
   p.lds_floats = lds / 4;
-  hipError_t err = hipFuncSetAttribute((const void*)backward_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  err = hipFuncSetAttribute((const void*)backward_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(backward_kernel, dim3(s.streams), dim3(kBT), lds, stream, p);
   return hipGetLastError();

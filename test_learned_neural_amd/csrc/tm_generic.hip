@@ -49,9 +49,12 @@ struct GParams {
   const float* theta;
   const float* W_in;
   const float* S_in;
-  void* y;
+  void* y;            // NULL: no retrieval (the state sweep only)
   float* W;
   float* S;
+  int64_t state_stride;   // floats between streams in W, S (P unless they live in another layout)
+  float* ckpt;        // optional: (W, S) at every chunk start, [chunk][W | S] per stream
+  int64_t ckpt_stride;    // floats between streams in ckpt
   float* ws;
   int64_t ws_stride;  // floats per stream
 };
@@ -171,8 +174,8 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
   const int d = p.d, L = p.L;
-  float* W = p.W + (int64_t)s * p.P;
-  float* S = p.S + (int64_t)s * p.P;
+  float* W = p.W + (int64_t)s * p.state_stride;
+  float* S = p.S + (int64_t)s * p.state_stride;
   const float* Win = p.W_in + (int64_t)s * p.P;
   const float* Sin = p.S_in + (int64_t)s * p.P;
   if (W != Win)
@@ -186,6 +189,15 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
 
   for (int c0 = 0; c0 < p.N; c0 += p.chunk) {
     const int n = min(p.chunk, p.N - c0);
+    if (p.ckpt) {
+      // the state at this chunk's start (read only here; it is next written
+      // by this chunk's fold, many barriers later)
+      float* ck = p.ckpt + (int64_t)s * p.ckpt_stride + (int64_t)(c0 / p.chunk) * 2 * p.P;
+      for (int64_t i = tid; i < p.P; i += kThreads) {
+        ck[i] = W[i];
+        ck[p.P + i] = S[i];
+      }
+    }
     // the chunk's gates: token j at index j * gs (one shared value when the
     // gates are given per chunk)
     const int64_t g0 = p.chunk_gates ? (int64_t)s * ((p.N + p.chunk - 1) / p.chunk) + c0 / p.chunk : tok0 + c0;
@@ -263,7 +275,7 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
     }
     // ---- a5: retrieval ----
     int cur = 0;
-    for (int l = 1; l <= L; ++l) {
+    for (int l = 1; l <= L && p.y; ++l) {
       const int nin = p.widths[l - 1], nout = p.widths[l];
       const float* Wl = W + p.off[l];
       const float* Sl = S + p.off[l];
@@ -427,8 +439,37 @@ hipError_t launch_generic(const Shape& s, int chunk, const void* k, const void* 
   p.y = y;
   p.W = W_out;
   p.S = S_out;
+  p.state_stride = s.P;
+  p.ckpt = nullptr;
+  p.ckpt_stride = 0;
   p.ws = ws;
   p.ws_stride = generic_ws_floats_per_stream(s, p.b);
+  hipLaunchKernelGGL(generic_kernel, dim3(s.streams), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_generic_checkpoints(const Shape& s, int chunk, const void* k, const void* v, const void* q,
+                                      const float* alpha, const float* eta, const float* theta, const float* W_in,
+                                      const float* S_in, float* W, float* S, int64_t state_stride, float* ckpt,
+                                      int64_t ckpt_stride, float* ws, int64_t ws_stride, hipStream_t stream) {
+  GParams p = make_params(s, chunk);
+  p.b = chunk < s.N ? chunk : (s.N > 0 ? s.N : 1);
+  p.k = k;
+  p.v = v;
+  p.q = q;
+  p.alpha = alpha;
+  p.eta = eta;
+  p.theta = theta;
+  p.W_in = W_in;
+  p.S_in = S_in;
+  p.y = nullptr;
+  p.W = W;
+  p.S = S;
+  p.state_stride = state_stride;
+  p.ckpt = ckpt;
+  p.ckpt_stride = ckpt_stride;
+  p.ws = ws;
+  p.ws_stride = ws_stride;
   hipLaunchKernelGGL(generic_kernel, dim3(s.streams), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }

@@ -43,6 +43,13 @@ hipError_t launch_mlp2(const Shape& s, int chunk, const void* k, const void* v, 
                        const float* W_in, const float* S_in, void* y, float* W_out,
                        float* S_out, void* ws, hipStream_t stream);
 
+// The generic kernel as a state sweep only (no retrieval), writing (W, S) at
+// every chunk start to ckpt; W, S and ckpt are strided per stream.
+hipError_t launch_generic_checkpoints(const Shape& s, int chunk, const void* k, const void* v, const void* q,
+                                      const float* alpha, const float* eta, const float* theta, const float* W_in,
+                                      const float* S_in, float* W, float* S, int64_t state_stride, float* ckpt,
+                                      int64_t ckpt_stride, float* ws, int64_t ws_stride, hipStream_t stream);
+
 // Backward pass through the memory (generic fp32, one workgroup per stream).
 constexpr int kMaxWidthBackward = 1024;
 bool backward_supported(const Shape& s, int chunk);
