@@ -145,17 +145,19 @@ def bench_input_side(args, np, torch, tmm, wl):
 
 
 def backward_flops_per_token(cfg):
-    """Algorithmic FLOPs of titans_mem_backward per memory token: the chunk
-    recomputation twice (forward sweep and reverse sweep: key forward,
-    backprop, state update), the retrieval forward and backward, the gate
-    inner products, and the Hessian-vector term (the inner backward's own
-    backward pass)."""
+    """Algorithmic FLOPs of titans_mem_backward per memory token: the chunked
+    state sweep that yields the chunk-start states (key forward, backprop
+    and the two weighted reductions), the reverse sweep's per-token
+    recomputation (key forward, backprop, state update), the retrieval
+    forward and backward, the gate inner products, and the Hessian-vector
+    term (the inner backward's own backward pass): 43 P - 8 d n_1."""
     w = cfg.widths
     P = cfg.param_count
     first = w[0] * w[1]
+    sweep = 2 * (4 * P - first)
     run_chunk = 10 * P - 2 * first
     reverse = 25 * P - 4 * first
-    return 2 * run_chunk + reverse
+    return sweep + run_chunk + reverse
 
 
 def bench_backward(args, np, torch, tmm, wl, prefix=1024, steps=3):
