@@ -245,3 +245,77 @@ def test_input_aliasing(lib, a, b_, shift):
 def test_input_empty_sequences(lib):
     desc = tmm.make_input_desc(3, 0, 256, 4, 64, 4)
     assert InputBuffers(desc).call(desc) == tmm.OK
+
+
+# ----------------------------------------------------------------------------
+# titans_mem_backward (gradients through the memory)
+# ----------------------------------------------------------------------------
+class BackwardBuffers:
+    """Disjoint fake device ranges for one backward call."""
+
+    def __init__(self, desc, chunk):
+        esz = 2 if desc.io_dtype == tmm.IO_BF16 else 4
+        S = desc.B * desc.H
+        P = tmm.param_count(desc)
+        tok, gates, state = S * desc.N * desc.d, S * desc.N * 4, S * P * 4
+        self.ws_bytes = tmm.backward_workspace_bytes(desc, chunk)
+        sizes = dict(k=tok * esz, v=tok * esz, q=tok * esz, alpha=gates, eta=gates, theta=gates, W_in=state,
+                     S_in=state, dy=tok * 4, dW_out=state, dS_out=state, dk=tok * 4, dv=tok * 4, dq=tok * 4,
+                     dalpha=gates, deta=gates, dtheta=gates, dW_in=state, dS_in=state, ws=max(self.ws_bytes, 16))
+        self.ptr = {}
+        cur = BASE
+        for name, n in sizes.items():
+            self.ptr[name] = cur
+            cur += (n + 4095) // 4096 * 4096 + 4096
+
+    def call(self, desc, chunk, **over):
+        p = dict(self.ptr)
+        ws_bytes = over.pop("ws_bytes", self.ws_bytes)
+        p.update(over)
+        names = ("k", "v", "q", "alpha", "eta", "theta", "W_in", "S_in")
+        outs = ("dy", "dW_out", "dS_out", "dk", "dv", "dq", "dalpha", "deta", "dtheta", "dW_in", "dS_in")
+        return tmm.raw_backward(desc, *[p[n] for n in names], chunk, *[p[n] for n in outs], p["ws"], ws_bytes, 0)
+
+
+@pytest.fixture
+def bsetup(lib):
+    desc = tmm.make_desc(2, 3, 50, 16, 32, 2, "f32")
+    return desc, BackwardBuffers(desc, 8)
+
+
+def test_backward_workspace_query(lib):
+    d = tmm.make_desc(2, 3, 50, 16, 32, 2, "f32")
+    P = tmm.param_count(d)
+    nb = tmm.backward_workspace_bytes(d, 8)
+    assert nb >= 2 * 3 * (7 * 2 * P + 2 * 8 * P + 3 * P) * 4      # checkpoints, one chunk's states, adjoints
+    assert tmm.backward_workspace_bytes(d, 0) == tmm.ERR_INVALID
+    assert tmm.backward_workspace_bytes(tmm.make_desc(1, 1, 8, 6, 10, 2, "f32"), 4) == tmm.ERR_UNSUPPORTED
+    assert tmm.backward_workspace_bytes(tmm.make_desc(1, 1, 8, 16, 2048, 2, "f32"), 4) == tmm.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["k", "v", "q", "alpha", "eta", "theta", "W_in", "S_in", "dk", "dv", "dq",
+                                  "dalpha", "deta", "dtheta", "dW_in", "dS_in"])
+def test_backward_required_pointers(bsetup, name):
+    desc, b = bsetup
+    assert b.call(desc, 8, **{name: 0}) == tmm.ERR_INVALID
+    assert b.call(desc, 8, **{name: b.ptr[name] + 4}) == tmm.ERR_INVALID
+
+
+@pytest.mark.parametrize("name", ["dy", "dW_out", "dS_out"])
+def test_backward_optional_adjoints_must_be_aligned(bsetup, name):
+    desc, b = bsetup
+    assert b.call(desc, 8, **{name: b.ptr[name] + 8}) == tmm.ERR_INVALID
+
+
+def test_backward_workspace_and_chunk(bsetup):
+    desc, b = bsetup
+    assert b.call(desc, 8, ws_bytes=b.ws_bytes - 16) == tmm.ERR_WORKSPACE
+    assert b.call(desc, 8, ws=0, ws_bytes=0) == tmm.ERR_WORKSPACE
+    assert b.call(desc, 0) == tmm.ERR_INVALID
+
+
+@pytest.mark.parametrize("a,b_,shift", [("dk", "k", 0), ("dW_in", "W_in", 0), ("dS_in", "dW_in", 16),
+                                        ("dalpha", "deta", 0), ("ws", "dq", 64), ("dq", "dy", 32)])
+def test_backward_aliasing(bsetup, a, b_, shift):
+    desc, b = bsetup
+    assert b.call(desc, 8, **{a: b.ptr[b_] + shift}) == tmm.ERR_ALIAS
