@@ -175,10 +175,10 @@ struct Tile {   // one 32x32 fp32 accumulator tile of the state
   float r[16];
 };
 
-__device__ __forceinline__ h8 state_frag(const Tile& t, int s, int e) {
+__device__ __forceinline__ h8 state_frag(const Tile& t, int s, float fe) {
   h8 r;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (_Float16)ldexpf(ag_get(t.r[8 * s + i]), e);
+  for (int i = 0; i < 8; ++i) r[i] = (_Float16)(ag_get(t.r[8 * s + i]) * fe);
   return r;
 }
 
@@ -250,6 +250,12 @@ __device__ __forceinline__ int scale_exp(float amax) {
 // flushes towards zero (scaled values far below any tolerance floor).  k is
 // clamped below so that the factor stays finite.
 __device__ __forceinline__ float pow2neg(int k) { return ldexpf(1.f, -max(k, -126)); }
+// 2^e as a float multiplier for the scalings up to fp16 operands (one
+// multiply per element instead of an ldexp; computed once per block).  Equal
+// to ldexpf(x, e) whenever e <= 127, i.e. unless the block's amax is below
+// 2^-113, where the clamped scale leaves the operand smaller than [2^13, 2^14)
+// but still far below every tolerance floor.
+__device__ __forceinline__ float pow2pos(int e) { return ldexpf(1.f, min(e, 127)); }
 
 // per-token factors of the retrieval operands: (A_j, F_j) scaled by a
 // common power of two 2^s so that the larger lies in (0.5, 1] (fp16 keeps
@@ -590,6 +596,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       const int e1 = scale_exp(wave_max(m1));
       const int e2 = scale_exp(fmaxf(fmaxf(__int_as_float(ci[INT_M2]), __int_as_float(ci[INT_M2 + 1])),
                                      fmaxf(__int_as_float(ci[INT_M2 + 2]), __int_as_float(ci[INT_M2 + 3]))));
+      const float f1 = pow2pos(e1), f2 = pow2pos(e2);
 
       // ================= a2: key-side forward Z1 = K W1^T (rows j, cols h) =================
       // A1 = SiLU(Z1) (scaled fp16: kept for the update, copied to LDS for the
@@ -601,11 +608,12 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
         f16v Z[2];
         float am = 0.f;
         f16v zacc[2] = {{}, {}};
+        const float zun = pow2neg(e1);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
-            w1f[ct][st] = state_frag(W1m[ct], st, e1);
+            w1f[ct][st] = state_frag(W1m[ct], st, f1);
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt)
               zacc[jt] = mfma(lds_frag(sK + (32 * jt + lr) * RS, 32 * ct + 16 * st, lg), w1f[ct][st], zacc[jt]);
@@ -615,7 +623,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
           const f16v acc = zacc[jt];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float z = ldexpf(acc[r], -e1);
+            const float z = acc[r] * zun;
             const float sg = sigmoidf_(z);
             const float a = z * sg;
             Z[jt][r] = a;
@@ -635,7 +643,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
-            w2f[ct][st] = state_frag(W2m[ct], st, e2);
+            w2f[ct][st] = state_frag(W2m[ct], st, f2);
             _Float16* row = sRW2 + (32 * ct + lr) * RSA + 16 * st + 4 * lg;
             *(h4*)row = h4{w2f[ct][st][0], w2f[ct][st][1], w2f[ct][st][2], w2f[ct][st][3]};
             *(h4*)(row + 8) = h4{w2f[ct][st][4], w2f[ct][st][5], w2f[ct][st][6], w2f[ct][st][7]};
@@ -649,11 +657,12 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
         // A1 with the workgroup-wide scale, kept for the update and copied to LDS
         eA1 = scale_exp(fmaxf(fmaxf(__int_as_float(ci[INT_MA1]), __int_as_float(ci[INT_MA1 + 1])),
                               fmaxf(__int_as_float(ci[INT_MA1 + 2]), __int_as_float(ci[INT_MA1 + 3]))));
+        const float fA1 = pow2pos(eA1);
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const _Float16 hv = (_Float16)ldexpf(Z[jt][r], eA1);
+            const _Float16 hv = (_Float16)(Z[jt][r] * fA1);
             A1h[jt][r >> 3][r & 7] = hv;
             sRA[(32 * jt + crow(r, lg)) * RSA + lr] = hv;   // A1 copy [j][h_l]
           }
@@ -854,19 +863,21 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       }
       __syncthreads();   // every wave's SC1 and Delta2 amax is in
       const int eSC = scale_exp(__uint_as_float((unsigned)ci[INT_AMAX_SC1]));
+      const float fSC = pow2pos(eSC);
       if constexpr (kRW) {
         const int jt = w >> 1, it = w & 1;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          sSC1[(32 * jt + crow(r, lg)) * RS + 32 * it + lr] = (_Float16)ldexpf(sc[r], eSC);
+          sSC1[(32 * jt + crow(r, lg)) * RS + 32 * it + lr] = (_Float16)(sc[r] * fSC);
       }
       const int eD2 = scale_exp(__uint_as_float((unsigned)ci[INT_AMAX_D2]));
+      const float fD2 = pow2pos(eD2);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         h4 hv;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          hv[q] = (_Float16)ldexpf(d2v[4 * g + q], eD2);
+          hv[q] = (_Float16)(d2v[4 * g + q] * fD2);
           sD2T[(tc + 8 * g + q) * RS + tj] = hv[q];
         }
         *(h4*)(sD2 + tj * RS + tc + 8 * g) = hv;
@@ -879,6 +890,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
       {
         f16v Df[2];
         float am = 0.f;
+        const float dun = pow2neg(eD2 + e2);
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
           f16v acc = {};
@@ -890,16 +902,17 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
                          lds_frag(sRW + lr * RS, 32 * ct + 16 * st, lg), acc);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float x = ldexpf(acc[r], -(eD2 + e2)) * (float)SPh[jt][r >> 3][r & 7];
+            const float x = acc[r] * dun * (float)SPh[jt][r >> 3][r & 7];
             Df[jt][r] = x;
             am = fmaxf(am, fabsf(x));
           }
         }
         eD1 = scale_exp(wave_max(am));
+        const float fD1 = pow2pos(eD1);
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) D1h[jt][r >> 3][r & 7] = (_Float16)ldexpf(Df[jt][r], eD1);
+          for (int r = 0; r < 16; ++r) D1h[jt][r >> 3][r & 7] = (_Float16)(Df[jt][r] * fD1);
       }
 
       // ================= a5 layer 1: Zq1^T = W1 (A q)^T + S1 (F q)^T - Delta1^T SC1^T (rows h, cols j) =================
@@ -919,7 +932,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
-            const h8 wf = w1f[ct][st], sf = state_frag(S1m[ct], st, e1);
+            const h8 wf = w1f[ct][st], sf = state_frag(S1m[ct], st, f1);
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt) {
               const h8 qf = lds_frag(sQ + (32 * jt + lr) * RS, 32 * ct + 16 * st, lg);
@@ -946,8 +959,9 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
             am = fmaxf(am, fabsf(Hf[r]));
           }
           eH1[jt] = scale_exp(wave_max(am));
+          const float fH = pow2pos(eH1[jt]);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) H1h[jt][r >> 3][r & 7] = (_Float16)ldexpf(Hf[r], eH1[jt]);
+          for (int r = 0; r < 16; ++r) H1h[jt][r >> 3][r & 7] = (_Float16)(Hf[r] * fH);
         }
       }
       else {
@@ -974,14 +988,17 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
             am = fmaxf(am, fabsf(Hf[r]));
           }
           eH1[jt] = scale_exp(wave_max(am));
+          const float fH = pow2pos(eH1[jt]);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) H1h[jt][r >> 3][r & 7] = (_Float16)ldexpf(Hf[r], eH1[jt]);
+          for (int r = 0; r < 16; ++r) H1h[jt][r >> 3][r & 7] = (_Float16)(Hf[r] * fH);
         }
       }
 
       const float An = cf[COEF_A + n - 1], En = cf[COEF_E + n - 1], Fn = cf[COEF_F + n - 1];
       const int ewU = ci[INT_EWU], ewD = ci[INT_EWD];
       float m1n = 0.f, m2n = 0.f;
+      const float uD1 = pow2neg(ewD + eD1), uU1 = pow2neg(ewU + eD1);
+      const float uD2 = pow2neg(ewD + eA1 + eD2), uU2 = pow2neg(ewU + eA1 + eD2);
       // ================= a4, layer 1 (W1, S1 are not read again this chunk) =================
       // G1^T[c][h] = sum_j K[j][c] w_j Delta1[j][h]
 #pragma unroll
@@ -998,8 +1015,8 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float w0 = ag_get(W1m[ct].r[r]), s0 = ag_get(S1m[ct].r[r]);
-          const float wn = An * w0 + Fn * s0 - ldexpf(gD[r], -(ewD + eD1));
-          const float sn = En * s0 - ldexpf(gU[r], -(ewU + eD1));
+          const float wn = An * w0 + Fn * s0 - gD[r] * uD1;
+          const float sn = En * s0 - gU[r] * uU1;
           W1m[ct].r[r] = ag_put(wn);
           S1m[ct].r[r] = ag_put(sn);
           m1n = fmaxf(m1n, fmaxf(fabsf(wn), fabsf(sn)));
@@ -1034,11 +1051,12 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
           }
         }
         const int er = scale_exp(wave_max(am));
+        const float fr = pow2pos(er);
         eDP[jt] = er + eA1 + eH1[jt];   // the scale of the true scores
 #pragma unroll
         for (int it = 0; it < 2; ++it)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) DPh[it][jt][r >> 3][r & 7] = (_Float16)ldexpf(Pf[it][r], er);
+          for (int r = 0; r < 16; ++r) DPh[it][jt][r >> 3][r & 7] = (_Float16)(Pf[it][r] * fr);
       }
 
       // ================= a5 layer 2: y^T partial = W2 (A H1)^T + S2 (F H1)^T - Delta2^T (D o P)^T =================
@@ -1057,7 +1075,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
           f16v accY[2] = {};
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
-            const h8 wf = state_frag(W2m[ct], st, e2), sf = state_frag(S2m[ct], st, e2);
+            const h8 wf = state_frag(W2m[ct], st, f2), sf = state_frag(S2m[ct], st, f2);
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt) {
               accY[jt] = mfma(wf, hscale(H1h[jt][st], ajh[jt]), accY[jt]);
@@ -1093,7 +1111,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
           f16v accY[2] = {};
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
-            const h8 wf = state_frag(W2m[ct], st, e2);
+            const h8 wf = state_frag(W2m[ct], st, f2);
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt) accY[jt] = mfma(wf, H1h[jt][st], accY[jt]);
           }
@@ -1126,8 +1144,8 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_pair_kernel(Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float w0 = ag_get(W2m[ct].r[r]), s0 = ag_get(S2m[ct].r[r]);
-          const float wn = An * w0 + Fn * s0 - ldexpf(gD[r], -(ewD + eA1 + eD2));
-          const float sn = En * s0 - ldexpf(gU[r], -(ewU + eA1 + eD2));
+          const float wn = An * w0 + Fn * s0 - gD[r] * uD2;
+          const float sn = En * s0 - gU[r] * uU2;
           W2m[ct].r[r] = ag_put(wn);
           S2m[ct].r[r] = ag_put(sn);
           m2n = fmaxf(m2n, fmaxf(fabsf(wn), fabsf(sn)));
