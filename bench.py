@@ -23,6 +23,7 @@ if ROOT not in sys.path:
 # MI355X published peaks (dense matrix cores; fp32 matrix = fp32 vector peak)
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
+WORKLOAD_NAMES = ("linear", "mlp2_short", "headline", "long", "deep")
 
 
 # dominant kernel of each path: (kernel function, its source under csrc/)
@@ -163,7 +164,7 @@ def backward_flops_per_token(cfg):
 def bench_backward(args, np, torch, tmm, wl, prefix=1024, steps=3):
     """Gradients through the memory (titans_mem_backward) on the headline
     memory shape, every stream, the first `prefix` tokens."""
-    cfg = wl.CONFIGS[args.config].with_(N=prefix)
+    cfg = wl.WORKLOADS[args.workload].with_(N=prefix)
     inp = wl.make_inputs(cfg, workers=min(16, len(os.sched_getaffinity(0))))
     B, H, N, d, P = cfg.B, cfg.H, cfg.N, cfg.d, cfg.param_count
     if cfg.io == "bf16":
@@ -219,7 +220,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", type=int, default=3, help="workload index (1-5)")
+    ap.add_argument("--workload", default="headline", choices=sorted(WORKLOAD_NAMES),
+                    help="memory workload (default: the 2-layer d=64 h=256 memory over 128 streams x 16384 tokens)")
     ap.add_argument("--force-generic", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -267,7 +269,7 @@ def main():
                           "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
                           "data": "synthetic", **bench_input_side(args, np, torch, tmm, wl)}), flush=True)
         return
-    cfg = wl.CONFIGS[args.config]
+    cfg = wl.WORKLOADS[args.workload]
     t0 = time.time()
     inp = wl.make_inputs(cfg, workers=min(16, len(os.sched_getaffinity(0))))
     print(f"[bench] generated {cfg.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)

@@ -81,20 +81,20 @@ class MemoryConfig:
 
 # The five workloads.  Index 1 is the small linear case, 3 the headline
 # throughput case, 4 the million-token streaming case, 5 the deep memory.
-CONFIGS: Dict[int, MemoryConfig] = {
-    1: MemoryConfig("linear_d64_b1h1_n1024_c16_f32", 1001, B=1, H=1, N=1024, d=64,
+WORKLOADS: Dict[str, MemoryConfig] = {
+    "linear": MemoryConfig("linear_d64_b1h1_n1024_c16_f32", 1001, B=1, H=1, N=1024, d=64,
                     hidden=0, n_layers=1, chunk=16, io="f32", gate_law="uniform",
                     alpha_range=(0.0, 0.1), eta_range=(0.8, 1.0),
                     theta_range=(0.0, 0.1), w0="zero"),
-    2: MemoryConfig("mlp2_d64_h256_b4h8_n4096_c64_bf16", 1002, B=4, H=8, N=4096, d=64,
+    "mlp2_short": MemoryConfig("mlp2_d64_h256_b4h8_n4096_c64_bf16", 1002, B=4, H=8, N=4096, d=64,
                     hidden=256, n_layers=2, chunk=64, io="bf16", gate_law="uniform"),
-    3: MemoryConfig("mlp2_d64_h256_b8h16_n16384_c64_bf16", 1003, B=8, H=16, N=16384,
+    "headline": MemoryConfig("mlp2_d64_h256_b8h16_n16384_c64_bf16", 1003, B=8, H=16, N=16384,
                     d=64, hidden=256, n_layers=2, chunk=64, io="bf16",
                     gate_law="sigmoid"),
-    4: MemoryConfig("mlp2_d64_h256_b1h16_n1048576_c64_bf16", 1004, B=1, H=16,
+    "long": MemoryConfig("mlp2_d64_h256_b1h16_n1048576_c64_bf16", 1004, B=1, H=16,
                     N=1048576, d=64, hidden=256, n_layers=2, chunk=64, io="bf16",
                     gate_law="uniform"),
-    5: MemoryConfig("mlp4_d128_h512_b4h8_n32768_c128_bf16", 1005, B=4, H=8, N=32768,
+    "deep": MemoryConfig("mlp4_d128_h512_b4h8_n32768_c128_bf16", 1005, B=4, H=8, N=32768,
                     d=128, hidden=512, n_layers=4, chunk=128, io="bf16",
                     gate_law="uniform"),
 }

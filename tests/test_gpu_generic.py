@@ -38,15 +38,15 @@ def _check(cfg, inp, out, ref, tol, idx=None, windows=True):
 
 
 def test_generic_linear_config1_full():
-    cfg = wl.CONFIGS[1]
+    cfg = wl.WORKLOADS["linear"]
     inp = wl.make_inputs(cfg)
     out = run_gpu(cfg, to_device(cfg, inp), force_generic=True)
     _check(cfg, inp, out, run_oracle(cfg, inp), TOL["f32"])
 
 
-@pytest.mark.parametrize("cfg_i,n_tokens,BH", [(2, 640, (2, 3)), (3, 300, (1, 5)), (5, 300, (1, 3))])
-def test_generic_mlp_prefix(cfg_i, n_tokens, BH):
-    cfg = wl.CONFIGS[cfg_i].with_(B=BH[0], H=BH[1], N=n_tokens)
+@pytest.mark.parametrize("wname,n_tokens,BH", [("mlp2_short", 640, (2, 3)), ("headline", 300, (1, 5)), ("deep", 300, (1, 3))])
+def test_generic_mlp_prefix(wname, n_tokens, BH):
+    cfg = wl.WORKLOADS[wname].with_(B=BH[0], H=BH[1], N=n_tokens)
     inp = wl.make_inputs(cfg)
     out = run_gpu(cfg, to_device(cfg, inp), force_generic=True)
     _check(cfg, inp, out, run_oracle(cfg, inp), TOL["f32"])
@@ -56,7 +56,7 @@ def test_generic_mlp_prefix(cfg_i, n_tokens, BH):
                                               (3, 24, 40, 97, 16, "bf16"), (2, 32, 96, 65, 1, "bf16"),
                                               (2, 64, 256, 50, 64, "bf16"), (4, 8, 20, 33, 200, "f32")])
 def test_generic_shapes_and_ragged_chunks(L, d, h, N, chunk, io):
-    cfg = wl.CONFIGS[2].with_(B=1, H=2, N=N, d=d, hidden=h, n_layers=L, chunk=chunk, io=io)
+    cfg = wl.WORKLOADS["mlp2_short"].with_(B=1, H=2, N=N, d=d, hidden=h, n_layers=L, chunk=chunk, io=io)
     inp = wl.make_inputs(cfg)
     out = run_gpu(cfg, to_device(cfg, inp), force_generic=True)
     _check(cfg, inp, out, run_oracle(cfg, inp), TOL["f32"], windows=False)
@@ -71,7 +71,7 @@ def test_deep_memory_full_length():
     fixed point, so the final W and S must be below the error floor."""
     import torch
     from test_learned_neural_amd import titans_mem as tmm
-    cfg = wl.CONFIGS[5]
+    cfg = wl.WORKLOADS["deep"]
     desc = tmm.make_desc(cfg.B, cfg.H, cfg.N, cfg.d, cfg.hidden, cfg.n_layers, cfg.io)
     assert tmm.select_path(desc, cfg.chunk) == tmm.PATH_GENERIC_F32
     inp = wl.make_inputs(cfg, workers=16)
@@ -95,14 +95,14 @@ def test_deep_memory_full_length():
 
 def test_generic_deep_memory_prefix_all_streams():
     """Deep memory, 2048-token prefix, all 32 streams, y, W and S."""
-    cfg = wl.CONFIGS[5].with_(N=2048)
+    cfg = wl.WORKLOADS["deep"].with_(N=2048)
     inp = wl.make_inputs(cfg, workers=16)
     out = run_gpu(cfg, to_device(cfg, inp))
     _check(cfg, inp, out, run_oracle(cfg, inp, threads=16), TOL["f32"])
 
 
 def test_generic_read_chunk_start():
-    cfg = wl.CONFIGS[2].with_(B=1, H=3, N=200)
+    cfg = wl.WORKLOADS["mlp2_short"].with_(B=1, H=3, N=200)
     inp = wl.make_inputs(cfg)
     out = run_gpu(cfg, to_device(cfg, inp), force_generic=True, read_mode=1)
     _check(cfg, inp, out, run_oracle(cfg, inp, read_mode=1), TOL["f32"])
@@ -113,7 +113,7 @@ def test_retrieve_matches_memory_forward():
     from test_learned_neural_amd import titans_mem as tmm
     import torch
     for L, d, h in ((1, 64, 0), (2, 64, 256), (4, 128, 512), (3, 20, 36)):
-        cfg = wl.CONFIGS[2].with_(B=2, H=2, N=37, d=d, hidden=h, n_layers=L, io="bf16")
+        cfg = wl.WORKLOADS["mlp2_short"].with_(B=2, H=2, N=37, d=d, hidden=h, n_layers=L, io="bf16")
         inp = wl.make_inputs(cfg)
         dev = to_device(cfg, inp)
         W = dev["W0"] * 3.0
@@ -129,12 +129,12 @@ def test_retrieve_matches_memory_forward():
 
 def test_generic_empty_inplace_and_deterministic():
     import torch
-    cfg = wl.CONFIGS[2].with_(B=1, H=2, N=0)
+    cfg = wl.WORKLOADS["mlp2_short"].with_(B=1, H=2, N=0)
     inp = wl.make_inputs(cfg)
     dev = to_device(cfg, inp)
     y, W, S = run_gpu(cfg, dev, force_generic=True)
     assert torch.equal(W, dev["W0"]) and torch.equal(S, dev["S0"])
-    cfg = wl.CONFIGS[2].with_(B=1, H=2, N=150)
+    cfg = wl.WORKLOADS["mlp2_short"].with_(B=1, H=2, N=150)
     inp = wl.make_inputs(cfg)
     dev = to_device(cfg, inp)
     y1, W1, S1 = run_gpu(cfg, dev, force_generic=True)
@@ -148,7 +148,7 @@ def test_generic_empty_inplace_and_deterministic():
 
 def test_generic_split_resume():
     import torch
-    cfg = wl.CONFIGS[2].with_(B=1, H=2, N=256)
+    cfg = wl.WORKLOADS["mlp2_short"].with_(B=1, H=2, N=256)
     inp = wl.make_inputs(cfg)
     dev = to_device(cfg, inp)
     y, W, S = run_gpu(cfg, dev, force_generic=True)
@@ -166,7 +166,7 @@ def test_generic_split_resume():
 
 def test_generic_gate_edge_cases():
     import torch
-    cfg = wl.CONFIGS[2].with_(B=1, H=2, N=130)
+    cfg = wl.WORKLOADS["mlp2_short"].with_(B=1, H=2, N=130)
     inp = wl.make_inputs(cfg)
     dev = to_device(cfg, inp)
     # theta = 0: surprise stays zero, W decays by the product of (1 - alpha)
@@ -184,12 +184,12 @@ def test_generic_gate_edge_cases():
     assert rel < 1e-6, rel
 
 
-@pytest.mark.parametrize("cfg_i,n_tokens,BH,chunk,read_mode", [(1, 1000, (1, 4), 16, 0), (3, 300, (1, 5), 64, 0),
-                                                              (5, 250, (1, 2), 128, 1), (2, 97, (2, 3), 13, 0)])
-def test_generic_chunk_gates(cfg_i, n_tokens, BH, chunk, read_mode):
+@pytest.mark.parametrize("wname,n_tokens,BH,chunk,read_mode", [("linear", 1000, (1, 4), 16, 0), ("headline", 300, (1, 5), 64, 0),
+                                                              ("deep", 250, (1, 2), 128, 1), ("mlp2_short", 97, (2, 3), 13, 0)])
+def test_generic_chunk_gates(wname, n_tokens, BH, chunk, read_mode):
     """One alpha, eta, theta per chunk on the generic path, ragged tails
     included, against the oracle fed the same per-chunk gates."""
-    cfg = wl.CONFIGS[cfg_i].with_(B=BH[0], H=BH[1], N=n_tokens, chunk=chunk)
+    cfg = wl.WORKLOADS[wname].with_(B=BH[0], H=BH[1], N=n_tokens, chunk=chunk)
     inp = chunk_gate_inputs(wl.make_inputs(cfg), chunk)
     out = run_gpu(cfg, to_device(cfg, inp), force_generic=True, read_mode=read_mode, chunk_gates=True)
     _check(cfg, inp, out, run_oracle(cfg, inp, read_mode=read_mode, chunk_gates=True), TOL["f32"])

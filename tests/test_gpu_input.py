@@ -153,7 +153,7 @@ def test_input_feeds_the_memory():
     cfg = wl.INPUT_CONFIGS["small"].with_(B=2, N=256)
     inp = wl.make_input_side(cfg)
     k, v, q, a, e, t = _run_gpu_dev(cfg, inp)
-    mcfg = wl.CONFIGS[2].with_(B=cfg.B, H=cfg.H, N=cfg.N)
+    mcfg = wl.WORKLOADS["mlp2_short"].with_(B=cfg.B, H=cfg.H, N=cfg.N)
     W0n = wl.make_inputs(mcfg)["W0"].astype(np.float64)
     W0 = torch.from_numpy(W0n.astype(np.float32)).reshape(cfg.B, cfg.H, -1).cuda()
     y, W, S = tmm.forward(k, v, q, a, e, t, W0, torch.zeros_like(W0), 64, hidden=256, n_layers=2)

@@ -48,9 +48,9 @@ def _check(cfg, inp, out, ref, idx=None, tol=None, label=""):
     return e
 
 
-@pytest.mark.parametrize("cfg_i,n_tokens", [(2, 1024), (3, 2048), (4, 2048)])
-def test_mlp2_prefix_all_streams(cfg_i, n_tokens):
-    cfg = wl.CONFIGS[cfg_i].with_(N=n_tokens)
+@pytest.mark.parametrize("wname,n_tokens", [("mlp2_short", 1024), ("headline", 2048), ("long", 2048)])
+def test_mlp2_prefix_all_streams(wname, n_tokens):
+    cfg = wl.WORKLOADS[wname].with_(N=n_tokens)
     inp = wl.make_inputs(cfg, workers=8)
     out = run_gpu(cfg, to_device(cfg, inp))
     _check(cfg, inp, out, run_oracle(cfg, inp))
@@ -59,7 +59,7 @@ def test_mlp2_prefix_all_streams(cfg_i, n_tokens):
 @pytest.mark.parametrize("B,H,N,chunk", [(1, 1, 200, 64), (1, 3, 130, 64), (2, 5, 77, 16), (1, 2, 96, 1),
                                          (1, 4, 150, 40), (3, 3, 64, 64), (1, 1, 33, 64)])
 def test_mlp2_ragged_and_small_chunks(B, H, N, chunk):
-    cfg = wl.CONFIGS[2].with_(B=B, H=H, N=N, chunk=chunk)
+    cfg = wl.WORKLOADS["mlp2_short"].with_(B=B, H=H, N=N, chunk=chunk)
     inp = wl.make_inputs(cfg)
     out = run_gpu(cfg, to_device(cfg, inp))
     _check(cfg, inp, out, run_oracle(cfg, inp))
@@ -67,7 +67,7 @@ def test_mlp2_ragged_and_small_chunks(B, H, N, chunk):
 
 def test_mlp2_more_streams_than_resident_pairs():
     # 160 streams > 128 resident pairs: some pairs run two streams back to back
-    cfg = wl.CONFIGS[3].with_(B=10, H=16, N=192)
+    cfg = wl.WORKLOADS["headline"].with_(B=10, H=16, N=192)
     inp = wl.make_inputs(cfg, workers=8)
     out = run_gpu(cfg, to_device(cfg, inp))
     _check(cfg, inp, out, run_oracle(cfg, inp))
@@ -75,7 +75,7 @@ def test_mlp2_more_streams_than_resident_pairs():
 
 def test_mlp2_matches_generic_kernel():
     import torch
-    cfg = wl.CONFIGS[3].with_(B=2, H=8, N=512)
+    cfg = wl.WORKLOADS["headline"].with_(B=2, H=8, N=512)
     inp = wl.make_inputs(cfg)
     dev = to_device(cfg, inp)
     fast = _np(cfg, run_gpu(cfg, dev))
@@ -91,7 +91,7 @@ def test_mlp2_full_length_headline_all_streams():
     size, in the launch configuration the benchmark times, every stream
     against the oracle (y, W, S; the state has decayed below the floor by the
     end, so y windows and the prefix test carry the non-vacuous part)."""
-    cfg = wl.CONFIGS[3]
+    cfg = wl.WORKLOADS["headline"]
     inp = wl.make_inputs(cfg, workers=16)
     out = run_gpu(cfg, to_device(cfg, inp))
     _check(cfg, inp, out, run_oracle(cfg, inp, threads=16))
@@ -99,7 +99,7 @@ def test_mlp2_full_length_headline_all_streams():
 
 def test_mlp2_full_length_32_streams():
     """The 4 x 8-stream, 4096-token workload at full size against the oracle."""
-    cfg = wl.CONFIGS[2]
+    cfg = wl.WORKLOADS["mlp2_short"]
     inp = wl.make_inputs(cfg, workers=16)
     out = run_gpu(cfg, to_device(cfg, inp))
     _check(cfg, inp, out, run_oracle(cfg, inp, threads=16))
@@ -114,7 +114,7 @@ def test_mlp2_million_token_streams_full_length():
     the bias-free MLP (pinned on the oracle), so the final W and S must be
     below the error floor; every output must be finite."""
     import torch
-    cfg = wl.CONFIGS[4]
+    cfg = wl.WORKLOADS["long"]
     inp = wl.make_inputs(cfg, workers=16)
     dev = to_device(cfg, inp)
     y, W, S = run_gpu(cfg, dev)
@@ -137,12 +137,12 @@ def test_mlp2_million_token_streams_full_length():
 
 def test_mlp2_empty_inplace_deterministic():
     import torch
-    cfg = wl.CONFIGS[2].with_(B=1, H=3, N=0)
+    cfg = wl.WORKLOADS["mlp2_short"].with_(B=1, H=3, N=0)
     inp = wl.make_inputs(cfg)
     dev = to_device(cfg, inp)
     y, W, S = run_gpu(cfg, dev)
     assert torch.equal(W, dev["W0"]) and torch.equal(S, dev["S0"])
-    cfg = wl.CONFIGS[2].with_(B=2, H=4, N=300)
+    cfg = wl.WORKLOADS["mlp2_short"].with_(B=2, H=4, N=300)
     inp = wl.make_inputs(cfg)
     dev = to_device(cfg, inp)
     y1, W1, S1 = run_gpu(cfg, dev)
@@ -156,7 +156,7 @@ def test_mlp2_empty_inplace_deterministic():
 
 def test_mlp2_split_resume():
     import torch
-    cfg = wl.CONFIGS[3].with_(B=1, H=4, N=384)
+    cfg = wl.WORKLOADS["headline"].with_(B=1, H=4, N=384)
     inp = wl.make_inputs(cfg)
     dev = to_device(cfg, inp)
     y, W, S = run_gpu(cfg, dev)
@@ -173,7 +173,7 @@ def test_mlp2_split_resume():
 
 def test_mlp2_gate_edge_cases():
     import torch
-    cfg = wl.CONFIGS[2].with_(B=1, H=2, N=130)
+    cfg = wl.WORKLOADS["mlp2_short"].with_(B=1, H=2, N=130)
     inp = wl.make_inputs(cfg)
     dev = to_device(cfg, inp)
     dz = dev | {"theta": torch.zeros_like(dev["theta"])}
@@ -187,13 +187,13 @@ def test_mlp2_gate_edge_cases():
     assert rel < 1e-5, rel
 
 
-@pytest.mark.parametrize("cfg_i,n_tokens,BH,chunk", [(3, 2048, None, 64), (2, 130, (1, 3), 40), (2, 77, (2, 5), 16)])
-def test_mlp2_chunk_start_read(cfg_i, n_tokens, BH, chunk):
+@pytest.mark.parametrize("wname,n_tokens,BH,chunk", [("headline", 2048, None, 64), ("mlp2_short", 130, (1, 3), 40), ("mlp2_short", 77, (2, 5), 16)])
+def test_mlp2_chunk_start_read(wname, n_tokens, BH, chunk):
     """Retrieval at the chunk-start state (y_j = M_{W_0}(q_j), the read that
     precedes a segment's write) on the MFMA kernel, against the oracle in the
     same read mode; the state update is the same as in the default mode."""
     from test_learned_neural_amd import titans_mem as tmm
-    cfg = wl.CONFIGS[cfg_i].with_(N=n_tokens, chunk=chunk)
+    cfg = wl.WORKLOADS[wname].with_(N=n_tokens, chunk=chunk)
     if BH:
         cfg = cfg.with_(B=BH[0], H=BH[1])
     d = tmm.make_desc(cfg.B, cfg.H, cfg.N, cfg.d, cfg.hidden, cfg.n_layers, cfg.io, read_mode=1)
@@ -205,7 +205,7 @@ def test_mlp2_chunk_start_read(cfg_i, n_tokens, BH, chunk):
 
 def test_mlp2_chunk_start_read_matches_generic():
     import torch
-    cfg = wl.CONFIGS[3].with_(B=2, H=4, N=320)
+    cfg = wl.WORKLOADS["headline"].with_(B=2, H=4, N=320)
     inp = wl.make_inputs(cfg)
     dev = to_device(cfg, inp)
     fast = _np(cfg, run_gpu(cfg, dev, read_mode=1))
@@ -216,9 +216,9 @@ def test_mlp2_chunk_start_read_matches_generic():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("cfg_i,n_tokens,BH,chunk,read_mode", [(3, 2048, None, 64, 0), (2, 150, (1, 4), 40, 0),
-                                                              (2, 77, (2, 5), 16, 1), (2, 1024, (2, 4), 16, 0)])
-def test_mlp2_chunk_gates(cfg_i, n_tokens, BH, chunk, read_mode):
+@pytest.mark.parametrize("wname,n_tokens,BH,chunk,read_mode", [("headline", 2048, None, 64, 0), ("mlp2_short", 150, (1, 4), 40, 0),
+                                                              ("mlp2_short", 77, (2, 5), 16, 1), ("mlp2_short", 1024, (2, 4), 16, 0)])
+def test_mlp2_chunk_gates(wname, n_tokens, BH, chunk, read_mode):
     """One alpha, eta, theta per chunk (the chunk-constant parameterisation
     that makes each chunk a time-invariant system) on the MFMA kernel, ragged
     tails included, against the oracle fed the same per-chunk gates.  Long
@@ -227,7 +227,7 @@ def test_mlp2_chunk_gates(cfg_i, n_tokens, BH, chunk, read_mode):
     times over and some streams diverge (the oracle overflows too), which is
     the method's behaviour under such gates, not a kernel's."""
     from test_learned_neural_amd import titans_mem as tmm
-    cfg = wl.CONFIGS[cfg_i].with_(N=n_tokens, chunk=chunk)
+    cfg = wl.WORKLOADS[wname].with_(N=n_tokens, chunk=chunk)
     if BH:
         cfg = cfg.with_(B=BH[0], H=BH[1])
     d = tmm.make_desc(cfg.B, cfg.H, cfg.N, cfg.d, cfg.hidden, cfg.n_layers, cfg.io, read_mode=read_mode,
@@ -241,7 +241,7 @@ def test_mlp2_chunk_gates(cfg_i, n_tokens, BH, chunk, read_mode):
 
 def test_mlp2_chunk_gates_match_repeated_token_gates():
     """Per-chunk gates give what per-token gates repeated over each chunk give."""
-    cfg = wl.CONFIGS[3].with_(B=2, H=4, N=300)
+    cfg = wl.WORKLOADS["headline"].with_(B=2, H=4, N=300)
     inp = chunk_gate_inputs(wl.make_inputs(cfg), cfg.chunk)
     rep = dict(inp)
     for g in ("alpha", "eta", "theta"):

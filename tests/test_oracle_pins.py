@@ -122,7 +122,7 @@ def test_bf16_rounding_matches_torch():
 
 
 def test_generator_prefix_and_subset_are_consistent():
-    cfg = wl.CONFIGS[2]
+    cfg = wl.WORKLOADS["mlp2_short"]
     full = wl.make_inputs(cfg, streams=[(0, 0), (1, 2), (3, 7)], n_tokens=256)
     sub = wl.make_inputs(cfg, streams=[(1, 2)], n_tokens=100)
     for name in ("k", "v", "q", "alpha", "eta", "theta"):
@@ -134,13 +134,13 @@ def test_generator_prefix_and_subset_are_consistent():
 
 
 def test_generator_laws():
-    c3 = wl.make_inputs(wl.CONFIGS[3], streams=[(0, 0)], n_tokens=4096)
+    c3 = wl.make_inputs(wl.WORKLOADS["headline"], streams=[(0, 0)], n_tokens=4096)
     assert c3["alpha"].max() <= 0.1 and c3["theta"].max() <= 0.1 and c3["alpha"].min() > 0
     assert 0 < c3["eta"].min() and c3["eta"].max() < 1
-    c1 = wl.make_inputs(wl.CONFIGS[1], n_tokens=512)
+    c1 = wl.make_inputs(wl.WORKLOADS["linear"], n_tokens=512)
     assert c1["k"].dtype == np.float32 and not c1["W0"].any()
     assert 0.8 <= c1["eta"].min() and c1["alpha"].max() <= 0.1
-    c2 = wl.make_inputs(wl.CONFIGS[2], streams=[(0, 0)], n_tokens=8)
+    c2 = wl.make_inputs(wl.WORKLOADS["mlp2_short"], streams=[(0, 0)], n_tokens=8)
     bound = np.sqrt(6.0 / (64 + 256))
     assert np.abs(c2["W0"]).max() <= bound and np.abs(c2["W0"]).max() > 0.9 * bound
 
