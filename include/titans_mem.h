@@ -153,7 +153,10 @@ int titans_mem_forward(const titans_mem_desc* desc,
  *   q      [B,H,N,d] io dtype, device
  *   W      [B,H,P]   fp32, device (the state to read)
  *   y_out  [B,H,N,d] io dtype, device, must not overlap q or W
- * Uses desc's shape fields (read_mode and flags are ignored).
+ * Uses desc's shape fields; read_mode is ignored.  The 2-layer d=64
+ * hidden=256 bf16 memory runs on the matrix cores (bf16 operands, fp32 sums);
+ * every other shape, and any call with TM_FLAG_FORCE_GENERIC, on the
+ * shape-generic fp32 kernel (widths up to 1024).
  */
 int titans_mem_retrieve(const titans_mem_desc* desc, const void* q, const float* W,
                         void* y_out, void* stream);

@@ -168,7 +168,8 @@ int titans_mem_retrieve(const titans_mem_desc* desc, const void* q, const float*
   if (s.N > 0 && (!q || !y_out)) return TM_ERR_INVALID;
   if (!W || !aligned16(W) || (q && !aligned16(q)) || (y_out && !aligned16(y_out)))
     return TM_ERR_INVALID;
-  if (s.maxw > titans::kMaxWidthRetrieve) return TM_ERR_UNSUPPORTED;
+  const bool mfma = !(desc->flags & TM_FLAG_FORCE_GENERIC) && titans::retrieve_mlp2_supported(s);
+  if (!mfma && s.maxw > titans::kMaxWidthRetrieve) return TM_ERR_UNSUPPORTED;
   const int64_t esz = s.io == TM_IO_BF16 ? 2 : 4;
   const int64_t tok_bytes = (int64_t)s.streams * s.N * s.d * esz;
   const Range yr = {(const char*)y_out, tok_bytes, true};
@@ -176,7 +177,8 @@ int titans_mem_retrieve(const titans_mem_desc* desc, const void* q, const float*
       overlap(yr, Range{(const char*)W, (int64_t)s.streams * s.P * 4, false}))
     return TM_ERR_ALIAS;
   if (s.N == 0) return TM_OK;
-  hipError_t err = titans::launch_retrieve_generic(s, q, W, y_out, (hipStream_t)stream);
+  hipError_t err = mfma ? titans::launch_retrieve_mlp2(s, q, W, y_out, (hipStream_t)stream)
+                        : titans::launch_retrieve_generic(s, q, W, y_out, (hipStream_t)stream);
   return err == hipSuccess ? TM_OK : TM_ERR_HIP;
 }
 

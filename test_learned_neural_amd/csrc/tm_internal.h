@@ -43,6 +43,10 @@ hipError_t launch_mlp2(const Shape& s, int chunk, const void* k, const void* v, 
                        const float* W_in, const float* S_in, void* y, float* W_out,
                        float* S_out, void* ws, hipStream_t stream);
 
+// Retrieval at a fixed state on the matrix cores (2-layer, d=64, hidden=256, bf16).
+bool retrieve_mlp2_supported(const Shape& s);
+hipError_t launch_retrieve_mlp2(const Shape& s, const void* q, const float* W, void* y, hipStream_t stream);
+
 // The generic kernel as a state sweep only (no retrieval), writing (W, S) at
 // every chunk start to ckpt; W, S and ckpt are strided per stream.
 hipError_t launch_generic_checkpoints(const Shape& s, int chunk, const void* k, const void* v, const void* q,

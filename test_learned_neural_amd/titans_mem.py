@@ -217,12 +217,12 @@ def forward(k, v, q, alpha, eta, theta, W_in, S_in, chunk: int, *, hidden: int, 
     return y_out, W_out, S_out
 
 
-def retrieve(q, W, *, hidden: int, n_layers: int, y_out=None):
+def retrieve(q, W, *, hidden: int, n_layers: int, y_out=None, force_generic: bool = False):
     """y = M*_W(q) at a fixed state.  q: [B,H,N,d]; W: [B,H,P] float32."""
     torch = _torch()
     B, H, N, d = q.shape
     io = "bf16" if q.dtype == torch.bfloat16 else "f32"
-    desc = make_desc(B, H, N, d, hidden, n_layers, io)
+    desc = make_desc(B, H, N, d, hidden, n_layers, io, flags=FLAG_FORCE_GENERIC if force_generic else 0)
     P = param_count(desc)
     if P < 0:
         raise TitansMemError(P, "titans_mem_param_count")
