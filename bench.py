@@ -29,7 +29,8 @@ WORKLOAD_NAMES = ("linear", "mlp2_short", "headline", "long", "deep")
 # dominant kernel of each path: (kernel function, its source under csrc/)
 DOMINANT_KERNEL = {"mlp2_d64_h256_mfma": ("mlp2_pair_kernel", "tm_mlp2.hip"),
                    "generic_f32": ("generic_kernel", "tm_generic.hip"),
-                   "input_side": ("input_kernel", "tm_input.hip")}
+                   "input_side": ("input_kernel", "tm_input.hip"),
+                   "retrieve_mlp2": ("mlp2_retrieve_kernel", "tm_retrieve.hip")}
 
 
 def measured_traffic(kernel_path, workload):
@@ -215,6 +216,62 @@ def bench_backward(args, np, torch, tmm, wl, prefix=1024, steps=3):
     return res
 
 
+def bench_retrieve(args, np, torch, tmm, wl, steps=10):
+    """Retrieval at a fixed state (titans_mem_retrieve): y = M_W(q) for every
+    token of every stream of the workload, W = the workload's initial state."""
+    cfg = wl.WORKLOADS[args.workload]
+    inp = wl.make_inputs(cfg, workers=min(16, len(os.sched_getaffinity(0))))
+    B, H, N, d, P = cfg.B, cfg.H, cfg.N, cfg.d, cfg.param_count
+    if cfg.io == "bf16":
+        q = torch.from_numpy(inp["q"].view(np.int16)).view(torch.bfloat16).reshape(B, H, N, d).cuda()
+    else:
+        q = torch.from_numpy(inp["q"]).reshape(B, H, N, d).cuda()
+    W = torch.from_numpy(inp["W0"]).reshape(B, H, P).cuda()
+    y = tmm.retrieve(q, W, hidden=cfg.hidden, n_layers=cfg.n_layers)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    wall0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        tmm.retrieve(q, W, hidden=cfg.hidden, n_layers=cfg.n_layers, y_out=y)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    launch_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    tokens = B * H * N
+    w = cfg.widths
+    flops = 2.0 * tokens * P                       # one memory forward per token
+    esz = 2 if cfg.io == "bf16" else 4
+    byts = 2.0 * tokens * d * esz + B * H * P * 4  # q in, y out, the state once
+    mfma = tmm.select_path(tmm.make_desc(B, H, N, d, cfg.hidden, cfg.n_layers, cfg.io), cfg.chunk) == \
+        tmm.PATH_MLP2_D64_H256
+    dt = "bf16" if mfma else "f32"
+    achieved = flops / launch_s / 1e12
+    res = {"workload": cfg.name, "value": tokens / (wall / steps), "unit": "memory-tokens/s",
+           "ms_per_step": wall * 1e3 / steps, "dtype": dt, "steps": steps,
+           "roofline": {"bound": "mfma" if mfma else "alu", "achieved": achieved, "peak": PEAK_TFLOPS[dt],
+                        "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS[dt],
+                        "traffic": measured_traffic("retrieve_mlp2", cfg.name) if mfma else None,
+                        "algorithmic_flops_per_launch": flops, "avg_launch_ms": launch_s * 1e3,
+                        "hbm_achieved_gbs": byts / launch_s / 1e9, "hbm_peak_gbs": PEAK_HBM_GBS}}
+    print(f"[bench] retrieve {cfg.name}: {launch_s * 1e3:.3f} ms/launch, {tokens / launch_s:.3g} memory-tokens/s, "
+          f"{achieved:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        import oracle
+        Wn = inp["W0"][0].astype(np.float64)
+        qn = wl.io_to_f64(inp["q"][0], cfg.io)
+        t1 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t1 < 1.0 and n < N:
+            oracle.memory_apply(Wn, qn[n], d, cfg.hidden, cfg.n_layers)
+            n += 1
+        el = time.perf_counter() - t1
+        res["cpu_baseline"] = {"value": n / el, "unit": "memory-tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} tokens of one stream, fp64 C memory forward, {el:.2f} s"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,6 +284,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-input-side", action="store_true", help="skip the input-side leg")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
+    ap.add_argument("--no-retrieve", action="store_true", help="skip the fixed-state retrieval leg")
+    ap.add_argument("--retrieve-only", action="store_true",
+                    help="time only the fixed-state retrieval (titans_mem_retrieve) and print its JSON line")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the backward (gradients through the memory) and print its JSON line")
     ap.add_argument("--input-side-only", action="store_true",
@@ -259,6 +319,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tmm.load()
+    if args.retrieve_only:
+        print(json.dumps({"metric": "retrieval memory tokens/sec at a fixed state, 1 GPU", "n_gpus": 1,
+                          "higher_is_better": True, "data": "synthetic",
+                          **bench_retrieve(args, np, torch, tmm, wl)}), flush=True)
+        return
     if args.backward_only:
         print(json.dumps({"metric": "backward memory tokens/sec (gradients through the memory), 1 GPU", "n_gpus": 1,
                           "higher_is_better": True, "data": "synthetic",
@@ -383,6 +448,8 @@ def main():
     }
     if not args.no_input_side:
         out["input_side"] = bench_input_side(args, np, torch, tmm, wl)
+    if not args.no_retrieve:
+        out["retrieve"] = bench_retrieve(args, np, torch, tmm, wl)
     if not args.no_backward:
         out["backward"] = bench_backward(args, np, torch, tmm, wl)
     print(json.dumps(out), flush=True)
