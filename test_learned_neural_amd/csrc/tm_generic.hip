@@ -33,6 +33,37 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTile = 64;
 
+// Per-stream workspace of the chunked sweep, as float offsets (computed on
+// the host, read from the kernel arguments with scalar loads):
+//   act[l]   a^l of the chunk's keys, [b x n_l] (a^0 = K)
+//   sp[l]    SiLU'(z^l), l = 1..L-1;  delta[l]  delta^l, l = 1..L
+//   vin      V [b x d];  hq[0..1]  query-side activations, ping-pong [b x maxw]
+//   sc, D    masked scores and decay weights [b x b];  A, E, F, U  [b]
+struct WsLayout {
+  int64_t act[kMaxLayers + 1], sp[kMaxLayers + 1], delta[kMaxLayers + 1];
+  int64_t vin, hq[2], sc, D, A, E, F, U;
+  int64_t total;
+};
+
+WsLayout ws_layout(const Shape& s, int b) {
+  WsLayout w{};
+  int64_t cur = 0;
+  for (int l = 0; l <= s.L; ++l) { w.act[l] = cur; cur += (int64_t)b * s.widths[l]; }
+  for (int l = 1; l < s.L; ++l) { w.sp[l] = cur; cur += (int64_t)b * s.widths[l]; }
+  for (int l = 1; l <= s.L; ++l) { w.delta[l] = cur; cur += (int64_t)b * s.widths[l]; }
+  w.vin = cur; cur += (int64_t)b * s.d;
+  w.hq[0] = cur; cur += (int64_t)b * s.maxw;
+  w.hq[1] = cur; cur += (int64_t)b * s.maxw;
+  w.sc = cur; cur += (int64_t)b * b;
+  w.D = cur; cur += (int64_t)b * b;
+  w.A = cur; cur += b;
+  w.E = cur; cur += b;
+  w.F = cur; cur += b;
+  w.U = cur; cur += b;
+  w.total = (cur + 63) / 64 * 64;                                     // keep 256-byte alignment
+  return w;
+}
+
 struct GParams {
   int N, d, L, io, read_mode, chunk;
   int chunk_gates;   // gates hold one value per chunk
@@ -57,6 +88,7 @@ struct GParams {
   int64_t ckpt_stride;    // floats between streams in ckpt
   float* ws;
   int64_t ws_stride;  // floats per stream
+  WsLayout lay;
 };
 
 __device__ __forceinline__ float logistic(float z) { return 1.0f / (1.0f + __expf(-z)); }
@@ -82,93 +114,139 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // C[M x N] = sum_k A(m, k) B(k, n), handed to epi(m, n, value).  The whole
 // workgroup cooperates; operands come through accessors (global/L2 reads)
-// and are staged through LDS in kGk x 64 k-major tiles, the next tile's
-// operands loaded into registers while the current one is multiplied.  Each
-// of the four waves computes one 32 x 32 quarter of a 64 x 64 output tile
-// with the fp32 matrix instruction v_mfma_f32_32x32x2_f32 (lane l supplies
-// A[l%32][l/32] and B[l/32][l%32]; accumulator register r holds row
-// 8(r/4) + 4(l/32) + r%4, column l%32), so the arithmetic stays fp32.
-constexpr int kGk = 32;                                  // k per staged tile
-constexpr int kGPer = kTile * kGk / kThreads;             // operand elements per thread per tile
-template <class FA, class FB, class FE>
-__device__ void block_gemm(int M, int N, int K, FA fa, FB fb, FE epi) {
-  __shared__ float As[kGk][kTile + 1];
-  __shared__ float Bs[kGk][kTile + 1];
+// and are staged through LDS in kGk-deep slices, the next slice's operands
+// loaded into registers while the current one is multiplied.  Output tiles
+// are 64 x 128 when N > 64 (each of the four waves computes a 32 x 64 part
+// as two 32 x 32 blocks), else 64 x 64 (each wave a 32 x 32 quarter with
+// the slice's even and odd k-pairs in two accumulators, summed at the end),
+// so every wave keeps two independent chains of the fp32 matrix instruction
+// v_mfma_f32_32x32x2_f32 (lane l supplies A[l%32][l/32] and B[l/32][l%32];
+// accumulator register r holds row 8(r/4) + 4(l/32) + r%4, column l%32) and
+// the arithmetic stays fp32.  The accessors are read in the order that keeps
+// a wavefront's loads on few cache lines: A_KMAJOR says A(m, k) is
+// contiguous in k (else in m); bkmaj(k0) says whether the B slice starting
+// at k0 is contiguous in k (else in n).
+//
+// So that a wave keeps all of a slice's loads in flight at once, the
+// accessors and the epilogue are called unconditionally, with indices
+// clamped into range (M, N, K >= 1): fa(m, k), fb(k, n) and epi(m, n, value,
+// ok) must be branch-free reads of valid addresses; operands outside the
+// product are zeroed when staged, and epi stores only where ok is set.
+constexpr int kGk = 32;                                   // k per staged slice
+constexpr int kGN = 2 * kTile;                            // output columns per wide tile
+constexpr int kGPerA = kTile * kGk / kThreads;            // A elements per thread per slice
+constexpr int kGPerB = kGN * kGk / kThreads;              // B elements per thread per wide slice
+constexpr int kGemmLdsFloats = kGk * (kTile + 1) + kGk * (kGN + 1);
+
+// one LDS allocation shared by every block_gemm instantiation of a kernel
+__device__ __forceinline__ float* gemm_lds() {
+  __shared__ float buf[kGemmLdsFloats];
+  return buf;
+}
+
+template <bool A_KMAJOR, bool WIDE, class FA, class FB, class FBK, class FE>
+__device__ void block_gemm_tiles(int M, int N, int K, FA fa, FB fb, FBK bkmaj, FE epi) {
+  float* As = gemm_lds();                 // [kGk][kTile + 1]
+  float* Bs = As + kGk * (kTile + 1);     // [kGk][kGN + 1]
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const int wm = (wv >> 1) * 32, wn = (wv & 1) * 32;   // this wave's quarter
+  constexpr bool wide = WIDE;
+  constexpr int tn = wide ? kGN : kTile;                // output columns per tile
+  constexpr int nb = wide ? kGPerB : kGPerB / 2;        // B elements per thread per slice
+  const int wm = (wv >> 1) * 32, wn = (wv & 1) * (wide ? 64 : 32);
   const int li = lane & 31, lk = lane >> 5;
+  auto a_at = [&](int q, int& mm, int& ka) {
+    const int e = tid + q * kThreads;
+    if (A_KMAJOR) { mm = e / kGk; ka = e % kGk; } else { ka = e / kTile; mm = e % kTile; }
+  };
+  auto b_at = [&](bool kmaj, int q, int& kb, int& nn) {
+    const int e = tid + q * kThreads;
+    if (kmaj) { nn = e / kGk; kb = e % kGk; } else { kb = e / tn; nn = e % tn; }
+  };
   for (int m0 = 0; m0 < M; m0 += kTile) {
-    for (int n0 = 0; n0 < N; n0 += kTile) {
-      float ra[kGPer], rb[kGPer];
-      auto fetch = [&](int k0) {
+    for (int n0 = 0; n0 < N; n0 += tn) {
+      float ra[kGPerA], rb[kGPerB];
+      bool bk = bkmaj(0);
+      auto fetch = [&](int k0, bool kmaj) {   // raw values, clamped addresses
 #pragma unroll
-        for (int q = 0; q < kGPer; ++q) {
-          const int e = tid + q * kThreads;
-          const int mm = e / kGk, ka = e % kGk;        // A element (m0 + mm, k0 + ka)
-          ra[q] = (m0 + mm < M && k0 + ka < K) ? fa(m0 + mm, k0 + ka) : 0.f;
-          const int kb = e / kTile, nn = e % kTile;    // B element (k0 + kb, n0 + nn)
-          rb[q] = (n0 + nn < N && k0 + kb < K) ? fb(k0 + kb, n0 + nn) : 0.f;
+        for (int q = 0; q < kGPerA; ++q) {
+          int mm, ka;
+          a_at(q, mm, ka);
+          ra[q] = fa(min(m0 + mm, M - 1), min(k0 + ka, K - 1));
+        }
+#pragma unroll
+        for (int q = 0; q < nb; ++q) {
+          int kb, nn;
+          b_at(kmaj, q, kb, nn);
+          rb[q] = fb(min(k0 + kb, K - 1), min(n0 + nn, N - 1));
         }
       };
-      fetch(0);
-      f32x16 acc = {};
+      fetch(0, bk);
+      f32x16 acc0 = {}, acc1 = {};
       for (int k0 = 0; k0 < K; k0 += kGk) {
 #pragma unroll
-        for (int q = 0; q < kGPer; ++q) {
-          const int e = tid + q * kThreads;
-          As[e % kGk][e / kGk] = ra[q];
-          Bs[e / kTile][e % kTile] = rb[q];
+        for (int q = 0; q < kGPerA; ++q) {
+          int mm, ka;
+          a_at(q, mm, ka);
+          As[ka * (kTile + 1) + mm] = (m0 + mm < M && k0 + ka < K) ? ra[q] : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < nb; ++q) {
+          int kb, nn;
+          b_at(bk, q, kb, nn);
+          Bs[kb * (kGN + 1) + nn] = (n0 + nn < N && k0 + kb < K) ? rb[q] : 0.f;
         }
         __syncthreads();
-        if (k0 + kGk < K) fetch(k0 + kGk);   // in flight during the products below
+        // the next slice's loads are in flight during the products below (past
+        // the last slice they reread the clamped last column: unused)
+        bk = bkmaj(k0 + kGk);
+        fetch(k0 + kGk, bk);
+        if constexpr (wide) {
 #pragma unroll
-        for (int kk = 0; kk < kGk; kk += 2)
-          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[kk + lk][wm + li], Bs[kk + lk][wn + li], acc, 0, 0, 0);
+          for (int kk = 0; kk < kGk; kk += 2) {
+            const float a = As[(kk + lk) * (kTile + 1) + wm + li];
+            const float* br = Bs + (kk + lk) * (kGN + 1) + wn + li;
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, br[0], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, br[32], acc1, 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < kGk; kk += 4) {
+            const float* ar = As + (kk + lk) * (kTile + 1) + wm + li;
+            const float* br = Bs + (kk + lk) * (kGN + 1) + wn + li;
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(ar[0], br[0], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(ar[2 * (kTile + 1)], br[2 * (kGN + 1)], acc1, 0, 0, 0);
+          }
+        }
         __syncthreads();
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + wm + 8 * (r >> 2) + 4 * lk + (r & 3), n = n0 + wn + li;
-        if (m < M && n < N) epi(m, n, acc[r]);
+        const int mc = min(m, M - 1);
+        if constexpr (wide) {
+          epi(mc, min(n, N - 1), acc0[r], m < M && n < N);
+          epi(mc, min(n + 32, N - 1), acc1[r], m < M && n + 32 < N);
+        } else {
+          epi(mc, min(n, N - 1), acc0[r] + acc1[r], m < M && n < N);
+        }
       }
     }
   }
   __syncthreads();
 }
 
-struct Work {
-  float* act[kMaxLayers + 1];    // a^0 = K, a^l [b x n_l]
-  float* sp[kMaxLayers + 1];     // SiLU'(z^l), l = 1..L-1
-  float* delta[kMaxLayers + 1];  // delta^l, l = 1..L
-  float* vin;                    // V [b x d]
-  float* hq[2];                  // query-side activations, ping-pong [b x maxw]
-  float* sc;                     // masked scores [b x b]
-  float* D;                      // [b x b]
-  float* A;
-  float* E;
-  float* F;
-  float* U;
-};
-
-__device__ Work carve(const GParams& p, float* base) {
-  Work w;
-  float* cur = base;
-  const int b = p.b;
-  for (int l = 0; l <= p.L; ++l) { w.act[l] = cur; cur += (int64_t)b * p.widths[l]; }
-  for (int l = 1; l < p.L; ++l) { w.sp[l] = cur; cur += (int64_t)b * p.widths[l]; }
-  for (int l = 1; l <= p.L; ++l) { w.delta[l] = cur; cur += (int64_t)b * p.widths[l]; }
-  w.vin = cur; cur += (int64_t)b * p.d;
-  w.hq[0] = cur; cur += (int64_t)b * p.maxw;
-  w.hq[1] = cur; cur += (int64_t)b * p.maxw;
-  w.sc = cur; cur += (int64_t)b * b;
-  w.D = cur; cur += (int64_t)b * b;
-  w.A = cur; cur += b;
-  w.E = cur; cur += b;
-  w.F = cur; cur += b;
-  w.U = cur; cur += b;
-  return w;
+template <bool A_KMAJOR, class FA, class FB, class FBK, class FE>
+__device__ void block_gemm(int M, int N, int K, FA fa, FB fb, FBK bkmaj, FE epi) {
+  if (N > kTile)
+    block_gemm_tiles<A_KMAJOR, true>(M, N, K, fa, fb, bkmaj, epi);
+  else
+    block_gemm_tiles<A_KMAJOR, false>(M, N, K, fa, fb, bkmaj, epi);
 }
+
+// the B slice's layout when it is the same for every slice
+constexpr auto kB_KMAJOR = [](int) { return true; };
+constexpr auto kB_NMAJOR = [](int) { return false; };
 
 __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
   const int s = blockIdx.x;
@@ -184,7 +262,15 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
     for (int64_t i = tid; i < p.P; i += kThreads) S[i] = Sin[i];
   __syncthreads();
   if (p.N == 0) return;
-  Work w = carve(p, p.ws + (int64_t)s * p.ws_stride);
+  float* const wsb = p.ws + (int64_t)s * p.ws_stride;
+  const WsLayout& lay = p.lay;
+  struct {
+    float *vin, *sc, *D, *A, *E, *F, *U;
+  } w = {wsb + lay.vin, wsb + lay.sc, wsb + lay.D, wsb + lay.A, wsb + lay.E, wsb + lay.F, wsb + lay.U};
+  auto act = [&](int l) { return wsb + lay.act[l]; };
+  auto spv = [&](int l) { return wsb + lay.sp[l]; };
+  auto delta = [&](int l) { return wsb + lay.delta[l]; };
+  auto hq = [&](int i) { return wsb + lay.hq[i]; };
   const int64_t tok0 = (int64_t)s * p.N;
 
   for (int c0 = 0; c0 < p.N; c0 += p.chunk) {
@@ -209,9 +295,9 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
     // ---- load the chunk's keys, values and queries (fp32 copies) ----
     for (int e = tid; e < n * d; e += kThreads) {
       const int64_t gi = (tok0 + c0) * d + e;
-      w.act[0][e] = load_io(p.k, gi, p.io);
+      act(0)[e] = load_io(p.k, gi, p.io);
       w.vin[e] = load_io(p.v, gi, p.io);
-      w.hq[0][(e / d) * p.maxw + (e % d)] = load_io(p.q, gi, p.io);
+      hq(0)[(e / d) * p.maxw + (e % d)] = load_io(p.q, gi, p.io);
     }
     // ---- a1: coefficient recurrences (one thread per column i of D) ----
     for (int i = tid; i < n; i += kThreads) {
@@ -242,20 +328,23 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
     for (int l = 1; l <= L; ++l) {
       const int nin = p.widths[l - 1], nout = p.widths[l];
       const float* Wl = W + p.off[l];
-      const float* ain = w.act[l - 1];
-      float* aout = w.act[l];
-      float* spl = w.sp[l];
-      float* dl = w.delta[l];
+      const float* ain = act(l - 1);
+      float* aout = act(l);
+      float* spl = spv(l);
+      float* dl = delta(l);
       const float* vin = w.vin;
       const bool last = (l == L);
-      block_gemm(
+      block_gemm<true>(
           n, nout, nin, [=](int j, int c) { return ain[j * nin + c]; },
-          [=](int c, int r) { return Wl[(int64_t)r * nin + c]; },
-          [=](int j, int r, float z) {
+          [=](int c, int r) { return Wl[(int64_t)r * nin + c]; }, kB_KMAJOR,
+          [=](int j, int r, float z, bool ok) {
             if (last) {
-              aout[j * nout + r] = z;
-              dl[j * nout + r] = z - vin[j * nout + r];  // a3: residual M(k) - v
-            } else {
+              const float vv = vin[j * nout + r];
+              if (ok) {
+                aout[j * nout + r] = z;
+                dl[j * nout + r] = z - vv;  // a3: residual M(k) - v
+              }
+            } else if (ok) {
               aout[j * nout + r] = silu(z);
               spl[j * nout + r] = silu_prime(z);
             }
@@ -265,13 +354,16 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
     for (int l = L; l >= 2; --l) {
       const int nin = p.widths[l - 1], nout = p.widths[l];
       const float* Wl = W + p.off[l];
-      const float* dl = w.delta[l];
-      float* dprev = w.delta[l - 1];
-      const float* spp = w.sp[l - 1];
-      block_gemm(
+      const float* dl = delta(l);
+      float* dprev = delta(l - 1);
+      const float* spp = spv(l - 1);
+      block_gemm<true>(
           n, nin, nout, [=](int j, int r) { return dl[j * nout + r]; },
-          [=](int r, int c) { return Wl[(int64_t)r * nin + c]; },
-          [=](int j, int c, float x) { dprev[j * nin + c] = x * spp[j * nin + c]; });
+          [=](int r, int c) { return Wl[(int64_t)r * nin + c]; }, kB_NMAJOR,
+          [=](int j, int c, float x, bool ok) {
+            const float sp = spp[j * nin + c];
+            if (ok) dprev[j * nin + c] = x * sp;
+          });
     }
     // ---- a5: retrieval ----
     int cur = 0;
@@ -279,46 +371,54 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
       const int nin = p.widths[l - 1], nout = p.widths[l];
       const float* Wl = W + p.off[l];
       const float* Sl = S + p.off[l];
-      const float* h = w.hq[cur];
-      float* hn = w.hq[cur ^ 1];
-      const float* ak = w.act[l - 1];
-      const float* dl = w.delta[l];
+      const float* h = hq(cur);
+      float* hn = hq(cur ^ 1);
+      const float* ak = act(l - 1);
+      const float* dl = delta(l);
       const bool last = (l == L);
       const int maxw = p.maxw;
-      auto epi = [=](int j, int r, float zq) {
+      auto epi = [=](int j, int r, float zq, bool ok) {
+        if (!ok) return;
         if (last)
           store_io(p.y, (tok0 + c0 + j) * d + r, zq, p.io);
         else
           hn[j * maxw + r] = silu(zq);
       };
       if (p.read_mode == TM_READ_CHUNK_START) {
-        block_gemm(
+        block_gemm<true>(
             n, nout, nin, [=](int j, int c) { return h[j * maxw + c]; },
-            [=](int c, int r) { return Wl[(int64_t)r * nin + c]; }, epi);
+            [=](int c, int r) { return Wl[(int64_t)r * nin + c]; }, kB_KMAJOR, epi);
       } else {
         float* sc = w.sc;
         const float* D = w.D;
         // masked, decay-weighted scores (D o (h a^T)), lower triangle
-        block_gemm(
+        block_gemm<true>(
             n, n, nin, [=](int j, int c) { return h[j * maxw + c]; },
-            [=](int c, int i) { return ak[i * nin + c]; },
-            [=](int j, int i, float x) { sc[j * n + i] = (i <= j) ? D[j * n + i] * x : 0.f; });
+            [=](int c, int i) { return ak[i * nin + c]; }, kB_KMAJOR,
+            [=](int j, int i, float x, bool ok) {
+              const float dji = D[j * n + i];
+              if (ok) sc[j * n + i] = (i <= j) ? dji * x : 0.f;
+            });
         const float* A = w.A;
         const float* F = w.F;
         // zq = diag(A) h W^T + diag(F) h S^T - sc delta, as one contraction
         // over the concatenated index [W-part | S-part | token part]
-        block_gemm(
+        block_gemm<true>(
             n, nout, 2 * nin + n,
-            [=](int j, int kk) {
-              if (kk < nin) return A[j] * h[j * maxw + kk];
-              if (kk < 2 * nin) return F[j] * h[j * maxw + kk - nin];
-              return -sc[j * n + kk - 2 * nin];
+            [=](int j, int kk) {   // branch-free: pick the address, then the factor
+              const bool st = kk < 2 * nin;
+              const float* x = st ? h + j * maxw + (kk < nin ? kk : kk - nin) : sc + j * n + (kk - 2 * nin);
+              const float f = *(kk < nin ? A + j : F + j);
+              const float v = *x;
+              return st ? f * v : -v;
             },
             [=](int kk, int r) {
-              if (kk < nin) return Wl[(int64_t)r * nin + kk];
-              if (kk < 2 * nin) return Sl[(int64_t)r * nin + kk - nin];
-              return dl[(kk - 2 * nin) * nout + r];
+              const float* x = kk < nin       ? Wl + (int64_t)r * nin + kk
+                               : kk < 2 * nin ? Sl + (int64_t)r * nin + (kk - nin)
+                                              : dl + (int64_t)(kk - 2 * nin) * nout + r;
+              return *x;
             },
+            [=](int k0) { return k0 + kGk <= 2 * nin; },   // the token part is contiguous in r
             epi);
       }
       cur ^= 1;
@@ -332,21 +432,23 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
         const int nin = p.widths[l - 1], nout = p.widths[l];
         float* Wl = W + p.off[l];
         float* Sl = S + p.off[l];
-        const float* dl = w.delta[l];
-        const float* ak = w.act[l - 1];
-        block_gemm(
+        const float* dl = delta(l);
+        const float* ak = act(l - 1);
+        block_gemm<false>(
             nout, nin, n, [=](int r, int j) { return Dlast[j] * dl[j * nout + r]; },
-            [=](int j, int c) { return ak[j * nin + c]; },
-            [=](int r, int c, float g) {
+            [=](int j, int c) { return ak[j * nin + c]; }, kB_NMAJOR,
+            [=](int r, int c, float g, bool ok) {
               const int64_t i = (int64_t)r * nin + c;
-              Wl[i] = An * Wl[i] + Fn * Sl[i] - g;
+              const float wi = Wl[i], si = Sl[i];
+              if (ok) Wl[i] = An * wi + Fn * si - g;
             });
-        block_gemm(
+        block_gemm<false>(
             nout, nin, n, [=](int r, int j) { return U[j] * dl[j * nout + r]; },
-            [=](int j, int c) { return ak[j * nin + c]; },
-            [=](int r, int c, float g) {
+            [=](int j, int c) { return ak[j * nin + c]; }, kB_NMAJOR,
+            [=](int r, int c, float g, bool ok) {
               const int64_t i = (int64_t)r * nin + c;
-              Sl[i] = En * Sl[i] - g;
+              const float si = Sl[i];
+              if (ok) Sl[i] = En * si - g;
             });
       }
     }
@@ -410,17 +512,7 @@ GParams make_params(const Shape& s, int chunk) {
 
 }  // namespace
 
-int64_t generic_ws_floats_per_stream(const Shape& s, int b) {
-  int64_t f = 0;
-  for (int l = 0; l <= s.L; ++l) f += (int64_t)b * s.widths[l];       // act
-  for (int l = 1; l < s.L; ++l) f += (int64_t)b * s.widths[l];        // sp
-  for (int l = 1; l <= s.L; ++l) f += (int64_t)b * s.widths[l];       // delta
-  f += (int64_t)b * s.d;                                              // vin
-  f += 2 * (int64_t)b * s.maxw;                                       // hq
-  f += 2 * (int64_t)b * b;                                            // sc, D
-  f += 4 * (int64_t)b;                                                // A, E, F, U
-  return (f + 63) / 64 * 64;                                          // keep 256-byte alignment
-}
+int64_t generic_ws_floats_per_stream(const Shape& s, int b) { return ws_layout(s, b).total; }
 
 hipError_t launch_generic(const Shape& s, int chunk, const void* k, const void* v, const void* q,
                           const float* alpha, const float* eta, const float* theta,
@@ -428,6 +520,7 @@ hipError_t launch_generic(const Shape& s, int chunk, const void* k, const void* 
                           float* S_out, float* ws, hipStream_t stream) {
   GParams p = make_params(s, chunk);
   p.b = chunk < s.N ? chunk : (s.N > 0 ? s.N : 1);
+  p.lay = ws_layout(s, p.b);
   p.k = k;
   p.v = v;
   p.q = q;
@@ -454,6 +547,7 @@ hipError_t launch_generic_checkpoints(const Shape& s, int chunk, const void* k, 
                                       int64_t ckpt_stride, float* ws, int64_t ws_stride, hipStream_t stream) {
   GParams p = make_params(s, chunk);
   p.b = chunk < s.N ? chunk : (s.N > 0 ? s.N : 1);
+  p.lay = ws_layout(s, p.b);
   p.k = k;
   p.v = v;
   p.q = q;
