@@ -5,64 +5,102 @@
 // "Objective": the memory's parameters are the inner loop, the rest of the
 // architecture the outer one).
 //
-// Forward being differentiated, per token t of chunk c (gradients at the
-// chunk-start weights W_c, section 3.2; momentum and forgetting of section
-// 3.1):
-//   g_t = grad of 0.5 ||M_{W_c}(k_t) - v_t||^2 = {delta_l a_{l-1}^T}
-//   S_t = eta_t S_{t-1} - theta_t g_t,   W_t = (1 - alpha_t) W_{t-1} + S_t
-//   y_t = M_{W_t}(q_t)   (or M_{W_c}(q_t) with the chunk-start read)
-// Reverse mode, token by token from the last (adjoints carry a bar):
-//   Wbar += retrieval backprop of ybar_t;  qbar_t from the same backprop
-//   alphabar_t = -<Wbar, W_{t-1}>;  Sbar += Wbar;  Wbar *= (1 - alpha_t)
-//   etabar_t = <Sbar, S_{t-1}>;  thetabar_t = -<Sbar, g_t>
-//   W_c receives the derivative of phi = <Gbar, g_t(W_c, k_t, v_t)> with
-//   Gbar = -theta_t Sbar (a Hessian-vector product of the inner loss, which
-//   also gives kbar_t and vbar_t); Sbar *= eta_t
-// and at the start of each chunk Wbar += (what W_c received).  phi's
-// derivative is the backward pass of the inner backward pass:
-//   u_l = Gbar_l a_{l-1},  r_l = Gbar_l^T delta_l
-//   deltabar_1 = u_1;  e_{l-1} = deltabar_{l-1} * s'(z_{l-1});
-//   deltabar_l = u_l + W_l e_{l-1};  W_l gets delta_l e_{l-1}^T;
-//   zbar_{l-1} gets deltabar_{l-1} * b_{l-1} * s''(z_{l-1})  (b_{l-1} = W_l^T delta_l)
-//   vbar = -deltabar_L;  zbar_L = deltabar_L;  then the forward's adjoints
-//   top-down with abar_{l-1} = W_l^T zbar_l + r_l, W_l gets zbar_l a_{l-1}^T,
-//   zbar_{l-1} gets abar_{l-1} * s'(z_{l-1});  kbar = abar_0.
+// Forward being differentiated, chunk by chunk (section 3.2: every gradient
+// of a chunk is taken at its chunk-start weights W; momentum and forgetting
+// of section 3.1).  Per layer, with g_i = delta_i a_i^T the inner gradient
+// of token i at W, and the chunk coefficients of the gates (t, i local):
+//   A_t = prod_{m<=t} (1 - alpha_m)   E_t = prod_{m<=t} eta_m
+//   F_t = (1 - alpha_t) F_{t-1} + E_t  P[t,i] = prod_{i<m<=t} eta_m
+//   D[t,i] = (1 - alpha_t) D[t-1,i] + theta_i P[t,i]  (D[i,i] = theta_i)
+//   U_i = theta_i P[n-1,i]
+// the state after token t is W_t = A_t W + F_t S - sum_{i<=t} D[t,i] g_i,
+// the chunk ends at (W_{n-1}, E_{n-1} S - sum_i U_i g_i), and the read of
+// token t (after its write) is, layer by layer from h^0 = q_t,
+//   zq^l_t = A_t W h_t + F_t S h_t - sum_{i<=t} D[t,i] (a_i . h_t) delta_i.
 //
-// Execution: one workgroup per stream, fp32 throughout.  A forward sweep
-// (the generic kernel's chunked closed form, without retrieval) stores
-// (W, S) at every chunk start in the workspace; the reverse sweep
-// recomputes each chunk's per-token states W_t, S_t and the key-side
-// vectors (z, delta, b at W_c) into the workspace, then walks its tokens
-// backwards.  Matrices stay in global memory (L2-resident for the small
-// memories); vectors live in LDS.  Matrix-vector products use 16-lane
-// groups per row (float4 loads, DPP sums) or column groups with an LDS
-// reduction; the state adjoints are updated in one float4 pass per layer
-// that folds in every rank-1 term of the step.
+// Reverse mode runs over the chunks from the last, carrying the adjoints
+// (Wbar, Sbar) of the chunk-end state.  Per chunk, from the chunk-start
+// checkpoint (W, S), every step is a contraction over the chunk's tokens or
+// over a layer width, i.e. a matrix product of the same shapes as the
+// forward's closed form (adjoints carry a bar; rho^l_t = dL/dzq^l_t):
+//   reads    rho^L = dy;  Abar_t += rho.(W h), Fbar_t += rho.(S h)
+//            Dbar[t,i] -= (rho_t . delta_i)(a_i . h_t)
+//            hbar = A W^T rho + F S^T rho - sum_i D[t,i] (rho_t . delta_i) a_i
+//            rho^{l-1} = hbar * SiLU'(zq^{l-1}),  qbar = hbar at l = 1
+//            deltabar_i -= sum_t D[t,i] (a_i . h_t) rho_t
+//            abar_i     -= sum_t D[t,i] (rho_t . delta_i) h_t
+//   fold     deltabar_i -= D[n-1,i] Wbar a_i + U_i Sbar a_i
+//            abar_i     -= D[n-1,i] Wbar^T delta_i + U_i Sbar^T delta_i
+//            Dbar[n-1,i] -= delta_i . Wbar a_i,  Ubar_i -= delta_i . Sbar a_i
+//            Abar_{n-1} += <Wbar, W>, Fbar_{n-1} += <Wbar, S>, Ebar_{n-1} = <Sbar, S>
+//   inner gradient (delta^L = a^L - v, delta^l = b^l * SiLU'(z^l) with
+//            b^l = W^{l+1 T} delta^{l+1}; its backward pass carries the
+//            second-order terms):
+//            bbar^l = deltabar^l * SiLU'(z^l), zbar^l = deltabar^l * b^l * SiLU''(z^l),
+//            deltabar^{l+1} += W^{l+1} bbar^l;  vbar = -deltabar^L, zbar^L = deltabar^L;
+//            zbar^l += abar^l * SiLU'(z^l), abar^{l-1} += W^{l T} zbar^l;  kbar = abar^0
+//   state    Sbar <- F_{n-1} Wbar + E_{n-1} Sbar + sum_t F_t rho_t h_t^T
+//            Wbar <- A_{n-1} Wbar + sum_t A_t rho_t h_t^T
+//                    + sum_i (delta^l_i bbar^{l-1 T}_i + zbar^l_i a^{l-1 T}_i)
+//   gates    the adjoints of A, E, F, D, P, U back through their recurrences
+// With the chunk-start read, zq^l_t = W h_t: hbar = W^T rho and Wbar gains
+// sum_t rho_t h_t^T; no coefficient enters the reads.
+//
+// Execution: a forward sweep (the generic kernel's chunked closed form,
+// without retrieval) stores (W, S) at every chunk start in the workspace;
+// then one workgroup per stream walks the chunks backwards.  Every product
+// is block_gemm (fp32 on the matrix cores); the chunk's vectors live in a
+// per-stream workspace region, the adjoints (Wbar, Sbar) in dW_in, dS_in.
 #include "tm_internal.h"
+#include "tm_block_gemm.h"
 
 #include <hip/hip_bf16.h>
+
+#include <algorithm>
 
 namespace titans {
 namespace {
 
-constexpr int kBT = 512;      // threads per workgroup
+constexpr int kBT = kGemmThreads;   // threads per workgroup
 constexpr int kBW = kBT / 64;
 
+// Per-stream workspace region of the reverse sweep (float offsets, b rows
+// per chunk; "[b x n_l]" is token-major).  Filled on the host.
+struct BwLayout {
+  int64_t act[kMaxLayers + 1];   // a^l of the keys, l = 0..L (a^0 = k)       [b x n_l]
+  int64_t z[kMaxLayers + 1];     // z^l, l = 1..L-1
+  int64_t dl[kMaxLayers + 1];    // delta^l, l = 1..L
+  int64_t bv[kMaxLayers + 1];    // b^l = W^{l+1 T} delta^{l+1}, l = 1..L-1
+  int64_t h[kMaxLayers + 1];     // read activations h^l, l = 0..L-1 (h^0 = q)
+  int64_t zq[kMaxLayers + 1];    // read pre-activations, l = 1..L-1
+  int64_t uw[kMaxLayers + 1];    // W^l h^{l-1}, l = 1..L
+  int64_t us[kMaxLayers + 1];    // S^l h^{l-1}, l = 1..L
+  int64_t rho[kMaxLayers + 1];   // dL/dzq^l, l = 1..L
+  int64_t sc[kMaxLayers + 1];    // a^{l-1}_i . h^{l-1}_t, l = 1..L           [b x b], [t][i]
+  int64_t dbar[kMaxLayers + 1];  // deltabar^l, l = 1..L (also zbar^L)
+  int64_t abar[kMaxLayers + 1];  // abar^l, l = 0..L-1
+  int64_t bbar[kMaxLayers + 1];  // bbar^l, l = 1..L-1
+  int64_t zbar[kMaxLayers + 1];  // zbar^l, l = 1..L-1
+  int64_t vin, xw, xs;           // v [b x d]; Wbar a, Sbar a [b x maxw]
+  int64_t dsc, dr;               // -D o sc, -D o (rho delta^T)               [b x b]
+  int64_t D, P, Dbar, Ca, Ce;    // [b x b]
+  int64_t A, E, F, U, Abar, Fbar, Ubar, ga, ge, gt;   // [b]
+  int64_t red;                   // 64 floats
+  int64_t total;
+};
+
 struct BwdParams {
-  int N, chunk, nchunks, streams, L, d, io, read_mode, chunk_gates;
+  int N, chunk, nchunks, b, L, d, io, read_mode, chunk_gates;
   int w[kMaxLayers + 1];
   int64_t off[kMaxLayers + 1];
   int64_t P;
-  int maxw, sumn;
-  int zo[kMaxLayers + 1];      // offset of layer l's vector (l = 1..L) in a sum-of-widths vector
+  int maxw;
   const void* k;
   const void* v;
   const void* q;
   const float* alpha;
   const float* eta;
   const float* theta;
-  const float* W_in;
-  const float* S_in;
   const float* dy;
   const float* dW_out;
   const float* dS_out;
@@ -72,28 +110,23 @@ struct BwdParams {
   float* dalpha;
   float* deta;
   float* dtheta;
-  float* dW_in;
-  float* dS_in;
+  float* dW_in;       // Wbar during the sweep
+  float* dS_in;       // Sbar during the sweep
   float* ws;
-  int64_t ws_stream;           // floats per stream
-  int64_t o_cw, o_cs, o_tv, o_wb, o_sb, o_wcb;   // offsets (floats) in a stream's region; checkpoints at 0
-  int lds_floats;
+  int64_t ws_stream;  // floats per stream
+  int64_t o_buf;      // offset of the reverse sweep's region (checkpoints before it)
+  BwLayout lay;
 };
 
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, true));
 }
-// sum over the aligned 16-lane group (result in every lane of the group)
-__device__ __forceinline__ float sum16(float x) {
+__device__ __forceinline__ float wave_sum(float x) {
   x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
   x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
   x += dpp<0x141>(x);  // row_half_mirror
-  x += dpp<0x140>(x);  // row_mirror
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-  x = sum16(x);
+  x += dpp<0x140>(x);  // row_mirror: every lane holds its 16-lane group's sum
   return __shfl(x, 0) + __shfl(x, 16) + __shfl(x, 32) + __shfl(x, 48);
 }
 // total over the workgroup, returned to every thread
@@ -109,400 +142,635 @@ __device__ float block_sum(float x, float* red) {
 }
 
 __device__ __forceinline__ float sgm(float z) { return 1.0f / (1.0f + expf(-z)); }
-__device__ __forceinline__ float act(float z) { return z * sgm(z); }                       // SiLU
-__device__ __forceinline__ float dact(float z) { const float s = sgm(z); return s * (1.f + z * (1.f - s)); }
-__device__ __forceinline__ float d2act(float z) {
+__device__ __forceinline__ float silu(float z) { return z * sgm(z); }
+__device__ __forceinline__ float dsilu(float z) { const float s = sgm(z); return s * (1.f + z * (1.f - s)); }
+__device__ __forceinline__ float d2silu(float z) {
   const float s = sgm(z);
   return s * (1.f - s) * (2.f + z * (1.f - 2.f * s));
 }
 
-// out[i] = sum_j M[i][j] x[j] (M row-major n_out x n_in, n_in % 4 == 0);
-// 16 lanes per row, float4 loads.  Ends with a barrier.
-__device__ void mv_rows(float* out, const float* M, const float* x, int n_out, int n_in) {
-  const int sl = threadIdx.x & 15, gr = threadIdx.x >> 4;
-  constexpr int kRowsPerPass = kBT / 16;
-  // four row passes at a time, so that four independent loads are in flight
-  for (int i0 = 0; i0 < n_out; i0 += 4 * kRowsPerPass) {
-    float s[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 4 * sl; j < n_in; j += 64) {
-      float4 m[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * kRowsPerPass + gr;
-        m[u] = i < n_out ? *(const float4*)(M + (int64_t)i * n_in + j) : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-      const float x0 = x[j], x1 = x[j + 1], x2 = x[j + 2], x3 = x[j + 3];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) s[u] += m[u].x * x0 + m[u].y * x1 + m[u].z * x2 + m[u].w * x3;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float t = sum16(s[u]);
-      const int i = i0 + u * kRowsPerPass + gr;
-      if (i < n_out && sl == 0) out[i] = t;
-    }
-  }
-  __syncthreads();
-}
-
-// out[j] = sum_i M[i][j] z[i] (+ add[j] if add): column groups of 4, rows
-// split over the remaining threads, partial sums reduced through `red`
-// (kBT * 4 floats).  Ends with a barrier.
-__device__ void mv_cols(float* out, const float* M, const float* z, int n_out, int n_in, float* red,
-                        const float* add = nullptr, float add_scale = 0.f) {
-  const int cg = n_in / 4;
-  if (cg >= kBT) {
-    for (int c = threadIdx.x; c < cg; c += kBT) {
-      float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int i = 0; i < n_out; ++i) {
-        const float4 m = *(const float4*)(M + (int64_t)i * n_in + 4 * c);
-        const float zi = z[i];
-        s.x += m.x * zi; s.y += m.y * zi; s.z += m.z * zi; s.w += m.w * zi;
-      }
-      const float o[4] = {s.x, s.y, s.z, s.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) out[4 * c + e] = o[e] + (add ? add_scale * add[4 * c + e] : 0.f);
-    }
-    __syncthreads();
-    return;
-  }
-  const int rg = kBT / cg;                 // row groups
-  const int c = threadIdx.x % cg, g = threadIdx.x / cg;
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (g < rg) {
-#pragma unroll 4
-    for (int i = g; i < n_out; i += rg) {
-      const float4 m = *(const float4*)(M + (int64_t)i * n_in + 4 * c);
-      const float zi = z[i];
-      s.x += m.x * zi; s.y += m.y * zi; s.z += m.z * zi; s.w += m.w * zi;
-    }
-    *(float4*)(red + (g * cg + c) * 4) = s;
-  }
-  __syncthreads();
-  for (int j = threadIdx.x; j < n_in; j += kBT) {
-    float t = 0.f;
-    for (int gg = 0; gg < rg; ++gg) t += red[(gg * cg + j / 4) * 4 + (j & 3)];
-    out[j] = t + (add ? add_scale * add[j] : 0.f);
-  }
-  __syncthreads();
-}
-
 __device__ __forceinline__ float io_load(const void* base, int io, int64_t i) {
-  if (io == TM_IO_BF16) {
-    const unsigned short u = ((const unsigned short*)base)[i];
-    return __uint_as_float((unsigned)u << 16);
-  }
+  if (io == TM_IO_BF16) return __bfloat162float(((const __hip_bfloat16*)base)[i]);
   return ((const float*)base)[i];
 }
 
-
-// Recompute chunk c from its checkpoint: per token j the key-side vectors at
-// W_c (z, delta, b into tv), and S_t, W_t into cs[j], cw[j].  Leaves xk
-// holding the last token's key.  Ends with a barrier.
-__device__ void run_chunk(const BwdParams& p, int s, int c, float* base, float* lds) {
-  const int64_t P = p.P;
-  const int c0 = c * p.chunk;
-  const int n = min(p.chunk, p.N - c0);
-  const float* Wc = base + (int64_t)c * 2 * P;
-  const float* Sc = Wc + P;
-  float* xk = lds;                       // a_0 = k_t
-  float* za = xk + p.maxw;               // z at W_c (sum of widths)
-  float* aa = za + p.sumn;               // activations a_l, l = 1..L-1 (same offsets as z)
-  float* dl = aa + p.sumn;               // delta
-  float* bb = dl + p.sumn;               // b_l = W_{l+1}^T delta_{l+1}
-  float* red = bb + p.sumn;              // kBT * 4
-  const int64_t tok0 = (int64_t)s * p.N + c0;
-  for (int j = 0; j < n; ++j) {
-    const int64_t tt = tok0 + j;
-    for (int i = threadIdx.x; i < p.d; i += kBT) xk[i] = io_load(p.k, p.io, tt * p.d + i);
-    __syncthreads();
-    // forward at W_c
-    for (int l = 1; l <= p.L; ++l) {
-      const float* ain = l == 1 ? xk : aa + p.zo[l - 1];
-      mv_rows(za + p.zo[l], Wc + p.off[l], ain, p.w[l], p.w[l - 1]);
-      if (l < p.L)
-        for (int i = threadIdx.x; i < p.w[l]; i += kBT) aa[p.zo[l] + i] = act(za[p.zo[l] + i]);
-      __syncthreads();
-    }
-    // backprop of 0.5 ||o - v||^2 at W_c
-    for (int i = threadIdx.x; i < p.d; i += kBT) dl[p.zo[p.L] + i] = za[p.zo[p.L] + i] - io_load(p.v, p.io, tt * p.d + i);
-    __syncthreads();
-    for (int l = p.L; l >= 2; --l) {
-      mv_cols(bb + p.zo[l - 1], Wc + p.off[l], dl + p.zo[l], p.w[l], p.w[l - 1], red);
-      for (int i = threadIdx.x; i < p.w[l - 1]; i += kBT)
-        dl[p.zo[l - 1] + i] = bb[p.zo[l - 1] + i] * dact(za[p.zo[l - 1] + i]);
-      __syncthreads();
-    }
-    // key-side vectors of this token
-    float* tv = base + p.o_tv + (int64_t)j * 3 * p.sumn;
-    for (int i = threadIdx.x; i < p.sumn; i += kBT) {
-      tv[i] = za[i];
-      tv[p.sumn + i] = dl[i];
-      tv[2 * p.sumn + i] = bb[i];
-    }
-    // S_t = eta S_{t-1} - theta delta a^T, W_t = (1 - alpha) W_{t-1} + S_t
-    const int64_t gi = p.chunk_gates ? (int64_t)s * p.nchunks + c : tt;
-    const float al = p.alpha[gi], et = p.eta[gi], th = p.theta[gi];
-    const float* Wp = j == 0 ? Wc : base + p.o_cw + (int64_t)(j - 1) * P;
-    const float* Sp = j == 0 ? Sc : base + p.o_cs + (int64_t)(j - 1) * P;
-    float* Wt = base + p.o_cw + (int64_t)j * P;
-    float* St = base + p.o_cs + (int64_t)j * P;
-    for (int l = 1; l <= p.L; ++l) {
-      const float* ain = l == 1 ? xk : aa + p.zo[l - 1];
-      const float* dd = dl + p.zo[l];
-      const int n_in = p.w[l - 1];
-      const int64_t n4 = (int64_t)p.w[l] * n_in / 4;
-#pragma unroll 4
-      for (int64_t e = threadIdx.x; e < n4; e += kBT) {
-        const int64_t f = p.off[l] + 4 * e;
-        const int i = (int)(4 * e / n_in), m = (int)(4 * e - (int64_t)i * n_in);
-        const float4 sp = *(const float4*)(Sp + f), wp = *(const float4*)(Wp + f);
-        const float td = th * dd[i];
-        float4 sn, wn;
-        sn.x = et * sp.x - td * ain[m];     wn.x = (1.f - al) * wp.x + sn.x;
-        sn.y = et * sp.y - td * ain[m + 1]; wn.y = (1.f - al) * wp.y + sn.y;
-        sn.z = et * sp.z - td * ain[m + 2]; wn.z = (1.f - al) * wp.z + sn.z;
-        sn.w = et * sp.w - td * ain[m + 3]; wn.w = (1.f - al) * wp.w + sn.w;
-        *(float4*)(St + f) = sn;
-        *(float4*)(Wt + f) = wn;
-      }
-    }
-    __syncthreads();
+// out[t] += sum_{c < w} X[t*ldx + c] * Y[t*ldy + c] for rows t < n, one wave
+// per row (each wave walks its own rows; no barrier inside).
+__device__ void row_dots(float* out, const float* X, int ldx, const float* Y, int ldy, int n, int w) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int t = wv; t < n; t += kBW) {
+    float acc = 0.f;
+    for (int c = lane; c < w; c += 64) acc += X[(int64_t)t * ldx + c] * Y[(int64_t)t * ldy + c];
+    acc = wave_sum(acc);
+    if (lane == 0) out[t] += acc;
   }
 }
 
 __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
-  extern __shared__ __attribute__((aligned(16))) float lds[];
   const int s = blockIdx.x;
-  if (s >= p.streams) return;
+  const int tid = threadIdx.x;
+  const int L = p.L, d = p.d, bb = p.b, mw = p.maxw;
   const int64_t P = p.P;
-  float* base = p.ws + (int64_t)s * p.ws_stream;
-  float* Wb = base + p.o_wb;
-  float* Sb = base + p.o_sb;
-  float* Wcb = base + p.o_wcb;
-
-  // (W, S) at every chunk start are in the workspace: the chunked forward
-  // sweep that precedes this kernel on the stream wrote them.
-  // ---- reverse sweep ----
-  for (int64_t e = threadIdx.x; e < P; e += kBT) {
-    Wb[e] = p.dW_out ? p.dW_out[(int64_t)s * P + e] : 0.f;
-    Sb[e] = p.dS_out ? p.dS_out[(int64_t)s * P + e] : 0.f;
+  float* const Wb = p.dW_in + (int64_t)s * P;
+  float* const Sb = p.dS_in + (int64_t)s * P;
+  for (int64_t i = tid; i < P; i += kBT) {
+    Wb[i] = p.dW_out ? p.dW_out[(int64_t)s * P + i] : 0.f;
+    Sb[i] = p.dS_out ? p.dS_out[(int64_t)s * P + i] : 0.f;
   }
+  float* const base = p.ws + (int64_t)s * p.ws_stream;
+  float* const wsb = base + p.o_buf;
+  const BwLayout& y = p.lay;
+  auto V = [&](int64_t o) { return wsb + o; };
+  float* const red = V(y.red);
+  float* const cA = V(y.A);
+  float* const cE = V(y.E);
+  float* const cF = V(y.F);
+  float* const cU = V(y.U);
+  float* const cD = V(y.D);
+  float* const cP = V(y.P);
+  float* const Abar = V(y.Abar);
+  float* const Fbar = V(y.Fbar);
+  float* const Ubar = V(y.Ubar);
+  float* const Dbar = V(y.Dbar);
+  float* const Ca = V(y.Ca);
+  float* const Ce = V(y.Ce);
+  float* const ga = V(y.ga);
+  float* const ge = V(y.ge);
+  float* const gt = V(y.gt);
+  float* const vin = V(y.vin);
+  float* const xw = V(y.xw);
+  float* const xs = V(y.xs);
+  float* const dsc = V(y.dsc);
+  float* const dr = V(y.dr);
+  const bool reads = p.dy != nullptr;
+  const bool cstart = p.read_mode == TM_READ_CHUNK_START;
+  const int64_t tok0 = (int64_t)s * p.N;
   __syncthreads();
-  // LDS beyond run_chunk's area
-  float* xk = lds;
-  float* za = xk + p.maxw;
-  float* aa = za + p.sumn;
-  float* dl = aa + p.sumn;
-  float* bb = dl + p.sumn;
-  float* red = bb + p.sumn;            // kBT * 4
-  float* xq = red + kBT * 4;           // q_t
-  float* qz = xq + p.maxw;             // z of the query forward
-  float* qa = qz + p.sumn;             // its activations
-  float* v1 = qa + p.sumn;             // working vectors (maxw each)
-  float* v2 = v1 + p.maxw;
-  float* up = v2 + p.maxw;             // u'_l = Sbar_l a_{l-1} (sum of widths)
-  float* db = up + p.sumn;             // deltabar
-  float* zb = db + p.sumn;             // zbar
-  float* zs = zb + p.sumn;             // the s'' part of zbar
-  float* rp = zs + p.sumn;             // r'_l = Sbar_l^T delta_l, [L][maxw]
-  float* dzq = rp + p.L * p.maxw;      // the retrieval backprop's dz_l (sum of widths)
-  float* ee = dzq + p.sumn;            // e_l = deltabar_l * s'(z_l) of the Hessian-vector term
 
-  float eta_prev = 1.f;   // Sbar still owes this factor (the last processed token's eta)
   for (int c = p.nchunks - 1; c >= 0; --c) {
-    run_chunk(p, s, c, base, lds);
     const int c0 = c * p.chunk;
     const int n = min(p.chunk, p.N - c0);
-    const float* Wc = base + (int64_t)c * 2 * P;
-    const float* Sc = Wc + P;
-    for (int64_t e = threadIdx.x; e < P; e += kBT) Wcb[e] = 0.f;
-    __syncthreads();
-    float gsum_a = 0.f, gsum_e = 0.f, gsum_t = 0.f;   // chunk-gate sums (thread 0)
-    for (int j = n - 1; j >= 0; --j) {
-      const int64_t tt = (int64_t)s * p.N + c0 + j;
-      const float* Wt = base + p.o_cw + (int64_t)j * P;
-      const float* Wp = j == 0 ? Wc : base + p.o_cw + (int64_t)(j - 1) * P;
-      const float* Sp = j == 0 ? Sc : base + p.o_cs + (int64_t)(j - 1) * P;
-      const int64_t gi = p.chunk_gates ? (int64_t)s * p.nchunks + c : tt;
-      const float al = p.alpha[gi], et = p.eta[gi], th = p.theta[gi];
+    const float* const W = base + (int64_t)c * 2 * P;   // chunk-start checkpoint
+    const float* const S = W + P;
+    const int64_t g0 = p.chunk_gates ? (int64_t)s * p.nchunks + c : tok0 + c0;
+    const int gs = p.chunk_gates ? 0 : 1;
+    const float* al = p.alpha + g0;
+    const float* et = p.eta + g0;
+    const float* th = p.theta + g0;
+    const int64_t row0 = tok0 + c0;                       // first token row of the chunk
 
-      // (1) retrieval: y_t = M_{Wr}(q_t)
-      const float* Wr = p.read_mode == TM_READ_CHUNK_START ? Wc : Wt;
-      if (p.dy) {
-        for (int i = threadIdx.x; i < p.d; i += kBT) {
-          xq[i] = io_load(p.q, p.io, tt * p.d + i);
-          v1[i] = p.dy[tt * p.d + i];                // dz_L
-        }
-        __syncthreads();
-        for (int l = 1; l <= p.L; ++l) {
-          const float* ain = l == 1 ? xq : qa + p.zo[l - 1];
-          mv_rows(qz + p.zo[l], Wr + p.off[l], ain, p.w[l], p.w[l - 1]);
-          if (l < p.L)
-            for (int i = threadIdx.x; i < p.w[l]; i += kBT) qa[p.zo[l] + i] = act(qz[p.zo[l] + i]);
-          __syncthreads();
-        }
-        for (int l = p.L; l >= 1; --l) {
-          // da = Wr_l^T dz_l; dz_l is kept for the fused state-adjoint passes
-          mv_cols(v2, Wr + p.off[l], v1, p.w[l], p.w[l - 1], red);
-          for (int i = threadIdx.x; i < p.w[l]; i += kBT) dzq[p.zo[l] + i] = v1[i];
-          __syncthreads();
-          if (l > 1) {
-            for (int i = threadIdx.x; i < p.w[l - 1]; i += kBT) v1[i] = v2[i] * dact(qz[p.zo[l - 1] + i]);
-          } else {
-            for (int i = threadIdx.x; i < p.d; i += kBT) p.dq[tt * p.d + i] = v2[i];
-          }
-          __syncthreads();
-        }
+    // ---- chunk inputs; adjoint accumulators cleared ----
+    for (int e = tid; e < n * d; e += kBT) {
+      const int64_t gi = row0 * d + e;
+      V(y.act[0])[e] = io_load(p.k, p.io, gi);
+      vin[e] = io_load(p.v, p.io, gi);
+      if (reads) {
+        V(y.h[0])[e] = io_load(p.q, p.io, gi);
+        V(y.rho[L])[e] = p.dy[gi];
       } else {
-        for (int i = threadIdx.x; i < p.d; i += kBT) p.dq[tt * p.d + i] = 0.f;
+        p.dq[gi] = 0.f;
       }
-      // the retrieval's rank-1 terms go to Wbar (read-after-write) or to W_c's
-      // adjoint (chunk-start read); none without dL/dy (xq and qa are then unset)
-      const bool rw = p.dy && p.read_mode != TM_READ_CHUNK_START;
-      const bool rc = p.dy && p.read_mode == TM_READ_CHUNK_START;
-
-      // (2) W_t = (1 - alpha) W_{t-1} + S_t, and eta's inner product.  Folded
-      // into the same pass: the retrieval's rank-1 terms dz_l aq_{l-1}^T
-      // (read-after-write) and the previous token's Sbar <- eta Sbar.
-      float pa = 0.f, pe = 0.f;
-      for (int l = 1; l <= p.L; ++l) {
-        const float* aq = l == 1 ? xq : qa + p.zo[l - 1];
-        const float* dz = dzq + p.zo[l];
-        const int n_in = p.w[l - 1];
-        const int64_t n4 = (int64_t)p.w[l] * n_in / 4;
-        float4* wb4 = (float4*)(Wb + p.off[l]);
-        float4* sb4 = (float4*)(Sb + p.off[l]);
-        const float4* wp4 = (const float4*)(Wp + p.off[l]);
-        const float4* sp4 = (const float4*)(Sp + p.off[l]);
-#pragma unroll 4
-        for (int64_t e = threadIdx.x; e < n4; e += kBT) {
-          const int i = (int)(4 * e / n_in), j = (int)(4 * e - (int64_t)i * n_in);
-          float4 wb = wb4[e], sb = sb4[e];
-          const float4 wp = wp4[e], sp = sp4[e];
-          if (rw) {
-            const float di = dz[i];
-            wb.x += di * aq[j]; wb.y += di * aq[j + 1]; wb.z += di * aq[j + 2]; wb.w += di * aq[j + 3];
-          }
-          pa += wb.x * wp.x + wb.y * wp.y + wb.z * wp.z + wb.w * wp.w;
-          sb.x = eta_prev * sb.x + wb.x; sb.y = eta_prev * sb.y + wb.y;
-          sb.z = eta_prev * sb.z + wb.z; sb.w = eta_prev * sb.w + wb.w;
-          pe += sb.x * sp.x + sb.y * sp.y + sb.z * sp.z + sb.w * sp.w;
-          wb.x *= 1.f - al; wb.y *= 1.f - al; wb.z *= 1.f - al; wb.w *= 1.f - al;
-          wb4[e] = wb;
-          sb4[e] = sb;
-        }
-      }
-      const float abar = -block_sum(pa, red);
-      const float ebar = block_sum(pe, red);
-
-      // (3) S_t = eta S_{t-1} - theta g_t: thetabar and the Hessian-vector term at W_c
-      const float* tv = base + p.o_tv + (int64_t)j * 3 * p.sumn;
-      for (int i = threadIdx.x; i < p.sumn; i += kBT) {
-        za[i] = tv[i];
-        dl[i] = tv[p.sumn + i];
-        bb[i] = tv[2 * p.sumn + i];
-      }
-      for (int i = threadIdx.x; i < p.d; i += kBT) xk[i] = io_load(p.k, p.io, tt * p.d + i);
-      __syncthreads();
-      for (int l = 1; l < p.L; ++l)
-        for (int i = threadIdx.x; i < p.w[l]; i += kBT) aa[p.zo[l] + i] = act(za[p.zo[l] + i]);
-      __syncthreads();
-      for (int l = 1; l <= p.L; ++l) {
-        const float* ain = l == 1 ? xk : aa + p.zo[l - 1];
-        mv_rows(up + p.zo[l], Sb + p.off[l], ain, p.w[l], p.w[l - 1]);
-        mv_cols(rp + (l - 1) * p.maxw, Sb + p.off[l], dl + p.zo[l], p.w[l], p.w[l - 1], red);
-      }
-      float pt = 0.f;
-      for (int i = threadIdx.x; i < p.sumn; i += kBT) pt += dl[i] * up[i];
-      const float tbar = -block_sum(pt, red);
-      // deltabar chain, bottom-up (u = -theta u')
-      for (int i = threadIdx.x; i < p.w[1]; i += kBT) db[p.zo[1] + i] = -th * up[p.zo[1] + i];
-      __syncthreads();
-      for (int l = 2; l <= p.L; ++l) {
-        const int nl = p.w[l - 1];
-        for (int i = threadIdx.x; i < nl; i += kBT) {
-          const float z = za[p.zo[l - 1] + i], dbv = db[p.zo[l - 1] + i];
-          ee[p.zo[l - 1] + i] = dbv * dact(z);                     // e_{l-1}
-          zs[p.zo[l - 1] + i] = dbv * bb[p.zo[l - 1] + i] * d2act(z);
-        }
-        __syncthreads();
-        mv_rows(v2, Wc + p.off[l], ee + p.zo[l - 1], p.w[l], nl);  // W_l e_{l-1}
-        for (int i = threadIdx.x; i < p.w[l]; i += kBT) db[p.zo[l] + i] = -th * up[p.zo[l] + i] + v2[i];
-        __syncthreads();
-      }
-      // v enters through delta_L = o - v; then the forward's adjoints top-down
-      for (int i = threadIdx.x; i < p.d; i += kBT) {
-        p.dv[tt * p.d + i] = -db[p.zo[p.L] + i];
-        zb[p.zo[p.L] + i] = db[p.zo[p.L] + i];
-      }
-      __syncthreads();
-      for (int l = p.L; l >= 1; --l) {
-        const float* ain = l == 1 ? xk : aa + p.zo[l - 1];
-        // abar_{l-1} = W_l^T zbar_l + r_l, r_l = -theta r'_l
-        mv_cols(v2, Wc + p.off[l], zb + p.zo[l], p.w[l], p.w[l - 1], red, rp + (l - 1) * p.maxw, -th);
-        // W_c's adjoint, layer l: zbar_l a_{l-1}^T + delta_l e_{l-1}^T (l >= 2), and with the
-        // chunk-start read the retrieval's dz_l aq_{l-1}^T
-        {
-          const float* zbl = zb + p.zo[l];
-          const float* dll = dl + p.zo[l];
-          const float* eel = ee + p.zo[l - 1];
-          const float* dzl = dzq + p.zo[l];
-          const float* aq = l == 1 ? xq : qa + p.zo[l - 1];
-          const bool two = l >= 2, three = rc;
-          const int n_in = p.w[l - 1];
-          const int64_t n4 = (int64_t)p.w[l] * n_in / 4;
-          float4* m4 = (float4*)(Wcb + p.off[l]);
-#pragma unroll 4
-          for (int64_t e = threadIdx.x; e < n4; e += kBT) {
-            const int i = (int)(4 * e / n_in), j = (int)(4 * e - (int64_t)i * n_in);
-            float4 m = m4[e];
-            const float zi = zbl[i];
-            m.x += zi * ain[j]; m.y += zi * ain[j + 1]; m.z += zi * ain[j + 2]; m.w += zi * ain[j + 3];
-            if (two) {
-              const float di = dll[i];
-              m.x += di * eel[j]; m.y += di * eel[j + 1]; m.z += di * eel[j + 2]; m.w += di * eel[j + 3];
-            }
-            if (three) {
-              const float qi = dzl[i];
-              m.x += qi * aq[j]; m.y += qi * aq[j + 1]; m.z += qi * aq[j + 2]; m.w += qi * aq[j + 3];
-            }
-            m4[e] = m;
-          }
-        }
-        __syncthreads();
-        if (l > 1) {
-          for (int i = threadIdx.x; i < p.w[l - 1]; i += kBT)
-            zb[p.zo[l - 1] + i] = v2[i] * dact(za[p.zo[l - 1] + i]) + zs[p.zo[l - 1] + i];
-        } else {
-          for (int i = threadIdx.x; i < p.d; i += kBT) p.dk[tt * p.d + i] = v2[i];
-        }
-        __syncthreads();
-      }
-      // S_{t-1}'s adjoint is eta_t Sbar: applied in the next token's pass (or at the end)
-      eta_prev = et;
-      if (threadIdx.x == 0) {
-        if (p.chunk_gates) {
-          gsum_a += abar; gsum_e += ebar; gsum_t += tbar;
-        } else {
-          p.dalpha[tt] = abar; p.deta[tt] = ebar; p.dtheta[tt] = tbar;
-        }
-      }
-      __syncthreads();
     }
-    if (threadIdx.x == 0 && p.chunk_gates) {
-      const int64_t gi = (int64_t)s * p.nchunks + c;
-      p.dalpha[gi] = gsum_a; p.deta[gi] = gsum_e; p.dtheta[gi] = gsum_t;
+    for (int l = 0; l <= L; ++l) {
+      if (l >= 1)
+        for (int e = tid; e < n * p.w[l]; e += kBT) V(y.dbar[l])[e] = 0.f;
+      if (l < L)
+        for (int e = tid; e < n * p.w[l]; e += kBT) V(y.abar[l])[e] = 0.f;
     }
-    // the chunk-start state is also the previous chunk's last state
-    for (int64_t e = threadIdx.x; e < P; e += kBT) Wb[e] += Wcb[e];
+    for (int e = tid; e < n * bb; e += kBT) Dbar[e] = 0.f;
+    for (int e = tid; e < n; e += kBT) {
+      Abar[e] = 0.f;
+      Fbar[e] = 0.f;
+      Ubar[e] = 0.f;
+    }
+    // ---- coefficients: one thread per column i of D and P ----
+    for (int i = tid; i < n; i += kBT) {
+      const float ti = th[i * gs];
+      float di = ti, pr = 1.f;
+      for (int t = 0; t < i; ++t) {
+        cD[t * bb + i] = 0.f;
+        cP[t * bb + i] = 0.f;
+      }
+      cD[i * bb + i] = di;
+      cP[i * bb + i] = 1.f;
+      for (int t = i + 1; t < n; ++t) {
+        pr *= et[t * gs];
+        di = (1.f - al[t * gs]) * di + ti * pr;
+        cD[t * bb + i] = di;
+        cP[t * bb + i] = pr;
+      }
+      cU[i] = ti * pr;
+    }
+    if (tid == 0) {
+      float a = 1.f, e = 1.f, f = 0.f;
+      for (int t = 0; t < n; ++t) {
+        a *= 1.f - al[t * gs];
+        e *= et[t * gs];
+        f = (1.f - al[t * gs]) * f + e;
+        cA[t] = a;
+        cE[t] = e;
+        cF[t] = f;
+      }
+    }
     __syncthreads();
-  }
-  for (int64_t e = threadIdx.x; e < P; e += kBT) {
-    p.dW_in[(int64_t)s * P + e] = Wb[e];
-    p.dS_in[(int64_t)s * P + e] = eta_prev * Sb[e];
+
+    // ---- key side at W: z^l, a^l, delta^l, b^l ----
+    for (int l = 1; l <= L; ++l) {
+      const int nin = p.w[l - 1], nout = p.w[l];
+      const float* Wl = W + p.off[l];
+      const float* ain = V(y.act[l - 1]);
+      float* aout = V(y.act[l]);
+      float* zl = V(y.z[l]);
+      float* dl = V(y.dl[l]);
+      const bool last = l == L;
+      block_gemm<true>(
+          n, nout, nin, [=](int j, int cc) { return ain[j * nin + cc]; },
+          [=](int cc, int r) { return Wl[(int64_t)r * nin + cc]; }, kB_KMAJOR,
+          [=](int j, int r, float x, bool ok) {
+            if (last) {
+              const float vv = vin[j * nout + r];
+              if (ok) {
+                aout[j * nout + r] = x;
+                dl[j * nout + r] = x - vv;
+              }
+            } else if (ok) {
+              zl[j * nout + r] = x;
+              aout[j * nout + r] = silu(x);
+            }
+          });
+    }
+    for (int l = L - 1; l >= 1; --l) {
+      const int nl = p.w[l], nu = p.w[l + 1];
+      const float* Wu = W + p.off[l + 1];
+      const float* du = V(y.dl[l + 1]);
+      const float* zl = V(y.z[l]);
+      float* bl = V(y.bv[l]);
+      float* dl = V(y.dl[l]);
+      block_gemm<true>(
+          n, nl, nu, [=](int j, int r) { return du[j * nu + r]; },
+          [=](int r, int cc) { return Wu[(int64_t)r * nl + cc]; }, kB_NMAJOR,
+          [=](int j, int cc, float x, bool ok) {
+            const float zz = zl[j * nl + cc];
+            if (ok) {
+              bl[j * nl + cc] = x;
+              dl[j * nl + cc] = x * dsilu(zz);
+            }
+          });
+    }
+
+    // ---- the reads, forward (what their backward needs) ----
+    if (reads) {
+      for (int l = 1; l <= L; ++l) {
+        const int nin = p.w[l - 1], nout = p.w[l];
+        const float* Wl = W + p.off[l];
+        const float* Sl = S + p.off[l];
+        const float* h = V(y.h[l - 1]);
+        float* hn = V(y.h[l < L ? l : 0]);
+        float* zq = V(y.zq[l < L ? l : 1]);
+        if (cstart) {
+          if (l == L) break;
+          block_gemm<true>(
+              n, nout, nin, [=](int t, int cc) { return h[t * nin + cc]; },
+              [=](int cc, int r) { return Wl[(int64_t)r * nin + cc]; }, kB_KMAJOR,
+              [=](int t, int r, float x, bool ok) {
+                if (ok) {
+                  zq[t * nout + r] = x;
+                  hn[t * nout + r] = silu(x);
+                }
+              });
+          continue;
+        }
+        const float* ak = V(y.act[l - 1]);
+        float* sc = V(y.sc[l]);
+        float* uw = V(y.uw[l]);
+        float* us = V(y.us[l]);
+        block_gemm<true>(
+            n, n, nin, [=](int t, int cc) { return h[t * nin + cc]; },
+            [=](int cc, int i) { return ak[i * nin + cc]; }, kB_KMAJOR,
+            [=](int t, int i, float x, bool ok) {
+              if (ok) sc[t * bb + i] = x;
+            });
+        block_gemm<true>(
+            n, nout, nin, [=](int t, int cc) { return h[t * nin + cc]; },
+            [=](int cc, int r) { return Wl[(int64_t)r * nin + cc]; }, kB_KMAJOR,
+            [=](int t, int r, float x, bool ok) {
+              if (ok) uw[t * nout + r] = x;
+            });
+        block_gemm<true>(
+            n, nout, nin, [=](int t, int cc) { return h[t * nin + cc]; },
+            [=](int cc, int r) { return Sl[(int64_t)r * nin + cc]; }, kB_KMAJOR,
+            [=](int t, int r, float x, bool ok) {
+              if (ok) us[t * nout + r] = x;
+            });
+        if (l == L) break;
+        // zq = A uw + F us - (D o sc) delta
+        const float* dl = V(y.dl[l]);
+        block_gemm<true>(
+            n, nout, n,
+            [=](int t, int i) {
+              const float dv = cD[t * bb + i], sv = sc[t * bb + i];
+              return i <= t ? dv * sv : 0.f;
+            },
+            [=](int i, int r) { return dl[i * nout + r]; }, kB_NMAJOR,
+            [=](int t, int r, float x, bool ok) {
+              const float zv = cA[t] * uw[t * nout + r] + cF[t] * us[t * nout + r] - x;
+              if (ok) {
+                zq[t * nout + r] = zv;
+                hn[t * nout + r] = silu(zv);
+              }
+            });
+      }
+
+      // ---- the reads, backward (top layer down) ----
+      for (int l = L; l >= 1; --l) {
+        const int nin = p.w[l - 1], nout = p.w[l];
+        const float* Wl = W + p.off[l];
+        const float* Sl = S + p.off[l];
+        const float* rho = V(y.rho[l]);
+        const float* h = V(y.h[l - 1]);
+        const bool first = l == 1;
+        float* rdn = V(y.rho[first ? l : l - 1]);        // used below layer 1 only
+        const float* zqd = V(y.zq[first ? 1 : l - 1]);   // used below layer 1 only
+        float* dqc = p.dq + row0 * d;
+        // hbar -> rho^{l-1} (or qbar)
+        auto hbar_epi = [=](int t, int cc, float x, bool ok) {
+          if (first) {
+            if (ok) dqc[t * d + cc] = x;
+          } else {
+            const float zz = zqd[t * nin + cc];
+            if (ok) rdn[t * nin + cc] = x * dsilu(zz);
+          }
+        };
+        if (cstart) {
+          block_gemm<true>(
+              n, nin, nout, [=](int t, int r) { return rho[t * nout + r]; },
+              [=](int r, int cc) { return Wl[(int64_t)r * nin + cc]; }, kB_NMAJOR, hbar_epi);
+          continue;
+        }
+        const float* uw = V(y.uw[l]);
+        const float* us = V(y.us[l]);
+        const float* sc = V(y.sc[l]);
+        const float* dl = V(y.dl[l]);
+        row_dots(Abar, rho, nout, uw, nout, n, nout);
+        row_dots(Fbar, rho, nout, us, nout, n, nout);
+        // R = rho delta^T: Dbar, and the masked products -D o R, -D o sc
+        block_gemm<true>(
+            n, n, nout, [=](int t, int r) { return rho[t * nout + r]; },
+            [=](int r, int i) { return dl[i * nout + r]; }, kB_KMAJOR,
+            [=](int t, int i, float x, bool ok) {
+              const int64_t e = (int64_t)t * bb + i;
+              const float dv = cD[e], sv = sc[e], db = Dbar[e];
+              const bool lo = i <= t;
+              if (ok) {
+                dr[e] = lo ? -dv * x : 0.f;
+                dsc[e] = lo ? -dv * sv : 0.f;
+                Dbar[e] = lo ? db - x * sv : db;
+              }
+            });
+        // hbar = [A rho | F rho | -D o R] x [W; S; a^{l-1}]
+        const float* ak = V(y.act[l - 1]);
+        block_gemm<true>(
+            n, nin, 2 * nout + n,
+            [=](int t, int kk) {
+              const bool st = kk < 2 * nout;
+              const float* x = st ? rho + t * nout + (kk < nout ? kk : kk - nout) : dr + (int64_t)t * bb + (kk - 2 * nout);
+              const float f = *(kk < nout ? cA + t : cF + t);
+              const float v = *x;
+              return st ? f * v : v;
+            },
+            [=](int kk, int cc) {
+              const float* x = kk < nout       ? Wl + (int64_t)kk * nin + cc
+                               : kk < 2 * nout ? Sl + (int64_t)(kk - nout) * nin + cc
+                                               : ak + (int64_t)(kk - 2 * nout) * nin + cc;
+              return *x;
+            },
+            kB_NMAJOR, hbar_epi);
+        // deltabar^l += (-D o sc)^T rho,  abar^{l-1} += (-D o R)^T h^{l-1}
+        float* dbl = V(y.dbar[l]);
+        float* abl = V(y.abar[l - 1]);
+        block_gemm<false>(
+            n, nout, n, [=](int i, int t) { return dsc[(int64_t)t * bb + i]; },
+            [=](int t, int r) { return rho[t * nout + r]; }, kB_NMAJOR,
+            [=](int i, int r, float x, bool ok) {
+              const float o = dbl[i * nout + r];
+              if (ok) dbl[i * nout + r] = o + x;
+            });
+        block_gemm<false>(
+            n, nin, n, [=](int i, int t) { return dr[(int64_t)t * bb + i]; },
+            [=](int t, int cc) { return h[t * nin + cc]; }, kB_NMAJOR,
+            [=](int i, int cc, float x, bool ok) {
+              const float o = abl[i * nin + cc];
+              if (ok) abl[i * nin + cc] = o + x;
+            });
+      }
+    }
+
+    // ---- the fold's adjoint (Wbar, Sbar of the chunk end) ----
+    for (int l = 1; l <= L; ++l) {
+      const int nin = p.w[l - 1], nout = p.w[l];
+      const float* Wbl = Wb + p.off[l];
+      const float* Sbl = Sb + p.off[l];
+      const float* ak = V(y.act[l - 1]);
+      const float* dl = V(y.dl[l]);
+      float* dbl = V(y.dbar[l]);
+      float* abl = V(y.abar[l - 1]);
+      const float* Dn = cD + (int64_t)(n - 1) * bb;
+      block_gemm<true>(
+          n, nout, nin, [=](int i, int cc) { return ak[i * nin + cc]; },
+          [=](int cc, int r) { return Wbl[(int64_t)r * nin + cc]; }, kB_KMAJOR,
+          [=](int i, int r, float x, bool ok) {
+            if (ok) xw[i * mw + r] = x;
+          });
+      block_gemm<true>(
+          n, nout, nin, [=](int i, int cc) { return ak[i * nin + cc]; },
+          [=](int cc, int r) { return Sbl[(int64_t)r * nin + cc]; }, kB_KMAJOR,
+          [=](int i, int r, float x, bool ok) {
+            if (ok) xs[i * mw + r] = x;
+          });
+      // deltabar_i -= D[n-1,i] xw_i + U_i xs_i;  Dbar[n-1,i], Ubar_i from delta_i . (xw_i, xs_i)
+      {
+        const int lane = tid & 63, wv = tid >> 6;
+        for (int i = wv; i < n; i += kBW) {
+          const float dn = Dn[i], ui = cU[i];
+          float s1 = 0.f, s2 = 0.f;
+          for (int r = lane; r < nout; r += 64) {
+            const float x1 = xw[i * mw + r], x2 = xs[i * mw + r], dv = dl[i * nout + r];
+            dbl[i * nout + r] -= dn * x1 + ui * x2;
+            s1 += dv * x1;
+            s2 += dv * x2;
+          }
+          s1 = wave_sum(s1);
+          s2 = wave_sum(s2);
+          if (lane == 0) {
+            Dbar[(int64_t)(n - 1) * bb + i] -= s1;
+            Ubar[i] -= s2;
+          }
+        }
+      }
+      // abar^{l-1} -= [D[n-1,i] delta_i | U_i delta_i] x [Wbar; Sbar]
+      block_gemm<true>(
+          n, nin, 2 * nout,
+          [=](int i, int kk) {
+            const float f = *(kk < nout ? Dn + i : cU + i);
+            return -f * dl[i * nout + (kk < nout ? kk : kk - nout)];
+          },
+          [=](int kk, int cc) {
+            return *(kk < nout ? Wbl + (int64_t)kk * nin + cc : Sbl + (int64_t)(kk - nout) * nin + cc);
+          },
+          kB_NMAJOR,
+          [=](int i, int cc, float x, bool ok) {
+            const float o = abl[i * nin + cc];
+            if (ok) abl[i * nin + cc] = o + x;
+          });
+    }
+
+    // ---- backward of the inner gradient (second-order terms) ----
+    for (int l = 1; l < L; ++l) {
+      const int nl = p.w[l], nu = p.w[l + 1];
+      const float* dbl = V(y.dbar[l]);
+      const float* zl = V(y.z[l]);
+      const float* bl = V(y.bv[l]);
+      float* bbl = V(y.bbar[l]);
+      float* zbl = V(y.zbar[l]);
+      for (int e = tid; e < n * nl; e += kBT) {
+        const float db = dbl[e], zz = zl[e];
+        bbl[e] = db * dsilu(zz);
+        zbl[e] = db * bl[e] * d2silu(zz);
+      }
+      __syncthreads();
+      const float* Wu = W + p.off[l + 1];
+      float* dbu = V(y.dbar[l + 1]);
+      block_gemm<true>(
+          n, nu, nl, [=](int i, int cc) { return bbl[i * nl + cc]; },
+          [=](int cc, int r) { return Wu[(int64_t)r * nl + cc]; }, kB_KMAJOR,
+          [=](int i, int r, float x, bool ok) {
+            const float o = dbu[i * nu + r];
+            if (ok) dbu[i * nu + r] = o + x;
+          });
+    }
+    {
+      const float* dbL = V(y.dbar[L]);
+      for (int e = tid; e < n * d; e += kBT) p.dv[row0 * d + e] = -dbL[e];
+    }
+    for (int l = L; l >= 1; --l) {
+      const int nin = p.w[l - 1], nout = p.w[l];
+      float* zbl = l == L ? V(y.dbar[L]) : V(y.zbar[l]);
+      if (l < L) {
+        const float* abl = V(y.abar[l]);
+        const float* zl = V(y.z[l]);
+        for (int e = tid; e < n * nout; e += kBT) zbl[e] += abl[e] * dsilu(zl[e]);
+        __syncthreads();
+      }
+      const float* Wl = W + p.off[l];
+      float* abd = V(y.abar[l - 1]);
+      block_gemm<true>(
+          n, nin, nout, [=](int i, int r) { return zbl[i * nout + r]; },
+          [=](int r, int cc) { return Wl[(int64_t)r * nin + cc]; }, kB_NMAJOR,
+          [=](int i, int cc, float x, bool ok) {
+            const float o = abd[i * nin + cc];
+            if (ok) abd[i * nin + cc] = o + x;
+          });
+    }
+    {
+      const float* ab0 = V(y.abar[0]);
+      for (int e = tid; e < n * d; e += kBT) p.dk[row0 * d + e] = ab0[e];
+    }
+
+    // ---- state adjoints: Sbar, then Wbar (both read the chunk-end Wbar) ----
+    const float An = cA[n - 1], En = cE[n - 1], Fn = cF[n - 1];
+    float sWW = 0.f, sWS = 0.f, sSS = 0.f;   // <Wbar, W>, <Wbar, S>, <Sbar, S>
+    for (int l = 1; l <= L; ++l) {
+      const int nin = p.w[l - 1], nout = p.w[l];
+      float* Wbl = Wb + p.off[l];
+      float* Sbl = Sb + p.off[l];
+      const float* Wl = W + p.off[l];
+      const float* Sl = S + p.off[l];
+      const float* rho = V(y.rho[l]);
+      const float* h = V(y.h[l - 1]);
+      auto sbar_epi = [&](int r, int cc, float x, bool ok) {
+        const int64_t e = (int64_t)r * nin + cc;
+        const float wbv = Wbl[e], sbv = Sbl[e], wv = Wl[e], sv = Sl[e];
+        if (ok) {
+          Sbl[e] = Fn * wbv + En * sbv + x;
+          sWW += wbv * wv;
+          sWS += wbv * sv;
+          sSS += sbv * sv;
+        }
+      };
+      if (reads && !cstart) {
+        block_gemm<false>(
+            nout, nin, n, [=](int r, int t) { return cF[t] * rho[t * nout + r]; },
+            [=](int t, int cc) { return h[t * nin + cc]; }, kB_NMAJOR, sbar_epi);
+      } else {
+        for (int e = tid; e < nout * nin; e += kBT) sbar_epi(e / nin, e % nin, 0.f, true);
+        __syncthreads();
+      }
+      // Wbar <- A_{n-1} Wbar + [rho-part | delta-bbar part | zbar-a part]
+      const int kt = reads ? n : 0;
+      const int kd = l >= 2 ? n : 0;
+      const float* dl = V(y.dl[l]);
+      const float* ak = V(y.act[l - 1]);
+      const float* bbd = l >= 2 ? V(y.bbar[l - 1]) : ak;   // unused below layer 2
+      const float* zbl = l == L ? V(y.dbar[L]) : V(y.zbar[l]);
+      const bool unit_t = cstart;
+      block_gemm<false>(
+          nout, nin, kt + kd + n,
+          [=](int r, int kk) {
+            const bool pt = kk < kt, pd = !pt && kk < kt + kd;
+            const int i = pt ? kk : pd ? kk - kt : kk - kt - kd;
+            const float* x = pt ? rho + i * nout + r : pd ? dl + i * nout + r : zbl + i * nout + r;
+            const float f = (pt && !unit_t) ? cA[i] : 1.f;
+            return f * *x;
+          },
+          [=](int kk, int cc) {
+            const bool pt = kk < kt, pd = !pt && kk < kt + kd;
+            const int i = pt ? kk : pd ? kk - kt : kk - kt - kd;
+            const float* x = pt ? h + i * nin + cc : pd ? bbd + i * nin + cc : ak + i * nin + cc;
+            return *x;
+          },
+          kB_NMAJOR,
+          [=](int r, int cc, float x, bool ok) {
+            const int64_t e = (int64_t)r * nin + cc;
+            const float o = Wbl[e];
+            if (ok) Wbl[e] = An * o + x;
+          });
+    }
+    sWW = block_sum(sWW, red);
+    sWS = block_sum(sWS, red);
+    sSS = block_sum(sSS, red);
+
+    // ---- gate gradients: the coefficient adjoints back through their recurrences ----
+    if (tid == 0) {
+      Abar[n - 1] += sWW;
+      Fbar[n - 1] += sWS;
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += kBT) {
+      // column i of D and P (t > i), and U_i = theta_i P[n-1,i]
+      const float ti = th[i * gs];
+      float tb = cP[(int64_t)(n - 1) * bb + i] * Ubar[i];
+      float dacc = 0.f, pacc = ti * Ubar[i];
+      for (int t = n - 1; t > i; --t) {
+        const int64_t e = (int64_t)t * bb + i, em = e - bb;
+        dacc += Dbar[e];
+        Ca[e] = -cD[em] * dacc;                 // D[t,i] = (1 - alpha_t) D[t-1,i] + theta_i P[t,i]
+        tb += cP[e] * dacc;
+        pacc += ti * dacc;
+        Ce[e] = cP[em] * pacc;                  // P[t,i] = eta_t P[t-1,i]
+        pacc *= et[t * gs];
+        dacc *= 1.f - al[t * gs];
+      }
+      dacc += Dbar[(int64_t)i * bb + i];
+      gt[i] = tb + dacc;                        // D[i,i] = theta_i
+    }
+    if (tid == 0) {
+      float abar = 0.f, fbar = 0.f, ebar = sSS;
+      for (int t = n - 1; t >= 0; --t) {
+        const float am = t > 0 ? cA[t - 1] : 1.f, em = t > 0 ? cE[t - 1] : 1.f, fm = t > 0 ? cF[t - 1] : 0.f;
+        const float a1 = 1.f - al[t * gs];
+        abar += Abar[t];
+        fbar += Fbar[t];
+        ebar += fbar;                           // F_t = (1 - alpha_t) F_{t-1} + E_t
+        ga[t] = -am * abar - fm * fbar;         // A_t = (1 - alpha_t) A_{t-1}
+        ge[t] = em * ebar;                      // E_t = eta_t E_{t-1}
+        abar *= a1;
+        fbar *= a1;
+        ebar *= et[t * gs];
+      }
+    }
+    __syncthreads();
+    {
+      const int lane = tid & 63, wv = tid >> 6;
+      for (int t = wv; t < n; t += kBW) {
+        float sa = 0.f, se = 0.f;
+        for (int i = lane; i < t; i += 64) {
+          sa += Ca[(int64_t)t * bb + i];
+          se += Ce[(int64_t)t * bb + i];
+        }
+        sa = wave_sum(sa);
+        se = wave_sum(se);
+        if (lane == 0) {
+          ga[t] += sa;
+          ge[t] += se;
+        }
+      }
+    }
+    __syncthreads();
+    if (p.chunk_gates) {
+      float sa = 0.f, se = 0.f, st = 0.f;
+      for (int t = tid; t < n; t += kBT) {
+        sa += ga[t];
+        se += ge[t];
+        st += gt[t];
+      }
+      sa = block_sum(sa, red);
+      se = block_sum(se, red);
+      st = block_sum(st, red);
+      if (tid == 0) {
+        p.dalpha[g0] = sa;
+        p.deta[g0] = se;
+        p.dtheta[g0] = st;
+      }
+    } else {
+      for (int t = tid; t < n; t += kBT) {
+        p.dalpha[g0 + t] = ga[t];
+        p.deta[g0 + t] = ge[t];
+        p.dtheta[g0 + t] = gt[t];
+      }
+    }
+    __syncthreads();
   }
 }
+
+BwLayout bw_layout(const Shape& s, int b) {
+  BwLayout y{};
+  int64_t cur = 0;
+  auto take = [&](int64_t n) {
+    const int64_t o = cur;
+    cur += (n + 3) / 4 * 4;
+    return o;
+  };
+  const int L = s.L;
+  for (int l = 0; l <= L; ++l) y.act[l] = take((int64_t)b * s.widths[l]);
+  for (int l = 1; l < L; ++l) y.z[l] = take((int64_t)b * s.widths[l]);
+  for (int l = 1; l <= L; ++l) y.dl[l] = take((int64_t)b * s.widths[l]);
+  for (int l = 1; l < L; ++l) y.bv[l] = take((int64_t)b * s.widths[l]);
+  for (int l = 0; l < L; ++l) y.h[l] = take((int64_t)b * s.widths[l]);
+  for (int l = 1; l < L; ++l) y.zq[l] = take((int64_t)b * s.widths[l]);
+  for (int l = 1; l <= L; ++l) y.uw[l] = take((int64_t)b * s.widths[l]);
+  for (int l = 1; l <= L; ++l) y.us[l] = take((int64_t)b * s.widths[l]);
+  for (int l = 1; l <= L; ++l) y.rho[l] = take((int64_t)b * s.widths[l]);
+  for (int l = 1; l <= L; ++l) y.sc[l] = take((int64_t)b * b);
+  for (int l = 1; l <= L; ++l) y.dbar[l] = take((int64_t)b * s.widths[l]);
+  for (int l = 0; l < L; ++l) y.abar[l] = take((int64_t)b * s.widths[l]);
+  for (int l = 1; l < L; ++l) y.bbar[l] = take((int64_t)b * s.widths[l]);
+  for (int l = 1; l < L; ++l) y.zbar[l] = take((int64_t)b * s.widths[l]);
+  y.vin = take((int64_t)b * s.d);
+  y.xw = take((int64_t)b * s.maxw);
+  y.xs = take((int64_t)b * s.maxw);
+  y.dsc = take((int64_t)b * b);
+  y.dr = take((int64_t)b * b);
+  y.D = take((int64_t)b * b);
+  y.P = take((int64_t)b * b);
+  y.Dbar = take((int64_t)b * b);
+  y.Ca = take((int64_t)b * b);
+  y.Ce = take((int64_t)b * b);
+  y.A = take(b);
+  y.E = take(b);
+  y.F = take(b);
+  y.U = take(b);
+  y.Abar = take(b);
+  y.Fbar = take(b);
+  y.Ubar = take(b);
+  y.ga = take(b);
+  y.ge = take(b);
+  y.gt = take(b);
+  y.red = take(64);
+  y.total = cur;
+  return y;
+}
+
+int rows_per_chunk(const Shape& s, int chunk) { return chunk < s.N ? chunk : s.N; }
 
 }  // namespace
 
@@ -511,24 +779,16 @@ bool backward_supported(const Shape& s, int chunk) {
   if (s.maxw > kMaxWidthBackward) return false;
   for (int l = 0; l <= s.L; ++l)
     if (s.widths[l] % 4 != 0) return false;
-  return backward_lds_bytes(s) <= 160 * 1024;
-}
-
-int backward_lds_bytes(const Shape& s) {
-  int sumn = 0;
-  for (int l = 1; l <= s.L; ++l) sumn += s.widths[l];
-  // run_chunk: xk, z, a, delta, b, red; reverse sweep: xq, qz, qa, v1, v2, up, db, zb, zs, rp, dzq, ee
-  const int floats = s.maxw + 4 * sumn + kBT * 4 + 3 * s.maxw + 8 * sumn + s.L * s.maxw;
-  return floats * 4;
+  return true;
 }
 
 int64_t backward_ws_floats_per_stream(const Shape& s, int chunk) {
-  const int nchunks = (s.N + chunk - 1) / chunk;
-  const int b = chunk < s.N ? chunk : s.N;
-  int sumn = 0;
-  for (int l = 1; l <= s.L; ++l) sumn += s.widths[l];
-  return (int64_t)nchunks * 2 * s.P + 2 * (int64_t)b * s.P + (int64_t)b * 3 * sumn + 3 * s.P +
-         (generic_ws_floats_per_stream(s, b) + 3) / 4 * 4 + 64;
+  const int64_t nchunks = (s.N + chunk - 1) / chunk;
+  const int b = rows_per_chunk(s, chunk);
+  // the forward sweep's workspace and the reverse sweep's region share the
+  // space after the checkpoints (the sweep ends before the reverse starts)
+  const int64_t region = std::max(bw_layout(s, b).total, generic_ws_floats_per_stream(s, b));
+  return nchunks * 2 * s.P + (region + 63) / 64 * 64;
 }
 
 hipError_t launch_backward(const Shape& s, int chunk, const void* k, const void* v, const void* q,
@@ -536,11 +796,11 @@ hipError_t launch_backward(const Shape& s, int chunk, const void* k, const void*
                            const float* S_in, const float* dy, const float* dW_out, const float* dS_out, float* dk,
                            float* dv, float* dq, float* dalpha, float* deta, float* dtheta, float* dW_in,
                            float* dS_in, float* ws, hipStream_t stream) {
-  BwdParams p;
+  BwdParams p{};
   p.N = s.N;
   p.chunk = chunk;
   p.nchunks = (s.N + chunk - 1) / chunk;
-  p.streams = s.streams;
+  p.b = rows_per_chunk(s, chunk);
   p.L = s.L;
   p.d = s.d;
   p.io = s.io;
@@ -550,42 +810,22 @@ hipError_t launch_backward(const Shape& s, int chunk, const void* k, const void*
   for (int l = 1; l <= s.L; ++l) p.off[l] = s.off[l];
   p.P = s.P;
   p.maxw = s.maxw;
-  int zo = 0;
-  for (int l = 1; l <= s.L; ++l) {
-    p.zo[l] = zo;
-    zo += s.widths[l];
-  }
-  p.sumn = zo;
-  p.zo[0] = 0;
   p.k = k; p.v = v; p.q = q;
   p.alpha = alpha; p.eta = eta; p.theta = theta;
-  p.W_in = W_in; p.S_in = S_in;
   p.dy = dy; p.dW_out = dW_out; p.dS_out = dS_out;
   p.dk = dk; p.dv = dv; p.dq = dq;
   p.dalpha = dalpha; p.deta = deta; p.dtheta = dtheta;
   p.dW_in = dW_in; p.dS_in = dS_in;
   p.ws = ws;
   p.ws_stream = backward_ws_floats_per_stream(s, chunk);
-  const int b = chunk < s.N ? chunk : s.N;
-  p.o_cw = (int64_t)p.nchunks * 2 * s.P;
-  p.o_cs = p.o_cw + (int64_t)b * s.P;
-  p.o_tv = p.o_cs + (int64_t)b * s.P;
-  p.o_wb = p.o_tv + ((int64_t)b * 3 * p.sumn + 3) / 4 * 4;
-  p.o_sb = p.o_wb + s.P;
-  p.o_wcb = p.o_sb + s.P;
-  const int64_t o_gen = p.o_wcb + s.P;
-  // forward sweep: the chunk-start states, through the generic kernel's
-  // chunked form (its running state lives in this stream's Wbar, Sbar slots,
-  // which the reverse sweep then initialises)
-  hipError_t err = launch_generic_checkpoints(s, chunk, k, v, q, alpha, eta, theta, W_in, S_in, ws + p.o_wb,
-                                              ws + p.o_sb, p.ws_stream, ws, p.ws_stream, ws + o_gen, p.ws_stream,
-                                              stream);
+  p.o_buf = (int64_t)p.nchunks * 2 * s.P;
+  p.lay = bw_layout(s, p.b);
+  // forward sweep: the chunk-start states into the checkpoints; its running
+  // state lives in dW_in, dS_in (re-initialised by the reverse sweep)
+  hipError_t err = launch_generic_checkpoints(s, chunk, k, v, q, alpha, eta, theta, W_in, S_in, dW_in, dS_in, s.P,
+                                              ws, p.ws_stream, ws + p.o_buf, p.ws_stream, stream);
   if (err != hipSuccess) return err;
-  const int lds = backward_lds_bytes(s);
-  p.lds_floats = lds / 4;
-  err = hipFuncSetAttribute((const void*)backward_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(backward_kernel, dim3(s.streams), dim3(kBT), lds, stream, p);
+  hipLaunchKernelGGL(backward_kernel, dim3(s.streams), dim3(kBT), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -57,7 +57,6 @@ hipError_t launch_generic_checkpoints(const Shape& s, int chunk, const void* k, 
 // Backward pass through the memory (generic fp32, one workgroup per stream).
 constexpr int kMaxWidthBackward = 1024;
 bool backward_supported(const Shape& s, int chunk);
-int backward_lds_bytes(const Shape& s);
 int64_t backward_ws_floats_per_stream(const Shape& s, int chunk);
 hipError_t launch_backward(const Shape& s, int chunk, const void* k, const void* v, const void* q,
                            const float* alpha, const float* eta, const float* theta, const float* W_in,
