@@ -147,19 +147,23 @@ def bench_input_side(args, np, torch, tmm, wl):
 
 
 def backward_flops_per_token(cfg):
-    """Algorithmic FLOPs of titans_mem_backward per memory token: the chunked
-    state sweep that yields the chunk-start states (key forward, backprop
-    and the two weighted reductions), the reverse sweep's per-token
-    recomputation (key forward, backprop, state update), the retrieval
-    forward and backward, the gate inner products, and the Hessian-vector
-    term (the inner backward's own backward pass): 43 P - 8 d n_1."""
+    """Algorithmic FLOPs of titans_mem_backward per memory token, with dL/dy
+    given and the read after each write: the chunked state sweep that yields
+    the chunk-start states (key forward, backprop, the two weighted
+    reductions: 8 P - 2 d n_1), and the chunk-wise reverse sweep's products
+    (key forward and backprop again, the reads' forward and backward, the
+    fold's adjoint, the inner gradient's backward pass and the two state
+    adjoints: 32 P - 6 d n_1), plus the [b x b] score products of the reads,
+    b per token times 2 (sum_l n_{l-1} + sum_{l<L} n_l) + 4 sum_l (n_l + n_{l-1})."""
     w = cfg.widths
+    L = len(w) - 1
     P = cfg.param_count
     first = w[0] * w[1]
-    sweep = 2 * (4 * P - first)
-    run_chunk = 10 * P - 2 * first
-    reverse = 25 * P - 4 * first
-    return sweep + run_chunk + reverse
+    b = min(cfg.chunk, cfg.N)
+    sweep = 8 * P - 2 * first
+    reverse = 32 * P - 6 * first
+    scores = b * (2 * (sum(w[:L]) + sum(w[1:L])) + 4 * sum(w[l] + w[l - 1] for l in range(1, L + 1)))
+    return sweep + reverse + scores
 
 
 def bench_backward(args, np, torch, tmm, wl, prefix=1024, steps=3):
@@ -197,7 +201,7 @@ def bench_backward(args, np, torch, tmm, wl, prefix=1024, steps=3):
     achieved = flops / launch_s / 1e12
     res = {"workload": f"{cfg.name} (first {prefix} tokens of every stream)", "value": tokens / (wall / steps),
            "unit": "memory-tokens/s", "ms_per_step": wall * 1e3 / steps, "dtype": "f32", "steps": steps,
-           "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
+           "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
                         "frac": achieved / PEAK_TFLOPS["f32"], "traffic": None,
                         "algorithmic_flops_per_launch": flops, "avg_launch_ms": launch_s * 1e3}}
     print(f"[bench] backward {cfg.name}, {prefix} tokens: {launch_s * 1e3:.1f} ms/launch, "

@@ -286,9 +286,9 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
       block_gemm<true>(
           n, nout, nin, [=](int j, int cc) { return ain[j * nin + cc]; },
           [=](int cc, int r) { return Wl[(int64_t)r * nin + cc]; }, kB_KMAJOR,
-          [=](int j, int r, float x, bool ok) {
+          [=](int j, int r) { return last ? vin[j * nout + r] : 0.f; },
+          [=](int j, int r, float x, float vv, bool ok) {
             if (last) {
-              const float vv = vin[j * nout + r];
               if (ok) {
                 aout[j * nout + r] = x;
                 dl[j * nout + r] = x - vv;
@@ -309,8 +309,8 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
       block_gemm<true>(
           n, nl, nu, [=](int j, int r) { return du[j * nu + r]; },
           [=](int r, int cc) { return Wu[(int64_t)r * nl + cc]; }, kB_NMAJOR,
-          [=](int j, int cc, float x, bool ok) {
-            const float zz = zl[j * nl + cc];
+          [=](int j, int cc) { return zl[j * nl + cc]; },
+          [=](int j, int cc, float x, float zz, bool ok) {
             if (ok) {
               bl[j * nl + cc] = x;
               dl[j * nl + cc] = x * dsilu(zz);
@@ -372,8 +372,9 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
               return i <= t ? dv * sv : 0.f;
             },
             [=](int i, int r) { return dl[i * nout + r]; }, kB_NMAJOR,
-            [=](int t, int r, float x, bool ok) {
-              const float zv = cA[t] * uw[t * nout + r] + cF[t] * us[t * nout + r] - x;
+            [=](int t, int r) { return cA[t] * uw[t * nout + r] + cF[t] * us[t * nout + r]; },
+            [=](int t, int r, float x, float base, bool ok) {
+              const float zv = base - x;
               if (ok) {
                 zq[t * nout + r] = zv;
                 hn[t * nout + r] = silu(zv);
@@ -393,18 +394,18 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
         const float* zqd = V(y.zq[first ? 1 : l - 1]);   // used below layer 1 only
         float* dqc = p.dq + row0 * d;
         // hbar -> rho^{l-1} (or qbar)
-        auto hbar_epi = [=](int t, int cc, float x, bool ok) {
+        auto hbar_pre = [=](int t, int cc) { return first ? 0.f : zqd[t * nin + cc]; };
+        auto hbar_epi = [=](int t, int cc, float x, float zz, bool ok) {
           if (first) {
             if (ok) dqc[t * d + cc] = x;
-          } else {
-            const float zz = zqd[t * nin + cc];
-            if (ok) rdn[t * nin + cc] = x * dsilu(zz);
+          } else if (ok) {
+            rdn[t * nin + cc] = x * dsilu(zz);
           }
         };
         if (cstart) {
           block_gemm<true>(
               n, nin, nout, [=](int t, int r) { return rho[t * nout + r]; },
-              [=](int r, int cc) { return Wl[(int64_t)r * nin + cc]; }, kB_NMAJOR, hbar_epi);
+              [=](int r, int cc) { return Wl[(int64_t)r * nin + cc]; }, kB_NMAJOR, hbar_pre, hbar_epi);
           continue;
         }
         const float* uw = V(y.uw[l]);
@@ -417,9 +418,13 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
         block_gemm<true>(
             n, n, nout, [=](int t, int r) { return rho[t * nout + r]; },
             [=](int r, int i) { return dl[i * nout + r]; }, kB_KMAJOR,
-            [=](int t, int i, float x, bool ok) {
+            [=](int t, int i) {
               const int64_t e = (int64_t)t * bb + i;
-              const float dv = cD[e], sv = sc[e], db = Dbar[e];
+              return make_float3(cD[e], sc[e], Dbar[e]);
+            },
+            [=](int t, int i, float x, float3 pv, bool ok) {
+              const int64_t e = (int64_t)t * bb + i;
+              const float dv = pv.x, sv = pv.y, db = pv.z;
               const bool lo = i <= t;
               if (ok) {
                 dr[e] = lo ? -dv * x : 0.f;
@@ -444,22 +449,22 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
                                                : ak + (int64_t)(kk - 2 * nout) * nin + cc;
               return *x;
             },
-            kB_NMAJOR, hbar_epi);
+            kB_NMAJOR, hbar_pre, hbar_epi);
         // deltabar^l += (-D o sc)^T rho,  abar^{l-1} += (-D o R)^T h^{l-1}
         float* dbl = V(y.dbar[l]);
         float* abl = V(y.abar[l - 1]);
         block_gemm<false>(
             n, nout, n, [=](int i, int t) { return dsc[(int64_t)t * bb + i]; },
             [=](int t, int r) { return rho[t * nout + r]; }, kB_NMAJOR,
-            [=](int i, int r, float x, bool ok) {
-              const float o = dbl[i * nout + r];
+            [=](int i, int r) { return dbl[i * nout + r]; },
+            [=](int i, int r, float x, float o, bool ok) {
               if (ok) dbl[i * nout + r] = o + x;
             });
         block_gemm<false>(
             n, nin, n, [=](int i, int t) { return dr[(int64_t)t * bb + i]; },
             [=](int t, int cc) { return h[t * nin + cc]; }, kB_NMAJOR,
-            [=](int i, int cc, float x, bool ok) {
-              const float o = abl[i * nin + cc];
+            [=](int i, int cc) { return abl[i * nin + cc]; },
+            [=](int i, int cc, float x, float o, bool ok) {
               if (ok) abl[i * nin + cc] = o + x;
             });
       }
@@ -518,8 +523,8 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
             return *(kk < nout ? Wbl + (int64_t)kk * nin + cc : Sbl + (int64_t)(kk - nout) * nin + cc);
           },
           kB_NMAJOR,
-          [=](int i, int cc, float x, bool ok) {
-            const float o = abl[i * nin + cc];
+          [=](int i, int cc) { return abl[i * nin + cc]; },
+          [=](int i, int cc, float x, float o, bool ok) {
             if (ok) abl[i * nin + cc] = o + x;
           });
     }
@@ -543,8 +548,8 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
       block_gemm<true>(
           n, nu, nl, [=](int i, int cc) { return bbl[i * nl + cc]; },
           [=](int cc, int r) { return Wu[(int64_t)r * nl + cc]; }, kB_KMAJOR,
-          [=](int i, int r, float x, bool ok) {
-            const float o = dbu[i * nu + r];
+          [=](int i, int r) { return dbu[i * nu + r]; },
+          [=](int i, int r, float x, float o, bool ok) {
             if (ok) dbu[i * nu + r] = o + x;
           });
     }
@@ -566,8 +571,8 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
       block_gemm<true>(
           n, nin, nout, [=](int i, int r) { return zbl[i * nout + r]; },
           [=](int r, int cc) { return Wl[(int64_t)r * nin + cc]; }, kB_NMAJOR,
-          [=](int i, int cc, float x, bool ok) {
-            const float o = abd[i * nin + cc];
+          [=](int i, int cc) { return abd[i * nin + cc]; },
+          [=](int i, int cc, float x, float o, bool ok) {
             if (ok) abd[i * nin + cc] = o + x;
           });
     }
@@ -587,9 +592,13 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
       const float* Sl = S + p.off[l];
       const float* rho = V(y.rho[l]);
       const float* h = V(y.h[l - 1]);
-      auto sbar_epi = [&](int r, int cc, float x, bool ok) {
+      auto sbar_pre = [=](int r, int cc) {
         const int64_t e = (int64_t)r * nin + cc;
-        const float wbv = Wbl[e], sbv = Sbl[e], wv = Wl[e], sv = Sl[e];
+        return make_float4(Wbl[e], Sbl[e], Wl[e], Sl[e]);
+      };
+      auto sbar_epi = [&](int r, int cc, float x, float4 pv, bool ok) {
+        const int64_t e = (int64_t)r * nin + cc;
+        const float wbv = pv.x, sbv = pv.y, wv = pv.z, sv = pv.w;
         if (ok) {
           Sbl[e] = Fn * wbv + En * sbv + x;
           sWW += wbv * wv;
@@ -600,9 +609,9 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
       if (reads && !cstart) {
         block_gemm<false>(
             nout, nin, n, [=](int r, int t) { return cF[t] * rho[t * nout + r]; },
-            [=](int t, int cc) { return h[t * nin + cc]; }, kB_NMAJOR, sbar_epi);
+            [=](int t, int cc) { return h[t * nin + cc]; }, kB_NMAJOR, sbar_pre, sbar_epi);
       } else {
-        for (int e = tid; e < nout * nin; e += kBT) sbar_epi(e / nin, e % nin, 0.f, true);
+        for (int e = tid; e < nout * nin; e += kBT) sbar_epi(e / nin, e % nin, 0.f, sbar_pre(e / nin, e % nin), true);
         __syncthreads();
       }
       // Wbar <- A_{n-1} Wbar + [rho-part | delta-bbar part | zbar-a part]
@@ -629,10 +638,9 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
             return *x;
           },
           kB_NMAJOR,
-          [=](int r, int cc, float x, bool ok) {
-            const int64_t e = (int64_t)r * nin + cc;
-            const float o = Wbl[e];
-            if (ok) Wbl[e] = An * o + x;
+          [=](int r, int cc) { return An * Wbl[(int64_t)r * nin + cc]; },
+          [=](int r, int cc, float x, float base, bool ok) {
+            if (ok) Wbl[(int64_t)r * nin + cc] = base + x;
           });
     }
     sWW = block_sum(sWW, red);

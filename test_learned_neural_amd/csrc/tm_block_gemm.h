@@ -30,13 +30,16 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 //
 // So that a wave keeps all of a slice's loads in flight at once, the
 // accessors and the epilogue are called unconditionally, with indices
-// clamped into range (M, N, K >= 1): fa(m, k), fb(k, n) and epi(m, n, value,
-// ok) must be branch-free reads of valid addresses; operands outside the
-// product are zeroed when staged, and epi stores only where ok is set.
+// clamped into range (M, N, K >= 1): fa(m, k) and fb(k, n) must be
+// branch-free reads of valid addresses; operands outside the product are
+// zeroed when staged.  The epilogue is split in two: pre(m, n) reads what
+// the element's update needs (any value type), epi(m, n, value, pre, ok)
+// stores, only where ok is set.
 constexpr int kGk = 32;                                   // k per staged slice
 constexpr int kGN = 2 * kGemmTile;                            // output columns per wide tile
 constexpr int kGPerA = kGemmTile * kGk / kGemmThreads;            // A elements per thread per slice
 constexpr int kGPerB = kGN * kGk / kGemmThreads;              // B elements per thread per wide slice
+constexpr int kEpiGroup = 8;                              // accumulator rows per epilogue group
 constexpr int kGemmLdsFloats = kGk * (kGemmTile + 1) + kGk * (kGN + 1);
 
 // one LDS allocation shared by every block_gemm instantiation of a kernel
@@ -45,8 +48,9 @@ __device__ __forceinline__ float* gemm_lds() {
   return buf;
 }
 
-template <bool A_KMAJOR, bool WIDE, class FA, class FB, class FBK, class FE>
-__device__ void block_gemm_tiles(int M, int N, int K, FA fa, FB fb, FBK bkmaj, FE epi) {
+template <bool A_KMAJOR, bool WIDE, class FA, class FB, class FBK, class FP, class FE>
+__device__ void block_gemm_tiles(int M, int N, int K, FA fa, FB fb, FBK bkmaj, FP pre, FE epi) {
+  using PreT = decltype(pre(0, 0));
   float* As = gemm_lds();                 // [kGk][kGemmTile + 1]
   float* Bs = As + kGk * (kGemmTile + 1);     // [kGk][kGN + 1]
   const int tid = threadIdx.x;
@@ -121,15 +125,28 @@ __device__ void block_gemm_tiles(int M, int N, int K, FA fa, FB fb, FBK bkmaj, F
         }
         __syncthreads();
       }
+      // epilogue in groups of kEpiGroup accumulator rows: every pre() read
+      // of a group is issued before its epi() stores (a store may alias a
+      // later element's read, so reads are never moved past it)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm + 8 * (r >> 2) + 4 * lk + (r & 3), n = n0 + wn + li;
-        const int mc = min(m, M - 1);
-        if constexpr (wide) {
-          epi(mc, min(n, N - 1), acc0[r], m < M && n < N);
-          epi(mc, min(n + 32, N - 1), acc1[r], m < M && n + 32 < N);
-        } else {
-          epi(mc, min(n, N - 1), acc0[r] + acc1[r], m < M && n < N);
+      for (int g = 0; g < 16; g += kEpiGroup) {
+        PreT pv0[kEpiGroup], pv1[kEpiGroup];
+#pragma unroll
+        for (int r = g; r < g + kEpiGroup; ++r) {
+          const int mc = min(m0 + wm + 8 * (r >> 2) + 4 * lk + (r & 3), M - 1), n = n0 + wn + li;
+          pv0[r - g] = pre(mc, min(n, N - 1));
+          if constexpr (wide) pv1[r - g] = pre(mc, min(n + 32, N - 1));
+        }
+#pragma unroll
+        for (int r = g; r < g + kEpiGroup; ++r) {
+          const int m = m0 + wm + 8 * (r >> 2) + 4 * lk + (r & 3), n = n0 + wn + li;
+          const int mc = min(m, M - 1);
+          if constexpr (wide) {
+            epi(mc, min(n, N - 1), acc0[r], pv0[r - g], m < M && n < N);
+            epi(mc, min(n + 32, N - 1), acc1[r], pv1[r - g], m < M && n + 32 < N);
+          } else {
+            epi(mc, min(n, N - 1), acc0[r] + acc1[r], pv0[r - g], m < M && n < N);
+          }
         }
       }
     }
@@ -137,12 +154,20 @@ __device__ void block_gemm_tiles(int M, int N, int K, FA fa, FB fb, FBK bkmaj, F
   __syncthreads();
 }
 
+template <bool A_KMAJOR, class FA, class FB, class FBK, class FP, class FE>
+__device__ void block_gemm(int M, int N, int K, FA fa, FB fb, FBK bkmaj, FP pre, FE epi) {
+  if (N > kGemmTile)
+    block_gemm_tiles<A_KMAJOR, true>(M, N, K, fa, fb, bkmaj, pre, epi);
+  else
+    block_gemm_tiles<A_KMAJOR, false>(M, N, K, fa, fb, bkmaj, pre, epi);
+}
+
+// the same with an epilogue that only stores: epi(m, n, value, ok)
 template <bool A_KMAJOR, class FA, class FB, class FBK, class FE>
 __device__ void block_gemm(int M, int N, int K, FA fa, FB fb, FBK bkmaj, FE epi) {
-  if (N > kGemmTile)
-    block_gemm_tiles<A_KMAJOR, true>(M, N, K, fa, fb, bkmaj, epi);
-  else
-    block_gemm_tiles<A_KMAJOR, false>(M, N, K, fa, fb, bkmaj, epi);
+  block_gemm<A_KMAJOR>(
+      M, N, K, fa, fb, bkmaj, [](int, int) { return 0.f; },
+      [=](int m, int n, float x, float, bool ok) { epi(m, n, x, ok); });
 }
 
 // the B slice's layout when it is the same for every slice

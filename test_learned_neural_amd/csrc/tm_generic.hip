@@ -200,9 +200,9 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
       block_gemm<true>(
           n, nout, nin, [=](int j, int c) { return ain[j * nin + c]; },
           [=](int c, int r) { return Wl[(int64_t)r * nin + c]; }, kB_KMAJOR,
-          [=](int j, int r, float z, bool ok) {
+          [=](int j, int r) { return last ? vin[j * nout + r] : 0.f; },
+          [=](int j, int r, float z, float vv, bool ok) {
             if (last) {
-              const float vv = vin[j * nout + r];
               if (ok) {
                 aout[j * nout + r] = z;
                 dl[j * nout + r] = z - vv;  // a3: residual M(k) - v
@@ -223,8 +223,8 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
       block_gemm<true>(
           n, nin, nout, [=](int j, int r) { return dl[j * nout + r]; },
           [=](int r, int c) { return Wl[(int64_t)r * nin + c]; }, kB_NMAJOR,
-          [=](int j, int c, float x, bool ok) {
-            const float sp = spp[j * nin + c];
+          [=](int j, int c) { return spp[j * nin + c]; },
+          [=](int j, int c, float x, float sp, bool ok) {
             if (ok) dprev[j * nin + c] = x * sp;
           });
     }
@@ -258,8 +258,8 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
         block_gemm<true>(
             n, n, nin, [=](int j, int c) { return h[j * maxw + c]; },
             [=](int c, int i) { return ak[i * nin + c]; }, kB_KMAJOR,
-            [=](int j, int i, float x, bool ok) {
-              const float dji = D[j * n + i];
+            [=](int j, int i) { return D[j * n + i]; },
+            [=](int j, int i, float x, float dji, bool ok) {
               if (ok) sc[j * n + i] = (i <= j) ? dji * x : 0.f;
             });
         const float* A = w.A;
@@ -300,18 +300,19 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
         block_gemm<false>(
             nout, nin, n, [=](int r, int j) { return Dlast[j] * dl[j * nout + r]; },
             [=](int j, int c) { return ak[j * nin + c]; }, kB_NMAJOR,
-            [=](int r, int c, float g, bool ok) {
+            [=](int r, int c) {
               const int64_t i = (int64_t)r * nin + c;
-              const float wi = Wl[i], si = Sl[i];
-              if (ok) Wl[i] = An * wi + Fn * si - g;
+              return An * Wl[i] + Fn * Sl[i];
+            },
+            [=](int r, int c, float g, float base, bool ok) {
+              if (ok) Wl[(int64_t)r * nin + c] = base - g;
             });
         block_gemm<false>(
             nout, nin, n, [=](int r, int j) { return U[j] * dl[j * nout + r]; },
             [=](int j, int c) { return ak[j * nin + c]; }, kB_NMAJOR,
-            [=](int r, int c, float g, bool ok) {
-              const int64_t i = (int64_t)r * nin + c;
-              const float si = Sl[i];
-              if (ok) Sl[i] = En * si - g;
+            [=](int r, int c) { return En * Sl[(int64_t)r * nin + c]; },
+            [=](int r, int c, float g, float base, bool ok) {
+              if (ok) Sl[(int64_t)r * nin + c] = base - g;
             });
       }
     }
