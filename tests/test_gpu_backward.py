@@ -4,8 +4,10 @@ The kernel is fp32 throughout, so the bar is the fp32 tolerance, 1e-3,
 norm-wise per stream for every gradient (dk, dv, dq, the three gates, dW_in,
 dS_in).  Cases: linear, 2- and 3-layer memories, both read modes, chunks
 from 1 to longer than the sequence, ragged tails, per-chunk gates, bf16
-inputs, each output adjoint alone, and the headline memory shape (d = 64,
-hidden = 256) on a short prefix.
+inputs, each output adjoint alone, the headline memory shape (d = 64,
+hidden = 256) on a short prefix, the benchmark's own launch (all 128
+headline streams over 1,024 tokens, two streams checked in full) and the
+4-layer d = 128 memory over 32 streams.
 """
 import numpy as np
 import pytest
@@ -125,3 +127,50 @@ def test_backward_headline_shape_prefix():
     """d = 64, hidden = 256, chunk 64 (the headline memory) on 96 tokens."""
     x, adj, P = _problem(205, 1, 2, 96, 64, 256, 2, io="bf16")
     _run(x, adj, 1, 2, 96, 64, 256, 2, 64, io="bf16")
+
+
+def _workload_run(cfg, sampled, chunk_gates=False):
+    """The backward over every stream of a workload configuration, as the
+    benchmark launches it, checked on sampled streams against the oracle."""
+    import torch
+    from test_learned_neural_amd import titans_mem as tmm
+    B, H, N, d, P = cfg.B, cfg.H, cfg.N, cfg.d, cfg.param_count
+    inp = wl.make_inputs(cfg, workers=16)
+    if cfg.io == "bf16":
+        tok = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).reshape(B, H, N, d).cuda()
+    else:
+        tok = lambda a: torch.from_numpy(a).reshape(B, H, N, d).cuda()
+    per = lambda a, n: torch.from_numpy(np.ascontiguousarray(a)).reshape(B, H, n).cuda()
+    rng = np.random.default_rng(31)
+    dy = rng.standard_normal((B * H, N, d)).astype(np.float32)
+    g = tmm.backward(tok(inp["k"]), tok(inp["v"]), tok(inp["q"]), per(inp["alpha"], N), per(inp["eta"], N),
+                     per(inp["theta"], N), per(inp["W0"], P), per(inp["S0"], P), cfg.chunk, hidden=cfg.hidden,
+                     n_layers=cfg.n_layers, dy=torch.from_numpy(dy).reshape(B, H, N, d).cuda())
+    torch.cuda.synchronize()
+    for b, h in sampled:
+        s = b * H + h
+        f = wl.inputs_f64(cfg, wl.make_inputs(cfg, streams=[(b, h)]))
+        ref = oracle.backward(f["k"], f["v"], f["q"], f["alpha"], f["eta"], f["theta"], f["W0"], f["S0"],
+                              dy[s:s + 1].astype(np.float64), None, None, d=d, hidden=cfg.hidden,
+                              n_layers=cfg.n_layers, chunk=cfg.chunk)
+        errs = {}
+        for name, r in ref.items():
+            gg = g[name].reshape(B * H, *r.shape[1:])[s].cpu().double().numpy()
+            assert np.all(np.isfinite(gg)), name
+            errs[name] = np.linalg.norm(gg - r[0]) / max(np.linalg.norm(r[0]), 1e-30)
+        print(f"{cfg.name} N{N} stream ({b},{h}): " + " ".join(f"{n} {e:.1e}" for n, e in errs.items()), flush=True)
+        for name, e in errs.items():
+            assert e < TOL, (name, e)
+
+
+def test_backward_benchmark_configuration_sampled():
+    """The benchmark's backward launch: the headline workload's 128 streams
+    (2-layer d = 64 h = 256, bf16 inputs, chunk 64) over their first 1,024
+    tokens, with dL/dy; two streams checked in full against the oracle."""
+    _workload_run(wl.WORKLOADS["headline"].with_(N=1024), [(0, 0), (7, 13)])
+
+
+def test_backward_deep_memory_prefix():
+    """The 4-layer d = 128 hidden = 512 memory (chunk 128), all 32 streams
+    over 160 tokens (one full chunk and a ragged one), one stream checked."""
+    _workload_run(wl.WORKLOADS["deep"].with_(N=160), [(2, 5)])
