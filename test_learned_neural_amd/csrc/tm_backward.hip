@@ -154,15 +154,57 @@ __device__ __forceinline__ float io_load(const void* base, int io, int64_t i) {
   return ((const float*)base)[i];
 }
 
-// out[t] += sum_{c < w} X[t*ldx + c] * Y[t*ldy + c] for rows t < n, one wave
-// per row (each wave walks its own rows; no barrier inside).
-__device__ void row_dots(float* out, const float* X, int ldx, const float* Y, int ldy, int n, int w) {
+// Loops over workspace arrays issue their reads in batches ahead of their
+// stores: a store may alias any later read, so a loop that stores every
+// iteration would otherwise wait out a full memory round trip per iteration.
+constexpr int kBatch = 8;
+
+// Elementwise pass over [0, count): value = load(e) for kBatch iterations
+// per thread, then store(e, value) for each.  No barrier inside.
+template <class FL, class FS>
+__device__ void each(int count, FL load, FS store) {
+  using T = decltype(load(0));
+  for (int e0 = threadIdx.x; e0 < count; e0 += kBT * kBatch) {
+    T v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) v[j] = load(min(e0 + j * kBT, count - 1));
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (e0 + j * kBT < count) store(e0 + j * kBT, v[j]);
+  }
+}
+
+// out[t] += scale * sum_{c < w} X[t*ldx + c] * Y[t*ldy + c] for rows t < n,
+// one wave per row; the row sums of a round of 256 rows stay in lanes (row
+// t0 + wave + 4j in lane j) and are stored once at the round's end.  No
+// barrier inside.
+__device__ void row_dots(float* out, const float* X, int ldx, const float* Y, int ldy, int n, int w,
+                         float scale = 1.f) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int t = wv; t < n; t += kBW) {
-    float acc = 0.f;
-    for (int c = lane; c < w; c += 64) acc += X[(int64_t)t * ldx + c] * Y[(int64_t)t * ldy + c];
-    acc = wave_sum(acc);
-    if (lane == 0) out[t] += acc;
+  for (int t0 = 0; t0 < n; t0 += kBT) {
+    const int jn = min(64, (n - t0 - wv + kBW - 1) / kBW);   // this wave's rows in the round
+    float held = 0.f;
+    for (int j0 = 0; j0 < jn; j0 += 4) {                     // four rows' loads in flight together
+      int64_t ox[4], oy[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t t = t0 + wv + kBW * min(j0 + u, jn - 1);
+        ox[u] = t * ldx;
+        oy[u] = t * ldy;
+      }
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int c = lane; c < w; c += 64) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] += X[ox[u] + c] * Y[oy[u] + c];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float r = wave_sum(acc[u]);
+        held = lane == j0 + u ? r : held;   // lanes past the wave's rows are never stored
+      }
+    }
+    const int t = t0 + wv + kBW * lane;
+    if (t < n) out[t] += scale * held;
   }
 }
 
@@ -220,16 +262,27 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
     const int64_t row0 = tok0 + c0;                       // first token row of the chunk
 
     // ---- chunk inputs; adjoint accumulators cleared ----
-    for (int e = tid; e < n * d; e += kBT) {
-      const int64_t gi = row0 * d + e;
-      V(y.act[0])[e] = io_load(p.k, p.io, gi);
-      vin[e] = io_load(p.v, p.io, gi);
-      if (reads) {
-        V(y.h[0])[e] = io_load(p.q, p.io, gi);
-        V(y.rho[L])[e] = p.dy[gi];
-      } else {
-        p.dq[gi] = 0.f;
-      }
+    {
+      float* a0 = V(y.act[0]);
+      float* h0 = V(y.h[0]);
+      float* rL = V(y.rho[L]);
+      each(
+          n * d,
+          [&](int e) {
+            const int64_t gi = row0 * d + e;
+            return make_float4(io_load(p.k, p.io, gi), io_load(p.v, p.io, gi), reads ? io_load(p.q, p.io, gi) : 0.f,
+                               reads ? p.dy[gi] : 0.f);
+          },
+          [&](int e, float4 x) {
+            a0[e] = x.x;
+            vin[e] = x.y;
+            if (reads) {
+              h0[e] = x.z;
+              rL[e] = x.w;
+            } else {
+              p.dq[row0 * d + e] = 0.f;
+            }
+          });
     }
     for (int l = 0; l <= L; ++l) {
       if (l >= 1)
@@ -253,23 +306,47 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
       }
       cD[i * bb + i] = di;
       cP[i * bb + i] = 1.f;
-      for (int t = i + 1; t < n; ++t) {
-        pr *= et[t * gs];
-        di = (1.f - al[t * gs]) * di + ti * pr;
-        cD[t * bb + i] = di;
-        cP[t * bb + i] = pr;
+      for (int t0 = i + 1; t0 < n; t0 += kBatch) {
+        float ev[kBatch], av[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int t = min(t0 + j, n - 1);
+          ev[j] = et[t * gs];
+          av[j] = al[t * gs];
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          if (t0 + j < n) {
+            pr *= ev[j];
+            di = (1.f - av[j]) * di + ti * pr;
+            cD[(t0 + j) * bb + i] = di;
+            cP[(t0 + j) * bb + i] = pr;
+          }
+        }
       }
       cU[i] = ti * pr;
     }
     if (tid == 0) {
       float a = 1.f, e = 1.f, f = 0.f;
-      for (int t = 0; t < n; ++t) {
-        a *= 1.f - al[t * gs];
-        e *= et[t * gs];
-        f = (1.f - al[t * gs]) * f + e;
-        cA[t] = a;
-        cE[t] = e;
-        cF[t] = f;
+      for (int t0 = 0; t0 < n; t0 += kBatch) {
+        float ev[kBatch], av[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int t = min(t0 + j, n - 1);
+          ev[j] = et[t * gs];
+          av[j] = al[t * gs];
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          if (t0 + j < n) {
+            a *= 1.f - av[j];
+            e *= ev[j];
+            f = (1.f - av[j]) * f + e;
+            cA[t0 + j] = a;
+            cE[t0 + j] = e;
+            cF[t0 + j] = f;
+          }
+        }
       }
     }
     __syncthreads();
@@ -493,25 +570,15 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
             if (ok) xs[i * mw + r] = x;
           });
       // deltabar_i -= D[n-1,i] xw_i + U_i xs_i;  Dbar[n-1,i], Ubar_i from delta_i . (xw_i, xs_i)
-      {
-        const int lane = tid & 63, wv = tid >> 6;
-        for (int i = wv; i < n; i += kBW) {
-          const float dn = Dn[i], ui = cU[i];
-          float s1 = 0.f, s2 = 0.f;
-          for (int r = lane; r < nout; r += 64) {
-            const float x1 = xw[i * mw + r], x2 = xs[i * mw + r], dv = dl[i * nout + r];
-            dbl[i * nout + r] -= dn * x1 + ui * x2;
-            s1 += dv * x1;
-            s2 += dv * x2;
-          }
-          s1 = wave_sum(s1);
-          s2 = wave_sum(s2);
-          if (lane == 0) {
-            Dbar[(int64_t)(n - 1) * bb + i] -= s1;
-            Ubar[i] -= s2;
-          }
-        }
-      }
+      each(
+          n * nout,
+          [&](int e) {
+            const int i = e / nout, r = e % nout;
+            return dbl[e] - (Dn[i] * xw[i * mw + r] + cU[i] * xs[i * mw + r]);
+          },
+          [&](int e, float x) { dbl[e] = x; });
+      row_dots(Dbar + (int64_t)(n - 1) * bb, dl, nout, xw, mw, n, nout, -1.f);
+      row_dots(Ubar, dl, nout, xs, mw, n, nout, -1.f);
       // abar^{l-1} -= [D[n-1,i] delta_i | U_i delta_i] x [Wbar; Sbar]
       block_gemm<true>(
           n, nin, 2 * nout,
@@ -537,11 +604,16 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
       const float* bl = V(y.bv[l]);
       float* bbl = V(y.bbar[l]);
       float* zbl = V(y.zbar[l]);
-      for (int e = tid; e < n * nl; e += kBT) {
-        const float db = dbl[e], zz = zl[e];
-        bbl[e] = db * dsilu(zz);
-        zbl[e] = db * bl[e] * d2silu(zz);
-      }
+      each(
+          n * nl,
+          [&](int e) {
+            const float db = dbl[e], zz = zl[e];
+            return make_float2(db * dsilu(zz), db * bl[e] * d2silu(zz));
+          },
+          [&](int e, float2 x) {
+            bbl[e] = x.x;
+            zbl[e] = x.y;
+          });
       __syncthreads();
       const float* Wu = W + p.off[l + 1];
       float* dbu = V(y.dbar[l + 1]);
@@ -555,7 +627,7 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
     }
     {
       const float* dbL = V(y.dbar[L]);
-      for (int e = tid; e < n * d; e += kBT) p.dv[row0 * d + e] = -dbL[e];
+      each(n * d, [&](int e) { return -dbL[e]; }, [&](int e, float x) { p.dv[row0 * d + e] = x; });
     }
     for (int l = L; l >= 1; --l) {
       const int nin = p.w[l - 1], nout = p.w[l];
@@ -563,7 +635,7 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
       if (l < L) {
         const float* abl = V(y.abar[l]);
         const float* zl = V(y.z[l]);
-        for (int e = tid; e < n * nout; e += kBT) zbl[e] += abl[e] * dsilu(zl[e]);
+        each(n * nout, [&](int e) { return zbl[e] + abl[e] * dsilu(zl[e]); }, [&](int e, float x) { zbl[e] = x; });
         __syncthreads();
       }
       const float* Wl = W + p.off[l];
@@ -578,7 +650,7 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
     }
     {
       const float* ab0 = V(y.abar[0]);
-      for (int e = tid; e < n * d; e += kBT) p.dk[row0 * d + e] = ab0[e];
+      each(n * d, [&](int e) { return ab0[e]; }, [&](int e, float x) { p.dk[row0 * d + e] = x; });
     }
 
     // ---- state adjoints: Sbar, then Wbar (both read the chunk-end Wbar) ----
@@ -611,7 +683,9 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
             nout, nin, n, [=](int r, int t) { return cF[t] * rho[t * nout + r]; },
             [=](int t, int cc) { return h[t * nin + cc]; }, kB_NMAJOR, sbar_pre, sbar_epi);
       } else {
-        for (int e = tid; e < nout * nin; e += kBT) sbar_epi(e / nin, e % nin, 0.f, sbar_pre(e / nin, e % nin), true);
+        each(
+            nout * nin, [&](int e) { return sbar_pre(e / nin, e % nin); },
+            [&](int e, float4 pv) { sbar_epi(e / nin, e % nin, 0.f, pv, true); });
         __syncthreads();
       }
       // Wbar <- A_{n-1} Wbar + [rho-part | delta-bbar part | zbar-a part]
@@ -658,48 +732,100 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
       const float ti = th[i * gs];
       float tb = cP[(int64_t)(n - 1) * bb + i] * Ubar[i];
       float dacc = 0.f, pacc = ti * Ubar[i];
-      for (int t = n - 1; t > i; --t) {
-        const int64_t e = (int64_t)t * bb + i, em = e - bb;
-        dacc += Dbar[e];
-        Ca[e] = -cD[em] * dacc;                 // D[t,i] = (1 - alpha_t) D[t-1,i] + theta_i P[t,i]
-        tb += cP[e] * dacc;
-        pacc += ti * dacc;
-        Ce[e] = cP[em] * pacc;                  // P[t,i] = eta_t P[t-1,i]
-        pacc *= et[t * gs];
-        dacc *= 1.f - al[t * gs];
+      for (int t0 = n - 1; t0 > i; t0 -= kBatch) {
+        float db[kBatch], dm[kBatch], pe[kBatch], pm[kBatch], ev[kBatch], av[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int t = max(t0 - j, i + 1);
+          const int64_t e = (int64_t)t * bb + i;
+          db[j] = Dbar[e];
+          dm[j] = cD[e - bb];
+          pe[j] = cP[e];
+          pm[j] = cP[e - bb];
+          ev[j] = et[t * gs];
+          av[j] = al[t * gs];
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int t = t0 - j;
+          if (t > i) {
+            const int64_t e = (int64_t)t * bb + i;
+            dacc += db[j];
+            Ca[e] = -dm[j] * dacc;                // D[t,i] = (1 - alpha_t) D[t-1,i] + theta_i P[t,i]
+            tb += pe[j] * dacc;
+            pacc += ti * dacc;
+            Ce[e] = pm[j] * pacc;                 // P[t,i] = eta_t P[t-1,i]
+            pacc *= ev[j];
+            dacc *= 1.f - av[j];
+          }
+        }
       }
       dacc += Dbar[(int64_t)i * bb + i];
       gt[i] = tb + dacc;                        // D[i,i] = theta_i
     }
     if (tid == 0) {
       float abar = 0.f, fbar = 0.f, ebar = sSS;
-      for (int t = n - 1; t >= 0; --t) {
-        const float am = t > 0 ? cA[t - 1] : 1.f, em = t > 0 ? cE[t - 1] : 1.f, fm = t > 0 ? cF[t - 1] : 0.f;
-        const float a1 = 1.f - al[t * gs];
-        abar += Abar[t];
-        fbar += Fbar[t];
-        ebar += fbar;                           // F_t = (1 - alpha_t) F_{t-1} + E_t
-        ga[t] = -am * abar - fm * fbar;         // A_t = (1 - alpha_t) A_{t-1}
-        ge[t] = em * ebar;                      // E_t = eta_t E_{t-1}
-        abar *= a1;
-        fbar *= a1;
-        ebar *= et[t * gs];
+      for (int t0 = n - 1; t0 >= 0; t0 -= kBatch) {
+        float am[kBatch], em[kBatch], fm[kBatch], ab[kBatch], fb[kBatch], ev[kBatch], av[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int t = max(t0 - j, 0), tm = max(t - 1, 0);
+          am[j] = t > 0 ? cA[tm] : 1.f;
+          em[j] = t > 0 ? cE[tm] : 1.f;
+          fm[j] = t > 0 ? cF[tm] : 0.f;
+          ab[j] = Abar[t];
+          fb[j] = Fbar[t];
+          ev[j] = et[t * gs];
+          av[j] = al[t * gs];
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int t = t0 - j;
+          if (t >= 0) {
+            const float a1 = 1.f - av[j];
+            abar += ab[j];
+            fbar += fb[j];
+            ebar += fbar;                         // F_t = (1 - alpha_t) F_{t-1} + E_t
+            ga[t] = -am[j] * abar - fm[j] * fbar;  // A_t = (1 - alpha_t) A_{t-1}
+            ge[t] = em[j] * ebar;                 // E_t = eta_t E_{t-1}
+            abar *= a1;
+            fbar *= a1;
+            ebar *= ev[j];
+          }
+        }
       }
     }
     __syncthreads();
     {
+      // row sums over i < t of Ca, Ce (rows held in lanes as in row_dots)
       const int lane = tid & 63, wv = tid >> 6;
-      for (int t = wv; t < n; t += kBW) {
-        float sa = 0.f, se = 0.f;
-        for (int i = lane; i < t; i += 64) {
-          sa += Ca[(int64_t)t * bb + i];
-          se += Ce[(int64_t)t * bb + i];
+      for (int t0 = 0; t0 < n; t0 += kBT) {
+        const int jn = min(64, (n - t0 - wv + kBW - 1) / kBW);
+        float ha = 0.f, he = 0.f;
+        for (int j0 = 0; j0 < jn; j0 += 4) {
+          int tu[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) tu[u] = t0 + wv + kBW * min(j0 + u, jn - 1);
+          float sa[4] = {0.f, 0.f, 0.f, 0.f}, se[4] = {0.f, 0.f, 0.f, 0.f};
+          for (int i = lane; i < tu[3]; i += 64) {   // tu[3] is the group's longest row
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const float xa = Ca[(int64_t)tu[u] * bb + i], xe = Ce[(int64_t)tu[u] * bb + i];
+              sa[u] += i < tu[u] ? xa : 0.f;
+              se[u] += i < tu[u] ? xe : 0.f;
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float ra = wave_sum(sa[u]), re = wave_sum(se[u]);
+            ha = lane == j0 + u ? ra : ha;
+            he = lane == j0 + u ? re : he;
+          }
         }
-        sa = wave_sum(sa);
-        se = wave_sum(se);
-        if (lane == 0) {
-          ga[t] += sa;
-          ge[t] += se;
+        const int t = t0 + wv + kBW * lane;
+        if (t < n) {
+          ga[t] += ha;
+          ge[t] += he;
         }
       }
     }
