@@ -154,26 +154,6 @@ __device__ __forceinline__ float io_load(const void* base, int io, int64_t i) {
   return ((const float*)base)[i];
 }
 
-// Loops over workspace arrays issue their reads in batches ahead of their
-// stores: a store may alias any later read, so a loop that stores every
-// iteration would otherwise wait out a full memory round trip per iteration.
-constexpr int kBatch = 8;
-
-// Elementwise pass over [0, count): value = load(e) for kBatch iterations
-// per thread, then store(e, value) for each.  No barrier inside.
-template <class FL, class FS>
-__device__ void each(int count, FL load, FS store) {
-  using T = decltype(load(0));
-  for (int e0 = threadIdx.x; e0 < count; e0 += kBT * kBatch) {
-    T v[kBatch];
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) v[j] = load(min(e0 + j * kBT, count - 1));
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j)
-      if (e0 + j * kBT < count) store(e0 + j * kBT, v[j]);
-  }
-}
-
 // out[t] += scale * sum_{c < w} X[t*ldx + c] * Y[t*ldy + c] for rows t < n,
 // one wave per row; the row sums of a round of 256 rows stay in lanes (row
 // t0 + wave + 4j in lane j) and are stored once at the round's end.  No
@@ -215,10 +195,15 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
   const int64_t P = p.P;
   float* const Wb = p.dW_in + (int64_t)s * P;
   float* const Sb = p.dS_in + (int64_t)s * P;
-  for (int64_t i = tid; i < P; i += kBT) {
-    Wb[i] = p.dW_out ? p.dW_out[(int64_t)s * P + i] : 0.f;
-    Sb[i] = p.dS_out ? p.dS_out[(int64_t)s * P + i] : 0.f;
-  }
+  each(
+      (int)P,
+      [&](int i) {
+        return make_float2(p.dW_out ? p.dW_out[(int64_t)s * P + i] : 0.f, p.dS_out ? p.dS_out[(int64_t)s * P + i] : 0.f);
+      },
+      [&](int i, float2 x) {
+        Wb[i] = x.x;
+        Sb[i] = x.y;
+      });
   float* const base = p.ws + (int64_t)s * p.ws_stream;
   float* const wsb = base + p.o_buf;
   const BwLayout& y = p.lay;

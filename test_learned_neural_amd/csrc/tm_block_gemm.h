@@ -174,5 +174,26 @@ __device__ void block_gemm(int M, int N, int K, FA fa, FB fb, FBK bkmaj, FE epi)
 constexpr auto kB_KMAJOR = [](int) { return true; };
 constexpr auto kB_NMAJOR = [](int) { return false; };
 
+// Loops over global arrays issue their reads in batches ahead of their
+// stores: a store may alias any later read, so a loop that stores every
+// iteration would otherwise wait out a full memory round trip per iteration.
+constexpr int kBatch = 8;
+
+// Elementwise pass of the workgroup over [0, count): value = load(e) for
+// kBatch iterations per thread, then store(e, value) for each.  No barrier
+// inside.
+template <class FL, class FS>
+__device__ void each(int count, FL load, FS store) {
+  using T = decltype(load(0));
+  for (int e0 = threadIdx.x; e0 < count; e0 += kGemmThreads * kBatch) {
+    T v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) v[j] = load(min(e0 + j * kGemmThreads, count - 1));
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (e0 + j * kGemmThreads < count) store(e0 + j * kGemmThreads, v[j]);
+  }
+}
+
 }  // namespace
 }  // namespace titans

@@ -119,10 +119,8 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
   float* S = p.S + (int64_t)s * p.state_stride;
   const float* Win = p.W_in + (int64_t)s * p.P;
   const float* Sin = p.S_in + (int64_t)s * p.P;
-  if (W != Win)
-    for (int64_t i = tid; i < p.P; i += kThreads) W[i] = Win[i];
-  if (S != Sin)
-    for (int64_t i = tid; i < p.P; i += kThreads) S[i] = Sin[i];
+  if (W != Win) each((int)p.P, [&](int i) { return Win[i]; }, [&](int i, float x) { W[i] = x; });
+  if (S != Sin) each((int)p.P, [&](int i) { return Sin[i]; }, [&](int i, float x) { S[i] = x; });
   __syncthreads();
   if (p.N == 0) return;
   float* const wsb = p.ws + (int64_t)s * p.ws_stride;
@@ -142,10 +140,12 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
       // the state at this chunk's start (read only here; it is next written
       // by this chunk's fold, many barriers later)
       float* ck = p.ckpt + (int64_t)s * p.ckpt_stride + (int64_t)(c0 / p.chunk) * 2 * p.P;
-      for (int64_t i = tid; i < p.P; i += kThreads) {
-        ck[i] = W[i];
-        ck[p.P + i] = S[i];
-      }
+      each(
+          (int)p.P, [&](int i) { return make_float2(W[i], S[i]); },
+          [&](int i, float2 x) {
+            ck[i] = x.x;
+            ck[p.P + i] = x.y;
+          });
     }
     // the chunk's gates: token j at index j * gs (one shared value when the
     // gates are given per chunk)
@@ -156,33 +156,69 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
     const float* th = p.theta + g0;
 
     // ---- load the chunk's keys, values and queries (fp32 copies) ----
-    for (int e = tid; e < n * d; e += kThreads) {
-      const int64_t gi = (tok0 + c0) * d + e;
-      act(0)[e] = load_io(p.k, gi, p.io);
-      w.vin[e] = load_io(p.v, gi, p.io);
-      hq(0)[(e / d) * p.maxw + (e % d)] = load_io(p.q, gi, p.io);
+    {
+      float* a0 = act(0);
+      float* q0 = hq(0);
+      const bool rq = p.y != nullptr;
+      each(
+          n * d,
+          [&](int e) {
+            const int64_t gi = (tok0 + c0) * d + e;
+            return make_float3(load_io(p.k, gi, p.io), load_io(p.v, gi, p.io), rq ? load_io(p.q, gi, p.io) : 0.f);
+          },
+          [&](int e, float3 x) {
+            a0[e] = x.x;
+            w.vin[e] = x.y;
+            if (rq) q0[(e / d) * p.maxw + (e % d)] = x.z;
+          });
     }
     // ---- a1: coefficient recurrences (one thread per column i of D) ----
+    // (gates read kBatch steps ahead of the stores, which may alias them)
     for (int i = tid; i < n; i += kThreads) {
-      float di = th[i * gs], pr = 1.f;
+      const float ti = th[i * gs];
+      float di = ti, pr = 1.f;
       for (int j = 0; j < i; ++j) w.D[j * n + i] = 0.f;
       w.D[i * n + i] = di;
-      for (int j = i + 1; j < n; ++j) {
-        pr *= et[j * gs];
-        di = (1.f - al[j * gs]) * di + th[i * gs] * pr;
-        w.D[j * n + i] = di;
+      for (int j0 = i + 1; j0 < n; j0 += kBatch) {
+        float ev[kBatch], av[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int j = min(j0 + u, n - 1);
+          ev[u] = et[j * gs];
+          av[u] = al[j * gs];
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          if (j0 + u < n) {
+            pr *= ev[u];
+            di = (1.f - av[u]) * di + ti * pr;
+            w.D[(j0 + u) * n + i] = di;
+          }
+        }
       }
-      w.U[i] = th[i * gs] * pr;
+      w.U[i] = ti * pr;
     }
     if (tid == 0) {
       float a = 1.f, e = 1.f, f = 0.f;
-      for (int j = 0; j < n; ++j) {
-        a *= 1.f - al[j * gs];
-        e *= et[j * gs];
-        f = (1.f - al[j * gs]) * f + e;
-        w.A[j] = a;
-        w.E[j] = e;
-        w.F[j] = f;
+      for (int j0 = 0; j0 < n; j0 += kBatch) {
+        float ev[kBatch], av[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int j = min(j0 + u, n - 1);
+          ev[u] = et[j * gs];
+          av[u] = al[j * gs];
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          if (j0 + u < n) {
+            a *= 1.f - av[u];
+            e *= ev[u];
+            f = (1.f - av[u]) * f + e;
+            w.A[j0 + u] = a;
+            w.E[j0 + u] = e;
+            w.F[j0 + u] = f;
+          }
+        }
       }
     }
     __syncthreads();
