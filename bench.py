@@ -135,14 +135,21 @@ def bench_input_side(args, np, torch, tmm, wl):
           f"({achieved / PEAK_TFLOPS['bf16'] * 100:.1f}% of bf16 peak)", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         import oracle
-        f = wl.input_side_f64(wl.make_input_side(icfg.with_(B=1)))
-        t1 = time.perf_counter()
-        oracle.input_side(f["x"], f["w_proj"], f["conv_w"], f["w_gate"], f["b_gate"], f["gate_scale"],
-                          H=icfg.H, d=icfg.d)
-        el = time.perf_counter() - t1
-        res["cpu_baseline"] = {"value": icfg.N / el, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
-                               "kind": "oracle",
-                               "sample": f"1 of {icfg.B} sequences x {icfg.N} tokens, fp64 numpy matmuls, {el:.2f} s"}
+        el, done = 0.0, 0
+        for b in range(icfg.B):   # whole sequences until about half the CPU budget is spent
+            one = {k: (v[b:b + 1] if k == "x" else v) for k, v in inp.items()}
+            f = wl.input_side_f64(one)
+            t1 = time.perf_counter()
+            oracle.input_side(f["x"], f["w_proj"], f["conv_w"], f["w_gate"], f["b_gate"], f["gate_scale"],
+                              H=icfg.H, d=icfg.d)
+            el += time.perf_counter() - t1
+            done += 1
+            if el > args.cpu_seconds / 2:
+                break
+        res["cpu_baseline"] = {"value": done * icfg.N / el, "unit": "tokens/s",
+                               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                               "sample": f"{done} of {icfg.B} sequences x {icfg.N} tokens, fp64 numpy matmuls, "
+                                         f"{el:.2f} s"}
     return res
 
 
@@ -208,15 +215,20 @@ def bench_backward(args, np, torch, tmm, wl, prefix=1024, steps=3):
           f"{tokens / launch_s:.3g} memory-tokens/s, {achieved:.2f} TFLOP/s fp32", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         import oracle
-        f = wl.inputs_f64(cfg, wl.make_inputs(cfg, streams=[(0, 0)], n_tokens=64))
-        dyn = dy[0, 0, :64].double().cpu().numpy()[None]
-        t1 = time.perf_counter()
-        oracle.backward(f["k"], f["v"], f["q"], f["alpha"], f["eta"], f["theta"], f["W0"], f["S0"], dyn, None, None,
-                        d=d, hidden=cfg.hidden, n_layers=cfg.n_layers, chunk=cfg.chunk)
-        el = time.perf_counter() - t1
-        res["cpu_baseline"] = {"value": 64 / el, "unit": "memory-tokens/s", "cores": torch.get_num_threads(),
+        el, done = 0.0, 0
+        for b, h in wl.stream_ids(cfg):   # whole streams until about half the CPU budget is spent
+            f = wl.inputs_f64(cfg, wl.make_inputs(cfg, streams=[(b, h)]))
+            dyn = dy[b, h].double().cpu().numpy()[None]
+            t1 = time.perf_counter()
+            oracle.backward(f["k"], f["v"], f["q"], f["alpha"], f["eta"], f["theta"], f["W0"], f["S0"], dyn, None,
+                            None, d=d, hidden=cfg.hidden, n_layers=cfg.n_layers, chunk=cfg.chunk)
+            el += time.perf_counter() - t1
+            done += 1
+            if el > args.cpu_seconds / 2:
+                break
+        res["cpu_baseline"] = {"value": done * N / el, "unit": "memory-tokens/s", "cores": torch.get_num_threads(),
                                "kind": "oracle",
-                               "sample": f"1 stream x 64 tokens, fp64 torch reverse mode, {el:.2f} s"}
+                               "sample": f"{done} of {B * H} streams x {N} tokens, fp64 torch reverse mode, {el:.2f} s"}
     return res
 
 
@@ -263,16 +275,20 @@ def bench_retrieve(args, np, torch, tmm, wl, steps=10):
           f"{achieved:.1f} TFLOP/s", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         import oracle
-        Wn = inp["W0"][0].astype(np.float64)
-        qn = wl.io_to_f64(inp["q"][0], cfg.io)
         t1 = time.perf_counter()
         n = 0
-        while time.perf_counter() - t1 < 1.0 and n < N:
-            oracle.memory_apply(Wn, qn[n], d, cfg.hidden, cfg.n_layers)
-            n += 1
+        for s in range(B * H):   # whole streams, token by token, until about a quarter of the CPU budget
+            Wn = inp["W0"][s].astype(np.float64)
+            qn = wl.io_to_f64(inp["q"][s], cfg.io)
+            for t in range(N):
+                oracle.memory_apply(Wn, qn[t], d, cfg.hidden, cfg.n_layers)
+            n += N
+            if time.perf_counter() - t1 > args.cpu_seconds / 4:
+                break
         el = time.perf_counter() - t1
         res["cpu_baseline"] = {"value": n / el, "unit": "memory-tokens/s", "cores": 1, "kind": "oracle",
-                               "sample": f"{n} tokens of one stream, fp64 C memory forward, {el:.2f} s"}
+                               "sample": f"{n // N} of {B * H} streams x {N} tokens, fp64 C memory forward, "
+                                         f"{el:.2f} s"}
     return res
 
 
