@@ -35,11 +35,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // zeroed when staged.  The epilogue is split in two: pre(m, n) reads what
 // the element's update needs (any value type), epi(m, n, value, pre, ok)
 // stores, only where ok is set.
-constexpr int kGk = 32;                                   // k per staged slice
-constexpr int kGN = 2 * kGemmTile;                            // output columns per wide tile
-constexpr int kGPerA = kGemmTile * kGk / kGemmThreads;            // A elements per thread per slice
-constexpr int kGPerB = kGN * kGk / kGemmThreads;              // B elements per thread per wide slice
-constexpr int kEpiGroup = 8;                              // accumulator rows per epilogue group
+constexpr int kGk = 32;                                  // k per staged slice
+constexpr int kGN = 2 * kGemmTile;                       // output columns per wide tile
+constexpr int kGPerA = kGemmTile * kGk / kGemmThreads;   // A elements per thread per slice
+constexpr int kGPerB = kGN * kGk / kGemmThreads;         // B elements per thread per wide slice
+constexpr int kEpiGroup = 8;                             // accumulator rows per epilogue group
 constexpr int kGemmLdsFloats = kGk * (kGemmTile + 1) + kGk * (kGN + 1);
 
 // one LDS allocation shared by every block_gemm instantiation of a kernel
@@ -51,13 +51,13 @@ __device__ __forceinline__ float* gemm_lds() {
 template <bool A_KMAJOR, bool WIDE, class FA, class FB, class FBK, class FP, class FE>
 __device__ void block_gemm_tiles(int M, int N, int K, FA fa, FB fb, FBK bkmaj, FP pre, FE epi) {
   using PreT = decltype(pre(0, 0));
-  float* As = gemm_lds();                 // [kGk][kGemmTile + 1]
-  float* Bs = As + kGk * (kGemmTile + 1);     // [kGk][kGN + 1]
+  float* As = gemm_lds();                   // [kGk][kGemmTile + 1]
+  float* Bs = As + kGk * (kGemmTile + 1);   // [kGk][kGN + 1]
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   constexpr bool wide = WIDE;
-  constexpr int tn = wide ? kGN : kGemmTile;                // output columns per tile
-  constexpr int nb = wide ? kGPerB : kGPerB / 2;        // B elements per thread per slice
+  constexpr int tn = wide ? kGN : kGemmTile;       // output columns per tile
+  constexpr int nb = wide ? kGPerB : kGPerB / 2;   // B elements per thread per slice
   const int wm = (wv >> 1) * 32, wn = (wv & 1) * (wide ? 64 : 32);
   const int li = lane & 31, lk = lane >> 5;
   auto a_at = [&](int q, int& mm, int& ka) {
