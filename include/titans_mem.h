@@ -180,7 +180,8 @@ int titans_mem_retrieve(const titans_mem_desc* desc, const void* q, const float*
  * gradients (each token's inner gradient depends on W at its chunk start).
  * Both read modes.  Arithmetic is fp32 whatever the io dtype (bf16 inputs
  * are read exactly).  Outputs must not overlap each other or any input.
- * Supported: every layer width a multiple of 4, at most 1024, N >= 1.
+ * Supported: every layer width a multiple of 4, at most 1024, N >= 1,
+ * chunk <= 4096 (TM_ERR_UNSUPPORTED otherwise).
  * The workspace holds (W, S) at every chunk start and one chunk's token
  * vectors: titans_mem_backward_workspace_bytes(desc, chunk) bytes.
  */

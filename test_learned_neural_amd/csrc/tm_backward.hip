@@ -894,7 +894,9 @@ int rows_per_chunk(const Shape& s, int chunk) { return chunk < s.N ? chunk : s.N
 }  // namespace
 
 bool backward_supported(const Shape& s, int chunk) {
-  if (chunk < 1 || s.N < 1) return false;
+  // the chunk bound of the forward sweep (the generic kernel); it also keeps
+  // every [b x b] index inside int
+  if (chunk < 1 || chunk > kMaxChunkGeneric || s.N < 1) return false;
   if (s.maxw > kMaxWidthBackward) return false;
   for (int l = 0; l <= s.L; ++l)
     if (s.widths[l] % 4 != 0) return false;

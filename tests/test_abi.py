@@ -291,6 +291,7 @@ def test_backward_workspace_query(lib):
     assert tmm.backward_workspace_bytes(d, 0) == tmm.ERR_INVALID
     assert tmm.backward_workspace_bytes(tmm.make_desc(1, 1, 8, 6, 10, 2, "f32"), 4) == tmm.ERR_UNSUPPORTED
     assert tmm.backward_workspace_bytes(tmm.make_desc(1, 1, 8, 16, 2048, 2, "f32"), 4) == tmm.ERR_UNSUPPORTED
+    assert tmm.backward_workspace_bytes(tmm.make_desc(1, 1, 8000, 16, 32, 2, "f32"), 4097) == tmm.ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("name", ["k", "v", "q", "alpha", "eta", "theta", "W_in", "S_in", "dk", "dv", "dq",
