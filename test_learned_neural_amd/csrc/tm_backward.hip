@@ -406,23 +406,24 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
         float* sc = V(y.sc[l]);
         float* uw = V(y.uw[l]);
         float* us = V(y.us[l]);
+        // one product for the three that share h: columns [a^{l-1} | W | S]
         block_gemm<true>(
-            n, n, nin, [=](int t, int cc) { return h[t * nin + cc]; },
-            [=](int cc, int i) { return ak[i * nin + cc]; }, kB_KMAJOR,
-            [=](int t, int i, float x, bool ok) {
-              if (ok) sc[t * bb + i] = x;
-            });
-        block_gemm<true>(
-            n, nout, nin, [=](int t, int cc) { return h[t * nin + cc]; },
-            [=](int cc, int r) { return Wl[(int64_t)r * nin + cc]; }, kB_KMAJOR,
-            [=](int t, int r, float x, bool ok) {
-              if (ok) uw[t * nout + r] = x;
-            });
-        block_gemm<true>(
-            n, nout, nin, [=](int t, int cc) { return h[t * nin + cc]; },
-            [=](int cc, int r) { return Sl[(int64_t)r * nin + cc]; }, kB_KMAJOR,
-            [=](int t, int r, float x, bool ok) {
-              if (ok) us[t * nout + r] = x;
+            n, n + 2 * nout, nin, [=](int t, int cc) { return h[t * nin + cc]; },
+            [=](int cc, int j) {
+              const float* x = j < n          ? ak + (int64_t)j * nin + cc
+                               : j < n + nout ? Wl + (int64_t)(j - n) * nin + cc
+                                              : Sl + (int64_t)(j - n - nout) * nin + cc;
+              return *x;
+            },
+            kB_KMAJOR,
+            [=](int t, int j, float x, bool ok) {
+              if (!ok) return;
+              if (j < n)
+                sc[t * bb + j] = x;
+              else if (j < n + nout)
+                uw[t * nout + j - n] = x;
+              else
+                us[t * nout + j - n - nout] = x;
             });
         if (l == L) break;
         // zq = A uw + F us - (D o sc) delta
@@ -542,17 +543,19 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
       float* dbl = V(y.dbar[l]);
       float* abl = V(y.abar[l - 1]);
       const float* Dn = cD + (int64_t)(n - 1) * bb;
+      // Wbar a_i and Sbar a_i in one product: columns [Wbar | Sbar]
       block_gemm<true>(
-          n, nout, nin, [=](int i, int cc) { return ak[i * nin + cc]; },
-          [=](int cc, int r) { return Wbl[(int64_t)r * nin + cc]; }, kB_KMAJOR,
-          [=](int i, int r, float x, bool ok) {
-            if (ok) xw[i * mw + r] = x;
-          });
-      block_gemm<true>(
-          n, nout, nin, [=](int i, int cc) { return ak[i * nin + cc]; },
-          [=](int cc, int r) { return Sbl[(int64_t)r * nin + cc]; }, kB_KMAJOR,
-          [=](int i, int r, float x, bool ok) {
-            if (ok) xs[i * mw + r] = x;
+          n, 2 * nout, nin, [=](int i, int cc) { return ak[i * nin + cc]; },
+          [=](int cc, int j) {
+            return *(j < nout ? Wbl + (int64_t)j * nin + cc : Sbl + (int64_t)(j - nout) * nin + cc);
+          },
+          kB_KMAJOR,
+          [=](int i, int j, float x, bool ok) {
+            if (!ok) return;
+            if (j < nout)
+              xw[i * mw + j] = x;
+            else
+              xs[i * mw + j - nout] = x;
           });
       // deltabar_i -= D[n-1,i] xw_i + U_i xs_i;  Dbar[n-1,i], Ubar_i from delta_i . (xw_i, xs_i)
       each(
