@@ -8,25 +8,27 @@
 namespace titans {
 namespace {
 
-constexpr int kGemmThreads = 256;   // workgroup size every caller launches with
+constexpr int kGemmThreads = 512;   // workgroup size every caller launches with
 constexpr int kGemmTile = 64;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// C[M x N] = sum_k A(m, k) B(k, n), handed to epi(m, n, value).  The whole
-// workgroup cooperates; operands come through accessors (global/L2 reads)
-// and are staged through LDS in kGk-deep slices, the next slice's operands
-// loaded into registers while the current one is multiplied.  Output tiles
-// are 64 x 128 when N > 64 (each of the four waves computes a 32 x 64 part
-// as two 32 x 32 blocks), else 64 x 64 (each wave a 32 x 32 quarter with
-// the slice's even and odd k-pairs in two accumulators, summed at the end),
-// so every wave keeps two independent chains of the fp32 matrix instruction
+// C[M x N] = sum_k A(m, k) B(k, n), handed to an epilogue per element.  The
+// whole workgroup (eight waves, two per SIMD, so one wave's memory waits
+// overlap the other's work) cooperates; operands come through accessors
+// (global/L2 reads) and are staged through LDS in kGk-deep slices, the next
+// slice's operands loaded into registers while the current one is
+// multiplied.  Output tiles are 64 x 128 when N > 64 (each wave computes
+// one 32 x 32 block over the whole slice), else 64 x 64 (two waves per
+// block, each over half the slice's k; the second hands its partial sums to
+// the first through LDS at the end).  A wave splits its k over two
+// accumulators, i.e. two independent chains of the fp32 matrix instruction
 // v_mfma_f32_32x32x2_f32 (lane l supplies A[l%32][l/32] and B[l/32][l%32];
-// accumulator register r holds row 8(r/4) + 4(l/32) + r%4, column l%32) and
-// the arithmetic stays fp32.  The accessors are read in the order that keeps
-// a wavefront's loads on few cache lines: A_KMAJOR says A(m, k) is
-// contiguous in k (else in m); bkmaj(k0) says whether the B slice starting
-// at k0 is contiguous in k (else in n).
+// accumulator register r holds row 8(r/4) + 4(l/32) + r%4, column l%32),
+// summed before the epilogue, and the arithmetic stays fp32.  The accessors
+// are read in the order that keeps a wavefront's loads on few cache lines:
+// A_KMAJOR says A(m, k) is contiguous in k (else in m); bkmaj(k0) says
+// whether the B slice starting at k0 is contiguous in k (else in n).
 //
 // So that a wave keeps all of a slice's loads in flight at once, the
 // accessors and the epilogue are called unconditionally, with indices
@@ -42,6 +44,8 @@ constexpr int kGPerB = kGN * kGk / kGemmThreads;         // B elements per threa
 constexpr int kEpiGroup = 8;                             // accumulator rows per epilogue group
 constexpr int kGemmLdsFloats = kGk * (kGemmTile + 1) + kGk * (kGN + 1);
 
+static_assert(4 * 64 * 17 <= kGemmLdsFloats, "the narrow-tile reduction reuses the staging area");
+
 // one LDS allocation shared by every block_gemm instantiation of a kernel
 __device__ __forceinline__ float* gemm_lds() {
   __shared__ float buf[kGemmLdsFloats];
@@ -54,11 +58,17 @@ __device__ void block_gemm_tiles(int M, int N, int K, FA fa, FB fb, FBK bkmaj, F
   float* As = gemm_lds();                   // [kGk][kGemmTile + 1]
   float* Bs = As + kGk * (kGemmTile + 1);   // [kGk][kGN + 1]
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // eight waves (wave-uniform)
   constexpr bool wide = WIDE;
   constexpr int tn = wide ? kGN : kGemmTile;       // output columns per tile
   constexpr int nb = wide ? kGPerB : kGPerB / 2;   // B elements per thread per slice
-  const int wm = (wv >> 1) * 32, wn = (wv & 1) * (wide ? 64 : 32);
+  // wide: wave w owns the 32 x 32 block (w / 4, w % 4) and all of a slice's
+  // k; narrow: waves 2b, 2b + 1 share block b, each taking half the slice's k
+  const int blk = wide ? wv : (wv >> 1);
+  const int wm = wide ? (blk >> 2) * 32 : (blk >> 1) * 32;
+  const int wn = wide ? (blk & 3) * 32 : (blk & 1) * 32;
+  const int kh = wide ? 0 : (wv & 1);
   const int li = lane & 31, lk = lane >> 5;
   auto a_at = [&](int q, int& mm, int& ka) {
     const int e = tid + q * kGemmThreads;
@@ -106,46 +116,50 @@ __device__ void block_gemm_tiles(int M, int N, int K, FA fa, FB fb, FBK bkmaj, F
         // the last slice they reread the clamped last column: unused)
         bk = bkmaj(k0 + kGk);
         fetch(k0 + kGk, bk);
-        if constexpr (wide) {
+        constexpr int ksteps = wide ? kGk : kGk / 2;   // k rows of the slice this wave multiplies
 #pragma unroll
-          for (int kk = 0; kk < kGk; kk += 2) {
-            const float a = As[(kk + lk) * (kGemmTile + 1) + wm + li];
-            const float* br = Bs + (kk + lk) * (kGN + 1) + wn + li;
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, br[0], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, br[32], acc1, 0, 0, 0);
-          }
-        } else {
-#pragma unroll
-          for (int kk = 0; kk < kGk; kk += 4) {
-            const float* ar = As + (kk + lk) * (kGemmTile + 1) + wm + li;
-            const float* br = Bs + (kk + lk) * (kGN + 1) + wn + li;
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(ar[0], br[0], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(ar[2 * (kGemmTile + 1)], br[2 * (kGN + 1)], acc1, 0, 0, 0);
-          }
+        for (int kk = 0; kk < ksteps; kk += 4) {
+          const int k = kh * (kGk / 2) + kk + lk;
+          const float* ar = As + k * (kGemmTile + 1) + wm + li;
+          const float* br = Bs + k * (kGN + 1) + wn + li;
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(ar[0], br[0], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(ar[2 * (kGemmTile + 1)], br[2 * (kGN + 1)], acc1, 0, 0, 0);
         }
         __syncthreads();
       }
-      // epilogue in groups of kEpiGroup accumulator rows: every pre() read
-      // of a group is issued before its epi() stores (a store may alias a
-      // later element's read, so reads are never moved past it)
 #pragma unroll
-      for (int g = 0; g < 16; g += kEpiGroup) {
-        PreT pv0[kEpiGroup], pv1[kEpiGroup];
+      for (int r = 0; r < 16; ++r) acc0[r] += acc1[r];
+      if constexpr (!wide) {
+        // the pair's second wave hands its partial sums to the first through
+        // the (now free) staging area
+        float* red = As + (blk * 64 + lane) * 17;
+        if (kh) {
 #pragma unroll
-        for (int r = g; r < g + kEpiGroup; ++r) {
-          const int mc = min(m0 + wm + 8 * (r >> 2) + 4 * lk + (r & 3), M - 1), n = n0 + wn + li;
-          pv0[r - g] = pre(mc, min(n, N - 1));
-          if constexpr (wide) pv1[r - g] = pre(mc, min(n + 32, N - 1));
+          for (int r = 0; r < 16; ++r) red[r] = acc0[r];
         }
+        __syncthreads();
+        if (!kh) {
 #pragma unroll
-        for (int r = g; r < g + kEpiGroup; ++r) {
-          const int m = m0 + wm + 8 * (r >> 2) + 4 * lk + (r & 3), n = n0 + wn + li;
-          const int mc = min(m, M - 1);
-          if constexpr (wide) {
-            epi(mc, min(n, N - 1), acc0[r], pv0[r - g], m < M && n < N);
-            epi(mc, min(n + 32, N - 1), acc1[r], pv1[r - g], m < M && n + 32 < N);
-          } else {
-            epi(mc, min(n, N - 1), acc0[r] + acc1[r], pv0[r - g], m < M && n < N);
+          for (int r = 0; r < 16; ++r) acc0[r] += red[r];
+        }
+        __syncthreads();
+      }
+      if (wide || !kh) {
+        // epilogue in groups of kEpiGroup accumulator rows: every pre() read
+        // of a group is issued before its epi() stores (a store may alias a
+        // later element's read, so reads are never moved past it)
+#pragma unroll
+        for (int g = 0; g < 16; g += kEpiGroup) {
+          PreT pv[kEpiGroup];
+#pragma unroll
+          for (int r = g; r < g + kEpiGroup; ++r) {
+            const int mc = min(m0 + wm + 8 * (r >> 2) + 4 * lk + (r & 3), M - 1), n = n0 + wn + li;
+            pv[r - g] = pre(mc, min(n, N - 1));
+          }
+#pragma unroll
+          for (int r = g; r < g + kEpiGroup; ++r) {
+            const int m = m0 + wm + 8 * (r >> 2) + 4 * lk + (r & 3), n = n0 + wn + li;
+            epi(min(m, M - 1), min(n, N - 1), acc0[r], pv[r - g], m < M && n < N);
           }
         }
       }
