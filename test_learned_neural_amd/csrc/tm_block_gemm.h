@@ -18,14 +18,15 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // overlap the other's work) cooperates; operands come through accessors
 // (global/L2 reads) and are staged through LDS in kGk-deep slices, the next
 // slice's operands loaded into registers while the current one is
-// multiplied.  Output tiles are 64 x 128 when N > 64 (each wave computes
-// one 32 x 32 block over the whole slice), else 64 x 64 (two waves per
-// block, each over half the slice's k; the second hands its partial sums to
-// the first through LDS at the end).  A wave splits its k over two
-// accumulators, i.e. two independent chains of the fp32 matrix instruction
-// v_mfma_f32_32x32x2_f32 (lane l supplies A[l%32][l/32] and B[l/32][l%32];
-// accumulator register r holds row 8(r/4) + 4(l/32) + r%4, column l%32),
-// summed before the epilogue, and the arithmetic stays fp32.  The accessors
+// multiplied.  Output tiles are 64 x 128 when N > 64, else 64 x 64; with
+// eight waves each wave of a wide tile computes one 32 x 32 block over the
+// whole slice, and in a narrow tile two waves share a block, each over half
+// the slice's k, the second handing its partial sums to the first through
+// LDS at the end.  A wave splits its k over two accumulators, i.e. two
+// independent chains of the fp32 matrix instruction v_mfma_f32_32x32x2_f32
+// (lane l supplies A[l%32][l/32] and B[l/32][l%32]; accumulator register r
+// holds row 8(r/4) + 4(l/32) + r%4, column l%32), summed before the
+// epilogue, and the arithmetic stays fp32.  The accessors
 // are read in the order that keeps a wavefront's loads on few cache lines:
 // A_KMAJOR says A(m, k) is contiguous in k (else in m); bkmaj(k0) says
 // whether the B slice starting at k0 is contiguous in k (else in n).
@@ -42,9 +43,10 @@ constexpr int kGN = 2 * kGemmTile;                       // output columns per w
 constexpr int kGPerA = kGemmTile * kGk / kGemmThreads;   // A elements per thread per slice
 constexpr int kGPerB = kGN * kGk / kGemmThreads;         // B elements per thread per wide slice
 constexpr int kEpiGroup = 8;                             // accumulator rows per epilogue group
-constexpr int kGemmLdsFloats = kGk * (kGemmTile + 1) + kGk * (kGN + 1);
-
-static_assert(4 * 64 * 17 <= kGemmLdsFloats, "the narrow-tile reduction reuses the staging area");
+constexpr int kGemmWaves = kGemmThreads / 64;
+constexpr int kGemmStageFloats = kGk * (kGemmTile + 1) + kGk * (kGN + 1);
+constexpr int kGemmRedFloats = 4 * (kGemmWaves / 4 - 1) * 64 * 17;   // narrow tiles: 4 blocks
+constexpr int kGemmLdsFloats = kGemmStageFloats > kGemmRedFloats ? kGemmStageFloats : kGemmRedFloats;
 
 // one LDS allocation shared by every block_gemm instantiation of a kernel
 __device__ __forceinline__ float* gemm_lds() {
@@ -59,16 +61,18 @@ __device__ void block_gemm_tiles(int M, int N, int K, FA fa, FB fb, FBK bkmaj, F
   float* Bs = As + kGk * (kGemmTile + 1);   // [kGk][kGN + 1]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // eight waves (wave-uniform)
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (wave-uniform)
   constexpr bool wide = WIDE;
   constexpr int tn = wide ? kGN : kGemmTile;       // output columns per tile
   constexpr int nb = wide ? kGPerB : kGPerB / 2;   // B elements per thread per slice
-  // wide: wave w owns the 32 x 32 block (w / 4, w % 4) and all of a slice's
-  // k; narrow: waves 2b, 2b + 1 share block b, each taking half the slice's k
-  const int blk = wide ? wv : (wv >> 1);
+  // the tile's 32 x 32 blocks (8 wide, 4 narrow) are shared out over the
+  // waves; the ksplit waves of one block each take 1/ksplit of the slice's k
+  constexpr int nblk = wide ? 8 : 4;                 // 32 x 32 blocks per tile
+  constexpr int ksplit = kGemmWaves / nblk;          // waves per block, each over part of the slice's k
+  const int blk = wv / ksplit;
   const int wm = wide ? (blk >> 2) * 32 : (blk >> 1) * 32;
   const int wn = wide ? (blk & 3) * 32 : (blk & 1) * 32;
-  const int kh = wide ? 0 : (wv & 1);
+  const int kh = wv % ksplit;
   const int li = lane & 31, lk = lane >> 5;
   auto a_at = [&](int q, int& mm, int& ka) {
     const int e = tid + q * kGemmThreads;
@@ -116,10 +120,10 @@ __device__ void block_gemm_tiles(int M, int N, int K, FA fa, FB fb, FBK bkmaj, F
         // the last slice they reread the clamped last column: unused)
         bk = bkmaj(k0 + kGk);
         fetch(k0 + kGk, bk);
-        constexpr int ksteps = wide ? kGk : kGk / 2;   // k rows of the slice this wave multiplies
+        constexpr int ksteps = kGk / ksplit;   // k rows of the slice this wave multiplies
 #pragma unroll
         for (int kk = 0; kk < ksteps; kk += 4) {
-          const int k = kh * (kGk / 2) + kk + lk;
+          const int k = kh * ksteps + kk + lk;
           const float* ar = As + k * (kGemmTile + 1) + wm + li;
           const float* br = Bs + k * (kGN + 1) + wn + li;
           acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(ar[0], br[0], acc0, 0, 0, 0);
@@ -129,22 +133,26 @@ __device__ void block_gemm_tiles(int M, int N, int K, FA fa, FB fb, FBK bkmaj, F
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc0[r] += acc1[r];
-      if constexpr (!wide) {
-        // the pair's second wave hands its partial sums to the first through
-        // the (now free) staging area
-        float* red = As + (blk * 64 + lane) * 17;
+      if constexpr (ksplit > 1) {
+        // the block's other waves hand their partial sums to its first wave
+        // through the (now free) staging area
         if (kh) {
+          float* red = As + ((blk * (ksplit - 1) + kh - 1) * 64 + lane) * 17;
 #pragma unroll
           for (int r = 0; r < 16; ++r) red[r] = acc0[r];
         }
         __syncthreads();
         if (!kh) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc0[r] += red[r];
+          for (int h = 0; h < ksplit - 1; ++h) {
+            const float* red = As + ((blk * (ksplit - 1) + h) * 64 + lane) * 17;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc0[r] += red[r];
+          }
         }
         __syncthreads();
       }
-      if (wide || !kh) {
+      if (!kh) {
         // epilogue in groups of kEpiGroup accumulator rows: every pre() read
         // of a group is issued before its epi() stores (a store may alias a
         // later element's read, so reads are never moved past it)
