@@ -174,3 +174,15 @@ def test_backward_deep_memory_prefix():
     """The 4-layer d = 128 hidden = 512 memory (chunk 128), all 32 streams
     over 160 tokens (one full chunk and a ragged one), one stream checked."""
     _workload_run(wl.WORKLOADS["deep"].with_(N=160), [(2, 5)])
+
+
+@pytest.mark.parametrize("B,H,N,d,h,L,chunk,read_mode,chunk_gates", [
+    (1, 1, 1, 4, 8, 2, 1, 0, False),        # a single token
+    (1, 1, 3, 4, 0, 1, 2, 0, False),        # linear, ragged second chunk of one token
+    (1, 2, 23, 8, 16, 2, 5, 1, True),       # chunk-start read with per-chunk gates
+    (1, 1, 26, 8, 12, 3, 7, 1, False),      # 3 layers, chunk-start read
+    (2, 1, 17, 12, 20, 2, 17, 0, True),     # one chunk exactly the sequence, per-chunk gates
+])
+def test_backward_edge_cases(B, H, N, d, h, L, chunk, read_mode, chunk_gates):
+    x, adj, P = _problem(300 + N + L + chunk, B, H, N, d, h, L, chunk_gates=chunk_gates, chunk=chunk)
+    _run(x, adj, B, H, N, d, h, L, chunk, read_mode=read_mode, chunk_gates=chunk_gates)
