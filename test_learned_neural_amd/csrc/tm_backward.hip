@@ -155,12 +155,12 @@ __device__ __forceinline__ float io_load(const void* base, int io, int64_t i) {
 }
 
 // out[t] += scale * sum_{c < w} X[t*ldx + c] * Y[t*ldy + c] for rows t < n,
-// one wave per row; the row sums of a round of 256 rows stay in lanes (row
-// t0 + wave + 4j in lane j) and are stored once at the round's end.  No
+// one wave per row; the row sums of a round of kBT rows stay in lanes (row
+// t0 + wave + kBW j in lane j) and are stored once at the round's end.  No
 // barrier inside.
 __device__ void row_dots(float* out, const float* X, int ldx, const float* Y, int ldy, int n, int w,
                          float scale = 1.f) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   for (int t0 = 0; t0 < n; t0 += kBT) {
     const int jn = min(64, (n - t0 - wv + kBW - 1) / kBW);   // this wave's rows in the round
     float held = 0.f;
@@ -409,10 +409,11 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
         // one product for the three that share h: columns [a^{l-1} | W | S]
         block_gemm<true>(
             n, n + 2 * nout, nin, [=](int t, int cc) { return h[t * nin + cc]; },
-            [=](int cc, int j) {
-              const float* x = j < n          ? ak + (int64_t)j * nin + cc
-                               : j < n + nout ? Wl + (int64_t)(j - n) * nin + cc
-                                              : Sl + (int64_t)(j - n - nout) * nin + cc;
+            [=](int cc, int j) {   // every arm's offset kept in range (only one is read)
+              const int ja = j < n ? j : 0, jw = j >= n && j < n + nout ? j - n : 0, js = j >= n + nout ? j - n - nout : 0;
+              const float* x = j < n          ? ak + (int64_t)ja * nin + cc
+                               : j < n + nout ? Wl + (int64_t)jw * nin + cc
+                                              : Sl + (int64_t)js * nin + cc;
               return *x;
             },
             kB_KMAJOR,
@@ -500,16 +501,19 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
         block_gemm<true>(
             n, nin, 2 * nout + n,
             [=](int t, int kk) {
-              const bool st = kk < 2 * nout;
-              const float* x = st ? rho + t * nout + (kk < nout ? kk : kk - nout) : dr + (int64_t)t * bb + (kk - 2 * nout);
+              const bool st = kk < 2 * nout;   // every arm's offset kept in range (only one is read)
+              const int kr = kk < nout ? kk : (st ? kk - nout : 0), kd = st ? 0 : kk - 2 * nout;
+              const float* x = st ? rho + t * nout + kr : dr + (int64_t)t * bb + kd;
               const float f = *(kk < nout ? cA + t : cF + t);
               const float v = *x;
               return st ? f * v : v;
             },
             [=](int kk, int cc) {
-              const float* x = kk < nout       ? Wl + (int64_t)kk * nin + cc
-                               : kk < 2 * nout ? Sl + (int64_t)(kk - nout) * nin + cc
-                                               : ak + (int64_t)(kk - 2 * nout) * nin + cc;
+              const int kw = kk < nout ? kk : 0, ks = kk >= nout && kk < 2 * nout ? kk - nout : 0,
+                        ka = kk >= 2 * nout ? kk - 2 * nout : 0;
+              const float* x = kk < nout       ? Wl + (int64_t)kw * nin + cc
+                               : kk < 2 * nout ? Sl + (int64_t)ks * nin + cc
+                                               : ak + (int64_t)ka * nin + cc;
               return *x;
             },
             kB_NMAJOR, hbar_pre, hbar_epi);
@@ -547,7 +551,8 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
       block_gemm<true>(
           n, 2 * nout, nin, [=](int i, int cc) { return ak[i * nin + cc]; },
           [=](int cc, int j) {
-            return *(j < nout ? Wbl + (int64_t)j * nin + cc : Sbl + (int64_t)(j - nout) * nin + cc);
+            const int jw = j < nout ? j : 0, js = j < nout ? 0 : j - nout;
+            return *(j < nout ? Wbl + (int64_t)jw * nin + cc : Sbl + (int64_t)js * nin + cc);
           },
           kB_KMAJOR,
           [=](int i, int j, float x, bool ok) {
@@ -575,7 +580,8 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
             return -f * dl[i * nout + (kk < nout ? kk : kk - nout)];
           },
           [=](int kk, int cc) {
-            return *(kk < nout ? Wbl + (int64_t)kk * nin + cc : Sbl + (int64_t)(kk - nout) * nin + cc);
+            const int kw = kk < nout ? kk : 0, ks = kk < nout ? 0 : kk - nout;
+            return *(kk < nout ? Wbl + (int64_t)kw * nin + cc : Sbl + (int64_t)ks * nin + cc);
           },
           kB_NMAJOR,
           [=](int i, int cc) { return abl[i * nin + cc]; },
@@ -786,7 +792,7 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
     __syncthreads();
     {
       // row sums over i < t of Ca, Ce (rows held in lanes as in row_dots)
-      const int lane = tid & 63, wv = tid >> 6;
+      const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
       for (int t0 = 0; t0 < n; t0 += kBT) {
         const int jn = min(64, (n - t0 - wv + kBW - 1) / kBW);
         float ha = 0.f, he = 0.f;

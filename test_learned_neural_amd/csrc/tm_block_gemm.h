@@ -34,8 +34,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // So that a wave keeps all of a slice's loads in flight at once, the
 // accessors and the epilogue are called unconditionally, with indices
 // clamped into range (M, N, K >= 1): fa(m, k) and fb(k, n) must be
-// branch-free reads of valid addresses; operands outside the product are
-// zeroed when staged.  The epilogue is split in two: pre(m, n) reads what
+// branch-free reads of valid addresses (an accessor that selects between
+// arrays keeps every arm's pointer in range, read or not: an out-of-range
+// pointer is undefined and lets the compiler fold the selection wrongly);
+// operands outside the product are zeroed when staged.  The epilogue is split in two: pre(m, n) reads what
 // the element's update needs (any value type), epi(m, n, value, pre, ok)
 // stores, only where ok is set.
 constexpr int kGk = 32;                                  // k per staged slice

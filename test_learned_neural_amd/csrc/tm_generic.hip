@@ -305,16 +305,19 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
         block_gemm<true>(
             n, nout, 2 * nin + n,
             [=](int j, int kk) {   // branch-free: pick the address, then the factor
-              const bool st = kk < 2 * nin;
-              const float* x = st ? h + j * maxw + (kk < nin ? kk : kk - nin) : sc + j * n + (kk - 2 * nin);
+              const bool st = kk < 2 * nin;   // every arm's offset kept in range (only one is read)
+              const int kc = kk < nin ? kk : (st ? kk - nin : 0), kt = st ? 0 : kk - 2 * nin;
+              const float* x = st ? h + j * maxw + kc : sc + j * n + kt;
               const float f = *(kk < nin ? A + j : F + j);
               const float v = *x;
               return st ? f * v : -v;
             },
             [=](int kk, int r) {
-              const float* x = kk < nin       ? Wl + (int64_t)r * nin + kk
-                               : kk < 2 * nin ? Sl + (int64_t)r * nin + (kk - nin)
-                                              : dl + (int64_t)(kk - 2 * nin) * nout + r;
+              const int kw = kk < nin ? kk : 0, ks = kk >= nin && kk < 2 * nin ? kk - nin : 0,
+                        kt = kk >= 2 * nin ? kk - 2 * nin : 0;
+              const float* x = kk < nin       ? Wl + (int64_t)r * nin + kw
+                               : kk < 2 * nin ? Sl + (int64_t)r * nin + ks
+                                              : dl + (int64_t)kt * nout + r;
               return *x;
             },
             [=](int k0) { return k0 + kGk <= 2 * nin; },   // the token part is contiguous in r
