@@ -51,7 +51,7 @@ constexpr int kStageB = kNT * kKT * 2;
 constexpr int kStage = kStageA + kStageB;
 constexpr int kRowGroup = 8;      // token tiles of one XCD sharing each channel tile's weights
 constexpr int kGatePass = 64;     // gate logits per epilogue pass
-constexpr int kGateStride = kGatePass + 1;
+constexpr int kGateStride = kGatePass + 4;   // padded row (16-byte aligned rows for the tile writes)
 constexpr float kNormFloor2 = 1e-12f;   // (1e-6)^2: k, q = s / max(||s||, 1e-6)
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -75,11 +75,15 @@ struct InParams {
 
 template <int kD>
 constexpr int pass_width() { return kD > 64 ? kD : 64; }
+// row pitch (floats) of the epilogue's fp32 tile: padded so that the
+// accumulators' 16-byte row pieces of 32 consecutive rows spread over banks
+template <int kD>
+constexpr int ep_stride() { return pass_width<kD>() + 4; }
 
 template <int kD>
 constexpr int lds_bytes() {
   int m = 2 * kStage;
-  if (kMT * pass_width<kD>() * 4 > m) m = kMT * pass_width<kD>() * 4;
+  if (kMT * ep_stride<kD>() * 4 > m) m = kMT * ep_stride<kD>() * 4;
   if (kMT * kGateStride * 4 > m) m = kMT * kGateStride * 4;
   return m;
 }
@@ -158,6 +162,7 @@ template <int kD>
 __device__ __forceinline__ void kvq_epilogue(const InParams& p, float* ep, const f32x16 (&acc)[2][4], int col,
                                              int64_t r0, int tid) {
   constexpr int PW = pass_width<kD>();
+  constexpr int ES = ep_stride<kD>();
   constexpr int G = kD / 4;          // lanes per (token, head)
   constexpr int HP = PW / kD;        // heads per pass
   constexpr int NR = kThreads / G / HP;   // token ranges per pass
@@ -175,8 +180,9 @@ __device__ __forceinline__ void kvq_epilogue(const InParams& p, float* ep, const
 #pragma unroll
       for (int ct = pp * PW / 32; ct < (pp + 1) * PW / 32; ++ct)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          ep[(64 * wv + 32 * rt + acc_row(r, lane)) * PW + 32 * ct - pp * PW + (lane & 31)] = acc[rt][ct][r];
+        for (int g = 0; g < 4; ++g)   // registers 4g .. 4g+3: channels acc_row(4g, lane) .. +3 of token lane % 32
+          *(float4*)(ep + (64 * wv + 32 * rt + (lane & 31)) * ES + 32 * ct - pp * PW + acc_row(4 * g, lane)) =
+              make_float4(acc[rt][ct][4 * g], acc[rt][ct][4 * g + 1], acc[rt][ct][4 * g + 2], acc[rt][ct][4 * g + 3]);
     __syncthreads();
 
     const int cl = hp * kD + 4 * sl;                 // channel within the pass
@@ -199,9 +205,9 @@ __device__ __forceinline__ void kvq_epilogue(const InParams& p, float* ep, const
     uint16_t* dst = base + ((bb * p.H + h) * p.N + t) * kD + cq;
     // the three previous rows' projections (rows before the tile's halo
     // are never needed: i0 - tau < 0 only for taps tau >= w, which are 0)
-    float4 w1 = p.w > 1 ? *(const float4*)(ep + (i0 - 1) * PW + cl) : make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 w2 = p.w > 2 ? *(const float4*)(ep + (i0 - 2) * PW + cl) : make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 w3 = p.w > 3 ? *(const float4*)(ep + (i0 - 3) * PW + cl) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 w1 = p.w > 1 ? *(const float4*)(ep + (i0 - 1) * ES + cl) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 w2 = p.w > 2 ? *(const float4*)(ep + (i0 - 2) * ES + cl) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 w3 = p.w > 3 ? *(const float4*)(ep + (i0 - 3) * ES + cl) : make_float4(0.f, 0.f, 0.f, 0.f);
     auto emit = [&](const float4& c, const float4& a1, const float4& a2, const float4& a3, uint16_t* o) {
       const float u0 = tap[0][0] * c.x + tap[0][1] * a1.x + tap[0][2] * a2.x + tap[0][3] * a3.x;
       const float u1 = tap[1][0] * c.y + tap[1][1] * a1.y + tap[1][2] * a2.y + tap[1][3] * a3.y;
@@ -227,10 +233,10 @@ __device__ __forceinline__ void kvq_epilogue(const InParams& p, float* ep, const
       // advances by one head row per token
       int i = i0;
       for (; i + 4 <= iend; i += 4) {
-        const float4 c0 = *(const float4*)(ep + (i + 0) * PW + cl);
-        const float4 c1 = *(const float4*)(ep + (i + 1) * PW + cl);
-        const float4 c2 = *(const float4*)(ep + (i + 2) * PW + cl);
-        const float4 c3 = *(const float4*)(ep + (i + 3) * PW + cl);
+        const float4 c0 = *(const float4*)(ep + (i + 0) * ES + cl);
+        const float4 c1 = *(const float4*)(ep + (i + 1) * ES + cl);
+        const float4 c2 = *(const float4*)(ep + (i + 2) * ES + cl);
+        const float4 c3 = *(const float4*)(ep + (i + 3) * ES + cl);
         emit(c0, w1, w2, w3, dst);
         emit(c1, c0, w1, w2, dst + kD);
         emit(c2, c1, c0, w1, dst + 2 * kD);
@@ -241,7 +247,7 @@ __device__ __forceinline__ void kvq_epilogue(const InParams& p, float* ep, const
         w1 = c3;
       }
       for (; i < iend; ++i) {
-        const float4 c0 = *(const float4*)(ep + i * PW + cl);
+        const float4 c0 = *(const float4*)(ep + i * ES + cl);
         emit(c0, w1, w2, w3, dst);
         dst += kD;
         w3 = w2;
@@ -252,7 +258,7 @@ __device__ __forceinline__ void kvq_epilogue(const InParams& p, float* ep, const
       // a sequence starts inside the range (or just before it): taps that
       // would reach before the start are dropped
       for (int i = i0; i < iend; ++i) {
-        const float4 c0 = *(const float4*)(ep + i * PW + cl);
+        const float4 c0 = *(const float4*)(ep + i * ES + cl);
         emit(c0, t >= 1 ? w1 : z4, t >= 2 ? w2 : z4, t >= 3 ? w3 : z4, dst);
         w3 = w2;
         w2 = w1;
@@ -285,9 +291,9 @@ __device__ __forceinline__ void gate_epilogue(const InParams& p, float* ep, cons
 #pragma unroll
       for (int ct = 2 * pp; ct < 2 * pp + 2; ++ct)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          ep[(64 * wv + 32 * rt + acc_row(r, lane)) * kGateStride + 32 * (ct - 2 * pp) + (lane & 31)] =
-              acc[rt][ct][r];
+        for (int g = 0; g < 4; ++g)
+          *(float4*)(ep + (64 * wv + 32 * rt + (lane & 31)) * kGateStride + 32 * (ct - 2 * pp) + acc_row(4 * g, lane)) =
+              make_float4(acc[rt][ct][4 * g], acc[rt][ct][4 * g + 1], acc[rt][ct][4 * g + 2], acc[rt][ct][4 * g + 3]);
     __syncthreads();
     if (!live) continue;
     for (int c = 0; c < kGatePass; ++c) {
@@ -354,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 2) void input_kernel(InParams p) {
 #pragma unroll
       for (int r = 0; r < 2; ++r)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[r][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r], b[q], acc[r][q], 0, 0, 0);
+        for (int q = 0; q < 4; ++q) acc[r][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[q], a[r], acc[r][q], 0, 0, 0);
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stage fully read before its refill
   }
