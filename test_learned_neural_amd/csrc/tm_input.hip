@@ -23,10 +23,13 @@
 //   stored at chunk ^ ((row >> 1) & 3) so that the fragment reads of eight
 //   consecutive rows hit eight different 16-byte bank groups.
 // - Each wave owns 64 token rows x 128 channels: 2 x 4 accumulators of
-//   v_mfma_f32_32x32x16_bf16 (128 fp32 per lane).  bf16 x bf16 products are
-//   exact in fp32; sums are fp32.
-// - Epilogue: the fp32 tile goes through LDS, one pass of max(64, d)
-//   channels at a time; groups of d/4 lanes own one (token, head) with 4
+//   v_mfma_f32_32x32x16_bf16 (128 fp32 per lane), computed transposed
+//   (weights as the first operand: accumulator rows are channels, lanes are
+//   tokens).  bf16 x bf16 products are exact in fp32; sums are fp32.
+// - Epilogue: the fp32 tile goes through LDS (each lane's four consecutive
+//   channels of a token as one 16-byte store, rows padded to 68 floats), one
+//   pass of max(64, d) channels at a time; groups of d/4 lanes own one
+//   (token, head) with 4
 //   channels per lane for the convolution, SiLU, the head's sum of squares
 //   (lane shuffles), the normalisation and the bf16 store (8 bytes per lane,
 //   a head row per group).  Gate tiles read logits from a padded LDS copy
