@@ -82,7 +82,7 @@ extern "C" {
                                      time-invariant) */
 
 /* kernel paths reported by titans_mem_select_path */
-#define TM_PATH_GENERIC_F32   0   /* any shape: fp32 VALU, state in global memory */
+#define TM_PATH_GENERIC_F32   0   /* any shape: fp32 (matrix instructions), state in global memory */
 #define TM_PATH_MLP2_D64_H256 1   /* 2-layer, d=64, hidden=256, chunk<=64, bf16 io, either read mode:
                                      MFMA, register-resident state */
 
