@@ -317,7 +317,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the memory's (batch, head) streams are independent "
-              "and this build runs them on a single device; --gpus must be 1", file=sys.stderr)
+              "and this benchmark runs them on a single device; --gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

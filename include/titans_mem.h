@@ -57,7 +57,7 @@ extern "C" {
 /* status codes */
 #define TM_OK               0
 #define TM_ERR_INVALID     -1  /* null pointer, dimension <= 0, chunk <= 0, misaligned pointer, bad enum, wrong abi_version */
-#define TM_ERR_UNSUPPORTED -2  /* shape / dtype / flag combination this build has no kernel for */
+#define TM_ERR_UNSUPPORTED -2  /* shape / dtype / flag combination the library has no kernel for */
 #define TM_ERR_WORKSPACE   -3  /* workspace smaller than titans_mem_workspace_bytes() */
 #define TM_ERR_ALIAS       -4  /* illegal overlap between buffers */
 #define TM_ERR_HIP         -5  /* the HIP runtime reported an error when launching */
