@@ -89,7 +89,15 @@ struct GParams {
   float* ws;
   int64_t ws_stride;  // floats per stream
   WsLayout lay;
+  int lds_state;      // 1: the state and the workspace live in LDS for the whole sweep
+  int64_t P4;         // P rounded up to a multiple of 4 (LDS layout: W, S, workspace)
 };
+
+// Small problems keep the state (W, S) and the chunk workspace in LDS for the
+// whole sweep, copied in at the start and out at the end: every contraction
+// then reads and writes LDS instead of global memory.  Budget for that
+// dynamic LDS, beside the contractions' own staging area.
+constexpr int64_t kLdsStateBytes = 120 * 1024;
 
 __device__ __forceinline__ float logistic(float z) { return 1.0f / (1.0f + __expf(-z)); }
 __device__ __forceinline__ float silu(float z) { return z * logistic(z); }
@@ -112,18 +120,22 @@ __device__ __forceinline__ void store_io(void* p, int64_t i, float x, int io) {
 
 
 __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
+  extern __shared__ __attribute__((aligned(16))) float dyn_lds[];
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
   const int d = p.d, L = p.L;
-  float* W = p.W + (int64_t)s * p.state_stride;
-  float* S = p.S + (int64_t)s * p.state_stride;
+  float* const Wg = p.W + (int64_t)s * p.state_stride;
+  float* const Sg = p.S + (int64_t)s * p.state_stride;
   const float* Win = p.W_in + (int64_t)s * p.P;
   const float* Sin = p.S_in + (int64_t)s * p.P;
+  const bool in_lds = p.lds_state && p.N > 0;
+  float* const W = in_lds ? dyn_lds : Wg;
+  float* const S = in_lds ? dyn_lds + p.P4 : Sg;
   if (W != Win) each((int)p.P, [&](int i) { return Win[i]; }, [&](int i, float x) { W[i] = x; });
   if (S != Sin) each((int)p.P, [&](int i) { return Sin[i]; }, [&](int i, float x) { S[i] = x; });
   __syncthreads();
   if (p.N == 0) return;
-  float* const wsb = p.ws + (int64_t)s * p.ws_stride;
+  float* const wsb = in_lds ? dyn_lds + 2 * p.P4 : p.ws + (int64_t)s * p.ws_stride;
   const WsLayout& lay = p.lay;
   struct {
     float *vin, *sc, *D, *A, *E, *F, *U;
@@ -357,6 +369,10 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
     }
     __syncthreads();
   }
+  if (in_lds) {   // the final state back to global memory
+    each((int)p.P, [&](int i) { return W[i]; }, [&](int i, float x) { Wg[i] = x; });
+    each((int)p.P, [&](int i) { return S[i]; }, [&](int i, float x) { Sg[i] = x; });
+  }
 }
 
 // y = M_W(q) for a tile of tokens; activations ping-pong through LDS.
@@ -395,6 +411,24 @@ __global__ void __launch_bounds__(kThreads) retrieve_kernel(GParams p) {
     h = hn;
     hn = t;
   }
+}
+
+// LDS mode when the state and the workspace fit the budget; returns the
+// dynamic LDS bytes of the launch (0: global memory)
+int set_lds_mode(GParams& p) {
+  p.P4 = (p.P + 3) / 4 * 4;
+  const int64_t bytes = (2 * p.P4 + p.lay.total) * (int64_t)sizeof(float);
+  p.lds_state = p.N > 0 && bytes <= kLdsStateBytes;
+  return p.lds_state ? (int)bytes : 0;
+}
+
+hipError_t launch_generic_kernel(const GParams& p, int streams, int lds, hipStream_t stream) {
+  if (lds > 0) {
+    const hipError_t e = hipFuncSetAttribute((const void*)generic_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(generic_kernel, dim3(streams), dim3(kThreads), lds, stream, p);
+  return hipGetLastError();
 }
 
 GParams make_params(const Shape& s, int chunk) {
@@ -440,8 +474,7 @@ hipError_t launch_generic(const Shape& s, int chunk, const void* k, const void* 
   p.ckpt_stride = 0;
   p.ws = ws;
   p.ws_stride = generic_ws_floats_per_stream(s, p.b);
-  hipLaunchKernelGGL(generic_kernel, dim3(s.streams), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+  return launch_generic_kernel(p, s.streams, set_lds_mode(p), stream);
 }
 
 hipError_t launch_generic_checkpoints(const Shape& s, int chunk, const void* k, const void* v, const void* q,
@@ -467,8 +500,7 @@ hipError_t launch_generic_checkpoints(const Shape& s, int chunk, const void* k, 
   p.ckpt_stride = ckpt_stride;
   p.ws = ws;
   p.ws_stride = ws_stride;
-  hipLaunchKernelGGL(generic_kernel, dim3(s.streams), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+  return launch_generic_kernel(p, s.streams, set_lds_mode(p), stream);
 }
 
 hipError_t launch_retrieve_generic(const Shape& s, const void* q, const float* W, void* y,
