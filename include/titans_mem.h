@@ -182,8 +182,12 @@ int titans_mem_retrieve(const titans_mem_desc* desc, const void* q, const float*
  * are read exactly).  Outputs must not overlap each other or any input.
  * Supported: every layer width a multiple of 4, at most 1024, N >= 1,
  * chunk <= 4096 (TM_ERR_UNSUPPORTED otherwise).
- * The workspace holds (W, S) at every chunk start and one chunk's token
+ * The workspace holds (W, S) at every chunk start and two chunks' token
  * vectors: titans_mem_backward_workspace_bytes(desc, chunk) bytes.
+ * The work is ordered on `stream`; part of it runs on a second stream of
+ * the library's own (one per device, created on the first call, default
+ * priority), forked from and joined back into `stream` with events, so
+ * work enqueued on `stream` after the call sees every result.
  */
 int64_t titans_mem_backward_workspace_bytes(const titans_mem_desc* desc, int32_t chunk);
 

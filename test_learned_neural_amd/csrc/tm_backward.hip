@@ -48,15 +48,20 @@
 //
 // Execution: a forward sweep (the generic kernel's chunked closed form,
 // without retrieval) stores (W, S) at every chunk start in the workspace;
-// then one workgroup per stream walks the chunks backwards.  Every product
-// is block_gemm (fp32 on the matrix cores); the chunk's vectors live in a
-// per-stream workspace region, the adjoints (Wbar, Sbar) in dW_in, dS_in.
+// then the chunks are walked backwards, one workgroup per stream and two
+// launches per chunk: the part of a chunk that does not depend on the
+// carried adjoints (inputs, coefficients, key side, reads) runs on a second
+// stream one chunk ahead of the rest, so the two overlap on the device.
+// Every product is block_gemm (fp32 on the matrix cores); a chunk's vectors
+// live in one of two per-stream workspace regions (chunk parity), the
+// adjoints (Wbar, Sbar) in dW_in, dS_in.
 #include "tm_internal.h"
 #include "tm_block_gemm.h"
 
 #include <hip/hip_bf16.h>
 
 #include <algorithm>
+#include <mutex>
 
 namespace titans {
 namespace {
@@ -114,7 +119,8 @@ struct BwdParams {
   float* dS_in;       // Sbar during the sweep
   float* ws;
   int64_t ws_stream;  // floats per stream
-  int64_t o_buf;      // offset of the reverse sweep's region (checkpoints before it)
+  int64_t o_buf;      // offset of the reverse sweep's two regions (checkpoints before them)
+  int64_t region;     // floats per region
   BwLayout lay;
 };
 
@@ -188,24 +194,35 @@ __device__ void row_dots(float* out, const float* X, int ldx, const float* Y, in
   }
 }
 
-__global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
+// One chunk c of the reverse sweep, one workgroup per stream, in two phases
+// launched separately: kProduce (the chunk's inputs, coefficients, key side
+// and the reads -- nothing that depends on the carried adjoints) and
+// kConsume (the fold, the inner gradient's backward, the state adjoints and
+// the gates).  Chunk c's phase-1 results sit in workspace region c % 2, so
+// phase 1 of chunk c - 1 can run beside phase 2 of chunk c.
+enum { kProduce = 1, kConsume = 2 };
+
+__global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p, int c, int phase) {
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
   const int L = p.L, d = p.d, bb = p.b, mw = p.maxw;
   const int64_t P = p.P;
   float* const Wb = p.dW_in + (int64_t)s * P;
   float* const Sb = p.dS_in + (int64_t)s * P;
-  each(
-      (int)P,
-      [&](int i) {
-        return make_float2(p.dW_out ? p.dW_out[(int64_t)s * P + i] : 0.f, p.dS_out ? p.dS_out[(int64_t)s * P + i] : 0.f);
-      },
-      [&](int i, float2 x) {
-        Wb[i] = x.x;
-        Sb[i] = x.y;
-      });
+  if (phase == kConsume && c == p.nchunks - 1) {
+    each(
+        (int)P,
+        [&](int i) {
+          return make_float2(p.dW_out ? p.dW_out[(int64_t)s * P + i] : 0.f, p.dS_out ? p.dS_out[(int64_t)s * P + i] : 0.f);
+        },
+        [&](int i, float2 x) {
+          Wb[i] = x.x;
+          Sb[i] = x.y;
+        });
+    __syncthreads();
+  }
   float* const base = p.ws + (int64_t)s * p.ws_stream;
-  float* const wsb = base + p.o_buf;
+  float* const wsb = base + p.o_buf + (int64_t)(c & 1) * p.region;
   const BwLayout& y = p.lay;
   auto V = [&](int64_t o) { return wsb + o; };
   float* const red = V(y.red);
@@ -232,20 +249,18 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
   const bool reads = p.dy != nullptr;
   const bool cstart = p.read_mode == TM_READ_CHUNK_START;
   const int64_t tok0 = (int64_t)s * p.N;
-  __syncthreads();
+  const int c0 = c * p.chunk;
+  const int n = min(p.chunk, p.N - c0);
+  const float* const W = base + (int64_t)c * 2 * P;   // chunk-start checkpoint
+  const float* const S = W + P;
+  const int64_t g0 = p.chunk_gates ? (int64_t)s * p.nchunks + c : tok0 + c0;
+  const int gs = p.chunk_gates ? 0 : 1;
+  const float* al = p.alpha + g0;
+  const float* et = p.eta + g0;
+  const float* th = p.theta + g0;
+  const int64_t row0 = tok0 + c0;                     // first token row of the chunk
 
-  for (int c = p.nchunks - 1; c >= 0; --c) {
-    const int c0 = c * p.chunk;
-    const int n = min(p.chunk, p.N - c0);
-    const float* const W = base + (int64_t)c * 2 * P;   // chunk-start checkpoint
-    const float* const S = W + P;
-    const int64_t g0 = p.chunk_gates ? (int64_t)s * p.nchunks + c : tok0 + c0;
-    const int gs = p.chunk_gates ? 0 : 1;
-    const float* al = p.alpha + g0;
-    const float* et = p.eta + g0;
-    const float* th = p.theta + g0;
-    const int64_t row0 = tok0 + c0;                       // first token row of the chunk
-
+  if (phase == kProduce) {
     // ---- chunk inputs; adjoint accumulators cleared ----
     {
       float* a0 = V(y.act[0]);
@@ -537,6 +552,8 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
       }
     }
 
+  }   // kProduce
+  if (phase == kConsume) {
     // ---- the fold's adjoint (Wbar, Sbar of the chunk end) ----
     for (int l = 1; l <= L; ++l) {
       const int nin = p.w[l - 1], nout = p.w[l];
@@ -846,8 +863,7 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p) {
         p.dtheta[g0 + t] = gt[t];
       }
     }
-    __syncthreads();
-  }
+  }   // kConsume
 }
 
 BwLayout bw_layout(const Shape& s, int b) {
@@ -900,6 +916,32 @@ BwLayout bw_layout(const Shape& s, int b) {
 
 int rows_per_chunk(const Shape& s, int chunk) { return chunk < s.N ? chunk : s.N; }
 
+int64_t bw_region_floats(const Shape& s, int b) { return (bw_layout(s, b).total + 63) / 64 * 64; }
+
+// The second stream of the reverse sweep and the events that order it
+// against the caller's stream, created once per device (default priority)
+// and kept until the process ends.  Calls are serialised while they enqueue.
+struct SideStream {
+  hipStream_t st = nullptr;
+  hipEvent_t fork = nullptr, prod[2] = {nullptr, nullptr}, cons[2] = {nullptr, nullptr};
+};
+std::mutex g_side_mu;
+SideStream g_side[64];
+
+hipError_t side_stream(int dev, SideStream** out) {
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!g_side[dev].st) {
+    SideStream x;
+    hipError_t e = hipStreamCreateWithFlags(&x.st, hipStreamNonBlocking);
+    hipEvent_t* evs[5] = {&x.fork, &x.prod[0], &x.prod[1], &x.cons[0], &x.cons[1]};
+    for (int i = 0; i < 5 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(evs[i], hipEventDisableTiming);
+    if (e != hipSuccess) return e;   // (what was created is kept: a few handles)
+    g_side[dev] = x;
+  }
+  *out = &g_side[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 bool backward_supported(const Shape& s, int chunk) {
@@ -915,9 +957,9 @@ bool backward_supported(const Shape& s, int chunk) {
 int64_t backward_ws_floats_per_stream(const Shape& s, int chunk) {
   const int64_t nchunks = (s.N + chunk - 1) / chunk;
   const int b = rows_per_chunk(s, chunk);
-  // the forward sweep's workspace and the reverse sweep's region share the
-  // space after the checkpoints (the sweep ends before the reverse starts)
-  const int64_t region = std::max(bw_layout(s, b).total, generic_ws_floats_per_stream(s, b));
+  // the forward sweep's workspace and the reverse sweep's two regions share
+  // the space after the checkpoints (the sweep ends before the reverse starts)
+  const int64_t region = std::max(2 * bw_region_floats(s, b), generic_ws_floats_per_stream(s, b));
   return nchunks * 2 * s.P + (region + 63) / 64 * 64;
 }
 
@@ -949,14 +991,35 @@ hipError_t launch_backward(const Shape& s, int chunk, const void* k, const void*
   p.ws = ws;
   p.ws_stream = backward_ws_floats_per_stream(s, chunk);
   p.o_buf = (int64_t)p.nchunks * 2 * s.P;
+  p.region = bw_region_floats(s, p.b);
   p.lay = bw_layout(s, p.b);
   // forward sweep: the chunk-start states into the checkpoints; its running
   // state lives in dW_in, dS_in (re-initialised by the reverse sweep)
   hipError_t err = launch_generic_checkpoints(s, chunk, k, v, q, alpha, eta, theta, W_in, S_in, dW_in, dS_in, s.P,
                                               ws, p.ws_stream, ws + p.o_buf, p.ws_stream, stream);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(backward_kernel, dim3(s.streams), dim3(kBT), 0, stream, p);
-  return hipGetLastError();
+  // reverse sweep: chunk c's first phase on the side stream after the second
+  // phase of chunk c + 2 (which used the same region), its second phase on
+  // the caller's stream after its first phase; the last first phase is also
+  // the side stream's last work, so the caller's stream has joined it at the end
+  int dev = 0;
+  if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream* x = nullptr;
+  if ((err = side_stream(dev, &x)) != hipSuccess) return err;
+  if ((err = hipEventRecord(x->fork, stream)) != hipSuccess) return err;
+  if ((err = hipStreamWaitEvent(x->st, x->fork, 0)) != hipSuccess) return err;
+  for (int c = p.nchunks - 1; c >= 0; --c) {
+    if (c + 2 < p.nchunks && (err = hipStreamWaitEvent(x->st, x->cons[c & 1], 0)) != hipSuccess) return err;
+    hipLaunchKernelGGL(backward_kernel, dim3(s.streams), dim3(kBT), 0, x->st, p, c, (int)kProduce);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = hipEventRecord(x->prod[c & 1], x->st)) != hipSuccess) return err;
+    if ((err = hipStreamWaitEvent(stream, x->prod[c & 1], 0)) != hipSuccess) return err;
+    hipLaunchKernelGGL(backward_kernel, dim3(s.streams), dim3(kBT), 0, stream, p, c, (int)kConsume);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = hipEventRecord(x->cons[c & 1], stream)) != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace titans
