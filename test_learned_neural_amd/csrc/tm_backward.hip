@@ -326,7 +326,9 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p, int c, int p
       }
       cU[i] = ti * pr;
     }
-    if (tid == 0) {
+    // A, E, F on the last thread, whose columns above are the shortest, so
+    // its recurrence runs beside the long ones of the first wave
+    if (tid == kBT - 1) {
       float a = 1.f, e = 1.f, f = 0.f;
       for (int t0 = 0; t0 < n; t0 += kBatch) {
         float ev[kBatch], av[kBatch];
@@ -774,7 +776,7 @@ __global__ void __launch_bounds__(kBT) backward_kernel(BwdParams p, int c, int p
       dacc += Dbar[(int64_t)i * bb + i];
       gt[i] = tb + dacc;                        // D[i,i] = theta_i
     }
-    if (tid == 0) {
+    if (tid == kBT - 1) {   // beside the column recurrences, as in the forward coefficients
       float abar = 0.f, fbar = 0.f, ebar = sSS;
       for (int t0 = n - 1; t0 >= 0; t0 -= kBatch) {
         float am[kBatch], em[kBatch], fm[kBatch], ab[kBatch], fb[kBatch], ev[kBatch], av[kBatch];
