@@ -920,18 +920,17 @@ int rows_per_chunk(const Shape& s, int chunk) { return chunk < s.N ? chunk : s.N
 
 int64_t bw_region_floats(const Shape& s, int b) { return (bw_layout(s, b).total + 63) / 64 * 64; }
 
-// The second stream of the reverse sweep and the events that order it
-// against the caller's stream, created once per device (default priority)
-// and kept until the process ends.  Calls are serialised while they enqueue.
-struct SideStream {
-  hipStream_t st = nullptr;
-  hipEvent_t fork = nullptr, prod[2] = {nullptr, nullptr}, cons[2] = {nullptr, nullptr};
-};
+
+}  // namespace
+
+namespace {
 std::mutex g_side_mu;
 SideStream g_side[64];
+}  // namespace
 
-hipError_t side_stream(int dev, SideStream** out) {
+hipError_t side_stream(int dev, SideStream** out, std::unique_lock<std::mutex>& lock) {
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  lock = std::unique_lock<std::mutex>(g_side_mu);
   if (!g_side[dev].st) {
     SideStream x;
     hipError_t e = hipStreamCreateWithFlags(&x.st, hipStreamNonBlocking);
@@ -943,8 +942,6 @@ hipError_t side_stream(int dev, SideStream** out) {
   *out = &g_side[dev];
   return hipSuccess;
 }
-
-}  // namespace
 
 bool backward_supported(const Shape& s, int chunk) {
   // the chunk bound of the forward sweep (the generic kernel); it also keeps
@@ -1006,9 +1003,9 @@ hipError_t launch_backward(const Shape& s, int chunk, const void* k, const void*
   // the side stream's last work, so the caller's stream has joined it at the end
   int dev = 0;
   if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
-  std::lock_guard<std::mutex> lock(g_side_mu);
+  std::unique_lock<std::mutex> lock;
   SideStream* x = nullptr;
-  if ((err = side_stream(dev, &x)) != hipSuccess) return err;
+  if ((err = side_stream(dev, &x, lock)) != hipSuccess) return err;
   if ((err = hipEventRecord(x->fork, stream)) != hipSuccess) return err;
   if ((err = hipStreamWaitEvent(x->st, x->fork, 0)) != hipSuccess) return err;
   for (int c = p.nchunks - 1; c >= 0; --c) {

@@ -20,13 +20,24 @@
 //         with G(w) = sum_j w_j delta_j a_j^T
 //
 // The state lives in W_out/S_out (global memory) and the chunk's
-// intermediates in a per-stream workspace; every contraction is an fp32 FMA
-// tile loop staged through LDS.  This path serves any shape and the fp32-io
-// linear memory, and is the fallback where no specialised kernel exists.
+// intermediates in a per-stream workspace; every contraction is an fp32
+// matrix-instruction tile loop staged through LDS.  This path serves any
+// shape and the fp32-io linear memory, and is the fallback where no
+// specialised kernel exists.
+//
+// A large state with few streams leaves most CUs idle with one workgroup per
+// stream; there the forward call runs one chunk per launch in two phases:
+// the sweep (a1-a4, on the caller's stream) and the reads (a5, on a second
+// stream), which depend on the chunk-start state but not on the fold, so the
+// reads of chunk c run beside the sweep of chunk c + 1.  The chunk-start
+// states rotate through three buffers (the last one is W_out/S_out) and the
+// chunk's intermediates through two workspace regions.
 #include "tm_internal.h"
 #include "tm_block_gemm.h"
 
 #include <hip/hip_bf16.h>
+
+#include <mutex>
 
 namespace titans {
 namespace {
@@ -84,6 +95,7 @@ struct GParams {
   float* W;
   float* S;
   int64_t state_stride;   // floats between streams in W, S (P unless they live in another layout)
+  int64_t in_stride;      // floats between streams in W_in, S_in
   float* ckpt;        // optional: (W, S) at every chunk start, [chunk][W | S] per stream
   int64_t ckpt_stride;    // floats between streams in ckpt
   float* ws;
@@ -91,7 +103,10 @@ struct GParams {
   WsLayout lay;
   int lds_state;      // 1: the state and the workspace live in LDS for the whole sweep
   int64_t P4;         // P rounded up to a multiple of 4 (LDS layout: W, S, workspace)
+  int64_t region;     // floats between the two workspace regions of the per-chunk launches
 };
+
+enum { kSweep = 1, kReads = 2, kBoth = 3 };
 
 // Small problems keep the state (W, S) and the chunk workspace in LDS for the
 // whole sweep, copied in at the start and out at the end: every contraction
@@ -119,23 +134,33 @@ __device__ __forceinline__ void store_io(void* p, int64_t i, float x, int io) {
 }
 
 
-__global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
+// cs < 0: every chunk in order, the state folded in place in (W, S) after a
+// copy from (W_in, S_in).  cs >= 0: chunk cs only, its start state read from
+// (W_in, S_in) and the folded state written to (W, S); `phase` selects the
+// sweep (a1-a4) and/or the reads (a5).
+__global__ void __launch_bounds__(kThreads) generic_kernel(GParams p, int cs, int phase) {
   extern __shared__ __attribute__((aligned(16))) float dyn_lds[];
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
   const int d = p.d, L = p.L;
+  const bool one = cs >= 0;
+  const bool sweep = phase & kSweep, rd = (phase & kReads) && p.y;
   float* const Wg = p.W + (int64_t)s * p.state_stride;
   float* const Sg = p.S + (int64_t)s * p.state_stride;
-  const float* Win = p.W_in + (int64_t)s * p.P;
-  const float* Sin = p.S_in + (int64_t)s * p.P;
-  const bool in_lds = p.lds_state && p.N > 0;
+  const float* Win = p.W_in + (int64_t)s * p.in_stride;
+  const float* Sin = p.S_in + (int64_t)s * p.in_stride;
+  const bool in_lds = p.lds_state && p.N > 0;   // (never with one chunk per launch)
   float* const W = in_lds ? dyn_lds : Wg;
   float* const S = in_lds ? dyn_lds + p.P4 : Sg;
-  if (W != Win) each((int)p.P, [&](int i) { return Win[i]; }, [&](int i, float x) { W[i] = x; });
-  if (S != Sin) each((int)p.P, [&](int i) { return Sin[i]; }, [&](int i, float x) { S[i] = x; });
+  const float* const Wr = one ? Win : W;   // the chunk-start state this launch reads
+  const float* const Sr = one ? Sin : S;
+  if (!one) {
+    if (W != Win) each((int)p.P, [&](int i) { return Win[i]; }, [&](int i, float x) { W[i] = x; });
+    if (S != Sin) each((int)p.P, [&](int i) { return Sin[i]; }, [&](int i, float x) { S[i] = x; });
+  }
   __syncthreads();
   if (p.N == 0) return;
-  float* const wsb = in_lds ? dyn_lds + 2 * p.P4 : p.ws + (int64_t)s * p.ws_stride;
+  float* const wsb = (in_lds ? dyn_lds + 2 * p.P4 : p.ws + (int64_t)s * p.ws_stride) + (one ? (int64_t)(cs & 1) * p.region : 0);
   const WsLayout& lay = p.lay;
   struct {
     float *vin, *sc, *D, *A, *E, *F, *U;
@@ -146,18 +171,20 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
   auto hq = [&](int i) { return wsb + lay.hq[i]; };
   const int64_t tok0 = (int64_t)s * p.N;
 
-  for (int c0 = 0; c0 < p.N; c0 += p.chunk) {
+  for (int c0 = one ? cs * p.chunk : 0; c0 < p.N; c0 += p.chunk) {
     const int n = min(p.chunk, p.N - c0);
     if (p.ckpt) {
       // the state at this chunk's start (read only here; it is next written
       // by this chunk's fold, many barriers later)
       float* ck = p.ckpt + (int64_t)s * p.ckpt_stride + (int64_t)(c0 / p.chunk) * 2 * p.P;
       each(
-          (int)p.P, [&](int i) { return make_float2(W[i], S[i]); },
+          (int)p.P, [&](int i) { return make_float2(Wr[i], Sr[i]); },
           [&](int i, float2 x) {
             ck[i] = x.x;
             ck[p.P + i] = x.y;
           });
+      // a sweep for checkpoints only ends at the last chunk's start
+      if (!p.y && c0 + p.chunk >= p.N) break;
     }
     // the chunk's gates: token j at index j * gs (one shared value when the
     // gates are given per chunk)
@@ -171,22 +198,24 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
     {
       float* a0 = act(0);
       float* q0 = hq(0);
-      const bool rq = p.y != nullptr;
       each(
           n * d,
           [&](int e) {
             const int64_t gi = (tok0 + c0) * d + e;
-            return make_float3(load_io(p.k, gi, p.io), load_io(p.v, gi, p.io), rq ? load_io(p.q, gi, p.io) : 0.f);
+            return make_float3(sweep ? load_io(p.k, gi, p.io) : 0.f, sweep ? load_io(p.v, gi, p.io) : 0.f,
+                               rd ? load_io(p.q, gi, p.io) : 0.f);
           },
           [&](int e, float3 x) {
-            a0[e] = x.x;
-            w.vin[e] = x.y;
-            if (rq) q0[(e / d) * p.maxw + (e % d)] = x.z;
+            if (sweep) {
+              a0[e] = x.x;
+              w.vin[e] = x.y;
+            }
+            if (rd) q0[(e / d) * p.maxw + (e % d)] = x.z;
           });
     }
     // ---- a1: coefficient recurrences (one thread per column i of D) ----
     // (gates read kBatch steps ahead of the stores, which may alias them)
-    for (int i = tid; i < n; i += kThreads) {
+    for (int i = tid; i < n && sweep; i += kThreads) {
       const float ti = th[i * gs];
       float di = ti, pr = 1.f;
       for (int j = 0; j < i; ++j) w.D[j * n + i] = 0.f;
@@ -210,7 +239,9 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
       }
       w.U[i] = ti * pr;
     }
-    if (tid == 0) {
+    // A, E, F on the last thread, whose columns above are the shortest, so
+    // its recurrence runs beside the long ones of the first wave
+    if (tid == kThreads - 1 && sweep) {
       float a = 1.f, e = 1.f, f = 0.f;
       for (int j0 = 0; j0 < n; j0 += kBatch) {
         float ev[kBatch], av[kBatch];
@@ -236,9 +267,9 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
     __syncthreads();
 
     // ---- a2: key-side forward at the chunk-start weights ----
-    for (int l = 1; l <= L; ++l) {
+    for (int l = 1; l <= L && sweep; ++l) {
       const int nin = p.widths[l - 1], nout = p.widths[l];
-      const float* Wl = W + p.off[l];
+      const float* Wl = Wr + p.off[l];
       const float* ain = act(l - 1);
       float* aout = act(l);
       float* spl = spv(l);
@@ -262,9 +293,9 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
           });
     }
     // ---- a3: backprop to every layer's delta ----
-    for (int l = L; l >= 2; --l) {
+    for (int l = L; l >= 2 && sweep; --l) {
       const int nin = p.widths[l - 1], nout = p.widths[l];
-      const float* Wl = W + p.off[l];
+      const float* Wl = Wr + p.off[l];
       const float* dl = delta(l);
       float* dprev = delta(l - 1);
       const float* spp = spv(l - 1);
@@ -278,10 +309,10 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
     }
     // ---- a5: retrieval ----
     int cur = 0;
-    for (int l = 1; l <= L && p.y; ++l) {
+    for (int l = 1; l <= L && rd; ++l) {
       const int nin = p.widths[l - 1], nout = p.widths[l];
-      const float* Wl = W + p.off[l];
-      const float* Sl = S + p.off[l];
+      const float* Wl = Wr + p.off[l];
+      const float* Sl = Sr + p.off[l];
       const float* h = hq(cur);
       float* hn = hq(cur ^ 1);
       const float* ak = act(l - 1);
@@ -338,14 +369,16 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
       cur ^= 1;
     }
     // ---- a4: fold the chunk into the state (after every read of W_0, S_0) ----
-    {
+    if (sweep) {
       const float An = w.A[n - 1], En = w.E[n - 1], Fn = w.F[n - 1];
       const float* Dlast = w.D + (n - 1) * n;
       const float* U = w.U;
       for (int l = 1; l <= L; ++l) {
         const int nin = p.widths[l - 1], nout = p.widths[l];
-        float* Wl = W + p.off[l];
-        float* Sl = S + p.off[l];
+        const float* Wl = Wr + p.off[l];
+        const float* Sl = Sr + p.off[l];
+        float* Wo = W + p.off[l];
+        float* So = S + p.off[l];
         const float* dl = delta(l);
         const float* ak = act(l - 1);
         block_gemm<false>(
@@ -356,18 +389,19 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p) {
               return An * Wl[i] + Fn * Sl[i];
             },
             [=](int r, int c, float g, float base, bool ok) {
-              if (ok) Wl[(int64_t)r * nin + c] = base - g;
+              if (ok) Wo[(int64_t)r * nin + c] = base - g;
             });
         block_gemm<false>(
             nout, nin, n, [=](int r, int j) { return U[j] * dl[j * nout + r]; },
             [=](int j, int c) { return ak[j * nin + c]; }, kB_NMAJOR,
             [=](int r, int c) { return En * Sl[(int64_t)r * nin + c]; },
             [=](int r, int c, float g, float base, bool ok) {
-              if (ok) Sl[(int64_t)r * nin + c] = base - g;
+              if (ok) So[(int64_t)r * nin + c] = base - g;
             });
       }
     }
     __syncthreads();
+    if (one) break;
   }
   if (in_lds) {   // the final state back to global memory
     each((int)p.P, [&](int i) { return W[i]; }, [&](int i, float x) { Wg[i] = x; });
@@ -422,13 +456,28 @@ int set_lds_mode(GParams& p) {
   return p.lds_state ? (int)bytes : 0;
 }
 
-hipError_t launch_generic_kernel(const GParams& p, int streams, int lds, hipStream_t stream) {
+hipError_t launch_generic_kernel(const GParams& p, int streams, int lds, hipStream_t stream, int cs = -1,
+                                 int phase = kBoth) {
   if (lds > 0) {
     const hipError_t e = hipFuncSetAttribute((const void*)generic_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(generic_kernel, dim3(streams), dim3(kThreads), lds, stream, p);
+  hipLaunchKernelGGL(generic_kernel, dim3(streams), dim3(kThreads), lds, stream, p, cs, phase);
   return hipGetLastError();
+}
+
+int rows_reserved(const Shape& s, int chunk) { return chunk < s.N ? chunk : (s.N > 0 ? s.N : 1); }
+
+// LDS mode (set_lds_mode) for this shape and chunk
+bool lds_fits(const Shape& s, int b) {
+  return s.N > 0 && (2 * ((s.P + 3) / 4 * 4) + ws_layout(s, b).total) * (int64_t)sizeof(float) <= kLdsStateBytes;
+}
+
+// The forward call runs one chunk per launch, sweep and reads side by side,
+// when the state is too large for LDS (so the per-chunk work is large) and
+// the chunks are long enough for the per-launch cost not to matter.
+bool split_forward(const Shape& s, int chunk) {
+  return !lds_fits(s, rows_reserved(s, chunk)) && chunk >= 16 && s.N > chunk;
 }
 
 GParams make_params(const Shape& s, int chunk) {
@@ -451,12 +500,18 @@ GParams make_params(const Shape& s, int chunk) {
 
 int64_t generic_ws_floats_per_stream(const Shape& s, int b) { return ws_layout(s, b).total; }
 
+int64_t generic_forward_ws_floats_per_stream(const Shape& s, int chunk) {
+  const int64_t region = ws_layout(s, rows_reserved(s, chunk)).total;   // a multiple of 64
+  if (!split_forward(s, chunk)) return region;
+  return 2 * region + 4 * ((s.P + 63) / 64 * 64);   // two regions, two rotating (W, S) buffers
+}
+
 hipError_t launch_generic(const Shape& s, int chunk, const void* k, const void* v, const void* q,
                           const float* alpha, const float* eta, const float* theta,
                           const float* W_in, const float* S_in, void* y, float* W_out,
                           float* S_out, float* ws, hipStream_t stream) {
   GParams p = make_params(s, chunk);
-  p.b = chunk < s.N ? chunk : (s.N > 0 ? s.N : 1);
+  p.b = rows_reserved(s, chunk);
   p.lay = ws_layout(s, p.b);
   p.k = k;
   p.v = v;
@@ -466,6 +521,7 @@ hipError_t launch_generic(const Shape& s, int chunk, const void* k, const void* 
   p.theta = theta;
   p.W_in = W_in;
   p.S_in = S_in;
+  p.in_stride = s.P;
   p.y = y;
   p.W = W_out;
   p.S = S_out;
@@ -473,8 +529,52 @@ hipError_t launch_generic(const Shape& s, int chunk, const void* k, const void* 
   p.ckpt = nullptr;
   p.ckpt_stride = 0;
   p.ws = ws;
-  p.ws_stride = generic_ws_floats_per_stream(s, p.b);
-  return launch_generic_kernel(p, s.streams, set_lds_mode(p), stream);
+  p.ws_stride = generic_forward_ws_floats_per_stream(s, chunk);
+  // (an in-place call keeps the single launch: chunk 0's reads need the
+  // input state after the output buffers have started to rotate)
+  if (!split_forward(s, chunk) || W_out == W_in || S_out == S_in)
+    return launch_generic_kernel(p, s.streams, set_lds_mode(p), stream);
+
+  // One chunk per launch.  Chunk c's start state is buffer c % 3 (c = 0: the
+  // inputs) and its fold goes to buffer (c + 1) % 3; buffer nchunks % 3 is
+  // (W_out, S_out), the other two follow the regions in the workspace.  The
+  // sweep of chunk c waits for the reads of chunk c - 2, which used its
+  // region and its destination buffer; the reads of chunk c wait for its sweep.
+  p.region = p.lay.total;
+  const int nchunks = (s.N + chunk - 1) / chunk;
+  const int64_t pb = (s.P + 63) / 64 * 64;
+  float* wsbuf = ws + 2 * p.region;
+  struct Buf { float *W, *S; int64_t stride; } buf[3];
+  for (int i = 0, j = 0; i < 3; ++i) {
+    if (i == nchunks % 3) {
+      buf[i] = Buf{W_out, S_out, s.P};
+    } else {
+      buf[i] = Buf{wsbuf + 2 * pb * j, wsbuf + 2 * pb * j + pb, p.ws_stride};
+      ++j;
+    }
+  }
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  std::unique_lock<std::mutex> lock;
+  SideStream* x = nullptr;
+  if ((err = side_stream(dev, &x, lock)) != hipSuccess) return err;
+  for (int c = 0; c < nchunks; ++c) {
+    const Buf src = c == 0 ? Buf{(float*)W_in, (float*)S_in, s.P} : buf[c % 3], dst = buf[(c + 1) % 3];
+    p.W_in = src.W;
+    p.S_in = src.S;
+    p.in_stride = src.stride;
+    p.W = dst.W;
+    p.S = dst.S;
+    p.state_stride = dst.stride;
+    if (c >= 2 && (err = hipStreamWaitEvent(stream, x->cons[c & 1], 0)) != hipSuccess) return err;
+    if ((err = launch_generic_kernel(p, s.streams, 0, stream, c, kSweep)) != hipSuccess) return err;
+    if ((err = hipEventRecord(x->prod[c & 1], stream)) != hipSuccess) return err;
+    if ((err = hipStreamWaitEvent(x->st, x->prod[c & 1], 0)) != hipSuccess) return err;
+    if ((err = launch_generic_kernel(p, s.streams, 0, x->st, c, kReads)) != hipSuccess) return err;
+    if ((err = hipEventRecord(x->cons[c & 1], x->st)) != hipSuccess) return err;
+  }
+  return hipStreamWaitEvent(stream, x->cons[(nchunks - 1) & 1], 0);
 }
 
 hipError_t launch_generic_checkpoints(const Shape& s, int chunk, const void* k, const void* v, const void* q,
@@ -492,6 +592,7 @@ hipError_t launch_generic_checkpoints(const Shape& s, int chunk, const void* k, 
   p.theta = theta;
   p.W_in = W_in;
   p.S_in = S_in;
+  p.in_stride = s.P;
   p.y = nullptr;
   p.W = W;
   p.S = S;

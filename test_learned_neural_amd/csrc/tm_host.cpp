@@ -67,8 +67,7 @@ int select_path(const titans_mem_desc* desc, const Shape& s, int chunk) {
 
 int64_t workspace_for(const Shape& s, int path, int chunk) {
   if (path == TM_PATH_MLP2_D64_H256) return titans::mlp2_ws_bytes(s, chunk);
-  const int b = chunk < s.N ? chunk : (s.N > 0 ? s.N : 1);
-  return titans::generic_ws_floats_per_stream(s, b) * (int64_t)sizeof(float) * s.streams;
+  return titans::generic_forward_ws_floats_per_stream(s, chunk) * (int64_t)sizeof(float) * s.streams;
 }
 
 }  // namespace

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "titans_mem.h"
 
 namespace titans {
@@ -24,8 +26,21 @@ struct Shape {
   int maxw;
 };
 
-// Workspace floats per stream of the generic kernel for chunk b.
+// Workspace floats per stream of the generic kernel for chunk b (one region).
 int64_t generic_ws_floats_per_stream(const Shape& s, int b);
+// Workspace floats per stream of launch_generic (the forward call).
+int64_t generic_forward_ws_floats_per_stream(const Shape& s, int chunk);
+
+// The library's second stream on a device and the events that order it
+// against the caller's stream: created on first use (default priority) and
+// kept until the process ends.  side_stream() returns the current device's
+// with `lock` held, which serialises the calls that enqueue on it (each
+// call records every event before waiting on it).
+struct SideStream {
+  hipStream_t st = nullptr;
+  hipEvent_t fork = nullptr, prod[2] = {nullptr, nullptr}, cons[2] = {nullptr, nullptr};
+};
+hipError_t side_stream(int dev, SideStream** out, std::unique_lock<std::mutex>& lock);
 
 hipError_t launch_generic(const Shape& s, int chunk, const void* k, const void* v, const void* q,
                           const float* alpha, const float* eta, const float* theta,
@@ -48,7 +63,8 @@ bool retrieve_mlp2_supported(const Shape& s);
 hipError_t launch_retrieve_mlp2(const Shape& s, const void* q, const float* W, void* y, hipStream_t stream);
 
 // The generic kernel as a state sweep only (no retrieval), writing (W, S) at
-// every chunk start to ckpt; W, S and ckpt are strided per stream.
+// every chunk start to ckpt; W, S and ckpt are strided per stream.  The last
+// chunk is not folded: W, S end at its start state.
 hipError_t launch_generic_checkpoints(const Shape& s, int chunk, const void* k, const void* v, const void* q,
                                       const float* alpha, const float* eta, const float* theta, const float* W_in,
                                       const float* S_in, float* W, float* S, int64_t state_stride, float* ckpt,
