@@ -84,8 +84,12 @@ __device__ void block_gemm_tiles(int M, int N, int K, FA fa, FB fb, FBK bkmaj, F
     const int e = tid + q * kGemmThreads;
     if (kmaj) { nn = e / kGk; kb = e % kGk; } else { kb = e / tn; nn = e % tn; }
   };
-  for (int m0 = 0; m0 < M; m0 += kGemmTile) {
-    for (int n0 = 0; n0 < N; n0 += tn) {
+  // the workgroups of a launch's y dimension share out the output tiles
+  // (one workgroup, gridDim.y == 1, takes them all)
+  const int ntn = (N + tn - 1) / tn, ntiles = ((M + kGemmTile - 1) / kGemmTile) * ntn;
+  for (int tile = blockIdx.y; tile < ntiles; tile += gridDim.y) {
+    {
+      const int m0 = (tile / ntn) * kGemmTile, n0 = (tile % ntn) * tn;
       float ra[kGPerA], rb[kGPerB];
       bool bk = bkmaj(0);
       auto fetch = [&](int k0, bool kmaj) {   // raw values, clamped addresses

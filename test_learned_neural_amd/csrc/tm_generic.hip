@@ -25,18 +25,21 @@
 // shape and the fp32-io linear memory, and is the fallback where no
 // specialised kernel exists.
 //
-// A large state with few streams leaves most CUs idle with one workgroup per
-// stream; there the forward call runs one chunk per launch in two phases:
-// the sweep (a1-a4, on the caller's stream) and the reads (a5, on a second
-// stream), which depend on the chunk-start state but not on the fold, so the
-// reads of chunk c run beside the sweep of chunk c + 1.  The chunk-start
-// states rotate through three buffers (the last one is W_out/S_out) and the
-// chunk's intermediates through two workspace regions.
+// A state too large for LDS leaves most CUs idle with one workgroup per
+// stream; there the forward call runs each chunk in two phases: the sweep
+// (a1-a4, on the caller's stream) and the reads (a5, on a second stream),
+// which depend on the chunk-start state but not on the fold, so the reads of
+// chunk c run beside the sweep of chunk c + 1.  The chunk-start states
+// rotate through three buffers (the last one is W_out/S_out) and the chunk's
+// intermediates through two workspace regions.  With few streams (at most a
+// quarter as many as CUs) every step of a phase is a launch of its own, its
+// contraction's output tiles spread over several workgroups per stream.
 #include "tm_internal.h"
 #include "tm_block_gemm.h"
 
 #include <hip/hip_bf16.h>
 
+#include <algorithm>
 #include <mutex>
 
 namespace titans {
@@ -107,6 +110,10 @@ struct GParams {
 };
 
 enum { kSweep = 1, kReads = 2, kBoth = 3 };
+// One stage per launch (stage != kAllStages): the chunk's inputs and
+// coefficients, or one contraction of one layer, its output tiles shared out
+// over the launch's y dimension.
+enum { kAllStages = 0, kLoad, kKey, kBack, kScores, kRead, kFoldW, kFoldS };
 
 // Small problems keep the state (W, S) and the chunk workspace in LDS for the
 // whole sweep, copied in at the start and out at the end: every contraction
@@ -137,8 +144,8 @@ __device__ __forceinline__ void store_io(void* p, int64_t i, float x, int io) {
 // cs < 0: every chunk in order, the state folded in place in (W, S) after a
 // copy from (W_in, S_in).  cs >= 0: chunk cs only, its start state read from
 // (W_in, S_in) and the folded state written to (W, S); `phase` selects the
-// sweep (a1-a4) and/or the reads (a5).
-__global__ void __launch_bounds__(kThreads) generic_kernel(GParams p, int cs, int phase) {
+// sweep (a1-a4) and/or the reads (a5), `stage` and `layer` one step of them.
+__global__ void __launch_bounds__(kThreads) generic_kernel(GParams p, int cs, int phase, int stage, int layer) {
   extern __shared__ __attribute__((aligned(16))) float dyn_lds[];
   const int s = blockIdx.x;
   const int tid = threadIdx.x;
@@ -170,6 +177,8 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p, int cs, in
   auto delta = [&](int l) { return wsb + lay.delta[l]; };
   auto hq = [&](int i) { return wsb + lay.hq[i]; };
   const int64_t tok0 = (int64_t)s * p.N;
+  const bool all = stage == kAllStages;
+  auto run = [&](int st, int l) { return all || (stage == st && layer == l); };
 
   for (int c0 = one ? cs * p.chunk : 0; c0 < p.N; c0 += p.chunk) {
     const int n = min(p.chunk, p.N - c0);
@@ -195,7 +204,7 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p, int cs, in
     const float* th = p.theta + g0;
 
     // ---- load the chunk's keys, values and queries (fp32 copies) ----
-    {
+    if (all || stage == kLoad) {
       float* a0 = act(0);
       float* q0 = hq(0);
       each(
@@ -215,7 +224,8 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p, int cs, in
     }
     // ---- a1: coefficient recurrences (one thread per column i of D) ----
     // (gates read kBatch steps ahead of the stores, which may alias them)
-    for (int i = tid; i < n && sweep; i += kThreads) {
+    const bool coef = sweep && (all || stage == kLoad);
+    for (int i = tid; i < n && coef; i += kThreads) {
       const float ti = th[i * gs];
       float di = ti, pr = 1.f;
       for (int j = 0; j < i; ++j) w.D[j * n + i] = 0.f;
@@ -241,7 +251,7 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p, int cs, in
     }
     // A, E, F on the last thread, whose columns above are the shortest, so
     // its recurrence runs beside the long ones of the first wave
-    if (tid == kThreads - 1 && sweep) {
+    if (tid == kThreads - 1 && coef) {
       float a = 1.f, e = 1.f, f = 0.f;
       for (int j0 = 0; j0 < n; j0 += kBatch) {
         float ev[kBatch], av[kBatch];
@@ -268,6 +278,7 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p, int cs, in
 
     // ---- a2: key-side forward at the chunk-start weights ----
     for (int l = 1; l <= L && sweep; ++l) {
+      if (!run(kKey, l)) continue;
       const int nin = p.widths[l - 1], nout = p.widths[l];
       const float* Wl = Wr + p.off[l];
       const float* ain = act(l - 1);
@@ -294,6 +305,7 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p, int cs, in
     }
     // ---- a3: backprop to every layer's delta ----
     for (int l = L; l >= 2 && sweep; --l) {
+      if (!run(kBack, l)) continue;
       const int nin = p.widths[l - 1], nout = p.widths[l];
       const float* Wl = Wr + p.off[l];
       const float* dl = delta(l);
@@ -308,8 +320,9 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p, int cs, in
           });
     }
     // ---- a5: retrieval ----
-    int cur = 0;
     for (int l = 1; l <= L && rd; ++l) {
+      if (!run(kScores, l) && !run(kRead, l)) continue;
+      const int cur = (l - 1) & 1;   // query-side activations ping-pong
       const int nin = p.widths[l - 1], nout = p.widths[l];
       const float* Wl = Wr + p.off[l];
       const float* Sl = Sr + p.off[l];
@@ -327,13 +340,15 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p, int cs, in
           hn[j * maxw + r] = silu(zq);
       };
       if (p.read_mode == TM_READ_CHUNK_START) {
-        block_gemm<true>(
-            n, nout, nin, [=](int j, int c) { return h[j * maxw + c]; },
-            [=](int c, int r) { return Wl[(int64_t)r * nin + c]; }, kB_KMAJOR, epi);
+        if (run(kRead, l))
+          block_gemm<true>(
+              n, nout, nin, [=](int j, int c) { return h[j * maxw + c]; },
+              [=](int c, int r) { return Wl[(int64_t)r * nin + c]; }, kB_KMAJOR, epi);
       } else {
         float* sc = w.sc;
         const float* D = w.D;
         // masked, decay-weighted scores (D o (h a^T)), lower triangle
+        if (run(kScores, l))
         block_gemm<true>(
             n, n, nin, [=](int j, int c) { return h[j * maxw + c]; },
             [=](int c, int i) { return ak[i * nin + c]; }, kB_KMAJOR,
@@ -345,6 +360,7 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p, int cs, in
         const float* F = w.F;
         // zq = diag(A) h W^T + diag(F) h S^T - sc delta, as one contraction
         // over the concatenated index [W-part | S-part | token part]
+        if (run(kRead, l))
         block_gemm<true>(
             n, nout, 2 * nin + n,
             [=](int j, int kk) {   // branch-free: pick the address, then the factor
@@ -366,7 +382,6 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p, int cs, in
             [=](int k0) { return k0 + kGk <= 2 * nin; },   // the token part is contiguous in r
             epi);
       }
-      cur ^= 1;
     }
     // ---- a4: fold the chunk into the state (after every read of W_0, S_0) ----
     if (sweep) {
@@ -381,6 +396,7 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p, int cs, in
         float* So = S + p.off[l];
         const float* dl = delta(l);
         const float* ak = act(l - 1);
+        if (run(kFoldW, l))
         block_gemm<false>(
             nout, nin, n, [=](int r, int j) { return Dlast[j] * dl[j * nout + r]; },
             [=](int j, int c) { return ak[j * nin + c]; }, kB_NMAJOR,
@@ -391,6 +407,7 @@ __global__ void __launch_bounds__(kThreads) generic_kernel(GParams p, int cs, in
             [=](int r, int c, float g, float base, bool ok) {
               if (ok) Wo[(int64_t)r * nin + c] = base - g;
             });
+        if (run(kFoldS, l))
         block_gemm<false>(
             nout, nin, n, [=](int r, int j) { return U[j] * dl[j * nout + r]; },
             [=](int j, int c) { return ak[j * nin + c]; }, kB_NMAJOR,
@@ -457,13 +474,19 @@ int set_lds_mode(GParams& p) {
 }
 
 hipError_t launch_generic_kernel(const GParams& p, int streams, int lds, hipStream_t stream, int cs = -1,
-                                 int phase = kBoth) {
+                                 int phase = kBoth, int stage = kAllStages, int layer = 0, int ytiles = 1) {
   if (lds > 0) {
     const hipError_t e = hipFuncSetAttribute((const void*)generic_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(generic_kernel, dim3(streams), dim3(kThreads), lds, stream, p, cs, phase);
+  hipLaunchKernelGGL(generic_kernel, dim3(streams, ytiles), dim3(kThreads), lds, stream, p, cs, phase, stage, layer);
   return hipGetLastError();
+}
+
+// output tiles of an M x N block_gemm contraction
+int gemm_tiles(int M, int N) {
+  const int tn = N > kGemmTile ? kGN : kGemmTile;
+  return ((M + kGemmTile - 1) / kGemmTile) * ((N + tn - 1) / tn);
 }
 
 int rows_reserved(const Shape& s, int chunk) { return chunk < s.N ? chunk : (s.N > 0 ? s.N : 1); }
@@ -553,9 +576,15 @@ hipError_t launch_generic(const Shape& s, int chunk, const void* k, const void* 
       ++j;
     }
   }
-  int dev = 0;
+  int dev = 0, cus = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
+  if ((err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return err;
+  // with at least half the CUs idle under one workgroup per stream and
+  // phase, every step gets a launch of its own and its contraction's tiles
+  // spread over workgroups; otherwise one launch per phase (short launches
+  // would then cost more than they spread)
+  const bool per_step = 4 * (int64_t)s.streams <= cus;
   std::unique_lock<std::mutex> lock;
   SideStream* x = nullptr;
   if ((err = side_stream(dev, &x, lock)) != hipSuccess) return err;
@@ -567,11 +596,38 @@ hipError_t launch_generic(const Shape& s, int chunk, const void* k, const void* 
     p.W = dst.W;
     p.S = dst.S;
     p.state_stride = dst.stride;
+    // per step: one launch per step, each contraction's output tiles shared
+    // out over the workgroups of the launch's y dimension
+    const int n = std::min(chunk, s.N - c * chunk);
+    auto step = [&](hipStream_t st, int phase, int stage, int l, int M, int N) {
+      return launch_generic_kernel(p, s.streams, 0, st, c, phase, stage, l, gemm_tiles(M, N));
+    };
+    const int* wd = s.widths;
     if (c >= 2 && (err = hipStreamWaitEvent(stream, x->cons[c & 1], 0)) != hipSuccess) return err;
-    if ((err = launch_generic_kernel(p, s.streams, 0, stream, c, kSweep)) != hipSuccess) return err;
+    if (!per_step) {
+      if ((err = launch_generic_kernel(p, s.streams, 0, stream, c, kSweep)) != hipSuccess) return err;
+      if ((err = hipEventRecord(x->prod[c & 1], stream)) != hipSuccess) return err;
+      if ((err = hipStreamWaitEvent(x->st, x->prod[c & 1], 0)) != hipSuccess) return err;
+      if ((err = launch_generic_kernel(p, s.streams, 0, x->st, c, kReads)) != hipSuccess) return err;
+      if ((err = hipEventRecord(x->cons[c & 1], x->st)) != hipSuccess) return err;
+      continue;
+    }
+    if ((err = step(stream, kSweep, kLoad, 0, 1, 1)) != hipSuccess) return err;
+    for (int l = 1; l <= s.L; ++l)
+      if ((err = step(stream, kSweep, kKey, l, n, wd[l])) != hipSuccess) return err;
+    for (int l = s.L; l >= 2; --l)
+      if ((err = step(stream, kSweep, kBack, l, n, wd[l - 1])) != hipSuccess) return err;
+    for (int l = 1; l <= s.L; ++l) {
+      if ((err = step(stream, kSweep, kFoldW, l, wd[l], wd[l - 1])) != hipSuccess) return err;
+      if ((err = step(stream, kSweep, kFoldS, l, wd[l], wd[l - 1])) != hipSuccess) return err;
+    }
     if ((err = hipEventRecord(x->prod[c & 1], stream)) != hipSuccess) return err;
     if ((err = hipStreamWaitEvent(x->st, x->prod[c & 1], 0)) != hipSuccess) return err;
-    if ((err = launch_generic_kernel(p, s.streams, 0, x->st, c, kReads)) != hipSuccess) return err;
+    if ((err = step(x->st, kReads, kLoad, 0, 1, 1)) != hipSuccess) return err;
+    for (int l = 1; l <= s.L; ++l) {
+      if (s.read_mode != TM_READ_CHUNK_START && (err = step(x->st, kReads, kScores, l, n, n)) != hipSuccess) return err;
+      if ((err = step(x->st, kReads, kRead, l, n, wd[l])) != hipSuccess) return err;
+    }
     if ((err = hipEventRecord(x->cons[c & 1], x->st)) != hipSuccess) return err;
   }
   return hipStreamWaitEvent(stream, x->cons[(nchunks - 1) & 1], 0);
