@@ -186,3 +186,39 @@ def test_backward_deep_memory_prefix():
 def test_backward_edge_cases(B, H, N, d, h, L, chunk, read_mode, chunk_gates):
     x, adj, P = _problem(300 + N + L + chunk, B, H, N, d, h, L, chunk_gates=chunk_gates, chunk=chunk)
     _run(x, adj, B, H, N, d, h, L, chunk, read_mode=read_mode, chunk_gates=chunk_gates)
+
+
+def test_backward_calls_on_two_streams():
+    """Two backward calls enqueued on two torch streams without a
+    synchronisation between them (they share the library's side stream and
+    its events) give bitwise the results of the calls run one after the
+    other."""
+    import torch
+    from test_learned_neural_amd import titans_mem as tmm
+    probs = []
+    for seed, (B, H, N, d, h, L, chunk) in ((11, (1, 2, 37, 8, 16, 2, 5)), (12, (2, 1, 30, 8, 12, 3, 4))):
+        x, adj, P = _problem(seed, B, H, N, d, h, L, chunk=chunk)
+        dev = {n: _to_dev(x[n], (B, H, N, d)) for n in ("k", "v", "q")}
+        dev.update({n: _to_dev(x[n], (B, H, N)) for n in ("alpha", "eta", "theta")})
+        dev.update({n: _to_dev(x[n], (B, H, P)) for n in ("W_in", "S_in")})
+        dev["dy"] = _to_dev(adj["dy"], (B, H, N, d))
+        probs.append((dev, chunk, h, L))
+
+    def call(dev, chunk, h, L):
+        return tmm.backward(dev["k"], dev["v"], dev["q"], dev["alpha"], dev["eta"], dev["theta"], dev["W_in"],
+                            dev["S_in"], chunk, hidden=h, n_layers=L, dy=dev["dy"])
+    refs = []
+    for pr in probs:
+        refs.append(call(*pr))
+        torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s1):
+        g1 = call(*probs[0])
+    with torch.cuda.stream(s2):
+        g2 = call(*probs[1])
+    torch.cuda.synchronize()
+    for g, r in ((g1, refs[0]), (g2, refs[1])):
+        for name in r:
+            assert torch.equal(g[name], r[name]), name

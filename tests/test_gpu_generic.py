@@ -225,3 +225,28 @@ def test_generic_many_streams_split():
     inp = wl.make_inputs(cfg, workers=16)
     out = run_gpu(cfg, to_device(cfg, inp), force_generic=True)
     _check(cfg, inp, out, run_oracle(cfg, inp, threads=16), TOL["f32"])
+
+
+def test_generic_split_calls_on_two_streams():
+    """Two forward calls on the split path enqueued on two torch streams
+    without a synchronisation between them (they share the library's side
+    stream and its events) give bitwise the results of the calls run one
+    after the other."""
+    import torch
+    cfg1 = wl.WORKLOADS["mlp2_short"].with_(B=1, H=3, N=64 * 4 - 9)
+    cfg2 = wl.WORKLOADS["mlp2_short"].with_(B=1, H=2, N=64 * 5 - 3)
+    d1, d2 = to_device(cfg1, wl.make_inputs(cfg1)), to_device(cfg2, wl.make_inputs(cfg2))
+    ref1 = run_gpu(cfg1, d1, force_generic=True)
+    torch.cuda.synchronize()
+    ref2 = run_gpu(cfg2, d2, force_generic=True)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s1):
+        out1 = run_gpu(cfg1, d1, force_generic=True)
+    with torch.cuda.stream(s2):
+        out2 = run_gpu(cfg2, d2, force_generic=True)
+    torch.cuda.synchronize()
+    for a, b in zip(out1 + out2, ref1 + ref2):
+        assert torch.equal(a, b)
