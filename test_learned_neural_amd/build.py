@@ -19,7 +19,8 @@ OUT = os.path.join(PKG, "libtitans_mem.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["tm_host.cpp", "tm_generic.hip", "tm_mlp2.hip", "tm_input.hip", "tm_backward.hip", "tm_retrieve.hip"]
+SOURCES = ["tm_host.cpp", "tm_generic.hip", "tm_linear.hip", "tm_mlp2.hip", "tm_input.hip", "tm_backward.hip",
+           "tm_retrieve.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-I" + CSRC]
 # no packed fp32 instructions in device code (v_pk_* fp32 forms)

@@ -533,6 +533,8 @@ hipError_t launch_generic(const Shape& s, int chunk, const void* k, const void* 
                           const float* alpha, const float* eta, const float* theta,
                           const float* W_in, const float* S_in, void* y, float* W_out,
                           float* S_out, float* ws, hipStream_t stream) {
+  if (linear_supported(s, chunk))
+    return launch_linear(s, chunk, k, v, q, alpha, eta, theta, W_in, S_in, y, W_out, S_out, stream);
   GParams p = make_params(s, chunk);
   p.b = rows_reserved(s, chunk);
   p.lay = ws_layout(s, p.b);

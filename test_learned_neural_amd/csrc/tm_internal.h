@@ -50,6 +50,14 @@ hipError_t launch_generic(const Shape& s, int chunk, const void* k, const void* 
 hipError_t launch_retrieve_generic(const Shape& s, const void* q, const float* W, void* y,
                                    hipStream_t stream);
 
+// The linear memory (L = 1, d <= 64 and a multiple of 4, chunk <= 64) on one
+// workgroup per stream with the state and the chunk in LDS; part of the
+// generic path (fp32 arithmetic, no workspace).
+bool linear_supported(const Shape& s, int chunk);
+hipError_t launch_linear(const Shape& s, int chunk, const void* k, const void* v, const void* q,
+                         const float* alpha, const float* eta, const float* theta, const float* W_in,
+                         const float* S_in, void* y, float* W_out, float* S_out, hipStream_t stream);
+
 // Specialised 2-layer d=64 hidden=256 MFMA kernel (chunk <= 64, bf16 io).
 bool mlp2_supported(const Shape& s, int chunk);
 int64_t mlp2_ws_bytes(const Shape& s, int chunk);

@@ -250,3 +250,22 @@ def test_generic_split_calls_on_two_streams():
     torch.cuda.synchronize()
     for a, b in zip(out1 + out2, ref1 + ref2):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("d,N,chunk,read_mode,io", [(64, 300, 64, 1, "bf16"), (32, 129, 1, 0, "f32"),
+                                                    (8, 50, 7, 0, "bf16"), (64, 200, 16, 0, "f32")])
+def test_linear_memory_kernel(d, N, chunk, read_mode, io):
+    """The linear memory (d <= 64, chunk <= 64) runs on its own one-workgroup
+    kernel within the generic path: both read modes, both io dtypes, chunks
+    of one token and ragged tails; an in-place call agrees bitwise."""
+    import torch
+    cfg = wl.WORKLOADS["linear"].with_(B=2, H=2, N=N, d=d, chunk=chunk, io=io)
+    inp = wl.make_inputs(cfg)
+    dev = to_device(cfg, inp)
+    out = run_gpu(cfg, dev, force_generic=True, read_mode=read_mode)
+    _check(cfg, inp, out, run_oracle(cfg, inp, read_mode=read_mode), TOL["f32"], windows=False)
+    Wi, Si = dev["W0"].clone(), dev["S0"].clone()
+    y2, W2, S2 = run_gpu(cfg, dev | {"W0": Wi, "S0": Si}, force_generic=True, read_mode=read_mode, W_out=Wi,
+                         S_out=Si)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, out[0]) and torch.equal(W2, out[1]) and torch.equal(S2, out[2])
