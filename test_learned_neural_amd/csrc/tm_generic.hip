@@ -22,8 +22,9 @@
 // The state lives in W_out/S_out (global memory) and the chunk's
 // intermediates in a per-stream workspace; every contraction is an fp32
 // matrix-instruction tile loop staged through LDS.  This path serves any
-// shape and the fp32-io linear memory, and is the fallback where no
-// specialised kernel exists.
+// shape (the linear memory up to d = 64 goes to the one-workgroup kernel of
+// tm_linear.hip instead), and is the fallback where no specialised kernel
+// exists.
 //
 // A state too large for LDS leaves most CUs idle with one workgroup per
 // stream; there the forward call runs each chunk in two phases: the sweep
