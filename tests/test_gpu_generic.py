@@ -195,23 +195,28 @@ def test_generic_chunk_gates(wname, n_tokens, BH, chunk, read_mode):
     _check(cfg, inp, out, run_oracle(cfg, inp, read_mode=read_mode, chunk_gates=True), TOL["f32"])
 
 
-@pytest.mark.parametrize("n_chunks,H", [(2, 3), (4, 3), (5, 3), (4, 80)])
-def test_generic_split_launches_match_single_launch(n_chunks, H):
+@pytest.mark.parametrize("n_chunks,H,read_mode,chunk_gates", [(2, 3, 0, False), (4, 3, 0, False), (5, 3, 0, False),
+                                                           (4, 80, 0, False), (4, 3, 1, True), (5, 80, 1, True)])
+def test_generic_split_launches_match_single_launch(n_chunks, H, read_mode, chunk_gates):
     """A state too large for LDS with chunks of 64 runs each chunk as two
     launches (sweep and reads on two streams), the chunk-start states
     rotating through three buffers of which W_out/S_out is one; an in-place
     call runs the single launch.  Both must agree bitwise, for every
     rotation phase (chunk counts 2, 4, 5 leave the outputs as buffer 2, 1,
     2 of the rotation; 3 chunks are covered above), ragged last chunk
-    included.  Few streams run every step as a launch of its own, tiles
-    spread over workgroups; 80 streams one launch per phase."""
+    included, both read modes, per-token and per-chunk gates.  Few streams
+    run every step as a launch of its own, tiles spread over workgroups; 80
+    streams one launch per phase."""
     import torch
     cfg = wl.WORKLOADS["mlp2_short"].with_(B=1, H=H, N=64 * n_chunks - 9)
     inp = wl.make_inputs(cfg)
+    if chunk_gates:
+        inp = chunk_gate_inputs(inp, cfg.chunk)
     dev = to_device(cfg, inp)
-    y1, W1, S1 = run_gpu(cfg, dev, force_generic=True)
+    kw = dict(force_generic=True, read_mode=read_mode, chunk_gates=chunk_gates)
+    y1, W1, S1 = run_gpu(cfg, dev, **kw)
     Wi, Si = dev["W0"].clone(), dev["S0"].clone()
-    y2, W2, S2 = run_gpu(cfg, dev | {"W0": Wi, "S0": Si}, force_generic=True, W_out=Wi, S_out=Si)
+    y2, W2, S2 = run_gpu(cfg, dev | {"W0": Wi, "S0": Si}, W_out=Wi, S_out=Si, **kw)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(W1, W2) and torch.equal(S1, S2)
     assert not torch.equal(W1, dev["W0"])
