@@ -27,7 +27,7 @@ WORKLOAD_NAMES = ("linear", "mlp2_short", "headline", "long", "deep")
 
 
 # dominant kernel of each path: (kernel function, its source under csrc/)
-DOMINANT_KERNEL = {"mlp2_d64_h256_mfma": ("mlp2_pair_kernel", "tm_mlp2.hip"),
+DOMINANT_KERNEL = {"mlp2_d64_h256_mfma": ("mlp2_group_kernel", "tm_mlp2_group.hip"),
                    "generic_f32": ("generic_kernel", "tm_generic.hip"),
                    "input_side": ("input_kernel", "tm_input.hip"),
                    "retrieve_mlp2": ("mlp2_retrieve_kernel", "tm_retrieve.hip")}

@@ -40,8 +40,14 @@
  *   stream): they return after enqueueing and never synchronise.  Argument
  *   errors (codes -1..-4) are detected on the host before anything is
  *   enqueued, so they can be tested without a GPU.
- * - The library allocates no device memory and keeps no global mutable
- *   state; calls are re-entrant.  The caller owns every buffer.
+ * - The library allocates no device memory; the caller owns every buffer.
+ * - Process-wide state: per device, one HIP stream of the library's own
+ *   (default priority) and six events, created on the first call that needs
+ *   them and kept until the process ends.  The shape-generic forward (when
+ *   the state does not fit on chip) and the backward run part of their work
+ *   there, forked from and joined back into the caller's `stream` with
+ *   events, on every return path; a mutex serialises the enqueueing of such
+ *   calls.  Calls are thread-safe.
  */
 #ifndef TITANS_MEM_H
 #define TITANS_MEM_H
@@ -61,6 +67,9 @@ extern "C" {
 #define TM_ERR_WORKSPACE   -3  /* workspace smaller than titans_mem_workspace_bytes() */
 #define TM_ERR_ALIAS       -4  /* illegal overlap between buffers */
 #define TM_ERR_HIP         -5  /* the HIP runtime reported an error when launching */
+#define TM_ERR_GAVE_UP     -6  /* titans_mem_workspace_status: the MFMA kernel's paired
+                                  workgroups gave up waiting for each other; the call's
+                                  y, W_out and S_out hold NaN */
 
 /* dtype of k, v, q and y (the io tensors); state and gates are always fp32 */
 #define TM_IO_F32  0
@@ -80,6 +89,10 @@ extern "C" {
                                      Test Time", mer.dev notes, section 3.2 "Parameters as the
                                      Function of Chunks": inside a chunk the update is then
                                      time-invariant) */
+#define TM_FLAG_NO_WAIT       4u  /* test hook for the failure path of the MFMA kernel: its paired
+                                     workgroups give up at their first wait for each other, so the
+                                     call ends normally with NaN outputs and the give-up status
+                                     (ignored by the other kernels) */
 
 /* kernel paths reported by titans_mem_select_path */
 #define TM_PATH_GENERIC_F32   0   /* any shape: fp32 (matrix instructions), state in global memory */
@@ -140,6 +153,15 @@ int64_t titans_mem_workspace_bytes(const titans_mem_desc* desc, int32_t chunk);
  * Returns TM_OK or a negative status.  Resuming: passing (W_out, S_out) of
  * a call as (W_in, S_in) of the next, with a split on a chunk boundary,
  * continues the same sequence.
+ *
+ * The MFMA path (TM_PATH_MLP2_D64_H256) runs each stream on two workgroups
+ * that wait for each other every chunk.  Both must be resident at once; the
+ * launch sizes its grid to half the device's CUs, but work that other
+ * streams or processes keep on the CUs can hold one back.  A workgroup whose
+ * partner does not arrive within a bounded wait (about 2^21 polls) gives up
+ * instead of hanging: the call still completes, y, W_out and S_out of the
+ * pair's streams hold NaN, and titans_mem_workspace_status reports
+ * TM_ERR_GAVE_UP.
  */
 int titans_mem_forward(const titans_mem_desc* desc,
                        const void* k, const void* v, const void* q,
@@ -149,6 +171,22 @@ int titans_mem_forward(const titans_mem_desc* desc,
                        void* y_out, float* W_out, float* S_out,
                        void* workspace, int64_t workspace_bytes,
                        void* stream);
+
+/*
+ * titans_mem_workspace_status -- outcome of the last titans_mem_forward call
+ * that used `workspace` (same desc and chunk).  Waits for `stream` to drain
+ * (hipStreamSynchronize) and reads the status word the MFMA kernel keeps in
+ * its workspace.
+ *
+ * Returns TM_OK when the call completed, TM_ERR_GAVE_UP when paired
+ * workgroups of the MFMA kernel gave up waiting for each other (its outputs
+ * hold NaN), an argument error (-1..-3) like titans_mem_forward's, or
+ * TM_ERR_HIP when the copy or the synchronisation fails.  Paths without
+ * cross-workgroup waits always report TM_OK (workspace may then be NULL).
+ */
+int titans_mem_workspace_status(const titans_mem_desc* desc, int32_t chunk,
+                                const void* workspace, int64_t workspace_bytes,
+                                void* stream);
 
 /*
  * titans_mem_retrieve -- pure retrieval y = M*_W(q) at a fixed state

@@ -19,7 +19,7 @@ OUT = os.path.join(PKG, "libtitans_mem.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["tm_host.cpp", "tm_generic.hip", "tm_linear.hip", "tm_mlp2.hip", "tm_input.hip", "tm_backward.hip",
+SOURCES = ["tm_host.cpp", "tm_generic.hip", "tm_linear.hip", "tm_mlp2_group.hip", "tm_input.hip", "tm_backward.hip",
            "tm_retrieve.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-I" + CSRC]
@@ -29,8 +29,8 @@ DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-p
 
 
 # MFMA results in VGPRs: the MFMA kernel post-processes every accumulator on
-# the VALU, and its AGPRs hold the memory state
-PER_FILE = {"tm_mlp2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# the VALU and keeps the memory state in VGPRs
+PER_FILE = {"tm_mlp2_group.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:
@@ -40,8 +40,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str, extra=()) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra=(), build_dir: str = BUILD_DIR) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     path = os.path.join(CSRC, src)
     cmd = [hipcc()] + COMMON + list(extra)
     if src.endswith(".hip"):
@@ -51,16 +51,19 @@ def _compile(src: str, extra=()) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, extra=(), out: str = OUT, build_dir: str = BUILD_DIR) -> str:
+    """Compile every source and link the library at ``out`` (``extra``:
+    additional compiler flags, e.g. -DTM_STAGE_STAMPS=1 for the stage-timing
+    build, which stage_stamps.py places beside the library)."""
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = OUT + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda s: _compile(s, extra, build_dir), SOURCES))
+    tmp = out + ".tmp%d" % os.getpid()
     subprocess.check_call([hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs)
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print("built", OUT)
-    return OUT
+        print("built", out)
+    return out
 
 
 if __name__ == "__main__":

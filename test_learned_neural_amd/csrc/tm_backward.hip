@@ -934,13 +934,20 @@ hipError_t side_stream(int dev, SideStream** out, std::unique_lock<std::mutex>& 
   if (!g_side[dev].st) {
     SideStream x;
     hipError_t e = hipStreamCreateWithFlags(&x.st, hipStreamNonBlocking);
-    hipEvent_t* evs[5] = {&x.fork, &x.prod[0], &x.prod[1], &x.cons[0], &x.cons[1]};
-    for (int i = 0; i < 5 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(evs[i], hipEventDisableTiming);
+    hipEvent_t* evs[6] = {&x.fork, &x.join, &x.prod[0], &x.prod[1], &x.cons[0], &x.cons[1]};
+    for (int i = 0; i < 6 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(evs[i], hipEventDisableTiming);
     if (e != hipSuccess) return e;   // (what was created is kept: a few handles)
     g_side[dev] = x;
   }
   *out = &g_side[dev];
   return hipSuccess;
+}
+
+hipError_t join_side(SideStream* x, hipStream_t stream, hipError_t err) {
+  hipError_t e = hipEventRecord(x->join, x->st);
+  if (e == hipSuccess) e = hipStreamWaitEvent(stream, x->join, 0);
+  if (e != hipSuccess) (void)hipGetLastError();   // (cleared, so the first error is the one reported)
+  return err != hipSuccess ? err : e;
 }
 
 bool backward_supported(const Shape& s, int chunk) {
@@ -1008,17 +1015,21 @@ hipError_t launch_backward(const Shape& s, int chunk, const void* k, const void*
   if ((err = side_stream(dev, &x, lock)) != hipSuccess) return err;
   if ((err = hipEventRecord(x->fork, stream)) != hipSuccess) return err;
   if ((err = hipStreamWaitEvent(x->st, x->fork, 0)) != hipSuccess) return err;
-  for (int c = p.nchunks - 1; c >= 0; --c) {
-    if (c + 2 < p.nchunks && (err = hipStreamWaitEvent(x->st, x->cons[c & 1], 0)) != hipSuccess) return err;
-    hipLaunchKernelGGL(backward_kernel, dim3(s.streams), dim3(kBT), 0, x->st, p, c, (int)kProduce);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    if ((err = hipEventRecord(x->prod[c & 1], x->st)) != hipSuccess) return err;
-    if ((err = hipStreamWaitEvent(stream, x->prod[c & 1], 0)) != hipSuccess) return err;
-    hipLaunchKernelGGL(backward_kernel, dim3(s.streams), dim3(kBT), 0, stream, p, c, (int)kConsume);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    if ((err = hipEventRecord(x->cons[c & 1], stream)) != hipSuccess) return err;
-  }
-  return hipSuccess;
+  auto reverse = [&]() -> hipError_t {
+    hipError_t e;
+    for (int c = p.nchunks - 1; c >= 0; --c) {
+      if (c + 2 < p.nchunks && (e = hipStreamWaitEvent(x->st, x->cons[c & 1], 0)) != hipSuccess) return e;
+      hipLaunchKernelGGL(backward_kernel, dim3(s.streams), dim3(kBT), 0, x->st, p, c, (int)kProduce);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = hipEventRecord(x->prod[c & 1], x->st)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(stream, x->prod[c & 1], 0)) != hipSuccess) return e;
+      hipLaunchKernelGGL(backward_kernel, dim3(s.streams), dim3(kBT), 0, stream, p, c, (int)kConsume);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = hipEventRecord(x->cons[c & 1], stream)) != hipSuccess) return e;
+    }
+    return hipSuccess;
+  };
+  return join_side(x, stream, reverse());
 }
 
 }  // namespace titans

@@ -591,49 +591,56 @@ hipError_t launch_generic(const Shape& s, int chunk, const void* k, const void* 
   std::unique_lock<std::mutex> lock;
   SideStream* x = nullptr;
   if ((err = side_stream(dev, &x, lock)) != hipSuccess) return err;
-  for (int c = 0; c < nchunks; ++c) {
-    const Buf src = c == 0 ? Buf{(float*)W_in, (float*)S_in, s.P} : buf[c % 3], dst = buf[(c + 1) % 3];
-    p.W_in = src.W;
-    p.S_in = src.S;
-    p.in_stride = src.stride;
-    p.W = dst.W;
-    p.S = dst.S;
-    p.state_stride = dst.stride;
-    // per step: one launch per step, each contraction's output tiles shared
-    // out over the workgroups of the launch's y dimension
-    const int n = std::min(chunk, s.N - c * chunk);
-    auto step = [&](hipStream_t st, int phase, int stage, int l, int M, int N) {
-      return launch_generic_kernel(p, s.streams, 0, st, c, phase, stage, l, gemm_tiles(M, N));
-    };
-    const int* wd = s.widths;
-    if (c >= 2 && (err = hipStreamWaitEvent(stream, x->cons[c & 1], 0)) != hipSuccess) return err;
-    if (!per_step) {
-      if ((err = launch_generic_kernel(p, s.streams, 0, stream, c, kSweep)) != hipSuccess) return err;
-      if ((err = hipEventRecord(x->prod[c & 1], stream)) != hipSuccess) return err;
-      if ((err = hipStreamWaitEvent(x->st, x->prod[c & 1], 0)) != hipSuccess) return err;
-      if ((err = launch_generic_kernel(p, s.streams, 0, x->st, c, kReads)) != hipSuccess) return err;
-      if ((err = hipEventRecord(x->cons[c & 1], x->st)) != hipSuccess) return err;
-      continue;
+  auto chunks = [&]() -> hipError_t {
+    hipError_t e;
+    for (int c = 0; c < nchunks; ++c) {
+      const Buf src = c == 0 ? Buf{(float*)W_in, (float*)S_in, s.P} : buf[c % 3], dst = buf[(c + 1) % 3];
+      p.W_in = src.W;
+      p.S_in = src.S;
+      p.in_stride = src.stride;
+      p.W = dst.W;
+      p.S = dst.S;
+      p.state_stride = dst.stride;
+      // per step: one launch per step, each contraction's output tiles shared
+      // out over the workgroups of the launch's y dimension
+      const int n = std::min(chunk, s.N - c * chunk);
+      auto step = [&](hipStream_t st, int phase, int stage, int l, int M, int N) {
+        return launch_generic_kernel(p, s.streams, 0, st, c, phase, stage, l, gemm_tiles(M, N));
+      };
+      const int* wd = s.widths;
+      if (c >= 2 && (e = hipStreamWaitEvent(stream, x->cons[c & 1], 0)) != hipSuccess) return e;
+      if (!per_step) {
+        if ((e = launch_generic_kernel(p, s.streams, 0, stream, c, kSweep)) != hipSuccess) return e;
+        if ((e = hipEventRecord(x->prod[c & 1], stream)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(x->st, x->prod[c & 1], 0)) != hipSuccess) return e;
+        if ((e = launch_generic_kernel(p, s.streams, 0, x->st, c, kReads)) != hipSuccess) return e;
+        if ((e = hipEventRecord(x->cons[c & 1], x->st)) != hipSuccess) return e;
+        continue;
+      }
+      if ((e = step(stream, kSweep, kLoad, 0, 1, 1)) != hipSuccess) return e;
+      for (int l = 1; l <= s.L; ++l)
+        if ((e = step(stream, kSweep, kKey, l, n, wd[l])) != hipSuccess) return e;
+      for (int l = s.L; l >= 2; --l)
+        if ((e = step(stream, kSweep, kBack, l, n, wd[l - 1])) != hipSuccess) return e;
+      for (int l = 1; l <= s.L; ++l) {
+        if ((e = step(stream, kSweep, kFoldW, l, wd[l], wd[l - 1])) != hipSuccess) return e;
+        if ((e = step(stream, kSweep, kFoldS, l, wd[l], wd[l - 1])) != hipSuccess) return e;
+      }
+      if ((e = hipEventRecord(x->prod[c & 1], stream)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(x->st, x->prod[c & 1], 0)) != hipSuccess) return e;
+      if ((e = step(x->st, kReads, kLoad, 0, 1, 1)) != hipSuccess) return e;
+      for (int l = 1; l <= s.L; ++l) {
+        if (s.read_mode != TM_READ_CHUNK_START && (e = step(x->st, kReads, kScores, l, n, n)) != hipSuccess) return e;
+        if ((e = step(x->st, kReads, kRead, l, n, wd[l])) != hipSuccess) return e;
+      }
+      if ((e = hipEventRecord(x->cons[c & 1], x->st)) != hipSuccess) return e;
     }
-    if ((err = step(stream, kSweep, kLoad, 0, 1, 1)) != hipSuccess) return err;
-    for (int l = 1; l <= s.L; ++l)
-      if ((err = step(stream, kSweep, kKey, l, n, wd[l])) != hipSuccess) return err;
-    for (int l = s.L; l >= 2; --l)
-      if ((err = step(stream, kSweep, kBack, l, n, wd[l - 1])) != hipSuccess) return err;
-    for (int l = 1; l <= s.L; ++l) {
-      if ((err = step(stream, kSweep, kFoldW, l, wd[l], wd[l - 1])) != hipSuccess) return err;
-      if ((err = step(stream, kSweep, kFoldS, l, wd[l], wd[l - 1])) != hipSuccess) return err;
-    }
-    if ((err = hipEventRecord(x->prod[c & 1], stream)) != hipSuccess) return err;
-    if ((err = hipStreamWaitEvent(x->st, x->prod[c & 1], 0)) != hipSuccess) return err;
-    if ((err = step(x->st, kReads, kLoad, 0, 1, 1)) != hipSuccess) return err;
-    for (int l = 1; l <= s.L; ++l) {
-      if (s.read_mode != TM_READ_CHUNK_START && (err = step(x->st, kReads, kScores, l, n, n)) != hipSuccess) return err;
-      if ((err = step(x->st, kReads, kRead, l, n, wd[l])) != hipSuccess) return err;
-    }
-    if ((err = hipEventRecord(x->cons[c & 1], x->st)) != hipSuccess) return err;
-  }
-  return hipStreamWaitEvent(stream, x->cons[(nchunks - 1) & 1], 0);
+    return hipSuccess;
+  };
+  // the side stream's last work is the reads of the last chunk: the join
+  // makes the caller's stream wait for it (and for whatever was enqueued
+  // before an error)
+  return join_side(x, stream, chunks());
 }
 
 hipError_t launch_generic_checkpoints(const Shape& s, int chunk, const void* k, const void* v, const void* q,

@@ -18,7 +18,7 @@ int build_shape(const titans_mem_desc* desc, Shape* s) {
   if (desc->io_dtype != TM_IO_F32 && desc->io_dtype != TM_IO_BF16) return TM_ERR_INVALID;
   if (desc->read_mode != TM_READ_AFTER_WRITE && desc->read_mode != TM_READ_CHUNK_START)
     return TM_ERR_INVALID;
-  if (desc->flags & ~(TM_FLAG_FORCE_GENERIC | TM_FLAG_CHUNK_GATES)) return TM_ERR_INVALID;
+  if (desc->flags & ~(TM_FLAG_FORCE_GENERIC | TM_FLAG_CHUNK_GATES | TM_FLAG_NO_WAIT)) return TM_ERR_INVALID;
   if (desc->n_layers > titans::kMaxLayers) return TM_ERR_UNSUPPORTED;
   const int64_t streams = (int64_t)desc->B * desc->H;
   if (streams > (int64_t)1 << 30) return TM_ERR_UNSUPPORTED;
@@ -30,6 +30,7 @@ int build_shape(const titans_mem_desc* desc, Shape* s) {
   s->io = desc->io_dtype;
   s->read_mode = desc->read_mode;
   s->chunk_gates = (desc->flags & TM_FLAG_CHUNK_GATES) ? 1 : 0;
+  s->flags = desc->flags;
   s->widths[0] = desc->d;
   for (int l = 1; l < s->L; ++l) s->widths[l] = desc->hidden;
   s->widths[s->L] = desc->d;
@@ -98,12 +99,18 @@ int64_t titans_mem_workspace_bytes(const titans_mem_desc* desc, int32_t chunk) {
   return workspace_for(s, path, chunk);
 }
 
-int titans_mem_forward(const titans_mem_desc* desc, const void* k, const void* v, const void* q,
-                       const float* alpha, const float* eta, const float* theta,
-                       const float* W_in, const float* S_in, int32_t chunk, void* y_out,
-                       float* W_out, float* S_out, void* workspace, int64_t workspace_bytes,
-                       void* stream) {
-  Shape s;
+}  // extern "C"
+
+namespace {
+
+// Validation of a forward call:
+// pointers, path, workspace size (has_ws: the caller passes one) and
+// aliasing, all on the host.  Fills s and path.
+int check_forward(const titans_mem_desc* desc, const void* k, const void* v, const void* q, const float* alpha,
+                  const float* eta, const float* theta, const float* W_in, const float* S_in, int32_t chunk,
+                  const void* y_out, const float* W_out, const float* S_out, const void* workspace,
+                  int64_t workspace_bytes, bool has_ws, Shape* sp, int* path_out) {
+  Shape& s = *sp;
   int rc = build_shape(desc, &s);
   if (rc) return rc;
   if (chunk <= 0) return TM_ERR_INVALID;
@@ -119,7 +126,7 @@ int titans_mem_forward(const titans_mem_desc* desc, const void* k, const void* v
   if (workspace && !aligned16(workspace)) return TM_ERR_INVALID;
   int path = select_path(desc, s, chunk);
   if (path < 0) return path;
-  const int64_t need = workspace_for(s, path, chunk);
+  const int64_t need = has_ws ? workspace_for(s, path, chunk) : 0;
   if (need > 0 && (!workspace || workspace_bytes < need)) return TM_ERR_WORKSPACE;
 
   const int64_t esz = s.io == TM_IO_BF16 ? 2 : 4;
@@ -147,7 +154,24 @@ int titans_mem_forward(const titans_mem_desc* desc, const void* k, const void* v
       return TM_ERR_ALIAS;
     }
   }
+  *path_out = path;
+  return TM_OK;
+}
 
+}  // namespace
+
+extern "C" {
+
+int titans_mem_forward(const titans_mem_desc* desc, const void* k, const void* v, const void* q,
+                       const float* alpha, const float* eta, const float* theta,
+                       const float* W_in, const float* S_in, int32_t chunk, void* y_out,
+                       float* W_out, float* S_out, void* workspace, int64_t workspace_bytes,
+                       void* stream) {
+  Shape s;
+  int path = 0;
+  int rc = check_forward(desc, k, v, q, alpha, eta, theta, W_in, S_in, chunk, y_out, W_out, S_out, workspace,
+                         workspace_bytes, true, &s, &path);
+  if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
   hipError_t err;
   if (path == TM_PATH_MLP2_D64_H256)
@@ -157,6 +181,27 @@ int titans_mem_forward(const titans_mem_desc* desc, const void* k, const void* v
     err = titans::launch_generic(s, chunk, k, v, q, alpha, eta, theta, W_in, S_in, y_out, W_out,
                              S_out, (float*)workspace, st);
   return err == hipSuccess ? TM_OK : TM_ERR_HIP;
+}
+
+int titans_mem_workspace_status(const titans_mem_desc* desc, int32_t chunk, const void* workspace,
+                                int64_t workspace_bytes, void* stream) {
+  Shape s;
+  int rc = build_shape(desc, &s);
+  if (rc) return rc;
+  const int path = select_path(desc, s, chunk);
+  if (path < 0) return path;
+  const hipStream_t st = (hipStream_t)stream;
+  if (path != TM_PATH_MLP2_D64_H256)
+    return hipStreamSynchronize(st) == hipSuccess ? TM_OK : TM_ERR_HIP;
+  if (workspace && !aligned16(workspace)) return TM_ERR_INVALID;
+  const int64_t need = workspace_for(s, path, chunk);
+  if (!workspace || workspace_bytes < need) return TM_ERR_WORKSPACE;
+  unsigned word = 0;
+  if (hipMemcpyAsync(&word, (const char*)workspace + titans::mlp2_status_offset(s), sizeof(word),
+                     hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return TM_ERR_HIP;
+  return word ? TM_ERR_GAVE_UP : TM_OK;
 }
 
 int titans_mem_retrieve(const titans_mem_desc* desc, const void* q, const float* W, void* y_out,
@@ -284,6 +329,7 @@ const char* titans_mem_status_string(int status) {
     case TM_ERR_WORKSPACE: return "workspace too small";
     case TM_ERR_ALIAS: return "illegal buffer overlap";
     case TM_ERR_HIP: return "HIP launch error";
+    case TM_ERR_GAVE_UP: return "paired workgroups gave up waiting for each other; outputs are NaN";
     default: return "unknown status";
   }
 }

@@ -20,6 +20,7 @@ constexpr int kMaxWidthRetrieve = 1024;
 struct Shape {
   int streams, N, d, hidden, L, io, read_mode;
   int chunk_gates;   // gates given per chunk (TM_FLAG_CHUNK_GATES)
+  unsigned flags;    // the desc's TM_FLAG_* bits
   int widths[kMaxLayers + 1];
   int64_t off[kMaxLayers + 1];
   int64_t P;
@@ -38,9 +39,15 @@ int64_t generic_forward_ws_floats_per_stream(const Shape& s, int chunk);
 // call records every event before waiting on it).
 struct SideStream {
   hipStream_t st = nullptr;
-  hipEvent_t fork = nullptr, prod[2] = {nullptr, nullptr}, cons[2] = {nullptr, nullptr};
+  hipEvent_t fork = nullptr, join = nullptr, prod[2] = {nullptr, nullptr}, cons[2] = {nullptr, nullptr};
 };
 hipError_t side_stream(int dev, SideStream** out, std::unique_lock<std::mutex>& lock);
+// Makes `stream` wait for everything enqueued so far on the side stream.
+// Every launcher calls it on each return path after its first enqueue on the
+// side stream (errors included), so that work the caller enqueues on
+// `stream` afterwards, such as freeing buffers, never overtakes it; returns
+// `err` when that is an error, else the join's own status.
+hipError_t join_side(SideStream* x, hipStream_t stream, hipError_t err);
 
 hipError_t launch_generic(const Shape& s, int chunk, const void* k, const void* v, const void* q,
                           const float* alpha, const float* eta, const float* theta,
@@ -61,6 +68,9 @@ hipError_t launch_linear(const Shape& s, int chunk, const void* k, const void* v
 // Specialised 2-layer d=64 hidden=256 MFMA kernel (chunk <= 64, bf16 io).
 bool mlp2_supported(const Shape& s, int chunk);
 int64_t mlp2_ws_bytes(const Shape& s, int chunk);
+// byte offset of the kernel's status word in its workspace (1 = a pair gave up)
+int64_t mlp2_status_offset(const Shape& s);
+
 hipError_t launch_mlp2(const Shape& s, int chunk, const void* k, const void* v, const void* q,
                        const float* alpha, const float* eta, const float* theta,
                        const float* W_in, const float* S_in, void* y, float* W_out,

@@ -1,0 +1,1259 @@
+// MFMA kernel for the 2-layer memory, d = 64, hidden = 256, chunk <= 64,
+// bf16 keys/values/queries/outputs, fp32 state and gates: eight waves per
+// workgroup, two per SIMD.
+//
+// Method ("Titans: Learning to Memorize at Test Time", mer.dev notes): the
+// chunked test-time update of section 3.2 (gradients of every token of a
+// chunk taken at the chunk-start weights), with the surprise momentum and
+// forgetting of section 3.1, and retrieval after each token's write.  Per
+// chunk of n tokens with chunk-start state (W_0, S_0):
+//
+//   a1  A_j = prod_{m<=j}(1-alpha_m), E_j = prod eta_m,
+//       F_j = (1-alpha_j) F_{j-1} + E_j, U_i = theta_i prod_{m>i} eta_m,
+//       D[j,i] = (1-alpha_j) D[j-1,i] + theta_i prod_{i<m<=j} eta_m (D[i,i] = theta_i)
+//   a2  Z1 = K W1_0^T, A1 = SiLU(Z1), O = A1 W2_0^T
+//   a3  Delta2 = O - V, Delta1 = (Delta2 W2_0) * SiLU'(Z1)
+//   a5  Zq1 = diag(A) Q W1_0^T + diag(F) Q S1_0^T - (D o Q K^T) Delta1, H1 = SiLU(Zq1)
+//       y   = diag(A) H1 W2_0^T + diag(F) H1 S2_0^T - (D o H1 A1^T) Delta2
+//   a4  W_l <- A_n W_l + F_n S_l - G_l(D[n-1,:]),  S_l <- E_n S_l - G_l(U)
+//       G_1(w) = sum_j w_j Delta1_j k_j^T,  G_2(w) = sum_j w_j Delta2_j a1_j^T
+//
+// MI355X mapping
+// --------------
+// * Each (batch, head) stream runs on a PAIR of workgroups (two CUs), one per
+//   half of the hidden layer.  A workgroup is eight waves, two per SIMD, and
+//   wave w owns 16 hidden units: its share of the state (W1, S1, W2, S2
+//   restricted to those units, 64 floats per lane) lives in ordinary VGPRs
+//   for the whole sequence, in the accumulator layout of
+//   v_mfma_f32_16x16x32_f16 with rows = the d index and lanes = the units.
+//   Such a tile is, without any move, the MFMA operand of every product that
+//   contracts over d (Z1, Zq1, Delta1), and the weighted outer-product folds
+//   (G_1, G_2) land in that same layout.
+// * Products that contract over the tokens of the chunk (the folds, the
+//   masked first-layer term) take the per-wave activations straight from
+//   their accumulators (lanes = units, registers = tokens).
+// * Products that contract over the hidden units (O, the masked scores
+//   H1 A1^T, y) run once per workgroup: every wave writes its A1, H1 and
+//   W2/S2 pieces to LDS and computes two 16x16 output tiles over all 128
+//   units of the workgroup.  Only O (needed before the backprop: one
+//   exchange per chunk on the critical path) and y (exchanged one chunk late,
+//   riding on the next O exchange) cross the pair, as fp32 partial sums.
+// * The second wave per SIMD fills the issue gaps of the first: the
+//   element-wise work (SiLU, its derivative, scaling, conversions) and the
+//   barriers of one wave overlap the matrix work of the other.
+// * Every MFMA operand is fp16 with a power-of-two scale per operand block
+//   and chunk (fp32 accumulation, exact rescaling): the state, the
+//   activations and the residuals.  Scores produced by one wave and consumed
+//   in one K-step carry that wave's own scale, so they need no workgroup-wide
+//   maximum.
+// * The pair exchanges its partial sums through global memory in 8-byte
+//   words that carry the chunk's sequence number beside the value (single-
+//   copy-atomic 64-bit agent-coherent stores): each reader polls its own
+//   words until they carry the number it expects, so the exchange needs no
+//   flag, no wait for store completion and no barrier around the wait.  A
+//   formal release/acquire flag protocol at agent scope costs an L2
+//   writeback and invalidation per chunk (measured 3.5 -> 4.4 ms per call on
+//   the earlier four-wave kernel).  The coefficient scan and the products
+//   that need no partner data run while the exchange is in flight.  A
+//   thread whose partner's words do not arrive within a bounded spin gives
+//   up: the workgroup records the failure in the workspace status word
+//   (returned by titans_mem_workspace_status) and writes NaN to W_out, S_out
+//   and y of every stream the pair serves.  Sums are formed in a fixed order
+//   (half 0 + half 1), so results are bitwise reproducible and identical in
+//   both halves.
+#include "tm_internal.h"
+
+#include <hip/hip_bf16.h>
+
+namespace titans {
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 64;
+constexpr int kH = 256;
+constexpr int kB = 64;               // token rows per chunk tile
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kUW = 16;              // hidden units per wave
+constexpr int kUG = kWaves * kUW;    // hidden units per workgroup (half of kH)
+constexpr int kP = 2 * kD * kH;
+constexpr int RS = 72;               // fp16 row stride (halves) of 64-wide tiles: 144-byte rows
+constexpr int RW = 136;              // fp16 row stride of 128-wide tiles: 272-byte rows
+constexpr int RF = 68;               // fp32 row stride of D
+constexpr int kMaxPairs = 128;
+constexpr unsigned kSpinMax = 1u << 21;
+
+// ---- LDS layout (bytes) ----
+constexpr int kT64 = kB * RS * 2;    // 9216
+constexpr int kT128 = kB * RW * 2;   // 17408
+constexpr int OFF_K = 0;             // K   [j][c]
+constexpr int OFF_KT = OFF_K + kT64;     // K^T [c][j]
+constexpr int OFF_Q = OFF_KT + kT64;     // Q   [j][c]
+constexpr int OFF_D2 = OFF_Q + kT64;     // Delta2   [j][c]
+constexpr int OFF_D2T = OFF_D2 + kT64;   // Delta2^T [c][j]
+constexpr int OFF_SC = OFF_D2T + kT64;   // masked scores [j][i]: first layer, then second
+constexpr int OFF_DM = OFF_SC + kT64;    // D [j][i] fp32
+constexpr int OFF_A1 = OFF_DM + kB * RF * 4;   // A1 [j][u] over the workgroup's units
+constexpr int OFF_H1 = OFF_A1 + kT128;         // H1 [j][u]
+constexpr int OFF_W2 = OFF_H1 + kT128;         // W2 [c][u]
+constexpr int OFF_S2 = OFF_W2 + kT128;         // S2 [c][u]
+constexpr int OFF_COEF = OFF_S2 + kT128;
+// float index: XT = the D recurrences' carried products at rows 31 and 63
+// (see the a1 stage), T11/T12 = transfer of rows 32..63 (32 entries each)
+constexpr int COEF_XT = 0, COEF_T11 = 64, COEF_T12 = 96, COEF_THETA = 128, COEF_A = 192, COEF_E = 256,
+              COEF_F = 320;
+constexpr int COEF_H16 = 384 * 4;                                   // byte offset of fp16 arrays
+constexpr int H16_WU = 0, H16_WD = 64;                              // half index: the fold weights
+constexpr int COEF_INT = COEF_H16 + 128 * 2;                        // byte offset of int slots
+constexpr int COEF_PAIR = COEF_INT + 64 * 4;                        // byte offset of (1-alpha, eta) pairs
+constexpr int kCoefBytes = COEF_PAIR + kB * 8;
+constexpr int OFF_STAGE = (OFF_COEF + kCoefBytes + 255) / 256 * 256;
+// staging for the next chunk's raw bf16 K, Q rows (row-major, 128 bytes a
+// row) and gates, filled one chunk ahead with LDS-direct loads
+constexpr int kStageBytes = 2 * kB * kD * 2 + 3 * kB * 4;
+constexpr int kLdsBytes = OFF_STAGE + kStageBytes;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+static_assert(8 * 256 * 4 <= kT64, "the parked y tiles fit the Delta2 area");
+
+// int slots
+constexpr int INT_AMAX_D2 = 0, INT_EWU = 1, INT_EWD = 2, INT_FAIL = 3, INT_T22 = 4;
+constexpr int INT_M2 = 8;     // per-wave maxima of |W2|, |S2| (8 slots)
+constexpr int INT_MA1 = 16;   // per-wave maxima of |A1|
+constexpr int INT_MH1 = 24;   // per-wave maxima of |H1|
+constexpr int INT_ESC = 32;   // per-wave exponents of the first-layer masked scores
+constexpr int INT_EDP = 40;   // per-wave exponents of the second-layer masked scores
+
+// ---- global workspace layout, per pair (bytes) ----
+// Exchange words are 8 bytes: a float and the sequence number of the chunk
+// that wrote it (see tstore / tpoll8).
+constexpr int64_t kXO = 2 * 2 * kThreads * 8 * 8;    // [half][parity] x 512 threads x 8 words, thread-major
+constexpr int64_t kXY = 2 * 2 * 256 * 8 * 8;         // [half][parity] x 256 threads x 8 words, thread-major
+constexpr int64_t kPairBytes = kXO + kXY;
+
+// ---- stage timing (a build option; off in the library) ----
+// With TM_STAGE_STAMPS=1 the eight waves of workgroup 0 record the shader
+// clock (s_memtime) at every stage boundary of chunks kStampFrom ..
+// kStampFrom + kStampChunks - 1 of its first stream; titans_mem_stage_stamps
+// (exported by that build only) copies them out.  stage_stamps.py builds the
+// instrumented library and prints the per-stage table.
+#ifndef TM_STAGE_STAMPS
+#define TM_STAGE_STAMPS 0
+#endif
+constexpr int kStampStages = 24, kStampFrom = 16, kStampChunks = 64;
+#if TM_STAGE_STAMPS
+__device__ unsigned long long stage_stamps[kStampChunks * kWaves * kStampStages];
+#define STAMP(k)                                                                                       \
+  do {                                                                                                 \
+    if (stamp_slot >= 0 && lane == 0)                                                                  \
+      stage_stamps[(stamp_slot * kWaves + w) * kStampStages + (k)] = __builtin_amdgcn_s_memtime();     \
+  } while (0)
+#else
+#define STAMP(k) \
+  do {           \
+  } while (0)
+#endif
+
+struct Params {
+  int N, chunk, streams, n_pairs;
+  const __hip_bfloat16* k;
+  const __hip_bfloat16* v;
+  const __hip_bfloat16* q;
+  const float* alpha;
+  const float* eta;
+  const float* theta;
+  const float* W_in;
+  const float* S_in;
+  __hip_bfloat16* y;
+  float* W_out;
+  float* S_out;
+  unsigned char* xbuf;   // n_pairs * kPairBytes, zeroed before every launch
+  unsigned* status;      // set to 1 when a pair gave up waiting
+  unsigned spin_max;
+  int chunk_gates;       // gates hold one value per chunk
+  int gstride;           // gates per stream: N, or ceil(N / chunk) with per-chunk gates
+};
+
+// index of the gate of the first token of chunk ci (token c0) of stream s
+__device__ __forceinline__ int64_t gate_base(const Params& p, int s, int ci, int c0) {
+  return (int64_t)s * p.gstride + (p.chunk_gates ? ci : c0);
+}
+
+__device__ __forceinline__ f4v mfma(h8 a, h8 b, f4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Operand fragments of v_mfma_f32_16x16x32_f16.  Lane l serves row (A) or
+// column (B) l & 15 and K group g = l >> 4 with 8 values.  Two orders of the
+// K slots are used (any order works if both operands of a product agree):
+// * register order, for products with an operand taken from accumulator
+//   tiles: slot i < 4 is k = kb + 4g + i, slot i >= 4 is k = kb + 16 + 4g +
+//   i - 4, i.e. rows 4g + i of two consecutive 16-row tiles;
+// * consecutive order, for products with both operands in LDS: slot i is
+//   k = kb + 8g + i (one 16-byte read).
+__device__ __forceinline__ h8 frag_rk(const _Float16* row, int kb, int g) {
+  const h4 lo = *(const h4*)(row + kb + 4 * g);
+  const h4 hi = *(const h4*)(row + kb + 16 + 4 * g);
+  return h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ h8 frag_c8(const _Float16* row, int kb, int g) {
+  return *(const h8*)(row + kb + 8 * g);
+}
+// two accumulator tiles (rows 0-15 and 16-31 of a K block) as a
+// register-order fragment, scaled to fp16
+__device__ __forceinline__ h8 tiles_frag(const f4v a, const f4v b, float f) {
+  return h8{(_Float16)(a[0] * f), (_Float16)(a[1] * f), (_Float16)(a[2] * f), (_Float16)(a[3] * f),
+            (_Float16)(b[0] * f), (_Float16)(b[1] * f), (_Float16)(b[2] * f), (_Float16)(b[3] * f)};
+}
+
+// ---- cross-lane helpers on DPP (no LDS traffic); call with all 64 lanes active ----
+// DPP controls: quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E, row_shr:n = 0x110 + n,
+// row_mirror = 0x140, row_half_mirror = 0x141, row_bcast:15 = 0x142, row_bcast:31 = 0x143
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xf, 0xf, false));
+}
+// lanes whose DPP source is out of range (or whose row is masked off) get `ident`
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ float dpp_or(float ident, float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(ident), __float_as_int(x), kCtrl, kRowMask, 0xf, false));
+}
+__device__ __forceinline__ float lane_value(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// maximum over the wave, returned uniformly
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_mov<0xB1>(v));
+  v = fmaxf(v, dpp_mov<0x4E>(v));
+  v = fmaxf(v, dpp_mov<0x141>(v));
+  v = fmaxf(v, dpp_mov<0x140>(v));   // every lane of a row of 16 holds the row's maximum
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
+
+// inclusive prefix product over the lanes (lane l: x_0 * ... * x_l)
+__device__ __forceinline__ float wave_prefix_prod(float x) {
+  x *= dpp_or<0x111>(1.f, x);
+  x *= dpp_or<0x112>(1.f, x);
+  x *= dpp_or<0x114>(1.f, x);
+  x *= dpp_or<0x118>(1.f, x);
+  x *= dpp_or<0x142, 0xa>(1.f, x);
+  x *= dpp_or<0x143, 0xc>(1.f, x);
+  return x;
+}
+
+// inclusive scan of the affine maps f_l(u) = a_l u + b_l over the lanes:
+// on return lane l holds f_l o ... o f_0 as (a, b), i.e. a = a_0 ... a_l and
+// b = the value of u_l = a_l u_{l-1} + b_l started from u_{-1} = 0
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ void affine_step(float& a, float& b) {
+  const float a2 = dpp_or<kCtrl, kRowMask>(1.f, a);
+  const float b2 = dpp_or<kCtrl, kRowMask>(0.f, b);
+  b = fmaf(a, b2, b);
+  a *= a2;
+}
+__device__ __forceinline__ void wave_affine_scan(float& a, float& b) {
+  affine_step<0x111>(a, b);
+  affine_step<0x112>(a, b);
+  affine_step<0x114>(a, b);
+  affine_step<0x118>(a, b);
+  affine_step<0x142, 0xa>(a, b);
+  affine_step<0x143, 0xc>(a, b);
+}
+
+// power-of-two scale exponent bringing amax into [2^13, 2^14)
+__device__ __forceinline__ int scale_exp(float amax) {
+  if (!(amax > 0.f) || !(amax < INFINITY)) return 0;
+  int e;
+  (void)frexpf(amax, &e);
+  return 14 - e;
+}
+// 2^-k as a float multiplier: exact rescaling while 2^-k is a normal float,
+// i.e. k <= 126; beyond that the factor flushes towards zero (scaled values
+// far below any tolerance floor).  k is clamped below so that the factor
+// stays finite.
+__device__ __forceinline__ float pow2neg(int k) { return ldexpf(1.f, -max(k, -126)); }
+// 2^e as a float multiplier for the scalings up to fp16 operands (one
+// multiply per element instead of an ldexp; computed once per block).  Equal
+// to ldexpf(x, e) whenever e <= 127, i.e. unless the block's amax is below
+// 2^-113, where the clamped scale leaves the operand smaller than [2^13, 2^14)
+// but still far below every tolerance floor.
+__device__ __forceinline__ float pow2pos(int e) { return ldexpf(1.f, min(e, 127)); }
+
+__device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+
+__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ h8 bf16x8_to_h8(uint4 u) {
+  return h8{(_Float16)bf16_lo(u.x), (_Float16)bf16_hi(u.x), (_Float16)bf16_lo(u.y), (_Float16)bf16_hi(u.y),
+            (_Float16)bf16_lo(u.z), (_Float16)bf16_hi(u.z), (_Float16)bf16_lo(u.w), (_Float16)bf16_hi(u.w)};
+}
+
+// Pair exchange: every 8-byte word carries a float and the sequence number
+// of the chunk that wrote it, stored with one single-copy-atomic 64-bit
+// agent-coherent (sc1) store.  A reader polls its own words until each
+// carries the sequence number it expects, so no flag, store-completion wait
+// or barrier orders the exchange: a word is either the old one (old number)
+// or the new one, never a mix.  Sequence numbers start at 1 and the buffers
+// are zeroed before every launch, so no word of an earlier call can match.
+// The buffers are thread-major: word e of thread t sits at e * kT + t, so
+// each store or load instruction of a wave covers 512 contiguous bytes
+// (whole lines: an agent-coherent store writes through L2), and every thread
+// reads back exactly the words the same thread of the partner wrote.  Two
+// parities per half double-buffer the chunks: the partner overwrites a slot
+// two chunks later, after having read this half's next chunk, which this
+// half writes only after reading the slot.
+__device__ __forceinline__ void tstore(float* base, int idx, float v, unsigned tag) {
+  const unsigned long long wd = (unsigned long long)__float_as_uint(v) | ((unsigned long long)tag << 32);
+  __hip_atomic_store((unsigned long long*)base + idx, wd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// words t, t + kT, ..., t + 7 kT until all carry `tag`; false = gave up after
+// spin_max polls (spin_max = 0 gives up at once: the failure-path test hook)
+template <int kT>
+__device__ __forceinline__ bool tpoll8(const float* base, int t, unsigned tag, unsigned spin_max, float* out) {
+  for (unsigned it = 0; it < spin_max; ++it) {
+    unsigned long long wd[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      wd[e] = __hip_atomic_load((const unsigned long long*)base + (e * kT + t), __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+    bool ok = true;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      out[e] = __uint_as_float((unsigned)wd[e]);
+      ok = ok && (unsigned)(wd[e] >> 32) == tag;
+    }
+    if (ok) return true;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return false;
+}
+
+// A chunk's raw inputs, one thread's share: 16 bytes (8 bf16) of row
+// j = tid / 8 of K and of Q (columns 8 (tid % 8) ..), and for tid < 64 the
+// gates of token tid.  Rows and tokens past the chunk end read as zeros
+// (gates as "no forgetting, no decay, no write").
+struct ChunkRegs {
+  uint4 k, q;
+  float ga, ge, gt;
+};
+
+__device__ __forceinline__ ChunkRegs load_chunk_regs(const Params& p, int64_t row0, int64_t g0, int n, int tid) {
+  ChunkRegs r;
+  const int j = tid >> 3, cb = (tid & 7) * 8;
+  if (j < n) {
+    r.k = *(const uint4*)(p.k + (row0 + j) * kD + cb);
+    r.q = *(const uint4*)(p.q + (row0 + j) * kD + cb);
+  } else {
+    r.k = r.q = make_uint4(0, 0, 0, 0);
+  }
+  r.ga = 0.f; r.ge = 1.f; r.gt = 0.f;
+  if (tid < kB && tid < n) {
+    const int64_t gi = g0 + (p.chunk_gates ? 0 : tid);
+    r.ga = p.alpha[gi];
+    r.ge = p.eta[gi];
+    r.gt = p.theta[gi];
+  }
+  return r;
+}
+
+// Prefetch of a chunk's raw rows straight into the LDS staging area
+// (global_load_lds: lane l of an instruction writes 16 bytes at base + 16 l,
+// or 4 bytes at base + 4 l; lanes that do not load write nothing).  Thread t
+// loads the 16 bytes load_chunk_regs gives it into slot t of each area, so
+// the area holds the chunk's rows in row-major order and each thread later
+// reads back what it loaded itself.  Wave 0 loads the gates.  Rows and
+// tokens past the chunk end are left out and replaced on unstaging.
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+__device__ __forceinline__ void prefetch_chunk_lds(const Params& p, int64_t row0, int64_t g0, int n, int tid,
+                                                   unsigned char* stage) {
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int j = tid >> 3, cb = (tid & 7) * 8;
+  uint4* sk = (uint4*)stage;
+  uint4* sq = (uint4*)(stage + kB * kD * 2);
+  if (j < n) {
+    __builtin_amdgcn_global_load_lds((const void*)(p.k + (row0 + j) * kD + cb), (lds_void_ptr)(sk + 64 * w), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(p.q + (row0 + j) * kD + cb), (lds_void_ptr)(sq + 64 * w), 16, 0, 0);
+  }
+  if (w == 0 && lane < n) {
+    float* g = (float*)(stage + 2 * kB * kD * 2);
+    const int64_t gi = g0 + (p.chunk_gates ? 0 : lane);   // per-chunk gates: every lane loads the one value
+    __builtin_amdgcn_global_load_lds((const void*)(p.alpha + gi), (lds_void_ptr)g, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(p.eta + gi), (lds_void_ptr)(g + kB), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(p.theta + gi), (lds_void_ptr)(g + 2 * kB), 4, 0, 0);
+  }
+}
+
+__device__ __forceinline__ ChunkRegs unstage_chunk_regs(const unsigned char* stage, int n, int tid) {
+  ChunkRegs r;
+  const int j = tid >> 3;
+  if (j < n) {
+    r.k = ((const uint4*)stage)[tid];
+    r.q = ((const uint4*)(stage + kB * kD * 2))[tid];
+  } else {
+    r.k = r.q = make_uint4(0, 0, 0, 0);
+  }
+  r.ga = 0.f; r.ge = 1.f; r.gt = 0.f;
+  if (tid < kB && tid < n) {
+    const float* g = (const float*)(stage + 2 * kB * kD * 2);
+    r.ga = g[tid]; r.ge = g[kB + tid]; r.gt = g[2 * kB + tid];
+  }
+  return r;
+}
+
+// the exchange buffers (no word may carry a valid sequence number) and the
+// status word, cleared before every launch by a fill kernel
+__global__ void zero_exchange_kernel(uint4* buf, int64_t n16, unsigned* status) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
+    buf[i] = make_uint4(0, 0, 0, 0);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0u;
+}
+
+// A half that gave up waiting for its partner writes NaN to W_out, S_out
+// and y of every stream the pair serves (s = pair, pair + n_pairs, ...),
+// after all of its own earlier writes, so a give-up never passes for a
+// result, in place or not.  The partner gives up as well at its next wait
+// and does the same; only a partner that had already passed its last wait
+// can still write rows of its own afterwards.
+__device__ void poison_pair_streams(const Params& p, int pair, int tid) {
+  const unsigned fnan = __float_as_uint(__builtin_nanf(""));
+  const uint4 f4 = make_uint4(fnan, fnan, fnan, fnan);
+  const uint4 b8 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);   // bf16 quiet NaNs
+  for (int s = pair; s < p.streams; s += p.n_pairs) {
+    uint4* Wo = (uint4*)(p.W_out + (int64_t)s * kP);
+    uint4* So = (uint4*)(p.S_out + (int64_t)s * kP);
+    for (int i = tid; i < kP / 4; i += kThreads) {
+      Wo[i] = f4;
+      So[i] = f4;
+    }
+    uint4* yo = (uint4*)(p.y + (int64_t)s * p.N * kD);
+    const int64_t ny = (int64_t)p.N * kD / 8;
+    for (int64_t i = tid; i < ny; i += kThreads) yo[i] = b8;
+  }
+}
+
+__device__ __forceinline__ float max8(float m, const float* x) {
+  return fmaxf(fmaxf(fmaxf(m, fabsf(x[0])), fmaxf(fabsf(x[1]), fabsf(x[2]))),
+               fmaxf(fmaxf(fabsf(x[3]), fabsf(x[4])), fmaxf(fmaxf(fabsf(x[5]), fabsf(x[6])), fabsf(x[7]))));
+}
+__device__ __forceinline__ float max4(float m, f4v x) {
+  return fmaxf(fmaxf(m, fmaxf(fabsf(x[0]), fabsf(x[1]))), fmaxf(fabsf(x[2]), fabsf(x[3])));
+}
+
+// kRW: retrieval after each token's write (true) or at the chunk-start
+// state (false: y_j = M_{W_0}(q_j), without the masked correction terms)
+template <bool kRW>
+__global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  _Float16* sK = (_Float16*)(smem + OFF_K);
+  _Float16* sKT = (_Float16*)(smem + OFF_KT);
+  _Float16* sQ = (_Float16*)(smem + OFF_Q);
+  _Float16* sD2 = (_Float16*)(smem + OFF_D2);
+  _Float16* sD2T = (_Float16*)(smem + OFF_D2T);
+  _Float16* sSC = (_Float16*)(smem + OFF_SC);
+  float* sDM = (float*)(smem + OFF_DM);
+  _Float16* sA1 = (_Float16*)(smem + OFF_A1);
+  _Float16* sH1 = (_Float16*)(smem + OFF_H1);
+  _Float16* sW2 = (_Float16*)(smem + OFF_W2);
+  _Float16* sS2 = (_Float16*)(smem + OFF_S2);
+  float* cf = (float*)(smem + OFF_COEF);
+  _Float16* ch = (_Float16*)(smem + OFF_COEF + COEF_H16);
+  int* ci = (int*)(smem + OFF_COEF + COEF_INT);
+
+  const int tid0 = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid0 >> 6);
+  // The thread index is re-read at the top of every chunk (see `relane`):
+  // every LDS and global address of the chunk is derived from it, and the
+  // compiler would otherwise hoist dozens of such addresses out of the chunk
+  // loop and spill them.
+  int tid = tid0, lane = tid0 & 63, lc = lane & 15, g = lane >> 4;
+  // D[j][i] with the part carried over from row 31 (rows 32..63 of columns
+  // 0..31; see the a1 stage); the condition is uniform in every caller's wave
+  auto d_full = [&](int j, int i) {
+    float d = sDM[j * RF + i];
+    if (j >= 32 && i < 32)
+      d = fmaf(cf[COEF_T11 + j - 32], sDM[31 * RF + i], fmaf(cf[COEF_T12 + j - 32], cf[COEF_XT + i], d));
+    return d;
+  };
+  auto relane = [&] {
+    int t = tid0;
+    asm volatile("" : "+v"(t));
+    tid = t;
+    lane = t & 63;
+    lc = lane & 15;   // row / column inside a 16x16 tile
+    g = lane >> 4;    // K group; accumulator rows 4g .. 4g+3
+  };
+
+  // pair / half: blocks g and g + 8 usually share an XCD (round-robin dispatch),
+  // so pairs are formed that way when the grid allows it; correctness does
+  // not depend on the placement
+  int pair, half;
+  {
+    const int b = blockIdx.x;
+    if ((gridDim.x & 15) == 0) {
+      const int slot = b >> 3;
+      pair = (b & 7) + 8 * (slot >> 1);
+      half = slot & 1;
+    } else {
+      pair = b >> 1;
+      half = b & 1;
+    }
+  }
+  const int uw = kUW * w;               // this wave's first unit inside the workgroup's 128
+  const int hs = kUG * half + uw;        // ... and inside the layer's 256
+  // the workgroup-level output tiles of this wave (O, y: tokens tj, columns
+  // tc0, tc0 + 1; the masked scores: tokens tj, keys tc0, tc0 + 1)
+  const int tj = w >> 1, tc0 = 2 * (w & 1);
+  // y rows of tokens 32 half .. 32 half + 31 are finished by this half: its
+  // waves 4 half .. 4 half + 3 keep their y tiles, the others send theirs
+  const bool keeps_y = (tj >> 1) == half;
+
+  unsigned char* xb = p.xbuf + (int64_t)pair * kPairBytes;
+  float* xO_me = (float*)(xb) + half * 2 * kThreads * 16;
+  const float* xO_pt = (const float*)(xb) + (1 - half) * 2 * kThreads * 16;
+  float* xY_me = (float*)(xb + kXO) + half * 2 * 256 * 16;
+  const float* xY_pt = (const float*)(xb + kXO) + (1 - half) * 2 * 256 * 16;
+
+  // a half that gives up waiting for its partner records it (status word,
+  // and the workgroup's flag checked at its next barrier)
+  auto give_up = [&] {
+    ci[INT_FAIL] = 1;
+    __hip_atomic_store(p.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  bool failed = false;
+  if (tid0 == 0) ci[INT_FAIL] = 0;
+
+  // The y tiles of the previous chunk a keeping thread finishes (rows
+  // 16 tj + 4g + r, columns 16 (tc0 + i) + lc) wait across the chunk
+  // boundary in the Delta2 [j][c] area of LDS, whose only reader is the
+  // backprop product: it is free from there until the next chunk writes
+  // Delta2, after its exchange.  Registers would be spilled across the
+  // boundary, and every reload from scratch would wait for the exchange
+  // stores in flight.
+  float* ypark = (float*)(smem + OFF_D2);   // 8 floats x 256 keeping threads, thread-major
+  int64_t prev_row0 = -1;   // global token row of the previous chunk's first token
+  int prev_n = 0;
+  unsigned seq = 0;         // sequence number of the current chunk (1, 2, ...)
+  bool staged = false;      // the staging area holds the rows of the chunk about to start
+
+  // the partner's partial for my y tiles of the chunk numbered `tag`
+  // (thread-major over the 256 threads of the keeping / sending waves)
+  auto load_prev_y = [&](unsigned tag, float* pv) {
+    if (keeps_y && !tpoll8<256>(xY_pt + (tag & 1u) * 256 * 16, tid & 255, tag, p.spin_max, pv)) give_up();
+  };
+  // the fixed-order sum of the two partials, stored as bf16
+  auto finish_prev_y = [&](const float* pv) {
+    if (!keeps_y) return;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * tj + 4 * g + r;
+        if (j < prev_n) {
+          const float a = ypark[(4 * i + r) * 256 + (tid & 255)], b = pv[4 * i + r];
+          p.y[(prev_row0 + j) * kD + 16 * (tc0 + i) + lc] = __float2bfloat16(half == 0 ? a + b : b + a);
+        }
+      }
+  };
+  __syncthreads();
+
+  for (int s = pair; s < p.streams && !failed; s += p.n_pairs) {
+    const int64_t tok0 = (int64_t)s * p.N;
+    // ---- this wave's state, VGPR-resident ----
+    // W1s[ct]: rows c = 16 ct + 4g + r, lanes u = hs + lc   (W1[u][c])
+    // W2s[ct]: rows c = 16 ct + 4g + r, lanes u = hs + lc   (W2[c][u])
+    f4v W1s[4], S1s[4], W2s[4], S2s[4];
+    float m1 = 0.f, m2 = 0.f;   // this lane's max |W|,|S| per layer (for the operand scales)
+    {
+      const float* Wi = p.W_in + (int64_t)s * kP;
+      const float* Si = p.S_in + (int64_t)s * kP;
+      const int u = hs + lc;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int c = 16 * ct + 4 * g;
+        W1s[ct] = *(const f4v*)(Wi + u * kD + c);
+        S1s[ct] = *(const f4v*)(Si + u * kD + c);
+        m1 = max4(max4(m1, W1s[ct]), S1s[ct]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          W2s[ct][r] = Wi[kH * kD + (c + r) * kH + u];
+          S2s[ct][r] = Si[kH * kD + (c + r) * kH + u];
+        }
+        m2 = max4(max4(m2, W2s[ct]), S2s[ct]);
+      }
+    }
+
+    for (int c0 = 0, cidx = 0; c0 < p.N; c0 += p.chunk, ++cidx) {
+      const int n = min(p.chunk, p.N - c0);
+      relane();
+      ++seq;
+      const int stamp_slot = (TM_STAGE_STAMPS && blockIdx.x == 0 && s == pair && cidx >= kStampFrom &&
+                              cidx < kStampFrom + kStampChunks) ? cidx - kStampFrom : -1;
+      (void)stamp_slot;
+      STAMP(0);
+
+      // ================= the chunk's K, K^T, Q (fp16) and gates into LDS =================
+      {
+        // (this thread's staging loads were waited for after the previous
+        // chunk's exchange; waiting here would also wait for the y exchange
+        // stores just issued)
+        const ChunkRegs cr = staged ? unstage_chunk_regs(smem + OFF_STAGE, n, tid)
+                                    : load_chunk_regs(p, tok0 + c0, gate_base(p, s, cidx, c0), n, tid);
+        const int j = tid >> 3, cb = (tid & 7) * 8;
+        const h8 kv = bf16x8_to_h8(cr.k), qv = bf16x8_to_h8(cr.q);
+        *(h8*)(sK + j * RS + cb) = kv;
+        *(h8*)(sQ + j * RS + cb) = qv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sKT[(cb + i) * RS + j] = kv[i];
+        if (tid < kB) {
+          cf[COEF_THETA + tid] = cr.gt;
+          float2* pairs = (float2*)(smem + OFF_COEF + COEF_PAIR);
+          pairs[tid] = make_float2(1.f - cr.ga, cr.ge);
+        }
+        if (tid == 0) {
+          ci[INT_AMAX_D2] = 0;
+          ci[INT_FAIL] = 0;
+        }
+        const float wm2 = wave_max(m2);
+        if (lane == 0) ci[INT_M2 + w] = __float_as_int(wm2);
+      }
+      STAMP(1);
+      __syncthreads();
+      // the next chunk's rows go straight to the staging area (read at its start)
+      {
+        int next_s = s, next_c0 = c0 + p.chunk, next_ci = cidx + 1;
+        if (next_c0 >= p.N) { next_s = s + p.n_pairs; next_c0 = 0; next_ci = 0; }
+        const bool has_next = next_s < p.streams && p.N > 0;
+        if (has_next)
+          prefetch_chunk_lds(p, (int64_t)next_s * p.N + next_c0, gate_base(p, next_s, next_ci, next_c0),
+                             min(p.chunk, p.N - next_c0), tid, smem + OFF_STAGE);
+        staged = has_next;
+      }
+      STAMP(2);
+
+      STAMP(3);
+      // state scales: W1/S1 per wave; W2/S2 joint over the workgroup (the
+      // half's O and y are contractions over all its waves' W2 and S2 copies)
+      int e2;
+      {
+        float mm = 0.f;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) mm = fmaxf(mm, __int_as_float(ci[INT_M2 + i]));
+        e2 = scale_exp(mm);
+      }
+      const int e1 = scale_exp(wave_max(m1));
+      const float f1 = pow2pos(e1), f2 = pow2pos(e2);
+      // state operand fragments (register order over d: K-step s covers c = 32 s ..)
+      h8 w1f[2], s1f[2], w2f[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        w1f[st] = tiles_frag(W1s[2 * st], W1s[2 * st + 1], f1);
+        s1f[st] = tiles_frag(S1s[2 * st], S1s[2 * st + 1], f1);
+        w2f[st] = tiles_frag(W2s[2 * st], W2s[2 * st + 1], f2);
+      }
+      // W2 and S2 copies [c][u] over the workgroup's units (for O and y)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c = 16 * ct + 4 * g + r;
+          sW2[c * RW + uw + lc] = w2f[ct >> 1][4 * (ct & 1) + r];
+          sS2[c * RW + uw + lc] = (_Float16)(S2s[ct][r] * f2);
+        }
+
+      // ================= a2: key-side forward Z1 = K W1^T (rows j, lanes u) =================
+      // A1 = SiLU(Z1) and SiLU'(Z1) (fp16, for the backprop)
+      f4v A1f[4];
+      h4 SPh[4];
+      {
+        float am = 0.f;
+        const float zun = pow2neg(e1);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          f4v z = {};
+          const _Float16* krow = sK + (16 * tt + lc) * RS;
+#pragma unroll
+          for (int st = 0; st < 2; ++st) z = mfma(frag_rk(krow, 32 * st, g), w1f[st], z);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float zz = z[r] * zun;
+            const float sg = sigmoidf_(zz);
+            const float a = zz * sg;
+            A1f[tt][r] = a;
+            SPh[tt][r] = (_Float16)(sg + a * (1.f - sg));   // s (1 + z (1 - s))
+          }
+          am = max4(am, A1f[tt]);
+        }
+        const float wam = wave_max(am);
+        if (lane == 0) ci[INT_MA1 + w] = __float_as_int(wam);
+      }
+      STAMP(4);
+      __syncthreads();   // every wave's A1 maximum and W2/S2 copies
+      STAMP(5);
+      // A1 with the workgroup-wide scale: fragments (register order over the
+      // tokens) for the second-layer fold, and the copy [j][u] for O and the scores
+      int eA1;
+      h8 a1f[2];
+      {
+        float mm = 0.f;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) mm = fmaxf(mm, __int_as_float(ci[INT_MA1 + i]));
+        eA1 = scale_exp(mm);
+        const float fA1 = pow2pos(eA1);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) a1f[st] = tiles_frag(A1f[2 * st], A1f[2 * st + 1], fA1);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sA1[(16 * tt + 4 * g + r) * RW + uw + lc] = a1f[tt >> 1][4 * (tt & 1) + r];
+      }
+      STAMP(6);
+      __syncthreads();   // every wave's A1 copy
+      STAMP(7);
+
+      // ================= this half's O = A1 W2^T over its 128 units: tiles (tj, tc0 + i) =================
+      float om[8];
+      {
+        const float co = pow2neg(eA1 + e2);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          f4v acc = {};
+          const _Float16* arow = sA1 + (16 * tj + lc) * RW;
+          const _Float16* brow = sW2 + (16 * (tc0 + i) + lc) * RW;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) acc = mfma(frag_c8(arow, 32 * kk, g), frag_c8(brow, 32 * kk, g), acc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) om[4 * i + r] = acc[r] * co;
+        }
+      }
+      // publish this half's O (words tagged with this chunk's number)
+      const unsigned par = seq & 1u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tstore(xO_me + par * kThreads * 16, e * kThreads + tid, om[e], seq);
+      STAMP(8);
+
+      // ---- work that does not need the partner, while the exchange is in flight ----
+      // this chunk's V for the residual (used after the exchange)
+      // Issued unconditionally from a row clamped into the chunk (rows past
+      // its end are zeroed at use): a load under a branch would end a basic
+      // block and be waited for at once, which also waits for the exchange
+      // stores still in flight.
+      unsigned short vr[8];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = min(16 * tj + 4 * g + r, n - 1);
+          vr[4 * i + r] = *(const unsigned short*)(p.v + (tok0 + c0 + j) * kD + 16 * (tc0 + i) + lc);
+        }
+      // ================= a1: coefficients (both halves compute them identically) =================
+      // While the exchange is in flight.  Lane m of a wave holds token m's
+      // (1 - alpha_m, eta_m); padding tokens have alpha = 0, eta = 1, theta = 0.
+      //
+      // D, one lane per column i: t = theta_i prod_{i<m<=j} eta_m, started at
+      // j == i by adding theta_i to a zero product, and
+      // D[j][i] = (1 - alpha_j) D[j-1][i] + t -- one fma per row on each of the
+      // two carried values, the row's gates broadcast from LDS.  Wave 3 runs
+      // rows 0..31 and wave 5 rows 32..63, each starting from zero.  For
+      // columns i >= 32 wave 5's rows are exact (their recurrences start at
+      // row i); for i < 32 its rows lack the part carried over from row 31,
+      // which every reader adds (d_full) through the column-independent
+      // transfer
+      //   (D, t)_j += (T11_j D_31 + T12_j t_31, T22_j t_31),
+      // T11_j = prod_{32<=m<=j} (1 - alpha_m), T22_j = prod_{32<=m<=j} eta_m,
+      // T12_j = sum_{32<=l<=j} prod_{l<m<=j} (1 - alpha_m) T22_l,
+      // which wave 6 gets from prefix scans restarted at row 32, beside E_j (a
+      // prefix product of eta) and (A_j, F_j) (a prefix scan of the maps
+      // u -> (1 - alpha_j) u + E_j: A_j is the scan's product part, F_j its
+      // value from F_{-1} = 0).  First read after the barrier that follows
+      // the exchange.
+      if (w == 3 || w == 5) {
+        const int i = lane;
+        const int j0 = w == 3 ? 0 : 32;
+        const float thi = cf[COEF_THETA + i];
+        float di = 0.f, t = 0.f;
+        const float4* pairs4 = (const float4*)(smem + OFF_COEF + COEF_PAIR) + j0 / 2;
+#pragma unroll 2
+        for (int b = 0; b < 4; ++b) {
+          // 8 rows per batch: the steps' (1 - alpha_j, eta_j) pairs as LDS
+          // broadcasts (two steps per 16-byte read), the rows stored after
+          // the batch so that the gate reads never wait behind row stores
+          float4 gq[4];
+          float drows[8];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) gq[q] = pairs4[4 * b + q];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            const int j = j0 + 8 * b + jj;
+            const float ga = (jj & 1) ? gq[jj >> 1].z : gq[jj >> 1].x;
+            const float ge = (jj & 1) ? gq[jj >> 1].w : gq[jj >> 1].y;
+            const float inj = i == j ? thi : 0.f;   // theta_i enters at row i
+            t = fmaf(ge, t, inj);
+            di = fmaf(ga, di, t);
+            drows[jj] = di;
+          }
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) sDM[(j0 + 8 * b + jj) * RF + i] = drows[jj];
+        }
+        // wave 3: t at row 31 for i < 32; wave 5: t at row 63 (= U_i) for i >= 32
+        if ((w == 3) == (i < 32)) cf[COEF_XT + i] = t;
+      } else if (w == 6) {
+        const float2 gl = ((const float2*)(smem + OFF_COEF + COEF_PAIR))[lane];
+        const float e = wave_prefix_prod(gl.y);
+        float a = gl.x, f = e;
+        wave_affine_scan(a, f);
+        cf[COEF_A + lane] = a;
+        cf[COEF_E + lane] = e;
+        cf[COEF_F + lane] = f;
+        // the same scans restarted at row 32 (identity maps below it)
+        const bool lo = lane < 32;
+        const float eb = wave_prefix_prod(lo ? 1.f : gl.y);
+        float a2 = lo ? 1.f : gl.x, f2b = lo ? 0.f : eb;
+        wave_affine_scan(a2, f2b);
+        if (!lo) {
+          cf[COEF_T11 + lane - 32] = a2;
+          cf[COEF_T12 + lane - 32] = f2b;
+        }
+        if (lane == 63) ci[INT_T22] = __float_as_int(eb);
+      }
+      // the raw first-layer scores Q K^T (tiles (tj, tc0 + i)) and the query
+      // products Q W1^T, Q S1^T
+      f4v scr[2], accW[4], accS[4];
+      if constexpr (kRW) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          f4v acc = {};
+          const _Float16* arow = sQ + (16 * tj + lc) * RS;
+          const _Float16* brow = sK + (16 * (tc0 + i) + lc) * RS;
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) acc = mfma(frag_c8(arow, 32 * kk, g), frag_c8(brow, 32 * kk, g), acc);
+          scr[i] = acc;
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        f4v aw = {}, as = {};
+        const _Float16* qrow = sQ + (16 * tt + lc) * RS;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const h8 qf = frag_rk(qrow, 32 * st, g);
+          aw = mfma(qf, w1f[st], aw);
+          if constexpr (kRW) as = mfma(qf, s1f[st], as);
+        }
+        accW[tt] = aw;
+        accS[tt] = as;
+      }
+      STAMP(9);
+      // the partner's O for this thread's elements, and its part of my y tiles
+      // of the previous chunk
+      float pvv[8], pyv[8];
+      if (!tpoll8<kThreads>(xO_pt + par * kThreads * 16, tid, seq, p.spin_max, pvv)) give_up();
+      if (prev_row0 >= 0) load_prev_y(seq - 1, pyv);
+      // every vector memory operation of this thread done, the next chunk's
+      // staging loads included (a no-op after a poll, which waited for them)
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      STAMP(10);
+      // ================= O = half 0 + half 1, Delta2 = O - V (this thread's 8 elements) =================
+      float d2v[8];
+      {
+        float am = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = 16 * tj + 4 * g + (e & 3);
+          const float o = half == 0 ? om[e] + pvv[e] : pvv[e] + om[e];
+          const float vv = __uint_as_float((unsigned)vr[e] << 16);
+          d2v[e] = j < n ? o - vv : 0.f;
+        }
+        am = max8(am, d2v);
+        am = wave_max(am);
+        if (lane == 0) atomicMax((unsigned int*)&ci[INT_AMAX_D2], __float_as_uint(am));
+      }
+      // last chunk's y tiles
+      if (prev_row0 >= 0) finish_prev_y(pyv);
+      STAMP(11);
+      __syncthreads();   // every wave's Delta2 amax, the coefficients
+      if (ci[INT_FAIL]) { failed = true; break; }
+      STAMP(12);
+
+      // ---- Delta2 (fp16, workgroup-wide scale) as [j][c] and [c][j] ----
+      const int eD2 = scale_exp(__uint_as_float((unsigned)ci[INT_AMAX_D2]));
+      {
+        const float fD2 = pow2pos(eD2);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          h4 hv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            hv[r] = (_Float16)(d2v[4 * i + r] * fD2);
+            sD2[(16 * tj + 4 * g + r) * RS + 16 * (tc0 + i) + lc] = hv[r];
+          }
+          *(h4*)(sD2T + (16 * (tc0 + i) + lc) * RS + 16 * tj + 4 * g) = hv;
+        }
+      }
+      // ---- first-layer masked scores SC1 = D o (Q K^T), tiles (tj, tc0 + i), this wave's own scale ----
+      if constexpr (kRW) {
+        float sc[8], am = 0.f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            sc[4 * i + r] = scr[i][r] * d_full(16 * tj + 4 * g + r, 16 * (tc0 + i) + lc);
+        am = wave_max(max8(am, sc));
+        const int esc = scale_exp(am);
+        const float fsc = pow2pos(esc);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            sSC[(16 * tj + 4 * g + r) * RS + 16 * (tc0 + i) + lc] = (_Float16)(sc[4 * i + r] * fsc);
+        if (lane == 0) ci[INT_ESC + w] = esc;
+      }
+      if (w == 3) {
+        // weights of the state update: U_i = theta_i prod_{m>i} eta_m and
+        // D[n-1][i], each scaled into (0.5, 1] for fp16 (padding has eta = 1)
+        const int i = lane;
+        const float ti = cf[COEF_XT + i];
+        const float ui = i < 32 ? ti * __int_as_float(ci[INT_T22]) : ti;
+        const float dlast = d_full(n - 1, i);
+        const float mu = wave_max(fabsf(ui)), md = wave_max(fabsf(dlast));
+        int eu = 0, ed = 0;
+        if (mu > 0.f && mu < INFINITY) { (void)frexpf(mu, &eu); eu = -eu; }
+        if (md > 0.f && md < INFINITY) { (void)frexpf(md, &ed); ed = -ed; }
+        ch[H16_WU + i] = (_Float16)ldexpf(ui, eu);
+        ch[H16_WD + i] = (_Float16)ldexpf(dlast, ed);
+        if (lane == 0) { ci[INT_EWU] = eu; ci[INT_EWD] = ed; }
+      }
+      STAMP(13);
+      __syncthreads();   // Delta2 copies, the first-layer scores and the update weights
+      STAMP(14);
+
+      // ================= a3: Delta1 = (Delta2 W2) * SiLU'(Z1)  (rows j, lanes u) =================
+      h8 d1f[2];
+      int eD1;
+      {
+        f4v Df[4];
+        float am = 0.f;
+        const float dun = pow2neg(eD2 + e2);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          f4v acc = {};
+          const _Float16* arow = sD2 + (16 * tt + lc) * RS;
+#pragma unroll
+          for (int st = 0; st < 2; ++st) acc = mfma(frag_rk(arow, 32 * st, g), w2f[st], acc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Df[tt][r] = acc[r] * dun * (float)SPh[tt][r];
+          am = max4(am, Df[tt]);
+        }
+        eD1 = scale_exp(wave_max(am));
+        const float fD1 = pow2pos(eD1);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) d1f[st] = tiles_frag(Df[2 * st], Df[2 * st + 1], fD1);
+      }
+
+      STAMP(15);
+      // ================= a5 layer 1: Zq1 = diag(A) Q W1^T + diag(F) Q S1^T - SC1 Delta1 =================
+      f4v H1f[4];
+      {
+        float am = 0.f;
+        const float cz = pow2neg(e1);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          f4v z;
+          if constexpr (kRW) {
+            // the masked term's two K-steps carry the scales of the waves that produced them
+            const _Float16* srow = sSC + (16 * tt + lc) * RS;
+            f4v m0 = {}, m1v = {};
+            m0 = mfma(frag_rk(srow, 0, g), d1f[0], m0);
+            m1v = mfma(frag_rk(srow, 32, g), d1f[1], m1v);
+            const float c30 = pow2neg(eD1 + ci[INT_ESC + 2 * tt]), c31 = pow2neg(eD1 + ci[INT_ESC + 2 * tt + 1]);
+            const f4v av = *(const f4v*)(cf + COEF_A + 16 * tt + 4 * g);
+            const f4v fv = *(const f4v*)(cf + COEF_F + 16 * tt + 4 * g);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float main = fmaf(av[r], accW[tt][r], fv[r] * accS[tt][r]) * cz;
+              z[r] = fmaf(m0[r], -c30, fmaf(m1v[r], -c31, main));
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) z[r] = accW[tt][r] * cz;
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) H1f[tt][r] = z[r] * sigmoidf_(z[r]);
+          am = max4(am, H1f[tt]);
+        }
+        const float wam = wave_max(am);
+        if (lane == 0) ci[INT_MH1 + w] = __float_as_int(wam);
+      }
+
+      STAMP(16);
+      const float An = cf[COEF_A + n - 1], En = cf[COEF_E + n - 1], Fn = cf[COEF_F + n - 1];
+      const int ewU = ci[INT_EWU], ewD = ci[INT_EWD];
+      float m1n = 0.f, m2n = 0.f;
+      // the fold weights as fragments in register order over the tokens
+      h8 wuf[2], wdf[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        wuf[st] = frag_rk(ch + H16_WU, 32 * st, g);
+        wdf[st] = frag_rk(ch + H16_WD, 32 * st, g);
+      }
+      // ================= a4, layer 1 (W1, S1 are not read again this chunk) =================
+      // G1^T[c][u] = sum_j K[j][c] w_j Delta1[j][u]
+      {
+        const float uD1 = pow2neg(ewD + eD1), uU1 = pow2neg(ewU + eD1);
+        const h8 bu0 = d1f[0] * wuf[0], bu1 = d1f[1] * wuf[1];
+        const h8 bd0 = d1f[0] * wdf[0], bd1 = d1f[1] * wdf[1];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const _Float16* arow = sKT + (16 * ct + lc) * RS;
+          const h8 k0 = frag_rk(arow, 0, g), k1 = frag_rk(arow, 32, g);
+          f4v gU = {}, gD = {};
+          gU = mfma(k0, bu0, gU);
+          gU = mfma(k1, bu1, gU);
+          gD = mfma(k0, bd0, gD);
+          gD = mfma(k1, bd1, gD);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float w0 = W1s[ct][r], s0 = S1s[ct][r];
+            W1s[ct][r] = fmaf(gD[r], -uD1, fmaf(An, w0, Fn * s0));
+            S1s[ct][r] = fmaf(gU[r], -uU1, En * s0);
+          }
+          m1n = max4(max4(m1n, W1s[ct]), S1s[ct]);
+        }
+      }
+      STAMP(17);
+      __syncthreads();   // every wave's H1 maximum
+
+      // H1 with the workgroup-wide scale, copied [j][u] for the scores and y
+      int eH1;
+      {
+        float mm = 0.f;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) mm = fmaxf(mm, __int_as_float(ci[INT_MH1 + i]));
+        eH1 = scale_exp(mm);
+        const float fH = pow2pos(eH1);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sH1[(16 * tt + 4 * g + r) * RW + uw + lc] = (_Float16)(H1f[tt][r] * fH);
+      }
+      STAMP(18);
+      __syncthreads();   // every wave's H1 copy
+      STAMP(19);
+
+      // ================= masked second-layer scores D o (H1 A1^T): tiles (tj, tc0 + i) =================
+      if constexpr (kRW) {
+        float pv[8], am = 0.f;
+        const float cp = pow2neg(eH1 + eA1);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          f4v acc = {};
+          const _Float16* arow = sH1 + (16 * tj + lc) * RW;
+          const _Float16* brow = sA1 + (16 * (tc0 + i) + lc) * RW;
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) acc = mfma(frag_c8(arow, 32 * kk, g), frag_c8(brow, 32 * kk, g), acc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            pv[4 * i + r] = acc[r] * cp * d_full(16 * tj + 4 * g + r, 16 * (tc0 + i) + lc);
+        }
+        am = wave_max(max8(am, pv));
+        const int edp = scale_exp(am);
+        const float fdp = pow2pos(edp);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            sSC[(16 * tj + 4 * g + r) * RS + 16 * (tc0 + i) + lc] = (_Float16)(pv[4 * i + r] * fdp);
+        if (lane == 0) ci[INT_EDP + w] = edp;
+      }
+
+      STAMP(20);
+      // ================= a4, layer 2: G2^T[c][u] = sum_j Delta2[j][c] w_j A1[j][u] =================
+      {
+        const float uD2 = pow2neg(ewD + eA1 + eD2), uU2 = pow2neg(ewU + eA1 + eD2);
+        const h8 bu0 = a1f[0] * wuf[0], bu1 = a1f[1] * wuf[1];
+        const h8 bd0 = a1f[0] * wdf[0], bd1 = a1f[1] * wdf[1];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const _Float16* arow = sD2T + (16 * ct + lc) * RS;
+          const h8 d0 = frag_rk(arow, 0, g), d1 = frag_rk(arow, 32, g);
+          f4v gU = {}, gD = {};
+          gU = mfma(d0, bu0, gU);
+          gU = mfma(d1, bu1, gU);
+          gD = mfma(d0, bd0, gD);
+          gD = mfma(d1, bd1, gD);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float w0 = W2s[ct][r], s0 = S2s[ct][r];
+            W2s[ct][r] = fmaf(gD[r], -uD2, fmaf(An, w0, Fn * s0));
+            S2s[ct][r] = fmaf(gU[r], -uU2, En * s0);
+          }
+          m2n = max4(max4(m2n, W2s[ct]), S2s[ct]);
+        }
+      }
+      STAMP(21);
+      __syncthreads();   // every wave's second-layer scores
+
+      // ================= a5 layer 2: y = diag(A) H1 W2^T + diag(F) H1 S2^T - (D o P) Delta2 =================
+      {
+        float yv[8];
+        const float cy = pow2neg(eH1 + e2);
+        const f4v av = *(const f4v*)(cf + COEF_A + 16 * tj + 4 * g);
+        const f4v fv = *(const f4v*)(cf + COEF_F + 16 * tj + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const _Float16* arow = sH1 + (16 * tj + lc) * RW;
+          const int crow = 16 * (tc0 + i) + lc;
+          f4v aw = {}, as = {};
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const h8 hf = frag_c8(arow, 32 * kk, g);
+            aw = mfma(hf, frag_c8(sW2 + crow * RW, 32 * kk, g), aw);
+            if constexpr (kRW) as = mfma(hf, frag_c8(sS2 + crow * RW, 32 * kk, g), as);
+          }
+          if constexpr (kRW) {
+            const _Float16* drow = sSC + (16 * tj + lc) * RS;
+            f4v m0 = {}, m1v = {};
+            m0 = mfma(frag_c8(drow, 0, g), frag_c8(sD2T + crow * RS, 0, g), m0);
+            m1v = mfma(frag_c8(drow, 32, g), frag_c8(sD2T + crow * RS, 32, g), m1v);
+            const float c30 = pow2neg(eD2 + ci[INT_EDP + 2 * tj]), c31 = pow2neg(eD2 + ci[INT_EDP + 2 * tj + 1]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float main = fmaf(av[r], aw[r], fv[r] * as[r]) * cy;
+              yv[4 * i + r] = fmaf(m0[r], -c30, fmaf(m1v[r], -c31, main));
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) yv[4 * i + r] = aw[r] * cy;
+          }
+        }
+        // keep my rows, send the partner its rows
+        if (keeps_y) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ypark[e * 256 + (tid & 255)] = yv[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) tstore(xY_me + par * 256 * 16, e * 256 + (tid & 255), yv[e], seq);
+        }
+      }
+      STAMP(22);
+      m1 = m1n;
+      m2 = m2n;
+      prev_row0 = tok0 + c0;
+      prev_n = n;
+      __syncthreads();   // LDS tiles are rewritten by the next chunk
+      STAMP(23);
+    }
+
+    if (failed) break;
+    // ---- write this wave's part of the final state ----
+    {
+      float* Wo = p.W_out + (int64_t)s * kP;
+      float* So = p.S_out + (int64_t)s * kP;
+      const int u = hs + lc;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int c = 16 * ct + 4 * g;
+        *(f4v*)(Wo + u * kD + c) = W1s[ct];
+        *(f4v*)(So + u * kD + c) = S1s[ct];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          Wo[kH * kD + (c + r) * kH + u] = W2s[ct][r];
+          So[kH * kD + (c + r) * kH + u] = S2s[ct][r];
+        }
+      }
+    }
+  }
+
+  // the last chunk's y rows
+  if (!failed && prev_row0 >= 0) {
+    float pyv[8];
+    load_prev_y(seq, pyv);
+    finish_prev_y(pyv);   // (rows of a wait that gave up are overwritten below)
+    __syncthreads();
+    if (ci[INT_FAIL]) failed = true;
+  }
+  if (failed) poison_pair_streams(p, pair, tid);
+  // no load into this workgroup's LDS may outlive it (a pair that gave up
+  // can leave a staging prefetch in flight)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+}  // namespace
+
+bool mlp2_supported(const Shape& s, int chunk) {
+  return s.L == 2 && s.d == kD && s.hidden == kH && s.io == TM_IO_BF16 &&
+         (s.read_mode == TM_READ_AFTER_WRITE || s.read_mode == TM_READ_CHUNK_START) && chunk >= 1 && chunk <= kB;
+}
+
+static int64_t pairs_for(const Shape& s) { return s.streams < kMaxPairs ? s.streams : kMaxPairs; }
+
+int64_t mlp2_ws_bytes(const Shape& s, int) { return pairs_for(s) * kPairBytes + 256; }
+
+int64_t mlp2_status_offset(const Shape& s) { return pairs_for(s) * kPairBytes; }
+
+#if TM_STAGE_STAMPS
+}  // namespace titans
+extern "C" int titans_mem_stage_stamps(unsigned long long* dst, int64_t count) {
+  if (count > (int64_t)titans::kStampChunks * titans::kWaves * titans::kStampStages) return TM_ERR_INVALID;
+  return hipMemcpyFromSymbol(dst, HIP_SYMBOL(titans::stage_stamps), count * sizeof(unsigned long long), 0,
+                             hipMemcpyDeviceToHost) == hipSuccess ? TM_OK : TM_ERR_HIP;
+}
+namespace titans {
+#endif
+
+hipError_t launch_mlp2(const Shape& s, int chunk, const void* k, const void* v, const void* q,
+                       const float* alpha, const float* eta, const float* theta,
+                       const float* W_in, const float* S_in, void* y, float* W_out,
+                       float* S_out, void* ws, hipStream_t stream) {
+  // the kernel's dynamic LDS size, set on every call (no state kept between
+  // calls; idempotent and cheap next to the kernel)
+  const void* kfn = s.read_mode == TM_READ_AFTER_WRITE ? (const void*)mlp2_group_kernel<true>
+                                                       : (const void*)mlp2_group_kernel<false>;
+  hipError_t e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  if (e != hipSuccess) return e;
+  int dev = 0, cus = 0;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  // every pair must be resident at once (one workgroup per CU)
+  int64_t np = pairs_for(s);
+  if (np > cus / 2) np = cus / 2;
+  if (np < 1) return hipErrorInvalidConfiguration;
+  Params p;
+  p.N = s.N;
+  p.chunk = chunk;
+  p.streams = s.streams;
+  p.n_pairs = (int)np;
+  p.k = (const __hip_bfloat16*)k;
+  p.v = (const __hip_bfloat16*)v;
+  p.q = (const __hip_bfloat16*)q;
+  p.alpha = alpha;
+  p.eta = eta;
+  p.theta = theta;
+  p.W_in = W_in;
+  p.S_in = S_in;
+  p.y = (__hip_bfloat16*)y;
+  p.W_out = W_out;
+  p.S_out = S_out;
+  unsigned char* base = (unsigned char*)ws;
+  p.xbuf = base;
+  p.status = (unsigned*)(base + mlp2_status_offset(s));
+  p.spin_max = (s.flags & TM_FLAG_NO_WAIT) ? 0u : kSpinMax;
+  p.chunk_gates = s.chunk_gates;
+  p.gstride = s.chunk_gates ? (s.N + chunk - 1) / chunk : s.N;
+  const int64_t n16 = np * kPairBytes / 16;
+  hipLaunchKernelGGL(zero_exchange_kernel, dim3((unsigned)std::min<int64_t>((n16 + 255) / 256, 1024)), dim3(256), 0,
+                     stream, (uint4*)base, n16, p.status);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (s.read_mode == TM_READ_AFTER_WRITE)
+    hipLaunchKernelGGL(mlp2_group_kernel<true>, dim3((unsigned)(2 * np)), dim3(kThreads), kLdsBytes, stream, p);
+  else
+    hipLaunchKernelGGL(mlp2_group_kernel<false>, dim3((unsigned)(2 * np)), dim3(kThreads), kLdsBytes, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace titans

@@ -1,0 +1,102 @@
+"""Per-stage timing of the 2-layer d=64 h=256 MFMA kernel from clock stamps.
+
+    python -m test_learned_neural_amd.stage_stamps --build   # compile the instrumented library (CPU)
+    python -m test_learned_neural_amd.stage_stamps           # run it on the GPU and print the table
+
+The instrumented build (-DTM_STAGE_STAMPS=1, a separate library beside the
+product one) makes the eight waves of workgroup 0 record the shader clock at
+every stage boundary of 64 chunks of its first stream.  The table gives, per
+stage, the median over those chunks of each wave's cycles, as the minimum,
+median and maximum over the waves (the maximum across waves is what the
+barrier that follows waits for).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import os
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+STAMPS_LIB = os.path.join(PKG, "libtitans_mem_stamps.so")
+STAGES = 24
+WAVES = 8
+CHUNKS = 64
+
+STAGE_NAMES = [
+    "chunk inputs from the staging area into LDS",
+    "barrier; next chunk's prefetch issued",
+    "coefficients A, E, F, D (waves 1-3)",
+    "state fragments and W2/S2 copies; Z1 = K W1^T, SiLU, SiLU'",
+    "barrier; D rows completed",
+    "A1 fragments and copy",
+    "barrier",
+    "O over the workgroup's units; partials published",
+    "flag; V loads; raw scores Q K^T and Q W1^T, Q S1^T",
+    "wait for the partner (thread 0), barrier",
+    "O sum, Delta2, last chunk's y finished",
+    "barrier",
+    "Delta2 copies, masked scores SC1, update weights",
+    "barrier",
+    "Delta1 = (Delta2 W2) * SiLU'",
+    "Zq1, H1 = SiLU",
+    "layer-1 fold into W1, S1",
+    "barrier; H1 copy",
+    "barrier",
+    "masked scores D o (H1 A1^T)",
+    "layer-2 fold into W2, S2",
+    "barrier; y tiles, kept or sent",
+    "barrier (end of chunk)",
+]
+
+
+def build():
+    sys.path.insert(0, ROOT)
+    from test_learned_neural_amd import build as b
+    b.build(verbose=True, extra=["-DTM_STAGE_STAMPS=1"], out=STAMPS_LIB, build_dir=os.path.join(ROOT, "_build", "stamps"))
+
+
+def run(steps: int = 2):
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    from test_learned_neural_amd import titans_mem as tmm
+    from test_learned_neural_amd import workloads as wl
+    if not os.path.exists(STAMPS_LIB):
+        raise SystemExit(f"{STAMPS_LIB} is missing: run with --build first")
+    tmm.LIB_PATH = STAMPS_LIB
+    lib = tmm.load()
+    cfg = wl.WORKLOADS["headline"]
+    inp = wl.make_inputs(cfg, workers=16)
+    B, H, N, d, P = cfg.B, cfg.H, cfg.N, cfg.d, cfg.param_count
+    tok = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).reshape(B, H, N, d).cuda()
+    per = lambda a, n: torch.from_numpy(a).reshape(B, H, n).cuda()
+    args = (tok(inp["k"]), tok(inp["v"]), tok(inp["q"]), per(inp["alpha"], N), per(inp["eta"], N),
+            per(inp["theta"], N), per(inp["W0"], P), per(inp["S0"], P), cfg.chunk)
+    for _ in range(steps):
+        tmm.forward(*args, hidden=cfg.hidden, n_layers=cfg.n_layers)
+    torch.cuda.synchronize()
+    n = CHUNKS * WAVES * STAGES
+    buf = (ctypes.c_ulonglong * n)()
+    fn = lib.titans_mem_stage_stamps
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+    assert fn(ctypes.addressof(buf), n) == 0
+    st = np.frombuffer(buf, dtype=np.uint64).astype(np.int64).reshape(CHUNKS, WAVES, STAGES)
+    d = np.diff(st, axis=2)                      # [chunk, wave, stage]
+    med = np.median(d, axis=0)                   # [wave, stage]
+    total = np.median(st[:, :, -1] - st[:, :, 0], axis=0)
+    print(f"{cfg.name}: cycles per stage (median over {CHUNKS} chunks; min / median / max over {WAVES} waves)")
+    for k in range(STAGES - 1):
+        row = med[:, k]
+        print(f"  {k + 1:2d} {STAGE_NAMES[k]:<58s} {row.min():7.0f} {np.median(row):7.0f} {row.max():7.0f}")
+    nxt = np.median(st[1:, :, 0] - st[:-1, :, 0], axis=0)
+    print(f"  chunk (stamp 0 to stamp 23): {np.median(total):.0f} cycles; chunk to chunk: {np.median(nxt):.0f} cycles")
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--build", action="store_true")
+    a = ap.parse_args()
+    build() if a.build else run()

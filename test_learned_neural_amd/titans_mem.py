@@ -13,18 +13,19 @@ import os
 from typing import Optional, Tuple
 
 ABI_VERSION = 1
-OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_ALIAS, ERR_HIP = 0, -1, -2, -3, -4, -5
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_ALIAS, ERR_HIP, ERR_GAVE_UP = 0, -1, -2, -3, -4, -5, -6
 IO_F32, IO_BF16 = 0, 1
 ACT_SILU = 0
 READ_AFTER_WRITE, READ_CHUNK_START = 0, 1
 FLAG_FORCE_GENERIC = 1
 FLAG_CHUNK_GATES = 2
+FLAG_NO_WAIT = 4
 PATH_GENERIC_F32, PATH_MLP2_D64_H256 = 0, 1
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtitans_mem.so")
 
 EXPORTS = ("titans_mem_abi_version", "titans_mem_param_count", "titans_mem_select_path",
-           "titans_mem_workspace_bytes", "titans_mem_forward", "titans_mem_retrieve",
+           "titans_mem_workspace_bytes", "titans_mem_forward", "titans_mem_workspace_status", "titans_mem_retrieve",
            "titans_mem_input", "titans_mem_backward", "titans_mem_backward_workspace_bytes",
            "titans_mem_status_string")
 
@@ -83,6 +84,8 @@ def load():
     lib.titans_mem_workspace_bytes.argtypes = [dp, i32]
     lib.titans_mem_forward.restype = ctypes.c_int
     lib.titans_mem_forward.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, i32, vp, fp, fp, vp, i64, vp]
+    lib.titans_mem_workspace_status.restype = ctypes.c_int
+    lib.titans_mem_workspace_status.argtypes = [dp, i32, vp, i64, vp]
     lib.titans_mem_retrieve.restype = ctypes.c_int
     lib.titans_mem_retrieve.argtypes = [dp, vp, fp, vp, vp]
     lib.titans_mem_backward_workspace_bytes.restype = i64
@@ -123,6 +126,12 @@ def raw_forward(desc: Desc, k, v, q, alpha, eta, theta, W_in, S_in, chunk, y_out
     return int(load().titans_mem_forward(ctypes.byref(desc), k, v, q, alpha, eta, theta, W_in, S_in,
                                          int(chunk), y_out, W_out, S_out, workspace,
                                          int(workspace_bytes_), stream))
+
+
+def raw_workspace_status(desc: Desc, chunk: int, workspace, workspace_bytes_, stream) -> int:
+    """titans_mem_workspace_status with an integer device address; returns the status."""
+    return int(load().titans_mem_workspace_status(ctypes.byref(desc), int(chunk), workspace,
+                                                  int(workspace_bytes_), stream))
 
 
 def backward_workspace_bytes(desc: Desc, chunk: int) -> int:
@@ -170,7 +179,7 @@ def _check(t, name, shape, dtype, device):
 
 def forward(k, v, q, alpha, eta, theta, W_in, S_in, chunk: int, *, hidden: int, n_layers: int,
             read_mode: int = READ_AFTER_WRITE, force_generic: bool = False, chunk_gates: bool = False,
-            y_out=None, W_out=None, S_out=None, workspace=None) -> Tuple:
+            y_out=None, W_out=None, S_out=None, workspace=None, flags: int = 0) -> Tuple:
     """Run titans_mem_forward on torch tensors.
 
     k, v, q: [B, H, N, d] (float32 or bfloat16); alpha, eta, theta: [B, H, N]
@@ -181,7 +190,7 @@ def forward(k, v, q, alpha, eta, theta, W_in, S_in, chunk: int, *, hidden: int, 
     B, H, N, d = k.shape
     io = "bf16" if k.dtype == torch.bfloat16 else "f32"
     desc = make_desc(B, H, N, d, hidden, n_layers, io, read_mode,
-                     (FLAG_FORCE_GENERIC if force_generic else 0) | (FLAG_CHUNK_GATES if chunk_gates else 0))
+                     (FLAG_FORCE_GENERIC if force_generic else 0) | (FLAG_CHUNK_GATES if chunk_gates else 0) | flags)
     P = param_count(desc)
     if P < 0:
         raise TitansMemError(P, "titans_mem_param_count")
@@ -215,6 +224,23 @@ def forward(k, v, q, alpha, eta, theta, W_in, S_in, chunk: int, *, hidden: int, 
     if rc != OK:
         raise TitansMemError(rc, "titans_mem_forward")
     return y_out, W_out, S_out
+
+
+def workspace_status(k, chunk: int, workspace, *, hidden: int, n_layers: int, read_mode: int = READ_AFTER_WRITE,
+                     force_generic: bool = False, chunk_gates: bool = False, flags: int = 0) -> int:
+    """Outcome of the last forward() call that used ``workspace`` (same shape
+    as ``k`` and the same options): waits for torch's current stream and
+    returns OK or ERR_GAVE_UP."""
+    torch = _torch()
+    B, H, N, d = k.shape
+    io = "bf16" if k.dtype == torch.bfloat16 else "f32"
+    desc = make_desc(B, H, N, d, hidden, n_layers, io, read_mode,
+                     (FLAG_FORCE_GENERIC if force_generic else 0) | (FLAG_CHUNK_GATES if chunk_gates else 0) | flags)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = raw_workspace_status(desc, chunk, _ptr(workspace), ws_bytes, torch.cuda.current_stream(k.device).cuda_stream)
+    if rc not in (OK, ERR_GAVE_UP):
+        raise TitansMemError(rc, "titans_mem_workspace_status")
+    return rc
 
 
 def retrieve(q, W, *, hidden: int, n_layers: int, y_out=None, force_generic: bool = False):

@@ -4,6 +4,7 @@ Every error path of titans_mem_forward / titans_mem_retrieve is detected on
 the host before anything is enqueued, so each case below passes fake
 (aligned, never dereferenced) device addresses with exactly one defect.
 """
+import ctypes
 import re
 
 import pytest
@@ -186,8 +187,30 @@ def test_retrieve_validation(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4, -5, 17):
+    for code in (0, -1, -2, -3, -4, -5, -6, 17):
         assert isinstance(tmm.status_string(code), str) and tmm.status_string(code)
+    assert tmm.status_string(tmm.ERR_GAVE_UP) != tmm.status_string(17)
+
+
+def test_workspace_status_argument_errors(lib):
+    """titans_mem_workspace_status checks its arguments on the host before
+    touching the device: a bad descriptor, a missing, short or misaligned
+    workspace for the MFMA path."""
+    f = lib.titans_mem_workspace_status
+    d3 = tmm.make_desc(8, 16, 16384, 64, 256, 2, "bf16")
+    need = tmm.workspace_bytes(d3, 64)
+    assert need > 0
+    bad = tmm.make_desc(8, 16, 16384, 64, 256, 2, "bf16")
+    bad.abi_version = 2
+    assert f(ctypes.byref(bad), 64, BASE, need, 0) == tmm.ERR_INVALID
+    assert f(ctypes.byref(d3), 0, BASE, need, 0) == tmm.ERR_INVALID
+    assert f(ctypes.byref(d3), 64, 0, need, 0) == tmm.ERR_WORKSPACE
+    assert f(ctypes.byref(d3), 64, BASE, need - 1, 0) == tmm.ERR_WORKSPACE
+    assert f(ctypes.byref(d3), 64, BASE + 8, need, 0) == tmm.ERR_INVALID
+    # the no-wait test hook is a valid flag; other unknown bits are not
+    nw = tmm.make_desc(8, 16, 16384, 64, 256, 2, "bf16", flags=tmm.FLAG_NO_WAIT)
+    assert tmm.select_path(nw, 64) == tmm.PATH_MLP2_D64_H256
+    assert tmm.select_path(tmm.make_desc(8, 16, 16384, 64, 256, 2, "bf16", flags=8), 64) == tmm.ERR_INVALID
 
 
 # ----------------------------------------------------------------------------
