@@ -8,8 +8,9 @@ import numpy as np
 import pytest
 
 from test_learned_neural_amd import workloads as wl
-from parity_util import (TOL, chunk_gate_inputs, prefix_inputs, rel_err, run_gpu, run_oracle, state_below_floor,
-                         stream_errors, to_device, window_errors, y_errors, y_to_f64)
+from parity_util import (TOL, chunk_gate_inputs, live_lengths, prefix_inputs, rel_err, run_gpu, run_oracle,
+                         state_below_floor, state_row_errors, stream_errors, to_device, window_errors, y_errors,
+                         y_row_errors, y_to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -21,17 +22,24 @@ def gpu():
     return torch
 
 
-def _check(cfg, inp, out, ref, tol, idx=None, windows=True):
+def _check(cfg, inp, out, ref, tol, idx=None, windows=True, label=""):
     """y is held to its io dtype's bar (bf16 output rounding alone is ~2e-3);
-    W and S, fp32 end to end on this path, to ``tol``."""
+    W and S, fp32 end to end on this path, to ``tol``: norm-wise per stream,
+    y per window and per token, W and S per row and column of every layer."""
     y, W, S = out
     tol_y = max(tol, TOL[cfg.io])
     yg = y_to_f64(cfg, y)
     Wg = W.reshape(-1, cfg.param_count).cpu().double().numpy()
     Sg = S.reshape(-1, cfg.param_count).cpu().double().numpy()
-    e = stream_errors(cfg, inp, yg, Wg, Sg, *ref, idx=idx)
-    print(f"{cfg.name}: max e_y {e[:, 0].max():.2e} e_W {e[:, 1].max():.2e} e_S {e[:, 2].max():.2e}", flush=True)
+    e = stream_errors(cfg, inp, yg, Wg, Sg, *ref[:3], idx=idx)
+    ry, at_y = y_row_errors(cfg, inp, yg, ref[0], idx=idx)
+    rW, at_W = state_row_errors(cfg, inp, Wg, ref[1], idx=idx)
+    rS, at_S = state_row_errors(cfg, inp, Sg, ref[2], idx=idx)
+    print(f"{label or cfg.name}: max e_y {e[:, 0].max():.2e} e_W {e[:, 1].max():.2e} e_S {e[:, 2].max():.2e} | "
+          f"per token y {ry:.2e} at {at_y}, per row W {rW:.2e} at {at_W}, S {rS:.2e} at {at_S}", flush=True)
     assert np.all(e[:, 0] < tol_y) and np.all(e[:, 1:] < tol), e.max(axis=0)
+    assert ry < tol_y, (ry, at_y)
+    assert rW < tol and rS < tol, (rW, at_W, rS, at_S)   # fp32 end to end: at every length
     if windows:
         we = window_errors(cfg, inp, yg, ref[0], idx=idx)
         assert we < tol_y, we
@@ -64,11 +72,17 @@ def test_generic_shapes_and_ragged_chunks(L, d, h, N, chunk, io):
 
 def test_deep_memory_full_length():
     """The deep-memory workload (4-layer MLP, d = 128, hidden 512, 4 x 8
-    streams, 32768 tokens, chunk 128) at full size on the path that serves it.
-    The first 2048 tokens of every stream are checked against the oracle's
-    run on that prefix (prefix inputs are drawn bit-identically; outputs are
-    causal); by the end the fp64 state has decayed into the exactly-zero
-    fixed point, so the final W and S must be below the error floor."""
+    streams, 32768 tokens, chunk 128) at full size on the path that serves it
+    (prefix inputs are drawn bit-identically and outputs are causal, so an
+    oracle run over a prefix is the reference for it):
+
+    * every stream over the first 4096 tokens, y per token and window, with
+      each stream's live length (it must end inside that prefix);
+    * four sampled streams over the first 8192 tokens, y per token (the
+      window past the live length, where the reference is tiny but not zero);
+    * past each stream's live length, to the end: every output row below the
+      y floor, and the final W and S below the state floor.
+    """
     import torch
     from test_learned_neural_amd import titans_mem as tmm
     cfg = wl.WORKLOADS["deep"]
@@ -78,18 +92,38 @@ def test_deep_memory_full_length():
     y, W, S = run_gpu(cfg, to_device(cfg, inp))
     torch.cuda.synchronize()
     assert bool(torch.isfinite(y).all()) and bool(torch.isfinite(W).all()) and bool(torch.isfinite(S).all())
-    n_pre = 2048
+    n_pre = 4096
     pre = cfg.with_(N=n_pre)
     sub = prefix_inputs(inp, n_pre)
-    y_ref = run_oracle(pre, sub, threads=16)[0]
+    y_ref, _, _, wn = run_oracle(pre, sub, threads=16, want_w_norm=True)
+    live = live_lengths(pre, sub, wn)
+    assert max(live) < n_pre, live
     yg = y_to_f64(pre, y[:, :, :n_pre].contiguous())
     ey = y_errors(pre, sub, yg, y_ref)
     we = window_errors(pre, sub, yg, y_ref)
+    ry, at = y_row_errors(pre, sub, yg, y_ref)
+    print(f"{cfg.name}: prefix {n_pre} max e_y {ey.max():.2e} window_y {we:.2e} per token {ry:.2e} at {at}; "
+          f"live length min {min(live)} max {max(live)}", flush=True)
+    assert np.all(ey < TOL["bf16"]) and we < TOL["bf16"] and ry < TOL["bf16"], (ey.max(), we, ry, at)
+    n_pre2 = 8192
+    picks = [0, 11, 22, 31]
+    pre2 = cfg.with_(N=n_pre2)
+    sub2 = {k: (np.ascontiguousarray(a[picks, :n_pre2]) if a.ndim >= 2 and a.shape[1] == cfg.N else
+                np.ascontiguousarray(a[picks])) for k, a in inp.items()}
+    y_ref2 = run_oracle(pre2, sub2, threads=4)[0]
+    yg2 = y_to_f64(pre2, y[:, :, :n_pre2].contiguous())
+    ry2, at2 = y_row_errors(pre2, sub2, yg2, y_ref2, idx=picks)
+    print(f"{cfg.name}: streams {picks} prefix {n_pre2} per token y {ry2:.2e} at {at2}", flush=True)
+    assert ry2 < TOL["bf16"], (ry2, at2)
+    worst = 0.0
+    yall = y_to_f64(cfg, y)
+    for s in range(cfg.streams):
+        floor = 1e-30 * max(1.0, float(np.linalg.norm(wl.io_to_f64(inp["v"][s], "bf16"))))
+        worst = max(worst, float(np.max(np.linalg.norm(yall[s, live[s]:], axis=-1))) / floor)
     ok, es = state_below_floor(cfg, inp, W.reshape(-1, cfg.param_count).cpu().double().numpy(),
                                S.reshape(-1, cfg.param_count).cpu().double().numpy(), TOL["f32"])
-    print(f"{cfg.name}: prefix {n_pre} max e_y {ey.max():.2e} window_y {we:.2e}; final state vs zero {es:.2e}",
-          flush=True)
-    assert np.all(ey < TOL["bf16"]) and we < TOL["bf16"]
+    print(f"{cfg.name}: past the live length max ||y_t|| / floor {worst:.2e}; final state vs zero {es:.2e}", flush=True)
+    assert worst < TOL["bf16"], worst
     assert ok, es
 
 
@@ -274,3 +308,75 @@ def test_linear_memory_kernel(d, N, chunk, read_mode, io):
                          S_out=Si)
     torch.cuda.synchronize()
     assert torch.equal(y2, out[0]) and torch.equal(W2, out[1]) and torch.equal(S2, out[2])
+
+
+def _edge_gates(inp, case):
+    out = dict(inp)
+    if "eta0" in case:
+        out["eta"] = np.zeros_like(inp["eta"])
+    if "alpha1" in case:
+        out["alpha"] = np.ones_like(inp["alpha"])
+    return out
+
+
+@pytest.mark.parametrize("case", ["eta0", "alpha1", "eta0_alpha1"])
+@pytest.mark.parametrize("wname,BH,N,chunk", [("mlp2_short", (1, 3), 150, 64), ("linear", (1, 2), 200, 16),
+                                              ("deep", (1, 2), 140, 128)])
+def test_generic_gate_edges_against_oracle(case, wname, BH, N, chunk):
+    """eta = 0 and alpha = 1 on the generic path (and the linear-memory
+    kernel), where the coefficient recurrences must be exact, against the
+    oracle on y, W and S."""
+    cfg = wl.WORKLOADS[wname].with_(B=BH[0], H=BH[1], N=N, chunk=chunk)
+    inp = _edge_gates(wl.make_inputs(cfg), case)
+    out = run_gpu(cfg, to_device(cfg, inp), force_generic=True)
+    _check(cfg, inp, out, run_oracle(cfg, inp), TOL["f32"], label=f"{cfg.name} {case}")
+
+
+@pytest.mark.parametrize("N,chunk", [(64, 64), (300, 300), (45, 64)])
+def test_generic_causal_linear_attention(N, chunk):
+    """The linear memory with W_0 = S_0 = 0, alpha = eta = 0 and the whole
+    sequence in one chunk is causal linear attention,
+    y_t = sum_{i<=t} theta_i (k_i . q_t) v_i ("Titans", mer.dev notes,
+    section 2.1: linear attention as a memory written with each key-value
+    pair), computed here in fp64 from that formula.  Chunks up to 64 run on
+    the linear-memory kernel, 300 on the generic kernel."""
+    cfg = wl.WORKLOADS["linear"].with_(B=1, H=3, N=N, chunk=chunk)
+    inp = wl.make_inputs(cfg)
+    inp["alpha"][:] = 0.0
+    inp["eta"][:] = 0.0
+    assert not inp["W0"].any() and not inp["S0"].any()
+    out = run_gpu(cfg, to_device(cfg, inp), force_generic=True)
+    f = wl.inputs_f64(cfg, inp)
+    ref = np.stack([np.tril(f["q"][s] @ f["k"][s].T) * f["theta"][s][None, :] @ f["v"][s] for s in range(cfg.streams)])
+    yg = y_to_f64(cfg, out[0])
+    ry, at = y_row_errors(cfg, inp, yg, ref)
+    print(f"causal linear attention N={N} chunk={chunk}: per token y {ry:.2e} at {at}", flush=True)
+    assert ry < TOL["f32"], (ry, at)
+    _check(cfg, inp, out, run_oracle(cfg, inp), TOL["f32"], label="causal linear attention")
+
+
+def test_generic_kernelised_linear_attention():
+    """The 2-layer memory with W2_0 = 0, S_0 = 0, alpha = eta = 0 and one
+    chunk on the generic path: y_t = sum_{i<=t} theta_i (phi(k_i) . phi(q_t))
+    v_i with phi(x) = SiLU(W1_0 x), and W1 returned bitwise unchanged."""
+    import torch
+    cfg = wl.WORKLOADS["headline"].with_(B=1, H=2, N=100, chunk=128, io="f32")
+    inp = wl.make_inputs(cfg)
+    P1 = cfg.hidden * cfg.d
+    inp["W0"][:, P1:] = 0.0
+    inp["alpha"][:] = 0.0
+    inp["eta"][:] = 0.0
+    dev = to_device(cfg, inp)
+    y, W, S = run_gpu(cfg, dev, force_generic=True)
+    torch.cuda.synchronize()
+    f = wl.inputs_f64(cfg, inp)
+    refs = []
+    for s in range(cfg.streams):
+        W1 = f["W0"][s, :P1].reshape(cfg.hidden, cfg.d)
+        zk, zq = f["k"][s] @ W1.T, f["q"][s] @ W1.T
+        pk, pq = zk / (1 + np.exp(-zk)), zq / (1 + np.exp(-zq))
+        refs.append((np.tril(pq @ pk.T) * f["theta"][s][None, :]) @ f["v"][s])
+    ry, at = y_row_errors(cfg, inp, y_to_f64(cfg, y), np.stack(refs))
+    print(f"generic kernelised linear attention: per token y {ry:.2e} at {at}", flush=True)
+    assert ry < TOL["f32"], (ry, at)
+    assert torch.equal(W[..., :P1], dev["W0"][..., :P1]) and not S[..., :P1].any()
