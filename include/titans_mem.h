@@ -173,6 +173,36 @@ int titans_mem_forward(const titans_mem_desc* desc,
                        void* stream);
 
 /*
+ * titans_mem_forward_noalloc -- titans_mem_forward for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).
+ *
+ * Same arguments, results and asynchrony as titans_mem_forward without the
+ * workspace, for the shapes of the MFMA path (TM_PATH_MLP2_D64_H256:
+ * 2-layer, d = 64, hidden = 256, bf16 io, chunk <= 64; any B*H, N and read
+ * mode); TM_ERR_UNSUPPORTED for every other shape.  Its scratch (the
+ * paired workgroups' tagged exchange words and the status word) is a
+ * library-owned device array of 25,166,080 bytes (24 MiB + 256: enough for
+ * the kernel's largest grid of 128 workgroup pairs; TM_ERR_WORKSPACE if a
+ * shape ever needed more), one per GPU,
+ * allocated with the library's code and held until the process ends.  The
+ * call allocates nothing: it enqueues a small fill kernel and the memory
+ * kernel on `stream`.  The first call on a device looks up the array's
+ * address there.  All calls on one GPU share the array: calls that follow
+ * one another on a stream are independent, calls that overlap in time on one
+ * GPU (other streams, other threads) race and must not be issued.
+ * titans_mem_workspace_status with workspace NULL reports on the last such
+ * call on the current device.
+ */
+int titans_mem_forward_noalloc(const titans_mem_desc* desc,
+                               const void* k, const void* v, const void* q,
+                               const float* alpha, const float* eta, const float* theta,
+                               const float* W_in, const float* S_in,
+                               int32_t chunk,
+                               void* y_out, float* W_out, float* S_out,
+                               void* stream);
+
+/*
  * titans_mem_workspace_status -- outcome of the last titans_mem_forward call
  * that used `workspace` (same desc and chunk).  Waits for `stream` to drain
  * (hipStreamSynchronize) and reads the status word the MFMA kernel keeps in
@@ -182,7 +212,8 @@ int titans_mem_forward(const titans_mem_desc* desc,
  * workgroups of the MFMA kernel gave up waiting for each other (its outputs
  * hold NaN), an argument error (-1..-3) like titans_mem_forward's, or
  * TM_ERR_HIP when the copy or the synchronisation fails.  Paths without
- * cross-workgroup waits always report TM_OK (workspace may then be NULL).
+ * cross-workgroup waits always report TM_OK.  workspace NULL stands for the
+ * scratch of titans_mem_forward_noalloc on the current device.
  */
 int titans_mem_workspace_status(const titans_mem_desc* desc, int32_t chunk,
                                 const void* workspace, int64_t workspace_bytes,

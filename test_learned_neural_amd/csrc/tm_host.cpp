@@ -103,7 +103,7 @@ int64_t titans_mem_workspace_bytes(const titans_mem_desc* desc, int32_t chunk) {
 
 namespace {
 
-// Validation of a forward call:
+// Validation shared by titans_mem_forward and titans_mem_forward_noalloc:
 // pointers, path, workspace size (has_ws: the caller passes one) and
 // aliasing, all on the host.  Fills s and path.
 int check_forward(const titans_mem_desc* desc, const void* k, const void* v, const void* q, const float* alpha,
@@ -183,6 +183,24 @@ int titans_mem_forward(const titans_mem_desc* desc, const void* k, const void* v
   return err == hipSuccess ? TM_OK : TM_ERR_HIP;
 }
 
+int titans_mem_forward_noalloc(const titans_mem_desc* desc, const void* k, const void* v, const void* q,
+                               const float* alpha, const float* eta, const float* theta, const float* W_in,
+                               const float* S_in, int32_t chunk, void* y_out, float* W_out, float* S_out,
+                               void* stream) {
+  Shape s;
+  int path = 0;
+  int rc = check_forward(desc, k, v, q, alpha, eta, theta, W_in, S_in, chunk, y_out, W_out, S_out, nullptr, 0,
+                         false, &s, &path);
+  if (rc) return rc;
+  if (path != TM_PATH_MLP2_D64_H256) return TM_ERR_UNSUPPORTED;
+  if (titans::mlp2_ws_bytes(s, chunk) > titans::mlp2_scratch_bytes()) return TM_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  if (titans::mlp2_scratch(&scratch, true) != hipSuccess || !scratch) return TM_ERR_HIP;
+  hipError_t err = titans::launch_mlp2(s, chunk, k, v, q, alpha, eta, theta, W_in, S_in, y_out, W_out, S_out,
+                                       scratch, (hipStream_t)stream);
+  return err == hipSuccess ? TM_OK : TM_ERR_HIP;
+}
+
 int titans_mem_workspace_status(const titans_mem_desc* desc, int32_t chunk, const void* workspace,
                                 int64_t workspace_bytes, void* stream) {
   Shape s;
@@ -194,8 +212,16 @@ int titans_mem_workspace_status(const titans_mem_desc* desc, int32_t chunk, cons
   if (path != TM_PATH_MLP2_D64_H256)
     return hipStreamSynchronize(st) == hipSuccess ? TM_OK : TM_ERR_HIP;
   if (workspace && !aligned16(workspace)) return TM_ERR_INVALID;
+  if (!workspace) {
+    // the allocation-free variant's scratch on this device (never used: nothing to report)
+    void* scratch = nullptr;
+    if (titans::mlp2_scratch(&scratch, false) != hipSuccess) return TM_ERR_HIP;
+    if (!scratch) return hipStreamSynchronize(st) == hipSuccess ? TM_OK : TM_ERR_HIP;
+    workspace = scratch;
+    workspace_bytes = titans::mlp2_scratch_bytes();
+  }
   const int64_t need = workspace_for(s, path, chunk);
-  if (!workspace || workspace_bytes < need) return TM_ERR_WORKSPACE;
+  if (workspace_bytes < need) return TM_ERR_WORKSPACE;
   unsigned word = 0;
   if (hipMemcpyAsync(&word, (const char*)workspace + titans::mlp2_status_offset(s), sizeof(word),
                      hipMemcpyDeviceToHost, st) != hipSuccess ||

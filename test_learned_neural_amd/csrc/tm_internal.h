@@ -70,7 +70,12 @@ bool mlp2_supported(const Shape& s, int chunk);
 int64_t mlp2_ws_bytes(const Shape& s, int chunk);
 // byte offset of the kernel's status word in its workspace (1 = a pair gave up)
 int64_t mlp2_status_offset(const Shape& s);
-
+// The allocation-free variant's scratch: a file-scope device array of
+// mlp2_scratch_bytes() bytes in tm_mlp2_group.hip.  mlp2_scratch gives its device
+// address on the current device, looked up there on the first call with
+// lookup = true (nullptr while it never was).
+int64_t mlp2_scratch_bytes();
+hipError_t mlp2_scratch(void** out, bool lookup);
 hipError_t launch_mlp2(const Shape& s, int chunk, const void* k, const void* v, const void* q,
                        const float* alpha, const float* eta, const float* theta,
                        const float* W_in, const float* S_in, void* y, float* W_out,

@@ -1193,6 +1193,42 @@ int64_t mlp2_ws_bytes(const Shape& s, int) { return pairs_for(s) * kPairBytes + 
 
 int64_t mlp2_status_offset(const Shape& s) { return pairs_for(s) * kPairBytes; }
 
+// ---- scratch of titans_mem_forward_noalloc ----
+// The kernel's workspace (exchange buffers and status word) for the
+// largest pair count, as a file-scope device array: one copy per GPU,
+// allocated when the library's code object is loaded on that device and
+// held until the process ends.  Host code must not use the array's name as
+// an address: its device address is looked up once per device with
+// hipGetSymbolAddress and kept below.  Every call on one GPU shares the
+// array; every call clears the exchange buffers and the status word with a
+// fill kernel (no memset) before the memory kernel, so calls that follow one
+// another are independent, while calls that overlap on one GPU race.
+constexpr int64_t kScratchBytes = kMaxPairs * kPairBytes + 256;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];   // per device: the device address of `scratch`, once looked up
+}  // namespace
+
+int64_t mlp2_scratch_bytes() { return kScratchBytes; }
+
+hipError_t mlp2_scratch(void** out, bool lookup) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev] && lookup) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 #if TM_STAGE_STAMPS
 }  // namespace titans
 extern "C" int titans_mem_stage_stamps(unsigned long long* dst, int64_t count) {

@@ -25,7 +25,8 @@ PATH_GENERIC_F32, PATH_MLP2_D64_H256 = 0, 1
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtitans_mem.so")
 
 EXPORTS = ("titans_mem_abi_version", "titans_mem_param_count", "titans_mem_select_path",
-           "titans_mem_workspace_bytes", "titans_mem_forward", "titans_mem_workspace_status", "titans_mem_retrieve",
+           "titans_mem_workspace_bytes", "titans_mem_forward", "titans_mem_forward_noalloc",
+           "titans_mem_workspace_status", "titans_mem_retrieve",
            "titans_mem_input", "titans_mem_backward", "titans_mem_backward_workspace_bytes",
            "titans_mem_status_string")
 
@@ -84,6 +85,8 @@ def load():
     lib.titans_mem_workspace_bytes.argtypes = [dp, i32]
     lib.titans_mem_forward.restype = ctypes.c_int
     lib.titans_mem_forward.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, i32, vp, fp, fp, vp, i64, vp]
+    lib.titans_mem_forward_noalloc.restype = ctypes.c_int
+    lib.titans_mem_forward_noalloc.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, i32, vp, fp, fp, vp]
     lib.titans_mem_workspace_status.restype = ctypes.c_int
     lib.titans_mem_workspace_status.argtypes = [dp, i32, vp, i64, vp]
     lib.titans_mem_retrieve.restype = ctypes.c_int
@@ -126,6 +129,13 @@ def raw_forward(desc: Desc, k, v, q, alpha, eta, theta, W_in, S_in, chunk, y_out
     return int(load().titans_mem_forward(ctypes.byref(desc), k, v, q, alpha, eta, theta, W_in, S_in,
                                          int(chunk), y_out, W_out, S_out, workspace,
                                          int(workspace_bytes_), stream))
+
+
+def raw_forward_noalloc(desc: Desc, k, v, q, alpha, eta, theta, W_in, S_in, chunk, y_out, W_out, S_out,
+                        stream) -> int:
+    """titans_mem_forward_noalloc with integer device addresses; returns the status."""
+    return int(load().titans_mem_forward_noalloc(ctypes.byref(desc), k, v, q, alpha, eta, theta, W_in, S_in,
+                                                 int(chunk), y_out, W_out, S_out, stream))
 
 
 def raw_workspace_status(desc: Desc, chunk: int, workspace, workspace_bytes_, stream) -> int:

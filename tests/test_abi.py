@@ -204,13 +204,35 @@ def test_workspace_status_argument_errors(lib):
     bad.abi_version = 2
     assert f(ctypes.byref(bad), 64, BASE, need, 0) == tmm.ERR_INVALID
     assert f(ctypes.byref(d3), 0, BASE, need, 0) == tmm.ERR_INVALID
-    assert f(ctypes.byref(d3), 64, 0, need, 0) == tmm.ERR_WORKSPACE
     assert f(ctypes.byref(d3), 64, BASE, need - 1, 0) == tmm.ERR_WORKSPACE
     assert f(ctypes.byref(d3), 64, BASE + 8, need, 0) == tmm.ERR_INVALID
     # the no-wait test hook is a valid flag; other unknown bits are not
     nw = tmm.make_desc(8, 16, 16384, 64, 256, 2, "bf16", flags=tmm.FLAG_NO_WAIT)
     assert tmm.select_path(nw, 64) == tmm.PATH_MLP2_D64_H256
     assert tmm.select_path(tmm.make_desc(8, 16, 16384, 64, 256, 2, "bf16", flags=8), 64) == tmm.ERR_INVALID
+
+
+def test_forward_noalloc_argument_errors(lib):
+    """The allocation-free forward validates like titans_mem_forward (on
+    the host, nothing enqueued) and serves only the MFMA path's shapes."""
+    f = lib.titans_mem_forward_noalloc
+    d3 = tmm.make_desc(2, 2, 128, 64, 256, 2, "bf16")
+    tok, gate, state = 2 * 2 * 128 * 64 * 2, 2 * 2 * 128 * 4, 2 * 2 * 32768 * 4
+    ptrs = []
+    cur = BASE
+    for n in (tok, tok, tok, gate, gate, gate, state, state, tok, state, state):
+        ptrs.append(cur)
+        cur += (n + 4095) // 4096 * 4096
+    k, v, q, a, e, t, Wi, Si, y, Wo, So = ptrs
+    call = lambda desc, chunk=64, **kw: f(ctypes.byref(desc), kw.get("k", k), v, q, a, e, t, Wi, Si, chunk, y,
+                                          kw.get("Wo", Wo), So, 0)
+    assert call(d3, chunk=0) == tmm.ERR_INVALID
+    assert call(d3, k=0) == tmm.ERR_INVALID
+    assert call(d3, k=k + 8) == tmm.ERR_INVALID
+    assert call(d3, Wo=Si) == tmm.ERR_ALIAS
+    assert call(tmm.make_desc(2, 2, 128, 64, 256, 2, "bf16"), chunk=65) == tmm.ERR_UNSUPPORTED
+    assert call(tmm.make_desc(2, 2, 128, 64, 256, 2, "bf16", flags=tmm.FLAG_FORCE_GENERIC)) == tmm.ERR_UNSUPPORTED
+    assert call(tmm.make_desc(2, 2, 128, 64, 0, 1, "f32")) in (tmm.ERR_UNSUPPORTED, tmm.ERR_ALIAS)
 
 
 # ----------------------------------------------------------------------------
