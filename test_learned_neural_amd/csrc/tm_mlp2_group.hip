@@ -121,10 +121,15 @@ static_assert(8 * 256 * 4 <= kT64, "the parked y tiles fit the Delta2 area");
 // int slots
 constexpr int INT_AMAX_D2 = 0, INT_EWU = 1, INT_EWD = 2, INT_FAIL = 3, INT_T22 = 4;
 constexpr int INT_M2 = 8;     // per-wave maxima of |W2|, |S2| (8 slots)
-constexpr int INT_MA1 = 16;   // per-wave maxima of |A1|
+// (the state's slots M1, M2, N1 are written by the fold of the previous
+// chunk, or at the stream's start, and read after the next chunk's first
+// barrier: no per-lane value is carried across the chunk boundary)
+constexpr int INT_N1 = 16;    // per-wave maxima of |W1| (a bound on the A1 scale)
 constexpr int INT_MH1 = 24;   // per-wave maxima of |H1|
 constexpr int INT_ESC = 32;   // per-wave exponents of the first-layer masked scores
 constexpr int INT_EDP = 40;   // per-wave exponents of the second-layer masked scores
+constexpr int INT_NK = 48;    // per-wave maxima of |K|
+constexpr int INT_M1 = 56;    // per-wave maxima of |W1|, |S1| (each wave's own operand scale)
 
 // ---- global workspace layout, per pair (bytes) ----
 // Exchange words are 8 bytes: a float and the sequence number of the chunk
@@ -224,13 +229,18 @@ __device__ __forceinline__ float lane_value(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
 
-// maximum over the wave, returned uniformly
+// maximum over the wave, returned uniformly: the rows of 16 lanes reduce
+// among themselves, then rows 1 and 3 take in rows 0 and 2 (row_bcast:15)
+// and rows 2 and 3 take in the maximum of rows 0 and 1 (row_bcast:31), so
+// lane 63 ends with the wave's maximum (one lane read instead of four)
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_mov<0xB1>(v));
   v = fmaxf(v, dpp_mov<0x4E>(v));
   v = fmaxf(v, dpp_mov<0x141>(v));
   v = fmaxf(v, dpp_mov<0x140>(v));   // every lane of a row of 16 holds the row's maximum
-  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
+  v = fmaxf(v, dpp_or<0x142, 0xa>(v, v));
+  v = fmaxf(v, dpp_or<0x143, 0xc>(v, v));
+  return lane_value(v, 63);
 }
 
 // inclusive prefix product over the lanes (lane l: x_0 * ... * x_l)
@@ -477,6 +487,24 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
       d = fmaf(cf[COEF_T11 + j - 32], sDM[31 * RF + i], fmaf(cf[COEF_T12 + j - 32], cf[COEF_XT + i], d));
     return d;
   };
+  // D over the 16x16 tile of row block tr and column block tb: lane (g, lc)
+  // gets rows 16 tr + 4g + r of column 16 tb + lc.  The part carried over
+  // from row 31 (d_full) concerns only the tiles below row 32 and left of
+  // column 32, a condition uniform over the wave.
+  auto d_tile = [&](int tr, int tb) {
+    const int col = 16 * tb + lc;
+    f4v d;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) d[r] = sDM[(16 * tr + 4 * g + r) * RF + col];
+    if (tr >= 2 && tb < 2) {
+      const float d31 = sDM[31 * RF + col], xt = cf[COEF_XT + col];
+      const f4v t11 = *(const f4v*)(cf + COEF_T11 + 16 * tr + 4 * g - 32);
+      const f4v t12 = *(const f4v*)(cf + COEF_T12 + 16 * tr + 4 * g - 32);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) d[r] = fmaf(t11[r], d31, fmaf(t12[r], xt, d[r]));
+    }
+    return d;
+  };
   auto relane = [&] {
     int t = tid0;
     asm volatile("" : "+v"(t));
@@ -565,8 +593,9 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
     // W1s[ct]: rows c = 16 ct + 4g + r, lanes u = hs + lc   (W1[u][c])
     // W2s[ct]: rows c = 16 ct + 4g + r, lanes u = hs + lc   (W2[c][u])
     f4v W1s[4], S1s[4], W2s[4], S2s[4];
-    float m1 = 0.f, m2 = 0.f;   // this lane's max |W|,|S| per layer (for the operand scales)
     {
+      float m1 = 0.f, m2 = 0.f;   // this lane's max |W|,|S| per layer (for the operand scales)
+      float n1 = 0.f;             // this lane's max |W1| (a bound on the A1 scale)
       const float* Wi = p.W_in + (int64_t)s * kP;
       const float* Si = p.S_in + (int64_t)s * kP;
       const int u = hs + lc;
@@ -576,12 +605,19 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
         W1s[ct] = *(const f4v*)(Wi + u * kD + c);
         S1s[ct] = *(const f4v*)(Si + u * kD + c);
         m1 = max4(max4(m1, W1s[ct]), S1s[ct]);
+        n1 = max4(n1, W1s[ct]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           W2s[ct][r] = Wi[kH * kD + (c + r) * kH + u];
           S2s[ct][r] = Si[kH * kD + (c + r) * kH + u];
         }
         m2 = max4(max4(m2, W2s[ct]), S2s[ct]);
+      }
+      const float wm1 = wave_max(m1), wm2 = wave_max(m2), wn1 = wave_max(n1);
+      if (lane == 0) {
+        ci[INT_M1 + w] = __float_as_int(wm1);
+        ci[INT_M2 + w] = __float_as_int(wm2);
+        ci[INT_N1 + w] = __float_as_int(wn1);
       }
     }
 
@@ -616,8 +652,11 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
           ci[INT_AMAX_D2] = 0;
           ci[INT_FAIL] = 0;
         }
-        const float wm2 = wave_max(m2);
-        if (lane == 0) ci[INT_M2 + w] = __float_as_int(wm2);
+        float kn = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kn = fmaxf(kn, fabsf((float)kv[i]));
+        const float wnk = wave_max(kn);
+        if (lane == 0) ci[INT_NK + w] = __float_as_int(wnk);
       }
       STAMP(1);
       __syncthreads();
@@ -643,7 +682,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
         for (int i = 0; i < kWaves; ++i) mm = fmaxf(mm, __int_as_float(ci[INT_M2 + i]));
         e2 = scale_exp(mm);
       }
-      const int e1 = scale_exp(wave_max(m1));
+      const int e1 = scale_exp(__int_as_float(ci[INT_M1 + w]));
       const float f1 = pow2pos(e1), f2 = pow2pos(e2);
       // state operand fragments (register order over d: K-step s covers c = 32 s ..)
       h8 w1f[2], s1f[2], w2f[2];
@@ -664,11 +703,37 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
         }
 
       // ================= a2: key-side forward Z1 = K W1^T (rows j, lanes u) =================
-      // A1 = SiLU(Z1) and SiLU'(Z1) (fp16, for the backprop)
-      f4v A1f[4];
+      // A1 = SiLU(Z1) and SiLU'(Z1) (fp16, for the backprop).  A1's
+      // workgroup-wide operand scale comes from a bound known before the
+      // product, so the A1 copy needs no barrier of its own: a sum of 64
+      // products gives |Z1[j][u]| <= 64 max|K| max|W1|, and
+      // |SiLU(z)| = |z| sigmoid(z) <= |z|.  (Maxima of magnitudes, unlike
+      // sums of squares, do not underflow while the state decays.)  The bound
+      // may exceed the true maximum by a few binades, which leaves the fp16
+      // values normal and rounded exactly as with the exact maximum
+      // (power-of-two scaling); a factor 1.001 on the bound covers the fp16
+      // rounding of W1.
+      int eA1;
+      h8 a1f[2];
       h4 SPh[4];
       {
-        float am = 0.f;
+        float mn1 = 0.f, mnk = 0.f;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) {
+          mn1 = fmaxf(mn1, __int_as_float(ci[INT_N1 + i]));
+          mnk = fmaxf(mnk, __int_as_float(ci[INT_NK + i]));
+        }
+        // 2^-eA1 bounds 64.0641 max|K| max|W1| below 2^14, from the
+        // exponents alone (no product that could overflow or underflow)
+        eA1 = 0;
+        if (mn1 > 0.f && mn1 < INFINITY && mnk > 0.f && mnk < INFINITY) {
+          int ea, eb;
+          (void)frexpf(mn1, &ea);
+          (void)frexpf(mnk, &eb);
+          eA1 = 7 - ea - eb;
+        }
+        const float fA1 = pow2pos(eA1);
+        f4v A1f[4];
         const float zun = pow2neg(e1);
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
@@ -684,24 +749,9 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
             A1f[tt][r] = a;
             SPh[tt][r] = (_Float16)(sg + a * (1.f - sg));   // s (1 + z (1 - s))
           }
-          am = max4(am, A1f[tt]);
         }
-        const float wam = wave_max(am);
-        if (lane == 0) ci[INT_MA1 + w] = __float_as_int(wam);
-      }
-      STAMP(4);
-      __syncthreads();   // every wave's A1 maximum and W2/S2 copies
-      STAMP(5);
-      // A1 with the workgroup-wide scale: fragments (register order over the
-      // tokens) for the second-layer fold, and the copy [j][u] for O and the scores
-      int eA1;
-      h8 a1f[2];
-      {
-        float mm = 0.f;
-#pragma unroll
-        for (int i = 0; i < kWaves; ++i) mm = fmaxf(mm, __int_as_float(ci[INT_MA1 + i]));
-        eA1 = scale_exp(mm);
-        const float fA1 = pow2pos(eA1);
+        // A1 fragments (register order over the tokens) for the second-layer
+        // fold, and the copy [j][u] for O and the scores
 #pragma unroll
         for (int st = 0; st < 2; ++st) a1f[st] = tiles_frag(A1f[2 * st], A1f[2 * st + 1], fA1);
 #pragma unroll
@@ -709,8 +759,10 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) sA1[(16 * tt + 4 * g + r) * RW + uw + lc] = a1f[tt >> 1][4 * (tt & 1) + r];
       }
+      STAMP(4);
+      __syncthreads();   // every wave's A1 and W2/S2 copies
+      STAMP(5);
       STAMP(6);
-      __syncthreads();   // every wave's A1 copy
       STAMP(7);
 
       // ================= this half's O = A1 W2^T over its 128 units: tiles (tj, tc0 + i) =================
@@ -885,21 +937,21 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
         for (int i = 0; i < 2; ++i) {
           h4 hv;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            hv[r] = (_Float16)(d2v[4 * i + r] * fD2);
-            sD2[(16 * tj + 4 * g + r) * RS + 16 * (tc0 + i) + lc] = hv[r];
-          }
+          for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(d2v[4 * i + r] * fD2);
           *(h4*)(sD2T + (16 * (tc0 + i) + lc) * RS + 16 * tj + 4 * g) = hv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sD2[(16 * tj + 4 * g + r) * RS + 16 * (tc0 + i) + lc] = hv[r];
         }
       }
       // ---- first-layer masked scores SC1 = D o (Q K^T), tiles (tj, tc0 + i), this wave's own scale ----
       if constexpr (kRW) {
         float sc[8], am = 0.f;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i) {
+          const f4v dt = d_tile(tj, tc0 + i);
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            sc[4 * i + r] = scr[i][r] * d_full(16 * tj + 4 * g + r, 16 * (tc0 + i) + lc);
+          for (int r = 0; r < 4; ++r) sc[4 * i + r] = scr[i][r] * dt[r];
+        }
         am = wave_max(max8(am, sc));
         const int esc = scale_exp(am);
         const float fsc = pow2pos(esc);
@@ -990,7 +1042,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
       STAMP(16);
       const float An = cf[COEF_A + n - 1], En = cf[COEF_E + n - 1], Fn = cf[COEF_F + n - 1];
       const int ewU = ci[INT_EWU], ewD = ci[INT_EWD];
-      float m1n = 0.f, m2n = 0.f;
+      float m1n = 0.f, m2n = 0.f, n1n = 0.f;   // the new state's maxima (n1n: of |W1| alone)
       // the fold weights as fragments in register order over the tokens
       h8 wuf[2], wdf[2];
 #pragma unroll
@@ -1020,6 +1072,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
             S1s[ct][r] = fmaf(gU[r], -uU1, En * s0);
           }
           m1n = max4(max4(m1n, W1s[ct]), S1s[ct]);
+          n1n = max4(n1n, W1s[ct]);
         }
       }
       STAMP(17);
@@ -1053,9 +1106,9 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
           const _Float16* brow = sA1 + (16 * (tc0 + i) + lc) * RW;
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) acc = mfma(frag_c8(arow, 32 * kk, g), frag_c8(brow, 32 * kk, g), acc);
+          const f4v dt = d_tile(tj, tc0 + i);
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            pv[4 * i + r] = acc[r] * cp * d_full(16 * tj + 4 * g + r, 16 * (tc0 + i) + lc);
+          for (int r = 0; r < 4; ++r) pv[4 * i + r] = acc[r] * cp * dt[r];
         }
         am = wave_max(max8(am, pv));
         const int edp = scale_exp(am);
@@ -1137,9 +1190,17 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
           for (int e = 0; e < 8; ++e) tstore(xY_me + par * 256 * 16, e * 256 + (tid & 255), yv[e], seq);
         }
       }
+      // the new state's maxima for the next chunk's operand scales (reduced
+      // here, once the fold's products have long completed)
+      {
+        const float wm1 = wave_max(m1n), wn1 = wave_max(n1n), wm2 = wave_max(m2n);
+        if (lane == 0) {
+          ci[INT_M1 + w] = __float_as_int(wm1);
+          ci[INT_N1 + w] = __float_as_int(wn1);
+          ci[INT_M2 + w] = __float_as_int(wm2);
+        }
+      }
       STAMP(22);
-      m1 = m1n;
-      m2 = m2n;
       prev_row0 = tok0 + c0;
       prev_n = n;
       __syncthreads();   // LDS tiles are rewritten by the next chunk

@@ -27,14 +27,14 @@ CHUNKS = 64
 STAGE_NAMES = [
     "chunk inputs from the staging area into LDS",
     "barrier; next chunk's prefetch issued",
-    "coefficients A, E, F, D (waves 1-3)",
-    "state fragments and W2/S2 copies; Z1 = K W1^T, SiLU, SiLU'",
-    "barrier; D rows completed",
-    "A1 fragments and copy",
+    "(empty)",
+    "state fragments and W2/S2 copies; Z1 = K W1^T, SiLU, SiLU'; A1 copy",
     "barrier",
+    "(empty)",
+    "(empty)",
     "O over the workgroup's units; partials published",
-    "flag; V loads; raw scores Q K^T and Q W1^T, Q S1^T",
-    "wait for the partner (thread 0), barrier",
+    "V loads; coefficients; raw scores Q K^T and Q W1^T, Q S1^T",
+    "wait for the partner's O (every thread its own words)",
     "O sum, Delta2, last chunk's y finished",
     "barrier",
     "Delta2 copies, masked scores SC1, update weights",
