@@ -26,38 +26,75 @@ PEAK_HBM_GBS = 8000.0
 WORKLOAD_NAMES = ("linear", "mlp2_short", "headline", "long", "deep")
 
 
-# dominant kernel of each path: (kernel function, its source under csrc/)
-DOMINANT_KERNEL = {"mlp2_d64_h256_mfma": ("mlp2_group_kernel", "tm_mlp2_group.hip"),
-                   "generic_f32": ("generic_kernel", "tm_generic.hip"),
-                   "input_side": ("input_kernel", "tm_input.hip"),
-                   "retrieve_mlp2": ("mlp2_retrieve_kernel", "tm_retrieve.hip")}
+# dominant kernel of each path: (kernel function, the sources under csrc/ it is built from)
+DOMINANT_KERNEL = {"mlp2_d64_h256_mfma": ("mlp2_group_kernel", ("tm_mlp2_group.hip",)),
+                   "generic_f32": ("generic_kernel", ("tm_generic.hip", "tm_block_gemm.h")),
+                   "input_side": ("input_kernel", ("tm_input.hip",)),
+                   "retrieve_mlp2": ("mlp2_retrieve_kernel", ("tm_retrieve.hip",)),
+                   "backward": ("backward_kernel", ("tm_backward.hip", "tm_generic.hip", "tm_block_gemm.h"))}
 
 
-def measured_traffic(kernel_path, workload):
-    """HBM bytes per launch of the path's dominant kernel on ``workload``, from
-    the committed byte-counter summary, or None when there is none or it was
-    taken on another version of the kernel source."""
+def _source_digest(srcs):
     import hashlib
-    if kernel_path not in DOMINANT_KERNEL:
-        return None
-    kernel, src = DOMINANT_KERNEL[kernel_path]
-    summary = os.path.join(ROOT, "profiles", f"{kernel}__{workload}__hbm_traffic.txt")
-    if not os.path.exists(summary):
-        return None
-    with open(os.path.join(ROOT, "test_learned_neural_amd", "csrc", src), "rb") as fh:
-        digest = hashlib.sha256(fh.read()).hexdigest()
+    h = hashlib.sha256()
+    for src in srcs:
+        with open(os.path.join(ROOT, "test_learned_neural_amd", "csrc", src), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _summary_fields(path):
     fields = {}
-    with open(summary) as fh:
+    with open(path) as fh:
         for line in fh:
             if ":" in line:
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.split()[0] if v.split() else ""
-    if fields.get("kernel_source_sha256") != digest:
-        return None
-    try:
-        return float(fields["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+    return fields
+
+
+def committed_counters(kernel_path, workload):
+    """Counter figures per launch of the path's dominant kernel on ``workload``
+    from the committed rocprofv3 summaries in profiles/ (HBM bytes from the
+    FETCH_SIZE and WRITE_SIZE passes, scaled by a plain copy's readings;
+    executed matrix FLOPs from SQ_INSTS_MFMA), each only while the kernel
+    source hash recorded in it matches the current sources; None otherwise.
+    The counters are not re-read in the run: the JSON names their file."""
+    out = {"traffic": None, "traffic_source": None, "mfma_flops": None, "mfma_source": None}
+    if kernel_path not in DOMINANT_KERNEL:
+        return out
+    kernel, srcs = DOMINANT_KERNEL[kernel_path]
+    digest = _source_digest(srcs)
+    for kind, field, key in (("hbm_traffic", "hbm_bytes_per_launch", "traffic"),
+                             ("sq_counters", "mfma_flops_per_launch", "mfma_flops")):
+        rel = os.path.join("profiles", f"{kernel}__{workload}__{kind}.txt")
+        path = os.path.join(ROOT, rel)
+        if not os.path.exists(path):
+            continue
+        fields = _summary_fields(path)
+        if fields.get("kernel_source_sha256") != digest:
+            continue
+        try:
+            out[key] = float(fields[field])
+        except (KeyError, ValueError):
+            continue
+        out[key.replace("flops", "source") if key == "mfma_flops" else "traffic_source"] = rel
+    return out
+
+
+def counter_fields(kernel_path, workload, launch_s, peak):
+    """The roofline object's counter-derived entries: `traffic` (HBM bytes
+    per launch, or null), `traffic_source` (the committed summary it comes
+    from) and `counters` (executed MFMA rate and counted HBM rate over this
+    run's launch time)."""
+    c = committed_counters(kernel_path, workload)
+    ctr = {}
+    if c["mfma_flops"] is not None:
+        t = c["mfma_flops"] / launch_s / 1e12
+        ctr.update(mfma_executed_tflops=t, mfma_executed_frac=t / peak, mfma_source=c["mfma_source"])
+    if c["traffic"] is not None:
+        ctr["hbm_counted_gbs"] = c["traffic"] / launch_s / 1e9
+    return {"traffic": c["traffic"], "traffic_source": c["traffic_source"], "counters": ctr or None}
 
 
 def algorithmic_work(cfg):
@@ -128,7 +165,7 @@ def bench_input_side(args, np, torch, tmm, wl):
            "ms_per_step": wall * 1e3 / args.steps, "dtype": "bf16",
            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
                         "frac": achieved / PEAK_TFLOPS["bf16"],
-                        "traffic": measured_traffic("input_side", icfg.name),
+                        **counter_fields("input_side", icfg.name, launch_s, PEAK_TFLOPS["bf16"]),
                         "algorithmic_flops_per_launch": flops, "avg_launch_ms": launch_s * 1e3,
                         "hbm_achieved_gbs": byts / launch_s / 1e9, "hbm_peak_gbs": PEAK_HBM_GBS}}
     print(f"[bench] input side {icfg.name}: {launch_s * 1e3:.3f} ms/launch, {achieved:.1f} TFLOP/s "
@@ -176,7 +213,9 @@ def backward_flops_per_token(cfg):
 def bench_backward(args, np, torch, tmm, wl, prefix=1024, steps=3):
     """Gradients through the memory (titans_mem_backward) on the headline
     memory shape, every stream, the first `prefix` tokens."""
-    cfg = wl.WORKLOADS[args.workload].with_(N=prefix)
+    full = wl.WORKLOADS[args.workload]
+    cfg = full.with_(N=prefix)
+    prefix_name = full.name.replace(f"_n{full.N}_", f"_n{prefix}_")   # e.g. ..._n1024_c64_bf16
     inp = wl.make_inputs(cfg, workers=min(16, len(os.sched_getaffinity(0))))
     B, H, N, d, P = cfg.B, cfg.H, cfg.N, cfg.d, cfg.param_count
     if cfg.io == "bf16":
@@ -209,7 +248,8 @@ def bench_backward(args, np, torch, tmm, wl, prefix=1024, steps=3):
     res = {"workload": f"{cfg.name} (first {prefix} tokens of every stream)", "value": tokens / (wall / steps),
            "unit": "memory-tokens/s", "ms_per_step": wall * 1e3 / steps, "dtype": "f32", "steps": steps,
            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
-                        "frac": achieved / PEAK_TFLOPS["f32"], "traffic": None,
+                        "frac": achieved / PEAK_TFLOPS["f32"],
+                        **counter_fields("backward", prefix_name, launch_s, PEAK_TFLOPS["f32"]),
                         "algorithmic_flops_per_launch": flops, "avg_launch_ms": launch_s * 1e3}}
     print(f"[bench] backward {cfg.name}, {prefix} tokens: {launch_s * 1e3:.1f} ms/launch, "
           f"{tokens / launch_s:.3g} memory-tokens/s, {achieved:.2f} TFLOP/s fp32", file=sys.stderr, flush=True)
@@ -268,7 +308,8 @@ def bench_retrieve(args, np, torch, tmm, wl, steps=10):
            "ms_per_step": wall * 1e3 / steps, "dtype": dt, "steps": steps,
            "roofline": {"bound": "mfma" if mfma else "alu", "achieved": achieved, "peak": PEAK_TFLOPS[dt],
                         "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS[dt],
-                        "traffic": measured_traffic("retrieve_mlp2", cfg.name) if mfma else None,
+                        **(counter_fields("retrieve_mlp2", cfg.name, launch_s, PEAK_TFLOPS[dt]) if mfma
+                           else {"traffic": None, "traffic_source": None, "counters": None}),
                         "algorithmic_flops_per_launch": flops, "avg_launch_ms": launch_s * 1e3,
                         "hbm_achieved_gbs": byts / launch_s / 1e9, "hbm_peak_gbs": PEAK_HBM_GBS}}
     print(f"[bench] retrieve {cfg.name}: {launch_s * 1e3:.3f} ms/launch, {tokens / launch_s:.3g} memory-tokens/s, "
@@ -459,7 +500,7 @@ def main():
                    "kernel_path": kernel_path_name,
                    "sequence_tokens_per_s": B * N / (ms_per_step / 1e3)},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": measured_traffic(kernel_path_name, cfg.name),
+                     "frac": achieved / peak, **counter_fields(kernel_path_name, cfg.name, avg_launch_s, peak),
                      "algorithmic_flops_per_launch": flops_tok * mem_tokens,
                      "avg_launch_ms": avg_launch_s * 1e3,
                      "hbm_achieved_gbs": bytes_tok * mem_tokens / avg_launch_s / 1e9,

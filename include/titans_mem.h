@@ -40,7 +40,9 @@
  *   stream): they return after enqueueing and never synchronise.  Argument
  *   errors (codes -1..-4) are detected on the host before anything is
  *   enqueued, so they can be tested without a GPU.
- * - The library allocates no device memory; the caller owns every buffer.
+ * - The library allocates no device memory at run time; the caller owns
+ *   every buffer.  (The scratch of titans_mem_forward_noalloc is a device
+ *   array of the library's code object, present once per GPU from load.)
  * - Process-wide state: per device, one HIP stream of the library's own
  *   (default priority) and six events, created on the first call that needs
  *   them and kept until the process ends.  The shape-generic forward (when
