@@ -2,6 +2,7 @@
 
     python -m test_learned_neural_amd.stage_stamps --build   # compile the instrumented library (CPU)
     python -m test_learned_neural_amd.stage_stamps           # run it on the GPU and print the table
+    python -m test_learned_neural_amd.stage_stamps --isa     # instruction mix per stage (CPU, static)
 
 The instrumented build (-DTM_STAGE_STAMPS=1, a separate library beside the
 product one) makes the eight waves of workgroup 0 record the shader clock at
@@ -57,6 +58,65 @@ def build():
     b.build(verbose=True, extra=["-DTM_STAGE_STAMPS=1"], out=STAMPS_LIB, build_dir=os.path.join(ROOT, "_build", "stamps"))
 
 
+def isa():
+    """Static instruction counts of the instrumented build between consecutive
+    stage stamps (s_memtime) of the read-after-write instance, from its gfx950
+    assembly.  Straight-line counts: each branch's blocks count once, loops
+    once per body, and the compiler may move work across a stamp."""
+    import re
+    import subprocess
+    import tempfile
+    sys.path.insert(0, ROOT)
+    from test_learned_neural_amd import build as b
+    src = os.path.join(b.CSRC, "tm_mlp2_group.hip")
+    with tempfile.TemporaryDirectory() as td:
+        out = os.path.join(td, "k.s")
+        subprocess.check_call([b.hipcc()] + b.COMMON + ["-DTM_STAGE_STAMPS=1", "-x", "hip"] + b.DEVICE +
+                              b.PER_FILE["tm_mlp2_group.hip"] + ["--cuda-device-only", "-S", src, "-o", out],
+                              stderr=subprocess.DEVNULL)
+        lines = open(out).read().split("\n")
+    start = next(i for i, l in enumerate(lines) if re.match(r"^_Z\S*mlp2_group_kernelILb1E\S*:", l))
+    end = next(i for i in range(start, len(lines)) if "s_endpgm" in lines[i])
+    body = lines[start:end]
+    stamps = [i for i, l in enumerate(body) if "s_memtime" in l]
+    classes = ["valu", "trans", "lane", "mfma", "lds", "vmem", "salu"]
+
+    def cls(op):
+        if op.startswith("v_mfma"):
+            return "mfma"
+        if op.startswith(("v_readlane", "v_readfirstlane", "v_writelane")):
+            return "lane"
+        if op.startswith(("v_exp", "v_rcp", "v_log", "v_sqrt", "v_rsq")):
+            return "trans"
+        if op.startswith("v_"):
+            return "valu"
+        if op.startswith("ds_"):
+            return "lds"
+        if op.startswith(("global_", "buffer_", "flat_", "scratch_")):
+            return "vmem"
+        if op.startswith("s_") and not op.startswith(("s_waitcnt", "s_barrier", "s_nop")):
+            return "salu"
+        return None
+
+    print("static instructions per stage (read-after-write instance; 'valu' excludes transcendental and lane ops)")
+    print(f"  {'stage':<62s}" + "".join(f"{c:>7s}" for c in classes))
+    tot = dict.fromkeys(classes, 0)
+    for k, (a, z) in enumerate(zip(stamps, stamps[1:])):
+        cnt = dict.fromkeys(classes, 0)
+        for l in body[a + 1:z]:
+            t = l.strip().split()
+            if not t or t[0].startswith((";", ".")) or t[0].endswith(":"):
+                continue
+            c = cls(t[0])
+            if c:
+                cnt[c] += 1
+        for c in classes:
+            tot[c] += cnt[c]
+        name = STAGE_NAMES[k] if k < len(STAGE_NAMES) else f"stage {k + 1}"
+        print(f"  {k + 1:2d} {name[:59]:<59s}" + "".join(f"{cnt[c]:7d}" for c in classes))
+    print(f"  {'total':<62s}" + "".join(f"{tot[c]:7d}" for c in classes))
+
+
 def run(steps: int = 2):
     import numpy as np
     import torch
@@ -98,5 +158,6 @@ def run(steps: int = 2):
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--build", action="store_true")
+    ap.add_argument("--isa", action="store_true")
     a = ap.parse_args()
-    build() if a.build else run()
+    build() if a.build else isa() if a.isa else run()
