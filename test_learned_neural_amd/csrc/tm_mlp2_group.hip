@@ -75,20 +75,15 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 constexpr int kD = 64;
 constexpr int kH = 256;
 constexpr int kB = 64;               // token rows per chunk tile
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kUW = 16;              // hidden units per wave
-constexpr int kUG = kWaves * kUW;    // hidden units per workgroup (half of kH)
+constexpr int kMaxWaves = 8;         // per-wave LDS slots and stage stamps
 constexpr int kP = 2 * kD * kH;
 constexpr int RS = 72;               // fp16 row stride (halves) of 64-wide tiles: 144-byte rows
-constexpr int RW = 136;              // fp16 row stride of 128-wide tiles: 272-byte rows
 constexpr int RF = 68;               // fp32 row stride of D
-constexpr int kMaxPairs = 128;
 constexpr unsigned kSpinMax = 1u << 21;
 
-// ---- LDS layout (bytes) ----
+// ---- LDS layout (bytes): the part common to both workgroup sizes ----
 constexpr int kT64 = kB * RS * 2;    // 9216
-constexpr int kT128 = kB * RW * 2;   // 17408
 constexpr int OFF_K = 0;             // K   [j][c]
 constexpr int OFF_KT = OFF_K + kT64;     // K^T [c][j]
 constexpr int OFF_Q = OFF_KT + kT64;     // Q   [j][c]
@@ -96,11 +91,7 @@ constexpr int OFF_D2 = OFF_Q + kT64;     // Delta2   [j][c]
 constexpr int OFF_D2T = OFF_D2 + kT64;   // Delta2^T [c][j]
 constexpr int OFF_SC = OFF_D2T + kT64;   // masked scores [j][i]: first layer, then second
 constexpr int OFF_DM = OFF_SC + kT64;    // D [j][i] fp32
-constexpr int OFF_A1 = OFF_DM + kB * RF * 4;   // A1 [j][u] over the workgroup's units
-constexpr int OFF_H1 = OFF_A1 + kT128;         // H1 [j][u]
-constexpr int OFF_W2 = OFF_H1 + kT128;         // W2 [c][u]
-constexpr int OFF_S2 = OFF_W2 + kT128;         // S2 [c][u]
-constexpr int OFF_COEF = OFF_S2 + kT128;
+// coefficient area (relative offsets)
 // float index: XT = the D recurrences' carried products at rows 31 and 63
 // (see the a1 stage), T11/T12 = transfer of rows 32..63 (32 entries each)
 constexpr int COEF_XT = 0, COEF_T11 = 64, COEF_T12 = 96, COEF_THETA = 128, COEF_A = 192, COEF_E = 256,
@@ -110,13 +101,50 @@ constexpr int H16_WU = 0, H16_WD = 64;                              // half inde
 constexpr int COEF_INT = COEF_H16 + 128 * 2;                        // byte offset of int slots
 constexpr int COEF_PAIR = COEF_INT + 64 * 4;                        // byte offset of (1-alpha, eta) pairs
 constexpr int kCoefBytes = COEF_PAIR + kB * 8;
-constexpr int OFF_STAGE = (OFF_COEF + kCoefBytes + 255) / 256 * 256;
 // staging for the next chunk's raw bf16 K, Q rows (row-major, 128 bytes a
 // row) and gates, filled one chunk ahead with LDS-direct loads
 constexpr int kStageBytes = 2 * kB * kD * 2 + 3 * kB * 4;
-constexpr int kLdsBytes = OFF_STAGE + kStageBytes;
-static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-static_assert(8 * 256 * 4 <= kT64, "the parked y tiles fit the Delta2 area");
+
+// ---- the workgroup size: NW waves of 16 hidden units, 256 / (16 NW) workgroups per stream ----
+// The library uses NW = 8 (two workgroups per stream, two waves per SIMD);
+// the layout and the kernel are written for any NW that divides 16 with
+// NW >= 4, the group exchange for any number of workgroups per stream.
+template <int NW>
+struct Grp {
+  static constexpr int kWaves = NW;
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int kUG = kUW * NW;          // hidden units per workgroup
+  static constexpr int kG = kH / kUG;           // workgroups per stream
+  static constexpr int kT = 16 / NW;            // 16x16 tiles per wave of a 64x64 workgroup product
+  static constexpr int kE = 4 * kT;             // values per thread of such a product
+  static constexpr int kYRows = kB / kG;        // y rows (tokens) of a chunk one workgroup finishes
+  static constexpr int kYElems = kYRows * kD;   // ... as elements
+  static constexpr int kYPer = kYElems / kThreads;   // ... per thread
+  static constexpr int kKSteps = kUG / 32;      // K-steps of a product over the workgroup's units
+  static constexpr int kRowPasses = 512 / kThreads;   // 16-byte row pieces of a chunk tile per thread
+  static constexpr int RW = kUG + 8;            // fp16 row stride of the [j][u] / [c][u] tiles
+  static constexpr int kTU = kB * RW * 2;
+  static constexpr int OFF_A1 = OFF_DM + kB * RF * 4;   // A1 [j][u] over the workgroup's units
+  static constexpr int OFF_H1 = OFF_A1 + kTU;           // H1 [j][u]
+  static constexpr int OFF_W2 = OFF_H1 + kTU;           // W2 [c][u]
+  static constexpr int OFF_S2 = OFF_W2 + kTU;           // S2 [c][u]
+  static constexpr int OFF_COEF = OFF_S2 + kTU;
+  static constexpr int OFF_STAGE = (OFF_COEF + kCoefBytes + 255) / 256 * 256;
+  static constexpr int kLdsBytes = OFF_STAGE + kStageBytes;
+  // waves that run the coefficient recurrences during the exchange: D rows
+  // 0..31, D rows 32..63 (and the fold weights), the scans
+  static constexpr int kWD0 = NW == 8 ? 3 : 1, kWD1 = NW == 8 ? 5 : 2, kWS = NW == 8 ? 6 : 3;
+  // exchange words per group: O partials [workgroup][parity][word e][thread]
+  // and y partials [sender][receiver slot][parity][element of the receiver's rows]
+  static constexpr int64_t kXOWords = (int64_t)kG * 2 * kThreads * kE;
+  static constexpr int64_t kXYWords = (int64_t)kG * (kG - 1) * 2 * kYElems;
+  static constexpr int64_t kGroupBytes = (kXOWords + kXYWords) * 8;
+  static constexpr int kMaxGroups = 256 / kG;   // one workgroup per CU of a 256-CU device
+  static_assert(NW == 8 || NW == 4, "eight or four waves");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+  static_assert(kYElems * 4 <= kT64, "the parked y tiles fit the Delta2 area");
+  static_assert(kYPer * kThreads == kYElems, "every thread finishes the same number of y elements");
+};
 
 // int slots
 constexpr int INT_AMAX_D2 = 0, INT_EWU = 1, INT_EWD = 2, INT_FAIL = 3, INT_T22 = 4;
@@ -131,12 +159,8 @@ constexpr int INT_EDP = 40;   // per-wave exponents of the second-layer masked s
 constexpr int INT_NK = 48;    // per-wave maxima of |K|
 constexpr int INT_M1 = 56;    // per-wave maxima of |W1|, |S1| (each wave's own operand scale)
 
-// ---- global workspace layout, per pair (bytes) ----
 // Exchange words are 8 bytes: a float and the sequence number of the chunk
-// that wrote it (see tstore / tpoll8).
-constexpr int64_t kXO = 2 * 2 * kThreads * 8 * 8;    // [half][parity] x 512 threads x 8 words, thread-major
-constexpr int64_t kXY = 2 * 2 * 256 * 8 * 8;         // [half][parity] x 256 threads x 8 words, thread-major
-constexpr int64_t kPairBytes = kXO + kXY;
+// that wrote it (see tstore / tpoll).
 
 // ---- stage timing (a build option; off in the library) ----
 // With TM_STAGE_STAMPS=1 the eight waves of workgroup 0 record the shader
@@ -149,11 +173,11 @@ constexpr int64_t kPairBytes = kXO + kXY;
 #endif
 constexpr int kStampStages = 24, kStampFrom = 16, kStampChunks = 64;
 #if TM_STAGE_STAMPS
-__device__ unsigned long long stage_stamps[kStampChunks * kWaves * kStampStages];
+__device__ unsigned long long stage_stamps[kStampChunks * kMaxWaves * kStampStages];
 #define STAMP(k)                                                                                       \
   do {                                                                                                 \
     if (stamp_slot >= 0 && lane == 0)                                                                  \
-      stage_stamps[(stamp_slot * kWaves + w) * kStampStages + (k)] = __builtin_amdgcn_s_memtime();     \
+      stage_stamps[(stamp_slot * kMaxWaves + w) * kStampStages + (k)] = __builtin_amdgcn_s_memtime();  \
   } while (0)
 #else
 #define STAMP(k) \
@@ -162,7 +186,7 @@ __device__ unsigned long long stage_stamps[kStampChunks * kWaves * kStampStages]
 #endif
 
 struct Params {
-  int N, chunk, streams, n_pairs;
+  int N, chunk, streams, n_groups;
   const __hip_bfloat16* k;
   const __hip_bfloat16* v;
   const __hip_bfloat16* q;
@@ -174,8 +198,8 @@ struct Params {
   __hip_bfloat16* y;
   float* W_out;
   float* S_out;
-  unsigned char* xbuf;   // n_pairs * kPairBytes, zeroed before every launch
-  unsigned* status;      // set to 1 when a pair gave up waiting
+  unsigned char* xbuf;   // n_groups * Grp<NW>::kGroupBytes, zeroed before every launch
+  unsigned* status;      // set to 1 when a group gave up waiting
   unsigned spin_max;
   int chunk_gates;       // gates hold one value per chunk
   int gstride;           // gates per stream: N, or ceil(N / chunk) with per-chunk gates
@@ -301,63 +325,76 @@ __device__ __forceinline__ h8 bf16x8_to_h8(uint4 u) {
             (_Float16)bf16_lo(u.z), (_Float16)bf16_hi(u.z), (_Float16)bf16_lo(u.w), (_Float16)bf16_hi(u.w)};
 }
 
-// Pair exchange: every 8-byte word carries a float and the sequence number
+// Group exchange: every 8-byte word carries a float and the sequence number
 // of the chunk that wrote it, stored with one single-copy-atomic 64-bit
 // agent-coherent (sc1) store.  A reader polls its own words until each
 // carries the sequence number it expects, so no flag, store-completion wait
 // or barrier orders the exchange: a word is either the old one (old number)
 // or the new one, never a mix.  Sequence numbers start at 1 and the buffers
 // are zeroed before every launch, so no word of an earlier call can match.
-// The buffers are thread-major: word e of thread t sits at e * kT + t, so
-// each store or load instruction of a wave covers 512 contiguous bytes
+// The buffers are thread-major: word e of thread t sits at e * stride + t,
+// so each store or load instruction of a wave covers 512 contiguous bytes
 // (whole lines: an agent-coherent store writes through L2), and every thread
-// reads back exactly the words the same thread of the partner wrote.  Two
-// parities per half double-buffer the chunks: the partner overwrites a slot
-// two chunks later, after having read this half's next chunk, which this
-// half writes only after reading the slot.
-__device__ __forceinline__ void tstore(float* base, int idx, float v, unsigned tag) {
+// reads back exactly the words the same thread of a partner wrote.  Two
+// parities double-buffer the chunks: a partner overwrites a slot two chunks
+// later, after having read this workgroup's next chunk, which this
+// workgroup writes only after reading the slot.
+__device__ __forceinline__ void tstore(unsigned long long* base, int idx, float v, unsigned tag) {
   const unsigned long long wd = (unsigned long long)__float_as_uint(v) | ((unsigned long long)tag << 32);
-  __hip_atomic_store((unsigned long long*)base + idx, wd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(base + idx, wd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// words t, t + kT, ..., t + 7 kT until all carry `tag`; false = gave up after
-// spin_max polls (spin_max = 0 gives up at once: the failure-path test hook)
-template <int kT>
-__device__ __forceinline__ bool tpoll8(const float* base, int t, unsigned tag, unsigned spin_max, float* out) {
+// words t, t + kStride, ..., t + (kW - 1) kStride of each of the kN bases,
+// until all carry `tag` (the loads of all bases are in flight together);
+// false = gave up after spin_max polls (spin_max = 0 gives up at once: the
+// failure-path test hook)
+template <int kStride, int kW, int kN>
+__device__ __forceinline__ bool tpoll(const unsigned long long* const (&base)[kN], int t, unsigned tag,
+                                      unsigned spin_max, float (&out)[kN][kW]) {
   for (unsigned it = 0; it < spin_max; ++it) {
-    unsigned long long wd[8];
+    unsigned long long wd[kN][kW];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      wd[e] = __hip_atomic_load((const unsigned long long*)base + (e * kT + t), __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
+    for (int b = 0; b < kN; ++b)
+#pragma unroll
+      for (int e = 0; e < kW; ++e)
+        wd[b][e] = __hip_atomic_load(base[b] + (e * kStride + t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     bool ok = true;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      out[e] = __uint_as_float((unsigned)wd[e]);
-      ok = ok && (unsigned)(wd[e] >> 32) == tag;
-    }
+    for (int b = 0; b < kN; ++b)
+#pragma unroll
+      for (int e = 0; e < kW; ++e) {
+        out[b][e] = __uint_as_float((unsigned)wd[b][e]);
+        ok = ok && (unsigned)(wd[b][e] >> 32) == tag;
+      }
     if (ok) return true;
     __builtin_amdgcn_s_sleep(1);
   }
   return false;
 }
 
-// A chunk's raw inputs, one thread's share: 16 bytes (8 bf16) of row
-// j = tid / 8 of K and of Q (columns 8 (tid % 8) ..), and for tid < 64 the
-// gates of token tid.  Rows and tokens past the chunk end read as zeros
+// A chunk's raw inputs, one thread's share: for each of its row pieces
+// (piece = tid + r * kThreads, r < 512 / kThreads) 16 bytes (8 bf16) of row
+// j = piece / 8 of K and of Q (columns 8 (piece % 8) ..), and for tid < 64
+// the gates of token tid.  Rows and tokens past the chunk end read as zeros
 // (gates as "no forgetting, no decay, no write").
+template <int kPasses>
 struct ChunkRegs {
-  uint4 k, q;
+  uint4 k[kPasses], q[kPasses];
   float ga, ge, gt;
 };
 
-__device__ __forceinline__ ChunkRegs load_chunk_regs(const Params& p, int64_t row0, int64_t g0, int n, int tid) {
-  ChunkRegs r;
-  const int j = tid >> 3, cb = (tid & 7) * 8;
-  if (j < n) {
-    r.k = *(const uint4*)(p.k + (row0 + j) * kD + cb);
-    r.q = *(const uint4*)(p.q + (row0 + j) * kD + cb);
-  } else {
-    r.k = r.q = make_uint4(0, 0, 0, 0);
+template <int kThreads>
+__device__ __forceinline__ ChunkRegs<512 / kThreads> load_chunk_regs(const Params& p, int64_t row0, int64_t g0,
+                                                                      int n, int tid) {
+  ChunkRegs<512 / kThreads> r;
+#pragma unroll
+  for (int rr = 0; rr < 512 / kThreads; ++rr) {
+    const int piece = tid + rr * kThreads, j = piece >> 3, cb = (piece & 7) * 8;
+    if (j < n) {
+      r.k[rr] = *(const uint4*)(p.k + (row0 + j) * kD + cb);
+      r.q[rr] = *(const uint4*)(p.q + (row0 + j) * kD + cb);
+    } else {
+      r.k[rr] = r.q[rr] = make_uint4(0, 0, 0, 0);
+    }
   }
   r.ga = 0.f; r.ge = 1.f; r.gt = 0.f;
   if (tid < kB && tid < n) {
@@ -371,21 +408,26 @@ __device__ __forceinline__ ChunkRegs load_chunk_regs(const Params& p, int64_t ro
 
 // Prefetch of a chunk's raw rows straight into the LDS staging area
 // (global_load_lds: lane l of an instruction writes 16 bytes at base + 16 l,
-// or 4 bytes at base + 4 l; lanes that do not load write nothing).  Thread t
-// loads the 16 bytes load_chunk_regs gives it into slot t of each area, so
-// the area holds the chunk's rows in row-major order and each thread later
-// reads back what it loaded itself.  Wave 0 loads the gates.  Rows and
-// tokens past the chunk end are left out and replaced on unstaging.
+// or 4 bytes at base + 4 l; lanes that do not load write nothing).  Piece
+// `piece` of load_chunk_regs goes to slot `piece` of each area, so the area
+// holds the chunk's rows in row-major order and each thread later reads back
+// what it loaded itself.  Wave 0 loads the gates.  Rows and tokens past the
+// chunk end are left out and replaced on unstaging.
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
+template <int kThreads>
 __device__ __forceinline__ void prefetch_chunk_lds(const Params& p, int64_t row0, int64_t g0, int n, int tid,
                                                    unsigned char* stage) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int j = tid >> 3, cb = (tid & 7) * 8;
   uint4* sk = (uint4*)stage;
   uint4* sq = (uint4*)(stage + kB * kD * 2);
-  if (j < n) {
-    __builtin_amdgcn_global_load_lds((const void*)(p.k + (row0 + j) * kD + cb), (lds_void_ptr)(sk + 64 * w), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(p.q + (row0 + j) * kD + cb), (lds_void_ptr)(sq + 64 * w), 16, 0, 0);
+#pragma unroll
+  for (int rr = 0; rr < 512 / kThreads; ++rr) {
+    const int piece = tid + rr * kThreads, j = piece >> 3, cb = (piece & 7) * 8;
+    const int slot = 64 * (w + rr * (kThreads / 64));
+    if (j < n) {
+      __builtin_amdgcn_global_load_lds((const void*)(p.k + (row0 + j) * kD + cb), (lds_void_ptr)(sk + slot), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(p.q + (row0 + j) * kD + cb), (lds_void_ptr)(sq + slot), 16, 0, 0);
+    }
   }
   if (w == 0 && lane < n) {
     float* g = (float*)(stage + 2 * kB * kD * 2);
@@ -396,14 +438,18 @@ __device__ __forceinline__ void prefetch_chunk_lds(const Params& p, int64_t row0
   }
 }
 
-__device__ __forceinline__ ChunkRegs unstage_chunk_regs(const unsigned char* stage, int n, int tid) {
-  ChunkRegs r;
-  const int j = tid >> 3;
-  if (j < n) {
-    r.k = ((const uint4*)stage)[tid];
-    r.q = ((const uint4*)(stage + kB * kD * 2))[tid];
-  } else {
-    r.k = r.q = make_uint4(0, 0, 0, 0);
+template <int kThreads>
+__device__ __forceinline__ ChunkRegs<512 / kThreads> unstage_chunk_regs(const unsigned char* stage, int n, int tid) {
+  ChunkRegs<512 / kThreads> r;
+#pragma unroll
+  for (int rr = 0; rr < 512 / kThreads; ++rr) {
+    const int piece = tid + rr * kThreads;
+    if ((piece >> 3) < n) {
+      r.k[rr] = ((const uint4*)stage)[piece];
+      r.q[rr] = ((const uint4*)(stage + kB * kD * 2))[piece];
+    } else {
+      r.k[rr] = r.q[rr] = make_uint4(0, 0, 0, 0);
+    }
   }
   r.ga = 0.f; r.ge = 1.f; r.gt = 0.f;
   if (tid < kB && tid < n) {
@@ -421,17 +467,18 @@ __global__ void zero_exchange_kernel(uint4* buf, int64_t n16, unsigned* status) 
   if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0u;
 }
 
-// A half that gave up waiting for its partner writes NaN to W_out, S_out
-// and y of every stream the pair serves (s = pair, pair + n_pairs, ...),
+// A workgroup that gave up waiting for a partner writes NaN to W_out, S_out
+// and y of every stream its group serves (s = group, group + n_groups, ...),
 // after all of its own earlier writes, so a give-up never passes for a
-// result, in place or not.  The partner gives up as well at its next wait
-// and does the same; only a partner that had already passed its last wait
+// result, in place or not.  The partners give up as well at their next wait
+// and do the same; only a partner that had already passed its last wait
 // can still write rows of its own afterwards.
-__device__ void poison_pair_streams(const Params& p, int pair, int tid) {
+template <int kThreads>
+__device__ void poison_group_streams(const Params& p, int grp, int tid) {
   const unsigned fnan = __float_as_uint(__builtin_nanf(""));
   const uint4 f4 = make_uint4(fnan, fnan, fnan, fnan);
   const uint4 b8 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);   // bf16 quiet NaNs
-  for (int s = pair; s < p.streams; s += p.n_pairs) {
+  for (int s = grp; s < p.streams; s += p.n_groups) {
     uint4* Wo = (uint4*)(p.W_out + (int64_t)s * kP);
     uint4* So = (uint4*)(p.S_out + (int64_t)s * kP);
     for (int i = tid; i < kP / 4; i += kThreads) {
@@ -444,18 +491,52 @@ __device__ void poison_pair_streams(const Params& p, int pair, int tid) {
   }
 }
 
-__device__ __forceinline__ float max8(float m, const float* x) {
-  return fmaxf(fmaxf(fmaxf(m, fabsf(x[0])), fmaxf(fabsf(x[1]), fabsf(x[2]))),
-               fmaxf(fmaxf(fabsf(x[3]), fabsf(x[4])), fmaxf(fmaxf(fabsf(x[5]), fabsf(x[6])), fabsf(x[7]))));
+template <int kW>
+__device__ __forceinline__ float max_abs(float m, const float (&x)[kW]) {
+#pragma unroll
+  for (int e = 0; e < kW; ++e) m = fmaxf(m, fabsf(x[e]));
+  return m;
 }
 __device__ __forceinline__ float max4(float m, f4v x) {
   return fmaxf(fmaxf(m, fmaxf(fabsf(x[0]), fabsf(x[1]))), fmaxf(fabsf(x[2]), fabsf(x[3])));
 }
 
+// The group's partial sums added in the fixed order of the workgroups
+// (0 + 1 + ... + kG-1), identical in every workgroup: `own` is workgroup h's
+// partial, pt[m] the partial of its m-th partner in increasing order
+// (workgroup m for m < h, m + 1 above).  h is uniform, so one branch picks
+// the instance whose positions are known at compile time.
+template <int kG, int kW, int kHh = 0>
+__device__ __forceinline__ void ordered_sum(int h, const float (&own)[kW], const float (&pt)[kG - 1][kW],
+                                            float (&out)[kW]) {
+  if constexpr (kG == 2) {
+#pragma unroll
+    for (int e = 0; e < kW; ++e) out[e] = h == 0 ? own[e] + pt[0][e] : pt[0][e] + own[e];
+  } else if constexpr (kHh < kG) {
+    if (h == kHh) {
+#pragma unroll
+      for (int e = 0; e < kW; ++e) {
+        float acc = kHh == 0 ? own[e] : pt[0][e];
+#pragma unroll
+        for (int gg = 1; gg < kG; ++gg) acc += gg < kHh ? pt[gg][e] : gg == kHh ? own[e] : pt[gg - 1][e];
+        out[e] = acc;
+      }
+      return;
+    }
+    ordered_sum<kG, kW, kHh + 1>(h, own, pt, out);
+  }
+}
+
 // kRW: retrieval after each token's write (true) or at the chunk-start
-// state (false: y_j = M_{W_0}(q_j), without the masked correction terms)
-template <bool kRW>
-__global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
+// state (false: y_j = M_{W_0}(q_j), without the masked correction terms).
+// NW: waves per workgroup (Grp<NW>).
+template <bool kRW, int NW>
+__global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
+  using C = Grp<NW>;
+  constexpr int kWaves = C::kWaves, kThreads = C::kThreads, kUG = C::kUG, kG = C::kG, kT = C::kT, kE = C::kE;
+  constexpr int kYPer = C::kYPer, RW = C::RW;
+  constexpr int OFF_A1 = C::OFF_A1, OFF_H1 = C::OFF_H1, OFF_W2 = C::OFF_W2, OFF_S2 = C::OFF_S2,
+                OFF_COEF = C::OFF_COEF, OFF_STAGE = C::OFF_STAGE;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   _Float16* sK = (_Float16*)(smem + OFF_K);
   _Float16* sKT = (_Float16*)(smem + OFF_KT);
@@ -514,38 +595,51 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
     g = lane >> 4;    // K group; accumulator rows 4g .. 4g+3
   };
 
-  // pair / half: blocks g and g + 8 usually share an XCD (round-robin dispatch),
-  // so pairs are formed that way when the grid allows it; correctness does
-  // not depend on the placement
-  int pair, half;
+  // group / workgroup in it: blocks b, b + 8, b + 16, ... usually share an
+  // XCD (round-robin dispatch), so groups are formed that way when the grid
+  // allows it; correctness does not depend on the placement
+  int grp, h;
   {
     const int b = blockIdx.x;
-    if ((gridDim.x & 15) == 0) {
+    if (gridDim.x % (8 * kG) == 0) {
       const int slot = b >> 3;
-      pair = (b & 7) + 8 * (slot >> 1);
-      half = slot & 1;
+      grp = (b & 7) + 8 * (slot / kG);
+      h = slot % kG;
     } else {
-      pair = b >> 1;
-      half = b & 1;
+      grp = b / kG;
+      h = b % kG;
     }
   }
-  const int uw = kUW * w;               // this wave's first unit inside the workgroup's 128
-  const int hs = kUG * half + uw;        // ... and inside the layer's 256
+  const int uw = kUW * w;               // this wave's first unit inside the workgroup's kUG
+  const int hs = kUG * h + uw;          // ... and inside the layer's 256
   // the workgroup-level output tiles of this wave (O, y: tokens tj, columns
-  // tc0, tc0 + 1; the masked scores: tokens tj, keys tc0, tc0 + 1)
-  const int tj = w >> 1, tc0 = 2 * (w & 1);
-  // y rows of tokens 32 half .. 32 half + 31 are finished by this half: its
-  // waves 4 half .. 4 half + 3 keep their y tiles, the others send theirs
-  const bool keeps_y = (tj >> 1) == half;
+  // tc0 .. tc0 + kT - 1; the masked scores: tokens tj, keys tc0 ..)
+  const int tj = (w * kT) >> 2, tc0 = (w * kT) & 3;
+  // y rows kYRows h .. kYRows (h + 1) - 1 of a chunk are finished by
+  // workgroup h: the waves whose tiles lie there park them in LDS, the
+  // other workgroups' waves of those rows send theirs to it, and every
+  // thread of it then sums kYPer elements (one row of 64 per wave and step)
+  const int y_owner = (tj * kG) >> 2;
+  const bool keeps_y = y_owner == h;
+  // element of the owner's rows of this lane's tile element (i, r)
+  auto y_elem = [&](int i, int r) { return (16 * tj + 4 * g + r - C::kYRows * y_owner) * kD + 16 * (tc0 + i) + lc; };
+  // the wave that produced tiles (tt, 2 kk) and (tt, 2 kk + 1) of a masked
+  // score matrix, whose scale the kk-th K-step of a product over keys uses
+  auto score_wave = [](int tt, int kk) { return (4 * tt + 2 * kk) / kT; };
 
-  unsigned char* xb = p.xbuf + (int64_t)pair * kPairBytes;
-  float* xO_me = (float*)(xb) + half * 2 * kThreads * 16;
-  const float* xO_pt = (const float*)(xb) + (1 - half) * 2 * kThreads * 16;
-  float* xY_me = (float*)(xb + kXO) + half * 2 * 256 * 16;
-  const float* xY_pt = (const float*)(xb + kXO) + (1 - half) * 2 * 256 * 16;
+  unsigned long long* xw = (unsigned long long*)(p.xbuf + (int64_t)grp * C::kGroupBytes);
+  // O partials of workgroup wg, parity par
+  auto xO = [&](int wg, unsigned par) { return xw + ((int64_t)wg * 2 + par) * kThreads * kE; };
+  // y partials sent by workgroup snd to its receiver slot sl
+  // ((receiver - snd - 1) mod kG), parity par
+  auto xY = [&](int snd, int sl, unsigned par) {
+    return xw + C::kXOWords + (((int64_t)snd * (kG - 1) + sl) * 2 + par) * C::kYElems;
+  };
+  // the m-th partner in increasing order
+  auto partner = [&](int m) { return m < h ? m : m + 1; };
 
-  // a half that gives up waiting for its partner records it (status word,
-  // and the workgroup's flag checked at its next barrier)
+  // a workgroup that gives up waiting for a partner records it (status
+  // word, and the workgroup's flag checked at its next barrier)
   auto give_up = [&] {
     ci[INT_FAIL] = 1;
     __hip_atomic_store(p.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -560,34 +654,39 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
   // Delta2, after its exchange.  Registers would be spilled across the
   // boundary, and every reload from scratch would wait for the exchange
   // stores in flight.
-  float* ypark = (float*)(smem + OFF_D2);   // 8 floats x 256 keeping threads, thread-major
+  float* ypark = (float*)(smem + OFF_D2);   // kYElems floats: this workgroup's partial of its y rows
   int64_t prev_row0 = -1;   // global token row of the previous chunk's first token
   int prev_n = 0;
   unsigned seq = 0;         // sequence number of the current chunk (1, 2, ...)
   bool staged = false;      // the staging area holds the rows of the chunk about to start
 
-  // the partner's partial for my y tiles of the chunk numbered `tag`
-  // (thread-major over the 256 threads of the keeping / sending waves)
-  auto load_prev_y = [&](unsigned tag, float* pv) {
-    if (keeps_y && !tpoll8<256>(xY_pt + (tag & 1u) * 256 * 16, tid & 255, tag, p.spin_max, pv)) give_up();
+  // the partners' partials of this thread's y elements (tid + kThreads e of
+  // this workgroup's rows) for the chunk numbered `tag`
+  auto load_prev_y = [&](unsigned tag, float (&pv)[kG - 1][kYPer]) {
+    const unsigned long long* bases[kG - 1];
+#pragma unroll
+    for (int m = 0; m < kG - 1; ++m) {
+      const int snd = partner(m);
+      bases[m] = xY(snd, (h - snd - 1 + kG) % kG, tag & 1u);
+    }
+    if (!tpoll<kThreads, kYPer, kG - 1>(bases, tid, tag, p.spin_max, pv)) give_up();
   };
-  // the fixed-order sum of the two partials, stored as bf16
-  auto finish_prev_y = [&](const float* pv) {
-    if (!keeps_y) return;
+  // the fixed-order sum of the group's partials, stored as bf16: element
+  // tid + kThreads e is row kYRows h + w + kWaves e, column `lane`
+  auto finish_prev_y = [&](const float (&pv)[kG - 1][kYPer]) {
+    float own[kYPer], sum[kYPer];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int e = 0; e < kYPer; ++e) own[e] = ypark[e * kThreads + tid];
+    ordered_sum<kG, kYPer>(h, own, pv, sum);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * tj + 4 * g + r;
-        if (j < prev_n) {
-          const float a = ypark[(4 * i + r) * 256 + (tid & 255)], b = pv[4 * i + r];
-          p.y[(prev_row0 + j) * kD + 16 * (tc0 + i) + lc] = __float2bfloat16(half == 0 ? a + b : b + a);
-        }
-      }
+    for (int e = 0; e < kYPer; ++e) {
+      const int j = C::kYRows * h + w + kWaves * e;
+      if (j < prev_n) p.y[(prev_row0 + j) * kD + lane] = __float2bfloat16(sum[e]);
+    }
   };
   __syncthreads();
 
-  for (int s = pair; s < p.streams && !failed; s += p.n_pairs) {
+  for (int s = grp; s < p.streams && !failed; s += p.n_groups) {
     const int64_t tok0 = (int64_t)s * p.N;
     // ---- this wave's state, VGPR-resident ----
     // W1s[ct]: rows c = 16 ct + 4g + r, lanes u = hs + lc   (W1[u][c])
@@ -625,7 +724,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
       const int n = min(p.chunk, p.N - c0);
       relane();
       ++seq;
-      const int stamp_slot = (TM_STAGE_STAMPS && blockIdx.x == 0 && s == pair && cidx >= kStampFrom &&
+      const int stamp_slot = (TM_STAGE_STAMPS && blockIdx.x == 0 && s == grp && cidx >= kStampFrom &&
                               cidx < kStampFrom + kStampChunks) ? cidx - kStampFrom : -1;
       (void)stamp_slot;
       STAMP(0);
@@ -635,14 +734,21 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
         // (this thread's staging loads were waited for after the previous
         // chunk's exchange; waiting here would also wait for the y exchange
         // stores just issued)
-        const ChunkRegs cr = staged ? unstage_chunk_regs(smem + OFF_STAGE, n, tid)
-                                    : load_chunk_regs(p, tok0 + c0, gate_base(p, s, cidx, c0), n, tid);
-        const int j = tid >> 3, cb = (tid & 7) * 8;
-        const h8 kv = bf16x8_to_h8(cr.k), qv = bf16x8_to_h8(cr.q);
-        *(h8*)(sK + j * RS + cb) = kv;
-        *(h8*)(sQ + j * RS + cb) = qv;
+        const ChunkRegs<C::kRowPasses> cr =
+            staged ? unstage_chunk_regs<kThreads>(smem + OFF_STAGE, n, tid)
+                   : load_chunk_regs<kThreads>(p, tok0 + c0, gate_base(p, s, cidx, c0), n, tid);
+        float kn = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sKT[(cb + i) * RS + j] = kv[i];
+        for (int rr = 0; rr < C::kRowPasses; ++rr) {
+          const int piece = tid + rr * kThreads, j = piece >> 3, cb = (piece & 7) * 8;
+          const h8 kv = bf16x8_to_h8(cr.k[rr]), qv = bf16x8_to_h8(cr.q[rr]);
+          *(h8*)(sK + j * RS + cb) = kv;
+          *(h8*)(sQ + j * RS + cb) = qv;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sKT[(cb + i) * RS + j] = kv[i];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) kn = fmaxf(kn, fabsf((float)kv[i]));
+        }
         if (tid < kB) {
           cf[COEF_THETA + tid] = cr.gt;
           float2* pairs = (float2*)(smem + OFF_COEF + COEF_PAIR);
@@ -652,9 +758,6 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
           ci[INT_AMAX_D2] = 0;
           ci[INT_FAIL] = 0;
         }
-        float kn = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) kn = fmaxf(kn, fabsf((float)kv[i]));
         const float wnk = wave_max(kn);
         if (lane == 0) ci[INT_NK + w] = __float_as_int(wnk);
       }
@@ -663,18 +766,19 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
       // the next chunk's rows go straight to the staging area (read at its start)
       {
         int next_s = s, next_c0 = c0 + p.chunk, next_ci = cidx + 1;
-        if (next_c0 >= p.N) { next_s = s + p.n_pairs; next_c0 = 0; next_ci = 0; }
+        if (next_c0 >= p.N) { next_s = s + p.n_groups; next_c0 = 0; next_ci = 0; }
         const bool has_next = next_s < p.streams && p.N > 0;
         if (has_next)
-          prefetch_chunk_lds(p, (int64_t)next_s * p.N + next_c0, gate_base(p, next_s, next_ci, next_c0),
-                             min(p.chunk, p.N - next_c0), tid, smem + OFF_STAGE);
+          prefetch_chunk_lds<kThreads>(p, (int64_t)next_s * p.N + next_c0, gate_base(p, next_s, next_ci, next_c0),
+                                       min(p.chunk, p.N - next_c0), tid, smem + OFF_STAGE);
         staged = has_next;
       }
       STAMP(2);
 
       STAMP(3);
       // state scales: W1/S1 per wave; W2/S2 joint over the workgroup (the
-      // half's O and y are contractions over all its waves' W2 and S2 copies)
+      // workgroup's O and y partials are contractions over all its waves'
+      // W2 and S2 copies)
       int e2;
       {
         float mm = 0.f;
@@ -765,25 +869,26 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
       STAMP(6);
       STAMP(7);
 
-      // ================= this half's O = A1 W2^T over its 128 units: tiles (tj, tc0 + i) =================
-      float om[8];
+      // ================= this workgroup's O = A1 W2^T over its units: tiles (tj, tc0 + i) =================
+      float om[kE];
       {
         const float co = pow2neg(eA1 + e2);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < kT; ++i) {
           f4v acc = {};
           const _Float16* arow = sA1 + (16 * tj + lc) * RW;
           const _Float16* brow = sW2 + (16 * (tc0 + i) + lc) * RW;
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) acc = mfma(frag_c8(arow, 32 * kk, g), frag_c8(brow, 32 * kk, g), acc);
+          for (int kk = 0; kk < C::kKSteps; ++kk)
+            acc = mfma(frag_c8(arow, 32 * kk, g), frag_c8(brow, 32 * kk, g), acc);
 #pragma unroll
           for (int r = 0; r < 4; ++r) om[4 * i + r] = acc[r] * co;
         }
       }
-      // publish this half's O (words tagged with this chunk's number)
+      // publish this workgroup's O (words tagged with this chunk's number)
       const unsigned par = seq & 1u;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) tstore(xO_me + par * kThreads * 16, e * kThreads + tid, om[e], seq);
+      for (int e = 0; e < kE; ++e) tstore(xO(h, par), e * kThreads + tid, om[e], seq);
       STAMP(8);
 
       // ---- work that does not need the partner, while the exchange is in flight ----
@@ -792,38 +897,39 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
       // its end are zeroed at use): a load under a branch would end a basic
       // block and be waited for at once, which also waits for the exchange
       // stores still in flight.
-      unsigned short vr[8];
+      unsigned short vr[kE];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < kT; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = min(16 * tj + 4 * g + r, n - 1);
           vr[4 * i + r] = *(const unsigned short*)(p.v + (tok0 + c0 + j) * kD + 16 * (tc0 + i) + lc);
         }
-      // ================= a1: coefficients (both halves compute them identically) =================
+      // ================= a1: coefficients (every workgroup computes them identically) =================
       // While the exchange is in flight.  Lane m of a wave holds token m's
       // (1 - alpha_m, eta_m); padding tokens have alpha = 0, eta = 1, theta = 0.
       //
       // D, one lane per column i: t = theta_i prod_{i<m<=j} eta_m, started at
       // j == i by adding theta_i to a zero product, and
       // D[j][i] = (1 - alpha_j) D[j-1][i] + t -- one fma per row on each of the
-      // two carried values, the row's gates broadcast from LDS.  Wave 3 runs
-      // rows 0..31 and wave 5 rows 32..63, each starting from zero.  For
-      // columns i >= 32 wave 5's rows are exact (their recurrences start at
-      // row i); for i < 32 its rows lack the part carried over from row 31,
+      // two carried values, the row's gates broadcast from LDS.  Wave kWD0
+      // runs rows 0..31 and wave kWD1 rows 32..63, each starting from zero.
+      // For columns i >= 32 the second wave's rows are exact (their
+      // recurrences start at row i); for i < 32 they lack the part carried
+      // over from row 31,
       // which every reader adds (d_full) through the column-independent
       // transfer
       //   (D, t)_j += (T11_j D_31 + T12_j t_31, T22_j t_31),
       // T11_j = prod_{32<=m<=j} (1 - alpha_m), T22_j = prod_{32<=m<=j} eta_m,
       // T12_j = sum_{32<=l<=j} prod_{l<m<=j} (1 - alpha_m) T22_l,
-      // which wave 6 gets from prefix scans restarted at row 32, beside E_j (a
+      // which wave kWS gets from prefix scans restarted at row 32, beside E_j (a
       // prefix product of eta) and (A_j, F_j) (a prefix scan of the maps
       // u -> (1 - alpha_j) u + E_j: A_j is the scan's product part, F_j its
       // value from F_{-1} = 0).  First read after the barrier that follows
       // the exchange.
-      if (w == 3 || w == 5) {
+      if (w == C::kWD0 || w == C::kWD1) {
         const int i = lane;
-        const int j0 = w == 3 ? 0 : 32;
+        const int j0 = w == C::kWD0 ? 0 : 32;
         const float thi = cf[COEF_THETA + i];
         float di = 0.f, t = 0.f;
         const float4* pairs4 = (const float4*)(smem + OFF_COEF + COEF_PAIR) + j0 / 2;
@@ -849,9 +955,9 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
 #pragma unroll
           for (int jj = 0; jj < 8; ++jj) sDM[(j0 + 8 * b + jj) * RF + i] = drows[jj];
         }
-        // wave 3: t at row 31 for i < 32; wave 5: t at row 63 (= U_i) for i >= 32
-        if ((w == 3) == (i < 32)) cf[COEF_XT + i] = t;
-      } else if (w == 6) {
+        // wave kWD0: t at row 31 for i < 32; wave kWD1: t at row 63 (= U_i) for i >= 32
+        if ((w == C::kWD0) == (i < 32)) cf[COEF_XT + i] = t;
+      } else if (w == C::kWS) {
         const float2 gl = ((const float2*)(smem + OFF_COEF + COEF_PAIR))[lane];
         const float e = wave_prefix_prod(gl.y);
         float a = gl.x, f = e;
@@ -872,10 +978,10 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
       }
       // the raw first-layer scores Q K^T (tiles (tj, tc0 + i)) and the query
       // products Q W1^T, Q S1^T
-      f4v scr[2], accW[4], accS[4];
+      f4v scr[kT], accW[4], accS[4];
       if constexpr (kRW) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < kT; ++i) {
           f4v acc = {};
           const _Float16* arow = sQ + (16 * tj + lc) * RS;
           const _Float16* brow = sK + (16 * (tc0 + i) + lc) * RS;
@@ -898,27 +1004,32 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
         accS[tt] = as;
       }
       STAMP(9);
-      // the partner's O for this thread's elements, and its part of my y tiles
-      // of the previous chunk
-      float pvv[8], pyv[8];
-      if (!tpoll8<kThreads>(xO_pt + par * kThreads * 16, tid, seq, p.spin_max, pvv)) give_up();
+      // the partners' O for this thread's elements, and their parts of my y
+      // tiles of the previous chunk
+      float pvv[kG - 1][kE], pyv[kG - 1][kYPer];
+      {
+        const unsigned long long* bases[kG - 1];
+#pragma unroll
+        for (int m = 0; m < kG - 1; ++m) bases[m] = xO(partner(m), par);
+        if (!tpoll<kThreads, kE, kG - 1>(bases, tid, seq, p.spin_max, pvv)) give_up();
+      }
       if (prev_row0 >= 0) load_prev_y(seq - 1, pyv);
       // every vector memory operation of this thread done, the next chunk's
       // staging loads included (a no-op after a poll, which waited for them)
       __builtin_amdgcn_s_waitcnt(0x0F70);
       STAMP(10);
-      // ================= O = half 0 + half 1, Delta2 = O - V (this thread's 8 elements) =================
-      float d2v[8];
+      // ================= O = the group's partials in workgroup order, Delta2 = O - V =================
+      float d2v[kE];
       {
-        float am = 0.f;
+        float am = 0.f, o[kE];
+        ordered_sum<kG, kE>(h, om, pvv, o);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < kE; ++e) {
           const int j = 16 * tj + 4 * g + (e & 3);
-          const float o = half == 0 ? om[e] + pvv[e] : pvv[e] + om[e];
           const float vv = __uint_as_float((unsigned)vr[e] << 16);
-          d2v[e] = j < n ? o - vv : 0.f;
+          d2v[e] = j < n ? o[e] - vv : 0.f;
         }
-        am = max8(am, d2v);
+        am = max_abs(am, d2v);
         am = wave_max(am);
         if (lane == 0) atomicMax((unsigned int*)&ci[INT_AMAX_D2], __float_as_uint(am));
       }
@@ -934,7 +1045,7 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
       {
         const float fD2 = pow2pos(eD2);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < kT; ++i) {
           h4 hv;
 #pragma unroll
           for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(d2v[4 * i + r] * fD2);
@@ -945,24 +1056,24 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
       }
       // ---- first-layer masked scores SC1 = D o (Q K^T), tiles (tj, tc0 + i), this wave's own scale ----
       if constexpr (kRW) {
-        float sc[8], am = 0.f;
+        float sc[kE], am = 0.f;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < kT; ++i) {
           const f4v dt = d_tile(tj, tc0 + i);
 #pragma unroll
           for (int r = 0; r < 4; ++r) sc[4 * i + r] = scr[i][r] * dt[r];
         }
-        am = wave_max(max8(am, sc));
+        am = wave_max(max_abs(am, sc));
         const int esc = scale_exp(am);
         const float fsc = pow2pos(esc);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < kT; ++i)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             sSC[(16 * tj + 4 * g + r) * RS + 16 * (tc0 + i) + lc] = (_Float16)(sc[4 * i + r] * fsc);
         if (lane == 0) ci[INT_ESC + w] = esc;
       }
-      if (w == 3) {
+      if (w == C::kWD0) {
         // weights of the state update: U_i = theta_i prod_{m>i} eta_m and
         // D[n-1][i], each scaled into (0.5, 1] for fp16 (padding has eta = 1)
         const int i = lane;
@@ -1019,7 +1130,8 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
             f4v m0 = {}, m1v = {};
             m0 = mfma(frag_rk(srow, 0, g), d1f[0], m0);
             m1v = mfma(frag_rk(srow, 32, g), d1f[1], m1v);
-            const float c30 = pow2neg(eD1 + ci[INT_ESC + 2 * tt]), c31 = pow2neg(eD1 + ci[INT_ESC + 2 * tt + 1]);
+            const float c30 = pow2neg(eD1 + ci[INT_ESC + score_wave(tt, 0)]),
+                        c31 = pow2neg(eD1 + ci[INT_ESC + score_wave(tt, 1)]);
             const f4v av = *(const f4v*)(cf + COEF_A + 16 * tt + 4 * g);
             const f4v fv = *(const f4v*)(cf + COEF_F + 16 * tt + 4 * g);
 #pragma unroll
@@ -1097,24 +1209,25 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
 
       // ================= masked second-layer scores D o (H1 A1^T): tiles (tj, tc0 + i) =================
       if constexpr (kRW) {
-        float pv[8], am = 0.f;
+        float pv[kE], am = 0.f;
         const float cp = pow2neg(eH1 + eA1);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < kT; ++i) {
           f4v acc = {};
           const _Float16* arow = sH1 + (16 * tj + lc) * RW;
           const _Float16* brow = sA1 + (16 * (tc0 + i) + lc) * RW;
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) acc = mfma(frag_c8(arow, 32 * kk, g), frag_c8(brow, 32 * kk, g), acc);
+          for (int kk = 0; kk < C::kKSteps; ++kk)
+            acc = mfma(frag_c8(arow, 32 * kk, g), frag_c8(brow, 32 * kk, g), acc);
           const f4v dt = d_tile(tj, tc0 + i);
 #pragma unroll
           for (int r = 0; r < 4; ++r) pv[4 * i + r] = acc[r] * cp * dt[r];
         }
-        am = wave_max(max8(am, pv));
+        am = wave_max(max_abs(am, pv));
         const int edp = scale_exp(am);
         const float fdp = pow2pos(edp);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < kT; ++i)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             sSC[(16 * tj + 4 * g + r) * RS + 16 * (tc0 + i) + lc] = (_Float16)(pv[4 * i + r] * fdp);
@@ -1150,17 +1263,17 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
 
       // ================= a5 layer 2: y = diag(A) H1 W2^T + diag(F) H1 S2^T - (D o P) Delta2 =================
       {
-        float yv[8];
+        float yv[kE];
         const float cy = pow2neg(eH1 + e2);
         const f4v av = *(const f4v*)(cf + COEF_A + 16 * tj + 4 * g);
         const f4v fv = *(const f4v*)(cf + COEF_F + 16 * tj + 4 * g);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < kT; ++i) {
           const _Float16* arow = sH1 + (16 * tj + lc) * RW;
           const int crow = 16 * (tc0 + i) + lc;
           f4v aw = {}, as = {};
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
+          for (int kk = 0; kk < C::kKSteps; ++kk) {
             const h8 hf = frag_c8(arow, 32 * kk, g);
             aw = mfma(hf, frag_c8(sW2 + crow * RW, 32 * kk, g), aw);
             if constexpr (kRW) as = mfma(hf, frag_c8(sS2 + crow * RW, 32 * kk, g), as);
@@ -1170,7 +1283,8 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
             f4v m0 = {}, m1v = {};
             m0 = mfma(frag_c8(drow, 0, g), frag_c8(sD2T + crow * RS, 0, g), m0);
             m1v = mfma(frag_c8(drow, 32, g), frag_c8(sD2T + crow * RS, 32, g), m1v);
-            const float c30 = pow2neg(eD2 + ci[INT_EDP + 2 * tj]), c31 = pow2neg(eD2 + ci[INT_EDP + 2 * tj + 1]);
+            const float c30 = pow2neg(eD2 + ci[INT_EDP + score_wave(tj, 0)]),
+                        c31 = pow2neg(eD2 + ci[INT_EDP + score_wave(tj, 1)]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float main = fmaf(av[r], aw[r], fv[r] * as[r]) * cy;
@@ -1181,13 +1295,18 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
             for (int r = 0; r < 4; ++r) yv[4 * i + r] = aw[r] * cy;
           }
         }
-        // keep my rows, send the partner its rows
+        // keep my rows, send the other rows to the workgroup that finishes them
         if (keeps_y) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ypark[e * 256 + (tid & 255)] = yv[e];
-        } else {
+          for (int i = 0; i < kT; ++i)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) tstore(xY_me + par * 256 * 16, e * 256 + (tid & 255), yv[e], seq);
+            for (int r = 0; r < 4; ++r) ypark[y_elem(i, r)] = yv[4 * i + r];
+        } else {
+          unsigned long long* yb = xY(h, (y_owner - h - 1 + kG) % kG, par);
+#pragma unroll
+          for (int i = 0; i < kT; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tstore(yb, y_elem(i, r), yv[4 * i + r], seq);
         }
       }
       // the new state's maxima for the next chunk's operand scales (reduced
@@ -1229,14 +1348,14 @@ __global__ void __launch_bounds__(kThreads, 1) mlp2_group_kernel(Params p) {
 
   // the last chunk's y rows
   if (!failed && prev_row0 >= 0) {
-    float pyv[8];
+    float pyv[kG - 1][kYPer];
     load_prev_y(seq, pyv);
     finish_prev_y(pyv);   // (rows of a wait that gave up are overwritten below)
     __syncthreads();
     if (ci[INT_FAIL]) failed = true;
   }
-  if (failed) poison_pair_streams(p, pair, tid);
-  // no load into this workgroup's LDS may outlive it (a pair that gave up
+  if (failed) poison_group_streams<kThreads>(p, grp, tid);
+  // no load into this workgroup's LDS may outlive it (a workgroup that gave up
   // can leave a staging prefetch in flight)
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
@@ -1248,15 +1367,23 @@ bool mlp2_supported(const Shape& s, int chunk) {
          (s.read_mode == TM_READ_AFTER_WRITE || s.read_mode == TM_READ_CHUNK_START) && chunk >= 1 && chunk <= kB;
 }
 
-static int64_t pairs_for(const Shape& s) { return s.streams < kMaxPairs ? s.streams : kMaxPairs; }
+// Eight waves per workgroup for every stream count: four-wave workgroups
+// in groups of four (a few streams over twice as many CUs) measured slower
+// per chunk, since a chunk's time is each wave's own dependency chain and
+// a four-wave workgroup's waves carry twice the workgroup-level tiles.
+using GrpUsed = Grp<8>;
+static int64_t groups_for(const Shape& s) {
+  return s.streams < GrpUsed::kMaxGroups ? s.streams : GrpUsed::kMaxGroups;
+}
+static int64_t group_bytes(const Shape&) { return GrpUsed::kGroupBytes; }
 
-int64_t mlp2_ws_bytes(const Shape& s, int) { return pairs_for(s) * kPairBytes + 256; }
+int64_t mlp2_ws_bytes(const Shape& s, int) { return groups_for(s) * group_bytes(s) + 256; }
 
-int64_t mlp2_status_offset(const Shape& s) { return pairs_for(s) * kPairBytes; }
+int64_t mlp2_status_offset(const Shape& s) { return groups_for(s) * group_bytes(s); }
 
 // ---- scratch of titans_mem_forward_noalloc ----
 // The kernel's workspace (exchange buffers and status word) for the
-// largest pair count, as a file-scope device array: one copy per GPU,
+// largest group count, as a file-scope device array: one copy per GPU,
 // allocated when the library's code object is loaded on that device and
 // held until the process ends.  Host code must not use the array's name as
 // an address: its device address is looked up once per device with
@@ -1264,7 +1391,7 @@ int64_t mlp2_status_offset(const Shape& s) { return pairs_for(s) * kPairBytes; }
 // array; every call clears the exchange buffers and the status word with a
 // fill kernel (no memset) before the memory kernel, so calls that follow one
 // another are independent, while calls that overlap on one GPU race.
-constexpr int64_t kScratchBytes = kMaxPairs * kPairBytes + 256;
+constexpr int64_t kScratchBytes = GrpUsed::kMaxGroups * GrpUsed::kGroupBytes + 256;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
@@ -1293,37 +1420,39 @@ hipError_t mlp2_scratch(void** out, bool lookup) {
 #if TM_STAGE_STAMPS
 }  // namespace titans
 extern "C" int titans_mem_stage_stamps(unsigned long long* dst, int64_t count) {
-  if (count > (int64_t)titans::kStampChunks * titans::kWaves * titans::kStampStages) return TM_ERR_INVALID;
+  if (count > (int64_t)titans::kStampChunks * titans::kMaxWaves * titans::kStampStages) return TM_ERR_INVALID;
   return hipMemcpyFromSymbol(dst, HIP_SYMBOL(titans::stage_stamps), count * sizeof(unsigned long long), 0,
                              hipMemcpyDeviceToHost) == hipSuccess ? TM_OK : TM_ERR_HIP;
 }
 namespace titans {
 #endif
 
-hipError_t launch_mlp2(const Shape& s, int chunk, const void* k, const void* v, const void* q,
-                       const float* alpha, const float* eta, const float* theta,
-                       const float* W_in, const float* S_in, void* y, float* W_out,
-                       float* S_out, void* ws, hipStream_t stream) {
+template <int NW>
+static hipError_t launch_group(const Shape& s, int chunk, const void* k, const void* v, const void* q,
+                               const float* alpha, const float* eta, const float* theta, const float* W_in,
+                               const float* S_in, void* y, float* W_out, float* S_out, void* ws,
+                               hipStream_t stream) {
+  using C = Grp<NW>;
   // the kernel's dynamic LDS size, set on every call (no state kept between
   // calls; idempotent and cheap next to the kernel)
-  const void* kfn = s.read_mode == TM_READ_AFTER_WRITE ? (const void*)mlp2_group_kernel<true>
-                                                       : (const void*)mlp2_group_kernel<false>;
-  hipError_t e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  const void* kfn = s.read_mode == TM_READ_AFTER_WRITE ? (const void*)mlp2_group_kernel<true, NW>
+                                                       : (const void*)mlp2_group_kernel<false, NW>;
+  hipError_t e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
   if (e != hipSuccess) return e;
   int dev = 0, cus = 0;
   e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  // every pair must be resident at once (one workgroup per CU)
-  int64_t np = pairs_for(s);
-  if (np > cus / 2) np = cus / 2;
-  if (np < 1) return hipErrorInvalidConfiguration;
+  // every group must be resident at once (one workgroup per CU)
+  int64_t ng = groups_for(s);
+  if (ng > cus / C::kG) ng = cus / C::kG;
+  if (ng < 1) return hipErrorInvalidConfiguration;
   Params p;
   p.N = s.N;
   p.chunk = chunk;
   p.streams = s.streams;
-  p.n_pairs = (int)np;
+  p.n_groups = (int)ng;
   p.k = (const __hip_bfloat16*)k;
   p.v = (const __hip_bfloat16*)v;
   p.q = (const __hip_bfloat16*)q;
@@ -1341,16 +1470,25 @@ hipError_t launch_mlp2(const Shape& s, int chunk, const void* k, const void* v, 
   p.spin_max = (s.flags & TM_FLAG_NO_WAIT) ? 0u : kSpinMax;
   p.chunk_gates = s.chunk_gates;
   p.gstride = s.chunk_gates ? (s.N + chunk - 1) / chunk : s.N;
-  const int64_t n16 = np * kPairBytes / 16;
+  const int64_t n16 = ng * C::kGroupBytes / 16;
   hipLaunchKernelGGL(zero_exchange_kernel, dim3((unsigned)std::min<int64_t>((n16 + 255) / 256, 1024)), dim3(256), 0,
                      stream, (uint4*)base, n16, p.status);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)(C::kG * ng)), block(C::kThreads);
   if (s.read_mode == TM_READ_AFTER_WRITE)
-    hipLaunchKernelGGL(mlp2_group_kernel<true>, dim3((unsigned)(2 * np)), dim3(kThreads), kLdsBytes, stream, p);
+    hipLaunchKernelGGL((mlp2_group_kernel<true, NW>), grid, block, C::kLdsBytes, stream, p);
   else
-    hipLaunchKernelGGL(mlp2_group_kernel<false>, dim3((unsigned)(2 * np)), dim3(kThreads), kLdsBytes, stream, p);
+    hipLaunchKernelGGL((mlp2_group_kernel<false, NW>), grid, block, C::kLdsBytes, stream, p);
   return hipGetLastError();
+}
+
+hipError_t launch_mlp2(const Shape& s, int chunk, const void* k, const void* v, const void* q,
+                       const float* alpha, const float* eta, const float* theta,
+                       const float* W_in, const float* S_in, void* y, float* W_out,
+                       float* S_out, void* ws, hipStream_t stream) {
+  return launch_group<GrpUsed::kWaves>(s, chunk, k, v, q, alpha, eta, theta, W_in, S_in, y, W_out, S_out, ws,
+                                       stream);
 }
 
 }  // namespace titans
