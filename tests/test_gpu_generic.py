@@ -294,9 +294,10 @@ def test_generic_split_calls_on_two_streams():
 @pytest.mark.parametrize("d,N,chunk,read_mode,io", [(64, 300, 64, 1, "bf16"), (32, 129, 1, 0, "f32"),
                                                     (8, 50, 7, 0, "bf16"), (64, 200, 16, 0, "f32")])
 def test_linear_memory_kernel(d, N, chunk, read_mode, io):
-    """The linear memory (d <= 64, chunk <= 64) runs on its own one-workgroup
-    kernel within the generic path: both read modes, both io dtypes, chunks
-    of one token and ragged tails; an in-place call agrees bitwise."""
+    """The linear memory (d <= 64, chunk <= 64) runs on its own kernel within
+    the generic path (four rows of W and S per workgroup): both read modes,
+    both io dtypes, chunks of one token and ragged tails, d from 8 to 64; an
+    in-place call agrees bitwise."""
     import torch
     cfg = wl.WORKLOADS["linear"].with_(B=2, H=2, N=N, d=d, chunk=chunk, io=io)
     inp = wl.make_inputs(cfg)
