@@ -184,7 +184,7 @@ int titans_mem_forward(const titans_mem_desc* desc,
  * 2-layer, d = 64, hidden = 256, bf16 io, chunk <= 64; any B*H, N and read
  * mode); TM_ERR_UNSUPPORTED for every other shape.  Its scratch (the
  * paired workgroups' tagged exchange words and the status word) is a
- * library-owned device array of 25,166,080 bytes (24 MiB + 256: enough for
+ * library-owned device array of 12,583,168 bytes (12 MiB + 256: enough for
  * the kernel's largest grid of 128 workgroup pairs; TM_ERR_WORKSPACE if a
  * shape ever needed more), one per GPU,
  * allocated with the library's code and held until the process ends.  The

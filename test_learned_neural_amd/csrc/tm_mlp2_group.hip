@@ -136,14 +136,14 @@ struct Grp {
   static constexpr int kWD0 = NW == 8 ? 3 : 1, kWD1 = NW == 8 ? 5 : 2, kWS = NW == 8 ? 6 : 3;
   // exchange words per group: O partials [workgroup][parity][word e][thread]
   // and y partials [sender][receiver slot][parity][element of the receiver's rows]
-  static constexpr int64_t kXOWords = (int64_t)kG * 2 * kThreads * kE;
-  static constexpr int64_t kXYWords = (int64_t)kG * (kG - 1) * 2 * kYElems;
+  static constexpr int64_t kXOWords = (int64_t)kG * 2 * kThreads * (kE / 2);   // two values a word
+  static constexpr int64_t kXYWords = (int64_t)kG * (kG - 1) * 2 * (kYElems / 2);
   static constexpr int64_t kGroupBytes = (kXOWords + kXYWords) * 8;
   static constexpr int kMaxGroups = 256 / kG;   // one workgroup per CU of a 256-CU device
   static_assert(NW == 8 || NW == 4, "eight or four waves");
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
   static_assert(kYElems * 4 <= kT64, "the parked y tiles fit the Delta2 area");
-  static_assert(kYPer * kThreads == kYElems, "every thread finishes the same number of y elements");
+  static_assert(kYPer * kThreads == kYElems && kYPer % 2 == 0, "every thread finishes the same number of y rows pairs");
 };
 
 // int slots
@@ -159,8 +159,8 @@ constexpr int INT_EDP = 40;   // per-wave exponents of the second-layer masked s
 constexpr int INT_NK = 48;    // per-wave maxima of |K|
 constexpr int INT_M1 = 56;    // per-wave maxima of |W1|, |S1| (each wave's own operand scale)
 
-// Exchange words are 8 bytes: a float and the sequence number of the chunk
-// that wrote it (see tstore / tpoll).
+// Exchange words are 8 bytes: two values and the low bits of the sequence
+// number of the chunk that wrote them (see tstore / tpoll).
 
 // ---- stage timing (a build option; off in the library) ----
 // With TM_STAGE_STAMPS=1 the eight waves of workgroup 0 record the shader
@@ -325,31 +325,40 @@ __device__ __forceinline__ h8 bf16x8_to_h8(uint4 u) {
             (_Float16)bf16_lo(u.z), (_Float16)bf16_hi(u.z), (_Float16)bf16_lo(u.w), (_Float16)bf16_hi(u.w)};
 }
 
-// Group exchange: every 8-byte word carries a float and the sequence number
-// of the chunk that wrote it, stored with one single-copy-atomic 64-bit
-// agent-coherent (sc1) store.  A reader polls its own words until each
-// carries the sequence number it expects, so no flag, store-completion wait
-// or barrier orders the exchange: a word is either the old one (old number)
-// or the new one, never a mix.  Sequence numbers start at 1 and the buffers
-// are zeroed before every launch, so no word of an earlier call can match.
-// The buffers are thread-major: word e of thread t sits at e * stride + t,
-// so each store or load instruction of a wave covers 512 contiguous bytes
-// (whole lines: an agent-coherent store writes through L2), and every thread
-// reads back exactly the words the same thread of a partner wrote.  Two
-// parities double-buffer the chunks: a partner overwrites a slot two chunks
+// Group exchange: every 8-byte word carries two values and the low 8 bits
+// of the sequence number of the chunk that wrote them, stored with one
+// single-copy-atomic 64-bit agent-coherent (sc1) store.  A reader polls its
+// own words until each carries the tag it expects, so no flag,
+// store-completion wait or barrier orders the exchange: a word is either
+// the old one (old tag) or the new one, never a mix.  A value keeps the
+// sign, the exponent and the 19 leading mantissa bits of its fp32 form
+// (truncated: a relative error below 2^-19, far under the fp16 rounding the
+// exchanged sums go through next).  Two parities double-buffer the chunks,
+// so a slot holds the words of chunk seq - 2 (tag seq - 2, distinct from
+// seq mod 256) until it is rewritten; sequence numbers start at 1 and the
+// buffers are zeroed before every launch, and by the first chunk whose tag
+// is 0 (seq = 256) every slot has been written, so no word of an earlier
+// call or an unwritten slot can match.  The buffers are thread-major: word
+// e of thread t sits at e * stride + t, so each store or load instruction
+// of a wave covers 512 contiguous bytes (whole lines: an agent-coherent
+// store writes through L2), and a partner's thread reads back exactly the
+// words the same thread wrote.  A partner overwrites a slot two chunks
 // later, after having read this workgroup's next chunk, which this
 // workgroup writes only after reading the slot.
-__device__ __forceinline__ void tstore(unsigned long long* base, int idx, float v, unsigned tag) {
-  const unsigned long long wd = (unsigned long long)__float_as_uint(v) | ((unsigned long long)tag << 32);
-  __hip_atomic_store(base + idx, wd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ unsigned long long tword(float v0, float v1, unsigned tag) {
+  return ((unsigned long long)(tag & 0xffu) << 56) | ((unsigned long long)(__float_as_uint(v1) >> 4) << 28) |
+         (unsigned long long)(__float_as_uint(v0) >> 4);
+}
+__device__ __forceinline__ void tstore(unsigned long long* base, int idx, float v0, float v1, unsigned tag) {
+  __hip_atomic_store(base + idx, tword(v0, v1, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // words t, t + kStride, ..., t + (kW - 1) kStride of each of the kN bases,
 // until all carry `tag` (the loads of all bases are in flight together);
-// false = gave up after spin_max polls (spin_max = 0 gives up at once: the
-// failure-path test hook)
+// word e holds values 2e and 2e + 1 of out[b].  false = gave up after
+// spin_max polls (spin_max = 0 gives up at once: the failure-path test hook)
 template <int kStride, int kW, int kN>
 __device__ __forceinline__ bool tpoll(const unsigned long long* const (&base)[kN], int t, unsigned tag,
-                                      unsigned spin_max, float (&out)[kN][kW]) {
+                                      unsigned spin_max, float (&out)[kN][2 * kW]) {
   for (unsigned it = 0; it < spin_max; ++it) {
     unsigned long long wd[kN][kW];
 #pragma unroll
@@ -362,8 +371,9 @@ __device__ __forceinline__ bool tpoll(const unsigned long long* const (&base)[kN
     for (int b = 0; b < kN; ++b)
 #pragma unroll
       for (int e = 0; e < kW; ++e) {
-        out[b][e] = __uint_as_float((unsigned)wd[b][e]);
-        ok = ok && (unsigned)(wd[b][e] >> 32) == tag;
+        out[b][2 * e] = __uint_as_float((unsigned)(wd[b][e] & 0x0fffffffu) << 4);
+        out[b][2 * e + 1] = __uint_as_float((unsigned)((wd[b][e] >> 28) & 0x0fffffffu) << 4);
+        ok = ok && (unsigned)(wd[b][e] >> 56) == (tag & 0xffu);
       }
     if (ok) return true;
     __builtin_amdgcn_s_sleep(1);
@@ -621,19 +631,24 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
   // thread of it then sums kYPer elements (one row of 64 per wave and step)
   const int y_owner = (tj * kG) >> 2;
   const bool keeps_y = y_owner == h;
-  // element of the owner's rows of this lane's tile element (i, r)
+  // element of the owner's rows of this lane's tile element (i, r), and the
+  // exchange word holding its rows r = 2 rp, 2 rp + 1: word k carries rows
+  // 2 (k / 64), 2 (k / 64) + 1 of the owner's rows, column k % 64
   auto y_elem = [&](int i, int r) { return (16 * tj + 4 * g + r - C::kYRows * y_owner) * kD + 16 * (tc0 + i) + lc; };
+  auto y_word = [&](int i, int rp) {
+    return ((16 * tj + 4 * g - C::kYRows * y_owner) / 2 + rp) * kD + 16 * (tc0 + i) + lc;
+  };
   // the wave that produced tiles (tt, 2 kk) and (tt, 2 kk + 1) of a masked
   // score matrix, whose scale the kk-th K-step of a product over keys uses
   auto score_wave = [](int tt, int kk) { return (4 * tt + 2 * kk) / kT; };
 
   unsigned long long* xw = (unsigned long long*)(p.xbuf + (int64_t)grp * C::kGroupBytes);
   // O partials of workgroup wg, parity par
-  auto xO = [&](int wg, unsigned par) { return xw + ((int64_t)wg * 2 + par) * kThreads * kE; };
+  auto xO = [&](int wg, unsigned par) { return xw + ((int64_t)wg * 2 + par) * kThreads * (kE / 2); };
   // y partials sent by workgroup snd to its receiver slot sl
   // ((receiver - snd - 1) mod kG), parity par
   auto xY = [&](int snd, int sl, unsigned par) {
-    return xw + C::kXOWords + (((int64_t)snd * (kG - 1) + sl) * 2 + par) * C::kYElems;
+    return xw + C::kXOWords + (((int64_t)snd * (kG - 1) + sl) * 2 + par) * (C::kYElems / 2);
   };
   // the m-th partner in increasing order
   auto partner = [&](int m) { return m < h ? m : m + 1; };
@@ -660,8 +675,9 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
   unsigned seq = 0;         // sequence number of the current chunk (1, 2, ...)
   bool staged = false;      // the staging area holds the rows of the chunk about to start
 
-  // the partners' partials of this thread's y elements (tid + kThreads e of
-  // this workgroup's rows) for the chunk numbered `tag`
+  // the partners' partials of this thread's y elements for the chunk
+  // numbered `tag`: words tid + kThreads e, i.e. rows 2 (w + kWaves e) and
+  // 2 (w + kWaves e) + 1 of this workgroup's rows, column `lane`
   auto load_prev_y = [&](unsigned tag, float (&pv)[kG - 1][kYPer]) {
     const unsigned long long* bases[kG - 1];
 #pragma unroll
@@ -669,18 +685,18 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
       const int snd = partner(m);
       bases[m] = xY(snd, (h - snd - 1 + kG) % kG, tag & 1u);
     }
-    if (!tpoll<kThreads, kYPer, kG - 1>(bases, tid, tag, p.spin_max, pv)) give_up();
+    if (!tpoll<kThreads, kYPer / 2, kG - 1>(bases, tid, tag, p.spin_max, pv)) give_up();
   };
-  // the fixed-order sum of the group's partials, stored as bf16: element
-  // tid + kThreads e is row kYRows h + w + kWaves e, column `lane`
+  // the fixed-order sum of the group's partials, stored as bf16 (value
+  // 2e + q is row kYRows h + 2 (w + kWaves e) + q, column `lane`)
   auto finish_prev_y = [&](const float (&pv)[kG - 1][kYPer]) {
     float own[kYPer], sum[kYPer];
 #pragma unroll
-    for (int e = 0; e < kYPer; ++e) own[e] = ypark[e * kThreads + tid];
+    for (int e = 0; e < kYPer; ++e) own[e] = ypark[(2 * (w + kWaves * (e >> 1)) + (e & 1)) * kD + lane];
     ordered_sum<kG, kYPer>(h, own, pv, sum);
 #pragma unroll
     for (int e = 0; e < kYPer; ++e) {
-      const int j = C::kYRows * h + w + kWaves * e;
+      const int j = C::kYRows * h + 2 * (w + kWaves * (e >> 1)) + (e & 1);
       if (j < prev_n) p.y[(prev_row0 + j) * kD + lane] = __float2bfloat16(sum[e]);
     }
   };
@@ -888,7 +904,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
       // publish this workgroup's O (words tagged with this chunk's number)
       const unsigned par = seq & 1u;
 #pragma unroll
-      for (int e = 0; e < kE; ++e) tstore(xO(h, par), e * kThreads + tid, om[e], seq);
+      for (int e = 0; e < kE / 2; ++e) tstore(xO(h, par), e * kThreads + tid, om[2 * e], om[2 * e + 1], seq);
       STAMP(8);
 
       // ---- work that does not need the partner, while the exchange is in flight ----
@@ -1011,7 +1027,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
         const unsigned long long* bases[kG - 1];
 #pragma unroll
         for (int m = 0; m < kG - 1; ++m) bases[m] = xO(partner(m), par);
-        if (!tpoll<kThreads, kE, kG - 1>(bases, tid, seq, p.spin_max, pvv)) give_up();
+        if (!tpoll<kThreads, kE / 2, kG - 1>(bases, tid, seq, p.spin_max, pvv)) give_up();
       }
       if (prev_row0 >= 0) load_prev_y(seq - 1, pyv);
       // every vector memory operation of this thread done, the next chunk's
@@ -1306,7 +1322,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
 #pragma unroll
           for (int i = 0; i < kT; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) tstore(yb, y_elem(i, r), yv[4 * i + r], seq);
+            for (int rp = 0; rp < 2; ++rp) tstore(yb, y_word(i, rp), yv[4 * i + 2 * rp], yv[4 * i + 2 * rp + 1], seq);
         }
       }
       // the new state's maxima for the next chunk's operand scales (reduced
