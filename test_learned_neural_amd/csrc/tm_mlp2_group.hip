@@ -70,6 +70,7 @@ namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 64;
@@ -235,6 +236,27 @@ __device__ __forceinline__ h8 frag_c8(const _Float16* row, int kb, int g) {
 __device__ __forceinline__ h8 tiles_frag(const f4v a, const f4v b, float f) {
   return h8{(_Float16)(a[0] * f), (_Float16)(a[1] * f), (_Float16)(a[2] * f), (_Float16)(a[3] * f),
             (_Float16)(b[0] * f), (_Float16)(b[1] * f), (_Float16)(b[2] * f), (_Float16)(b[3] * f)};
+}
+
+// An fp16 column strip of four rows (rows row0 .. row0 + 3 of column col,
+// one value per row, as a lane holds an accumulator tile) stored as whole
+// dwords: the lanes of columns col and col ^ 1 (neighbours, a DPP pair) swap
+// halves, so the even lane writes rows row0, row0 + 1 and the odd lane rows
+// row0 + 2, row0 + 3, each dword holding both columns.  (One 2-byte store
+// per value, two lanes into each dword, measured several times slower.)
+// col's parity must be the lane's; all 64 lanes active.
+__device__ __forceinline__ void store_col4(_Float16* tile, int stride, int row0, int col, h4 v) {
+  const bool odd = col & 1;
+  const unsigned p01 = __builtin_bit_cast(unsigned, h2{v[0], v[1]});
+  const unsigned p23 = __builtin_bit_cast(unsigned, h2{v[2], v[3]});
+  const unsigned send = odd ? p01 : p23;
+  const unsigned recv = (unsigned)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+  const unsigned keep = odd ? p23 : p01;
+  const unsigned lo = odd ? recv : keep, hi = odd ? keep : recv;   // the even column's rows, the odd column's
+  const unsigned d0 = (lo & 0xffffu) | (hi << 16), d1 = (lo >> 16) | (hi & 0xffff0000u);
+  const int r = row0 + (odd ? 2 : 0), c = col & ~1;
+  *(unsigned*)(tile + r * stride + c) = d0;
+  *(unsigned*)(tile + (r + 1) * stride + c) = d1;
 }
 
 // ---- cross-lane helpers on DPP (no LDS traffic); call with all 64 lanes active ----
@@ -760,8 +782,24 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
           const h8 kv = bf16x8_to_h8(cr.k[rr]), qv = bf16x8_to_h8(cr.q[rr]);
           *(h8*)(sK + j * RS + cb) = kv;
           *(h8*)(sQ + j * RS + cb) = qv;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) sKT[(cb + i) * RS + j] = kv[i];
+          {
+            // tokens j and j ^ 1 sit in lanes l and l ^ 8: swap half the
+            // columns so each lane writes four dwords (both tokens)
+            const bool oddj = j & 1;
+            const unsigned k01 = __builtin_bit_cast(unsigned, h2{kv[0], kv[1]});
+            const unsigned k23 = __builtin_bit_cast(unsigned, h2{kv[2], kv[3]});
+            const unsigned k45 = __builtin_bit_cast(unsigned, h2{kv[4], kv[5]});
+            const unsigned k67 = __builtin_bit_cast(unsigned, h2{kv[6], kv[7]});
+            const unsigned r0 = (unsigned)__builtin_amdgcn_mov_dpp((int)(oddj ? k01 : k45), 0x128, 0xf, 0xf, false);
+            const unsigned r1 = (unsigned)__builtin_amdgcn_mov_dpp((int)(oddj ? k23 : k67), 0x128, 0xf, 0xf, false);
+            const unsigned e0 = oddj ? r0 : k01, e1 = oddj ? r1 : k23;   // even token's values of the four rows
+            const unsigned o0 = oddj ? k45 : r0, o1 = oddj ? k67 : r1;   // odd token's
+            _Float16* dst = sKT + (cb + (oddj ? 4 : 0)) * RS + (j & ~1);
+            *(unsigned*)(dst) = (e0 & 0xffffu) | (o0 << 16);
+            *(unsigned*)(dst + RS) = (e0 >> 16) | (o0 & 0xffff0000u);
+            *(unsigned*)(dst + 2 * RS) = (e1 & 0xffffu) | (o1 << 16);
+            *(unsigned*)(dst + 3 * RS) = (e1 >> 16) | (o1 & 0xffff0000u);
+          }
 #pragma unroll
           for (int i = 0; i < 8; ++i) kn = fmaxf(kn, fabsf((float)kv[i]));
         }
@@ -814,13 +852,14 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
       }
       // W2 and S2 copies [c][u] over the workgroup's units (for O and y)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int c = 16 * ct + 4 * g + r;
-          sW2[c * RW + uw + lc] = w2f[ct >> 1][4 * (ct & 1) + r];
-          sS2[c * RW + uw + lc] = (_Float16)(S2s[ct][r] * f2);
-        }
+      for (int ct = 0; ct < 4; ++ct) {
+        const h8 wf = w2f[ct >> 1];
+        const int o = 4 * (ct & 1);
+        store_col4(sW2, RW, 16 * ct + 4 * g, uw + lc, h4{wf[o], wf[o + 1], wf[o + 2], wf[o + 3]});
+        store_col4(sS2, RW, 16 * ct + 4 * g, uw + lc,
+                   h4{(_Float16)(S2s[ct][0] * f2), (_Float16)(S2s[ct][1] * f2), (_Float16)(S2s[ct][2] * f2),
+                      (_Float16)(S2s[ct][3] * f2)});
+      }
 
       // ================= a2: key-side forward Z1 = K W1^T (rows j, lanes u) =================
       // A1 = SiLU(Z1) and SiLU'(Z1) (fp16, for the backprop).  A1's
@@ -875,9 +914,11 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
 #pragma unroll
         for (int st = 0; st < 2; ++st) a1f[st] = tiles_frag(A1f[2 * st], A1f[2 * st + 1], fA1);
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sA1[(16 * tt + 4 * g + r) * RW + uw + lc] = a1f[tt >> 1][4 * (tt & 1) + r];
+        for (int tt = 0; tt < 4; ++tt) {
+          const h8 af = a1f[tt >> 1];
+          const int o = 4 * (tt & 1);
+          store_col4(sA1, RW, 16 * tt + 4 * g, uw + lc, h4{af[o], af[o + 1], af[o + 2], af[o + 3]});
+        }
       }
       STAMP(4);
       __syncthreads();   // every wave's A1 and W2/S2 copies
@@ -1066,8 +1107,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(d2v[4 * i + r] * fD2);
           *(h4*)(sD2T + (16 * (tc0 + i) + lc) * RS + 16 * tj + 4 * g) = hv;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sD2[(16 * tj + 4 * g + r) * RS + 16 * (tc0 + i) + lc] = hv[r];
+          store_col4(sD2, RS, 16 * tj + 4 * g, 16 * (tc0 + i) + lc, hv);
         }
       }
       // ---- first-layer masked scores SC1 = D o (Q K^T), tiles (tj, tc0 + i), this wave's own scale ----
@@ -1084,9 +1124,9 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
         const float fsc = pow2pos(esc);
 #pragma unroll
         for (int i = 0; i < kT; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            sSC[(16 * tj + 4 * g + r) * RS + 16 * (tc0 + i) + lc] = (_Float16)(sc[4 * i + r] * fsc);
+          store_col4(sSC, RS, 16 * tj + 4 * g, 16 * (tc0 + i) + lc,
+                     h4{(_Float16)(sc[4 * i] * fsc), (_Float16)(sc[4 * i + 1] * fsc), (_Float16)(sc[4 * i + 2] * fsc),
+                        (_Float16)(sc[4 * i + 3] * fsc)});
         if (lane == 0) ci[INT_ESC + w] = esc;
       }
       if (w == C::kWD0) {
@@ -1216,8 +1256,9 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
         const float fH = pow2pos(eH1);
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sH1[(16 * tt + 4 * g + r) * RW + uw + lc] = (_Float16)(H1f[tt][r] * fH);
+          store_col4(sH1, RW, 16 * tt + 4 * g, uw + lc,
+                     h4{(_Float16)(H1f[tt][0] * fH), (_Float16)(H1f[tt][1] * fH), (_Float16)(H1f[tt][2] * fH),
+                        (_Float16)(H1f[tt][3] * fH)});
       }
       STAMP(18);
       __syncthreads();   // every wave's H1 copy
@@ -1244,9 +1285,9 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
         const float fdp = pow2pos(edp);
 #pragma unroll
         for (int i = 0; i < kT; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            sSC[(16 * tj + 4 * g + r) * RS + 16 * (tc0 + i) + lc] = (_Float16)(pv[4 * i + r] * fdp);
+          store_col4(sSC, RS, 16 * tj + 4 * g, 16 * (tc0 + i) + lc,
+                     h4{(_Float16)(pv[4 * i] * fdp), (_Float16)(pv[4 * i + 1] * fdp), (_Float16)(pv[4 * i + 2] * fdp),
+                        (_Float16)(pv[4 * i + 3] * fdp)});
         if (lane == 0) ci[INT_EDP + w] = edp;
       }
 
