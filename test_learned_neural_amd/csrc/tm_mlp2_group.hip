@@ -86,11 +86,10 @@ constexpr unsigned kSpinMax = 1u << 21;
 // ---- LDS layout (bytes): the part common to both workgroup sizes ----
 constexpr int kT64 = kB * RS * 2;    // 9216
 constexpr int OFF_K = 0;             // K   [j][c]
-constexpr int OFF_KT = OFF_K + kT64;     // K^T [c][j]
-constexpr int OFF_Q = OFF_KT + kT64;     // Q   [j][c]
-constexpr int OFF_D2 = OFF_Q + kT64;     // Delta2   [j][c]
-constexpr int OFF_D2T = OFF_D2 + kT64;   // Delta2^T [c][j]
-constexpr int OFF_SC = OFF_D2T + kT64;   // masked scores [j][i]: first layer, then second
+constexpr int OFF_Q = OFF_K + kT64;      // Q   [j][c]
+constexpr int OFF_YP = OFF_Q + kT64;     // y partials parked across the chunk boundary (fp32)
+constexpr int OFF_D2T = OFF_YP + kT64;   // Delta2^T [c][j]
+constexpr int OFF_SC = OFF_D2T + kT64;   // masked scores [i][j] (keys i, queries j): first layer, then second
 constexpr int OFF_DM = OFF_SC + kT64;    // D [j][i] fp32
 // coefficient area (relative offsets)
 // float index: XT = the D recurrences' carried products at rows 31 and 63
@@ -123,12 +122,11 @@ struct Grp {
   static constexpr int kYPer = kYElems / kThreads;   // ... per thread
   static constexpr int kKSteps = kUG / 32;      // K-steps of a product over the workgroup's units
   static constexpr int kRowPasses = 512 / kThreads;   // 16-byte row pieces of a chunk tile per thread
-  static constexpr int RW = kUG + 8;            // fp16 row stride of the [j][u] / [c][u] tiles
-  static constexpr int kTU = kB * RW * 2;
-  static constexpr int OFF_A1 = OFF_DM + kB * RF * 4;   // A1 [j][u] over the workgroup's units
-  static constexpr int OFF_H1 = OFF_A1 + kTU;           // H1 [j][u]
-  static constexpr int OFF_W2 = OFF_H1 + kTU;           // W2 [c][u]
-  static constexpr int OFF_S2 = OFF_W2 + kTU;           // S2 [c][u]
+  static constexpr int kTU = kUG * RS * 2;
+  static constexpr int OFF_A1 = OFF_DM + kB * RF * 4;   // A1^T [u][j] over the workgroup's units
+  static constexpr int OFF_H1 = OFF_A1 + kTU;           // H1^T [u][j]
+  static constexpr int OFF_W2 = OFF_H1 + kTU;           // W2^T [u][c]
+  static constexpr int OFF_S2 = OFF_W2 + kTU;           // S2^T [u][c]
   static constexpr int OFF_COEF = OFF_S2 + kTU;
   static constexpr int OFF_STAGE = (OFF_COEF + kCoefBytes + 255) / 256 * 256;
   static constexpr int kLdsBytes = OFF_STAGE + kStageBytes;
@@ -143,7 +141,7 @@ struct Grp {
   static constexpr int kMaxGroups = 256 / kG;   // one workgroup per CU of a 256-CU device
   static_assert(NW == 8 || NW == 4, "eight or four waves");
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-  static_assert(kYElems * 4 <= kT64, "the parked y tiles fit the Delta2 area");
+  static_assert(kYElems * 4 <= kT64, "the parked y tiles fit their area");
   static_assert(kYPer * kThreads == kYElems && kYPer % 2 == 0, "every thread finishes the same number of y rows pairs");
 };
 
@@ -238,25 +236,39 @@ __device__ __forceinline__ h8 tiles_frag(const f4v a, const f4v b, float f) {
             (_Float16)(b[0] * f), (_Float16)(b[1] * f), (_Float16)(b[2] * f), (_Float16)(b[3] * f)};
 }
 
-// An fp16 column strip of four rows (rows row0 .. row0 + 3 of column col,
-// one value per row, as a lane holds an accumulator tile) stored as whole
-// dwords: the lanes of columns col and col ^ 1 (neighbours, a DPP pair) swap
-// halves, so the even lane writes rows row0, row0 + 1 and the odd lane rows
-// row0 + 2, row0 + 3, each dword holding both columns.  (One 2-byte store
-// per value, two lanes into each dword, measured several times slower.)
-// col's parity must be the lane's; all 64 lanes active.
-__device__ __forceinline__ void store_col4(_Float16* tile, int stride, int row0, int col, h4 v) {
-  const bool odd = col & 1;
-  const unsigned p01 = __builtin_bit_cast(unsigned, h2{v[0], v[1]});
-  const unsigned p23 = __builtin_bit_cast(unsigned, h2{v[2], v[3]});
-  const unsigned send = odd ? p01 : p23;
-  const unsigned recv = (unsigned)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
-  const unsigned keep = odd ? p23 : p01;
-  const unsigned lo = odd ? recv : keep, hi = odd ? keep : recv;   // the even column's rows, the odd column's
-  const unsigned d0 = (lo & 0xffffu) | (hi << 16), d1 = (lo >> 16) | (hi & 0xffff0000u);
-  const int r = row0 + (odd ? 2 : 0), c = col & ~1;
-  *(unsigned*)(tile + r * stride + c) = d0;
-  *(unsigned*)(tile + (r + 1) * stride + c) = d1;
+// Transposing fp16 reads from LDS (ds_read_b64_tr_b16).  The 16 lanes of
+// K group g read a 4 x 16 block of a row-major tile T (row stride S halves):
+// rows k0 .. k0 + 3, columns n0 .. n0 + 15, k0 the same for the group; lane
+// (g, lc) receives column n0 + lc of the four rows.  Lane j of a group
+// supplies the address of row k0 + j / 4, columns n0 + 4 (j % 4) .. + 3: the
+// instruction hands element e of lane i the (i % 4)-th value read by lane
+// 4e + i / 4 of its group (lane layout measured on gfx950).  Tiles consumed
+// with K along both of their dimensions are stored once, K-major, with one
+// 8-byte store per accumulator tile and lane (its four consecutive rows),
+// and read along the other dimension with these reads.
+__device__ __forceinline__ h4 tr4(const _Float16* T, int S, int k0, int n0, int lc) {
+  typedef __fp16 fp16x4 __attribute__((vector_size(8)));
+  typedef __attribute__((address_space(3))) fp16x4 lds_fp16x4;
+  return __builtin_bit_cast(
+      h4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(T + (k0 + (lc >> 2)) * S + n0 + 4 * (lc & 3))));
+}
+// operand fragment of row / column n0 + lc from a K-major tile: register
+// order (frag_rk) and consecutive order (frag_c8) of the K slots
+__device__ __forceinline__ h8 frag_tr_rk(const _Float16* T, int S, int kb, int n0, int g, int lc) {
+  const h4 lo = tr4(T, S, kb + 4 * g, n0, lc), hi = tr4(T, S, kb + 16 + 4 * g, n0, lc);
+  return h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ h8 frag_tr_c8(const _Float16* T, int S, int kb, int n0, int g, int lc) {
+  const h4 lo = tr4(T, S, kb + 8 * g, n0, lc), hi = tr4(T, S, kb + 8 * g + 4, n0, lc);
+  return h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+// the four consecutive rows of a lane's accumulator tile, stored K-major:
+// row `row` of T, columns col0 .. col0 + 3
+__device__ __forceinline__ void store_rows4(_Float16* T, int S, int row, int col0, h4 v) {
+  *(h4*)(T + row * S + col0) = v;
+}
+__device__ __forceinline__ h4 to_h4(const f4v v, float f) {
+  return h4{(_Float16)(v[0] * f), (_Float16)(v[1] * f), (_Float16)(v[2] * f), (_Float16)(v[3] * f)};
 }
 
 // ---- cross-lane helpers on DPP (no LDS traffic); call with all 64 lanes active ----
@@ -566,14 +578,12 @@ template <bool kRW, int NW>
 __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
   using C = Grp<NW>;
   constexpr int kWaves = C::kWaves, kThreads = C::kThreads, kUG = C::kUG, kG = C::kG, kT = C::kT, kE = C::kE;
-  constexpr int kYPer = C::kYPer, RW = C::RW;
+  constexpr int kYPer = C::kYPer;
   constexpr int OFF_A1 = C::OFF_A1, OFF_H1 = C::OFF_H1, OFF_W2 = C::OFF_W2, OFF_S2 = C::OFF_S2,
                 OFF_COEF = C::OFF_COEF, OFF_STAGE = C::OFF_STAGE;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   _Float16* sK = (_Float16*)(smem + OFF_K);
-  _Float16* sKT = (_Float16*)(smem + OFF_KT);
   _Float16* sQ = (_Float16*)(smem + OFF_Q);
-  _Float16* sD2 = (_Float16*)(smem + OFF_D2);
   _Float16* sD2T = (_Float16*)(smem + OFF_D2T);
   _Float16* sSC = (_Float16*)(smem + OFF_SC);
   float* sDM = (float*)(smem + OFF_DM);
@@ -686,12 +696,10 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
 
   // The y tiles of the previous chunk a keeping thread finishes (rows
   // 16 tj + 4g + r, columns 16 (tc0 + i) + lc) wait across the chunk
-  // boundary in the Delta2 [j][c] area of LDS, whose only reader is the
-  // backprop product: it is free from there until the next chunk writes
-  // Delta2, after its exchange.  Registers would be spilled across the
-  // boundary, and every reload from scratch would wait for the exchange
+  // boundary in an LDS area of their own.  Registers would be spilled across
+  // the boundary, and every reload from scratch would wait for the exchange
   // stores in flight.
-  float* ypark = (float*)(smem + OFF_D2);   // kYElems floats: this workgroup's partial of its y rows
+  float* ypark = (float*)(smem + OFF_YP);   // kYElems floats: this workgroup's partial of its y rows
   int64_t prev_row0 = -1;   // global token row of the previous chunk's first token
   int prev_n = 0;
   unsigned seq = 0;         // sequence number of the current chunk (1, 2, ...)
@@ -767,7 +775,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
       (void)stamp_slot;
       STAMP(0);
 
-      // ================= the chunk's K, K^T, Q (fp16) and gates into LDS =================
+      // ================= the chunk's K, Q (fp16) and gates into LDS =================
       {
         // (this thread's staging loads were waited for after the previous
         // chunk's exchange; waiting here would also wait for the y exchange
@@ -782,24 +790,6 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
           const h8 kv = bf16x8_to_h8(cr.k[rr]), qv = bf16x8_to_h8(cr.q[rr]);
           *(h8*)(sK + j * RS + cb) = kv;
           *(h8*)(sQ + j * RS + cb) = qv;
-          {
-            // tokens j and j ^ 1 sit in lanes l and l ^ 8: swap half the
-            // columns so each lane writes four dwords (both tokens)
-            const bool oddj = j & 1;
-            const unsigned k01 = __builtin_bit_cast(unsigned, h2{kv[0], kv[1]});
-            const unsigned k23 = __builtin_bit_cast(unsigned, h2{kv[2], kv[3]});
-            const unsigned k45 = __builtin_bit_cast(unsigned, h2{kv[4], kv[5]});
-            const unsigned k67 = __builtin_bit_cast(unsigned, h2{kv[6], kv[7]});
-            const unsigned r0 = (unsigned)__builtin_amdgcn_mov_dpp((int)(oddj ? k01 : k45), 0x128, 0xf, 0xf, false);
-            const unsigned r1 = (unsigned)__builtin_amdgcn_mov_dpp((int)(oddj ? k23 : k67), 0x128, 0xf, 0xf, false);
-            const unsigned e0 = oddj ? r0 : k01, e1 = oddj ? r1 : k23;   // even token's values of the four rows
-            const unsigned o0 = oddj ? k45 : r0, o1 = oddj ? k67 : r1;   // odd token's
-            _Float16* dst = sKT + (cb + (oddj ? 4 : 0)) * RS + (j & ~1);
-            *(unsigned*)(dst) = (e0 & 0xffffu) | (o0 << 16);
-            *(unsigned*)(dst + RS) = (e0 >> 16) | (o0 & 0xffff0000u);
-            *(unsigned*)(dst + 2 * RS) = (e1 & 0xffffu) | (o1 << 16);
-            *(unsigned*)(dst + 3 * RS) = (e1 >> 16) | (o1 & 0xffff0000u);
-          }
 #pragma unroll
           for (int i = 0; i < 8; ++i) kn = fmaxf(kn, fabsf((float)kv[i]));
         }
@@ -850,15 +840,13 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
         s1f[st] = tiles_frag(S1s[2 * st], S1s[2 * st + 1], f1);
         w2f[st] = tiles_frag(W2s[2 * st], W2s[2 * st + 1], f2);
       }
-      // W2 and S2 copies [c][u] over the workgroup's units (for O and y)
+      // W2^T and S2^T copies [u][c] over the workgroup's units (for O and y)
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         const h8 wf = w2f[ct >> 1];
         const int o = 4 * (ct & 1);
-        store_col4(sW2, RW, 16 * ct + 4 * g, uw + lc, h4{wf[o], wf[o + 1], wf[o + 2], wf[o + 3]});
-        store_col4(sS2, RW, 16 * ct + 4 * g, uw + lc,
-                   h4{(_Float16)(S2s[ct][0] * f2), (_Float16)(S2s[ct][1] * f2), (_Float16)(S2s[ct][2] * f2),
-                      (_Float16)(S2s[ct][3] * f2)});
+        store_rows4(sW2, RS, uw + lc, 16 * ct + 4 * g, h4{wf[o], wf[o + 1], wf[o + 2], wf[o + 3]});
+        store_rows4(sS2, RS, uw + lc, 16 * ct + 4 * g, to_h4(S2s[ct], f2));
       }
 
       // ================= a2: key-side forward Z1 = K W1^T (rows j, lanes u) =================
@@ -910,14 +898,14 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
           }
         }
         // A1 fragments (register order over the tokens) for the second-layer
-        // fold, and the copy [j][u] for O and the scores
+        // fold, and the copy [u][j] for O and the scores
 #pragma unroll
         for (int st = 0; st < 2; ++st) a1f[st] = tiles_frag(A1f[2 * st], A1f[2 * st + 1], fA1);
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
           const h8 af = a1f[tt >> 1];
           const int o = 4 * (tt & 1);
-          store_col4(sA1, RW, 16 * tt + 4 * g, uw + lc, h4{af[o], af[o + 1], af[o + 2], af[o + 3]});
+          store_rows4(sA1, RS, uw + lc, 16 * tt + 4 * g, h4{af[o], af[o + 1], af[o + 2], af[o + 3]});
         }
       }
       STAMP(4);
@@ -933,11 +921,10 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < kT; ++i) {
           f4v acc = {};
-          const _Float16* arow = sA1 + (16 * tj + lc) * RW;
-          const _Float16* brow = sW2 + (16 * (tc0 + i) + lc) * RW;
 #pragma unroll
           for (int kk = 0; kk < C::kKSteps; ++kk)
-            acc = mfma(frag_c8(arow, 32 * kk, g), frag_c8(brow, 32 * kk, g), acc);
+            acc = mfma(frag_tr_c8(sA1, RS, 32 * kk, 16 * tj, g, lc), frag_tr_c8(sW2, RS, 32 * kk, 16 * (tc0 + i), g, lc),
+                       acc);
 #pragma unroll
           for (int r = 0; r < 4; ++r) om[4 * i + r] = acc[r] * co;
         }
@@ -1097,7 +1084,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
       if (ci[INT_FAIL]) { failed = true; break; }
       STAMP(12);
 
-      // ---- Delta2 (fp16, workgroup-wide scale) as [j][c] and [c][j] ----
+      // ---- Delta2 (fp16, workgroup-wide scale) as [c][j] ----
       const int eD2 = scale_exp(__uint_as_float((unsigned)ci[INT_AMAX_D2]));
       {
         const float fD2 = pow2pos(eD2);
@@ -1107,7 +1094,6 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(d2v[4 * i + r] * fD2);
           *(h4*)(sD2T + (16 * (tc0 + i) + lc) * RS + 16 * tj + 4 * g) = hv;
-          store_col4(sD2, RS, 16 * tj + 4 * g, 16 * (tc0 + i) + lc, hv);
         }
       }
       // ---- first-layer masked scores SC1 = D o (Q K^T), tiles (tj, tc0 + i), this wave's own scale ----
@@ -1124,9 +1110,9 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
         const float fsc = pow2pos(esc);
 #pragma unroll
         for (int i = 0; i < kT; ++i)
-          store_col4(sSC, RS, 16 * tj + 4 * g, 16 * (tc0 + i) + lc,
-                     h4{(_Float16)(sc[4 * i] * fsc), (_Float16)(sc[4 * i + 1] * fsc), (_Float16)(sc[4 * i + 2] * fsc),
-                        (_Float16)(sc[4 * i + 3] * fsc)});
+          store_rows4(sSC, RS, 16 * (tc0 + i) + lc, 16 * tj + 4 * g,
+                      h4{(_Float16)(sc[4 * i] * fsc), (_Float16)(sc[4 * i + 1] * fsc), (_Float16)(sc[4 * i + 2] * fsc),
+                         (_Float16)(sc[4 * i + 3] * fsc)});
         if (lane == 0) ci[INT_ESC + w] = esc;
       }
       if (w == C::kWD0) {
@@ -1158,9 +1144,8 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
           f4v acc = {};
-          const _Float16* arow = sD2 + (16 * tt + lc) * RS;
 #pragma unroll
-          for (int st = 0; st < 2; ++st) acc = mfma(frag_rk(arow, 32 * st, g), w2f[st], acc);
+          for (int st = 0; st < 2; ++st) acc = mfma(frag_tr_rk(sD2T, RS, 32 * st, 16 * tt, g, lc), w2f[st], acc);
 #pragma unroll
           for (int r = 0; r < 4; ++r) Df[tt][r] = acc[r] * dun * (float)SPh[tt][r];
           am = max4(am, Df[tt]);
@@ -1182,10 +1167,9 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
           f4v z;
           if constexpr (kRW) {
             // the masked term's two K-steps carry the scales of the waves that produced them
-            const _Float16* srow = sSC + (16 * tt + lc) * RS;
             f4v m0 = {}, m1v = {};
-            m0 = mfma(frag_rk(srow, 0, g), d1f[0], m0);
-            m1v = mfma(frag_rk(srow, 32, g), d1f[1], m1v);
+            m0 = mfma(frag_tr_rk(sSC, RS, 0, 16 * tt, g, lc), d1f[0], m0);
+            m1v = mfma(frag_tr_rk(sSC, RS, 32, 16 * tt, g, lc), d1f[1], m1v);
             const float c30 = pow2neg(eD1 + ci[INT_ESC + score_wave(tt, 0)]),
                         c31 = pow2neg(eD1 + ci[INT_ESC + score_wave(tt, 1)]);
             const f4v av = *(const f4v*)(cf + COEF_A + 16 * tt + 4 * g);
@@ -1226,8 +1210,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
         const h8 bd0 = d1f[0] * wdf[0], bd1 = d1f[1] * wdf[1];
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-          const _Float16* arow = sKT + (16 * ct + lc) * RS;
-          const h8 k0 = frag_rk(arow, 0, g), k1 = frag_rk(arow, 32, g);
+          const h8 k0 = frag_tr_rk(sK, RS, 0, 16 * ct, g, lc), k1 = frag_tr_rk(sK, RS, 32, 16 * ct, g, lc);
           f4v gU = {}, gD = {};
           gU = mfma(k0, bu0, gU);
           gU = mfma(k1, bu1, gU);
@@ -1246,7 +1229,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
       STAMP(17);
       __syncthreads();   // every wave's H1 maximum
 
-      // H1 with the workgroup-wide scale, copied [j][u] for the scores and y
+      // H1 with the workgroup-wide scale, copied [u][j] for the scores and y
       int eH1;
       {
         float mm = 0.f;
@@ -1256,9 +1239,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
         const float fH = pow2pos(eH1);
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
-          store_col4(sH1, RW, 16 * tt + 4 * g, uw + lc,
-                     h4{(_Float16)(H1f[tt][0] * fH), (_Float16)(H1f[tt][1] * fH), (_Float16)(H1f[tt][2] * fH),
-                        (_Float16)(H1f[tt][3] * fH)});
+          store_rows4(sH1, RS, uw + lc, 16 * tt + 4 * g, to_h4(H1f[tt], fH));
       }
       STAMP(18);
       __syncthreads();   // every wave's H1 copy
@@ -1271,11 +1252,10 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < kT; ++i) {
           f4v acc = {};
-          const _Float16* arow = sH1 + (16 * tj + lc) * RW;
-          const _Float16* brow = sA1 + (16 * (tc0 + i) + lc) * RW;
 #pragma unroll
           for (int kk = 0; kk < C::kKSteps; ++kk)
-            acc = mfma(frag_c8(arow, 32 * kk, g), frag_c8(brow, 32 * kk, g), acc);
+            acc = mfma(frag_tr_c8(sH1, RS, 32 * kk, 16 * tj, g, lc), frag_tr_c8(sA1, RS, 32 * kk, 16 * (tc0 + i), g, lc),
+                       acc);
           const f4v dt = d_tile(tj, tc0 + i);
 #pragma unroll
           for (int r = 0; r < 4; ++r) pv[4 * i + r] = acc[r] * cp * dt[r];
@@ -1285,9 +1265,9 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
         const float fdp = pow2pos(edp);
 #pragma unroll
         for (int i = 0; i < kT; ++i)
-          store_col4(sSC, RS, 16 * tj + 4 * g, 16 * (tc0 + i) + lc,
-                     h4{(_Float16)(pv[4 * i] * fdp), (_Float16)(pv[4 * i + 1] * fdp), (_Float16)(pv[4 * i + 2] * fdp),
-                        (_Float16)(pv[4 * i + 3] * fdp)});
+          store_rows4(sSC, RS, 16 * (tc0 + i) + lc, 16 * tj + 4 * g,
+                      h4{(_Float16)(pv[4 * i] * fdp), (_Float16)(pv[4 * i + 1] * fdp), (_Float16)(pv[4 * i + 2] * fdp),
+                         (_Float16)(pv[4 * i + 3] * fdp)});
         if (lane == 0) ci[INT_EDP + w] = edp;
       }
 
@@ -1326,20 +1306,18 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
         const f4v fv = *(const f4v*)(cf + COEF_F + 16 * tj + 4 * g);
 #pragma unroll
         for (int i = 0; i < kT; ++i) {
-          const _Float16* arow = sH1 + (16 * tj + lc) * RW;
           const int crow = 16 * (tc0 + i) + lc;
           f4v aw = {}, as = {};
 #pragma unroll
           for (int kk = 0; kk < C::kKSteps; ++kk) {
-            const h8 hf = frag_c8(arow, 32 * kk, g);
-            aw = mfma(hf, frag_c8(sW2 + crow * RW, 32 * kk, g), aw);
-            if constexpr (kRW) as = mfma(hf, frag_c8(sS2 + crow * RW, 32 * kk, g), as);
+            const h8 hf = frag_tr_c8(sH1, RS, 32 * kk, 16 * tj, g, lc);
+            aw = mfma(hf, frag_tr_c8(sW2, RS, 32 * kk, 16 * (tc0 + i), g, lc), aw);
+            if constexpr (kRW) as = mfma(hf, frag_tr_c8(sS2, RS, 32 * kk, 16 * (tc0 + i), g, lc), as);
           }
           if constexpr (kRW) {
-            const _Float16* drow = sSC + (16 * tj + lc) * RS;
             f4v m0 = {}, m1v = {};
-            m0 = mfma(frag_c8(drow, 0, g), frag_c8(sD2T + crow * RS, 0, g), m0);
-            m1v = mfma(frag_c8(drow, 32, g), frag_c8(sD2T + crow * RS, 32, g), m1v);
+            m0 = mfma(frag_tr_c8(sSC, RS, 0, 16 * tj, g, lc), frag_c8(sD2T + crow * RS, 0, g), m0);
+            m1v = mfma(frag_tr_c8(sSC, RS, 32, 16 * tj, g, lc), frag_c8(sD2T + crow * RS, 32, g), m1v);
             const float c30 = pow2neg(eD2 + ci[INT_EDP + score_wave(tj, 0)]),
                         c31 = pow2neg(eD2 + ci[INT_EDP + score_wave(tj, 1)]);
 #pragma unroll
