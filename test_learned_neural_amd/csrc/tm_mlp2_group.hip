@@ -535,15 +535,23 @@ __device__ void poison_group_streams(const Params& p, int grp, int tid) {
   }
 }
 
+// max(m, |a|, |b|) as one v_max3_f32 with absolute-value source modifiers.
+// (fmaxf on values the compiler cannot prove quiet costs a canonicalising
+// max per element first.)  These maxima only set operand scales; no NaN
+// reaches them from valid inputs.
+__device__ __forceinline__ float amax3(float m, float a, float b) {
+  float r;
+  asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(r) : "v"(m), "v"(a), "v"(b));
+  return r;
+}
 template <int kW>
 __device__ __forceinline__ float max_abs(float m, const float (&x)[kW]) {
+  static_assert(kW % 2 == 0, "pairs");
 #pragma unroll
-  for (int e = 0; e < kW; ++e) m = fmaxf(m, fabsf(x[e]));
+  for (int e = 0; e < kW; e += 2) m = amax3(m, x[e], x[e + 1]);
   return m;
 }
-__device__ __forceinline__ float max4(float m, f4v x) {
-  return fmaxf(fmaxf(m, fmaxf(fabsf(x[0]), fabsf(x[1]))), fmaxf(fabsf(x[2]), fabsf(x[3])));
-}
+__device__ __forceinline__ float max4(float m, f4v x) { return amax3(amax3(m, x[0], x[1]), x[2], x[3]); }
 
 // The group's partial sums added in the fixed order of the workgroups
 // (0 + 1 + ... + kG-1), identical in every workgroup: `own` is workgroup h's
@@ -739,8 +747,8 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
     // W2s[ct]: rows c = 16 ct + 4g + r, lanes u = hs + lc   (W2[c][u])
     f4v W1s[4], S1s[4], W2s[4], S2s[4];
     {
-      float m1 = 0.f, m2 = 0.f;   // this lane's max |W|,|S| per layer (for the operand scales)
-      float n1 = 0.f;             // this lane's max |W1| (a bound on the A1 scale)
+      float m1 = 0.f, m2 = 0.f;   // this lane's max |S1| and max |W2|,|S2| (for the operand scales)
+      float n1 = 0.f;             // this lane's max |W1| (a bound on the A1 scale; with m1, the layer-1 scale)
       const float* Wi = p.W_in + (int64_t)s * kP;
       const float* Si = p.S_in + (int64_t)s * kP;
       const int u = hs + lc;
@@ -749,8 +757,8 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
         const int c = 16 * ct + 4 * g;
         W1s[ct] = *(const f4v*)(Wi + u * kD + c);
         S1s[ct] = *(const f4v*)(Si + u * kD + c);
-        m1 = max4(max4(m1, W1s[ct]), S1s[ct]);
         n1 = max4(n1, W1s[ct]);
+        m1 = max4(m1, S1s[ct]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           W2s[ct][r] = Wi[kH * kD + (c + r) * kH + u];
@@ -758,7 +766,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
         }
         m2 = max4(max4(m2, W2s[ct]), S2s[ct]);
       }
-      const float wm1 = wave_max(m1), wm2 = wave_max(m2), wn1 = wave_max(n1);
+      const float wn1 = wave_max(n1), wm1 = fmaxf(wave_max(m1), wn1), wm2 = wave_max(m2);
       if (lane == 0) {
         ci[INT_M1 + w] = __float_as_int(wm1);
         ci[INT_M2 + w] = __float_as_int(wm2);
@@ -787,11 +795,14 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
 #pragma unroll
         for (int rr = 0; rr < C::kRowPasses; ++rr) {
           const int piece = tid + rr * kThreads, j = piece >> 3, cb = (piece & 7) * 8;
-          const h8 kv = bf16x8_to_h8(cr.k[rr]), qv = bf16x8_to_h8(cr.q[rr]);
+          const uint4 ku = cr.k[rr];
+          const h8 kv = bf16x8_to_h8(ku), qv = bf16x8_to_h8(cr.q[rr]);
+          // max |K| from the bf16 values: their fp16 conversion is exact in
+          // fp16's normal range, and the A1 bound leaves a factor 4 of headroom
+          kn = amax3(amax3(kn, bf16_lo(ku.x), bf16_hi(ku.x)), bf16_lo(ku.y), bf16_hi(ku.y));
+          kn = amax3(amax3(kn, bf16_lo(ku.z), bf16_hi(ku.z)), bf16_lo(ku.w), bf16_hi(ku.w));
           *(h8*)(sK + j * RS + cb) = kv;
           *(h8*)(sQ + j * RS + cb) = qv;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) kn = fmaxf(kn, fabsf((float)kv[i]));
         }
         if (tid < kB) {
           cf[COEF_THETA + tid] = cr.gt;
@@ -1194,7 +1205,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
       STAMP(16);
       const float An = cf[COEF_A + n - 1], En = cf[COEF_E + n - 1], Fn = cf[COEF_F + n - 1];
       const int ewU = ci[INT_EWU], ewD = ci[INT_EWD];
-      float m1n = 0.f, m2n = 0.f, n1n = 0.f;   // the new state's maxima (n1n: of |W1| alone)
+      float m1n = 0.f, m2n = 0.f, n1n = 0.f;   // the new state's maxima of |S1|, |W2| and |S2|, |W1|
       // the fold weights as fragments in register order over the tokens
       h8 wuf[2], wdf[2];
 #pragma unroll
@@ -1222,8 +1233,8 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
             W1s[ct][r] = fmaf(gD[r], -uD1, fmaf(An, w0, Fn * s0));
             S1s[ct][r] = fmaf(gU[r], -uU1, En * s0);
           }
-          m1n = max4(max4(m1n, W1s[ct]), S1s[ct]);
           n1n = max4(n1n, W1s[ct]);
+          m1n = max4(m1n, S1s[ct]);
         }
       }
       STAMP(17);
@@ -1347,7 +1358,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
       // the new state's maxima for the next chunk's operand scales (reduced
       // here, once the fold's products have long completed)
       {
-        const float wm1 = wave_max(m1n), wn1 = wave_max(n1n), wm2 = wave_max(m2n);
+        const float wn1 = wave_max(n1n), wm1 = fmaxf(wave_max(m1n), wn1), wm2 = wave_max(m2n);
         if (lane == 0) {
           ci[INT_M1 + w] = __float_as_int(wm1);
           ci[INT_N1 + w] = __float_as_int(wn1);
