@@ -213,6 +213,15 @@ __device__ __forceinline__ f4v mfma(h8 a, h8 b, f4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// x f rounded to fp16 as a multiply and a conversion (two values share one
+// v_cvt_pk_f16_f32).  The empty asm keeps the compiler from fusing the pair
+// into v_fma_mix, which issues more slowly on this hardware.
+__device__ __forceinline__ _Float16 sc16(float x, float f) {
+  float y = x * f;
+  asm("" : "+v"(y));
+  return (_Float16)y;
+}
+
 // Operand fragments of v_mfma_f32_16x16x32_f16.  Lane l serves row (A) or
 // column (B) l & 15 and K group g = l >> 4 with 8 values.  Two orders of the
 // K slots are used (any order works if both operands of a product agree):
@@ -232,8 +241,8 @@ __device__ __forceinline__ h8 frag_c8(const _Float16* row, int kb, int g) {
 // two accumulator tiles (rows 0-15 and 16-31 of a K block) as a
 // register-order fragment, scaled to fp16
 __device__ __forceinline__ h8 tiles_frag(const f4v a, const f4v b, float f) {
-  return h8{(_Float16)(a[0] * f), (_Float16)(a[1] * f), (_Float16)(a[2] * f), (_Float16)(a[3] * f),
-            (_Float16)(b[0] * f), (_Float16)(b[1] * f), (_Float16)(b[2] * f), (_Float16)(b[3] * f)};
+  return h8{sc16(a[0], f), sc16(a[1], f), sc16(a[2], f), sc16(a[3], f),
+            sc16(b[0], f), sc16(b[1], f), sc16(b[2], f), sc16(b[3], f)};
 }
 
 // Transposing fp16 reads from LDS (ds_read_b64_tr_b16).  The 16 lanes of
@@ -268,7 +277,7 @@ __device__ __forceinline__ void store_rows4(_Float16* T, int S, int row, int col
   *(h4*)(T + row * S + col0) = v;
 }
 __device__ __forceinline__ h4 to_h4(const f4v v, float f) {
-  return h4{(_Float16)(v[0] * f), (_Float16)(v[1] * f), (_Float16)(v[2] * f), (_Float16)(v[3] * f)};
+  return h4{sc16(v[0], f), sc16(v[1], f), sc16(v[2], f), sc16(v[3], f)};
 }
 
 // ---- cross-lane helpers on DPP (no LDS traffic); call with all 64 lanes active ----
@@ -873,7 +882,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
       // rounding of W1.
       int eA1;
       h8 a1f[2];
-      h4 SPh[4];
+      f4v SPh[4];   // SiLU'(Z1), fp32
       {
         float mn1 = 0.f, mnk = 0.f;
 #pragma unroll
@@ -905,7 +914,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
             const float sg = sigmoidf_(zz);
             const float a = zz * sg;
             A1f[tt][r] = a;
-            SPh[tt][r] = (_Float16)(sg + a * (1.f - sg));   // s (1 + z (1 - s))
+            SPh[tt][r] = fmaf(a, 1.f - sg, sg);   // s (1 + z (1 - s))
           }
         }
         // A1 fragments (register order over the tokens) for the second-layer
@@ -1103,7 +1112,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
         for (int i = 0; i < kT; ++i) {
           h4 hv;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) hv[r] = (_Float16)(d2v[4 * i + r] * fD2);
+          for (int r = 0; r < 4; ++r) hv[r] = sc16(d2v[4 * i + r], fD2);
           *(h4*)(sD2T + (16 * (tc0 + i) + lc) * RS + 16 * tj + 4 * g) = hv;
         }
       }
@@ -1122,8 +1131,8 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < kT; ++i)
           store_rows4(sSC, RS, 16 * (tc0 + i) + lc, 16 * tj + 4 * g,
-                      h4{(_Float16)(sc[4 * i] * fsc), (_Float16)(sc[4 * i + 1] * fsc), (_Float16)(sc[4 * i + 2] * fsc),
-                         (_Float16)(sc[4 * i + 3] * fsc)});
+                      h4{sc16(sc[4 * i], fsc), sc16(sc[4 * i + 1], fsc), sc16(sc[4 * i + 2], fsc),
+                         sc16(sc[4 * i + 3], fsc)});
         if (lane == 0) ci[INT_ESC + w] = esc;
       }
       if (w == C::kWD0) {
@@ -1158,7 +1167,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
 #pragma unroll
           for (int st = 0; st < 2; ++st) acc = mfma(frag_tr_rk(sD2T, RS, 32 * st, 16 * tt, g, lc), w2f[st], acc);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) Df[tt][r] = acc[r] * dun * (float)SPh[tt][r];
+          for (int r = 0; r < 4; ++r) Df[tt][r] = acc[r] * dun * SPh[tt][r];
           am = max4(am, Df[tt]);
         }
         eD1 = scale_exp(wave_max(am));
@@ -1277,8 +1286,8 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < kT; ++i)
           store_rows4(sSC, RS, 16 * (tc0 + i) + lc, 16 * tj + 4 * g,
-                      h4{(_Float16)(pv[4 * i] * fdp), (_Float16)(pv[4 * i + 1] * fdp), (_Float16)(pv[4 * i + 2] * fdp),
-                         (_Float16)(pv[4 * i + 3] * fdp)});
+                      h4{sc16(pv[4 * i], fdp), sc16(pv[4 * i + 1], fdp), sc16(pv[4 * i + 2], fdp),
+                         sc16(pv[4 * i + 3], fdp)});
         if (lane == 0) ci[INT_EDP + w] = edp;
       }
 

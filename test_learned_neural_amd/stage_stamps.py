@@ -117,7 +117,7 @@ def isa():
     print(f"  {'total':<62s}" + "".join(f"{tot[c]:7d}" for c in classes))
 
 
-def run(steps: int = 2):
+def run(steps: int = 2, per_wave: bool = False):
     import numpy as np
     import torch
     sys.path.insert(0, ROOT)
@@ -151,6 +151,10 @@ def run(steps: int = 2):
     for k in range(STAGES - 1):
         row = med[:, k]
         print(f"  {k + 1:2d} {STAGE_NAMES[k]:<58s} {row.min():7.0f} {np.median(row):7.0f} {row.max():7.0f}")
+    if per_wave:
+        print("  per wave (median over chunks), waves 0..%d:" % (WAVES - 1))
+        for k in range(STAGES - 1):
+            print(f"  {k + 1:2d} " + " ".join(f"{v:6.0f}" for v in med[:, k]))
     nxt = np.median(st[1:, :, 0] - st[:-1, :, 0], axis=0)
     print(f"  chunk (stamp 0 to stamp 23): {np.median(total):.0f} cycles; chunk to chunk: {np.median(nxt):.0f} cycles")
 
@@ -159,5 +163,6 @@ if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--build", action="store_true")
     ap.add_argument("--isa", action="store_true")
+    ap.add_argument("--per-wave", action="store_true", help="also print every wave's median per stage")
     a = ap.parse_args()
-    build() if a.build else isa() if a.isa else run()
+    build() if a.build else isa() if a.isa else run(per_wave=a.per_wave)
