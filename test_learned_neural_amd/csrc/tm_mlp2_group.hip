@@ -43,7 +43,9 @@
 //   barriers of one wave overlap the matrix work of the other.
 // * Every MFMA operand is fp16 with a power-of-two scale per operand block
 //   and chunk (fp32 accumulation, exact rescaling): the state, the
-//   activations and the residuals.  Scores produced by one wave and consumed
+//   activations and the residuals (A1 and H1, computed in units of -1/ln 2
+//   for their SiLUs, are converted back by their fp16 conversion factor).
+//   Scores produced by one wave and consumed
 //   in one K-step carry that wave's own scale, so they need no workgroup-wide
 //   maximum.
 // * The pair exchanges its partial sums through global memory in 8-byte
@@ -152,7 +154,7 @@ constexpr int INT_M2 = 8;     // per-wave maxima of |W2|, |S2| (8 slots)
 // chunk, or at the stream's start, and read after the next chunk's first
 // barrier: no per-lane value is carried across the chunk boundary)
 constexpr int INT_N1 = 16;    // per-wave maxima of |W1| (a bound on the A1 scale)
-constexpr int INT_MH1 = 24;   // per-wave maxima of |H1|
+constexpr int INT_MH1 = 24;   // per-wave maxima of |H1| log2 e
 constexpr int INT_ESC = 32;   // per-wave exponents of the first-layer masked scores
 constexpr int INT_EDP = 40;   // per-wave exponents of the second-layer masked scores
 constexpr int INT_NK = 48;    // per-wave maxima of |K|
@@ -359,7 +361,11 @@ __device__ __forceinline__ float pow2neg(int k) { return ldexpf(1.f, -max(k, -12
 // but still far below every tolerance floor.
 __device__ __forceinline__ float pow2pos(int e) { return ldexpf(1.f, min(e, 127)); }
 
-__device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+// The SiLUs take their argument in units of -1/ln 2 (x = -z log2 e, folded
+// into the scale that unscales z), so that sigmoid(z) = 1 / (1 + 2^x) needs
+// no multiply before the exponential.
+constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+__device__ __forceinline__ float sigmoid_x(float x) { return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x)); }
 
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
@@ -901,7 +907,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
         }
         const float fA1 = pow2pos(eA1);
         f4v A1f[4];
-        const float zun = pow2neg(e1);
+        const float cx = pow2neg(e1) * -kLog2e;   // Z1 in units of -1/ln 2
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
           f4v z = {};
@@ -910,17 +916,17 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
           for (int st = 0; st < 2; ++st) z = mfma(frag_rk(krow, 32 * st, g), w1f[st], z);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float zz = z[r] * zun;
-            const float sg = sigmoidf_(zz);
-            const float a = zz * sg;
-            A1f[tt][r] = a;
-            SPh[tt][r] = fmaf(a, 1.f - sg, sg);   // s (1 + z (1 - s))
+            const float x = z[r] * cx;
+            const float sg = sigmoid_x(x);
+            const float xs = x * sg;                          // -A1 log2 e
+            A1f[tt][r] = xs;
+            SPh[tt][r] = fmaf(xs, fmaf(sg, kLn2, -kLn2), sg);   // s + A1 (1 - s) = s (1 + z (1 - s))
           }
         }
         // A1 fragments (register order over the tokens) for the second-layer
         // fold, and the copy [u][j] for O and the scores
 #pragma unroll
-        for (int st = 0; st < 2; ++st) a1f[st] = tiles_frag(A1f[2 * st], A1f[2 * st + 1], fA1);
+        for (int st = 0; st < 2; ++st) a1f[st] = tiles_frag(A1f[2 * st], A1f[2 * st + 1], fA1 * -kLn2);
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
           const h8 af = a1f[tt >> 1];
@@ -1181,7 +1187,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
       f4v H1f[4];
       {
         float am = 0.f;
-        const float cz = pow2neg(e1);
+        const float cz = pow2neg(e1) * -kLog2e;   // Zq1 in units of -1/ln 2
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
           f4v z;
@@ -1190,21 +1196,21 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
             f4v m0 = {}, m1v = {};
             m0 = mfma(frag_tr_rk(sSC, RS, 0, 16 * tt, g, lc), d1f[0], m0);
             m1v = mfma(frag_tr_rk(sSC, RS, 32, 16 * tt, g, lc), d1f[1], m1v);
-            const float c30 = pow2neg(eD1 + ci[INT_ESC + score_wave(tt, 0)]),
-                        c31 = pow2neg(eD1 + ci[INT_ESC + score_wave(tt, 1)]);
+            const float c30 = pow2neg(eD1 + ci[INT_ESC + score_wave(tt, 0)]) * kLog2e,
+                        c31 = pow2neg(eD1 + ci[INT_ESC + score_wave(tt, 1)]) * kLog2e;
             const f4v av = *(const f4v*)(cf + COEF_A + 16 * tt + 4 * g);
             const f4v fv = *(const f4v*)(cf + COEF_F + 16 * tt + 4 * g);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float main = fmaf(av[r], accW[tt][r], fv[r] * accS[tt][r]) * cz;
-              z[r] = fmaf(m0[r], -c30, fmaf(m1v[r], -c31, main));
+              z[r] = fmaf(m0[r], c30, fmaf(m1v[r], c31, main));
             }
           } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) z[r] = accW[tt][r] * cz;
           }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) H1f[tt][r] = z[r] * sigmoidf_(z[r]);
+          for (int r = 0; r < 4; ++r) H1f[tt][r] = z[r] * sigmoid_x(z[r]);   // -H1 log2 e
           am = max4(am, H1f[tt]);
         }
         const float wam = wave_max(am);
@@ -1255,8 +1261,8 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
         float mm = 0.f;
 #pragma unroll
         for (int i = 0; i < kWaves; ++i) mm = fmaxf(mm, __int_as_float(ci[INT_MH1 + i]));
-        eH1 = scale_exp(mm);
-        const float fH = pow2pos(eH1);
+        eH1 = scale_exp(mm * kLn2);   // the waves' maxima are of |H1| log2 e
+        const float fH = pow2pos(eH1) * -kLn2;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
           store_rows4(sH1, RS, uw + lc, 16 * tt + 4 * g, to_h4(H1f[tt], fH));
