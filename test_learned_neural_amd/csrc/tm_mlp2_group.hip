@@ -430,6 +430,32 @@ __device__ __forceinline__ bool tpoll(const unsigned long long* const (&base)[kN
   return false;
 }
 
+// tpoll's first round issued early: the loads go out at once, the tags are
+// checked later (check), and only a miss falls back to tpoll
+template <int kStride, int kW, int kN>
+struct TPollEarly {
+  unsigned long long wd[kN][kW];
+  __device__ __forceinline__ void issue(const unsigned long long* const (&base)[kN], int t) {
+#pragma unroll
+    for (int b = 0; b < kN; ++b)
+#pragma unroll
+      for (int e = 0; e < kW; ++e)
+        wd[b][e] = __hip_atomic_load(base[b] + (e * kStride + t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __device__ __forceinline__ bool check(unsigned tag, float (&out)[kN][2 * kW]) const {
+    bool ok = true;
+#pragma unroll
+    for (int b = 0; b < kN; ++b)
+#pragma unroll
+      for (int e = 0; e < kW; ++e) {
+        out[b][2 * e] = __uint_as_float((unsigned)(wd[b][e] & 0x0fffffffu) << 4);
+        out[b][2 * e + 1] = __uint_as_float((unsigned)((wd[b][e] >> 28) & 0x0fffffffu) << 4);
+        ok = ok && (unsigned)(wd[b][e] >> 56) == (tag & 0xffu);
+      }
+    return ok;
+  }
+};
+
 // A chunk's raw inputs, one thread's share: for each of its row pieces
 // (piece = tid + r * kThreads, r < 512 / kThreads) 16 bytes (8 bf16) of row
 // j = piece / 8 of K and of Q (columns 8 (piece % 8) ..), and for tid < 64
@@ -997,6 +1023,11 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
       // u -> (1 - alpha_j) u + E_j: A_j is the scan's product part, F_j its
       // value from F_{-1} = 0).  First read after the barrier that follows
       // the exchange.
+      const unsigned long long* obases[kG - 1];
+#pragma unroll
+      for (int m = 0; m < kG - 1; ++m) obases[m] = xO(partner(m), par);
+      TPollEarly<kThreads, kE / 2, kG - 1> opoll;
+      const bool early = w == C::kWD0 || w == C::kWD1;
       if (w == C::kWD0 || w == C::kWD1) {
         const int i = lane;
         const int j0 = w == C::kWD0 ? 0 : 32;
@@ -1005,6 +1036,9 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
         const float4* pairs4 = (const float4*)(smem + OFF_COEF + COEF_PAIR) + j0 / 2;
 #pragma unroll 2
         for (int b = 0; b < 4; ++b) {
+          // halfway through the recurrence, these waves' first poll of the
+          // partner's O goes out (its tags are checked after the stage)
+          if (b == 2) opoll.issue(obases, tid);
           // 8 rows per batch: the steps' (1 - alpha_j, eta_j) pairs as LDS
           // broadcasts (two steps per 16-byte read), the rows stored after
           // the batch so that the gate reads never wait behind row stores
@@ -1077,12 +1111,8 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
       // the partners' O for this thread's elements, and their parts of my y
       // tiles of the previous chunk
       float pvv[kG - 1][kE], pyv[kG - 1][kYPer];
-      {
-        const unsigned long long* bases[kG - 1];
-#pragma unroll
-        for (int m = 0; m < kG - 1; ++m) bases[m] = xO(partner(m), par);
-        if (!tpoll<kThreads, kE / 2, kG - 1>(bases, tid, seq, p.spin_max, pvv)) give_up();
-      }
+      if (!(early && opoll.check(seq, pvv)) && !tpoll<kThreads, kE / 2, kG - 1>(obases, tid, seq, p.spin_max, pvv))
+        give_up();
       if (prev_row0 >= 0) load_prev_y(seq - 1, pyv);
       // every vector memory operation of this thread done, the next chunk's
       // staging loads included (a no-op after a poll, which waited for them)
