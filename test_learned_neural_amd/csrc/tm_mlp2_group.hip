@@ -37,7 +37,11 @@
 //   W2/S2 pieces to LDS and computes two 16x16 output tiles over all 128
 //   units of the workgroup.  Only O (needed before the backprop: one
 //   exchange per chunk on the critical path) and y (exchanged one chunk late,
-//   riding on the next O exchange) cross the pair, as fp32 partial sums.
+//   riding on the next O exchange) cross the pair, as partial sums.
+// * A tile used by products that contract over either of its dimensions is
+//   stored once in LDS, K-major for one use (a lane's four accumulator rows
+//   are one 8-byte store), and read along its other dimension with the
+//   transposing ds_read_b64_tr_b16 (see tr4).
 // * The second wave per SIMD fills the issue gaps of the first: the
 //   element-wise work (SiLU, its derivative, scaling, conversions) and the
 //   barriers of one wave overlap the matrix work of the other.
