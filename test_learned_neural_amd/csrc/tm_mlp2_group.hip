@@ -218,6 +218,13 @@ __device__ __forceinline__ int64_t gate_base(const Params& p, int s, int ci, int
 __device__ __forceinline__ f4v mfma(h8 a, h8 b, f4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
+typedef float f16v __attribute__((ext_vector_type(16)));
+// v_mfma_f32_32x32x16_f16: lane l serves row (A) or column (B) l % 32 with
+// K values 8 (l / 32) .. + 7; accumulator register r of lane l holds row
+// 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+__device__ __forceinline__ f16v mfma32(h8 a, h8 b, f16v c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 
 // x f rounded to fp16 as a multiply and a conversion (two values share one
 // v_cvt_pk_f16_f32).  The empty asm keeps the compiler from fusing the pair
@@ -1359,6 +1366,83 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
       __syncthreads();   // every wave's second-layer scores
 
       // ================= a5 layer 2: y = diag(A) H1 W2^T + diag(F) H1 S2^T - (D o P) Delta2 =================
+      if constexpr (NW == 8) {
+        // Four 32 x 32 blocks on v_mfma_f32_32x32x16_f16, one per wave of
+        // waves 0..3 (one per SIMD): block (jb, cb) = (32 (w >> 1), 32 (w & 1)).
+        // Each operand block is read from LDS once per block, against twice
+        // (H1, P) or four times (W2^T, S2^T, Delta2^T) over the eight waves'
+        // 16 x 16 tile pairs; the stage is bound by these reads.
+        if (w < 4) {
+          const int jb = 32 * (w >> 1), cb = 32 * (w & 1);
+          const int l32 = lane & 31, hk = lane >> 5, grp16 = lane >> 4;
+          // fragment of block columns n0 .. n0 + 31 over K rows kb .. kb + 15 of a K-major tile
+          auto fr32 = [&](const _Float16* T, int kb, int n0) {
+            const int k0 = kb + 8 * (grp16 >> 1), nn = n0 + 16 * (grp16 & 1);
+            const h4 lo = tr4(T, RS, k0, nn, lc), hi = tr4(T, RS, k0 + 4, nn, lc);
+            return h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          };
+          f16v aw = {}, as = {};
+#pragma unroll
+          for (int ks = 0; ks < kUG / 16; ++ks) {
+            const h8 hf = fr32(sH1, 16 * ks, jb);
+            aw = mfma32(hf, fr32(sW2, 16 * ks, cb), aw);
+            if constexpr (kRW) as = mfma32(hf, fr32(sS2, 16 * ks, cb), as);
+          }
+          if constexpr (kRW) {
+            // operand reads two K-steps ahead of the products (the reads'
+            // latency, not the matrix unit, bounds the chain otherwise)
+            __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+            for (int ks = 0; ks < kUG / 16; ++ks) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+              if (ks + 2 < kUG / 16) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+            }
+          }
+          float yv[16];
+          const float cy = pow2neg(eH1 + e2);
+          if constexpr (kRW) {
+            // the masked term over keys 0..31 and 32..63 separately: each half
+            // of a query tile's scores carries the scale of the wave that produced it
+            f16v m0 = {}, m1v = {};
+            const _Float16* drow = sD2T + (cb + l32) * RS + 8 * hk;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) m0 = mfma32(fr32(sSC, 16 * ks, jb), *(const h8*)(drow + 16 * ks), m0);
+#pragma unroll
+            for (int ks = 2; ks < 4; ++ks) m1v = mfma32(fr32(sSC, 16 * ks, jb), *(const h8*)(drow + 16 * ks), m1v);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int tjq = (jb >> 4) + (q >> 1);   // the query tile of rows jb + 8q + 4hk ..
+              const float c30 = pow2neg(eD2 + ci[INT_EDP + score_wave(tjq, 0)]),
+                          c31 = pow2neg(eD2 + ci[INT_EDP + score_wave(tjq, 1)]);
+              const f4v av = *(const f4v*)(cf + COEF_A + jb + 8 * q + 4 * hk);
+              const f4v fv = *(const f4v*)(cf + COEF_F + jb + 8 * q + 4 * hk);
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) {
+                const int r = 4 * q + rr;
+                const float main = fmaf(av[rr], aw[r], fv[rr] * as[r]) * cy;
+                yv[r] = fmaf(m0[r], -c30, fmaf(m1v[r], -c31, main));
+              }
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) yv[r] = aw[r] * cy;
+          }
+          // keep the block if its rows are this workgroup's, else send them
+          // (element / word indexing of the owner's rows as in finish_prev_y)
+          const int owner = jb / C::kYRows;
+          if (owner == h) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              ypark[(jb + 8 * (r >> 2) + 4 * hk + (r & 3) - C::kYRows * h) * kD + cb + l32] = yv[r];
+          } else {
+            unsigned long long* yb = xY(h, (owner - h - 1 + kG) % kG, par);
+#pragma unroll
+            for (int r = 0; r < 16; r += 2)
+              tstore(yb, ((jb + 8 * (r >> 2) + 4 * hk + (r & 3) - C::kYRows * owner) / 2) * kD + cb + l32, yv[r],
+                     yv[r + 1], seq);
+          }
+        }
+      } else {
       {
         float yv[kE];
         const float cy = pow2neg(eH1 + e2);
@@ -1403,6 +1487,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
 #pragma unroll
             for (int rp = 0; rp < 2; ++rp) tstore(yb, y_word(i, rp), yv[4 * i + 2 * rp], yv[4 * i + 2 * rp + 1], seq);
         }
+      }
       }
       // the new state's maxima for the next chunk's operand scales (reduced
       // here, once the fold's products have long completed)
