@@ -75,7 +75,7 @@ def isa():
                               b.PER_FILE["tm_mlp2_group.hip"] + ["--cuda-device-only", "-S", src, "-o", out],
                               stderr=subprocess.DEVNULL)
         lines = open(out).read().split("\n")
-    start = next(i for i, l in enumerate(lines) if re.match(r"^_Z\S*mlp2_group_kernelILb1E\S*:", l))
+    start = next(i for i, l in enumerate(lines) if re.match(r"^_Z\S*mlp2_group_kernelILb1ELi8ELb0E\S*:", l))
     end = next(i for i in range(start, len(lines)) if "s_endpgm" in lines[i])
     body = lines[start:end]
     stamps = [i for i, l in enumerate(body) if "s_memtime" in l]
