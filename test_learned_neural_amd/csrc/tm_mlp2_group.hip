@@ -34,8 +34,9 @@
 //   their accumulators (lanes = units, registers = tokens).
 // * Products that contract over the hidden units (O, the masked scores
 //   H1 A1^T, y) run once per workgroup: every wave writes its A1, H1 and
-//   W2/S2 pieces to LDS and computes two 16x16 output tiles over all 128
-//   units of the workgroup.  Only O (needed before the backprop: one
+//   W2/S2 pieces to LDS; O and the scores are two 16x16 output tiles per
+//   wave over all 128 units of the workgroup, y four 32x32 blocks on waves
+//   0..3 (one per SIMD).  Only O (needed before the backprop: one
 //   exchange per chunk on the critical path) and y (exchanged one chunk late,
 //   riding on the next O exchange) cross the pair, as partial sums.
 // * A tile used by products that contract over either of its dimensions is
