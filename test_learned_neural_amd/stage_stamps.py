@@ -117,7 +117,7 @@ def isa():
     print(f"  {'total':<62s}" + "".join(f"{tot[c]:7d}" for c in classes))
 
 
-def run(steps: int = 2, per_wave: bool = False):
+def run(steps: int = 2, per_wave: bool = False, workload: str = "headline"):
     import numpy as np
     import torch
     sys.path.insert(0, ROOT)
@@ -127,7 +127,7 @@ def run(steps: int = 2, per_wave: bool = False):
         raise SystemExit(f"{STAMPS_LIB} is missing: run with --build first")
     tmm.LIB_PATH = STAMPS_LIB
     lib = tmm.load()
-    cfg = wl.WORKLOADS["headline"]
+    cfg = wl.WORKLOADS[workload]
     inp = wl.make_inputs(cfg, workers=16)
     B, H, N, d, P = cfg.B, cfg.H, cfg.N, cfg.d, cfg.param_count
     tok = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).reshape(B, H, N, d).cuda()
@@ -164,5 +164,6 @@ if __name__ == "__main__":
     ap.add_argument("--build", action="store_true")
     ap.add_argument("--isa", action="store_true")
     ap.add_argument("--per-wave", action="store_true", help="also print every wave's median per stage")
+    ap.add_argument("--workload", default="headline", help="a 2-layer d=64 h=256 workload of workloads.py")
     a = ap.parse_args()
-    build() if a.build else isa() if a.isa else run(per_wave=a.per_wave)
+    build() if a.build else isa() if a.isa else run(per_wave=a.per_wave, workload=a.workload)
