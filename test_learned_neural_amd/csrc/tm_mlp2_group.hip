@@ -146,6 +146,17 @@ struct Grp {
   static constexpr int64_t kXYWords = (int64_t)kG * (kG - 1) * 2 * (kYElems / 2);
   static constexpr int64_t kGroupBytes = (kXOWords + kXYWords) * 8;
   static constexpr int kMaxGroups = 256 / kG;   // one workgroup per CU of a 256-CU device
+  // few-stream split (kSplit): the words a key-side workgroup hands its
+  // retrieval workgroup per thread and chunk ([half][parity][word][thread]),
+  // written at three points of the chunk: the chunk-start W2 and S2 copies
+  // and A1 (words PW_1 ..), Delta2 and the query products (PW_2 ..), Delta1
+  // (PW_3 ..); and the retrieval workgroups' receipts ([half][thread])
+  static constexpr int kPubW = 34;
+  static constexpr int PW_1 = 0, PW_2 = 17, PW_3 = 28;
+  static constexpr int64_t kXPWords = (int64_t)kG * 2 * kPubW * kThreads;
+  static constexpr int64_t kXAWords = (int64_t)kG * kThreads;
+  static constexpr int64_t kGroupBytesSplit = kGroupBytes + (kXPWords + kXAWords) * 8;
+  static constexpr int kMaxGroupsSplit = 256 / (2 * kG);
   static_assert(NW == 8 || NW == 4, "eight or four waves");
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
   static_assert(kYElems * 4 <= kT64, "the parked y tiles fit their area");
@@ -169,13 +180,18 @@ constexpr int INT_M1 = 56;    // per-wave maxima of |W1|, |S1| (each wave's own 
 // number of the chunk that wrote them (see tstore / tpoll).
 
 // ---- stage timing (a build option; off in the library) ----
-// With TM_STAGE_STAMPS=1 the eight waves of workgroup 0 record the shader
-// clock (s_memtime) at every stage boundary of chunks kStampFrom ..
-// kStampFrom + kStampChunks - 1 of its first stream; titans_mem_stage_stamps
-// (exported by that build only) copies them out.  stage_stamps.py builds the
-// instrumented library and prints the per-stage table.
+// With TM_STAGE_STAMPS=1 the eight waves of the first key-side workgroup
+// (with TM_STAMP_R=1 as well: of the first retrieval workgroup of a split
+// launch) record the shader clock (s_memtime) at every stage boundary of
+// chunks kStampFrom .. kStampFrom + kStampChunks - 1 of its first stream;
+// titans_mem_stage_stamps (exported by that build only) copies them out.
+// stage_stamps.py builds the instrumented library and prints the per-stage
+// table.
 #ifndef TM_STAGE_STAMPS
 #define TM_STAGE_STAMPS 0
+#endif
+#ifndef TM_STAMP_R
+#define TM_STAMP_R 0
 #endif
 constexpr int kStampStages = 24, kStampFrom = 16, kStampChunks = 64;
 #if TM_STAGE_STAMPS
@@ -468,6 +484,63 @@ struct TPollEarly {
   }
 };
 
+// Hand-over words (few-stream split, see kSplit): the same single-copy-
+// atomic tagged 8-byte words as the exchange above, carrying either three
+// 16-bit values (fp16 operands, or an operand's scale exponent as a 16-bit
+// integer, which can exceed 8 bits for values near fp32's underflow) and the
+// tag, or two truncated fp32 values and the tag (tword).
+__device__ __forceinline__ unsigned long long h3word(unsigned short a, unsigned short b, unsigned short c,
+                                                     unsigned tag) {
+  return (unsigned long long)a | ((unsigned long long)b << 16) | ((unsigned long long)c << 32) |
+         ((unsigned long long)(tag & 0xffu) << 56);
+}
+__device__ __forceinline__ unsigned short hbits(_Float16 x) { return __builtin_bit_cast(unsigned short, x); }
+__device__ __forceinline__ unsigned short ebits(int e) { return (unsigned short)(short)e; }
+__device__ __forceinline__ _Float16 h3_get(unsigned long long wd, int k) {
+  return __builtin_bit_cast(_Float16, (unsigned short)(wd >> (16 * k)));
+}
+__device__ __forceinline__ int h3_int(unsigned long long wd, int k) { return (int)(short)(unsigned short)(wd >> (16 * k)); }
+__device__ __forceinline__ float tword_lo(unsigned long long wd) { return __uint_as_float((unsigned)(wd & 0x0fffffffu) << 4); }
+__device__ __forceinline__ float tword_hi(unsigned long long wd) {
+  return __uint_as_float((unsigned)((wd >> 28) & 0x0fffffffu) << 4);
+}
+__device__ __forceinline__ bool tag_is(unsigned long long wd, unsigned tag) { return (unsigned)(wd >> 56) == (tag & 0xffu); }
+__device__ __forceinline__ void wstore(unsigned long long* p, unsigned long long wd) {
+  __hip_atomic_store(p, wd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// kW words of one thread (word e at e * kStride + t): the loads of a range
+// of them issued together, the range's tags checked later, and the range
+// reloaded until they match
+template <int kStride, int kW>
+struct TagWords {
+  unsigned long long wd[kW];
+  template <int kLo, int kHi>
+  __device__ __forceinline__ void issue(const unsigned long long* base, int t) {
+#pragma unroll
+    for (int e = kLo; e < kHi; ++e)
+      wd[e] = __hip_atomic_load(base + (e * kStride + t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  template <int kLo, int kHi>
+  __device__ __forceinline__ bool ok(unsigned tag) const {
+    bool r = true;
+#pragma unroll
+    for (int e = kLo; e < kHi; ++e) r = r && tag_is(wd[e], tag);
+    return r;
+  }
+  // false = gave up after spin_max polls
+  template <int kLo, int kHi>
+  __device__ __forceinline__ bool wait(const unsigned long long* base, int t, unsigned tag, unsigned spin_max) {
+    if (ok<kLo, kHi>(tag)) return true;
+    for (unsigned it = 0; it < spin_max; ++it) {
+      __builtin_amdgcn_s_sleep(1);
+      issue<kLo, kHi>(base, t);
+      if (ok<kLo, kHi>(tag)) return true;
+    }
+    return false;
+  }
+};
+
 // A chunk's raw inputs, one thread's share: for each of its row pieces
 // (piece = tid + r * kThreads, r < 512 / kThreads) 16 bytes (8 bf16) of row
 // j = piece / 8 of K and of Q (columns 8 (piece % 8) ..), and for tid < 64
@@ -635,10 +708,12 @@ __device__ __forceinline__ void ordered_sum(int h, const float (&own)[kW], const
 // kRW: retrieval after each token's write (true) or at the chunk-start
 // state (false: y_j = M_{W_0}(q_j), without the masked correction terms).
 // NW: waves per workgroup (Grp<NW>).  kEarly: move each chunk's inputs into
-// LDS during the previous chunk (eight waves only; see `early`).
-template <bool kRW, int NW, bool kEarly>
+// LDS during the previous chunk (eight waves only; see `early`).  kSplit:
+// each half's retrieval on a workgroup of its own (few streams; see is_r).
+template <bool kRW, int NW, bool kEarly, bool kSplit>
 __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
   using C = Grp<NW>;
+  static_assert(!kSplit || (kRW && NW == 8 && !kEarly), "the split runs eight-wave read-after-write workgroups");
   constexpr int kWaves = C::kWaves, kThreads = C::kThreads, kUG = C::kUG, kG = C::kG, kT = C::kT, kE = C::kE;
   constexpr int kYPer = C::kYPer;
   constexpr int OFF_A1 = C::OFF_A1, OFF_H1 = C::OFF_H1, OFF_W2 = C::OFF_W2, OFF_S2 = C::OFF_S2,
@@ -702,18 +777,26 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
   // group / workgroup in it: blocks b, b + 8, b + 16, ... usually share an
   // XCD (round-robin dispatch), so groups are formed that way when the grid
   // allows it; correctness does not depend on the placement
+  constexpr int kGS = kSplit ? 2 * kG : kG;   // workgroups per group
   int grp, h;
   {
     const int b = blockIdx.x;
-    if (gridDim.x % (8 * kG) == 0) {
+    if (gridDim.x % (8 * kGS) == 0) {
       const int slot = b >> 3;
-      grp = (b & 7) + 8 * (slot / kG);
-      h = slot % kG;
+      grp = (b & 7) + 8 * (slot / kGS);
+      h = slot % kGS;
     } else {
-      grp = b / kG;
-      h = b % kG;
+      grp = b / kGS;
+      h = b % kGS;
     }
   }
+  // With kSplit, workgroups kG .. 2 kG - 1 of a group are retrieval
+  // workgroups: the one of half h (h = its index - kG) takes from the
+  // key-side workgroup of that half, per chunk, the state copies, A1, Delta2,
+  // Delta1 and the query products the read needs, and computes the chunk's
+  // y (a5) one step behind, while the key side goes on with the next chunk.
+  const bool is_r = kSplit && h >= kG;
+  if (is_r) h -= kG;
   const int uw = kUW * w;               // this wave's first unit inside the workgroup's kUG
   const int hs = kUG * h + uw;          // ... and inside the layer's 256
   // the workgroup-level output tiles of this wave (O, y: tokens tj, columns
@@ -736,7 +819,14 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
   // score matrix, whose scale the kk-th K-step of a product over keys uses
   auto score_wave = [](int tt, int kk) { return (4 * tt + 2 * kk) / kT; };
 
-  unsigned long long* xw = (unsigned long long*)(p.xbuf + (int64_t)grp * C::kGroupBytes);
+  unsigned long long* xw =
+      (unsigned long long*)(p.xbuf + (int64_t)grp * (kSplit ? C::kGroupBytesSplit : C::kGroupBytes));
+  // the hand-over words of this workgroup's half, parity par (word e of
+  // thread t at e kThreads + t), and the receipts of its retrieval workgroup
+  auto xP = [&](unsigned par) {
+    return xw + C::kXOWords + C::kXYWords + ((int64_t)h * 2 + par) * C::kPubW * kThreads;
+  };
+  unsigned long long* const xA = xw + C::kXOWords + C::kXYWords + C::kXPWords + (int64_t)h * kThreads;
   // O partials of workgroup wg, parity par
   auto xO = [&](int wg, unsigned par) { return xw + ((int64_t)wg * 2 + par) * kThreads * (kE / 2); };
   // y partials sent by workgroup snd to its receiver slot sl
@@ -776,9 +866,11 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
   // gains.)
   constexpr bool early = kEarly && NW == 8;
   bool pre = false;         // the tiles already hold the inputs of the chunk about to start
-  // the half-workgroup share of the staged chunk: pieces t and t + 256 of
-  // waves 4..7 (t = tid - 256), the same threads that prefetched them
-  auto inputs_to_lds = [&](int nn, int t) {
+  // the half-workgroup share of the staged chunk: pieces t and t + 256,
+  // moved by the same threads that prefetched them (t = tid - 256 on waves
+  // 4..7, t = tid on waves 0..3), into the K and Q tiles dK, dQ; returns
+  // max |K| over the pieces, and the gates of token t (t < 64) in g3
+  auto inputs_to_lds = [&](int nn, int t, _Float16* dK, _Float16* dQ, float3& g3) {
     const ChunkRegs<2> cr = unstage_chunk_regs<256>(smem + OFF_STAGE, nn, t);
     float kn = 0.f;
 #pragma unroll
@@ -788,15 +880,18 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
       const h8 kv = bf16x8_to_h8(ku), qv = bf16x8_to_h8(cr.q[rr]);
       kn = amax3(amax3(kn, bf16_lo(ku.x), bf16_hi(ku.x)), bf16_lo(ku.y), bf16_hi(ku.y));
       kn = amax3(amax3(kn, bf16_lo(ku.z), bf16_hi(ku.z)), bf16_lo(ku.w), bf16_hi(ku.w));
-      *(h8*)(sK + j * RS + cb) = kv;
-      *(h8*)(sQ + j * RS + cb) = qv;
+      *(h8*)(dK + j * RS + cb) = kv;
+      *(h8*)(dQ + j * RS + cb) = qv;
     }
-    if (t < kB) {
-      cf[COEF_THETA + t] = cr.gt;
-      float2* pairs = (float2*)(smem + OFF_COEF + COEF_PAIR);
-      pairs[t] = make_float2(1.f - cr.ga, cr.ge);
-    }
+    g3 = make_float3(cr.ga, cr.ge, cr.gt);
     return kn;
+  };
+  auto gates_to_lds = [&](int t, float3 g3) {
+    if (t < kB) {
+      cf[COEF_THETA + t] = g3.z;
+      float2* pairs = (float2*)(smem + OFF_COEF + COEF_PAIR);
+      pairs[t] = make_float2(1.f - g3.x, g3.y);
+    }
   };
 
   // the partners' partials of this thread's y elements for the chunk
@@ -824,7 +919,556 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
       if (j < prev_n) p.y[(prev_row0 + j) * kD + lane] = __float2bfloat16(sum[e]);
     }
   };
+  // ================= a1: coefficients (every workgroup computes them identically) =================
+  // On the key side while the O exchange is in flight.  Lane m of a wave
+  // holds token m's (1 - alpha_m, eta_m); padding tokens have alpha = 0,
+  // eta = 1, theta = 0.
+  //
+  // D, one lane per column i: t = theta_i prod_{i<m<=j} eta_m, started at
+  // j == i by adding theta_i to a zero product, and
+  // D[j][i] = (1 - alpha_j) D[j-1][i] + t -- one fma per row on each of the
+  // two carried values, the row's gates broadcast from LDS.  Wave kWD0
+  // runs rows 0..31 and wave kWD1 rows 32..63, each starting from zero.
+  // For columns i >= 32 the second wave's rows are exact (their
+  // recurrences start at row i); for i < 32 they lack the part carried
+  // over from row 31,
+  // which every reader adds (d_full) through the column-independent
+  // transfer
+  //   (D, t)_j += (T11_j D_31 + T12_j t_31, T22_j t_31),
+  // T11_j = prod_{32<=m<=j} (1 - alpha_m), T22_j = prod_{32<=m<=j} eta_m,
+  // T12_j = sum_{32<=l<=j} prod_{l<m<=j} (1 - alpha_m) T22_l,
+  // which wave kWS gets from prefix scans restarted at row 32, beside E_j (a
+  // prefix product of eta) and (A_j, F_j) (a prefix scan of the maps
+  // u -> (1 - alpha_j) u + E_j: A_j is the scan's product part, F_j its
+  // value from F_{-1} = 0).  First read after the next barrier.
+  auto coef_stage = [&](auto&& mid) {
+    if (w == C::kWD0 || w == C::kWD1) {
+      const int i = lane;
+      const int j0 = w == C::kWD0 ? 0 : 32;
+      const float thi = cf[COEF_THETA + i];
+      float di = 0.f, t = 0.f;
+      const float4* pairs4 = (const float4*)(smem + OFF_COEF + COEF_PAIR) + j0 / 2;
+#pragma unroll 2
+      for (int b = 0; b < 4; ++b) {
+        // halfway through the recurrence (the key side's first poll of
+        // the partner's O goes out here; its tags are checked after the stage)
+        if (b == 2) mid();
+        // 8 rows per batch: the steps' (1 - alpha_j, eta_j) pairs as LDS
+        // broadcasts (two steps per 16-byte read), the rows stored after
+        // the batch so that the gate reads never wait behind row stores
+        float4 gq[4];
+        float drows[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) gq[q] = pairs4[4 * b + q];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int j = j0 + 8 * b + jj;
+          const float ga = (jj & 1) ? gq[jj >> 1].z : gq[jj >> 1].x;
+          const float ge = (jj & 1) ? gq[jj >> 1].w : gq[jj >> 1].y;
+          const float inj = i == j ? thi : 0.f;   // theta_i enters at row i
+          t = fmaf(ge, t, inj);
+          di = fmaf(ga, di, t);
+          drows[jj] = di;
+        }
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) sDM[(j0 + 8 * b + jj) * RF + i] = drows[jj];
+      }
+      // wave kWD0: t at row 31 for i < 32; wave kWD1: t at row 63 (= U_i) for i >= 32
+      if ((w == C::kWD0) == (i < 32)) cf[COEF_XT + i] = t;
+    } else if (w == C::kWS) {
+      const float2 gl = ((const float2*)(smem + OFF_COEF + COEF_PAIR))[lane];
+      const float e = wave_prefix_prod(gl.y);
+      float a = gl.x, f = e;
+      wave_affine_scan(a, f);
+      cf[COEF_A + lane] = a;
+      cf[COEF_E + lane] = e;
+      cf[COEF_F + lane] = f;
+      // the same scans restarted at row 32 (identity maps below it)
+      const bool lo = lane < 32;
+      const float eb = wave_prefix_prod(lo ? 1.f : gl.y);
+      float a2 = lo ? 1.f : gl.x, f2b = lo ? 0.f : eb;
+      wave_affine_scan(a2, f2b);
+      if (!lo) {
+        cf[COEF_T11 + lane - 32] = a2;
+        cf[COEF_T12 + lane - 32] = f2b;
+      }
+      if (lane == 63) ci[INT_T22] = __float_as_int(eb);
+    }
+  };
+  // the fold weights of token i: U_i and D[n-1][i], each scaled into
+  // (0.5, 1] for fp16 (one wave, lane per token)
+  auto store_fold_weights = [&](int i, float ui, float dlast) {
+    const float mu = wave_max(fabsf(ui)), md = wave_max(fabsf(dlast));
+    int eu = 0, ed = 0;
+    if (mu > 0.f && mu < INFINITY) { (void)frexpf(mu, &eu); eu = -eu; }
+    if (md > 0.f && md < INFINITY) { (void)frexpf(md, &ed); ed = -ed; }
+    ch[H16_WU + i] = (_Float16)ldexpf(ui, eu);
+    ch[H16_WD + i] = (_Float16)ldexpf(dlast, ed);
+    if (lane == 0) { ci[INT_EWU] = eu; ci[INT_EWD] = ed; }
+  };
+  // The key side of a split launch needs no D matrix (only the reads do):
+  // wave kWS scans A, E, F as above, and wave kWD0 gets the fold weights from
+  // scans over the lanes in reversed token order (lane l holds token
+  // i = 63 - l):
+  //   U_i = theta_i prod_{i<m} eta_m,
+  //   D[n-1][i] = theta_i R_i,  R_i = a_i + eta_{i+1} R_{i+1},  R_64 = 0,
+  //   a_i = prod_{i<m<=n-1} (1 - alpha_m) for i <= n-1, 0 beyond,
+  // which is D's recurrence summed along its last row (padding tokens carry
+  // alpha = 0, eta = 1, so the products may run to token 63).
+  auto key_coef_stage = [&](int n) {
+    const float2* pairs = (const float2*)(smem + OFF_COEF + COEF_PAIR);
+    if (w == C::kWS) {
+      const float2 gl = pairs[lane];
+      const float e = wave_prefix_prod(gl.y);
+      float a = gl.x, f = e;
+      wave_affine_scan(a, f);
+      cf[COEF_A + lane] = a;
+      cf[COEF_E + lane] = e;
+      cf[COEF_F + lane] = f;
+    } else if (w == C::kWD0) {
+      const int i = 63 - lane;
+      float2 gn = make_float2(1.f, 1.f);   // token i + 1's (1 - alpha, eta); none after token 63
+      if (lane > 0) gn = pairs[i + 1];
+      const float pa = wave_prefix_prod(gn.x), pe = wave_prefix_prod(gn.y);
+      float c = gn.y, r = i <= n - 1 ? pa : 0.f;
+      wave_affine_scan(c, r);
+      const float th = cf[COEF_THETA + i];
+      store_fold_weights(i, th * pe, th * r);
+    }
+  };
+
+  // the raw first-layer scores Q K^T, tiles (tj, tc0 + i)
+  auto raw_scores = [&](f4v (&scr)[kT]) {
+#pragma unroll
+    for (int i = 0; i < kT; ++i) {
+      f4v acc = {};
+      const _Float16* arow = sQ + (16 * tj + lc) * RS;
+      const _Float16* brow = sK + (16 * (tc0 + i) + lc) * RS;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) acc = mfma(frag_c8(arow, 32 * kk, g), frag_c8(brow, 32 * kk, g), acc);
+      scr[i] = acc;
+    }
+  };
+  // first-layer masked scores SC1 = D o (Q K^T) into sSC [key][query], tiles
+  // (tj, tc0 + i), with this wave's own scale
+  auto sc1_store = [&](const f4v (&scr)[kT]) {
+    float sc[kE], am = 0.f;
+#pragma unroll
+    for (int i = 0; i < kT; ++i) {
+      const f4v dt = d_tile(tj, tc0 + i);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[4 * i + r] = scr[i][r] * dt[r];
+    }
+    am = wave_max(max_abs(am, sc));
+    const int esc = scale_exp(am);
+    const float fsc = pow2pos(esc);
+#pragma unroll
+    for (int i = 0; i < kT; ++i)
+      store_rows4(sSC, RS, 16 * (tc0 + i) + lc, 16 * tj + 4 * g,
+                  h4{sc16(sc[4 * i], fsc), sc16(sc[4 * i + 1], fsc), sc16(sc[4 * i + 2], fsc),
+                     sc16(sc[4 * i + 3], fsc)});
+    if (lane == 0) ci[INT_ESC + w] = esc;
+  };
+  // ================= a5 layer 1: Zq1 = diag(A) Q W1^T + diag(F) Q S1^T - SC1 Delta1 =================
+  // H1 = SiLU(Zq1) over this wave's units (rows: query tiles), in units of
+  // -1/ln 2; main(tt) gives the first two terms of query tile tt in those units
+  auto zq1_h1 = [&](auto&& main, const h8 (&d1f)[2], int eD1, f4v (&H1f)[4]) {
+    float am = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      f4v z = main(tt);
+      if constexpr (kRW) {
+        // the masked term's two K-steps carry the scales of the waves that produced them
+        f4v m0 = {}, m1v = {};
+        m0 = mfma(frag_tr_rk(sSC, RS, 0, 16 * tt, g, lc), d1f[0], m0);
+        m1v = mfma(frag_tr_rk(sSC, RS, 32, 16 * tt, g, lc), d1f[1], m1v);
+        const float c30 = pow2neg(eD1 + ci[INT_ESC + score_wave(tt, 0)]) * kLog2e,
+                    c31 = pow2neg(eD1 + ci[INT_ESC + score_wave(tt, 1)]) * kLog2e;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) z[r] = fmaf(m0[r], c30, fmaf(m1v[r], c31, z[r]));
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) H1f[tt][r] = z[r] * sigmoid_x(z[r]);   // -H1 log2 e
+      am = max4(am, H1f[tt]);
+    }
+    const float wam = wave_max(am);
+    if (lane == 0) ci[INT_MH1 + w] = __float_as_int(wam);
+  };
+  // H1 with the workgroup-wide scale (its exponent returned), copied [u][j]
+  // for the scores and y; after a barrier that follows every wave's zq1_h1
+  auto h1_copy = [&](const f4v (&H1f)[4]) {
+    float mm = 0.f;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) mm = fmaxf(mm, __int_as_float(ci[INT_MH1 + i]));
+    const int eH1 = scale_exp(mm * kLn2);   // the waves' maxima are of |H1| log2 e
+    const float fH = pow2pos(eH1) * -kLn2;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) store_rows4(sH1, RS, uw + lc, 16 * tt + 4 * g, to_h4(H1f[tt], fH));
+    return eH1;
+  };
+  // ================= masked second-layer scores D o (H1 A1^T): tiles (tj, tc0 + i) =================
+  // into sSC [key][query], with this wave's own scale
+  auto p_scores = [&](int eH1, int eA1) {
+    float pv[kE], am = 0.f;
+    const float cp = pow2neg(eH1 + eA1);
+#pragma unroll
+    for (int i = 0; i < kT; ++i) {
+      f4v acc = {};
+#pragma unroll
+      for (int kk = 0; kk < C::kKSteps; ++kk)
+        acc = mfma(frag_tr_c8(sH1, RS, 32 * kk, 16 * tj, g, lc), frag_tr_c8(sA1, RS, 32 * kk, 16 * (tc0 + i), g, lc),
+                   acc);
+      const f4v dt = d_tile(tj, tc0 + i);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pv[4 * i + r] = acc[r] * cp * dt[r];
+    }
+    am = wave_max(max_abs(am, pv));
+    const int edp = scale_exp(am);
+    const float fdp = pow2pos(edp);
+#pragma unroll
+    for (int i = 0; i < kT; ++i)
+      store_rows4(sSC, RS, 16 * (tc0 + i) + lc, 16 * tj + 4 * g,
+                  h4{sc16(pv[4 * i], fdp), sc16(pv[4 * i + 1], fdp), sc16(pv[4 * i + 2], fdp),
+                     sc16(pv[4 * i + 3], fdp)});
+    if (lane == 0) ci[INT_EDP + w] = edp;
+  };
+  // ================= a5 layer 2: y = diag(A) H1 W2^T + diag(F) H1 S2^T - (D o P) Delta2 =================
+  // after a barrier that follows every wave's H1 copy and scores; the rows of
+  // other workgroups are sent to them (tagged `seq`, parity `par`)
+  auto y_stage = [&](int eH1, int e2, int eD2, unsigned par) {
+    if constexpr (NW == 8) {
+      // Four 32 x 32 blocks on v_mfma_f32_32x32x16_f16, one per wave of
+      // waves 0..3 (one per SIMD): block (jb, cb) = (32 (w >> 1), 32 (w & 1)).
+      // Each operand block is read from LDS once per block, against twice
+      // (H1, P) or four times (W2^T, S2^T, Delta2^T) over the eight waves'
+      // 16 x 16 tile pairs; the stage is bound by these reads.
+      if (w < 4) {
+        const int jb = 32 * (w >> 1), cb = 32 * (w & 1);
+        const int l32 = lane & 31, hk = lane >> 5, grp16 = lane >> 4;
+        // fragment of block columns n0 .. n0 + 31 over K rows kb .. kb + 15 of a K-major tile
+        auto fr32 = [&](const _Float16* T, int kb, int n0) {
+          const int k0 = kb + 8 * (grp16 >> 1), nn = n0 + 16 * (grp16 & 1);
+          const h4 lo = tr4(T, RS, k0, nn, lc), hi = tr4(T, RS, k0 + 4, nn, lc);
+          return h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        };
+        f16v aw = {}, as = {};
+#pragma unroll
+        for (int ks = 0; ks < kUG / 16; ++ks) {
+          const h8 hf = fr32(sH1, 16 * ks, jb);
+          aw = mfma32(hf, fr32(sW2, 16 * ks, cb), aw);
+          if constexpr (kRW) as = mfma32(hf, fr32(sS2, 16 * ks, cb), as);
+        }
+        if constexpr (kRW) {
+          // operand reads two K-steps ahead of the products (the reads'
+          // latency, not the matrix unit, bounds the chain otherwise)
+          __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+          for (int ks = 0; ks < kUG / 16; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if (ks + 2 < kUG / 16) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+          }
+        }
+        float yv[16];
+        const float cy = pow2neg(eH1 + e2);
+        if constexpr (kRW) {
+          // the masked term over keys 0..31 and 32..63 separately: each half
+          // of a query tile's scores carries the scale of the wave that produced it
+          f16v m0 = {}, m1v = {};
+          const _Float16* drow = sD2T + (cb + l32) * RS + 8 * hk;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) m0 = mfma32(fr32(sSC, 16 * ks, jb), *(const h8*)(drow + 16 * ks), m0);
+#pragma unroll
+          for (int ks = 2; ks < 4; ++ks) m1v = mfma32(fr32(sSC, 16 * ks, jb), *(const h8*)(drow + 16 * ks), m1v);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int tjq = (jb >> 4) + (q >> 1);   // the query tile of rows jb + 8q + 4hk ..
+            const float c30 = pow2neg(eD2 + ci[INT_EDP + score_wave(tjq, 0)]),
+                        c31 = pow2neg(eD2 + ci[INT_EDP + score_wave(tjq, 1)]);
+            const f4v av = *(const f4v*)(cf + COEF_A + jb + 8 * q + 4 * hk);
+            const f4v fv = *(const f4v*)(cf + COEF_F + jb + 8 * q + 4 * hk);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int r = 4 * q + rr;
+              const float main = fmaf(av[rr], aw[r], fv[rr] * as[r]) * cy;
+              yv[r] = fmaf(m0[r], -c30, fmaf(m1v[r], -c31, main));
+            }
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) yv[r] = aw[r] * cy;
+        }
+        // keep the block if its rows are this workgroup's, else send them
+        // (element / word indexing of the owner's rows as in finish_prev_y)
+        const int owner = jb / C::kYRows;
+        if (owner == h) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            ypark[(jb + 8 * (r >> 2) + 4 * hk + (r & 3) - C::kYRows * h) * kD + cb + l32] = yv[r];
+        } else {
+          unsigned long long* yb = xY(h, (owner - h - 1 + kG) % kG, par);
+#pragma unroll
+          for (int r = 0; r < 16; r += 2)
+            tstore(yb, ((jb + 8 * (r >> 2) + 4 * hk + (r & 3) - C::kYRows * owner) / 2) * kD + cb + l32, yv[r],
+                   yv[r + 1], seq);
+        }
+      }
+    } else {
+      float yv[kE];
+      const float cy = pow2neg(eH1 + e2);
+      const f4v av = *(const f4v*)(cf + COEF_A + 16 * tj + 4 * g);
+      const f4v fv = *(const f4v*)(cf + COEF_F + 16 * tj + 4 * g);
+#pragma unroll
+      for (int i = 0; i < kT; ++i) {
+        const int crow = 16 * (tc0 + i) + lc;
+        f4v aw = {}, as = {};
+#pragma unroll
+        for (int kk = 0; kk < C::kKSteps; ++kk) {
+          const h8 hf = frag_tr_c8(sH1, RS, 32 * kk, 16 * tj, g, lc);
+          aw = mfma(hf, frag_tr_c8(sW2, RS, 32 * kk, 16 * (tc0 + i), g, lc), aw);
+          if constexpr (kRW) as = mfma(hf, frag_tr_c8(sS2, RS, 32 * kk, 16 * (tc0 + i), g, lc), as);
+        }
+        if constexpr (kRW) {
+          f4v m0 = {}, m1v = {};
+          m0 = mfma(frag_tr_c8(sSC, RS, 0, 16 * tj, g, lc), frag_c8(sD2T + crow * RS, 0, g), m0);
+          m1v = mfma(frag_tr_c8(sSC, RS, 32, 16 * tj, g, lc), frag_c8(sD2T + crow * RS, 32, g), m1v);
+          const float c30 = pow2neg(eD2 + ci[INT_EDP + score_wave(tj, 0)]),
+                      c31 = pow2neg(eD2 + ci[INT_EDP + score_wave(tj, 1)]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float main = fmaf(av[r], aw[r], fv[r] * as[r]) * cy;
+            yv[4 * i + r] = fmaf(m0[r], -c30, fmaf(m1v[r], -c31, main));
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) yv[4 * i + r] = aw[r] * cy;
+        }
+      }
+      // keep my rows, send the other rows to the workgroup that finishes them
+      if (keeps_y) {
+#pragma unroll
+        for (int i = 0; i < kT; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ypark[y_elem(i, r)] = yv[4 * i + r];
+      } else {
+        unsigned long long* yb = xY(h, (y_owner - h - 1 + kG) % kG, par);
+#pragma unroll
+        for (int i = 0; i < kT; ++i)
+#pragma unroll
+          for (int rp = 0; rp < 2; ++rp) tstore(yb, y_word(i, rp), yv[4 * i + 2 * rp], yv[4 * i + 2 * rp + 1], seq);
+      }
+    }
+  };
   __syncthreads();
+
+  // ================= the retrieval workgroup of half h (kSplit) =================
+  // Per chunk: the inputs, the coefficients and the first-layer masked
+  // scores of its own; the key side's words of the chunk (loads issued before
+  // that work, so that a workgroup behind the key side finds them arrived),
+  // then a5 exactly as the unsplit kernel runs it.  The receipt sent once the
+  // words are read lets the key side reuse their slot two chunks later; the
+  // y rows cross between the retrieval pair as in the unsplit kernel, one
+  // chunk late.  The partner's y of chunk seq - 1 is read before this
+  // chunk's y is sent, so a slot is rewritten only after it was read.
+  if constexpr (kSplit) {
+    if (is_r) {
+      for (int s = grp; s < p.streams && !failed; s += p.n_groups) {
+        const int64_t tok0 = (int64_t)s * p.N;
+        for (int c0 = 0, cidx = 0; c0 < p.N; c0 += p.chunk, ++cidx) {
+          const int n = min(p.chunk, p.N - c0);
+          relane();
+          ++seq;
+          const int stamp_slot = (TM_STAGE_STAMPS && TM_STAMP_R && grp == 0 && h == 0 && s == grp &&
+                                  cidx >= kStampFrom && cidx < kStampFrom + kStampChunks) ? cidx - kStampFrom : -1;
+          (void)stamp_slot;
+          STAMP(0);
+          const unsigned par = seq & 1u;
+          int next_s = s, next_c0 = c0 + p.chunk, next_ci = cidx + 1;
+          if (next_c0 >= p.N) { next_s = s + p.n_groups; next_c0 = 0; next_ci = 0; }
+          const bool has_next = next_s < p.streams && p.N > 0;
+          if (tid == 0) ci[INT_FAIL] = 0;
+          // the chunk's K, Q (fp16) and gates into LDS, unless waves 4..7
+          // moved them in during the previous chunk's y
+          if (!pre) {
+            const ChunkRegs<C::kRowPasses> cr =
+                staged ? unstage_chunk_regs<kThreads>(smem + OFF_STAGE, n, tid)
+                       : load_chunk_regs<kThreads>(p, tok0 + c0, gate_base(p, s, cidx, c0), n, tid);
+#pragma unroll
+            for (int rr = 0; rr < C::kRowPasses; ++rr) {
+              const int piece = tid + rr * kThreads, j = piece >> 3, cb = (piece & 7) * 8;
+              *(h8*)(sK + j * RS + cb) = bf16x8_to_h8(cr.k[rr]);
+              *(h8*)(sQ + j * RS + cb) = bf16x8_to_h8(cr.q[rr]);
+            }
+            if (tid < kB) {
+              cf[COEF_THETA + tid] = cr.gt;
+              float2* pairs = (float2*)(smem + OFF_COEF + COEF_PAIR);
+              pairs[tid] = make_float2(1.f - cr.ga, cr.ge);
+            }
+            STAMP(1);
+            __syncthreads();   // the chunk's tiles and gates
+            // the next chunk's rows to the staging area, by the waves that
+            // move them into the tiles during this chunk's y (waited for at
+            // once, as during y: only a workgroup's first chunk comes here)
+            if (has_next && w >= 4) {
+              prefetch_chunk_lds<256>(p, (int64_t)next_s * p.N + next_c0, gate_base(p, next_s, next_ci, next_c0),
+                                      min(p.chunk, p.N - next_c0), tid - 256, smem + OFF_STAGE);
+              __builtin_amdgcn_s_waitcnt(0x0F70);
+            }
+            staged = has_next;
+          } else {
+            STAMP(1);
+          }
+          // The key side's words of this chunk: the copies' words loaded
+          // across the coefficient stage by the waves that have no
+          // recurrence there (all 44 in flight would spill registers), the
+          // rest after the coefficients' barrier, with the partner's y of
+          // the previous chunk (by then its stores have landed).
+          const unsigned long long* pb = xP(par);
+          TagWords<kThreads, C::kPubW> pw;
+          const unsigned long long* ybases[kG - 1];
+#pragma unroll
+          for (int m = 0; m < kG - 1; ++m) {
+            const int snd = partner(m);
+            ybases[m] = xY(snd, (h - snd - 1 + kG) % kG, (seq - 1) & 1u);
+          }
+          TPollEarly<kThreads, kYPer / 2, kG - 1> ypoll;
+          const bool coef_wave = w == C::kWD0 || w == C::kWD1 || w == C::kWS;
+          if (!coef_wave) pw.template issue<C::PW_1, C::PW_2>(pb, tid);
+          STAMP(2);
+          coef_stage([] {});
+          STAMP(3);
+          f4v scr[kT];
+          raw_scores(scr);
+          STAMP(4);
+          __syncthreads();   // the coefficients
+          STAMP(5);
+          if (coef_wave) pw.template issue<C::PW_1, C::PW_2>(pb, tid);
+          pw.template issue<C::PW_2, C::kPubW>(pb, tid);
+          if (prev_row0 >= 0) ypoll.issue(ybases, tid);
+          sc1_store(scr);
+          STAMP(6);
+          // the key side's words, in the order it writes them
+          bool got = pw.template wait<C::PW_1, C::PW_2>(pb, tid, seq, p.spin_max);
+          STAMP(7);
+          got = got && pw.template wait<C::PW_2, C::PW_3>(pb, tid, seq, p.spin_max);
+          STAMP(8);
+          got = got && pw.template wait<C::PW_3, C::kPubW>(pb, tid, seq, p.spin_max);
+          if (!got) give_up();
+          STAMP(9);
+          // the chunk-start W2^T, S2^T copies, A1^T and Delta2^T into their
+          // tiles, where the key side keeps them (value e of a group: word
+          // e / 3 of the group, place e % 3)
+          auto hval = [&](int w0, int e) { return h3_get(pw.wd[w0 + e / 3], e % 3); };
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            const int b = 4 * ct;
+            store_rows4(sW2, RS, uw + lc, 16 * ct + 4 * g,
+                        h4{hval(C::PW_1, b), hval(C::PW_1, b + 1), hval(C::PW_1, b + 2), hval(C::PW_1, b + 3)});
+            store_rows4(sS2, RS, uw + lc, 16 * ct + 4 * g,
+                        h4{hval(C::PW_1, 16 + b), hval(C::PW_1, 17 + b), hval(C::PW_1, 18 + b), hval(C::PW_1, 19 + b)});
+            store_rows4(sA1, RS, uw + lc, 16 * ct + 4 * g,
+                        h4{hval(C::PW_1, 32 + b), hval(C::PW_1, 33 + b), hval(C::PW_1, 34 + b), hval(C::PW_1, 35 + b)});
+          }
+#pragma unroll
+          for (int i = 0; i < kT; ++i)
+            *(h4*)(sD2T + (16 * (tc0 + i) + lc) * RS + 16 * tj + 4 * g) =
+                h4{hval(C::PW_2, 4 * i), hval(C::PW_2, 4 * i + 1), hval(C::PW_2, 4 * i + 2), hval(C::PW_2, 4 * i + 3)};
+          const int e2 = h3_int(pw.wd[C::PW_1 + 16], 0), eA1 = h3_int(pw.wd[C::PW_1 + 16], 1),
+                    eD2 = h3_int(pw.wd[C::PW_2 + 2], 2), eD1 = h3_int(pw.wd[C::PW_3 + 5], 1);
+          // the query products: twords 3 .. 10 of the second group
+          f4v mz[4];
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const unsigned long long wd = pw.wd[C::PW_2 + 3 + 2 * tt + (r >> 1)];
+              mz[tt][r] = (r & 1) ? tword_hi(wd) : tword_lo(wd);
+            }
+          h8 d1f[2];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) d1f[e >> 3][e & 7] = hval(C::PW_3, e);
+          // the previous chunk's y rows of this workgroup
+          if (prev_row0 >= 0) {
+            float pyv[kG - 1][kYPer];
+            if (!ypoll.check(seq - 1, pyv) &&
+                !tpoll<kThreads, kYPer / 2, kG - 1>(ybases, tid, seq - 1, p.spin_max, pyv))
+              give_up();
+            finish_prev_y(pyv);
+          }
+          STAMP(10);
+          __syncthreads();   // every wave's first-layer scores and copies
+          if (ci[INT_FAIL]) { failed = true; break; }
+          STAMP(11);
+          f4v H1f[4];
+          zq1_h1([&](int tt) { return mz[tt]; }, d1f, eD1, H1f);
+          STAMP(12);
+          __syncthreads();   // every wave's H1 maximum
+          STAMP(13);
+          const int eH1 = h1_copy(H1f);
+          STAMP(14);
+          __syncthreads();   // every wave's H1 copy
+          STAMP(15);
+          p_scores(eH1, eA1);
+          STAMP(16);
+          __syncthreads();   // every wave's second-layer scores
+          STAMP(17);
+          y_stage(eH1, e2, eD2, par);
+          // The receipt for this chunk's words (read long ago; sent only now,
+          // since any later wait for a load would also wait for this store)
+          if (got) __hip_atomic_store(xA + tid, tword(0.f, 0.f, seq), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          // the next chunk's inputs into their tiles (waves 4..7, beside y
+          // on waves 0..3; K and Q are not read after the raw scores), then
+          // the chunk after it into the staging area
+          if (staged && w >= 4) {
+            // (this thread's staging loads have landed)
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            float3 g3;
+            (void)inputs_to_lds(min(p.chunk, p.N - next_c0), tid - 256, sK, sQ, g3);
+            gates_to_lds(tid - 256, g3);
+            int s2 = next_s, c2 = next_c0 + p.chunk, i2 = next_ci + 1;
+            if (c2 >= p.N) { s2 = next_s + p.n_groups; c2 = 0; i2 = 0; }
+            if (s2 < p.streams) {
+              // this thread's staging reads are complete before the slots it
+              // read are refilled (the same threads refill them)
+              __builtin_amdgcn_s_waitcnt(0xC07F);
+              prefetch_chunk_lds<256>(p, (int64_t)s2 * p.N + c2, gate_base(p, s2, i2, c2), min(p.chunk, p.N - c2),
+                                      tid - 256, smem + OFF_STAGE);
+              // landed before the chunk ends (these waves wait for y anyway):
+              // an LDS load still in flight across the loop would make the
+              // next chunk's first barrier wait for every memory operation,
+              // the key side's words requested before it included
+              __builtin_amdgcn_s_waitcnt(0x0F70);
+            }
+          }
+          pre = staged;
+          if (staged) {
+            int s2 = next_s, c2 = next_c0 + p.chunk;
+            if (c2 >= p.N) { s2 = next_s + p.n_groups; c2 = 0; }
+            staged = s2 < p.streams;
+          }
+          prev_row0 = tok0 + c0;
+          prev_n = n;
+          STAMP(18);
+          __syncthreads();   // LDS tiles are rewritten by the next chunk
+          STAMP(19);
+          STAMP(20);
+          STAMP(21);
+          STAMP(22);
+          STAMP(23);
+        }
+      }
+      // the last chunk's y rows
+      if (!failed && prev_row0 >= 0) {
+        float pyv[kG - 1][kYPer];
+        load_prev_y(seq, pyv);
+        finish_prev_y(pyv);
+        __syncthreads();
+        if (ci[INT_FAIL]) failed = true;
+      }
+      if (failed) poison_group_streams<kThreads>(p, grp, tid);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      return;
+    }
+  }
 
   for (int s = grp; s < p.streams && !failed; s += p.n_groups) {
     const int64_t tok0 = (int64_t)s * p.N;
@@ -861,30 +1505,43 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
     }
     // every wave's maxima before the first chunk reads them (a chunk whose
     // inputs were moved in early has no barrier before its key-side stage)
-    if constexpr (early) __syncthreads();
+    if constexpr (early || kSplit) __syncthreads();
 
     for (int c0 = 0, cidx = 0; c0 < p.N; c0 += p.chunk, ++cidx) {
       const int n = min(p.chunk, p.N - c0);
       relane();
       ++seq;
-      const int stamp_slot = (TM_STAGE_STAMPS && blockIdx.x == 0 && s == grp && cidx >= kStampFrom &&
-                              cidx < kStampFrom + kStampChunks) ? cidx - kStampFrom : -1;
+      const int stamp_slot = (TM_STAGE_STAMPS && !TM_STAMP_R && grp == 0 && h == 0 && s == grp &&
+                              cidx >= kStampFrom && cidx < kStampFrom + kStampChunks) ? cidx - kStampFrom : -1;
       (void)stamp_slot;
       STAMP(0);
+      // (split) the receipt for this thread's hand-over words, checked
+      // before the words of two chunks back are overwritten
+      unsigned long long ackw = 0;
+      if constexpr (kSplit) ackw = __hip_atomic_load(xA + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
       // the next chunk (in this stream or the group's next one)
       int next_s = s, next_c0 = c0 + p.chunk, next_ci = cidx + 1;
       if (next_c0 >= p.N) { next_s = s + p.n_groups; next_c0 = 0; next_ci = 0; }
       const bool has_next = next_s < p.streams && p.N > 0;
-      if constexpr (early) {
+      if constexpr (early || kSplit) {
         if (tid == 0) {
           ci[INT_AMAX_D2] = 0;
           ci[INT_FAIL] = 0;
         }
       }
+      // The key side of a split launch keeps two sets of K and Q tiles (the
+      // y park and score areas, which only a retrieval workgroup uses, are
+      // the second): waves 0..3 move the next chunk's inputs into the other
+      // set after the O exchange, so a chunk starts without its input stage.
+      if constexpr (kSplit) {
+        const bool alt = seq & 1u;
+        sK = (_Float16*)(smem + (alt ? OFF_YP : OFF_K));
+        sQ = (_Float16*)(smem + (alt ? OFF_SC : OFF_Q));
+      }
 
       // ================= the chunk's K, Q (fp16) and gates into LDS =================
-      if (!(early && pre)) {
+      if (!((early || kSplit) && pre)) {
         // (this thread's staging loads were waited for after the previous
         // chunk's exchange; waiting here would also wait for the y exchange
         // stores just issued)
@@ -909,7 +1566,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
           float2* pairs = (float2*)(smem + OFF_COEF + COEF_PAIR);
           pairs[tid] = make_float2(1.f - cr.ga, cr.ge);
         }
-        if constexpr (!early) {
+        if constexpr (!early && !kSplit) {
           if (tid == 0) {
             ci[INT_AMAX_D2] = 0;
             ci[INT_FAIL] = 0;
@@ -927,6 +1584,8 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
           const int nn = min(p.chunk, p.N - next_c0);
           if constexpr (early) {
             if (w >= 4) prefetch_chunk_lds<256>(p, r0, g0, nn, tid - 256, smem + OFF_STAGE);
+          } else if constexpr (kSplit) {
+            if (w < 4) prefetch_chunk_lds<256>(p, r0, g0, nn, tid, smem + OFF_STAGE);
           } else {
             prefetch_chunk_lds<kThreads>(p, r0, g0, nn, tid, smem + OFF_STAGE);
           }
@@ -934,6 +1593,16 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
         staged = has_next;
       } else {
         STAMP(1);
+        if constexpr (kSplit) {
+          // the next chunk's rows to the staging area, by the threads that
+          // moved this chunk's out of it (their reads of it complete first)
+          if (has_next && w < 4) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            prefetch_chunk_lds<256>(p, (int64_t)next_s * p.N + next_c0, gate_base(p, next_s, next_ci, next_c0),
+                                    min(p.chunk, p.N - next_c0), tid, smem + OFF_STAGE);
+          }
+          staged = has_next;
+        }
       }
       STAMP(2);
 
@@ -1051,6 +1720,8 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
       const unsigned par = seq & 1u;
 #pragma unroll
       for (int e = 0; e < kE / 2; ++e) tstore(xO(h, par), e * kThreads + tid, om[2 * e], om[2 * e + 1], seq);
+      unsigned long long* const pub = xP(par) + tid;   // (split) this thread's hand-over words
+      float3 g3n;   // (split) the next chunk's gates, token tid (tid < 64)
       STAMP(8);
 
       // ---- work that does not need the partner, while the exchange is in flight ----
@@ -1067,99 +1738,22 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
           const int j = min(16 * tj + 4 * g + r, n - 1);
           vr[4 * i + r] = *(const unsigned short*)(p.v + (tok0 + c0 + j) * kD + 16 * (tc0 + i) + lc);
         }
-      // ================= a1: coefficients (every workgroup computes them identically) =================
-      // While the exchange is in flight.  Lane m of a wave holds token m's
-      // (1 - alpha_m, eta_m); padding tokens have alpha = 0, eta = 1, theta = 0.
-      //
-      // D, one lane per column i: t = theta_i prod_{i<m<=j} eta_m, started at
-      // j == i by adding theta_i to a zero product, and
-      // D[j][i] = (1 - alpha_j) D[j-1][i] + t -- one fma per row on each of the
-      // two carried values, the row's gates broadcast from LDS.  Wave kWD0
-      // runs rows 0..31 and wave kWD1 rows 32..63, each starting from zero.
-      // For columns i >= 32 the second wave's rows are exact (their
-      // recurrences start at row i); for i < 32 they lack the part carried
-      // over from row 31,
-      // which every reader adds (d_full) through the column-independent
-      // transfer
-      //   (D, t)_j += (T11_j D_31 + T12_j t_31, T22_j t_31),
-      // T11_j = prod_{32<=m<=j} (1 - alpha_m), T22_j = prod_{32<=m<=j} eta_m,
-      // T12_j = sum_{32<=l<=j} prod_{l<m<=j} (1 - alpha_m) T22_l,
-      // which wave kWS gets from prefix scans restarted at row 32, beside E_j (a
-      // prefix product of eta) and (A_j, F_j) (a prefix scan of the maps
-      // u -> (1 - alpha_j) u + E_j: A_j is the scan's product part, F_j its
-      // value from F_{-1} = 0).  First read after the barrier that follows
-      // the exchange.
       const unsigned long long* obases[kG - 1];
 #pragma unroll
       for (int m = 0; m < kG - 1; ++m) obases[m] = xO(partner(m), par);
       TPollEarly<kThreads, kE / 2, kG - 1> opoll;
-      const bool early_poll = w == C::kWD0 || w == C::kWD1;
-      if (w == C::kWD0 || w == C::kWD1) {
-        const int i = lane;
-        const int j0 = w == C::kWD0 ? 0 : 32;
-        const float thi = cf[COEF_THETA + i];
-        float di = 0.f, t = 0.f;
-        const float4* pairs4 = (const float4*)(smem + OFF_COEF + COEF_PAIR) + j0 / 2;
-#pragma unroll 2
-        for (int b = 0; b < 4; ++b) {
-          // halfway through the recurrence, these waves' first poll of the
-          // partner's O goes out (its tags are checked after the stage)
-          if (b == 2) opoll.issue(obases, tid);
-          // 8 rows per batch: the steps' (1 - alpha_j, eta_j) pairs as LDS
-          // broadcasts (two steps per 16-byte read), the rows stored after
-          // the batch so that the gate reads never wait behind row stores
-          float4 gq[4];
-          float drows[8];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) gq[q] = pairs4[4 * b + q];
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            const int j = j0 + 8 * b + jj;
-            const float ga = (jj & 1) ? gq[jj >> 1].z : gq[jj >> 1].x;
-            const float ge = (jj & 1) ? gq[jj >> 1].w : gq[jj >> 1].y;
-            const float inj = i == j ? thi : 0.f;   // theta_i enters at row i
-            t = fmaf(ge, t, inj);
-            di = fmaf(ga, di, t);
-            drows[jj] = di;
-          }
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) sDM[(j0 + 8 * b + jj) * RF + i] = drows[jj];
-        }
-        // wave kWD0: t at row 31 for i < 32; wave kWD1: t at row 63 (= U_i) for i >= 32
-        if ((w == C::kWD0) == (i < 32)) cf[COEF_XT + i] = t;
-      } else if (w == C::kWS) {
-        const float2 gl = ((const float2*)(smem + OFF_COEF + COEF_PAIR))[lane];
-        const float e = wave_prefix_prod(gl.y);
-        float a = gl.x, f = e;
-        wave_affine_scan(a, f);
-        cf[COEF_A + lane] = a;
-        cf[COEF_E + lane] = e;
-        cf[COEF_F + lane] = f;
-        // the same scans restarted at row 32 (identity maps below it)
-        const bool lo = lane < 32;
-        const float eb = wave_prefix_prod(lo ? 1.f : gl.y);
-        float a2 = lo ? 1.f : gl.x, f2b = lo ? 0.f : eb;
-        wave_affine_scan(a2, f2b);
-        if (!lo) {
-          cf[COEF_T11 + lane - 32] = a2;
-          cf[COEF_T12 + lane - 32] = f2b;
-        }
-        if (lane == 63) ci[INT_T22] = __float_as_int(eb);
+      const bool early_poll = kSplit || w == C::kWD0 || w == C::kWD1;
+      // ================= a1: coefficients, while the exchange is in flight =================
+      if constexpr (kSplit) {
+        key_coef_stage(n);
+        opoll.issue(obases, tid);
+      } else {
+        coef_stage([&] { opoll.issue(obases, tid); });
       }
       // the raw first-layer scores Q K^T (tiles (tj, tc0 + i)) and the query
       // products Q W1^T, Q S1^T
       f4v scr[kT], accW[4], accS[4];
-      if constexpr (kRW) {
-#pragma unroll
-        for (int i = 0; i < kT; ++i) {
-          f4v acc = {};
-          const _Float16* arow = sQ + (16 * tj + lc) * RS;
-          const _Float16* brow = sK + (16 * (tc0 + i) + lc) * RS;
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) acc = mfma(frag_c8(arow, 32 * kk, g), frag_c8(brow, 32 * kk, g), acc);
-          scr[i] = acc;
-        }
-      }
+      if constexpr (kRW && !kSplit) raw_scores(scr);
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         f4v aw = {}, as = {};
@@ -1179,7 +1773,9 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
       float pvv[kG - 1][kE], pyv[kG - 1][kYPer];
       if (!(early_poll && opoll.check(seq, pvv)) && !tpoll<kThreads, kE / 2, kG - 1>(obases, tid, seq, p.spin_max, pvv))
         give_up();
-      if (prev_row0 >= 0) load_prev_y(seq - 1, pyv);
+      if constexpr (!kSplit) {
+        if (prev_row0 >= 0) load_prev_y(seq - 1, pyv);
+      }
       // every vector memory operation of this thread done, the next chunk's
       // staging loads included (a no-op after a poll, which waited for them)
       __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -1199,58 +1795,111 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
         am = wave_max(am);
         if (lane == 0) atomicMax((unsigned int*)&ci[INT_AMAX_D2], __float_as_uint(am));
       }
-      // last chunk's y tiles
-      if (prev_row0 >= 0) finish_prev_y(pyv);
+      if constexpr (kSplit) {
+        // The retrieval workgroup has read this thread's words of chunk
+        // seq - 2 once its receipt carries seq - 2 or seq - 1 (it cannot be
+        // further ahead); then the chunk-start W2, S2 copies and A1 go out.
+        auto acked = [&](unsigned long long wd) { return tag_is(wd, seq - 2) || tag_is(wd, seq - 1); };
+        bool ok = seq <= 2 || acked(ackw);
+        for (unsigned it = 0; !ok && it < p.spin_max; ++it) {
+          __builtin_amdgcn_s_sleep(1);
+          ok = acked(__hip_atomic_load(xA + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        }
+        if (!ok) {
+          give_up();
+        } else {
+          // the W2^T and S2^T copies and A1^T in the order of their tiles'
+          // 4-value rows (16 each), three values a word, then e2 and eA1
+          _Float16 hv[48];
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            const int o = 4 * (ct & 1);
+            const h4 sv = to_h4(S2s[ct], f2);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              hv[4 * ct + r] = w2f[ct >> 1][o + r];
+              hv[16 + 4 * ct + r] = sv[r];
+              hv[32 + 4 * ct + r] = a1f[ct >> 1][o + r];
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < 16; ++k)
+            wstore(pub + (C::PW_1 + k) * kThreads, h3word(hbits(hv[3 * k]), hbits(hv[3 * k + 1]), hbits(hv[3 * k + 2]), seq));
+          wstore(pub + (C::PW_1 + 16) * kThreads, h3word(ebits(e2), ebits(eA1), 0, seq));
+        }
+        // the next chunk's K and Q into the other tile set (waves 0..3, from
+        // their own staging loads, complete since the exchange); its gates
+        // wait until every wave is past the coefficient stage
+        if (staged) {
+          if (w < 4) {
+            const float wnk = wave_max(inputs_to_lds(min(p.chunk, p.N - next_c0), tid,
+                                                     (_Float16*)(smem + ((seq & 1u) ? OFF_K : OFF_YP)),
+                                                     (_Float16*)(smem + ((seq & 1u) ? OFF_Q : OFF_SC)), g3n));
+            if (lane == 0) ci[INT_NK + w] = __float_as_int(wnk);
+          } else if (lane == 0) {
+            ci[INT_NK + w] = 0;   // (max |K| over the pieces of waves 0..3)
+          }
+        }
+      } else {
+        // last chunk's y tiles
+        if (prev_row0 >= 0) finish_prev_y(pyv);
+      }
       STAMP(11);
       __syncthreads();   // every wave's Delta2 amax, the coefficients
       if (ci[INT_FAIL]) { failed = true; break; }
       STAMP(12);
+      // the query products' part of Zq1 (diag(A) Q W1^T + diag(F) Q S1^T) in units of -1/ln 2
+      const float cz = pow2neg(e1) * -kLog2e;
+      auto zq_main = [&](int tt) {
+        f4v m;
+        if constexpr (kRW) {
+          const f4v av = *(const f4v*)(cf + COEF_A + 16 * tt + 4 * g);
+          const f4v fv = *(const f4v*)(cf + COEF_F + 16 * tt + 4 * g);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) m[r] = fmaf(av[r], accW[tt][r], fv[r] * accS[tt][r]) * cz;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) m[r] = accW[tt][r] * cz;
+        }
+        return m;
+      };
 
       // ---- Delta2 (fp16, workgroup-wide scale) as [c][j] ----
       const int eD2 = scale_exp(__uint_as_float((unsigned)ci[INT_AMAX_D2]));
       {
         const float fD2 = pow2pos(eD2);
+        h4 hv[kT];
 #pragma unroll
         for (int i = 0; i < kT; ++i) {
-          h4 hv;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) hv[r] = sc16(d2v[4 * i + r], fD2);
-          *(h4*)(sD2T + (16 * (tc0 + i) + lc) * RS + 16 * tj + 4 * g) = hv;
+          for (int r = 0; r < 4; ++r) hv[i][r] = sc16(d2v[4 * i + r], fD2);
+          *(h4*)(sD2T + (16 * (tc0 + i) + lc) * RS + 16 * tj + 4 * g) = hv[i];
+        }
+        if constexpr (kSplit) {
+          // Delta2 (8 values) and eD2 in three words, then the query
+          // products (eight twords)
+          static_assert(kT == 2, "eight Delta2 values a thread");
+          wstore(pub + (C::PW_2 + 0) * kThreads, h3word(hbits(hv[0][0]), hbits(hv[0][1]), hbits(hv[0][2]), seq));
+          wstore(pub + (C::PW_2 + 1) * kThreads, h3word(hbits(hv[0][3]), hbits(hv[1][0]), hbits(hv[1][1]), seq));
+          wstore(pub + (C::PW_2 + 2) * kThreads, h3word(hbits(hv[1][2]), hbits(hv[1][3]), ebits(eD2), seq));
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            const f4v m = zq_main(tt);
+            wstore(pub + (C::PW_2 + 3 + 2 * tt) * kThreads, tword(m[0], m[1], seq));
+            wstore(pub + (C::PW_2 + 4 + 2 * tt) * kThreads, tword(m[2], m[3], seq));
+          }
         }
       }
-      // ---- first-layer masked scores SC1 = D o (Q K^T), tiles (tj, tc0 + i), this wave's own scale ----
-      if constexpr (kRW) {
-        float sc[kE], am = 0.f;
-#pragma unroll
-        for (int i = 0; i < kT; ++i) {
-          const f4v dt = d_tile(tj, tc0 + i);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sc[4 * i + r] = scr[i][r] * dt[r];
-        }
-        am = wave_max(max_abs(am, sc));
-        const int esc = scale_exp(am);
-        const float fsc = pow2pos(esc);
-#pragma unroll
-        for (int i = 0; i < kT; ++i)
-          store_rows4(sSC, RS, 16 * (tc0 + i) + lc, 16 * tj + 4 * g,
-                      h4{sc16(sc[4 * i], fsc), sc16(sc[4 * i + 1], fsc), sc16(sc[4 * i + 2], fsc),
-                         sc16(sc[4 * i + 3], fsc)});
-        if (lane == 0) ci[INT_ESC + w] = esc;
+      if constexpr (kRW && !kSplit) sc1_store(scr);
+      if constexpr (kSplit) {
+        if (staged && w == 0) gates_to_lds(tid, g3n);
       }
-      if (w == C::kWD0) {
+      if (!kSplit && w == C::kWD0) {
         // weights of the state update: U_i = theta_i prod_{m>i} eta_m and
-        // D[n-1][i], each scaled into (0.5, 1] for fp16 (padding has eta = 1)
+        // D[n-1][i] (padding has eta = 1)
         const int i = lane;
         const float ti = cf[COEF_XT + i];
-        const float ui = i < 32 ? ti * __int_as_float(ci[INT_T22]) : ti;
-        const float dlast = d_full(n - 1, i);
-        const float mu = wave_max(fabsf(ui)), md = wave_max(fabsf(dlast));
-        int eu = 0, ed = 0;
-        if (mu > 0.f && mu < INFINITY) { (void)frexpf(mu, &eu); eu = -eu; }
-        if (md > 0.f && md < INFINITY) { (void)frexpf(md, &ed); ed = -ed; }
-        ch[H16_WU + i] = (_Float16)ldexpf(ui, eu);
-        ch[H16_WD + i] = (_Float16)ldexpf(dlast, ed);
-        if (lane == 0) { ci[INT_EWU] = eu; ci[INT_EWD] = ed; }
+        store_fold_weights(i, i < 32 ? ti * __int_as_float(ci[INT_T22]) : ti, d_full(n - 1, i));
       }
       STAMP(13);
       __syncthreads();   // Delta2 copies, the first-layer scores and the update weights
@@ -1277,41 +1926,21 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
 #pragma unroll
         for (int st = 0; st < 2; ++st) d1f[st] = tiles_frag(Df[2 * st], Df[2 * st + 1], fD1);
       }
+      if constexpr (kSplit) {
+        // Delta1's fragments (16 values) and eD1 in six words
+        unsigned short hv[18];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) hv[e] = hbits(d1f[e >> 3][e & 7]);
+        hv[16] = ebits(eD1);
+        hv[17] = 0;
+#pragma unroll
+        for (int k = 0; k < 6; ++k)
+          wstore(pub + (C::PW_3 + k) * kThreads, h3word(hv[3 * k], hv[3 * k + 1], hv[3 * k + 2], seq));
+      }
 
       STAMP(15);
-      // ================= a5 layer 1: Zq1 = diag(A) Q W1^T + diag(F) Q S1^T - SC1 Delta1 =================
       f4v H1f[4];
-      {
-        float am = 0.f;
-        const float cz = pow2neg(e1) * -kLog2e;   // Zq1 in units of -1/ln 2
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          f4v z;
-          if constexpr (kRW) {
-            // the masked term's two K-steps carry the scales of the waves that produced them
-            f4v m0 = {}, m1v = {};
-            m0 = mfma(frag_tr_rk(sSC, RS, 0, 16 * tt, g, lc), d1f[0], m0);
-            m1v = mfma(frag_tr_rk(sSC, RS, 32, 16 * tt, g, lc), d1f[1], m1v);
-            const float c30 = pow2neg(eD1 + ci[INT_ESC + score_wave(tt, 0)]) * kLog2e,
-                        c31 = pow2neg(eD1 + ci[INT_ESC + score_wave(tt, 1)]) * kLog2e;
-            const f4v av = *(const f4v*)(cf + COEF_A + 16 * tt + 4 * g);
-            const f4v fv = *(const f4v*)(cf + COEF_F + 16 * tt + 4 * g);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float main = fmaf(av[r], accW[tt][r], fv[r] * accS[tt][r]) * cz;
-              z[r] = fmaf(m0[r], c30, fmaf(m1v[r], c31, main));
-            }
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) z[r] = accW[tt][r] * cz;
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) H1f[tt][r] = z[r] * sigmoid_x(z[r]);   // -H1 log2 e
-          am = max4(am, H1f[tt]);
-        }
-        const float wam = wave_max(am);
-        if (lane == 0) ci[INT_MH1 + w] = __float_as_int(wam);
-      }
+      if constexpr (!kSplit) zq1_h1(zq_main, d1f, eD1, H1f);
 
       STAMP(16);
       const float An = cf[COEF_A + n - 1], En = cf[COEF_E + n - 1], Fn = cf[COEF_F + n - 1];
@@ -1349,49 +1978,15 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
         }
       }
       STAMP(17);
-      __syncthreads();   // every wave's H1 maximum
-
-      // H1 with the workgroup-wide scale, copied [u][j] for the scores and y
-      int eH1;
-      {
-        float mm = 0.f;
-#pragma unroll
-        for (int i = 0; i < kWaves; ++i) mm = fmaxf(mm, __int_as_float(ci[INT_MH1 + i]));
-        eH1 = scale_exp(mm * kLn2);   // the waves' maxima are of |H1| log2 e
-        const float fH = pow2pos(eH1) * -kLn2;
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-          store_rows4(sH1, RS, uw + lc, 16 * tt + 4 * g, to_h4(H1f[tt], fH));
+      int eH1 = 0;
+      if constexpr (!kSplit) {
+        __syncthreads();   // every wave's H1 maximum
+        eH1 = h1_copy(H1f);
       }
       STAMP(18);
-      __syncthreads();   // every wave's H1 copy
+      if constexpr (!kSplit) __syncthreads();   // every wave's H1 copy
       STAMP(19);
-
-      // ================= masked second-layer scores D o (H1 A1^T): tiles (tj, tc0 + i) =================
-      if constexpr (kRW) {
-        float pv[kE], am = 0.f;
-        const float cp = pow2neg(eH1 + eA1);
-#pragma unroll
-        for (int i = 0; i < kT; ++i) {
-          f4v acc = {};
-#pragma unroll
-          for (int kk = 0; kk < C::kKSteps; ++kk)
-            acc = mfma(frag_tr_c8(sH1, RS, 32 * kk, 16 * tj, g, lc), frag_tr_c8(sA1, RS, 32 * kk, 16 * (tc0 + i), g, lc),
-                       acc);
-          const f4v dt = d_tile(tj, tc0 + i);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) pv[4 * i + r] = acc[r] * cp * dt[r];
-        }
-        am = wave_max(max_abs(am, pv));
-        const int edp = scale_exp(am);
-        const float fdp = pow2pos(edp);
-#pragma unroll
-        for (int i = 0; i < kT; ++i)
-          store_rows4(sSC, RS, 16 * (tc0 + i) + lc, 16 * tj + 4 * g,
-                      h4{sc16(pv[4 * i], fdp), sc16(pv[4 * i + 1], fdp), sc16(pv[4 * i + 2], fdp),
-                         sc16(pv[4 * i + 3], fdp)});
-        if (lane == 0) ci[INT_EDP + w] = edp;
-      }
+      if constexpr (kRW && !kSplit) p_scores(eH1, eA1);
 
       STAMP(20);
       // ================= a4, layer 2: G2^T[c][u] = sum_j Delta2[j][c] w_j A1[j][u] =================
@@ -1418,131 +2013,9 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
         }
       }
       STAMP(21);
-      __syncthreads();   // every wave's second-layer scores
-
-      // ================= a5 layer 2: y = diag(A) H1 W2^T + diag(F) H1 S2^T - (D o P) Delta2 =================
-      if constexpr (NW == 8) {
-        // Four 32 x 32 blocks on v_mfma_f32_32x32x16_f16, one per wave of
-        // waves 0..3 (one per SIMD): block (jb, cb) = (32 (w >> 1), 32 (w & 1)).
-        // Each operand block is read from LDS once per block, against twice
-        // (H1, P) or four times (W2^T, S2^T, Delta2^T) over the eight waves'
-        // 16 x 16 tile pairs; the stage is bound by these reads.
-        if (w < 4) {
-          const int jb = 32 * (w >> 1), cb = 32 * (w & 1);
-          const int l32 = lane & 31, hk = lane >> 5, grp16 = lane >> 4;
-          // fragment of block columns n0 .. n0 + 31 over K rows kb .. kb + 15 of a K-major tile
-          auto fr32 = [&](const _Float16* T, int kb, int n0) {
-            const int k0 = kb + 8 * (grp16 >> 1), nn = n0 + 16 * (grp16 & 1);
-            const h4 lo = tr4(T, RS, k0, nn, lc), hi = tr4(T, RS, k0 + 4, nn, lc);
-            return h8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          };
-          f16v aw = {}, as = {};
-#pragma unroll
-          for (int ks = 0; ks < kUG / 16; ++ks) {
-            const h8 hf = fr32(sH1, 16 * ks, jb);
-            aw = mfma32(hf, fr32(sW2, 16 * ks, cb), aw);
-            if constexpr (kRW) as = mfma32(hf, fr32(sS2, 16 * ks, cb), as);
-          }
-          if constexpr (kRW) {
-            // operand reads two K-steps ahead of the products (the reads'
-            // latency, not the matrix unit, bounds the chain otherwise)
-            __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
-#pragma unroll
-            for (int ks = 0; ks < kUG / 16; ++ks) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-              if (ks + 2 < kUG / 16) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-            }
-          }
-          float yv[16];
-          const float cy = pow2neg(eH1 + e2);
-          if constexpr (kRW) {
-            // the masked term over keys 0..31 and 32..63 separately: each half
-            // of a query tile's scores carries the scale of the wave that produced it
-            f16v m0 = {}, m1v = {};
-            const _Float16* drow = sD2T + (cb + l32) * RS + 8 * hk;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) m0 = mfma32(fr32(sSC, 16 * ks, jb), *(const h8*)(drow + 16 * ks), m0);
-#pragma unroll
-            for (int ks = 2; ks < 4; ++ks) m1v = mfma32(fr32(sSC, 16 * ks, jb), *(const h8*)(drow + 16 * ks), m1v);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int tjq = (jb >> 4) + (q >> 1);   // the query tile of rows jb + 8q + 4hk ..
-              const float c30 = pow2neg(eD2 + ci[INT_EDP + score_wave(tjq, 0)]),
-                          c31 = pow2neg(eD2 + ci[INT_EDP + score_wave(tjq, 1)]);
-              const f4v av = *(const f4v*)(cf + COEF_A + jb + 8 * q + 4 * hk);
-              const f4v fv = *(const f4v*)(cf + COEF_F + jb + 8 * q + 4 * hk);
-#pragma unroll
-              for (int rr = 0; rr < 4; ++rr) {
-                const int r = 4 * q + rr;
-                const float main = fmaf(av[rr], aw[r], fv[rr] * as[r]) * cy;
-                yv[r] = fmaf(m0[r], -c30, fmaf(m1v[r], -c31, main));
-              }
-            }
-          } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) yv[r] = aw[r] * cy;
-          }
-          // keep the block if its rows are this workgroup's, else send them
-          // (element / word indexing of the owner's rows as in finish_prev_y)
-          const int owner = jb / C::kYRows;
-          if (owner == h) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              ypark[(jb + 8 * (r >> 2) + 4 * hk + (r & 3) - C::kYRows * h) * kD + cb + l32] = yv[r];
-          } else {
-            unsigned long long* yb = xY(h, (owner - h - 1 + kG) % kG, par);
-#pragma unroll
-            for (int r = 0; r < 16; r += 2)
-              tstore(yb, ((jb + 8 * (r >> 2) + 4 * hk + (r & 3) - C::kYRows * owner) / 2) * kD + cb + l32, yv[r],
-                     yv[r + 1], seq);
-          }
-        }
-      } else {
-      {
-        float yv[kE];
-        const float cy = pow2neg(eH1 + e2);
-        const f4v av = *(const f4v*)(cf + COEF_A + 16 * tj + 4 * g);
-        const f4v fv = *(const f4v*)(cf + COEF_F + 16 * tj + 4 * g);
-#pragma unroll
-        for (int i = 0; i < kT; ++i) {
-          const int crow = 16 * (tc0 + i) + lc;
-          f4v aw = {}, as = {};
-#pragma unroll
-          for (int kk = 0; kk < C::kKSteps; ++kk) {
-            const h8 hf = frag_tr_c8(sH1, RS, 32 * kk, 16 * tj, g, lc);
-            aw = mfma(hf, frag_tr_c8(sW2, RS, 32 * kk, 16 * (tc0 + i), g, lc), aw);
-            if constexpr (kRW) as = mfma(hf, frag_tr_c8(sS2, RS, 32 * kk, 16 * (tc0 + i), g, lc), as);
-          }
-          if constexpr (kRW) {
-            f4v m0 = {}, m1v = {};
-            m0 = mfma(frag_tr_c8(sSC, RS, 0, 16 * tj, g, lc), frag_c8(sD2T + crow * RS, 0, g), m0);
-            m1v = mfma(frag_tr_c8(sSC, RS, 32, 16 * tj, g, lc), frag_c8(sD2T + crow * RS, 32, g), m1v);
-            const float c30 = pow2neg(eD2 + ci[INT_EDP + score_wave(tj, 0)]),
-                        c31 = pow2neg(eD2 + ci[INT_EDP + score_wave(tj, 1)]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float main = fmaf(av[r], aw[r], fv[r] * as[r]) * cy;
-              yv[4 * i + r] = fmaf(m0[r], -c30, fmaf(m1v[r], -c31, main));
-            }
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) yv[4 * i + r] = aw[r] * cy;
-          }
-        }
-        // keep my rows, send the other rows to the workgroup that finishes them
-        if (keeps_y) {
-#pragma unroll
-          for (int i = 0; i < kT; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ypark[y_elem(i, r)] = yv[4 * i + r];
-        } else {
-          unsigned long long* yb = xY(h, (y_owner - h - 1 + kG) % kG, par);
-#pragma unroll
-          for (int i = 0; i < kT; ++i)
-#pragma unroll
-            for (int rp = 0; rp < 2; ++rp) tstore(yb, y_word(i, rp), yv[4 * i + 2 * rp], yv[4 * i + 2 * rp + 1], seq);
-        }
-      }
+      if constexpr (!kSplit) {
+        __syncthreads();   // every wave's second-layer scores
+        y_stage(eH1, e2, eD2, par);
       }
       // the new state's maxima for the next chunk's operand scales (reduced
       // here, once the fold's products have long completed)
@@ -1560,7 +2033,9 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
         if (staged) {
           if (w >= 4) {
             const int nn = min(p.chunk, p.N - next_c0);
-            const float wnk = wave_max(inputs_to_lds(nn, tid - 256));
+            float3 g3;
+            const float wnk = wave_max(inputs_to_lds(nn, tid - 256, sK, sQ, g3));
+            gates_to_lds(tid - 256, g3);
             if (lane == 0) ci[INT_NK + w] = __float_as_int(wnk);
             int s2 = next_s, c2 = next_c0 + p.chunk, i2 = next_ci + 1;
             if (c2 >= p.N) { s2 = next_s + p.n_groups; c2 = 0; i2 = 0; }
@@ -1582,6 +2057,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
           staged = s2 < p.streams;
         }
       }
+      if constexpr (kSplit) pre = staged;
       STAMP(22);
       prev_row0 = tok0 + c0;
       prev_n = n;
@@ -1590,6 +2066,19 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
     }
 
     if (failed) break;
+    if constexpr (kSplit) {
+      // The retrieval workgroup has read the stream's last words before the
+      // state goes out: a give-up of it until then (which poisons the
+      // stream's outputs) never precedes this write.
+      bool ok = tag_is(__hip_atomic_load(xA + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), seq);
+      for (unsigned it = 0; !ok && it < p.spin_max; ++it) {
+        __builtin_amdgcn_s_sleep(1);
+        ok = tag_is(__hip_atomic_load(xA + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), seq);
+      }
+      if (!ok) give_up();
+      __syncthreads();
+      if (ci[INT_FAIL]) { failed = true; break; }
+    }
     // ---- write this wave's part of the final state ----
     {
       float* Wo = p.W_out + (int64_t)s * kP;
@@ -1610,7 +2099,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
   }
 
   // the last chunk's y rows
-  if (!failed && prev_row0 >= 0) {
+  if (!kSplit && !failed && prev_row0 >= 0) {
     float pyv[kG - 1][kYPer];
     load_prev_y(seq, pyv);
     finish_prev_y(pyv);   // (rows of a wait that gave up are overwritten below)
@@ -1638,7 +2127,16 @@ using GrpUsed = Grp<8>;
 static int64_t groups_for(const Shape& s) {
   return s.streams < GrpUsed::kMaxGroups ? s.streams : GrpUsed::kMaxGroups;
 }
-static int64_t group_bytes(const Shape&) { return GrpUsed::kGroupBytes; }
+// With few streams (at most a quarter as many as a 256-CU device has CUs)
+// and retrieval after each write, each half's retrieval runs on a workgroup
+// of its own (kSplit), four workgroups per stream, when the device holds
+// them all at once; the workspace then also holds the hand-over words.
+static bool split_shape(const Shape& s) {
+  return s.read_mode == TM_READ_AFTER_WRITE && s.streams <= GrpUsed::kMaxGroupsSplit;
+}
+static int64_t group_bytes(const Shape& s) {
+  return split_shape(s) ? GrpUsed::kGroupBytesSplit : GrpUsed::kGroupBytes;
+}
 
 int64_t mlp2_ws_bytes(const Shape& s, int) { return groups_for(s) * group_bytes(s) + 256; }
 
@@ -1654,7 +2152,11 @@ int64_t mlp2_status_offset(const Shape& s) { return groups_for(s) * group_bytes(
 // array; every call clears the exchange buffers and the status word with a
 // fill kernel (no memset) before the memory kernel, so calls that follow one
 // another are independent, while calls that overlap on one GPU race.
-constexpr int64_t kScratchBytes = GrpUsed::kMaxGroups * GrpUsed::kGroupBytes + 256;
+constexpr int64_t kScratchBytes =
+    (GrpUsed::kMaxGroups * GrpUsed::kGroupBytes > GrpUsed::kMaxGroupsSplit * GrpUsed::kGroupBytesSplit
+         ? GrpUsed::kMaxGroups * GrpUsed::kGroupBytes
+         : GrpUsed::kMaxGroupsSplit * GrpUsed::kGroupBytesSplit) +
+    256;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
@@ -1705,15 +2207,19 @@ static hipError_t launch_group(const Shape& s, int chunk, const void* k, const v
   int64_t ng = groups_for(s);
   if (ng > cus / C::kG) ng = cus / C::kG;
   if (ng < 1) return hipErrorInvalidConfiguration;
-  // each chunk's inputs moved into LDS during the previous chunk only while
-  // at most half the CUs run a workgroup: 2% faster with few streams, 1%
-  // slower with every CU busy
-  const bool early = NW == 8 && 2 * C::kG * ng <= cus;
   const bool rw = s.read_mode == TM_READ_AFTER_WRITE;
-  const void* kfn = rw ? (early ? (const void*)mlp2_group_kernel<true, NW, true>
-                                : (const void*)mlp2_group_kernel<true, NW, false>)
-                       : (early ? (const void*)mlp2_group_kernel<false, NW, true>
-                                : (const void*)mlp2_group_kernel<false, NW, false>);
+  // the retrieval on workgroups of its own while every group's four fit at once
+  const bool split = NW == 8 && split_shape(s) && 2 * C::kG * ng <= cus;
+  // otherwise each chunk's inputs moved into LDS during the previous chunk
+  // only while at most half the CUs run a workgroup: 2% faster with few
+  // streams, 1% slower with every CU busy
+  const bool early = !split && NW == 8 && 2 * C::kG * ng <= cus;
+  const void* kfn = rw ? (early ? (const void*)mlp2_group_kernel<true, NW, true, false>
+                                : (const void*)mlp2_group_kernel<true, NW, false, false>)
+                       : (early ? (const void*)mlp2_group_kernel<false, NW, true, false>
+                                : (const void*)mlp2_group_kernel<false, NW, false, false>);
+  if constexpr (NW == 8)
+    if (split) kfn = (const void*)mlp2_group_kernel<true, NW, false, true>;
   // the kernel's dynamic LDS size, set on every call (no state kept between
   // calls; idempotent and cheap next to the kernel)
   e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
@@ -1740,20 +2246,24 @@ static hipError_t launch_group(const Shape& s, int chunk, const void* k, const v
   p.spin_max = (s.flags & TM_FLAG_NO_WAIT) ? 0u : kSpinMax;
   p.chunk_gates = s.chunk_gates;
   p.gstride = s.chunk_gates ? (s.N + chunk - 1) / chunk : s.N;
-  const int64_t n16 = ng * C::kGroupBytes / 16;
+  const int64_t n16 = ng * (split ? C::kGroupBytesSplit : C::kGroupBytes) / 16;
   hipLaunchKernelGGL(zero_exchange_kernel, dim3((unsigned)std::min<int64_t>((n16 + 255) / 256, 1024)), dim3(256), 0,
                      stream, (uint4*)base, n16, p.status);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)(C::kG * ng)), block(C::kThreads);
-  if (rw && early)
-    hipLaunchKernelGGL((mlp2_group_kernel<true, NW, true>), grid, block, C::kLdsBytes, stream, p);
-  else if (rw)
-    hipLaunchKernelGGL((mlp2_group_kernel<true, NW, false>), grid, block, C::kLdsBytes, stream, p);
-  else if (early)
-    hipLaunchKernelGGL((mlp2_group_kernel<false, NW, true>), grid, block, C::kLdsBytes, stream, p);
-  else
-    hipLaunchKernelGGL((mlp2_group_kernel<false, NW, false>), grid, block, C::kLdsBytes, stream, p);
+  const dim3 grid((unsigned)((split ? 2 : 1) * C::kG * ng)), block(C::kThreads);
+  if (split) {
+    if constexpr (NW == 8)
+      hipLaunchKernelGGL((mlp2_group_kernel<true, NW, false, true>), grid, block, C::kLdsBytes, stream, p);
+  } else if (rw && early) {
+    hipLaunchKernelGGL((mlp2_group_kernel<true, NW, true, false>), grid, block, C::kLdsBytes, stream, p);
+  } else if (rw) {
+    hipLaunchKernelGGL((mlp2_group_kernel<true, NW, false, false>), grid, block, C::kLdsBytes, stream, p);
+  } else if (early) {
+    hipLaunchKernelGGL((mlp2_group_kernel<false, NW, true, false>), grid, block, C::kLdsBytes, stream, p);
+  } else {
+    hipLaunchKernelGGL((mlp2_group_kernel<false, NW, false, false>), grid, block, C::kLdsBytes, stream, p);
+  }
   return hipGetLastError();
 }
 

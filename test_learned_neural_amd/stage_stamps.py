@@ -5,11 +5,13 @@
     python -m test_learned_neural_amd.stage_stamps --isa     # instruction mix per stage (CPU, static)
 
 The instrumented build (-DTM_STAGE_STAMPS=1, a separate library beside the
-product one) makes the eight waves of workgroup 0 record the shader clock at
-every stage boundary of 64 chunks of its first stream.  The table gives, per
-stage, the median over those chunks of each wave's cycles, as the minimum,
-median and maximum over the waves (the maximum across waves is what the
-barrier that follows waits for).
+product one) makes the eight waves of the first key-side workgroup record the
+shader clock at every stage boundary of 64 chunks of its first stream.  With
+--retrieval (build and run) the stamps come from the first retrieval
+workgroup of a few-stream launch instead (-DTM_STAMP_R=1, a library of its
+own).  The table gives, per stage, the median over those chunks of each
+wave's cycles, as the minimum, median and maximum over the waves (the
+maximum across waves is what the barrier that follows waits for).
 """
 from __future__ import annotations
 
@@ -21,6 +23,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 STAMPS_LIB = os.path.join(PKG, "libtitans_mem_stamps.so")
+STAMPS_R_LIB = os.path.join(PKG, "libtitans_mem_stamps_r.so")
 STAGES = 24
 WAVES = 8
 CHUNKS = 64
@@ -51,11 +54,42 @@ STAGE_NAMES = [
     "barrier (end of chunk)",
 ]
 
+STAGE_NAMES_R = [
+    "chunk inputs into LDS",
+    "barrier; next chunk's prefetch; copies' words requested",
+    "coefficients",
+    "raw scores Q K^T",
+    "barrier",
+    "masked scores SC1; remaining words requested",
+    "wait: W2, S2 copies and A1",
+    "wait: Delta2 and the query products",
+    "wait: Delta1; receipt",
+    "copies into LDS; last chunk's y finished",
+    "barrier",
+    "Zq1, H1 = SiLU",
+    "barrier",
+    "H1 copy",
+    "barrier",
+    "masked scores D o (H1 A1^T)",
+    "barrier",
+    "y tiles, kept or sent",
+    "barrier (end of chunk)",
+    "(empty)",
+    "(empty)",
+    "(empty)",
+    "(empty)",
+]
 
-def build():
+
+def build(retrieval: bool = False):
     sys.path.insert(0, ROOT)
     from test_learned_neural_amd import build as b
-    b.build(verbose=True, extra=["-DTM_STAGE_STAMPS=1"], out=STAMPS_LIB, build_dir=os.path.join(ROOT, "_build", "stamps"))
+    if retrieval:
+        b.build(verbose=True, extra=["-DTM_STAGE_STAMPS=1", "-DTM_STAMP_R=1"], out=STAMPS_R_LIB,
+                build_dir=os.path.join(ROOT, "_build", "stamps_r"))
+    else:
+        b.build(verbose=True, extra=["-DTM_STAGE_STAMPS=1"], out=STAMPS_LIB,
+                build_dir=os.path.join(ROOT, "_build", "stamps"))
 
 
 def isa():
@@ -75,7 +109,7 @@ def isa():
                               b.PER_FILE["tm_mlp2_group.hip"] + ["--cuda-device-only", "-S", src, "-o", out],
                               stderr=subprocess.DEVNULL)
         lines = open(out).read().split("\n")
-    start = next(i for i, l in enumerate(lines) if re.match(r"^_Z\S*mlp2_group_kernelILb1ELi8ELb0E\S*:", l))
+    start = next(i for i, l in enumerate(lines) if re.match(r"^_Z\S*mlp2_group_kernelILb1ELi8ELb0ELb0E\S*:", l))
     end = next(i for i in range(start, len(lines)) if "s_endpgm" in lines[i])
     body = lines[start:end]
     stamps = [i for i, l in enumerate(body) if "s_memtime" in l]
@@ -117,15 +151,17 @@ def isa():
     print(f"  {'total':<62s}" + "".join(f"{tot[c]:7d}" for c in classes))
 
 
-def run(steps: int = 2, per_wave: bool = False, workload: str = "headline"):
+def run(steps: int = 2, per_wave: bool = False, workload: str = "headline", retrieval: bool = False):
     import numpy as np
     import torch
     sys.path.insert(0, ROOT)
     from test_learned_neural_amd import titans_mem as tmm
     from test_learned_neural_amd import workloads as wl
-    if not os.path.exists(STAMPS_LIB):
-        raise SystemExit(f"{STAMPS_LIB} is missing: run with --build first")
-    tmm.LIB_PATH = STAMPS_LIB
+    lib_path = STAMPS_R_LIB if retrieval else STAMPS_LIB
+    names = STAGE_NAMES_R if retrieval else STAGE_NAMES
+    if not os.path.exists(lib_path):
+        raise SystemExit(f"{lib_path} is missing: run with --build first")
+    tmm.LIB_PATH = lib_path
     lib = tmm.load()
     cfg = wl.WORKLOADS[workload]
     inp = wl.make_inputs(cfg, workers=16)
@@ -150,7 +186,7 @@ def run(steps: int = 2, per_wave: bool = False, workload: str = "headline"):
     print(f"{cfg.name}: cycles per stage (median over {CHUNKS} chunks; min / median / max over {WAVES} waves)")
     for k in range(STAGES - 1):
         row = med[:, k]
-        print(f"  {k + 1:2d} {STAGE_NAMES[k]:<58s} {row.min():7.0f} {np.median(row):7.0f} {row.max():7.0f}")
+        print(f"  {k + 1:2d} {names[k]:<58s} {row.min():7.0f} {np.median(row):7.0f} {row.max():7.0f}")
     if per_wave:
         print("  per wave (median over chunks), waves 0..%d:" % (WAVES - 1))
         for k in range(STAGES - 1):
@@ -165,5 +201,12 @@ if __name__ == "__main__":
     ap.add_argument("--isa", action="store_true")
     ap.add_argument("--per-wave", action="store_true", help="also print every wave's median per stage")
     ap.add_argument("--workload", default="headline", help="a 2-layer d=64 h=256 workload of workloads.py")
+    ap.add_argument("--retrieval", action="store_true",
+                    help="stamps of the first retrieval workgroup (few-stream workloads only)")
     a = ap.parse_args()
-    build() if a.build else isa() if a.isa else run(per_wave=a.per_wave, workload=a.workload)
+    if a.build:
+        build(a.retrieval)
+    elif a.isa:
+        isa()
+    else:
+        run(per_wave=a.per_wave, workload=a.workload, retrieval=a.retrieval)
