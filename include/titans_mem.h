@@ -183,10 +183,11 @@ int titans_mem_forward(const titans_mem_desc* desc,
  * workspace, for the shapes of the MFMA path (TM_PATH_MLP2_D64_H256:
  * 2-layer, d = 64, hidden = 256, bf16 io, chunk <= 64; any B*H, N and read
  * mode); TM_ERR_UNSUPPORTED for every other shape.  Its scratch (the
- * paired workgroups' tagged exchange words and the status word) is a
- * library-owned device array of 12,583,168 bytes (12 MiB + 256: enough for
- * the kernel's largest grid of 128 workgroup pairs; TM_ERR_WORKSPACE if a
- * shape ever needed more), one per GPU,
+ * workgroups' tagged exchange and hand-over words and the status word) is a
+ * library-owned device array of 42,467,584 bytes (40.5 MiB + 256: enough for
+ * the kernel's largest grids, 128 workgroup pairs or, with at most 64
+ * streams, 64 groups of four workgroups; TM_ERR_WORKSPACE if a shape ever
+ * needed more), one per GPU,
  * allocated with the library's code and held until the process ends.  The
  * call allocates nothing: it enqueues a small fill kernel and the memory
  * kernel on `stream`.  The first call on a device looks up the array's
