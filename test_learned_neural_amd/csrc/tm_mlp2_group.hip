@@ -1412,9 +1412,6 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
           __syncthreads();   // every wave's second-layer scores
           STAMP(17);
           y_stage(eH1, e2, eD2, par);
-          // The receipt for this chunk's words (read long ago; sent only now,
-          // since any later wait for a load would also wait for this store)
-          if (got) __hip_atomic_store(xA + tid, tword(0.f, 0.f, seq), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           // the next chunk's inputs into their tiles (waves 4..7, beside y
           // on waves 0..3; K and Q are not read after the raw scores), then
           // the chunk after it into the staging area
@@ -1439,6 +1436,9 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
               __builtin_amdgcn_s_waitcnt(0x0F70);
             }
           }
+          // The receipt for this chunk's words (read long ago; sent last, as
+          // any later wait for a load would also wait for this store)
+          if (got) __hip_atomic_store(xA + tid, tword(0.f, 0.f, seq), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           pre = staged;
           if (staged) {
             int s2 = next_s, c2 = next_c0 + p.chunk;
