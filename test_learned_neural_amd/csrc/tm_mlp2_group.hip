@@ -68,6 +68,12 @@
 //   and y of every stream the pair serves.  Sums are formed in a fixed order
 //   (half 0 + half 1), so results are bitwise reproducible and identical in
 //   both halves.
+// * With few streams (at most a quarter as many as CUs) each half's
+//   retrieval runs on a workgroup of its own, one chunk behind (kSplit):
+//   the key-side workgroup hands it the chunk-start W2/S2 copies, A1, Delta2,
+//   Delta1 and the query products in the same tagged words, and the
+//   retrieval workgroup computes the masked scores, H1 and y.  A stream
+//   then keeps four CUs busy, and each side's chunk is the shorter for it.
 #include "tm_internal.h"
 
 #include <hip/hip_bf16.h>

@@ -95,6 +95,18 @@ def test_mlp2_ragged_and_small_chunks(B, H, N, chunk):
     _check(cfg, inp, out, run_oracle(cfg, inp))
 
 
+@pytest.mark.parametrize("B,H,N", [(8, 8, 256), (4, 9, 200)])
+def test_mlp2_split_full_grid_and_unaligned_groups(B, H, N):
+    """Few-stream launches run each half's retrieval on a workgroup of its
+    own (four workgroups per stream, at most 64 streams): 64 streams fill
+    all 256 CUs, and 36 streams give a grid (144) that is not a multiple of
+    32, so groups are formed without the XCD-aware placement."""
+    cfg = wl.WORKLOADS["mlp2_short"].with_(B=B, H=H, N=N)
+    inp = wl.make_inputs(cfg, workers=8)
+    out = run_gpu(cfg, to_device(cfg, inp))
+    _check(cfg, inp, out, run_oracle(cfg, inp, threads=16))
+
+
 def test_mlp2_more_streams_than_resident_pairs():
     # 160 streams > 128 resident pairs: some pairs run two streams back to back
     cfg = wl.WORKLOADS["headline"].with_(B=10, H=16, N=192)
