@@ -1268,13 +1268,14 @@ __global__ void __launch_bounds__(64 * NW, 1) mlp2_group_kernel(Params p) {
 
   // ================= the retrieval workgroup of half h (kSplit) =================
   // Per chunk: the inputs, the coefficients and the first-layer masked
-  // scores of its own; the key side's words of the chunk (loads issued before
-  // that work, so that a workgroup behind the key side finds them arrived),
-  // then a5 exactly as the unsplit kernel runs it.  The receipt sent once the
-  // words are read lets the key side reuse their slot two chunks later; the
-  // y rows cross between the retrieval pair as in the unsplit kernel, one
-  // chunk late.  The partner's y of chunk seq - 1 is read before this
-  // chunk's y is sent, so a slot is rewritten only after it was read.
+  // scores of its own; the key side's words of the chunk (partly requested
+  // before that work, so that a workgroup behind the key side finds them
+  // arrived), then a5 exactly as the unsplit kernel runs it.  The receipt,
+  // sent at the end of the chunk, lets the key side reuse the words' slot
+  // two chunks later; the y rows cross between the retrieval pair as in the
+  // unsplit kernel, one chunk late.  The partner's y of chunk seq - 1 is read
+  // before this chunk's y is sent, so a slot is rewritten only after it was
+  // read.
   if constexpr (kSplit) {
     if (is_r) {
       for (int s = grp; s < p.streams && !failed; s += p.n_groups) {
