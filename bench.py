@@ -31,7 +31,8 @@ DOMINANT_KERNEL = {"mlp2_d64_h256_mfma": ("mlp2_group_kernel", ("tm_mlp2_group.h
                    "generic_f32": ("generic_kernel", ("tm_generic.hip", "tm_block_gemm.h")),
                    "input_side": ("input_kernel", ("tm_input.hip",)),
                    "retrieve_mlp2": ("mlp2_retrieve_kernel", ("tm_retrieve.hip",)),
-                   "backward": ("backward_kernel", ("tm_backward.hip", "tm_generic.hip", "tm_block_gemm.h"))}
+                   "backward": ("backward_kernel", ("tm_backward.hip", "tm_generic.hip", "tm_block_gemm.h")),
+                   "deep_bf16_mfma": ("deep_read_kernel", ("tm_deep.hip",))}
 
 
 def _source_digest(srcs):
@@ -449,10 +450,12 @@ def main():
     value = mem_tokens / (ms_per_step / 1e3)
     flops_tok, bytes_tok = algorithmic_work(cfg)
     avg_launch_s = float(np.mean(launch_ms)) / 1e3
-    dtype = "f32" if path == tmm.PATH_GENERIC_F32 else "f16"
+    # the arithmetic type of each path's products: fp32 (generic), scaled fp16
+    # operands (the 2-layer d=64 kernel), bf16 operands (deep memories); sums fp32
+    dtype = {tmm.PATH_GENERIC_F32: "f32", tmm.PATH_MLP2_D64_H256: "f16", tmm.PATH_DEEP_BF16: "bf16"}[path]
     achieved = flops_tok * mem_tokens / avg_launch_s / 1e12
     peak = PEAK_TFLOPS[dtype]
-    bound = "mfma"   # both paths run their contractions on the matrix cores (fp16 / fp32 operands)
+    bound = "mfma"   # every path runs its contractions on the matrix cores
     print(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step, event avg {np.mean(launch_ms):.3f} ms, "
           f"min {np.min(launch_ms):.3f} ms; {achieved:.1f} TFLOP/s; HBM {bytes_tok * mem_tokens / avg_launch_s / 1e9:.0f} GB/s",
           file=sys.stderr, flush=True)
@@ -481,7 +484,8 @@ def main():
               flush=True)
 
     kernel_path_name = {tmm.PATH_GENERIC_F32: "generic_f32",
-                        tmm.PATH_MLP2_D64_H256: "mlp2_d64_h256_mfma"}.get(path, str(path))
+                        tmm.PATH_MLP2_D64_H256: "mlp2_d64_h256_mfma",
+                        tmm.PATH_DEEP_BF16: "deep_bf16_mfma"}.get(path, str(path))
     out = {
         "metric": "memory tokens/sec (retrieve + chunked update), 1 GPU",
         "value": value,

@@ -100,6 +100,10 @@ extern "C" {
 #define TM_PATH_GENERIC_F32   0   /* any shape: fp32 (matrix instructions), state in global memory */
 #define TM_PATH_MLP2_D64_H256 1   /* 2-layer, d=64, hidden=256, chunk<=64, bf16 io, either read mode:
                                      MFMA, register-resident state */
+#define TM_PATH_DEEP_BF16     2   /* MLP (n_layers >= 2) with d and hidden multiples of 64, chunk<=256,
+                                     bf16 io, N >= 1, either read mode: bf16 MFMA products with fp32
+                                     sums, fp32 state in W_out/S_out; every step of a chunk one launch
+                                     over all streams, the reads on the library's second stream */
 
 typedef struct {
     int32_t abi_version;  /* must equal TITANS_MEM_ABI_VERSION */

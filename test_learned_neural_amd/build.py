@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
 SOURCES = ["tm_host.cpp", "tm_generic.hip", "tm_linear.hip", "tm_mlp2_group.hip", "tm_input.hip", "tm_backward.hip",
-           "tm_retrieve.hip"]
+           "tm_retrieve.hip", "tm_deep.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-I" + CSRC]
 # no packed fp32 instructions in device code (v_pk_* fp32 forms)

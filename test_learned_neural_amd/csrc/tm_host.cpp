@@ -62,12 +62,14 @@ int select_path(const titans_mem_desc* desc, const Shape& s, int chunk) {
   if (chunk <= 0) return TM_ERR_INVALID;
   if (!(desc->flags & TM_FLAG_FORCE_GENERIC) && titans::mlp2_supported(s, chunk))
     return TM_PATH_MLP2_D64_H256;
+  if (!(desc->flags & TM_FLAG_FORCE_GENERIC) && titans::deep_supported(s, chunk)) return TM_PATH_DEEP_BF16;
   if (chunk > titans::kMaxChunkGeneric || s.maxw > titans::kMaxWidthGeneric) return TM_ERR_UNSUPPORTED;
   return TM_PATH_GENERIC_F32;
 }
 
 int64_t workspace_for(const Shape& s, int path, int chunk) {
   if (path == TM_PATH_MLP2_D64_H256) return titans::mlp2_ws_bytes(s, chunk);
+  if (path == TM_PATH_DEEP_BF16) return titans::deep_ws_bytes(s, chunk);
   return titans::generic_forward_ws_floats_per_stream(s, chunk) * (int64_t)sizeof(float) * s.streams;
 }
 
@@ -177,6 +179,8 @@ int titans_mem_forward(const titans_mem_desc* desc, const void* k, const void* v
   if (path == TM_PATH_MLP2_D64_H256)
     err = titans::launch_mlp2(s, chunk, k, v, q, alpha, eta, theta, W_in, S_in, y_out, W_out, S_out,
                           workspace, st);
+  else if (path == TM_PATH_DEEP_BF16)
+    err = titans::launch_deep(s, chunk, k, v, q, alpha, eta, theta, W_in, S_in, y_out, W_out, S_out, workspace, st);
   else
     err = titans::launch_generic(s, chunk, k, v, q, alpha, eta, theta, W_in, S_in, y_out, W_out,
                              S_out, (float*)workspace, st);

@@ -81,6 +81,14 @@ hipError_t launch_mlp2(const Shape& s, int chunk, const void* k, const void* v, 
                        const float* W_in, const float* S_in, void* y, float* W_out,
                        float* S_out, void* ws, hipStream_t stream);
 
+// Deep memories on the matrix cores: L >= 2, widths multiples of 64, bf16 io,
+// chunk <= 256; one launch per step of a chunk over all streams.
+bool deep_supported(const Shape& s, int chunk);
+int64_t deep_ws_bytes(const Shape& s, int chunk);
+hipError_t launch_deep(const Shape& s, int chunk, const void* k, const void* v, const void* q, const float* alpha,
+                       const float* eta, const float* theta, const float* W_in, const float* S_in, void* y,
+                       float* W_out, float* S_out, void* ws, hipStream_t stream);
+
 // Retrieval at a fixed state on the matrix cores (2-layer, d=64, hidden=256, bf16).
 bool retrieve_mlp2_supported(const Shape& s);
 hipError_t launch_retrieve_mlp2(const Shape& s, const void* q, const float* W, void* y, hipStream_t stream);

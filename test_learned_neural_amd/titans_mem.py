@@ -20,7 +20,7 @@ READ_AFTER_WRITE, READ_CHUNK_START = 0, 1
 FLAG_FORCE_GENERIC = 1
 FLAG_CHUNK_GATES = 2
 FLAG_NO_WAIT = 4
-PATH_GENERIC_F32, PATH_MLP2_D64_H256 = 0, 1
+PATH_GENERIC_F32, PATH_MLP2_D64_H256, PATH_DEEP_BF16 = 0, 1, 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtitans_mem.so")
 

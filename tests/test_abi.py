@@ -43,7 +43,15 @@ def test_param_count_and_paths(lib):
     d1 = tmm.make_desc(1, 1, 1024, 64, 0, 1, "f32")
     assert tmm.param_count(d1) == 64 * 64
     assert tmm.select_path(d1, 16) == tmm.PATH_GENERIC_F32
-    assert tmm.select_path(d5, 128) == tmm.PATH_GENERIC_F32
+    # the deep-memory matrix-core path: bf16 MLPs with widths a multiple of 64, chunks 1..256, N >= 1
+    assert tmm.select_path(d5, 128) == tmm.PATH_DEEP_BF16
+    assert tmm.select_path(d5, 256) == tmm.PATH_DEEP_BF16
+    assert tmm.select_path(d5, 257) == tmm.PATH_GENERIC_F32
+    assert tmm.select_path(tmm.make_desc(4, 8, 32768, 128, 512, 4, "f32"), 128) == tmm.PATH_GENERIC_F32
+    assert tmm.select_path(tmm.make_desc(4, 8, 32768, 128, 500, 4, "bf16"), 128) == tmm.PATH_GENERIC_F32
+    assert tmm.select_path(tmm.make_desc(4, 8, 0, 128, 512, 4, "bf16"), 128) == tmm.PATH_GENERIC_F32
+    assert tmm.select_path(tmm.make_desc(4, 8, 32768, 128, 512, 4, "bf16", flags=tmm.FLAG_FORCE_GENERIC),
+                           128) == tmm.PATH_GENERIC_F32
     assert tmm.select_path(d3, 0) == tmm.ERR_INVALID
     forced = tmm.make_desc(8, 16, 16384, 64, 256, 2, "bf16", flags=tmm.FLAG_FORCE_GENERIC)
     assert tmm.select_path(forced, 64) == tmm.PATH_GENERIC_F32
@@ -52,7 +60,7 @@ def test_param_count_and_paths(lib):
         d = tmm.make_desc(8, 16, 16384, 64, 256, 2, "bf16", read_mode=rm)
         assert tmm.select_path(d, 64) == tmm.PATH_MLP2_D64_H256
         assert tmm.select_path(d, 1) == tmm.PATH_MLP2_D64_H256
-        assert tmm.select_path(d, 65) == tmm.PATH_GENERIC_F32
+        assert tmm.select_path(d, 65) == tmm.PATH_DEEP_BF16
     assert tmm.select_path(tmm.make_desc(8, 16, 16384, 64, 256, 2, "f32"), 64) == tmm.PATH_GENERIC_F32
     assert tmm.workspace_bytes(d1, 16) > 0
 
