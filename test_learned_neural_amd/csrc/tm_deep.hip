@@ -46,13 +46,17 @@
 
 #include <hip/hip_bf16.h>
 
+#include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 namespace titans {
 namespace {
 
 constexpr int kT = 64;                 // output tile rows and columns
-constexpr int kThreads = 256;          // four waves
+constexpr int kThreads = 256;          // four waves (64-row tiles)
+constexpr int kMT = 128;               // token rows per tile of the key, backprop and read products
+constexpr int kThreadsW = 4 * kMT;     // eight waves
 constexpr int kMaxChunkDeep = 256;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -60,21 +64,30 @@ typedef __attribute__((ext_vector_type(8))) unsigned short u16x8;
 typedef __attribute__((ext_vector_type(4))) unsigned short u16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-// Byte offsets in one stream's workspace (every array fp32).
+// A "pair" array holds each value x as hi = bf16(x) and lo = bf16(x - hi)
+// (x - hi is exact in fp32): the hi plane, then the lo plane of the same
+// shape, the bytes of an fp32 array.  A product of two pair operands is
+// summed as hi*hi + hi*lo + lo*hi on the matrix cores with fp32 sums, about
+// 2^-16 relative per product instead of bf16's 2^-8.  The producers write
+// their results as pairs once; the contractions that re-read them stage
+// the planes as they are.  The fp32 state is split as it is staged.
+//
+// Byte offsets in one stream's workspace.
 struct DLayout {
   int b;   // token rows per region (the chunk rounded up to 64)
-  int64_t act[kMaxLayers + 1];    // a^l [b][w_l], l = 1..L-1
-  int64_t actT[kMaxLayers + 1];   // a^l transposed [w_l][b], l = 0..L-1 (a^0 = K)
-  int64_t sp[kMaxLayers + 1];     // SiLU'(z^l) [b][w_l], l = 1..L-1
-  int64_t dlt[kMaxLayers + 1];    // delta^l [b][w_l], l = 2..L
-  int64_t dltT[kMaxLayers + 1];   // delta^l transposed [w_l][b], l = 1..L
-  int64_t hq[2];                  // query-side activations [b][maxw], ping-pong
-  int64_t P;                      // masked scores [b][b]
-  int64_t D;                      // decay weights [b][b]
-  int64_t coef;                   // A, E, F, U, D[n-1, :]: [5][b]
+  int64_t act[kMaxLayers + 1];    // a^l [b][w_l] pair, l = 1..L-1
+  int64_t actD[kMaxLayers + 1];   // D[n-1, j] a^l_j, transposed [w_l][b] pair, l = 0..L-1 (a^0 = K)
+  int64_t actU[kMaxLayers + 1];   // U_j a^l_j, transposed [w_l][b] pair, l = 0..L-1
+  int64_t sp[kMaxLayers + 1];     // SiLU'(z^l) [b][w_l] fp32, l = 1..L-1
+  int64_t dlt[kMaxLayers + 1];    // delta^l [b][w_l] pair, l = 2..L
+  int64_t dltT[kMaxLayers + 1];   // delta^l transposed [w_l][b] pair, l = 1..L
+  int64_t hq[2];                  // query-side activations [b][maxw] pair, ping-pong
+  int64_t P;                      // masked scores [b][b] pair
+  int64_t D;                      // decay weights [b][b] fp32
+  int64_t coef;                   // A, E, F, U, D[n-1, :]: [5][b] fp32
   int64_t region;                 // bytes per region
-  int64_t copy;                   // bytes per state array (P floats, 256-byte aligned)
-  int64_t slot;                   // bytes per slot: W, S and W^T (per layer [n_in][n_out])
+  int64_t copy;                   // bytes per fp32 state array (P floats, 256-byte aligned)
+  int64_t slot;                   // bytes per slot: W and S
   int64_t total;                  // bytes per stream: two regions and three slots
 };
 
@@ -86,13 +99,14 @@ DLayout deep_layout(const Shape& s, int chunk) {
   y.b = (rows + kT - 1) / kT * kT;
   const int64_t b = y.b;
   int64_t cur = 0;
-  auto take = [&](int64_t floats) {
+  auto take = [&](int64_t elems) {   // 4 bytes per element: fp32, or a pair's two planes
     const int64_t at = cur;
-    cur += al256(floats * 4);
+    cur += al256(elems * 4);
     return at;
   };
   for (int l = 1; l < s.L; ++l) y.act[l] = take(b * s.widths[l]);
-  for (int l = 0; l < s.L; ++l) y.actT[l] = take(b * s.widths[l]);
+  for (int l = 0; l < s.L; ++l) y.actD[l] = take(b * s.widths[l]);
+  for (int l = 0; l < s.L; ++l) y.actU[l] = take(b * s.widths[l]);
   for (int l = 1; l < s.L; ++l) y.sp[l] = take(b * s.widths[l]);
   for (int l = 2; l <= s.L; ++l) y.dlt[l] = take(b * s.widths[l]);
   for (int l = 1; l <= s.L; ++l) y.dltT[l] = take(b * s.widths[l]);
@@ -103,7 +117,7 @@ DLayout deep_layout(const Shape& s, int chunk) {
   y.coef = take(5 * b);
   y.region = cur;
   y.copy = al256(s.P * 4);
-  y.slot = 3 * y.copy;
+  y.slot = 2 * y.copy;
   y.total = 2 * y.region + 3 * y.slot;
   return y;
 }
@@ -133,9 +147,9 @@ struct DP {
 // Per-launch view of one stream's chunk: region and slot pointers.
 struct View {
   int n, c0;
-  unsigned char* reg;                  // this chunk's region
-  const float *W0, *S0, *WT0;          // chunk-start state (slot c % 3)
-  float *W1, *S1, *WT1;                // the fold's result (slot (c + 1) % 3)
+  unsigned char* reg;          // this chunk's region
+  const float *W0, *S0;        // chunk-start state (slot c % 3)
+  float *W1, *S1;              // the fold's result (slot (c + 1) % 3)
 };
 
 __device__ __forceinline__ View view(const DP& p, int s, int c) {
@@ -148,10 +162,8 @@ __device__ __forceinline__ View view(const DP& p, int s, int c) {
   unsigned char* sw = base + 2 * p.lay.region + (int64_t)((c + 1) % 3) * p.lay.slot;
   v.W0 = (const float*)sr;
   v.S0 = (const float*)(sr + p.lay.copy);
-  v.WT0 = (const float*)(sr + 2 * p.lay.copy);
   v.W1 = (float*)sw;
   v.S1 = (float*)(sw + p.lay.copy);
-  v.WT1 = (float*)(sw + 2 * p.lay.copy);
   return v;
 }
 
@@ -171,175 +183,231 @@ __device__ __forceinline__ float silu_prime(float z) {
   return s * (1.0f + z * (1.0f - s));
 }
 
-// An operand: element (row, k) at p[row * ld + k], k contiguous, fp32 (F32)
-// or bf16; rows at or past `rows` read row rows - 1 (an address in range) and
-// count as zero, and so does every k >= K.  Every source is laid out so that
-// a 64-deep slice never reads past its allocation (rows padded to a multiple
-// of 64 in k, or K a multiple of 64).
+// An operand: element (row, k) at p[row * ld + k], k contiguous (kF32T:
+// p[k * ld + row]); a pair's lo plane starts `lo` elements after p.  Rows at
+// or past `rows` read row rows - 1 (an address in range) and count as zero,
+// and so does every k >= K.  Loads stop at the first piece (4 fp32 or 8 bf16
+// values) at or past K; a piece that straddles K reads up to K rounded up to
+// 8, which every source's row holds (K a multiple of 64, or rows padded to a
+// multiple of 64).
 struct Src {
   const void* p;
   int64_t ld;
   int rows;
+  int64_t lo;
 };
 
-// Split operands: an fp32 value x is staged as hi = bf16(x) and lo = bf16(x -
-// hi) (x - hi is exact in fp32), and a product of two split operands is
-// summed as hi*hi + hi*lo + lo*hi, each term on the matrix cores with fp32
-// sums: about 2^-16 relative per product instead of bf16's 2^-8.  bf16
-// inputs (keys and queries) are exact and stage only hi.  A staged slice is
-// 64 rows x KS k; its LDS tiles have row stride KS + 8 bf16.
-template <int KS>
-__host__ __device__ constexpr int tile_elems() { return kT * (KS + 8); }
+enum Kind { kBF16, kF32, kPair, kF32T };   // exact bf16 input, fp32, pair, fp32 read transposed
 
-template <bool F32, int KS>
+template <int KS, int ROWS = kT>
+__host__ __device__ constexpr int tile_elems() { return ROWS * (KS + 8); }
+
+// Staging of one operand's 64 x KS slice into its hi (and lo) LDS tiles
+// (row stride KS + 8 bf16).
+template <Kind K, int KS, int ROWS, int NT>
 struct Stage;
 
-template <int KS>
-struct Stage<true, KS> {   // fp32 source: pieces of 4 floats
-  static constexpr int kQ = KS / 4;                      // pieces per row
-  static constexpr int kPer = kT * kQ / kThreads;        // pieces per thread
-  static constexpr int kRSt = KS + 8;
-  float4 r[kPer];
-  __device__ __forceinline__ void fetch(const Src& a, int r0, int k0) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int e = tid + u * kThreads, row = e / kQ, kq = (e % kQ) * 4;
-      r[u] = *(const float4*)((const float*)a.p + (int64_t)min(r0 + row, a.rows - 1) * a.ld + k0 + kq);
-    }
-  }
-  // stores NC copies (hi tile 2c, lo tile 2c + 1 from `base`), copy c scaled
-  // per k by ks[c] when KSCALE
-  template <int NC, bool KSCALE>
-  __device__ __forceinline__ void store(uint16_t* base, int rows_left, int k_left, const float* ks0, const float* ks1,
-                                        int k0) const {
-    constexpr int TE = tile_elems<KS>();
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int e = tid + u * kThreads, row = e / kQ, kq = (e % kQ) * 4;
-      const int kv = row < rows_left ? k_left - kq : 0;
-      float x[4] = {r[u].x, r[u].y, r[u].z, r[u].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i >= kv) x[i] = 0.f;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        u16x4 h, l;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float xi = x[i];
-          if constexpr (KSCALE) xi *= (c == 0 ? ks0 : ks1)[min(k0 + kq + i, kMaxChunkDeep - 1)];
-          h[i] = f2bf(xi);
-          l[i] = f2bf(xi - bf2f(h[i]));
-        }
-        *(u16x4*)(base + 2 * c * TE + row * kRSt + kq) = h;
-        *(u16x4*)(base + (2 * c + 1) * TE + row * kRSt + kq) = l;
-      }
-    }
-  }
-};
-
-template <int KS>
-struct Stage<false, KS> {   // bf16 source: pieces of 8
-  static constexpr int kQ = KS / 8;
-  static constexpr int kPer = kT * kQ / kThreads;
-  static constexpr int kRSt = KS + 8;
+template <int KS, int ROWS, int NT>
+struct Stage<kBF16, KS, ROWS, NT> {   // pieces of 8 values; hi only
+  static constexpr int kQ = KS / 8, kPer = ROWS * kQ / NT, RS = KS + 8;
   uint4 r[kPer];
-  __device__ __forceinline__ void fetch(const Src& a, int r0, int k0) {
-    const int tid = threadIdx.x;
+  __device__ __forceinline__ void fetch(const Src& a, int r0, int k0, int K) {
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-      const int e = tid + u * kThreads, row = e / kQ, kq = (e % kQ) * 8;
-      r[u] = *(const uint4*)((const uint16_t*)a.p + (int64_t)min(r0 + row, a.rows - 1) * a.ld + k0 + kq);
+      const int e = threadIdx.x + u * NT, row = e / kQ, kq = (e % kQ) * 8;
+      r[u] = k0 + kq < K ? *(const uint4*)((const uint16_t*)a.p + (int64_t)min(r0 + row, a.rows - 1) * a.ld + k0 + kq)
+                         : make_uint4(0u, 0u, 0u, 0u);
     }
   }
-  template <int NC, bool KSCALE>
-  __device__ __forceinline__ void store(uint16_t* base, int rows_left, int k_left, const float*, const float*,
-                                        int) const {
-    static_assert(NC == 1 && !KSCALE, "bf16 operands are staged once, unscaled");
-    const int tid = threadIdx.x;
+  __device__ __forceinline__ void store(uint16_t* t, int rows_left, int k_left) const {
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-      const int e = tid + u * kThreads, row = e / kQ, kq = (e % kQ) * 8;
+      const int e = threadIdx.x + u * NT, row = e / kQ, kq = (e % kQ) * 8;
       const int kv = row < rows_left ? k_left - kq : 0;
       u16x8 x = __builtin_bit_cast(u16x8, r[u]);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         if (i >= kv) x[i] = 0;
-      *(u16x8*)(base + row * kRSt + kq) = x;
+      *(u16x8*)(t + row * RS + kq) = x;
     }
   }
 };
 
-// acc[c][t] += A_c(m0 + i, k) B_t(n0 + j, k) summed over k < K, for the
-// wave's 32 x 32 block (i, j in [0, 64)), as one pipeline: the next KS-deep
-// slice's loads are in flight while the current slice is multiplied.  NA
-// copies of A are staged from the same source, copy c with each element
-// scaled by ks[c][k] (per-k weights in LDS) when KSCALE; NB operands B_t
-// share the staged A.  LDS tiles: A copy c at hi 2c, lo 2c + 1, then B_t at
-// hi 2 NA + 2t, lo 2 NA + 2t + 1.
+template <int KS, int ROWS, int NT>
+struct Stage<kPair, KS, ROWS, NT> {   // pieces of 8 values from each plane
+  static constexpr int kQ = KS / 8, kPer = ROWS * kQ / NT, RS = KS + 8;
+  uint4 h[kPer], l[kPer];
+  __device__ __forceinline__ void fetch(const Src& a, int r0, int k0, int K) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = threadIdx.x + u * NT, row = e / kQ, kq = (e % kQ) * 8;
+      const uint16_t* x = (const uint16_t*)a.p + (int64_t)min(r0 + row, a.rows - 1) * a.ld + k0 + kq;
+      const bool in = k0 + kq < K;
+      h[u] = in ? *(const uint4*)x : make_uint4(0u, 0u, 0u, 0u);
+      l[u] = in ? *(const uint4*)(x + a.lo) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* t, int rows_left, int k_left) const {
+    constexpr int TE = tile_elems<KS, ROWS>();
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = threadIdx.x + u * NT, row = e / kQ, kq = (e % kQ) * 8;
+      const int kv = row < rows_left ? k_left - kq : 0;
+      u16x8 xh = __builtin_bit_cast(u16x8, h[u]), xl = __builtin_bit_cast(u16x8, l[u]);
+      if (kv < 8) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (i >= kv) xh[i] = xl[i] = 0;
+      }
+      *(u16x8*)(t + row * RS + kq) = xh;
+      *(u16x8*)(t + TE + row * RS + kq) = xl;
+    }
+  }
+};
+
+template <int KS, int ROWS, int NT>
+struct Stage<kF32, KS, ROWS, NT> {   // pieces of 4 fp32 values, split as they are stored
+  static constexpr int kQ = KS / 4, kPer = ROWS * kQ / NT, RS = KS + 8;
+  float4 r[kPer];
+  __device__ __forceinline__ void fetch(const Src& a, int r0, int k0, int K) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = threadIdx.x + u * NT, row = e / kQ, kq = (e % kQ) * 4;
+      r[u] = k0 + kq < K ? *(const float4*)((const float*)a.p + (int64_t)min(r0 + row, a.rows - 1) * a.ld + k0 + kq)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* t, int rows_left, int k_left) const {
+    constexpr int TE = tile_elems<KS, ROWS>();
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = threadIdx.x + u * NT, row = e / kQ, kq = (e % kQ) * 4;
+      const int kv = row < rows_left ? k_left - kq : 0;
+      const float x[4] = {r[u].x, r[u].y, r[u].z, r[u].w};
+      u16x4 hv, lv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float xi = i < kv ? x[i] : 0.f;
+        hv[i] = f2bf(xi);
+        lv[i] = f2bf(xi - bf2f(hv[i]));
+      }
+      *(u16x4*)(t + row * RS + kq) = hv;
+      *(u16x4*)(t + TE + row * RS + kq) = lv;
+    }
+  }
+};
+
+template <int KS, int ROWS, int NT>
+struct Stage<kF32T, KS, ROWS, NT> {   // fp32 read transposed: pieces of 4 rows at one k, split as they are stored
+  static constexpr int kQ = ROWS / 4, kPer = KS * kQ / NT, RS = KS + 8;
+  float4 r[kPer];
+  __device__ __forceinline__ void fetch(const Src& a, int r0, int k0, int K) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = threadIdx.x + u * NT, k = e / kQ, rq = (e % kQ) * 4;
+      r[u] = k0 + k < K ? *(const float4*)((const float*)a.p + (int64_t)(k0 + k) * a.ld + r0 + rq)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* t, int rows_left, int k_left) const {
+    constexpr int TE = tile_elems<KS, ROWS>();
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = threadIdx.x + u * NT, k = e / kQ, rq = (e % kQ) * 4;
+      const float x[4] = {r[u].x, r[u].y, r[u].z, r[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float xi = (rq + i < rows_left && k < k_left) ? x[i] : 0.f;
+        const unsigned short hv = f2bf(xi);
+        t[(rq + i) * RS + k] = hv;
+        t[TE + (rq + i) * RS + k] = f2bf(xi - bf2f(hv));
+      }
+    }
+  }
+};
+
+__host__ __device__ constexpr bool has_lo(Kind k) { return k != kBF16; }
+
+// acc[t] += A(m0 + i, k) B_t(n0 + j, k) summed over k < K, for the wave's
+// 32 x 32 block (i in [0, MT), j in [0, 64)), as one pipeline: the next
+// KS-deep slice's loads are in flight while the current slice is multiplied.
+// MT / 16 waves (MT x 4 threads) cover the MT x 64 tile, wave w the block at
+// row 32 (w / 2), column 32 (w % 2).  The NB operands B_t share the staged
+// A.  LDS tiles: A hi, A lo (MT rows), then B_t hi, lo (64 rows).
 // v_mfma_f32_32x32x16_bf16: lane l supplies row (A) or column (B) l % 32 with
 // k values 8 (l / 32) .. + 7 of each 16-deep step; accumulator register r of
 // lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
-template <int KS, int NA, int NB, bool KSCALE, bool AF, bool BF>
-__device__ void gemm(f32x16 (&acc)[NA][NB], const Src A, const Src (&B)[NB], int m0, int n0, int K,
-                     const float* ks0, const float* ks1, uint16_t* lds) {
-  constexpr int TE = tile_elems<KS>(), RS = KS + 8;
+template <int KS, int NB, Kind AK, Kind BK, int MT = kT>
+__device__ void gemm(f32x16 (&acc)[NB], const Src A, const Src (&B)[NB], int m0, int n0, int K, uint16_t* lds) {
+  constexpr int NT = 4 * MT, RS = KS + 8;
+  constexpr int TA = tile_elems<KS, MT>(), TB = tile_elems<KS>();
+  constexpr bool alo = has_lo(AK), blo = has_lo(BK);
   uint16_t* const As = lds;
-  uint16_t* const Bs = lds + 2 * NA * TE;
+  uint16_t* const Bs = lds + 2 * TA;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wm = (wv >> 1) * 32, wn = (wv & 1) * 32;
-  Stage<AF, KS> sa;
-  Stage<BF, KS> sb[NB];
+  Stage<AK, KS, MT, NT> sa;
+  Stage<BK, KS, kT, NT> sb[NB];
   if (K <= 0) return;
-  sa.fetch(A, m0, 0);
+  sa.fetch(A, m0, 0, K);
 #pragma unroll
-  for (int t = 0; t < NB; ++t) sb[t].fetch(B[t], n0, 0);
+  for (int t = 0; t < NB; ++t) sb[t].fetch(B[t], n0, 0, K);
   for (int k0 = 0; k0 < K; k0 += KS) {
 #pragma unroll
-    for (int t = 0; t < NB; ++t)
-      sb[t].template store<1, false>(Bs + 2 * t * TE, B[t].rows - n0, K - k0, nullptr, nullptr, k0);
-    sa.template store<NA, KSCALE>(As, A.rows - m0, K - k0, ks0, ks1, k0);
+    for (int t = 0; t < NB; ++t) sb[t].store(Bs + 2 * t * TB, B[t].rows - n0, K - k0);
+    sa.store(As, A.rows - m0, K - k0);
     __syncthreads();
     if (k0 + KS < K) {
-      sa.fetch(A, m0, k0 + KS);
+      sa.fetch(A, m0, k0 + KS, K);
 #pragma unroll
-      for (int t = 0; t < NB; ++t) sb[t].fetch(B[t], n0, k0 + KS);
+      for (int t = 0; t < NB; ++t) sb[t].fetch(B[t], n0, k0 + KS, K);
     }
 #pragma unroll
     for (int kk = 0; kk < KS; kk += 16) {
       const int ko = kk + 8 * (lane >> 5);
+      const uint16_t* ar = As + (wm + (lane & 31)) * RS + ko;
+      const bf16x8 ah = *(const bf16x8*)ar;
+      bf16x8 al;
+      if constexpr (alo) al = *(const bf16x8*)(ar + TA);
 #pragma unroll
       for (int t = 0; t < NB; ++t) {
-        const uint16_t* bt = Bs + 2 * t * TE + (wn + (lane & 31)) * RS + ko;
-        const bf16x8 bh = *(const bf16x8*)bt;
-        bf16x8 bl;
-        if constexpr (BF) bl = *(const bf16x8*)(bt + TE);
-#pragma unroll
-        for (int c = 0; c < NA; ++c) {
-          const uint16_t* ac = As + 2 * c * TE + (wm + (lane & 31)) * RS + ko;
-          const bf16x8 ah = *(const bf16x8*)ac;
-          acc[c][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc[c][t], 0, 0, 0);
-          if constexpr (BF) acc[c][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[c][t], 0, 0, 0);
-          if constexpr (AF) {
-            const bf16x8 al = *(const bf16x8*)(ac + TE);
-            acc[c][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[c][t], 0, 0, 0);
-          }
+        const uint16_t* br = Bs + 2 * t * TB + (wn + (lane & 31)) * RS + ko;
+        const bf16x8 bh = *(const bf16x8*)br;
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc[t], 0, 0, 0);
+        if constexpr (blo) {
+          const bf16x8 bl = *(const bf16x8*)(br + TB);
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[t], 0, 0, 0);
         }
+        if constexpr (alo) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[t], 0, 0, 0);
       }
     }
     __syncthreads();
   }
 }
 
-// one A, one B
-template <int KS, bool AF, bool BF>
+template <int KS, Kind AK, Kind BK, int MT = kT>
 __device__ __forceinline__ void gemm1(f32x16& acc, const Src A, const Src B, int m0, int n0, int K, uint16_t* lds) {
-  f32x16 a[1][1] = {{acc}};
+  f32x16 a[1] = {acc};
   const Src b[1] = {B};
-  gemm<KS, 1, 1, false, AF, BF>(a, A, b, m0, n0, K, nullptr, nullptr, lds);
-  acc = a[0][0];
+  gemm<KS, 1, AK, BK, MT>(a, A, b, m0, n0, K, lds);
+  acc = a[0];
+}
+
+// (stream, tile) of this workgroup in a one-dimensional grid of T tiles for
+// each of the launch's streams.  Consecutive workgroups go to the eight XCDs
+// in turn; when the stream count is a multiple of 8, every tile of a stream
+// lands on one XCD (streams s, s + 8, ... on XCD s % 8, tile after tile), so
+// the operands its tiles share come from that XCD's L2 after the first read.
+struct Place {
+  int s, tile;
+};
+__device__ __forceinline__ Place place(int T) {
+  const int id = blockIdx.x, S = gridDim.x / T;
+  if ((S & 7) == 0) {
+    const int j = id >> 3;
+    return Place{(id & 7) + 8 * (j / T), j % T};
+  }
+  return Place{id / T, id % T};
 }
 
 // Row and column of accumulator register r in the tile at (m0, n0).
@@ -352,39 +420,110 @@ __device__ __forceinline__ int acc_col(int n0) {
   return n0 + (wv & 1) * 32 + (lane & 31);
 }
 
-// Stores the tile transposed: T[col][row .. row + 3] from registers 4g .. 4g + 3
-// (four consecutive rows), one 16-byte store per group.
-__device__ __forceinline__ void store_T(float* T, int64_t ldT, int m0, int n0, const float (&v)[16]) {
+// x as a pair at element i of the array whose lo plane starts lo after it
+__device__ __forceinline__ void put_pair(uint16_t* a, int64_t lo, int64_t i, float x) {
+  const unsigned short h = f2bf(x);
+  a[i] = h;
+  a[lo + i] = f2bf(x - bf2f(h));
+}
+
+// The tile transposed into a pair array: T[col][row .. row + 3] from
+// registers 4g .. 4g + 3 (four consecutive rows), each scaled by w[row - m0]
+// when w is given (LDS), one 8-byte store per plane and group.  T's rows
+// hold ldT tokens (a multiple of 64); groups at or past them are skipped.
+__device__ __forceinline__ void store_T(uint16_t* T, int64_t lo, int64_t ldT, int m0, int n0, const float (&v)[16],
+                                        const float* w = nullptr) {
   const int col = acc_col(n0);
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
-    *(float4*)(T + (int64_t)col * ldT + acc_row(m0, 4 * g)) = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2],
-                                                                           v[4 * g + 3]);
+  for (int g = 0; g < 4; ++g) {
+    const int row = acc_row(m0, 4 * g);
+    if (row >= ldT) continue;
+    u16x4 h, l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = w ? v[4 * g + i] * w[row - m0 + i] : v[4 * g + i];
+      h[i] = f2bf(x);
+      l[i] = f2bf(x - bf2f(h[i]));
+    }
+    *(u16x4*)(T + (int64_t)col * ldT + row) = h;
+    *(u16x4*)(T + lo + (int64_t)col * ldT + row) = l;
+  }
 }
 
 __device__ __forceinline__ const uint16_t* tok_rows(const uint16_t* base, const DP& p, int s, int c0) {
   return base + ((int64_t)s * p.N + c0) * p.d;
 }
 
-// the staging area every contraction of a kernel shares: six 64-deep tiles
-// (hi and lo of two A copies and one B, or of one A and two B) or four
-// 128-deep ones (hi and lo of one A and one B)
-constexpr int kLdsElems = 6 * tile_elems<64>() > 4 * tile_elems<128>() ? 6 * tile_elems<64>() : 4 * tile_elems<128>();
+// The staging area every contraction of a kernel shares, E bf16 elements
+// (one allocation per size): the key, backprop and read kernels hold hi and
+// lo of a 128-row A and one 64-row B 128 deep (or of two B 64 deep), the
+// scores kernel of a 64-row A and one B 128 deep, the fold of a 64-row A and
+// two B 64 deep.
+constexpr int kLdsW = 2 * tile_elems<128, kMT>() + 2 * tile_elems<128>();
+constexpr int kLdsScores = 4 * tile_elems<128>();
+constexpr int kLdsFold = 6 * tile_elems<64>();
+static_assert(kLdsW >= 2 * tile_elems<64, kMT>() + 4 * tile_elems<64>(), "read kernel staging");
+template <int E>
 __device__ __forceinline__ uint16_t* stage_lds() {
-  __shared__ __attribute__((aligned(16))) uint16_t buf[kLdsElems];
+  __shared__ __attribute__((aligned(16))) uint16_t buf[E];
   return buf;
 }
 
+// pair arrays of the region: pointer and lo-plane offset (elements)
+struct PairArr {
+  uint16_t* p;
+  int64_t lo;
+};
+__device__ __forceinline__ PairArr pair(unsigned char* reg, int64_t off, int64_t elems) {
+  return PairArr{at<uint16_t>(reg, off), elems};
+}
+
+// The fold weights D[n-1, i] and U_i of tokens m0 .. m0 + kMT - 1 of chunk
+// c (zero past the chunk's n tokens) into w[0, kMT) and w[kMT, 2 kMT): the
+// gates of the chunk's later tokens go through LDS, then one thread per
+// token runs its column's recurrence over them.
+__device__ void fold_weights(const DP& p, int s, int c, int n, int m0, float* w) {
+  __shared__ float ga[kMaxChunkDeep], ge[kMaxChunkDeep], gt[kMaxChunkDeep];
+  const int t = threadIdx.x;
+  const int64_t g0 = p.chunk_gates ? (int64_t)s * p.nch + c : (int64_t)s * p.N + (int64_t)c * p.chunk;
+  const int gs = p.chunk_gates ? 0 : 1;
+  for (int j = m0 + t; j < n; j += blockDim.x) {
+    ga[j] = p.alpha[g0 + j * gs];
+    ge[j] = p.eta[g0 + j * gs];
+    gt[j] = p.theta[g0 + j * gs];
+  }
+  __syncthreads();
+  if (t < kMT) {
+    const int i = m0 + t;
+    float di = 0.f, u = 0.f;
+    if (i < n) {
+      const float ti = gt[i];
+      float pr = 1.f;
+      di = ti;
+      for (int j = i + 1; j < n; ++j) {
+        pr *= ge[j];
+        di = (1.f - ga[j]) * di + ti * pr;
+      }
+      u = ti * pr;
+    }
+    w[t] = di;
+    w[kMT + t] = u;
+  }
+  __syncthreads();
+}
+
 // ---- key side: z^l = a^{l-1} W_0^l^T (and, in layer 1's extra workgroup
-// per stream, the chunk's coefficients and the transposed keys) ----
-__global__ void __launch_bounds__(kThreads) deep_key_kernel(DP p, int c, int l) {
-  const int s = blockIdx.y;
+// per stream, the chunk's coefficients and the scaled transposed keys) ----
+__global__ void __launch_bounds__(kThreadsW) deep_key_kernel(DP p, int c, int l) {
+  const int n = min(p.chunk, p.N - c * p.chunk);
+  const int nin = p.w[l - 1], nout = p.w[l];
+  const int ntn = nout / kT, ntiles = ((n + kMT - 1) / kMT) * ntn;
+  const Place pl = place(ntiles + (l == 1));
+  const int s = pl.s;
   const View v = view(p, s, c);
   const DLayout& y = p.lay;
-  const int b = y.b, n = v.n;
-  const int nin = p.w[l - 1], nout = p.w[l];
-  const int ntn = nout / kT, ntiles = ((n + kT - 1) / kT) * ntn;
-  if ((int)blockIdx.x >= ntiles) {
+  const int b = y.b;
+  if (pl.tile >= ntiles) {
     // coefficients of the chunk (one thread per column i of D; A, E, F on the last thread)
     __shared__ float gal[kMaxChunkDeep], get[kMaxChunkDeep], gth[kMaxChunkDeep];
     const int tid = threadIdx.x;
@@ -399,7 +538,7 @@ __global__ void __launch_bounds__(kThreads) deep_key_kernel(DP p, int c, int l) 
     float* D = at<float>(v.reg, y.D);
     float* cf = at<float>(v.reg, y.coef);
     for (int i = tid; i < b; i += kThreads) {
-      float di = 0.f, pr = 1.f;
+      float di = 0.f, pr = 1.f, ui = 0.f;
       if (i < n) {
         const float ti = gth[i];
         di = ti;
@@ -411,13 +550,13 @@ __global__ void __launch_bounds__(kThreads) deep_key_kernel(DP p, int c, int l) 
           D[(int64_t)j * b + i] = di;
         }
         for (int j = n; j < b; ++j) D[(int64_t)j * b + i] = 0.f;
-        cf[3 * b + i] = ti * pr;   // U
-        cf[4 * b + i] = di;        // D[n-1, i]
+        ui = ti * pr;
       } else {
         for (int j = 0; j < b; ++j) D[(int64_t)j * b + i] = 0.f;
-        cf[3 * b + i] = 0.f;
-        cf[4 * b + i] = 0.f;
+        di = 0.f;
       }
+      cf[3 * b + i] = ui;   // U
+      cf[4 * b + i] = di;   // D[n-1, i]
     }
     if (tid == kThreads - 1) {
       float a = 1.f, e = 1.f, f = 0.f;
@@ -430,88 +569,112 @@ __global__ void __launch_bounds__(kThreads) deep_key_kernel(DP p, int c, int l) 
         cf[2 * b + j] = f;
       }
     }
-    // K^T [d][b] (fp32) for the fold's contraction over tokens
-    const uint16_t* kr = tok_rows(p.k, p, s, v.c0);
-    float* KT = at<float>(v.reg, y.actT[0]);
-    for (int e = tid; e < n * (p.d / 8); e += kThreads) {
-      const int j = e / (p.d / 8), c8 = (e % (p.d / 8)) * 8;
-      const u16x8 x = *(const u16x8*)(kr + (int64_t)j * p.d + c8);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) KT[(int64_t)(c8 + i) * b + j] = bf2f(x[i]);
-    }
     return;
   }
-  const int m0 = (blockIdx.x / ntn) * kT, n0 = (blockIdx.x % ntn) * kT;
-  const Src B = {v.W0 + p.off[l], nin, nout};
-  f32x16 acc[1] = {};
+  const int m0 = (pl.tile / ntn) * kMT, n0 = (pl.tile % ntn) * kT;
+  const Src B = {v.W0 + p.off[l], nin, nout, 0};
+  f32x16 acc = {};
   if (l == 1)
-    gemm1<128, false, true>(acc[0], Src{tok_rows(p.k, p, s, v.c0), p.d, n}, B, m0, n0, nin, stage_lds());
+    gemm1<128, kBF16, kF32, kMT>(acc, Src{tok_rows(p.k, p, s, v.c0), p.d, n, 0}, B, m0, n0, nin, stage_lds<kLdsW>());
   else
-    gemm1<128, true, true>(acc[0], Src{at<float>(v.reg, y.act[l - 1]), nin, n}, B, m0, n0, nin, stage_lds());
+    gemm1<128, kPair, kF32, kMT>(acc, Src{at<uint16_t>(v.reg, y.act[l - 1]), nin, n, (int64_t)b * nin}, B, m0, n0,
+                                 nin, stage_lds<kLdsW>());
   const int col = acc_col(n0);
   float val[16];
   if (l < p.L) {
-    float* act = at<float>(v.reg, y.act[l]);
+    __shared__ float w[2 * kMT];
+    if (l == 1) {
+      fold_weights(p, s, c, n, m0, w);
+    } else {
+      const float* cf = at<float>(v.reg, y.coef);
+      if (threadIdx.x < kMT) {
+        const int i = min(m0 + (int)threadIdx.x, b - 1);
+        w[threadIdx.x] = cf[4 * b + i];
+        w[kMT + threadIdx.x] = cf[3 * b + i];
+      }
+      __syncthreads();
+    }
+    const PairArr act = pair(v.reg, y.act[l], (int64_t)b * nout);
     float* sp = at<float>(v.reg, y.sp[l]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = acc_row(m0, r);
-      const float z = acc[0][r];
+      const float z = acc[r];
       val[r] = silu(z);
       if (row < n) {
-        act[(int64_t)row * nout + col] = val[r];
+        put_pair(act.p, act.lo, (int64_t)row * nout + col, val[r]);
         sp[(int64_t)row * nout + col] = silu_prime(z);
       }
     }
-    store_T(at<float>(v.reg, y.actT[l]), b, m0, n0, val);
+    const PairArr aD = pair(v.reg, y.actD[l], (int64_t)nout * b), aU = pair(v.reg, y.actU[l], (int64_t)nout * b);
+    store_T(aD.p, aD.lo, b, m0, n0, val, w);
+    store_T(aU.p, aU.lo, b, m0, n0, val, w + kMT);
+    if (l == 1 && n0 == 0) {
+      // the keys of these kMT tokens, scaled by the fold weights, into K^T
+      // [d][b] pairs for the fold's contraction over tokens (consecutive
+      // tokens along each row of K^T, so the stores are whole rows)
+      const uint16_t* kr = tok_rows(p.k, p, s, v.c0);
+      const PairArr KD = pair(v.reg, y.actD[0], (int64_t)p.d * b), KU = pair(v.reg, y.actU[0], (int64_t)p.d * b);
+      const int rows = min(kMT, b - m0);
+      for (int e = threadIdx.x; e < rows * p.d; e += kThreadsW) {
+        const int j = e % rows, cc = e / rows;
+        const float x = bf2f(kr[(int64_t)min(m0 + j, n - 1) * p.d + cc]);
+        put_pair(KD.p, KD.lo, (int64_t)cc * b + m0 + j, w[j] * x);
+        put_pair(KU.p, KU.lo, (int64_t)cc * b + m0 + j, w[kMT + j] * x);
+      }
+    }
   } else {
     const uint16_t* vr = tok_rows(p.v, p, s, v.c0);
-    float* dl = at<float>(v.reg, y.dlt[l]);
+    const PairArr dl = pair(v.reg, y.dlt[l], (int64_t)b * nout), dT = pair(v.reg, y.dltT[l], (int64_t)nout * b);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = acc_row(m0, r);
-      val[r] = acc[0][r] - bf2f(vr[(int64_t)min(row, n - 1) * p.d + col]);   // residual M(k) - v
-      if (row < n) dl[(int64_t)row * nout + col] = val[r];
+      val[r] = acc[r] - bf2f(vr[(int64_t)min(row, n - 1) * p.d + col]);   // residual M(k) - v
+      if (row < n) put_pair(dl.p, dl.lo, (int64_t)row * nout + col, val[r]);
     }
-    store_T(at<float>(v.reg, y.dltT[l]), b, m0, n0, val);
+    store_T(dT.p, dT.lo, b, m0, n0, val);
   }
 }
 
 // ---- backprop: delta^{l-1} = (delta^l W_0^l) * SiLU'(z^{l-1}) ----
-__global__ void __launch_bounds__(kThreads) deep_back_kernel(DP p, int c, int l) {
-  const int s = blockIdx.y;
-  const View v = view(p, s, c);
-  const DLayout& y = p.lay;
-  const int b = y.b, n = v.n;
+__global__ void __launch_bounds__(kThreadsW) deep_back_kernel(DP p, int c, int l) {
+  const int n = min(p.chunk, p.N - c * p.chunk);
   const int nin = p.w[l - 1], nout = p.w[l];
   const int ntn = nin / kT;
-  const int m0 = (blockIdx.x / ntn) * kT, n0 = (blockIdx.x % ntn) * kT;
-  const Src A = {at<float>(v.reg, y.dlt[l]), nout, n};
-  const Src B = {v.WT0 + p.off[l], nout, nin};   // W^l transposed: [nin][nout]
-  f32x16 acc[1] = {};
-  gemm1<128, true, true>(acc[0], A, B, m0, n0, nout, stage_lds());
+  const Place pl = place(((n + kMT - 1) / kMT) * ntn);
+  const int s = pl.s;
+  const View v = view(p, s, c);
+  const DLayout& y = p.lay;
+  const int b = y.b;
+  const int m0 = (pl.tile / ntn) * kMT, n0 = (pl.tile % ntn) * kT;
+  // B(c, r) = W^l[r][c], staged transposed from W^l [nout][nin]
+  f32x16 acc = {};
+  gemm1<128, kPair, kF32T, kMT>(acc, Src{at<uint16_t>(v.reg, y.dlt[l]), nout, n, (int64_t)b * nout},
+                                Src{v.W0 + p.off[l], nin, nin, 0}, m0, n0, nout, stage_lds<kLdsW>());
   const int col = acc_col(n0);
   const float* sp = at<float>(v.reg, y.sp[l - 1]);
-  float* dl = l - 1 >= 2 ? at<float>(v.reg, y.dlt[l - 1]) : nullptr;
+  const PairArr dl = pair(v.reg, y.dlt[l - 1], (int64_t)b * nin), dT = pair(v.reg, y.dltT[l - 1], (int64_t)nin * b);
   float val[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = acc_row(m0, r);
-    val[r] = acc[0][r] * sp[(int64_t)min(row, n - 1) * nin + col];
-    if (dl && row < n) dl[(int64_t)row * nin + col] = val[r];
+    val[r] = acc[r] * sp[(int64_t)min(row, n - 1) * nin + col];
+    if (l - 1 >= 2 && row < n) put_pair(dl.p, dl.lo, (int64_t)row * nin + col, val[r]);
   }
-  store_T(at<float>(v.reg, y.dltT[l - 1]), b, m0, n0, val);
+  store_T(dT.p, dT.lo, b, m0, n0, val);
 }
 
 // ---- fold of the chunk into the state, every layer in one launch: from
 // slot c % 3 into slot (c + 1) % 3, or into (W_out, S_out) at the last chunk ----
 __global__ void __launch_bounds__(kThreads) deep_fold_kernel(DP p, int c, int last) {
-  __shared__ float wD[kMaxChunkDeep], wU[kMaxChunkDeep];
-  const int s = blockIdx.y;
+  int T = 0;
+  for (int l = 1; l <= p.L; ++l) T += (p.w[l] / kT) * (p.w[l - 1] / kT);
+  const Place pl = place(T);
+  const int s = pl.s;
   const View v = view(p, s, c);
   const DLayout& y = p.lay;
   const int b = y.b, n = v.n;
-  int l = 1, t = blockIdx.x;
+  int l = 1, t = pl.tile;
   while (l < p.L && t >= (p.w[l] / kT) * (p.w[l - 1] / kT)) {
     t -= (p.w[l] / kT) * (p.w[l - 1] / kT);
     ++l;
@@ -519,142 +682,129 @@ __global__ void __launch_bounds__(kThreads) deep_fold_kernel(DP p, int c, int la
   const int nin = p.w[l - 1], nout = p.w[l];
   const int ntn = nin / kT;
   const int m0 = (t / ntn) * kT, n0 = (t % ntn) * kT;
-  const float* cf = at<float>(v.reg, y.coef);
-  for (int j = threadIdx.x; j < kMaxChunkDeep; j += kThreads) {
-    wD[j] = j < n ? cf[4 * b + j] : 0.f;
-    wU[j] = j < n ? cf[3 * b + j] : 0.f;
-  }
-  __syncthreads();
-  const Src A = {at<float>(v.reg, y.dltT[l]), b, nout};
-  const Src B[1] = {{at<float>(v.reg, y.actT[l - 1]), b, nin}};
-  f32x16 g[2][1] = {};
-  gemm<64, 2, 1, true, true, true>(g, A, B, m0, n0, n, wD, wU, stage_lds());
-  const f32x16 acc[2] = {g[0][0], g[1][0]};
-  const float An = cf[n - 1], En = cf[b + n - 1], Fn = cf[2 * b + n - 1];
+  const int col = acc_col(n0);
   const float* Wsrc = v.W0 + p.off[l];
   const float* Ssrc = v.S0 + p.off[l];
+  // the state tile's loads go out before the contraction
+  float w0[16], s0[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t i = (int64_t)acc_row(m0, r) * nin + col;
+    w0[r] = Wsrc[i];
+    s0[r] = Ssrc[i];
+  }
+  // G(D[n-1, :]) and G(U): the deltas against the keys' activations scaled per token
+  const Src B[2] = {{at<uint16_t>(v.reg, y.actD[l - 1]), b, nin, (int64_t)nin * b},
+                    {at<uint16_t>(v.reg, y.actU[l - 1]), b, nin, (int64_t)nin * b}};
+  f32x16 g[2] = {};
+  gemm<64, 2, kPair, kPair>(g, Src{at<uint16_t>(v.reg, y.dltT[l]), b, nout, (int64_t)nout * b}, B, m0, n0, n,
+                            stage_lds<kLdsFold>());
+  const float* cf = at<float>(v.reg, y.coef);
+  const float An = cf[n - 1], En = cf[b + n - 1], Fn = cf[2 * b + n - 1];
   float* Wd = (last ? p.W + (int64_t)s * p.P : v.W1) + p.off[l];
   float* Sd = (last ? p.S + (int64_t)s * p.P : v.S1) + p.off[l];
-  const int col = acc_col(n0);
-  float wn[16], sn[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int64_t i = (int64_t)acc_row(m0, r) * nin + col;
-    const float w0 = Wsrc[i], s0 = Ssrc[i];
-    wn[r] = An * w0 + Fn * s0 - acc[0][r];
-    sn[r] = En * s0 - acc[1][r];
+    Wd[i] = An * w0[r] + Fn * s0[r] - g[0][r];
+    Sd[i] = En * s0[r] - g[1][r];
   }
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int64_t i = (int64_t)acc_row(m0, r) * nin + col;
-    Wd[i] = wn[r];
-    Sd[i] = sn[r];
-  }
-  if (!last) store_T(v.WT1 + p.off[l], nout, m0, n0, wn);
 }
 
 // ---- reads: masked, decay-weighted scores D o (h a^{l-1 T}), lower triangle ----
 __global__ void __launch_bounds__(kThreads) deep_scores_kernel(DP p, int c, int l) {
-  const int s = blockIdx.y;
-  const View v = view(p, s, c);
-  const DLayout& y = p.lay;
-  const int b = y.b, n = v.n;
+  const int n = min(p.chunk, p.N - c * p.chunk);
   const int nin = p.w[l - 1];
   const int ntn = (n + kT - 1) / kT;
-  const int m0 = (blockIdx.x / ntn) * kT, n0 = (blockIdx.x % ntn) * kT;
-  f32x16 acc[1] = {};
+  const Place pl = place(ntn * ntn);
+  const int s = pl.s;
+  const View v = view(p, s, c);
+  const DLayout& y = p.lay;
+  const int b = y.b;
+  const int m0 = (pl.tile / ntn) * kT, n0 = (pl.tile % ntn) * kT;
+  f32x16 acc = {};
   if (n0 <= m0 + kT - 1) {   // tiles above the diagonal are zero
     if (l == 1)
-      gemm1<128, false, false>(acc[0], Src{tok_rows(p.q, p, s, v.c0), p.d, n}, Src{tok_rows(p.k, p, s, v.c0), p.d, n},
-                               m0, n0, nin, stage_lds());
+      gemm1<128, kBF16, kBF16>(acc, Src{tok_rows(p.q, p, s, v.c0), p.d, n, 0}, Src{tok_rows(p.k, p, s, v.c0), p.d, n, 0},
+                               m0, n0, nin, stage_lds<kLdsScores>());
     else
-      gemm1<128, true, true>(acc[0], Src{at<float>(v.reg, y.hq[(l - 1) & 1]), p.maxw, n},
-                             Src{at<float>(v.reg, y.act[l - 1]), nin, n}, m0, n0, nin, stage_lds());
+      gemm1<128, kPair, kPair>(acc, Src{at<uint16_t>(v.reg, y.hq[(l - 1) & 1]), p.maxw, n, (int64_t)b * p.maxw},
+                               Src{at<uint16_t>(v.reg, y.act[l - 1]), nin, n, (int64_t)b * nin}, m0, n0, nin,
+                               stage_lds<kLdsScores>());
   }
   const float* D = at<float>(v.reg, y.D);
-  float* P = at<float>(v.reg, y.P);
+  const PairArr P = pair(v.reg, y.P, (int64_t)b * b);
   const int col = acc_col(n0);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = acc_row(m0, r);
-    P[(int64_t)row * b + col] = (col <= row && row < n && col < n) ? D[(int64_t)row * b + col] * acc[0][r] : 0.f;
+    put_pair(P.p, P.lo, (int64_t)row * b + col,
+             (col <= row && row < n && col < n) ? D[(int64_t)row * b + col] * acc[r] : 0.f);
   }
 }
 
 // ---- reads: zq^l = diag(A) h W_0^T + diag(F) h S_0^T - P delta^l, then SiLU
 // (or y at the last layer); chunk-start reads take zq^l = h W_0^T ----
-__global__ void __launch_bounds__(kThreads) deep_read_kernel(DP p, int c, int l) {
-  const int s = blockIdx.y;
-  const View v = view(p, s, c);
-  const DLayout& y = p.lay;
-  const int b = y.b, n = v.n;
+__global__ void __launch_bounds__(kThreadsW) deep_read_kernel(DP p, int c, int l) {
+  const int n = min(p.chunk, p.N - c * p.chunk);
   const int nin = p.w[l - 1], nout = p.w[l];
   const int ntn = nout / kT;
-  const int m0 = (blockIdx.x / ntn) * kT, n0 = (blockIdx.x % ntn) * kT;
+  const Place pl = place(((n + kMT - 1) / kMT) * ntn);
+  const int s = pl.s;
+  const View v = view(p, s, c);
+  const DLayout& y = p.lay;
+  const int b = y.b;
+  const int m0 = (pl.tile / ntn) * kMT, n0 = (pl.tile % ntn) * kT;
   const bool raw = p.read_mode == TM_READ_AFTER_WRITE;
   // h W_0^T and h S_0^T share the staged h (one pipeline); the masked term
   // runs over the chunk's tokens
-  f32x16 ws[1][2] = {}, at_ = {};
-  const Src WS[2] = {{v.W0 + p.off[l], nin, nout}, {v.S0 + p.off[l], nin, nout}};
+  f32x16 ws[2] = {}, wo[1] = {}, tk = {};
+  const Src WS[2] = {{v.W0 + p.off[l], nin, nout, 0}, {v.S0 + p.off[l], nin, nout, 0}};
   const Src Wonly[1] = {WS[0]};
-  f32x16 wo[1][1] = {};
   if (l == 1) {
-    const Src H = {tok_rows(p.q, p, s, v.c0), p.d, n};
+    const Src H = {tok_rows(p.q, p, s, v.c0), p.d, n, 0};
     if (raw)
-      gemm<64, 1, 2, false, false, true>(ws, H, WS, m0, n0, nin, nullptr, nullptr, stage_lds());
+      gemm<64, 2, kBF16, kF32, kMT>(ws, H, WS, m0, n0, nin, stage_lds<kLdsW>());
     else
-      gemm<128, 1, 1, false, false, true>(wo, H, Wonly, m0, n0, nin, nullptr, nullptr, stage_lds());
+      gemm<128, 1, kBF16, kF32, kMT>(wo, H, Wonly, m0, n0, nin, stage_lds<kLdsW>());
   } else {
-    const Src H = {at<float>(v.reg, y.hq[(l - 1) & 1]), p.maxw, n};
+    const Src H = {at<uint16_t>(v.reg, y.hq[(l - 1) & 1]), p.maxw, n, (int64_t)b * p.maxw};
     if (raw)
-      gemm<64, 1, 2, false, true, true>(ws, H, WS, m0, n0, nin, nullptr, nullptr, stage_lds());
+      gemm<64, 2, kPair, kF32, kMT>(ws, H, WS, m0, n0, nin, stage_lds<kLdsW>());
     else
-      gemm<128, 1, 1, false, true, true>(wo, H, Wonly, m0, n0, nin, nullptr, nullptr, stage_lds());
+      gemm<128, 1, kPair, kF32, kMT>(wo, H, Wonly, m0, n0, nin, stage_lds<kLdsW>());
   }
   if (raw)
-    gemm1<64, true, true>(at_, Src{at<float>(v.reg, y.P), b, n}, Src{at<float>(v.reg, y.dltT[l]), b, nout}, m0, n0,
-                          n, stage_lds());
-  const f32x16 aw[1] = {raw ? ws[0][0] : wo[0][0]}, as[1] = {ws[0][1]};
+    gemm1<64, kPair, kPair, kMT>(tk, Src{at<uint16_t>(v.reg, y.P), b, n, (int64_t)b * b},
+                                 Src{at<uint16_t>(v.reg, y.dltT[l]), b, nout, (int64_t)nout * b}, m0, n0, n,
+                                 stage_lds<kLdsW>());
   const float* cf = at<float>(v.reg, y.coef);
   const int col = acc_col(n0);
   const bool lastl = l == p.L;
-  float* hn = at<float>(v.reg, y.hq[l & 1]);
+  const PairArr hn = pair(v.reg, y.hq[l & 1], (int64_t)b * p.maxw);
   uint16_t* yo = p.y + ((int64_t)s * p.N + v.c0) * p.d;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = acc_row(m0, r);
     const int rc = min(row, n - 1);
-    const float zq = raw ? cf[rc] * aw[0][r] + cf[2 * b + rc] * as[0][r] - at_[r] : aw[0][r];
+    const float zq = raw ? cf[rc] * ws[0][r] + cf[2 * b + rc] * ws[1][r] - tk[r] : wo[0][r];
     if (row < n) {
       if (lastl)
         yo[(int64_t)row * p.d + col] = f2bf(zq);
       else
-        hn[(int64_t)row * p.maxw + col] = silu(zq);
+        put_pair(hn.p, hn.lo, (int64_t)row * p.maxw + col, silu(zq));
     }
   }
 }
 
-// ---- the input state into slot 0: W, S and W^T per layer ----
+// ---- the input state into slot 0 ----
 __global__ void __launch_bounds__(kThreads) deep_convert_kernel(DP p) {
   const int s = blockIdx.y;
   const int64_t i4 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
   if (i4 >= p.P) return;
-  int l = 1;
-  while (l < p.L && i4 >= p.off[l + 1]) ++l;
-  const int nin = p.w[l - 1], nout = p.w[l];
-  const int64_t e = i4 - p.off[l];
-  const int r = (int)(e / nin), c4 = (int)(e % nin);
   unsigned char* base = p.ws + (int64_t)s * p.ws_stride + 2 * p.lay.region;
-  float* W = (float*)base;
-  float* S = (float*)(base + p.lay.copy);
-  float* WT = (float*)(base + 2 * p.lay.copy);
-  const float4 w = *(const float4*)(p.W_in + (int64_t)s * p.P + i4);
-  const float4 x = *(const float4*)(p.S_in + (int64_t)s * p.P + i4);
-  *(float4*)(W + i4) = w;
-  *(float4*)(S + i4) = x;
-  const float wv[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) WT[p.off[l] + (int64_t)(c4 + i) * nout + r] = wv[i];
+  *(float4*)((float*)base + i4) = *(const float4*)(p.W_in + (int64_t)s * p.P + i4);
+  *(float4*)((float*)(base + p.lay.copy) + i4) = *(const float4*)(p.S_in + (int64_t)s * p.P + i4);
 }
 
 DP make_dp(const Shape& s, int chunk) {
@@ -682,7 +832,16 @@ bool deep_supported(const Shape& s, int chunk) {
   if (chunk <= 0 || chunk > kMaxChunkDeep) return false;
   for (int l = 0; l <= s.L; ++l)
     if (s.widths[l] % kT != 0 || s.widths[l] > 4096) return false;
-  return s.streams <= 65535;
+  // one-dimensional grids of tiles x streams (the input copy: streams in y)
+  const int64_t mt = ((chunk < s.N ? chunk : s.N) + kT - 1) / kT;
+  int64_t tiles = mt * mt;
+  int64_t fold = 0;
+  for (int l = 1; l <= s.L; ++l) {
+    tiles = std::max<int64_t>(tiles, mt * (s.widths[l] / kT) + 1);
+    fold += (int64_t)(s.widths[l] / kT) * (s.widths[l - 1] / kT);
+  }
+  tiles = std::max(tiles, fold);
+  return s.streams <= 65535 && (int64_t)s.streams * tiles < ((int64_t)1 << 31);
 }
 
 int64_t deep_ws_bytes(const Shape& s, int chunk) { return deep_layout(s, chunk).total * (int64_t)s.streams; }
@@ -719,17 +878,17 @@ hipError_t launch_deep(const Shape& s, int chunk, const void* k, const void* v, 
     hipError_t err;
     for (int c = 0; c < p.nch; ++c) {
       const int n = std::min(chunk, s.N - c * chunk);
-      const int mt = (n + kT - 1) / kT;
+      const int mt = (n + kT - 1) / kT, mw = (n + kMT - 1) / kMT;
       // the sweep of chunk c reuses region c % 2 and writes slot (c + 1) % 3,
       // both last read by the reads of chunk c - 2
       if (c >= 2 && (err = hipStreamWaitEvent(stream, x->cons[c & 1], 0)) != hipSuccess) return err;
       for (int l = 1; l <= L; ++l) {
-        hipLaunchKernelGGL(deep_key_kernel, dim3(mt * (s.widths[l] / kT) + (l == 1), S), dim3(kThreads), 0, stream,
+        hipLaunchKernelGGL(deep_key_kernel, dim3((mw * (s.widths[l] / kT) + (l == 1)) * S), dim3(kThreadsW), 0, stream,
                            p, c, l);
         if ((err = hipGetLastError()) != hipSuccess) return err;
       }
       for (int l = L; l >= 2; --l) {
-        hipLaunchKernelGGL(deep_back_kernel, dim3(mt * (s.widths[l - 1] / kT), S), dim3(kThreads), 0, stream, p, c,
+        hipLaunchKernelGGL(deep_back_kernel, dim3(mw * (s.widths[l - 1] / kT) * S), dim3(kThreadsW), 0, stream, p, c,
                            l);
         if ((err = hipGetLastError()) != hipSuccess) return err;
       }
@@ -737,16 +896,16 @@ hipError_t launch_deep(const Shape& s, int chunk, const void* k, const void* v, 
       if ((err = hipStreamWaitEvent(x->st, x->prod[c & 1], 0)) != hipSuccess) return err;
       for (int l = 1; l <= L; ++l) {
         if (raw) {
-          hipLaunchKernelGGL(deep_scores_kernel, dim3(mt * mt, S), dim3(kThreads), 0, x->st, p, c, l);
+          hipLaunchKernelGGL(deep_scores_kernel, dim3(mt * mt * S), dim3(kThreads), 0, x->st, p, c, l);
           if ((err = hipGetLastError()) != hipSuccess) return err;
         }
-        hipLaunchKernelGGL(deep_read_kernel, dim3(mt * (s.widths[l] / kT), S), dim3(kThreads), 0, x->st, p, c, l);
+        hipLaunchKernelGGL(deep_read_kernel, dim3(mw * (s.widths[l] / kT) * S), dim3(kThreadsW), 0, x->st, p, c, l);
         if ((err = hipGetLastError()) != hipSuccess) return err;
       }
       if ((err = hipEventRecord(x->cons[c & 1], x->st)) != hipSuccess) return err;
       int tiles = 0;
       for (int l = 1; l <= L; ++l) tiles += (s.widths[l] / kT) * (s.widths[l - 1] / kT);
-      hipLaunchKernelGGL(deep_fold_kernel, dim3(tiles, S), dim3(kThreads), 0, stream, p, c, c == p.nch - 1 ? 1 : 0);
+      hipLaunchKernelGGL(deep_fold_kernel, dim3(tiles * S), dim3(kThreads), 0, stream, p, c, c == p.nch - 1 ? 1 : 0);
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     return hipSuccess;
