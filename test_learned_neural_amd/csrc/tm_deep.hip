@@ -20,7 +20,7 @@
 // Mapping on gfx950.  A deep memory's state (5.2 MB per stream at d = 128,
 // hidden 512, four layers, W and S in fp32) fits neither one CU nor a few, so
 // every step of a chunk is one launch over all streams, its output tiles
-// (64 x 64, four waves each holding a 32 x 32 block) spread over the CUs:
+// spread over the CUs:
 //
 //   sweep (caller's stream)  key(1) .. key(L), back(L) .. back(2), fold
 //   reads (a second stream)  scores(1), read(1), .. scores(L), read(L)
@@ -28,20 +28,31 @@
 // The reads of chunk c need the chunk-start state and the chunk's
 // activations and deltas, not the fold, so they run beside the fold of
 // chunk c and the sweep of chunk c + 1.  Every contraction runs on
-// v_mfma_f32_32x32x16_bf16 with bf16 operands and fp32 sums: both operands
-// are staged through LDS in 64-deep k slices, the next slice's loads in
-// flight during the current slice's products.  The operands always have k
-// contiguous in memory; the producers write a transposed copy where a later
-// contraction runs over the other index (the tokens of a^l and delta^l, the
-// output units of W^l).
+// v_mfma_f32_32x32x16_bf16 with fp32 sums; its operands are staged through
+// LDS in 64- or 128-deep k slices, the next slice's loads in flight while
+// the current slice is multiplied.  The key, backprop and read products take
+// 128 token rows per workgroup (eight waves), so each reads the chunk-start
+// state once; the scores and the fold take 64 x 64 tiles (four waves).  Every
+// tile of a stream runs on one XCD (place()).
 //
-// The state stays fp32 in W_out / S_out, read and written only by the fold;
-// the fold also leaves bf16 copies of the new state (W, S and W^T per layer)
-// for the next chunk's products.  The copies rotate through three slots and
-// the chunk intermediates through two regions of the workspace, so the
+// Precision: a product of two bf16-rounded operands carries about 2^-8 of
+// error, and through four layers, the masked scores and the fold that sits
+// at the edge of the 2e-2 bar (alpha = 1: 2.1e-2 per token).  So every
+// operand but the exact bf16 keys and queries is split into hi = bf16(x) and
+// lo = bf16(x - hi), and products are summed as hi*hi + hi*lo + lo*hi (three
+// instructions, about 2^-16).  The producers write their results (a^l,
+// delta^l, the query activations, the scores) as hi/lo pairs once; the
+// fp32 state is split as it is staged.  Operands always have k contiguous in
+// memory: the producers write a transposed copy where a later contraction
+// runs over the tokens (a^l scaled by the fold weights D[n-1, .] and U,
+// delta^l), and the backprop stages W^l transposed.
+//
+// The state stays fp32.  The fold reads it from slot c % 3 of the workspace
+// and writes the new state to slot (c + 1) % 3 (W_out / S_out at the last
+// chunk); the chunk intermediates alternate between two regions.  So the
 // reads of chunk c (slot c % 3, region c % 2) never meet the writes of the
-// two chunks after it.  The fold's weights (D's last row, U) scale the
-// deltas as they are staged.
+// two chunks after it: the sweep of chunk c + 2 waits for the reads of chunk
+// c before it starts.
 #include "tm_internal.h"
 
 #include <hip/hip_bf16.h>
