@@ -334,6 +334,74 @@ def bench_retrieve(args, np, torch, tmm, wl, steps=10):
     return res
 
 
+def bench_workloads(args, np, torch, tmm, wl):
+    """Every other memory workload (the linear fp32 memory, 32 streams x
+    4096, 16 streams x 1,048,576 tokens, the 4-layer deep memory): one
+    warmup and two timed titans_mem_forward calls each, with HIP events on
+    the launch stream; inputs resident in HBM.  Returns a list of objects
+    (workload, kernel path, ms per call, memory-tokens/s, algorithmic
+    roofline fraction against the path's peak)."""
+    dev = torch.device("cuda:0")
+    paths = {tmm.PATH_GENERIC_F32: ("generic_f32", "f32"), tmm.PATH_MLP2_D64_H256: ("mlp2_d64_h256_mfma", "f16"),
+             tmm.PATH_DEEP_BF16: ("deep_bf16_mfma", "bf16")}
+    out = []
+    for name in ("linear", "mlp2_short", "long", "deep"):
+        if name == args.workload:
+            continue
+        cfg = wl.WORKLOADS[name]
+        t0 = time.time()
+        inp = wl.make_inputs(cfg, workers=min(16, len(os.sched_getaffinity(0))))
+        B, H, N, d, P = cfg.B, cfg.H, cfg.N, cfg.d, cfg.param_count
+
+        def tok(a):
+            t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if cfg.io == "bf16" else torch.from_numpy(a)
+            return t.reshape(B, H, N, d).to(dev)
+
+        def per(a, n):
+            return torch.from_numpy(a).reshape(B, H, n).to(dev)
+
+        k, v, q = tok(inp["k"]), tok(inp["v"]), tok(inp["q"])
+        alpha, eta, theta = per(inp["alpha"], N), per(inp["eta"], N), per(inp["theta"], N)
+        W0, S0 = per(inp["W0"], P), per(inp["S0"], P)
+        del inp
+        y, W_out, S_out = torch.empty_like(k), torch.empty_like(W0), torch.empty_like(S0)
+        desc = tmm.make_desc(B, H, N, d, cfg.hidden, cfg.n_layers, cfg.io)
+        path = tmm.select_path(desc, cfg.chunk)
+        ws_bytes = tmm.workspace_bytes(desc, cfg.chunk)
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        stream = torch.cuda.current_stream(dev)
+
+        def step():
+            rc = tmm.raw_forward(desc, k.data_ptr(), v.data_ptr(), q.data_ptr(), alpha.data_ptr(), eta.data_ptr(),
+                                 theta.data_ptr(), W0.data_ptr(), S0.data_ptr(), cfg.chunk, y.data_ptr(),
+                                 W_out.data_ptr(), S_out.data_ptr(), ws.data_ptr(), ws_bytes, stream.cuda_stream)
+            if rc != tmm.OK:
+                raise tmm.TitansMemError(rc, "titans_mem_forward")
+
+        step()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2)]
+        for a, b in ev:
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        flops_tok, _ = algorithmic_work(cfg)
+        pname, dt = paths.get(path, (str(path), "f32"))
+        tflops = flops_tok * B * H * N / (ms / 1e3) / 1e12
+        res = {"workload": cfg.name, "kernel_path": pname, "ms_per_call": ms,
+               "memory_tokens_per_s": B * H * N / (ms / 1e3), "achieved_tflops": tflops,
+               "peak_tflops": PEAK_TFLOPS[dt], "frac": tflops / PEAK_TFLOPS[dt]}
+        out.append(res)
+        print(f"[bench] {cfg.name}: {ms:.3f} ms per call on {pname} ({res['memory_tokens_per_s']:.3g} memory-tokens/s, "
+              f"{tflops / PEAK_TFLOPS[dt] * 100:.1f}% of {dt} peak; inputs {time.time() - t0:.1f} s)",
+              file=sys.stderr, flush=True)
+        del k, v, q, alpha, eta, theta, W0, S0, y, W_out, S_out, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -347,6 +415,8 @@ def main():
     ap.add_argument("--no-input-side", action="store_true", help="skip the input-side leg")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-retrieve", action="store_true", help="skip the fixed-state retrieval leg")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other memory workloads (one line each in the `workloads` list)")
     ap.add_argument("--retrieve-only", action="store_true",
                     help="time only the fixed-state retrieval (titans_mem_retrieve) and print its JSON line")
     ap.add_argument("--backward-only", action="store_true",
@@ -517,6 +587,8 @@ def main():
         out["retrieve"] = bench_retrieve(args, np, torch, tmm, wl)
     if not args.no_backward:
         out["backward"] = bench_backward(args, np, torch, tmm, wl)
+    if not args.no_workloads:
+        out["workloads"] = bench_workloads(args, np, torch, tmm, wl)
     print(json.dumps(out), flush=True)
 
 
