@@ -74,6 +74,13 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) unsigned short u16x8;
 typedef __attribute__((ext_vector_type(4))) unsigned short u16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+// a 16-byte load that does not stay in the caches (the state, read once a chunk)
+__device__ __forceinline__ float4 load_stream(const float* p) {
+  const f32x4 v = __builtin_nontemporal_load((const f32x4*)p);
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
 
 // A "pair" array holds each value x as hi = bf16(x) and lo = bf16(x - hi)
 // (x - hi is exact in fp32): the hi plane, then the lo plane of the same
@@ -284,7 +291,7 @@ struct Stage<kF32, KS, ROWS, NT> {   // pieces of 4 fp32 values, split as they a
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int e = threadIdx.x + u * NT, row = e / kQ, kq = (e % kQ) * 4;
-      r[u] = k0 + kq < K ? *(const float4*)((const float*)a.p + (int64_t)min(r0 + row, a.rows - 1) * a.ld + k0 + kq)
+      r[u] = k0 + kq < K ? load_stream((const float*)a.p + (int64_t)min(r0 + row, a.rows - 1) * a.ld + k0 + kq)
                          : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
@@ -316,7 +323,7 @@ struct Stage<kF32T, KS, ROWS, NT> {   // fp32 read transposed: pieces of 4 rows 
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int e = threadIdx.x + u * NT, k = e / kQ, rq = (e % kQ) * 4;
-      r[u] = k0 + k < K ? *(const float4*)((const float*)a.p + (int64_t)(k0 + k) * a.ld + r0 + rq)
+      r[u] = k0 + k < K ? load_stream((const float*)a.p + (int64_t)(k0 + k) * a.ld + r0 + rq)
                         : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
@@ -701,8 +708,8 @@ __global__ void __launch_bounds__(kThreads) deep_fold_kernel(DP p, int c, int la
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int64_t i = (int64_t)acc_row(m0, r) * nin + col;
-    w0[r] = Wsrc[i];
-    s0[r] = Ssrc[i];
+    w0[r] = __builtin_nontemporal_load(Wsrc + i);
+    s0[r] = __builtin_nontemporal_load(Ssrc + i);
   }
   // G(D[n-1, :]) and G(U): the deltas against the keys' activations scaled per token
   const Src B[2] = {{at<uint16_t>(v.reg, y.actD[l - 1]), b, nin, (int64_t)nin * b},
@@ -717,8 +724,8 @@ __global__ void __launch_bounds__(kThreads) deep_fold_kernel(DP p, int c, int la
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int64_t i = (int64_t)acc_row(m0, r) * nin + col;
-    Wd[i] = An * w0[r] + Fn * s0[r] - g[0][r];
-    Sd[i] = En * s0[r] - g[1][r];
+    __builtin_nontemporal_store(An * w0[r] + Fn * s0[r] - g[0][r], Wd + i);
+    __builtin_nontemporal_store(En * s0[r] - g[1][r], Sd + i);
   }
 }
 
