@@ -150,11 +150,13 @@ int64_t titans_mem_workspace_bytes(const titans_mem_desc* desc, int32_t chunk);
  *              chunk) bytes (may be NULL when that is 0); its contents on
  *              entry do not matter and are undefined on return.
  *   stream     hipStream_t to enqueue on (NULL = default stream).  On the
- *              shape-generic kernel, when the state does not fit on chip
+ *              deep-memory path (TM_PATH_DEEP_BF16), and on the
+ *              shape-generic kernel when the state does not fit on chip
  *              and chunk >= 16 (and the call is not in place), part of the
- *              work runs on a second stream of the library's own (one per
- *              device, default priority), ordered against `stream` with
- *              events and joined back into it before the call's work ends.
+ *              work (the retrieval) runs on a second stream of the
+ *              library's own (one per device, default priority), ordered
+ *              against `stream` with events and joined back into it before
+ *              the call's work ends.
  *
  * Returns TM_OK or a negative status.  Resuming: passing (W_out, S_out) of
  * a call as (W_in, S_in) of the next, with a split on a chunk boundary,
