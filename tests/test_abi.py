@@ -52,6 +52,13 @@ def test_param_count_and_paths(lib):
     assert tmm.select_path(tmm.make_desc(4, 8, 0, 128, 512, 4, "bf16"), 128) == tmm.PATH_GENERIC_F32
     assert tmm.select_path(tmm.make_desc(4, 8, 32768, 128, 512, 4, "bf16", flags=tmm.FLAG_FORCE_GENERIC),
                            128) == tmm.PATH_GENERIC_F32
+    # its workspace: the same bytes per stream whatever the stream count, at least the fp32 state's
+    # three rotating (W, S) slots, and a single short chunk needs no more than a full one
+    w5 = tmm.workspace_bytes(d5, 128)
+    assert w5 > 0 and w5 % 32 == 0
+    assert tmm.workspace_bytes(tmm.make_desc(2, 8, 32768, 128, 512, 4, "bf16"), 128) * 2 == w5
+    assert w5 // 32 >= 3 * 2 * 4 * tmm.param_count(d5)
+    assert tmm.workspace_bytes(tmm.make_desc(4, 8, 100, 128, 512, 4, "bf16"), 128) <= w5
     assert tmm.select_path(d3, 0) == tmm.ERR_INVALID
     forced = tmm.make_desc(8, 16, 16384, 64, 256, 2, "bf16", flags=tmm.FLAG_FORCE_GENERIC)
     assert tmm.select_path(forced, 64) == tmm.PATH_GENERIC_F32
