@@ -47,7 +47,10 @@
 // runs over the tokens (a^l scaled by the fold weights D[n-1, .] and U,
 // delta^l), and the backprop stages W^l transposed.
 //
-// The state stays fp32.  The fold reads it from slot c % 3 of the workspace
+// The state stays fp32 and is read and written with non-temporal (streaming)
+// loads and stores: it is touched once per chunk by each product, and kept
+// out of L2 it leaves room there for the activations and deltas that a
+// stream's tiles re-read.  The fold reads it from slot c % 3 of the workspace
 // and writes the new state to slot (c + 1) % 3 (W_out / S_out at the last
 // chunk); the chunk intermediates alternate between two regions.  So the
 // reads of chunk c (slot c % 3, region c % 2) never meet the writes of the
