@@ -32,7 +32,8 @@ DOMINANT_KERNEL = {"mlp2_d64_h256_mfma": ("mlp2_group_kernel", ("tm_mlp2_group.h
                    "input_side": ("input_kernel", ("tm_input.hip",)),
                    "retrieve_mlp2": ("mlp2_retrieve_kernel", ("tm_retrieve.hip",)),
                    "backward": ("backward_kernel", ("tm_backward.hip", "tm_generic.hip", "tm_block_gemm.h")),
-                   "deep_bf16_mfma": ("deep_read_kernel", ("tm_deep.hip",))}
+                   "deep_bf16_mfma": ("deep_read_kernel", ("tm_deep.hip",)),
+                   "linear_f32": ("linear_kernel", ("tm_linear.hip",))}
 
 
 def _source_digest(srcs):
@@ -556,6 +557,8 @@ def main():
     kernel_path_name = {tmm.PATH_GENERIC_F32: "generic_f32",
                         tmm.PATH_MLP2_D64_H256: "mlp2_d64_h256_mfma",
                         tmm.PATH_DEEP_BF16: "deep_bf16_mfma"}.get(path, str(path))
+    if path == tmm.PATH_GENERIC_F32 and cfg.n_layers == 1 and cfg.d <= 64 and cfg.d % 4 == 0 and cfg.chunk <= 64:
+        kernel_path_name = "linear_f32"   # the generic path's linear-memory kernel
     out = {
         "metric": "memory tokens/sec (retrieve + chunked update), 1 GPU",
         "value": value,
